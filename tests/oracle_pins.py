@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with a hand-worked value, a closed form, a library routine
+(numpy / scipy / torch), a brute-force computation or an invariant.  The
+same battery runs against the oracle (every pin must pass) and against the
+planted-mistake builds (each must fail at least one pin), see
+test_oracle_pins.py and test_oracle_mutants.py.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import scipy.special
+import torch
+
+from gemv_router_softmax_amd import synth
+import dense_ref
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TINY = synth.Dims(E=16, topk=4, H=128, I=64, G=16)
+SMALL = synth.Dims(E=32, topk=8, H=256, I=128, G=64)
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _hex(s):
+    return int(s, 16)
+
+
+# ------------------------------------------------------------------ formats
+
+def pin_fp16_decode_exhaustive(o):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = o.fp16_decode(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_bf16_decode_exhaustive(o):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = o.bf16_decode(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_bf16_round_from_f32(o):
+    """float32 inputs: one rounding, so torch's float32->bf16 RNE is exact."""
+    rng = np.random.default_rng(1)
+    raw = rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    # every bf16 rounding midpoint (low half 0x8000) and its neighbours
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    mids = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001, hi])
+    f = np.concatenate([raw, mids]).view(np.float32)
+    f = f[np.isfinite(f)]
+    got = o.round_bf16(f.astype(np.float64))
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} mismatches"
+
+
+def _exact_bf16(v: float) -> int:
+    """Nearest bf16 by exact rational comparison among neighbours of a guess."""
+    guess = int(torch.tensor([v], dtype=torch.float64).to(torch.bfloat16).view(torch.int16)
+                .numpy().view(np.uint16)[0])
+    best = None
+    target = Fraction(v)
+    for c in (guess - 1, guess, guess + 1):
+        c &= 0xFFFF
+        if (c & 0x7F80) == 0x7F80:
+            continue
+        val = Fraction(float(dense_ref.bf16_to_f64(np.array([c], np.uint16))[0]))
+        dist = abs(val - target)
+        key = (dist, c & 1)           # ties: even significand wins
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def pin_bf16_round_from_double(o):
+    """float64 inputs that are not float32: brute-force exact rounding."""
+    rng = np.random.default_rng(2)
+    v = rng.standard_normal(400) * np.exp2(rng.integers(-60, 60, 400))
+    # values just beside a midpoint, where a double rounding would go wrong
+    base = dense_ref.bf16_to_f64(np.array([0x3F80, 0x4000, 0x417B, 0x3C00], np.uint16))
+    half_ulp = base * 2.0 ** -8
+    v = np.concatenate([v, base + half_ulp * (1 + 2.0 ** -30), base + half_ulp * (1 - 2.0 ** -30),
+                        base + half_ulp, base + 3 * half_ulp])
+    got = o.round_bf16(v)
+    for vi, gi in zip(v, got):
+        assert int(gi) == _exact_bf16(float(vi)), (vi, hex(int(gi)))
+
+
+# ---------------------------------------------------------- dequantisation
+
+def pin_nibble_order_golden(o):
+    g = golden("dequant_examples.json")
+    p2 = g["power_of_two_group"]
+    s = np.full((1, 1), _hex(p2["scale_bits"]), np.uint16)
+    b = np.full((1, 1), _hex(p2["bias_bits"]), np.uint16)
+    for ex in g["nibble_order"]:
+        q = np.full((1, 8), _hex(ex["word"]), np.uint32)        # one row, K=64
+        for k, code in enumerate(ex["codes"]):
+            want = p2["w_of_code"].get(str(code), (code - 7.5) / 256)
+            assert o.dequant(q, s, b, 0, 64, 64, k) == want, (ex, k)
+
+
+def pin_fp16_scale_golden(o):
+    f = golden("dequant_examples.json")["fp16_scale_example"]
+    s = np.full((1, 1), _hex(f["scale_bits"]), np.uint16)
+    b = np.full((1, 1), _hex(f["bias_bits"]), np.uint16)
+    assert o.fp16_decode(s)[0, 0] == f["scale_value"]
+    assert o.fp16_decode(b)[0, 0] == f["bias_value"]
+    q0 = np.zeros((1, 8), np.uint32)
+    q15 = np.full((1, 8), 0xFFFFFFFF, np.uint32)
+    assert o.dequant(q0, s, b, 0, 64, 64, 5) == f["w_code0"]
+    assert o.dequant(q15, s, b, 0, 64, 64, 63) == f["w_code15"]
+
+
+def _one_expert_layer(dims, gate_word, scale_bits, bias_bits):
+    """Layer whose gate/up/down are constant words (identical experts)."""
+    L = synth.constant_layer(dims, 0, scale_bits, bias_bits)
+    for q in (L.routed, L.shared):
+        q.gate_q[...] = gate_word
+        q.up_q[...] = gate_word
+    return L
+
+
+def pin_group_closed_form(o):
+    """x = one-hot at k=1 and x = 1 on one group, read back through the
+    expert's gate product (via its SwiGLU output h)."""
+    g = golden("dequant_examples.json")["power_of_two_group"]
+    d = synth.Dims(E=1, topk=1, H=64, I=8, G=64)
+    for word, want_sum in ((0x76543210, g["group_sum_x1_8x_0x76543210"]),
+                           (0xFEDCBA98, g["group_sum_x1_8x_0xFEDCBA98"])):
+        L = _one_expert_layer(d, word, _hex(g["scale_bits"]), _hex(g["bias_bits"]))
+        x = np.full((1, 64), 0x3F80, np.uint16)                 # bf16 1.0
+        _, hb = o.expert_ffn(L, x, np.array([0, 1], np.int32), np.array([0], np.int32),
+                             want_h=True)
+        h = o.bf16_decode(hb)
+        gval = want_sum
+        want_h = dense_ref.f64_to_bf16_bits(np.array([gval * scipy.special.expit(gval) * gval]))
+        assert np.all(hb == want_h[0]), (hex(word), h[0, :2])
+    # one-hot at k = 1
+    L = _one_expert_layer(d, 0x76543210, _hex(g["scale_bits"]), _hex(g["bias_bits"]))
+    x = np.zeros((1, 64), np.uint16)
+    x[0, 1] = 0x3F80
+    _, hb = o.expert_ffn(L, x, np.array([0, 1], np.int32), np.array([0], np.int32),
+                         want_h=True)
+    gk = g["one_hot_k1_word_0x76543210"]
+    want_h = dense_ref.f64_to_bf16_bits(np.array([gk * scipy.special.expit(gk) * gk]))
+    assert np.all(hb == want_h[0])
+
+
+# ------------------------------------------------------------------ routing
+
+def _rand_layer(dims, seed=0, skewed=False):
+    return synth.make_layer(dims, seed=seed, layer=0, skewed_bias=skewed)
+
+
+def pin_router_vs_numpy(o):
+    for dims, T, skew in ((TINY, 40, False), (SMALL, 24, True), (synth.PROD, 3, True)):
+        L = _rand_layer(dims, seed=3, skewed=skew)
+        x = synth.make_x(T, dims, seed=3)
+        r = o.route(L, x)
+        xr = dense_ref.bf16_to_f64(x)
+        logits, sel, w, sg = dense_ref.route_dense(L, xr)
+        assert np.allclose(r.logits, logits, rtol=1e-12, atol=1e-12)
+        assert np.allclose(r.sg, sg, rtol=1e-12, atol=0)
+        # weights compared by expert id (selection itself is pinned below)
+        assert np.array_equal(np.sort(r.ids, 1), np.sort(sel, 1))
+        for t in range(T):
+            wm = dict(zip(sel[t].tolist(), w[t].tolist()))
+            for j, e in enumerate(r.ids[t]):
+                assert abs(r.w[t, j] - wm[int(e)]) < 1e-13
+
+
+def pin_topk_bruteforce(o):
+    for dims, T in ((TINY, 64), (synth.PROD, 4)):
+        L = _rand_layer(dims, seed=5)
+        x = synth.make_x(T, dims, seed=5)
+        r = o.route(L, x)
+        want = np.argsort(-r.logits.astype(np.float32), axis=1, kind="stable")[:, :dims.topk]
+        assert np.array_equal(r.ids, want)
+        # gap = k-th largest minus the best unselected (float64 logits)
+        srt = np.sort(r.logits, axis=1)[:, ::-1]
+        assert np.allclose(r.gap, srt[:, dims.topk - 1] - srt[:, dims.topk], atol=1e-15)
+
+
+def pin_topk_ties(o):
+    """Duplicate router rows make exactly equal logits: lower index first."""
+    d = TINY
+    L = _rand_layer(d, seed=6)
+    L.w_router[9] = L.w_router[2]
+    L.w_router[12] = L.w_router[2]
+    L.w_router[3] = L.w_router[14]
+    x = synth.make_x(32, d, seed=6)
+    r = o.route(L, x)
+    want = np.argsort(-r.logits.astype(np.float32), axis=1, kind="stable")[:, :d.topk]
+    assert np.array_equal(r.ids, want)
+    # make expert 2 (and its copies) the clear winner for every token
+    L.w_router[2] = dense_ref.f64_to_bf16_bits(dense_ref.bf16_to_f64(x[0]) * 0.5)
+    L.w_router[9] = L.w_router[2]
+    L.w_router[12] = L.w_router[2]
+    r = o.route(L, x[:1])
+    assert list(r.ids[0, :3]) == [2, 9, 12]
+
+
+def pin_route_zero_input(o):
+    z = golden("closed_forms.json")["zero_input"]
+    L = _rand_layer(synth.PROD, seed=7)
+    x = np.zeros((2, synth.PROD.H), np.uint16)
+    r = o.route(L, x)
+    assert np.all(r.logits == 0.0)
+    assert np.array_equal(r.ids, np.tile(np.array(z["ids"], np.int32), (2, 1)))
+    assert np.all(r.w == z["w"]) and np.all(r.sg == z["sg"])
+
+
+def pin_weights_sum_to_one(o):
+    L = _rand_layer(synth.PROD, seed=8, skewed=True)
+    r = o.route(L, synth.make_x(16, synth.PROD, seed=8))
+    assert np.allclose(r.w.sum(1), 1.0, rtol=0, atol=4e-16)
+    assert np.all(r.w > 0) and np.all(np.diff(r.w, axis=1) <= 1e-15)  # descending logits
+
+
+# -------------------------------------------------------------- permutation
+
+def pin_permute_bruteforce(o):
+    rng = np.random.default_rng(9)
+    for dims, T in ((TINY, 1), (TINY, 37), (synth.PROD, 513)):
+        ids = np.stack([rng.permutation(dims.E)[:dims.topk] for _ in range(T)]).astype(np.int32)
+        p = o.permute(dims, ids)
+        flat = ids.ravel()
+        assert np.array_equal(p.perm, np.argsort(flat, kind="stable"))
+        assert np.array_equal(p.inv[p.perm], np.arange(flat.size))
+        assert np.array_equal(p.counts, np.bincount(flat, minlength=dims.E))
+        assert p.offsets[0] == 0 and p.offsets[-1] == dims.topk * T
+        assert np.array_equal(np.diff(p.offsets), p.counts)
+        tok = p.perm // dims.topk
+        assert np.array_equal(np.bincount(tok, minlength=T), np.full(T, dims.topk))
+        for e in range(dims.E):                       # ascending tokens per segment
+            seg = p.perm[p.offsets[e]:p.offsets[e + 1]]
+            assert np.all(np.diff(seg) > 0)
+    # everything on one expert (a skewed chunk)
+    ids = np.tile(np.arange(TINY.topk, dtype=np.int32), (50, 1))
+    p = o.permute(TINY, ids)
+    assert np.array_equal(p.perm, np.argsort(ids.ravel(), kind="stable"))
+
+
+# --------------------------------------------------------------- expert FFN
+
+def pin_ffn_closed_form(o):
+    c = golden("closed_forms.json")
+    g = golden("dequant_examples.json")["power_of_two_group"]
+    L = synth.constant_layer(synth.PROD, 8, _hex(g["scale_bits"]), _hex(g["bias_bits"]))
+    x = np.full((2, synth.PROD.H), 0x3F80, np.uint16)
+    r = o.layer_forward(L, x)
+    assert np.all(r.y == _hex(c["y_bf16_bits"])), hex(int(r.y[0, 0]))
+    assert np.all(r.y32 == c["y32"])
+    rt = o.route(L, x)
+    pm = o.permute(L.dims, rt.ids)
+    out, hb = o.expert_ffn(L, x, pm.offsets, pm.perm, want_h=True)
+    assert np.all(hb == _hex(c["h_bf16_bits"]))
+    assert np.all(out == c["d"])
+
+
+def pin_dense_all_experts(o):
+    """Sparse oracle == dense masked evaluation over all experts."""
+    for dims, T, skew in ((TINY, 48, False), (SMALL, 16, True), (synth.PROD, 2, False)):
+        L = _rand_layer(dims, seed=11, skewed=skew)
+        x = synth.make_x(T, dims, seed=11)
+        r = o.layer_forward(L, x)
+        y_d, y32_d, ids_d, w_d, sg_d = dense_ref.layer_dense(L, x)
+        assert np.array_equal(np.sort(r.ids, 1), np.sort(ids_d, 1))
+        rel = np.abs(r.y32 - y32_d) / (np.abs(y32_d) + 1e-30)
+        # an h flip (one bf16 ulp of one of I intermediates) moves y32 by ~1e-4 of
+        # the value; without one the two agree to rounding level
+        assert np.median(rel) < 1e-12
+        assert np.mean(rel < 1e-9) > 0.99
+        flips = np.count_nonzero(r.y != y_d)
+        assert flips <= max(2, y_d.size // 1000), flips
+
+
+def pin_shared_gate_and_expert(o):
+    """Shared expert alone: routed experts zeroed out by a zero down matrix."""
+    dims = SMALL
+    L = _rand_layer(dims, seed=12)
+    L.routed.down_q[...] = 0
+    L.routed.down_s[...] = 0
+    L.routed.down_b[...] = 0
+    x = synth.make_x(8, dims, seed=12)
+    r = o.layer_forward(L, x)
+    xr = dense_ref.bf16_to_f64(x)
+    ds, _ = dense_ref.expert_dense(L.shared, 0, xr, dims)
+    sg = scipy.special.expit(xr @ dense_ref.bf16_to_f64(L.w_shared_gate))
+    assert np.allclose(r.y32, sg[:, None] * ds, rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------- invariants
+
+def pin_down_scaling_doubles_output(o):
+    dims = SMALL
+    L = _rand_layer(dims, seed=13)
+    x = synth.make_x(12, dims, seed=13)
+    r1 = o.layer_forward(L, x)
+    for q in (L.routed, L.shared):
+        q.down_s[...] = q.down_s + np.uint16(0x0400)          # exponent + 1: x2
+        q.down_b[...] = q.down_b + np.uint16(0x0400)
+    r2 = o.layer_forward(L, x)
+    assert np.array_equal(r2.y32, 2 * r1.y32)
+    assert np.array_equal(dense_ref.bf16_to_f64(r2.y), 2 * dense_ref.bf16_to_f64(r1.y))
+
+
+def pin_token_permutation_equivariance(o):
+    dims = SMALL
+    L = _rand_layer(dims, seed=14)
+    x = synth.make_x(20, dims, seed=14)
+    pi = np.random.default_rng(14).permutation(20)
+    r1 = o.layer_forward(L, x)
+    r2 = o.layer_forward(L, x[pi].copy())
+    assert np.array_equal(r2.y, r1.y[pi]) and np.array_equal(r2.ids, r1.ids[pi])
+
+
+def pin_chunking_is_exact(o):
+    dims = SMALL
+    L = _rand_layer(dims, seed=15, skewed=True)
+    x = synth.make_x(64, dims, seed=15)
+    whole = o.layer_forward(L, x)
+    parts = np.concatenate([o.layer_forward(L, x[i:i + 16].copy()).y for i in range(0, 64, 16)])
+    assert np.array_equal(whole.y, parts)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
