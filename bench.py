@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""MoE-layer benchmark on one MI355X.
+
+Headline workload (one step = one token through the whole hot path of 40
+distinct seeded MoE layers -- router, top-8, permutation, expert FFNs with
+in-kernel 4-bit dequantisation, combine -- with a residual add between
+layers and a fresh N(0,1) input per step): decode, T = 1.  The 40-layer
+chain is captured once in a HIP graph and replayed per step.
+
+Also measured in the same run and reported in the same JSON line:
+  - the dominant kernel of the decode step (the expert FFN launch) timed
+    with HIP events on the stream it runs on, against HBM peak;
+  - the measured sustained HBM read rate (a streaming read probe);
+  - prefill, T = 4096 tokens through one layer (rotating over the 40 layers
+    so the weights are not cache resident), with MFMA utilisation;
+  - the CPU oracle on a bounded sample of the decode workload.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+H, I, E, TOPK = 2048, 512, 256, 8
+EXPERT_BYTES = 3 * I * H // 2 + 3 * (I * H // 64) * 2 * 2      # 1,769,472 B
+EXPERT_FLOP_PER_TOKEN = 2 * 3 * I * H                           # 6,291,456
+HBM_PEAK_GBS = 8000.0
+BF16_DENSE_PEAK_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk/CU (fp16 = bf16 rate)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gen_layers(n, skewed=False, threads=16):
+    from gemv_router_softmax_amd import synth
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(lambda l: synth.make_layer(synth.PROD, seed=0, layer=l,
+                                                      skewed_bias=skewed), range(n)))
+
+
+def event_pairs(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def decode_chain(D, args):
+    import torch
+    import gemv_router_softmax_amd as moe
+    from gemv_router_softmax_amd import synth
+
+    K, W = args.steps, args.warmup
+    xs = torch.from_numpy(np.stack([synth.make_x(1, seed=0, step=s) for s in range(W + K)])
+                          .view(np.int16)).cuda()                       # [W+K, 1, H]
+    x0 = torch.empty((1, H), dtype=torch.int16, device="cuda")
+    bufs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in range(2)]
+    y = torch.empty((1, H), dtype=torch.int16, device="cuda")
+    ws = moe.workspace(1)
+
+    def chain():
+        cur = x0
+        for l, Dl in enumerate(D):
+            nxt = bufs[l % 2]
+            moe.moe_layer_forward_ex(cur, Dl, y, ws, residual_out=nxt)
+            cur = nxt
+
+    x0.copy_(xs[0])
+    chain()
+    torch.cuda.synchronize()
+    g = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            chain()
+        torch.cuda.synchronize()
+
+    def step(s):
+        x0.copy_(xs[s])
+        if g is not None:
+            g.replay()
+        else:
+            chain()
+
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    e0, e1 = event_pairs(1)[0]
+    e0.record()
+    for s in range(K):
+        step(W + s)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    return ms, xs
+
+
+def decode_kernel_timing(D, xs, reps):
+    """HIP events around the decode expert-FFN launch (plan + gate/up GEMV +
+    down GEMV) on the stream it is launched on, per layer, with the real
+    routing of the token."""
+    import torch
+    import gemv_router_softmax_amd as moe
+
+    T = 1
+    ws = moe.workspace(T)
+    ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
+    sg = torch.empty((T,), dtype=torch.float32, device="cuda")
+    counts = torch.empty(256, dtype=torch.int32, device="cuda")
+    offs = torch.empty(257, dtype=torch.int32, device="cuda")
+    perm = torch.empty(8 * T, dtype=torch.int32, device="cuda")
+    inv = torch.empty(8 * T, dtype=torch.int32, device="cuda")
+    out = torch.empty((9 * T, H), dtype=torch.float32, device="cuda")
+    pairs = event_pairs(reps * len(D))
+    k = 0
+    for r in range(reps + 1):
+        for l, Dl in enumerate(D):
+            x = xs[(r * len(D) + l) % xs.shape[0]]
+            moe.moe_route(x, Dl.w_router, Dl.router_bias, Dl.w_shared_gate, ids, w, sg, ws)
+            moe.moe_permute(ids, counts, offs, perm, inv, ws)
+            if r == 0:      # warm-up pass
+                moe.moe_expert_ffn(x, Dl, offs, perm, out, ws, path=moe.MOE_PATH_DECODE)
+                continue
+            a, b = pairs[k]
+            a.record()
+            moe.moe_expert_ffn(x, Dl, offs, perm, out, ws, path=moe.MOE_PATH_DECODE)
+            b.record()
+            k += 1
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in pairs])
+    return float(ms.mean()), float(np.median(ms))
+
+
+def read_ceiling(gib=4, reps=5):
+    import torch
+    import gemv_router_softmax_amd as moe
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    moe.moe_probe_read(buf, sink)
+    pairs = event_pairs(reps)
+    for a, b in pairs:
+        a.record()
+        moe.moe_probe_read(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    best = min(a.elapsed_time(b) for a, b in pairs)
+    del buf
+    return buf_gbs(gib << 30, best)
+
+
+def buf_gbs(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def prefill(D, T, iters):
+    import torch
+    import gemv_router_softmax_amd as moe
+    from gemv_router_softmax_amd import synth
+
+    x = moe.to_device_bits(synth.make_x(T, seed=0))
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ws = moe.workspace(T)
+    for i in range(3):
+        moe.moe_layer_forward(x, D[i % len(D)], y, ws)
+    torch.cuda.synchronize()
+    pairs = event_pairs(iters)
+    for i, (a, b) in enumerate(pairs):
+        a.record()
+        moe.moe_layer_forward(x, D[(i + 3) % len(D)], y, ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in pairs])
+    # the expert FFN (grouped GEMM) alone, on the same routing
+    ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
+    sg = torch.empty((T,), dtype=torch.float32, device="cuda")
+    counts = torch.empty(256, dtype=torch.int32, device="cuda")
+    offs = torch.empty(257, dtype=torch.int32, device="cuda")
+    perm = torch.empty(8 * T, dtype=torch.int32, device="cuda")
+    inv = torch.empty(8 * T, dtype=torch.int32, device="cuda")
+    out = torch.empty((9 * T, H), dtype=torch.float32, device="cuda")
+    fp = event_pairs(iters)
+    for i, (a, b) in enumerate(fp):
+        Dl = D[(i + 7) % len(D)]
+        moe.moe_route(x, Dl.w_router, Dl.router_bias, Dl.w_shared_gate, ids, w, sg, ws)
+        moe.moe_permute(ids, counts, offs, perm, inv, ws)
+        a.record()
+        moe.moe_expert_ffn(x, Dl, offs, perm, out, ws, path=moe.MOE_PATH_PREFILL)
+        b.record()
+    torch.cuda.synchronize()
+    fms = np.array([a.elapsed_time(b) for a, b in fp])
+    flops = EXPERT_FLOP_PER_TOKEN * 9 * T
+    return {
+        "T": T,
+        "layer_ms": float(ms.mean()),
+        "tokens_per_s": T / (ms.mean() * 1e-3),
+        "layer_mfma_util": flops / (ms.mean() * 1e-3) / (BF16_DENSE_PEAK_TFLOPS * 1e12),
+        "expert_ffn_ms": float(fms.mean()),
+        "expert_ffn_tflops": flops / (fms.mean() * 1e-3) / 1e12,
+        "expert_ffn_mfma_util": flops / (fms.mean() * 1e-3) / (BF16_DENSE_PEAK_TFLOPS * 1e12),
+    }
+
+
+def cpu_baseline(layers, budget_s):
+    import oracle
+    from gemv_router_softmax_amd import synth
+    o = oracle.load()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        x = synth.make_x(1, seed=0, step=n)
+        for L in layers:
+            y = o.layer_forward(L, x).y
+            x = o.round_bf16(o.bf16_decode(x) + o.bf16_decode(y))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 64:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": o.threads(), "kind": "oracle",
+            "sample": f"{n} decode steps (T=1) through the same {len(layers)}-layer chain, "
+                      f"{el:.1f} s of CPU work"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=40)
+    ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
+              "(no collectives are built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemv_router_softmax_amd as moe
+    moe.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    t = time.time()
+    host = gen_layers(args.layers)
+    log(f"generated {args.layers} layers in {time.time() - t:.1f}s")
+    t = time.time()
+    D = [moe.DeviceLayer(L) for L in host]
+    torch.cuda.synchronize()
+    log(f"uploaded {sum(d.nbytes for d in D) / 1e9:.2f} GB in {time.time() - t:.1f}s")
+    if args.no_cpu_baseline:
+        del host
+
+    ms, xs = decode_chain(D, args)
+    ms_per_step = ms / args.steps
+    tok_s = args.steps / (ms * 1e-3)
+    log(f"decode chain: {ms_per_step * 1e3:.1f} us/token, {tok_s:.1f} tokens/s")
+
+    k_mean, k_med = decode_kernel_timing(D, xs, args.kernel_reps)
+    per_launch_bytes = 9 * EXPERT_BYTES
+    achieved = per_launch_bytes / (k_mean * 1e-3) / 1e9
+    log(f"decode expert FFN: {k_mean * 1e3:.2f} us/launch (median {k_med * 1e3:.2f}), "
+        f"{achieved:.0f} GB/s")
+    ceiling = read_ceiling()
+    log(f"read ceiling: {ceiling:.0f} GB/s")
+
+    pre = None
+    if not args.no_prefill:
+        pre = prefill(D, 4096, args.prefill_iters)
+        log(f"prefill T=4096: {pre}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+
+    chain_bytes = args.layers * 9 * EXPERT_BYTES
+    out = {
+        "metric": "MoE-layer tokens/s; HBM GB/s at T=1 decode; MFMA util at T=4096 prefill",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded layers and inputs, random-init weights)",
+        "config": {"workload": f"decode T=1 through a {args.layers}-layer MoE chain with "
+                               "residual adds, fresh N(0,1) input per step",
+                   "layers": args.layers, "T": 1, "hidden": H, "experts": E, "topk": TOPK,
+                   "expert_width": I, "group": 64, "weights": "uint4 + fp16 scale/bias",
+                   "hip_graph": not args.no_graph},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode expert FFN launch (plan_tiles + decode_gateup + "
+                               "decode_down)",
+                     "bytes_per_launch": per_launch_bytes, "launch_us": k_mean * 1e3},
+        "active_expert_bytes_per_token": chain_bytes,
+        "wallclock_gbs": chain_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_read_ceiling_gbs": ceiling,
+        "prefill_t4096": pre,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,285 @@
+"""Python binding of libmoe.so, the MI355X sparse mixture-of-experts layer.
+
+Argument marshalling only: every function checks the torch tensors it is
+given (device, dtype, shape, contiguity -- the C side cannot see shapes),
+passes raw device pointers and the current HIP stream to the C ABI of the
+same name (include/moe.h), and raises MoeError on a non-zero status.  All
+computation happens in the HIP kernels; if libmoe.so is missing the calls
+fail loudly, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_HIDDEN = 2048
+MOE_INTER = 512
+MOE_EXPERTS = 256
+MOE_TOPK = 8
+MOE_GROUP = 64
+MOE_T_MAX = 65536
+MOE_DECODE_T = 8
+MOE_DECODE_T_MAX = 32
+
+MOE_PATH_AUTO = 0
+MOE_PATH_DECODE = 1
+MOE_PATH_PREFILL = 2
+
+# Every symbol include/moe.h declares.
+EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_route", "moe_permute",
+           "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
+           "moe_probe_read", "moe_probe_copy")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} ({status})")
+        self.status = status
+
+
+class moe_qffn(C.Structure):
+    _fields_ = [("gate_q", C.c_void_p), ("up_q", C.c_void_p), ("down_q", C.c_void_p),
+                ("gate_s", C.c_void_p), ("gate_b", C.c_void_p), ("up_s", C.c_void_p),
+                ("up_b", C.c_void_p), ("down_s", C.c_void_p), ("down_b", C.c_void_p)]
+
+
+class moe_layer(C.Structure):
+    _fields_ = [("w_router", C.c_void_p), ("router_bias", C.c_void_p),
+                ("w_shared_gate", C.c_void_p), ("routed", moe_qffn), ("shared", moe_qffn)]
+
+
+class moe_options(C.Structure):
+    _fields_ = [("path", C.c_int), ("residual_out", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(or python gemv_router_softmax_amd/build.py)")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, sz = C.c_void_p, C.c_int, C.c_size_t
+    L.moe_workspace_bytes.argtypes = [i32]
+    L.moe_workspace_bytes.restype = sz
+    L.moe_status_string.argtypes = [i32]
+    L.moe_status_string.restype = C.c_char_p
+    L.moe_route.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_permute.argtypes = [vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_ffn.argtypes = [vp, i32, C.POINTER(moe_qffn), C.POINTER(moe_qffn), vp, vp, vp,
+                                 vp, sz, vp, C.POINTER(moe_options)]
+    L.moe_combine.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+    L.moe_layer_forward.argtypes = [vp, i32, C.POINTER(moe_layer), vp, vp, sz, vp]
+    L.moe_layer_forward_ex.argtypes = [vp, i32, C.POINTER(moe_layer), vp, vp, sz, vp,
+                                       C.POINTER(moe_options)]
+    L.moe_probe_read.argtypes = [vp, sz, vp, vp]
+    L.moe_probe_copy.argtypes = [vp, vp, sz, vp]
+    for fn in EXPORTS[2:]:
+        getattr(L, fn).restype = i32
+    _lib = L
+    return L
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_workspace_bytes(T: int) -> int:
+    return int(lib().moe_workspace_bytes(T))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoeError(fn, status, moe_status_string(status))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_U16 = (torch.int16, torch.bfloat16, torch.float16, torch.uint16)
+_U32 = (torch.int32, torch.uint32)
+
+
+class DeviceQFFN:
+    """A quantised expert stack resident in device memory."""
+
+    def __init__(self, q, n: int, device="cuda"):
+        H, I, G = MOE_HIDDEN, MOE_INTER, MOE_GROUP
+
+        def up(a, shape, dt):
+            a = np.ascontiguousarray(a)
+            assert a.shape == shape, (a.shape, shape)
+            return torch.from_numpy(a.view(dt)).to(device)
+
+        self.tensors = {
+            "gate_q": up(q.gate_q, (n, I, H // 8), np.int32),
+            "up_q": up(q.up_q, (n, I, H // 8), np.int32),
+            "down_q": up(q.down_q, (n, H, I // 8), np.int32),
+            "gate_s": up(q.gate_s, (n, I, H // G), np.int16),
+            "gate_b": up(q.gate_b, (n, I, H // G), np.int16),
+            "up_s": up(q.up_s, (n, I, H // G), np.int16),
+            "up_b": up(q.up_b, (n, I, H // G), np.int16),
+            "down_s": up(q.down_s, (n, H, I // G), np.int16),
+            "down_b": up(q.down_b, (n, H, I // G), np.int16),
+        }
+        self.c = moe_qffn(**{k: v.data_ptr() for k, v in self.tensors.items()})
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.tensors.values())
+
+
+class DeviceLayer:
+    """One MoE layer resident in device memory, with its C descriptor."""
+
+    def __init__(self, layer, device="cuda"):
+        assert (layer.dims.E, layer.dims.topk, layer.dims.H, layer.dims.I, layer.dims.G) == (
+            MOE_EXPERTS, MOE_TOPK, MOE_HIDDEN, MOE_INTER, MOE_GROUP), "production shape only"
+        self.w_router = torch.from_numpy(np.ascontiguousarray(layer.w_router).view(np.int16)).to(device)
+        self.w_shared_gate = torch.from_numpy(
+            np.ascontiguousarray(layer.w_shared_gate).view(np.int16)).to(device)
+        self.router_bias = (None if layer.router_bias is None else
+                            torch.from_numpy(np.ascontiguousarray(layer.router_bias, np.float32)).to(device))
+        self.routed = DeviceQFFN(layer.routed, MOE_EXPERTS, device)
+        self.shared = DeviceQFFN(layer.shared, 1, device)
+        assert tuple(self.w_router.shape) == (MOE_EXPERTS, MOE_HIDDEN)
+        assert tuple(self.w_shared_gate.shape) == (MOE_HIDDEN,)
+        self.c = moe_layer(self.w_router.data_ptr(),
+                           None if self.router_bias is None else self.router_bias.data_ptr(),
+                           self.w_shared_gate.data_ptr(), self.routed.c, self.shared.c)
+
+    @property
+    def nbytes(self) -> int:
+        return (self.routed.nbytes + self.shared.nbytes + self.w_router.numel() * 2 +
+                self.w_shared_gate.numel() * 2)
+
+
+def workspace(T: int, device="cuda") -> torch.Tensor:
+    """Device workspace sized by moe_workspace_bytes(T) (allocated by torch)."""
+    return torch.empty(max(moe_workspace_bytes(T), 256), dtype=torch.uint8, device=device)
+
+
+def _ws(ws: torch.Tensor):
+    return _ptr(ws, "ws", torch.uint8), ws.numel()
+
+
+def moe_route(x, w_router, router_bias, w_shared_gate, topk_ids, topk_w, shared_gate, ws,
+              stream=None) -> None:
+    T = x.shape[0]
+    wsp, wsn = _ws(ws)
+    _check("moe_route", lib().moe_route(
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T,
+        _ptr(w_router, "w_router", _U16, (MOE_EXPERTS, MOE_HIDDEN)),
+        _ptr(router_bias, "router_bias", torch.float32, (MOE_EXPERTS,)),
+        _ptr(w_shared_gate, "w_shared_gate", _U16, (MOE_HIDDEN,)),
+        _ptr(topk_ids, "topk_ids", torch.int32, (T, MOE_TOPK)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, MOE_TOPK)),
+        _ptr(shared_gate, "shared_gate", torch.float32, (T,)), wsp, wsn, _stream(stream)))
+
+
+def moe_permute(topk_ids, expert_counts, expert_offsets, perm, inv_perm, ws, stream=None) -> None:
+    T = topk_ids.shape[0]
+    wsp, wsn = _ws(ws)
+    _check("moe_permute", lib().moe_permute(
+        _ptr(topk_ids, "topk_ids", torch.int32, (T, MOE_TOPK)), T,
+        _ptr(expert_counts, "expert_counts", torch.int32, (MOE_EXPERTS,)),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, (MOE_EXPERTS + 1,)),
+        _ptr(perm, "perm", torch.int32, (T * MOE_TOPK,)),
+        _ptr(inv_perm, "inv_perm", torch.int32, (T * MOE_TOPK,)), wsp, wsn, _stream(stream)))
+
+
+def moe_expert_ffn(x, layer: DeviceLayer, expert_offsets, perm, expert_out, ws,
+                   path: int = MOE_PATH_AUTO, stream=None) -> None:
+    T = x.shape[0]
+    wsp, wsn = _ws(ws)
+    opt = moe_options(path, None)
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.routed.c), C.byref(layer.shared.c),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, (MOE_EXPERTS + 1,)),
+        _ptr(perm, "perm", torch.int32, (T * MOE_TOPK,)),
+        _ptr(expert_out, "expert_out", torch.float32, ((MOE_TOPK + 1) * T, MOE_HIDDEN)),
+        wsp, wsn, _stream(stream), C.byref(opt)))
+
+
+def moe_combine(expert_out, inv_perm, topk_w, shared_gate, y, stream=None) -> None:
+    T = y.shape[0]
+    _check("moe_combine", lib().moe_combine(
+        _ptr(expert_out, "expert_out", torch.float32, ((MOE_TOPK + 1) * T, MOE_HIDDEN)),
+        _ptr(inv_perm, "inv_perm", torch.int32, (T * MOE_TOPK,)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, MOE_TOPK)),
+        _ptr(shared_gate, "shared_gate", torch.float32, (T,)), T,
+        _ptr(y, "y", _U16, (T, MOE_HIDDEN)), _stream(stream)))
+
+
+def moe_layer_forward_ex(x, layer: DeviceLayer, y, ws, path: int = MOE_PATH_AUTO,
+                         residual_out=None, stream=None) -> None:
+    T = x.shape[0]
+    wsp, wsn = _ws(ws)
+    opt = moe_options(path, _ptr(residual_out, "residual_out", _U16, (T, MOE_HIDDEN)))
+    _check("moe_layer_forward_ex", lib().moe_layer_forward_ex(
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.c),
+        _ptr(y, "y", _U16, (T, MOE_HIDDEN)), wsp, wsn, _stream(stream), C.byref(opt)))
+
+
+def moe_layer_forward(x, layer: DeviceLayer, y, ws, stream=None) -> None:
+    T = x.shape[0]
+    wsp, wsn = _ws(ws)
+    _check("moe_layer_forward", lib().moe_layer_forward(
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.c),
+        _ptr(y, "y", _U16, (T, MOE_HIDDEN)), wsp, wsn, _stream(stream)))
+
+
+def moe_probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    _check("moe_probe_read", lib().moe_probe_read(
+        _ptr(src, "src"), n, _ptr(sink, "sink", torch.float32), _stream(stream)))
+
+
+def moe_probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= n
+    _check("moe_probe_copy", lib().moe_probe_copy(
+        _ptr(dst, "dst"), _ptr(src, "src"), n, _stream(stream)))
+
+
+def to_device_bits(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """bf16/fp16 bit patterns (uint16 numpy) -> int16 device tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+
+def bits_to_numpy(t: torch.Tensor) -> np.ndarray:
+    """int16/bf16 device tensor -> uint16 bit patterns on the host."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)

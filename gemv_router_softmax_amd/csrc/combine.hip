@@ -1,0 +1,92 @@
+// combine.hip -- weighted un-permute plus the shared expert, and the
+// read/copy probes used to measure the sustained HBM rate.
+#include "common.hpp"
+
+namespace moe {
+
+// y[t] = bf16( sum_j w[t][j] out[inv[8t+j]] + sg[t] out[8T+t] ); optionally
+// res[t] = bf16( x[t] + y[t] ).  One thread per 4 columns; grid (T, H/1024).
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ wts,
+                                                      const float* __restrict__ sg, int T,
+                                                      uint16_t* __restrict__ y,
+                                                      const uint16_t* __restrict__ x,
+                                                      uint16_t* __restrict__ res) {
+    const int t = blockIdx.x;
+    const int m = (blockIdx.y * 256 + threadIdx.x) * 4;
+    float4v acc = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < TOPK; ++j) {
+        const int p = inv[(size_t)t * TOPK + j];
+        if (p < 0 || p >= TOPK * T) continue;
+        const float w = wts[(size_t)t * TOPK + j];
+        const float4v d = *reinterpret_cast<const float4v*>(out + (size_t)p * H + m);
+        acc += w * d;
+    }
+    {
+        const float4v d = *reinterpret_cast<const float4v*>(out + ((size_t)TOPK * T + t) * H + m);
+        acc += sg[t] * d;
+    }
+    uint32_t yb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yb[i] = f32_to_bf16(acc[i]);
+    uint2 yv;
+    yv.x = yb[0] | (yb[1] << 16);
+    yv.y = yb[2] | (yb[3] << 16);
+    *reinterpret_cast<uint2*>(y + (size_t)t * H + m) = yv;
+    if (res) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * H + m);
+        const uint32_t xs[4] = {xv.x & 0xFFFFu, xv.x >> 16, xv.y & 0xFFFFu, xv.y >> 16};
+        uint32_t rb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rb[i] = f32_to_bf16(bf16_to_f32(xs[i]) + bf16_to_f32(yb[i]));
+        uint2 rv;
+        rv.x = rb[0] | (rb[1] << 16);
+        rv.y = rb[2] | (rb[3] << 16);
+        *reinterpret_cast<uint2*>(res + (size_t)t * H + m) = rv;
+    }
+}
+
+void launch_combine(const float* out, const int32_t* inv, const float* wts, const float* sg, int T,
+                    uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st) {
+    hipLaunchKernelGGL(combine_kernel, dim3(T, H / 1024), dim3(256), 0, st, out, inv, wts, sg, T,
+                       y, x, res);
+}
+
+// ------------------------------------------------------------------ probes
+
+constexpr int PROBE_BLOCKS = 4096;
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const uint4v* __restrict__ src,
+                                                         size_t n16, float* __restrict__ sink) {
+    uint32_t acc = 0;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * 256) {
+        const uint4v v = __builtin_nontemporal_load(src + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    // a data-dependent (practically never taken) store keeps the loads alive
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = (float)threadIdx.x;
+}
+
+__global__ __launch_bounds__(256) void probe_copy_kernel(uint4v* __restrict__ dst,
+                                                         const uint4v* __restrict__ src,
+                                                         size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * 256)
+        dst[i] = src[i];
+}
+
+void launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t st) {
+    hipLaunchKernelGGL(probe_read_kernel, dim3(PROBE_BLOCKS), dim3(256), 0, st,
+                       reinterpret_cast<const uint4v*>(src), bytes / 16, sink);
+}
+
+void launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {
+    hipLaunchKernelGGL(probe_copy_kernel, dim3(PROBE_BLOCKS), dim3(256), 0, st,
+                       reinterpret_cast<uint4v*>(dst), reinterpret_cast<const uint4v*>(src),
+                       bytes / 16);
+}
+
+}  // namespace moe

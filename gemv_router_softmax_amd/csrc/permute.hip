@@ -1,0 +1,241 @@
+// permute.hip -- token -> expert permutation (stable counting sort) and the
+// row-tile list of the grouped expert kernels.
+//
+// The permutation is a pure integer function of the expert ids, so it is
+// computed bit-exactly: a histogram, an exclusive scan and a stable scatter
+// whose in-block ranks come from wave ballots (no order-dependent atomics
+// decide a position).  Each expert's segment lists its slots f = 8t + j in
+// ascending order.
+//
+//   perm_small      one workgroup does everything (8T <= SMALL_MAX entries)
+//   perm_count      large T: per-chunk expert histograms       (grid: chunks)
+//   perm_scan       large T: column scans -> per-chunk bases   (one workgroup)
+//   perm_scatter    large T: stable scatter of every chunk     (grid: chunks)
+//   plan_tiles      row tiles of <= MT_ROWS rows per expert (expert 256 is the
+//                   shared expert over all T tokens), read by the expert
+//                   kernels from device memory so the host never needs the
+//                   expert counts.
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int PERM_CHUNK = 4096;   // entries per chunk in the large path
+constexpr int SMALL_MAX = 4096;    // entries handled by perm_small
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & 63;
+    return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// Exclusive scan of one int per thread over a 256-thread block.
+__device__ int block_excl_scan256(int v, int* lds /* >= 4 ints */, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int n = __shfl_up(inc, o, WAVE);
+        if (lane >= o) inc += n;
+    }
+    if (lane == 63) lds[wave] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        int s = lds[w];
+        if (w < wave) base += s;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + inc - v;
+}
+
+// Stable scatter of entries [f0, f1).  base[e] (LDS) is the next sorted
+// position of expert e and advances as entries are placed; wcnt (LDS,
+// 4*256 ints) must be zero on entry and is zero on exit.
+__device__ void stable_scatter(const int32_t* __restrict__ ids, int f0, int f1, int* base,
+                               int* wcnt, int32_t* __restrict__ perm,
+                               int32_t* __restrict__ inv) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    for (int c0 = f0; c0 < f1; c0 += 256) {
+        const int f = c0 + tid;
+        const bool valid = f < f1;
+        const int e = valid ? ids[f] : -1;
+        const bool ok = valid && e >= 0 && e < E;
+        if (valid && !ok) inv[f] = -1;
+        const int key = ok ? e : 511;
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 9; ++b) {
+            uint64_t m = __ballot((key >> b) & 1);
+            peers &= ((key >> b) & 1) ? m : ~m;
+        }
+        const uint64_t below = peers & lanemask_lt();
+        const int rank = __popcll(below);
+        if (ok && below == 0) wcnt[wave * 256 + e] = __popcll(peers);
+        __syncthreads();
+        if (ok) {
+            int pre = 0;
+            for (int w = 0; w < wave; ++w) pre += wcnt[w * 256 + e];
+            const int pos = base[e] + pre + rank;
+            perm[pos] = f;
+            inv[f] = pos;
+        }
+        __syncthreads();
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            s += wcnt[w * 256 + tid];
+            wcnt[w * 256 + tid] = 0;
+        }
+        base[tid] += s;
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ ids, int n,
+                                                  int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm,
+                                                  int32_t* __restrict__ inv) {
+    __shared__ int hist[256];
+    __shared__ int base[256];
+    __shared__ int wcnt[4 * 256];
+    __shared__ int scr[4];
+    const int tid = threadIdx.x;
+    hist[tid] = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
+    __syncthreads();
+    for (int f = tid; f < n; f += 256) {
+        int e = ids[f];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    const int c = hist[tid];
+    int total;
+    const int off = block_excl_scan256(c, scr, &total);
+    counts[tid] = c;
+    offsets[tid] = off;
+    if (tid == 0) offsets[E] = total;
+    base[tid] = off;
+    __syncthreads();
+    stable_scatter(ids, 0, n, base, wcnt, perm, inv);
+}
+
+__global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int n,
+                                                  int32_t* __restrict__ chunk_counts) {
+    __shared__ int hist[256];
+    const int tid = threadIdx.x;
+    hist[tid] = 0;
+    __syncthreads();
+    const int f0 = blockIdx.x * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
+    for (int f = f0 + tid; f < f1; f += 256) {
+        int e = ids[f];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    chunk_counts[(size_t)blockIdx.x * 256 + tid] = hist[tid];
+}
+
+// One workgroup: chunk_counts[b][e] becomes the absolute first position of
+// chunk b's entries of expert e.
+__global__ __launch_bounds__(256) void perm_scan(int nchunks, int32_t* __restrict__ chunk_counts,
+                                                 int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets) {
+    __shared__ int scr[4];
+    const int tid = threadIdx.x;
+    int run = 0;
+    for (int b = 0; b < nchunks; ++b) {
+        int c = chunk_counts[(size_t)b * 256 + tid];
+        chunk_counts[(size_t)b * 256 + tid] = run;
+        run += c;
+    }
+    int total;
+    const int off = block_excl_scan256(run, scr, &total);
+    counts[tid] = run;
+    offsets[tid] = off;
+    if (tid == 0) offsets[E] = total;
+    for (int b = 0; b < nchunks; ++b) chunk_counts[(size_t)b * 256 + tid] += off;
+}
+
+__global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ ids, int n,
+                                                    const int32_t* __restrict__ chunk_base,
+                                                    int32_t* __restrict__ perm,
+                                                    int32_t* __restrict__ inv) {
+    __shared__ int base[256];
+    __shared__ int wcnt[4 * 256];
+    const int tid = threadIdx.x;
+    base[tid] = chunk_base[(size_t)blockIdx.x * 256 + tid];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
+    __syncthreads();
+    const int f0 = blockIdx.x * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
+    stable_scatter(ids, f0, f1, base, wcnt, perm, inv);
+}
+
+// Row tiles: routed expert e owns rows offsets[e] .. offsets[e+1]-1, the
+// shared expert (group 256) owns rows 8T .. 9T-1.  Each group is cut into
+// ceil(n/MT_ROWS) tiles.  At most `cap` tiles are written (offsets from
+// moe_permute never need more than max_tiles(T); malformed caller offsets
+// cannot overrun the tile buffer).
+__global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ offsets, int T,
+                                                  int cap, Tile* __restrict__ tiles,
+                                                  int* __restrict__ tile_count) {
+    __shared__ int scr[4];
+    const int tid = threadIdx.x;
+    // clamp caller-provided offsets into the routed row space [0, 8T)
+    const int lim = TOPK * T;
+    const int r0 = min(max(offsets[tid], 0), lim);
+    const int r1 = min(max(offsets[tid + 1], r0), lim);
+    const int n = r1 - r0;
+    const int nt = (n + MT_ROWS - 1) / MT_ROWS;
+    int total;
+    const int tb = block_excl_scan256(nt, scr, &total);
+    for (int i = 0; i < nt; ++i) {
+        Tile tl;
+        tl.group = tid;
+        tl.row0 = r0 + i * MT_ROWS;
+        tl.nrows = min(MT_ROWS, n - i * MT_ROWS);
+        tl.pad = 0;
+        if (tb + i < cap) tiles[tb + i] = tl;
+    }
+    const int ns = (T + MT_ROWS - 1) / MT_ROWS;
+    for (int i = tid; i < ns; i += 256) {
+        Tile tl;
+        tl.group = E;
+        tl.row0 = TOPK * T + i * MT_ROWS;
+        tl.nrows = min(MT_ROWS, T - i * MT_ROWS);
+        tl.pad = 0;
+        if (total + i < cap) tiles[total + i] = tl;
+    }
+    if (tid == 0) *tile_count = min(total + ns, cap);
+}
+
+int perm_chunks(int T) { return (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK; }
+
+int max_tiles(int T) {
+    const int n = TOPK * T;
+    return n / MT_ROWS + (n < E ? n : E) + (T + MT_ROWS - 1) / MT_ROWS;
+}
+
+void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
+                    int32_t* inv, int32_t* chunk_counts, hipStream_t st) {
+    const int n = TOPK * T;
+    if (n <= SMALL_MAX) {
+        hipLaunchKernelGGL(perm_small, dim3(1), dim3(256), 0, st, ids, n, counts, offsets, perm,
+                           inv);
+        return;
+    }
+    const int nb = perm_chunks(T);
+    hipLaunchKernelGGL(perm_count, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts);
+    hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, st, nb, chunk_counts, counts, offsets);
+    hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts, perm, inv);
+}
+
+void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st) {
+    hipLaunchKernelGGL(plan_tiles, dim3(1), dim3(256), 0, st, offsets, T, max_tiles(T), tiles,
+                       tile_count);
+}
+
+}  // namespace moe

@@ -117,6 +117,7 @@ class Oracle:
         self.lib = L
         vp, i32, i64 = C.c_void_p, C.c_int, C.c_int64
         L.oracle_mutant.restype = i32
+        L.oracle_threads.restype = i32
         L.oracle_bf16_to_double.argtypes = [C.c_uint16]
         L.oracle_bf16_to_double.restype = C.c_double
         L.oracle_fp16_to_double.argtypes = [C.c_uint16]
@@ -141,6 +142,9 @@ class Oracle:
                                            vp, vp, vp, vp]
         L.oracle_layer_forward.restype = i32
         self.mutant = L.oracle_mutant()
+
+    def threads(self) -> int:
+        return int(self.lib.oracle_threads())
 
     # ---- formats
     def round_bf16(self, a) -> np.ndarray:

@@ -36,6 +36,7 @@
  * build (ORACLE_MUTANT undefined) is the oracle.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -60,6 +61,9 @@ typedef struct {
 } oracle_qffn;
 
 int oracle_mutant(void) { return ORACLE_MUTANT; }
+
+/* Threads the OpenMP loops use (reported with the CPU baseline). */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- formats */
 

@@ -1,0 +1,157 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol the header declares, sizes its workspace monotonically and rejects
+bad arguments on the host (returning before anything is enqueued).
+
+Every call below is built to FAIL validation (or be a T == 0 no-op): the
+fake addresses are never handed to a kernel, so these tests are safe on a
+machine with a GPU too."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import gemv_router_softmax_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, ALIGN, WS = 0, 1, 2, 3
+A = 0x100000          # fake, 16-byte aligned "device" address (never dereferenced)
+MIS = 0x100004        # fake misaligned address
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(moe_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared()
+    assert len(names) == 10, names
+    assert sorted(moe.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    for name in ("MOE_HIDDEN", "MOE_INTER", "MOE_EXPERTS", "MOE_TOPK", "MOE_GROUP", "MOE_T_MAX",
+                 "MOE_DECODE_T", "MOE_DECODE_T_MAX"):
+        m = re.search(rf"#define {name} (\d+)", src)
+        assert int(m.group(1)) == getattr(moe, name), name
+
+
+def test_workspace_bytes(L):
+    assert moe.moe_workspace_bytes(-1) == 0
+    assert moe.moe_workspace_bytes(moe.MOE_T_MAX + 1) == 0
+    prev = 0
+    for T in [0, 1, 2, 7, 8, 9, 16, 63, 64, 512, 4095, 4096, 4097, 16384, 65536]:
+        b = moe.moe_workspace_bytes(T)
+        assert b >= prev and b % 256 == 0
+        prev = b
+    # the split outputs fit: [9T][2048] fp32 scratch is part of it
+    assert moe.moe_workspace_bytes(4096) >= 9 * 4096 * 2048 * 4
+
+
+def test_status_strings():
+    assert moe.moe_status_string(0) == "MOE_OK"
+    assert moe.moe_status_string(3) == "MOE_ERR_WORKSPACE"
+    assert moe.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def _qffn(p=A):
+    return moe.moe_qffn(*([p] * 9))
+
+
+def _layer(p=A):
+    return moe.moe_layer(p, None, p, _qffn(p), _qffn(p))
+
+
+def test_route_validation(L):
+    big = moe.moe_workspace_bytes(4)
+    f = L.moe_route
+    assert f(A, -1, A, None, A, A, A, A, A, big, None) == INVALID
+    assert f(A, moe.MOE_T_MAX + 1, A, None, A, A, A, A, A, big, None) == INVALID
+    assert f(None, 0, None, None, None, None, None, None, None, 0, None) == OK
+    assert f(None, 4, A, None, A, A, A, A, A, big, None) == INVALID
+    assert f(A, 4, A, None, None, A, A, A, A, big, None) == INVALID
+    assert f(MIS, 4, A, None, A, A, A, A, A, big, None) == ALIGN
+    assert f(A, 4, A, MIS + 1, A, A, A, A, A, big, None) == ALIGN
+    assert f(A, 4, A, None, A, A, A, A, A, big - 1, None) == WS
+
+
+def test_permute_validation(L):
+    big = moe.moe_workspace_bytes(100)
+    f = L.moe_permute
+    assert f(A, 0, None, None, None, None, None, 0, None) == OK
+    assert f(A, 100, A, None, A, A, A, big, None) == INVALID
+    assert f(A, 100, A, A, A, A + 2, A, big, None) == ALIGN
+    assert f(A, 100, A, A, A, A, A, 16, None) == WS
+
+
+def test_expert_ffn_validation(L):
+    big = moe.moe_workspace_bytes(16)
+    f = L.moe_expert_ffn
+    q = _qffn()
+    assert f(A, 16, None, C.byref(q), A, A, A, A, big, None, None) == INVALID
+    bad = _qffn()
+    bad.down_b = None
+    assert f(A, 16, C.byref(bad), C.byref(q), A, A, A, A, big, None, None) == INVALID
+    mis = _qffn()
+    mis.up_s = MIS
+    assert f(A, 16, C.byref(q), C.byref(mis), A, A, A, A, big, None, None) == ALIGN
+    assert f(A, 16, C.byref(q), C.byref(q), A, A, A, A, big - 256, None, None) == WS
+    # forcing the decode path above its limit, or an unknown path
+    opt = moe.moe_options(moe.MOE_PATH_DECODE, None)
+    assert f(A, moe.MOE_DECODE_T_MAX + 1, C.byref(q), C.byref(q), A, A, A, A, 1 << 40, None,
+             C.byref(opt)) == INVALID
+    opt = moe.moe_options(7, None)
+    assert f(A, 16, C.byref(q), C.byref(q), A, A, A, A, big, None, C.byref(opt)) == INVALID
+
+
+def test_combine_validation(L):
+    f = L.moe_combine
+    assert f(None, None, None, None, 0, None, None) == OK
+    assert f(A, A, A, None, 3, A, None) == INVALID
+    assert f(A, A, A, A, 3, MIS, None) == ALIGN
+
+
+def test_layer_forward_validation(L):
+    big = moe.moe_workspace_bytes(64)
+    f = L.moe_layer_forward_ex
+    lay = _layer()
+    assert f(A, 0, None, None, None, 0, None, None) == OK
+    assert f(A, 64, None, A, A, big, None, None) == INVALID
+    assert f(A, -3, C.byref(lay), A, A, big, None, None) == INVALID
+    assert f(A, 64, C.byref(lay), A, A, big - 1, None, None) == WS
+    assert f(A, 64, C.byref(lay), MIS, A, big, None, None) == ALIGN
+    opt = moe.moe_options(moe.MOE_PATH_PREFILL, MIS)
+    assert f(A, 64, C.byref(lay), A, A, big, None, C.byref(opt)) == ALIGN
+    lb = _layer()
+    lb.router_bias = A + 2
+    assert f(A, 64, C.byref(lb), A, A, big, None, None) == ALIGN
+    lz = _layer()
+    lz.w_router = None
+    assert L.moe_layer_forward(A, 64, C.byref(lz), A, A, big, None) == INVALID
+
+
+def test_probe_validation(L):
+    assert L.moe_probe_read(A, 0, A, None) == INVALID
+    assert L.moe_probe_read(A, 17, A, None) == INVALID
+    assert L.moe_probe_copy(A, MIS, 32, None) == ALIGN
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "gemv_router_softmax_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), fn
+                assert "moe_oracle" not in src and "libmoe_oracle" not in src, fn

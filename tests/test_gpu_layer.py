@@ -1,0 +1,83 @@
+"""moe_layer_forward (whole layer, one stream, no host sync) vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gemv_router_softmax_amd as moe
+from gemv_router_softmax_amd import synth
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+AUTO, DEC, PRE = moe.MOE_PATH_AUTO, moe.MOE_PATH_DECODE, moe.MOE_PATH_PREFILL
+
+
+def gpu_layer(x, D, path=AUTO, residual=False):
+    T = x.shape[0]
+    xd = moe.to_device_bits(x)
+    y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    res = torch.empty_like(y) if residual else None
+    moe.moe_layer_forward_ex(xd, D, y, moe.workspace(T), path=path, residual_out=res)
+    torch.cuda.synchronize()
+    return moe.bits_to_numpy(y), (moe.bits_to_numpy(res) if residual else None), xd
+
+
+def check_layer(T, path, seed=0, skewed=False, sample=None):
+    P.say(f"layer T={T} path={path} seed={seed} skewed={skewed}")
+    L, D = P.host_layer(0, 0, skewed), P.dev_layer(0, 0, skewed)
+    x = synth.make_x(T, seed=seed) if seed == 0 else synth.make_x(T, seed=seed, layer=T)
+    y, _, xd = gpu_layer(x, D, path)
+    ids, _, _ = P.gpu_route(xd, D)
+    rows = np.arange(T) if sample is None else sample
+    ref, diff = P.oracle_layer_substituted(L, np.ascontiguousarray(x[rows]), ids[rows])
+    P.assert_close(P.bf16_f64(y[rows]), P.bf16_f64(ref.y), f"y T={T} path={path}")
+    return y
+
+
+def test_config0_t16_decode(gpu):
+    check_layer(16, DEC)
+
+
+def test_config0_t16_prefill(gpu):
+    check_layer(16, PRE)
+
+
+@pytest.mark.parametrize("T", [1, 2, 8])
+def test_decode_auto(gpu, T):
+    check_layer(T, AUTO, seed=3)
+
+
+@pytest.mark.parametrize("T", [9, 64, 100, 512])
+def test_prefill_auto(gpu, T):
+    check_layer(T, AUTO, seed=4)
+
+
+@pytest.mark.parametrize("skewed", [False, True])
+def test_full_size_t4096_sampled(gpu, skewed):
+    rng = np.random.default_rng(1)
+    check_layer(4096, AUTO, seed=5, skewed=skewed, sample=np.sort(rng.choice(4096, 48, replace=False)))
+
+
+def test_residual_output(gpu):
+    D = P.dev_layer(0, 0)
+    x = synth.make_x(8, seed=6)
+    y, res, _ = gpu_layer(x, D, residual=True)
+    want = P.orc().round_bf16(P.bf16_f64(x) + P.bf16_f64(y))
+    assert np.array_equal(res, want)
+
+
+def test_layer_deterministic(gpu):
+    D = P.dev_layer(0, 0)
+    for T in (1, 700):
+        x = synth.make_x(T, seed=7)
+        a = gpu_layer(x, D)[0]
+        b = gpu_layer(x, D)[0]
+        assert np.array_equal(a, b)
+
+
+def test_t0_is_noop(gpu):
+    D = P.dev_layer(0, 0)
+    x = torch.zeros((0, 2048), dtype=torch.int16, device="cuda")
+    y = torch.zeros((0, 2048), dtype=torch.int16, device="cuda")
+    moe.moe_layer_forward(x, D, y, moe.workspace(0))
+    torch.cuda.synchronize()
