@@ -61,9 +61,12 @@ def test_paths_agree_at_16(gpu):
 
 
 @pytest.mark.parametrize("T", [1, 5, 16, 300])
-def test_combine_one_ulp(gpu, T):
-    """Identical fp32 inputs: the GPU's bf16 output is within one bf16 ulp of
-    the oracle's (which sums the same values in float64)."""
+def test_combine_within_rounding(gpu, T):
+    """Identical fp32 inputs.  The GPU sums nine fp32 products in fp32, the
+    oracle in float64; each GPU output must be the bf16 rounding of a value
+    within the fp32 summation bound (16 * 2^-24 * sum |terms|) of the exact
+    sum, i.e. |y_gpu - y_exact| <= bound + half a bf16 ulp; away from
+    cancellation that is at most one bf16 ulp."""
     P.say(f"combine T={T}")
     rng = np.random.default_rng(T)
     ids = np.argsort(rng.random((T, 256)), axis=1)[:, :8].astype(np.int32)
@@ -77,10 +80,15 @@ def test_combine_one_ulp(gpu, T):
                     torch.from_numpy(w).cuda(), torch.from_numpy(sg).cuda(), y)
     torch.cuda.synchronize()
     got = moe.bits_to_numpy(y)
-    ref, _ = P.orc().combine(synth.PROD, out.astype(np.float64), pm.inv, w.astype(np.float64),
-                             sg.astype(np.float64))
-    d = np.abs(got.astype(np.int32) - ref.astype(np.int32))
-    same_sign = (got >> 15) == (ref >> 15)
-    assert np.all(same_sign | (P.bf16_f64(got) == 0) | (P.bf16_f64(ref) == 0))
-    assert d.max() <= 1, f"combine off by {d.max()} bf16 ulps"
-    P.say(f"  combine T={T}: ulp flips={int((d == 1).sum())} of {d.size}")
+    o64 = out.astype(np.float64)
+    ref, y32 = P.orc().combine(synth.PROD, o64, pm.inv, w.astype(np.float64),
+                               sg.astype(np.float64))
+    terms = np.abs(w.astype(np.float64)[:, :, None] * o64[pm.inv.reshape(T, 8)]).sum(1)
+    terms += np.abs(sg.astype(np.float64)[:, None] * o64[8 * T:])
+    bound = 16 * 2.0 ** -24 * terms
+    g = P.bf16_f64(got)
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(g), np.abs(y32)) + 1e-300)) - 8)
+    assert np.all(np.abs(g - y32) <= bound + half_ulp), "combine outside the rounding bound"
+    same = np.mean(got == ref)
+    P.say(f"  combine T={T}: identical to the oracle's bf16 on {same:.5f} of outputs")
+    assert same > 0.999
