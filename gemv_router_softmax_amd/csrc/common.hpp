@@ -48,6 +48,44 @@ __device__ __forceinline__ float fp16_to_f32(uint16_t bits) {
     return (float)__builtin_bit_cast(_Float16, bits);
 }
 
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Exact-code dot products for the decode GEMVs.  A code word holds eight
+// 4-bit codes q0..q7 (q_k in bits 4k..4k+3).  ((w >> 4i) & 0x000F000F) |
+// 0x43004300 is the bf16 pair (128 + q_i, 128 + q_{i+4}) -- exact, since bf16
+// spacing at 128 is 1 -- so v_dot2_f32_bf16 against the activation pair
+// (a_i, a_{i+4}) accumulates sum_k a_k (128 + q_k).  With sa = sum_k a_k the
+// group's contribution is  s * (dot - 128 sa) + b * sa = s * dot + (b - 128 s) sa.
+__device__ __forceinline__ float dot8_codes(uint32_t w, uint4v apairs, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t p = ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, p),
+                                              __builtin_bit_cast(bf16x2v, apairs[i]), acc, false);
+    }
+    return acc;
+}
+
+// Sum of the eight bf16 activations of a pair vector.
+__device__ __forceinline__ float sum8_bf16(uint4v apairs, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, 0x3F803F80u),
+                                              __builtin_bit_cast(bf16x2v, apairs[i]), acc, false);
+    return acc;
+}
+
+// Eight natural-order bf16 values (a0,a1),(a2,a3),(a4,a5),(a6,a7) -> the
+// code-pair order (a0,a4),(a1,a5),(a2,a6),(a3,a7).
+__device__ __forceinline__ uint4v pair_i_i4(uint4v v) {
+    uint4v r;
+    r[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+    r[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+    r[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+    return r;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);

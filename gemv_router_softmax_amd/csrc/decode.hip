@@ -1,0 +1,289 @@
+// decode.hip -- the few-token (decode) path of the MoE layer.
+//
+// Decode is memory bound (leslieli.dev note on the Lily engine, paragraph 5:
+// the sparse GEMV barely changes when its arithmetic is removed) and, at one
+// token, dominated by latency, so the layer runs as four kernels with no
+// host involvement:
+//
+//   route_logits_gemv   (route.hip) logits of the 256 experts
+//   route_select        ONE workgroup: top-8 per token by radix selection on
+//                       the fp32 logits (ties to the lower expert index),
+//                       renormalised softmax weights, the shared-expert gate,
+//                       the stable permutation and the row-tile list
+//   decode_gateup       16 gate rows + 16 up rows of one active expert per
+//                       workgroup; every lane streams 16 B of each row
+//                       (coalesced 128-bit loads, all issued up front) and
+//                       applies the group scale/bias once per lane on exact
+//                       codes; eight dot products are reduced together with a
+//                       transposing butterfly; h = bf16(silu(g) u)
+//   decode_down_combine 4 output rows per workgroup for ALL active experts:
+//                       down GEMV on exact codes, then the weighted combine
+//                       with the shared expert and the residual add, so the
+//                       expert outputs never go to memory
+//
+// Fusing the chain follows "A Rust + Metal Inference Engine for
+// Qwen3.6-35B-A3B on Apple Silicon", paragraph 5 (decode fuses kernel
+// chains).
+#include "block_util.hpp"
+
+namespace moe {
+
+// One workgroup (256 threads), T <= MOE_DECODE_T_MAX.  logits [T][256] from
+// route_logits_gemv; writes ids, weights, shared gate, counts, offsets,
+// perm, inv and the row tiles.
+__global__ __launch_bounds__(256) void route_select(const float* __restrict__ logits,
+                                                    const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ wsg, int T,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ wts,
+                                                    float* __restrict__ sg,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm,
+                                                    int32_t* __restrict__ inv,
+                                                    Tile* __restrict__ tiles,
+                                                    int* __restrict__ tile_count) {
+    __shared__ int ids_l[MOE_DECODE_T_MAX * TOPK];
+    __shared__ int hist[256];
+    __shared__ int base[256];
+    __shared__ int offs_l[257];
+    __shared__ int wcnt[4 * 256];
+    __shared__ int scr[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    hist[tid] = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
+    for (int t = wave; t < T; t += 4) {
+        wave_top8(logits + (size_t)t * E, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK,
+                  ids_l + t * TOPK);
+        const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
+        const uint4v* gr = reinterpret_cast<const uint4v*>(wsg) + lane * 4;
+        float z = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4v a = xr[c], b = gr[c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                z = fmaf(bf16_to_f32(a[i] & 0xFFFFu), bf16_to_f32(b[i] & 0xFFFFu), z);
+                z = fmaf(bf16_to_f32(a[i] >> 16), bf16_to_f32(b[i] >> 16), z);
+            }
+        }
+        z = wave_sum(z);
+        if (lane == 0) sg[t] = 1.f / (1.f + expf(-z));
+    }
+    __syncthreads();
+    const int n = TOPK * T;
+    for (int f = tid; f < n; f += 256) atomicAdd(&hist[ids_l[f]], 1);
+    __syncthreads();
+    const int c = hist[tid];
+    int total;
+    const int off = block_excl_scan256(c, scr, &total);
+    counts[tid] = c;
+    offsets[tid] = off;
+    offs_l[tid] = off;
+    if (tid == 0) { offsets[E] = total; offs_l[E] = total; }
+    base[tid] = off;
+    __syncthreads();
+    stable_scatter(ids_l, 0, n, base, wcnt, perm, inv);
+    // row tiles: one per active expert (T <= 32 rows each), then the shared expert
+    const int active = c > 0 ? 1 : 0;
+    int na;
+    const int slot = block_excl_scan256(active, scr, &na);
+    if (active) {
+        Tile tl;
+        tl.group = tid;
+        tl.row0 = off;
+        tl.nrows = c;
+        tl.pad = 0;
+        tiles[slot] = tl;
+    }
+    if (tid == 0) {
+        Tile tl;
+        tl.group = E;
+        tl.row0 = n;
+        tl.nrows = T;
+        tl.pad = 0;
+        tiles[na] = tl;
+        *tile_count = na + 1;
+    }
+}
+
+// grid (max tiles, I / 16); 4 waves x 4 rows (gate and up) each.  Lane l
+// covers K = 32l .. 32l+31 (one 16-byte code load per row, half of one
+// 64-wide group).  h is written as bf16 in chunk-slot order (k = 0,4,1,5,
+// 2,6,3,7 inside every 8-element chunk), the pair order dot8_codes uses.
+__global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict__ x, int T,
+                                                     const int32_t* __restrict__ perm,
+                                                     const Tile* __restrict__ tiles,
+                                                     const int* __restrict__ tile_count,
+                                                     moe_qffn routed, moe_qffn shared,
+                                                     uint16_t* __restrict__ hout) {
+    if ((int)blockIdx.x >= *tile_count) return;
+    const Tile tl = tiles[blockIdx.x];
+    const bool sh = tl.group >= E;
+    const int e = sh ? 0 : tl.group;
+    const moe_qffn q = sh ? shared : routed;
+    const int lane = threadIdx.x & 63;
+    const int n0 = blockIdx.y * 16 + (threadIdx.x >> 6) * 4;
+    // value index i < 4: gate row n0+i, i >= 4: up row n0+i-4
+    uint4v wq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const size_t row = (size_t)e * I + n0 + (i & 3);
+        const uint32_t* qb = i < 4 ? q.gate_q : q.up_q;
+        wq[i] = reinterpret_cast<const uint4v*>(qb + row * (H / 8))[lane];
+    }
+    float s[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const size_t row = (size_t)e * I + n0 + (i & 3);
+        const uint16_t* sb = i < 4 ? q.gate_s : q.up_s;
+        const uint16_t* bb = i < 4 ? q.gate_b : q.up_b;
+        s[i] = fp16_to_f32(sb[row * (H / G) + (lane >> 1)]);
+        b[i] = fmaf(-128.f, s[i], fp16_to_f32(bb[row * (H / G) + (lane >> 1)]));
+    }
+    for (int rr = 0; rr < tl.nrows; ++rr) {
+        const int p = tl.row0 + rr;
+        int t;
+        if (p < TOPK * T) t = min(max(perm[p] >> 3, 0), T - 1);
+        else t = p - TOPK * T;
+        const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
+        uint4v xp[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) xp[cc] = pair_i_i4(xr[cc]);
+        float sx = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) sx = sum8_bf16(xp[cc], sx);
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float d = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) d = dot8_codes(wq[i][cc], xp[cc], d);
+            acc[i] = fmaf(s[i], d, b[i] * sx);
+        }
+        const float r = wave_sum8(acc);                 // lane holds value (lane>>3)&7
+        const float u = __shfl_xor(r, 32, WAVE);        // partner: up row for a gate lane
+        const int vi = (lane >> 3) & 7;
+        if (vi < 4 && (lane & 7) == 0) {
+            const float g = r;
+            const float a = g / (1.f + expf(-g));
+            const int n = n0 + vi;
+            hout[(size_t)p * I + (n & ~7) + chunk_slot(n & 7)] = (uint16_t)f32_to_bf16(a * u);
+        }
+    }
+}
+
+// grid (H / 4): 4 output rows per workgroup; wave w takes tiles w, w+4, ...;
+// 16 lanes per row (16 B of codes each, K = 32c .. 32c+31).
+// y[t] = bf16(sum over the token's experts of coef * d + sg * d_shared),
+// optionally res = bf16(x + y).
+__global__ __launch_bounds__(256) void decode_down_combine(
+    const uint16_t* __restrict__ hin, int T, const int32_t* __restrict__ perm,
+    const Tile* __restrict__ tiles, const int* __restrict__ tile_count,
+    const float* __restrict__ wts, const float* __restrict__ sg, moe_qffn routed,
+    moe_qffn shared, uint16_t* __restrict__ y, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ res) {
+    __shared__ float yacc[4][MOE_DECODE_T_MAX][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane >> 4, c = lane & 15;
+    const int m = blockIdx.x * 4 + r;
+    const int ntiles = *tile_count;
+    float acc[MOE_DECODE_T_MAX];
+#pragma unroll
+    for (int t = 0; t < MOE_DECODE_T_MAX; ++t) acc[t] = 0.f;
+    for (int ti0 = wave; ti0 < ntiles; ti0 += 16) {
+        // up to four tiles per pass, loads issued before any arithmetic
+        uint4v dw[4];
+        float ds[4], db[4];
+        Tile tl[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int ti = ti0 + 4 * k;
+            tl[k] = tiles[ti < ntiles ? ti : ti0];
+            const bool sh = tl[k].group >= E;
+            const int e = sh ? 0 : tl[k].group;
+            const moe_qffn& q = sh ? shared : routed;
+            const size_t row = (size_t)e * H + m;
+            dw[k] = reinterpret_cast<const uint4v*>(q.down_q + row * (I / 8))[c];
+            ds[k] = fp16_to_f32(q.down_s[row * (I / G) + (c >> 1)]);
+            db[k] = fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (ti0 + 4 * k >= ntiles) break;
+            const float bk = fmaf(-128.f, ds[k], db[k]);
+            for (int rr = 0; rr < tl[k].nrows; ++rr) {
+                const int p = tl[k].row0 + rr;
+                int t;
+                float coef;
+                if (p < TOPK * T) {
+                    const int f = perm[p];
+                    t = min(max(f >> 3, 0), T - 1);
+                    coef = wts[f];
+                } else {
+                    t = p - TOPK * T;
+                    coef = sg[t];
+                }
+                const uint4v* hr = reinterpret_cast<const uint4v*>(hin + (size_t)p * I) + c * 4;
+                float sh_ = 0.f, dot = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const uint4v hv = hr[cc];
+                    sh_ = sum8_bf16(hv, sh_);
+                    dot = dot8_codes(dw[k][cc], hv, dot);
+                }
+                const float part = coef * fmaf(ds[k], dot, bk * sh_);
+#pragma unroll
+                for (int tt = 0; tt < MOE_DECODE_T_MAX; ++tt)
+                    if (tt == t) acc[tt] += part;
+            }
+        }
+    }
+    // reduce the 16 lanes of each row, then the four waves in a fixed order
+#pragma unroll
+    for (int t = 0; t < MOE_DECODE_T_MAX; ++t) {
+        if (t < T) {
+            float v = acc[t];
+            v += __shfl_xor(v, 8, WAVE);
+            v += __shfl_xor(v, 4, WAVE);
+            v += __shfl_xor(v, 2, WAVE);
+            v += __shfl_xor(v, 1, WAVE);
+            if (c == 0) yacc[wave][t][r] = v;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < T * 4; i += 256) {
+        const int t = i >> 2, rr = i & 3;
+        const float v = ((yacc[0][t][rr] + yacc[1][t][rr]) + yacc[2][t][rr]) + yacc[3][t][rr];
+        const uint32_t yb = f32_to_bf16(v);
+        const size_t o = (size_t)t * H + blockIdx.x * 4 + rr;
+        y[o] = (uint16_t)yb;
+        if (res) res[o] = (uint16_t)f32_to_bf16(bf16_to_f32(x[o]) + bf16_to_f32(yb));
+    }
+}
+
+void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,
+                         int32_t* ids, float* wts, float* sg, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* inv, Tile* tiles, int* tile_count,
+                         hipStream_t st) {
+    hipLaunchKernelGGL(route_select, dim3(1), dim3(256), 0, st, logits, x, wsg, T, ids, wts, sg,
+                       counts, offsets, perm, inv, tiles, tile_count);
+}
+
+void launch_decode_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+                          const int* tile_count, int max_tiles, const moe_qffn& routed,
+                          const moe_qffn& shared, uint16_t* hbuf, hipStream_t st) {
+    hipLaunchKernelGGL(decode_gateup, dim3(max_tiles, I / 16), dim3(256), 0, st, x, T, perm, tiles,
+                       tile_count, routed, shared, hbuf);
+}
+
+void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm,
+                                const Tile* tiles, const int* tile_count, const float* wts,
+                                const float* sg, const moe_qffn& routed, const moe_qffn& shared,
+                                uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st) {
+    hipLaunchKernelGGL(decode_down_combine, dim3(H / 4), dim3(256), 0, st, hbuf, T, perm, tiles,
+                       tile_count, wts, sg, routed, shared, y, x, res);
+}
+
+}  // namespace moe

@@ -6,17 +6,12 @@
 // Work is described by the row-tile list built on the device (plan_tiles):
 // tile = (expert or shared group, first row, row count <= 128).
 //
-// Decode (few tokens, memory bound: leslieli.dev note on the Lily engine,
-// paragraph 5):
-//   decode_gateup  one wave per (gate row n, up row n) pair of an active
-//                  expert; each lane streams 16 B of gate codes and 16 B of up
-//                  codes (K = 32 per lane, one 64-wide group per lane pair) and
-//                  uses them for every token of the tile.  The group's scale and
-//                  bias are applied once per lane:  sum_k x_k (q_k s + b) =
-//                  s sum_k x_k q_k + b sum_k x_k, exact codes, fp32.
-//                  h = bf16(silu(g) u), natural order.
+// Decode (few tokens; the gate/up GEMV and the fused down+combine kernel
+// live in decode.hip):
 //   decode_down    16 lanes per output row (16 B of codes each), 4 rows per
-//                  wave, same exact-code scheme; writes fp32 rows.
+//                  wave; exact codes through v_dot2_f32_bf16 (dot8_codes),
+//                  group scale/bias applied once per lane; writes the fp32
+//                  expert rows of the split expert-FFN call.
 //
 // Prefill (grouped GEMM on MFMA):
 //   expert_mfma<2048, true>   gate/up: tile rows x 128 columns of gate and up
@@ -44,50 +39,6 @@ __device__ __forceinline__ int row_token(int row, int T, const int32_t* __restri
 
 // ------------------------------------------------------------------ decode
 
-__global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict__ x, int T,
-                                                     const int32_t* __restrict__ perm,
-                                                     const Tile* __restrict__ tiles,
-                                                     const int* __restrict__ tile_count,
-                                                     moe_qffn routed, moe_qffn shared,
-                                                     uint16_t* __restrict__ hout) {
-    if ((int)blockIdx.x >= *tile_count) return;
-    const Tile tl = tiles[blockIdx.x];
-    const bool sh = tl.group >= E;
-    const int e = sh ? 0 : tl.group;
-    const moe_qffn q = sh ? shared : routed;
-    const int lane = threadIdx.x & 63;
-    const int n = blockIdx.y * 4 + (threadIdx.x >> 6);
-    const size_t row = (size_t)e * I + n;
-    const uint4v gw = reinterpret_cast<const uint4v*>(q.gate_q + row * (H / 8))[lane];
-    const uint4v uw = reinterpret_cast<const uint4v*>(q.up_q + row * (H / 8))[lane];
-    const float gs = fp16_to_f32(q.gate_s[row * (H / G) + (lane >> 1)]);
-    const float gb = fp16_to_f32(q.gate_b[row * (H / G) + (lane >> 1)]);
-    const float us = fp16_to_f32(q.up_s[row * (H / G) + (lane >> 1)]);
-    const float ub = fp16_to_f32(q.up_b[row * (H / G) + (lane >> 1)]);
-    for (int rr = 0; rr < tl.nrows; ++rr) {
-        const int t = row_token(tl.row0 + rr, T, perm);
-        const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
-        float sx = 0.f, sxg = 0.f, sxu = 0.f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint4v xv = xr[c];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float xf = bf16_to_f32((xv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-                sx += xf;
-                sxg = fmaf(xf, (float)((gw[c] >> (4 * i)) & 0xFu), sxg);
-                sxu = fmaf(xf, (float)((uw[c] >> (4 * i)) & 0xFu), sxu);
-            }
-        }
-        float g = wave_sum(fmaf(gs, sxg, gb * sx));
-        float u = wave_sum(fmaf(us, sxu, ub * sx));
-        if (lane == 0) {
-            const float a = g / (1.f + expf(-g));
-            hout[(size_t)(tl.row0 + rr) * I + n] = (uint16_t)f32_to_bf16(a * u);
-        }
-    }
-}
-
 __global__ __launch_bounds__(256) void decode_down(const uint16_t* __restrict__ hin, int T,
                                                    const Tile* __restrict__ tiles,
                                                    const int* __restrict__ tile_count,
@@ -104,21 +55,18 @@ __global__ __launch_bounds__(256) void decode_down(const uint16_t* __restrict__ 
     const size_t row = (size_t)e * H + m;
     const uint4v dw = reinterpret_cast<const uint4v*>(q.down_q + row * (I / 8))[c];
     const float s = fp16_to_f32(q.down_s[row * (I / G) + (c >> 1)]);
-    const float b = fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]);
+    const float b = fmaf(-128.f, s, fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]));
     for (int rr = 0; rr < tl.nrows; ++rr) {
+        // h rows are bf16 in chunk-slot order (decode_gateup)
         const uint4v* hr = reinterpret_cast<const uint4v*>(hin + (size_t)(tl.row0 + rr) * I) + c * 4;
-        float sh_ = 0.f, shq = 0.f;
+        float sh_ = 0.f, dot = 0.f;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             const uint4v hv = hr[cc];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float hf = bf16_to_f32((hv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-                sh_ += hf;
-                shq = fmaf(hf, (float)((dw[cc] >> (4 * i)) & 0xFu), shq);
-            }
+            sh_ = sum8_bf16(hv, sh_);
+            dot = dot8_codes(dw[cc], hv, dot);
         }
-        float p = fmaf(s, shq, b * sh_);
+        float p = fmaf(s, dot, b * sh_);
         p += __shfl_xor(p, 8, WAVE);
         p += __shfl_xor(p, 4, WAVE);
         p += __shfl_xor(p, 2, WAVE);
@@ -334,11 +282,14 @@ __global__ __launch_bounds__(256) void prep_x_f16(const uint16_t* __restrict__ x
     reinterpret_cast<uint4v*>(xh)[c] = w;
 }
 
+void launch_decode_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+                          const int* tile_count, int max_tiles, const moe_qffn& routed,
+                          const moe_qffn& shared, uint16_t* hbuf, hipStream_t st);
+
 void launch_expert_decode(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
                           const int* tile_count, int max_tiles, const moe_qffn& routed,
                           const moe_qffn& shared, uint16_t* hbuf, float* dout, hipStream_t st) {
-    hipLaunchKernelGGL(decode_gateup, dim3(max_tiles, I / 4), dim3(256), 0, st, x, T, perm, tiles,
-                       tile_count, routed, shared, hbuf);
+    launch_decode_gateup(x, T, perm, tiles, tile_count, max_tiles, routed, shared, hbuf, st);
     hipLaunchKernelGGL(decode_down, dim3(max_tiles, H / 16), dim3(256), 0, st, hbuf, T, tiles,
                        tile_count, routed, shared, dout);
 }

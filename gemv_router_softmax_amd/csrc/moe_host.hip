@@ -13,6 +13,19 @@ namespace moe {
 void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                   const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
                   hipStream_t st);
+void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
+                         float* logits, hipStream_t st);
+void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,
+                         int32_t* ids, float* wts, float* sg, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* inv, Tile* tiles, int* tile_count,
+                         hipStream_t st);
+void launch_decode_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+                          const int* tile_count, int max_tiles, const moe_qffn& routed,
+                          const moe_qffn& shared, uint16_t* hbuf, hipStream_t st);
+void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm,
+                                const Tile* tiles, const int* tile_count, const float* wts,
+                                const float* sg, const moe_qffn& routed, const moe_qffn& shared,
+                                uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st);
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st);
@@ -143,9 +156,17 @@ int moe_route(const uint16_t* x, int T, const uint16_t* w_router, const float* r
         return MOE_ERR_ALIGN;
     const WsLayout L = ws_layout(T);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    launch_route(x, T, w_router, router_bias, w_shared_gate,
-                 at<float>(ws, L.logits), topk_ids, topk_w, shared_gate,
-                 (hipStream_t)stream);
+    hipStream_t st = (hipStream_t)stream;
+    if (T <= MOE_DECODE_T_MAX) {
+        launch_route_logits(x, T, w_router, router_bias, at<float>(ws, L.logits), st);
+        launch_route_select(at<float>(ws, L.logits), x, w_shared_gate, T, topk_ids, topk_w,
+                            shared_gate, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                            at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv), at<Tile>(ws, L.tiles),
+                            at<int>(ws, L.tile_count), st);
+    } else {
+        launch_route(x, T, w_router, router_bias, w_shared_gate, at<float>(ws, L.logits),
+                     topk_ids, topk_w, shared_gate, st);
+    }
     return launch_status();
 }
 
@@ -236,18 +257,24 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
     uint16_t* hbuf = at<uint16_t>(ws, L.h);
     float* dout = at<float>(ws, L.dout);
 
+    if (path == MOE_PATH_DECODE) {
+        // four kernels: logits | select (top-8, permutation, tiles) | gate/up | down+combine
+        launch_route_logits(x, T, layer->w_router, layer->router_bias, at<float>(ws, L.logits),
+                            st);
+        launch_route_select(at<float>(ws, L.logits), x, layer->w_shared_gate, T, ids, wts, sg,
+                            counts, offsets, perm, inv, tiles, tcount, st);
+        launch_decode_gateup(x, T, perm, tiles, tcount, max_tiles(T), layer->routed,
+                             layer->shared, hbuf, st);
+        launch_decode_down_combine(hbuf, T, perm, tiles, tcount, wts, sg, layer->routed,
+                                   layer->shared, y, x, res, st);
+        return launch_status();
+    }
     launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
                  at<float>(ws, L.logits), ids, wts, sg, st);
-    launch_permute(ids, T, counts, offsets, perm, inv,
-                   at<int32_t>(ws, L.chunk_counts), st);
+    launch_permute(ids, T, counts, offsets, perm, inv, at<int32_t>(ws, L.chunk_counts), st);
     launch_plan(offsets, T, tiles, tcount, st);
-    if (path == MOE_PATH_DECODE)
-        launch_expert_decode(x, T, perm, tiles, tcount, max_tiles(T), layer->routed,
-                             layer->shared, hbuf, dout, st);
-    else
-        launch_expert_prefill(x, T, perm, tiles, tcount, max_tiles(T), layer->routed,
-                              layer->shared, at<uint16_t>(ws, L.xh),
-                              hbuf, dout, st);
+    launch_expert_prefill(x, T, perm, tiles, tcount, max_tiles(T), layer->routed, layer->shared,
+                          at<uint16_t>(ws, L.xh), hbuf, dout, st);
     launch_combine(dout, inv, wts, sg, T, y, x, res, st);
     return launch_status();
 }

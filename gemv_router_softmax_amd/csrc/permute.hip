@@ -15,83 +15,12 @@
 //                   shared expert over all T tokens), read by the expert
 //                   kernels from device memory so the host never needs the
 //                   expert counts.
-#include "common.hpp"
+#include "block_util.hpp"
 
 namespace moe {
 
 constexpr int PERM_CHUNK = 4096;   // entries per chunk in the large path
 constexpr int SMALL_MAX = 4096;    // entries handled by perm_small
-
-__device__ __forceinline__ uint64_t lanemask_lt() {
-    const int lane = threadIdx.x & 63;
-    return lane ? (~0ull >> (64 - lane)) : 0ull;
-}
-
-// Exclusive scan of one int per thread over a 256-thread block.
-__device__ int block_excl_scan256(int v, int* lds /* >= 4 ints */, int* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int n = __shfl_up(inc, o, WAVE);
-        if (lane >= o) inc += n;
-    }
-    if (lane == 63) lds[wave] = inc;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        int s = lds[w];
-        if (w < wave) base += s;
-        tot += s;
-    }
-    __syncthreads();
-    *total = tot;
-    return base + inc - v;
-}
-
-// Stable scatter of entries [f0, f1).  base[e] (LDS) is the next sorted
-// position of expert e and advances as entries are placed; wcnt (LDS,
-// 4*256 ints) must be zero on entry and is zero on exit.
-__device__ void stable_scatter(const int32_t* __restrict__ ids, int f0, int f1, int* base,
-                               int* wcnt, int32_t* __restrict__ perm,
-                               int32_t* __restrict__ inv) {
-    const int tid = threadIdx.x, wave = tid >> 6;
-    for (int c0 = f0; c0 < f1; c0 += 256) {
-        const int f = c0 + tid;
-        const bool valid = f < f1;
-        const int e = valid ? ids[f] : -1;
-        const bool ok = valid && e >= 0 && e < E;
-        if (valid && !ok) inv[f] = -1;
-        const int key = ok ? e : 511;
-        uint64_t peers = ~0ull;
-#pragma unroll
-        for (int b = 0; b < 9; ++b) {
-            uint64_t m = __ballot((key >> b) & 1);
-            peers &= ((key >> b) & 1) ? m : ~m;
-        }
-        const uint64_t below = peers & lanemask_lt();
-        const int rank = __popcll(below);
-        if (ok && below == 0) wcnt[wave * 256 + e] = __popcll(peers);
-        __syncthreads();
-        if (ok) {
-            int pre = 0;
-            for (int w = 0; w < wave; ++w) pre += wcnt[w * 256 + e];
-            const int pos = base[e] + pre + rank;
-            perm[pos] = f;
-            inv[f] = pos;
-        }
-        __syncthreads();
-        int s = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            s += wcnt[w * 256 + tid];
-            wcnt[w * 256 + tid] = 0;
-        }
-        base[tid] += s;
-        __syncthreads();
-    }
-}
 
 __global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ ids, int n,
                                                   int32_t* __restrict__ counts,

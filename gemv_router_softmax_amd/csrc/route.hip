@@ -11,11 +11,12 @@
 //   route_logits_mfma   larger T: bf16 MFMA 16x16x32 tiles, 64 tokens x 16
 //                       experts per wave, fp32 accumulation (bf16 products
 //                       are exact in fp32).
-//   route_topk          one wave per token: 4 logits per lane, eight rounds of
-//                       wave arg-max (ties -> lower expert index), softmax
-//                       weights renormalised over the selected eight, and the
-//                       shared-expert gate sigmoid(x . w_sg).
-#include "common.hpp"
+//   route_topk          one wave per token: 4 logits per lane, radix selection
+//                       of the 8th largest fp32 logit with wave ballots (ties ->
+//                       lower expert index), softmax weights renormalised over
+//                       the selected eight, and the shared-expert gate
+//                       sigmoid(x . w_sg).
+#include "block_util.hpp"
 
 namespace moe {
 
@@ -93,7 +94,8 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t* __restr
     }
 }
 
-// grid: ceil(T/4) blocks of 4 waves; wave -> token.
+// grid: ceil(T/4) blocks of 4 waves; wave -> token: radix-selected top-8,
+// renormalised weights and the shared-expert gate.
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits,
                                                   const uint16_t* __restrict__ x,
                                                   const uint16_t* __restrict__ wsg, int T,
@@ -103,46 +105,7 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = logits[(size_t)t * E + lane + 64 * i];
-    unsigned taken = 0;
-    float selv[TOPK];
-    int sele[TOPK];
-#pragma unroll
-    for (int k = 0; k < TOPK; ++k) {
-        float bv = -__builtin_inff();
-        int be = 0x7FFFFFFF;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int ei = lane + 64 * i;
-            bool free_ = !((taken >> i) & 1u);
-            if (free_ && (v[i] > bv || (v[i] == bv && ei < be))) { bv = v[i]; be = ei; }
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            float ov = __shfl_xor(bv, o, WAVE);
-            int oe = __shfl_xor(be, o, WAVE);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-        }
-        selv[k] = bv;
-        sele[k] = be;
-        if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
-    }
-    // softmax over all experts renormalised over the selected ones: the full
-    // denominator cancels, leaving exp(l_j - l_max) / sum_sel exp(l - l_max).
-    const float m = selv[0];
-    float ex[TOPK], s = 0.f;
-#pragma unroll
-    for (int k = 0; k < TOPK; ++k) { ex[k] = expf(selv[k] - m); s += ex[k]; }
-#pragma unroll
-    for (int k = 0; k < TOPK; ++k) {
-        if (lane == k) {
-            ids[(size_t)t * TOPK + k] = sele[k];
-            wts[(size_t)t * TOPK + k] = ex[k] / s;
-        }
-    }
-    // shared-expert gate
+    wave_top8(logits + (size_t)t * E, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
     const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
     const uint4v* gr = reinterpret_cast<const uint4v*>(wsg) + lane * 4;
     float z = dot8_bf16(xr[0], gr[0]) + dot8_bf16(xr[1], gr[1]) + dot8_bf16(xr[2], gr[2]) +
@@ -151,9 +114,8 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
     if (lane == 0) sg[t] = 1.f / (1.f + expf(-z));
 }
 
-void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
-                  const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
-                  hipStream_t st) {
+void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
+                         float* logits, hipStream_t st) {
     if (T <= 32) {
         hipLaunchKernelGGL(route_logits_gemv, dim3(E / 4), dim3(256), 0, st, x, T, wr, bias,
                            logits);
@@ -161,6 +123,12 @@ void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bia
         hipLaunchKernelGGL(route_logits_mfma, dim3((T + 63) / 64, E / 64), dim3(256), 0, st, x,
                            T, wr, bias, logits);
     }
+}
+
+void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
+                  const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
+                  hipStream_t st) {
+    launch_route_logits(x, T, wr, bias, logits, st);
     hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, x, wsg, T, ids,
                        wts, sg);
 }

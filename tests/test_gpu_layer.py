@@ -81,3 +81,42 @@ def test_t0_is_noop(gpu):
     y = torch.zeros((0, 2048), dtype=torch.int16, device="cuda")
     moe.moe_layer_forward(x, D, y, moe.workspace(0))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [17, 32])
+def test_decode_forced_max(gpu, T):
+    check_layer(T, DEC, seed=8)
+
+
+def test_graph_capture_chain(gpu):
+    """A 3-layer decode chain captured in a HIP graph and replayed several
+    times, with eager work in between, matches the eager chain bit for bit."""
+    D = [P.dev_layer(0, l) for l in range(3)]
+    ws = moe.workspace(1)
+    x0 = torch.empty((1, 2048), dtype=torch.int16, device="cuda")
+    bufs = [torch.empty((1, 2048), dtype=torch.int16, device="cuda") for _ in range(2)]
+    y = torch.empty((1, 2048), dtype=torch.int16, device="cuda")
+
+    def chain():
+        cur = x0
+        for l, Dl in enumerate(D):
+            moe.moe_layer_forward_ex(cur, Dl, y, ws, residual_out=bufs[l % 2])
+            cur = bufs[l % 2]
+        return cur
+
+    xs = [moe.to_device_bits(synth.make_x(1, seed=0, step=s)) for s in range(4)]
+    eager = []
+    for s in range(4):
+        x0.copy_(xs[s])
+        eager.append(chain().clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = chain()
+    for s in range(4):
+        x0.copy_(xs[s])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[s]), f"replay {s} differs from eager"
+        # unrelated eager work between replays
+        moe.moe_layer_forward(xs[(s + 1) % 4], D[0], y, ws)
+        torch.cuda.synchronize()
