@@ -32,6 +32,12 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
 typedef uint16_t ushort8v __attribute__((ext_vector_type(8)));
 
+// Position of element k (0..7) inside an 8-element chunk of the fp16
+// operand layout used by every expert kernel.  The dequantiser produces the
+// eight codes of a word in the order k = 0,4,1,5,2,6,3,7 (two nibbles per
+// packed half2), so activations are stored in that same order.
+__device__ __forceinline__ int chunk_slot(int k) { return ((k & 3) << 1) | (k >> 2); }
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __builtin_bit_cast(float, bits16 << 16);
 }
@@ -48,42 +54,48 @@ __device__ __forceinline__ float fp16_to_f32(uint16_t bits) {
     return (float)__builtin_bit_cast(_Float16, bits);
 }
 
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-
 // Exact-code dot products for the decode GEMVs.  A code word holds eight
 // 4-bit codes q0..q7 (q_k in bits 4k..4k+3).  ((w >> 4i) & 0x000F000F) |
-// 0x43004300 is the bf16 pair (128 + q_i, 128 + q_{i+4}) -- exact, since bf16
-// spacing at 128 is 1 -- so v_dot2_f32_bf16 against the activation pair
-// (a_i, a_{i+4}) accumulates sum_k a_k (128 + q_k).  With sa = sum_k a_k the
-// group's contribution is  s * (dot - 128 sa) + b * sa = s * dot + (b - 128 s) sa.
+// 0x64006400 is the fp16 pair (1024 + q_i, 1024 + q_{i+4}); one packed
+// subtraction leaves (q_i, q_{i+4}) exactly, and v_dot2_f32_f16 against the
+// activation pair (a_i, a_{i+4}) -- activations stored as fp16 in chunk-slot
+// order -- adds a_i q_i + a_{i+4} q_{i+4} to an fp32 accumulator (exact
+// products).  The bf16 variant of the dot instruction is not used: it drops
+// addends far below the accumulator instead of keeping fp32 precision.
 __device__ __forceinline__ float dot8_codes(uint32_t w, uint4v apairs, float acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t p = ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, p),
-                                              __builtin_bit_cast(bf16x2v, apairs[i]), acc, false);
+        const uint32_t p = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        const half2v qh = __builtin_bit_cast(half2v, p) - (half2v){(_Float16)1024.f, (_Float16)1024.f};
+        acc = __builtin_amdgcn_fdot2(qh, __builtin_bit_cast(half2v, apairs[i]), acc, false);
     }
     return acc;
 }
 
-// Sum of the eight bf16 activations of a pair vector.
-__device__ __forceinline__ float sum8_bf16(uint4v apairs, float acc) {
+// Sum of the eight fp16 activations of a pair vector.
+__device__ __forceinline__ float sum8_h(uint4v apairs, float acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, 0x3F803F80u),
-                                              __builtin_bit_cast(bf16x2v, apairs[i]), acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, 0x3C003C00u),
+                                     __builtin_bit_cast(half2v, apairs[i]), acc, false);
     return acc;
 }
 
-// Eight natural-order bf16 values (a0,a1),(a2,a3),(a4,a5),(a6,a7) -> the
-// code-pair order (a0,a4),(a1,a5),(a2,a6),(a3,a7).
-__device__ __forceinline__ uint4v pair_i_i4(uint4v v) {
-    uint4v r;
-    r[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-    r[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-    r[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-    r[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-    return r;
+// Eight natural-order bf16 values -> fp16 in chunk-slot order (k = 0,4,1,5,
+// 2,6,3,7), the activation layout of every expert kernel.  bf16 -> fp16 is
+// exact for magnitudes in [2^-14, 65504]; smaller values keep fp16's
+// subnormal spacing 2^-24.
+__device__ __forceinline__ uint4v bf16x8_to_f16_slots(uint4v v) {
+    uint16_t o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float f = bf16_to_f32((v[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+        o[chunk_slot(k)] = __builtin_bit_cast(uint16_t, (_Float16)f);
+    }
+    uint4v w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)o[2 * i] | ((uint32_t)o[2 * i + 1] << 16);
+    return w;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -98,10 +110,5 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Position of element k (0..7) inside an 8-element chunk of the fp16
-// operand layout used by the MFMA kernels.  The dequantiser produces the
-// eight codes of a word in the order k = 0,4,1,5,2,6,3,7 (two nibbles per
-// packed half2), so activations are stored in that same order.
-__device__ __forceinline__ int chunk_slot(int k) { return ((k & 3) << 1) | (k >> 2); }
 
 }  // namespace moe

@@ -9,13 +9,15 @@
 //   route_select        ONE workgroup: top-8 per token by radix selection on
 //                       the fp32 logits (ties to the lower expert index),
 //                       renormalised softmax weights, the shared-expert gate,
-//                       the stable permutation and the row-tile list
+//                       the stable permutation, the row-tile list and the fp16
+//                       copy of x the GEMV reads
 //   decode_gateup       16 gate rows + 16 up rows of one active expert per
 //                       workgroup; every lane streams 16 B of each row
 //                       (coalesced 128-bit loads, all issued up front) and
 //                       applies the group scale/bias once per lane on exact
-//                       codes; eight dot products are reduced together with a
-//                       transposing butterfly; h = bf16(silu(g) u)
+//                       codes (v_dot2_f32_f16 on fp16 code pairs); eight dot
+//                       products are reduced together with a transposing
+//                       butterfly; h = bf16(silu(g) u)
 //   decode_down_combine 4 output rows per workgroup for ALL active experts:
 //                       down GEMV on exact codes, then the weighted combine
 //                       with the shared expert and the residual add, so the
@@ -42,7 +44,8 @@ __global__ __launch_bounds__(256) void route_select(const float* __restrict__ lo
                                                     int32_t* __restrict__ perm,
                                                     int32_t* __restrict__ inv,
                                                     Tile* __restrict__ tiles,
-                                                    int* __restrict__ tile_count) {
+                                                    int* __restrict__ tile_count,
+                                                    uint16_t* __restrict__ xh) {
     __shared__ int ids_l[MOE_DECODE_T_MAX * TOPK];
     __shared__ int hist[256];
     __shared__ int base[256];
@@ -71,6 +74,10 @@ __global__ __launch_bounds__(256) void route_select(const float* __restrict__ lo
         z = wave_sum(z);
         if (lane == 0) sg[t] = 1.f / (1.f + expf(-z));
     }
+    // fp16 activations in chunk-slot order for the gate/up GEMV
+    for (int ci = tid; ci < T * (H / 8); ci += 256)
+        reinterpret_cast<uint4v*>(xh)[ci] =
+            bf16x8_to_f16_slots(reinterpret_cast<const uint4v*>(x)[ci]);
     __syncthreads();
     const int n = TOPK * T;
     for (int f = tid; f < n; f += 256) atomicAdd(&hist[ids_l[f]], 1);
@@ -110,9 +117,10 @@ __global__ __launch_bounds__(256) void route_select(const float* __restrict__ lo
 
 // grid (max tiles, I / 16); 4 waves x 4 rows (gate and up) each.  Lane l
 // covers K = 32l .. 32l+31 (one 16-byte code load per row, half of one
-// 64-wide group).  h is written as bf16 in chunk-slot order (k = 0,4,1,5,
-// 2,6,3,7 inside every 8-element chunk), the pair order dot8_codes uses.
-__global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict__ x, int T,
+// 64-wide group).  xh: fp16 activations in chunk-slot order.  h = bf16(silu(g)
+// u) is stored as fp16 (exact) in chunk-slot order, the layout every expert
+// kernel reads.
+__global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict__ xh, int T,
                                                      const int32_t* __restrict__ perm,
                                                      const Tile* __restrict__ tiles,
                                                      const int* __restrict__ tile_count,
@@ -140,20 +148,20 @@ __global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict_
         const uint16_t* sb = i < 4 ? q.gate_s : q.up_s;
         const uint16_t* bb = i < 4 ? q.gate_b : q.up_b;
         s[i] = fp16_to_f32(sb[row * (H / G) + (lane >> 1)]);
-        b[i] = fmaf(-128.f, s[i], fp16_to_f32(bb[row * (H / G) + (lane >> 1)]));
+        b[i] = fp16_to_f32(bb[row * (H / G) + (lane >> 1)]);
     }
     for (int rr = 0; rr < tl.nrows; ++rr) {
         const int p = tl.row0 + rr;
         int t;
         if (p < TOPK * T) t = min(max(perm[p] >> 3, 0), T - 1);
         else t = p - TOPK * T;
-        const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
+        const uint4v* xr = reinterpret_cast<const uint4v*>(xh + (size_t)t * H) + lane * 4;
         uint4v xp[4];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) xp[cc] = pair_i_i4(xr[cc]);
+        for (int cc = 0; cc < 4; ++cc) xp[cc] = xr[cc];
         float sx = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) sx = sum8_bf16(xp[cc], sx);
+        for (int cc = 0; cc < 4; ++cc) sx = sum8_h(xp[cc], sx);
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -169,7 +177,9 @@ __global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict_
             const float g = r;
             const float a = g / (1.f + expf(-g));
             const int n = n0 + vi;
-            hout[(size_t)p * I + (n & ~7) + chunk_slot(n & 7)] = (uint16_t)f32_to_bf16(a * u);
+            const float hb = bf16_to_f32(f32_to_bf16(a * u));
+            hout[(size_t)p * I + (n & ~7) + chunk_slot(n & 7)] =
+                __builtin_bit_cast(uint16_t, (_Float16)hb);
         }
     }
 }
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(256) void decode_down_combine(
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (ti0 + 4 * k >= ntiles) break;
-            const float bk = fmaf(-128.f, ds[k], db[k]);
+            const float bk = db[k];
             for (int rr = 0; rr < tl[k].nrows; ++rr) {
                 const int p = tl[k].row0 + rr;
                 int t;
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(256) void decode_down_combine(
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
                     const uint4v hv = hr[cc];
-                    sh_ = sum8_bf16(hv, sh_);
+                    sh_ = sum8_h(hv, sh_);
                     dot = dot8_codes(dw[k][cc], hv, dot);
                 }
                 const float part = coef * fmaf(ds[k], dot, bk * sh_);
@@ -266,15 +276,15 @@ __global__ __launch_bounds__(256) void decode_down_combine(
 void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,
                          int32_t* ids, float* wts, float* sg, int32_t* counts, int32_t* offsets,
                          int32_t* perm, int32_t* inv, Tile* tiles, int* tile_count,
-                         hipStream_t st) {
+                         uint16_t* xh, hipStream_t st) {
     hipLaunchKernelGGL(route_select, dim3(1), dim3(256), 0, st, logits, x, wsg, T, ids, wts, sg,
-                       counts, offsets, perm, inv, tiles, tile_count);
+                       counts, offsets, perm, inv, tiles, tile_count, xh);
 }
 
-void launch_decode_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+void launch_decode_gateup(const uint16_t* xh, int T, const int32_t* perm, const Tile* tiles,
                           const int* tile_count, int max_tiles, const moe_qffn& routed,
                           const moe_qffn& shared, uint16_t* hbuf, hipStream_t st) {
-    hipLaunchKernelGGL(decode_gateup, dim3(max_tiles, I / 16), dim3(256), 0, st, x, T, perm, tiles,
+    hipLaunchKernelGGL(decode_gateup, dim3(max_tiles, I / 16), dim3(256), 0, st, xh, T, perm, tiles,
                        tile_count, routed, shared, hbuf);
 }
 

@@ -55,15 +55,15 @@ __global__ __launch_bounds__(256) void decode_down(const uint16_t* __restrict__ 
     const size_t row = (size_t)e * H + m;
     const uint4v dw = reinterpret_cast<const uint4v*>(q.down_q + row * (I / 8))[c];
     const float s = fp16_to_f32(q.down_s[row * (I / G) + (c >> 1)]);
-    const float b = fmaf(-128.f, s, fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]));
+    const float b = fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]);
     for (int rr = 0; rr < tl.nrows; ++rr) {
-        // h rows are bf16 in chunk-slot order (decode_gateup)
+        // h rows are fp16 in chunk-slot order (decode_gateup)
         const uint4v* hr = reinterpret_cast<const uint4v*>(hin + (size_t)(tl.row0 + rr) * I) + c * 4;
         float sh_ = 0.f, dot = 0.f;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             const uint4v hv = hr[cc];
-            sh_ = sum8_bf16(hv, sh_);
+            sh_ = sum8_h(hv, sh_);
             dot = dot8_codes(dw[cc], hv, dot);
         }
         float p = fmaf(s, dot, b * sh_);
@@ -264,32 +264,26 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
     }
 }
 
-// x (bf16) -> fp16 in chunk-slot order, the A operand layout of expert_mfma.
+// x (bf16) -> fp16 in chunk-slot order, the activation layout of the expert kernels.
 __global__ __launch_bounds__(256) void prep_x_f16(const uint16_t* __restrict__ x, int T,
                                                   uint16_t* __restrict__ xh) {
     const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;   // 8-element chunk index
     if (c >= (size_t)T * (H / 8)) return;
-    const uint4v v = reinterpret_cast<const uint4v*>(x)[c];
-    uint16_t o[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float f = bf16_to_f32((v[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
-        o[chunk_slot(k)] = __builtin_bit_cast(uint16_t, (_Float16)f);
-    }
-    uint4v w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)o[2 * i] | ((uint32_t)o[2 * i + 1] << 16);
-    reinterpret_cast<uint4v*>(xh)[c] = w;
+    reinterpret_cast<uint4v*>(xh)[c] = bf16x8_to_f16_slots(reinterpret_cast<const uint4v*>(x)[c]);
 }
 
-void launch_decode_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+void launch_decode_gateup(const uint16_t* xh, int T, const int32_t* perm, const Tile* tiles,
                           const int* tile_count, int max_tiles, const moe_qffn& routed,
                           const moe_qffn& shared, uint16_t* hbuf, hipStream_t st);
 
 void launch_expert_decode(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
                           const int* tile_count, int max_tiles, const moe_qffn& routed,
-                          const moe_qffn& shared, uint16_t* hbuf, float* dout, hipStream_t st) {
-    launch_decode_gateup(x, T, perm, tiles, tile_count, max_tiles, routed, shared, hbuf, st);
+                          const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
+                          hipStream_t st) {
+    const size_t chunks = (size_t)T * (H / 8);
+    hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
+                       xh);
+    launch_decode_gateup(xh, T, perm, tiles, tile_count, max_tiles, routed, shared, hbuf, st);
     hipLaunchKernelGGL(decode_down, dim3(max_tiles, H / 16), dim3(256), 0, st, hbuf, T, tiles,
                        tile_count, routed, shared, dout);
 }

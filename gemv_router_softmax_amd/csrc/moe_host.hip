@@ -18,8 +18,8 @@ void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const flo
 void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,
                          int32_t* ids, float* wts, float* sg, int32_t* counts, int32_t* offsets,
                          int32_t* perm, int32_t* inv, Tile* tiles, int* tile_count,
-                         hipStream_t st);
-void launch_decode_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+                         uint16_t* xh, hipStream_t st);
+void launch_decode_gateup(const uint16_t* xh, int T, const int32_t* perm, const Tile* tiles,
                           const int* tile_count, int max_tiles, const moe_qffn& routed,
                           const moe_qffn& shared, uint16_t* hbuf, hipStream_t st);
 void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm,
@@ -33,7 +33,8 @@ int perm_chunks(int T);
 int max_tiles(int T);
 void launch_expert_decode(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
                           const int* tile_count, int max_tiles, const moe_qffn& routed,
-                          const moe_qffn& shared, uint16_t* hbuf, float* dout, hipStream_t st);
+                          const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
+                          hipStream_t st);
 void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
                            const int* tile_count, int max_tiles, const moe_qffn& routed,
                            const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
@@ -162,7 +163,7 @@ int moe_route(const uint16_t* x, int T, const uint16_t* w_router, const float* r
         launch_route_select(at<float>(ws, L.logits), x, w_shared_gate, T, topk_ids, topk_w,
                             shared_gate, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
                             at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv), at<Tile>(ws, L.tiles),
-                            at<int>(ws, L.tile_count), st);
+                            at<int>(ws, L.tile_count), at<uint16_t>(ws, L.xh), st);
     } else {
         launch_route(x, T, w_router, router_bias, w_shared_gate, at<float>(ws, L.logits),
                      topk_ids, topk_w, shared_gate, st);
@@ -207,8 +208,8 @@ int moe_expert_ffn(const uint16_t* x, int T, const moe_qffn* routed, const moe_q
     uint16_t* hbuf = at<uint16_t>(ws, L.h);
     launch_plan(expert_offsets, T, tiles, tcount, st);
     if (path == MOE_PATH_DECODE)
-        launch_expert_decode(x, T, perm, tiles, tcount, max_tiles(T), *routed, *shared, hbuf,
-                             expert_out, st);
+        launch_expert_decode(x, T, perm, tiles, tcount, max_tiles(T), *routed, *shared,
+                             at<uint16_t>(ws, L.xh), hbuf, expert_out, st);
     else
         launch_expert_prefill(x, T, perm, tiles, tcount, max_tiles(T), *routed, *shared,
                               at<uint16_t>(ws, L.xh), hbuf,
@@ -261,9 +262,10 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
         // four kernels: logits | select (top-8, permutation, tiles) | gate/up | down+combine
         launch_route_logits(x, T, layer->w_router, layer->router_bias, at<float>(ws, L.logits),
                             st);
+        uint16_t* xh = at<uint16_t>(ws, L.xh);
         launch_route_select(at<float>(ws, L.logits), x, layer->w_shared_gate, T, ids, wts, sg,
-                            counts, offsets, perm, inv, tiles, tcount, st);
-        launch_decode_gateup(x, T, perm, tiles, tcount, max_tiles(T), layer->routed,
+                            counts, offsets, perm, inv, tiles, tcount, xh, st);
+        launch_decode_gateup(xh, T, perm, tiles, tcount, max_tiles(T), layer->routed,
                              layer->shared, hbuf, st);
         launch_decode_down_combine(hbuf, T, perm, tiles, tcount, wts, sg, layer->routed,
                                    layer->shared, y, x, res, st);
