@@ -67,7 +67,10 @@ __device__ __forceinline__ float dot8_codes(uint32_t w, uint4v apairs, float acc
     for (int i = 0; i < 4; ++i) {
         const uint32_t p = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
         const half2v qh = __builtin_bit_cast(half2v, p) - (half2v){(_Float16)1024.f, (_Float16)1024.f};
-        acc = __builtin_amdgcn_fdot2(qh, __builtin_bit_cast(half2v, apairs[i]), acc, false);
+        // (copy the element to a scalar first: bit-casting an ext-vector element
+        // directly reads element 0 with this compiler)
+        const uint32_t ai = apairs[i];
+        acc = __builtin_amdgcn_fdot2(qh, __builtin_bit_cast(half2v, ai), acc, false);
     }
     return acc;
 }
@@ -75,9 +78,11 @@ __device__ __forceinline__ float dot8_codes(uint32_t w, uint4v apairs, float acc
 // Sum of the eight fp16 activations of a pair vector.
 __device__ __forceinline__ float sum8_h(uint4v apairs, float acc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ai = apairs[i];
         acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, 0x3C003C00u),
-                                     __builtin_bit_cast(half2v, apairs[i]), acc, false);
+                                     __builtin_bit_cast(half2v, ai), acc, false);
+    }
     return acc;
 }
 
