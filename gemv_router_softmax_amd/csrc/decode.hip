@@ -273,6 +273,270 @@ __global__ __launch_bounds__(256) void decode_down_combine(
     }
 }
 
+// ---------------------------------------------------------------------
+// Few-token layer (T <= MOE_DECODE_T): three kernels, no select kernel.
+// The routing (top-8 of 256 logits per token, at most 8T active experts)
+// is recomputed inside every workgroup of the two expert kernels from the
+// logits in memory -- one 1 KB read per token and ~1 us of wave work, far
+// cheaper than a kernel boundary and its dependent loads.  Every workgroup
+// runs the same deterministic code on the same logits, so all of them
+// agree on the selection.
+
+struct BlockRoute {
+    int ids[MOE_DECODE_T][TOPK];
+    float w[MOE_DECODE_T][TOPK];
+    float sg[MOE_DECODE_T];
+    int active[MOE_DECODE_T * TOPK];     // active experts, ascending id
+    uint32_t tmask[MOE_DECODE_T * TOPK]; // tokens that selected active[a]
+    int mark[E];
+    int scr[4];
+    int nact;
+};
+
+// All T tokens' top-8 (one wave per token) and the active-expert list.
+__device__ void block_route(const float* __restrict__ logits, const float* __restrict__ z,
+                            int T, BlockRoute& R) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    R.mark[tid] = 0;
+    __syncthreads();
+    for (int t = wave; t < T; t += 4) wave_top8(logits + (size_t)t * E, R.ids[t], R.w[t], nullptr);
+    if (tid < T) R.sg[tid] = 1.f / (1.f + expf(-z[tid]));
+    __syncthreads();
+    if (tid < T * TOPK) atomicOr((unsigned*)&R.mark[R.ids[tid >> 3][tid & 7]], 1u << (tid >> 3));
+    __syncthreads();
+    const int mk = R.mark[tid];
+    int na;
+    const int slot = block_excl_scan256(mk ? 1 : 0, R.scr, &na);
+    if (mk) {
+        R.active[slot] = tid;
+        R.tmask[slot] = (uint32_t)mk;
+    }
+    if (tid == 0) R.nact = na;
+    __syncthreads();
+}
+
+// grid (E/4 + 1 + T): blocks < E/4: logits of 4 experts each (one wave per
+// expert row); block E/4: shared-gate logits z[t] = x[t] . w_sg; the last T
+// blocks: fp16 copy of x in chunk-slot order.
+__global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restrict__ x, int T,
+                                                        const uint16_t* __restrict__ wr,
+                                                        const float* __restrict__ bias,
+                                                        const uint16_t* __restrict__ wsg,
+                                                        float* __restrict__ logits,
+                                                        float* __restrict__ z,
+                                                        uint16_t* __restrict__ xh) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int b = blockIdx.x;
+    if (b > E / 4) {                      // x -> fp16, token b - E/4 - 1
+        const int t = b - E / 4 - 1;
+        const size_t ci = (size_t)t * (H / 8) + threadIdx.x;
+        reinterpret_cast<uint4v*>(xh)[ci] =
+            bf16x8_to_f16_slots(reinterpret_cast<const uint4v*>(x)[ci]);
+        return;
+    }
+    const uint16_t* row = b < E / 4 ? wr + (size_t)(b * 4 + wave) * H : wsg;
+    if (b == E / 4 && wave != 0) return;
+    const uint4v* wrow = reinterpret_cast<const uint4v*>(row) + lane * 4;
+    const uint4v w0 = wrow[0], w1 = wrow[1], w2 = wrow[2], w3 = wrow[3];
+    uint4v xv[MOE_DECODE_T][4];
+#pragma unroll
+    for (int t = 0; t < MOE_DECODE_T; ++t) {
+        if (t < T) {
+            const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xv[t][c] = xr[c];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MOE_DECODE_T; ++t) {
+        if (t < T) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint4v wv = c == 0 ? w0 : (c == 1 ? w1 : (c == 2 ? w2 : w3));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a = xv[t][c][i], bb = wv[i];
+                    s = fmaf(bf16_to_f32(a & 0xFFFFu), bf16_to_f32(bb & 0xFFFFu), s);
+                    s = fmaf(bf16_to_f32(a >> 16), bf16_to_f32(bb >> 16), s);
+                }
+            }
+            s = wave_sum(s);
+            if (lane == 0) {
+                if (b < E / 4) {
+                    const int e = b * 4 + wave;
+                    logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
+                } else {
+                    z[t] = s;
+                }
+            }
+        }
+    }
+}
+
+// grid (1 + 8T, I/16).  Slot 0 is the shared expert (no routing needed, so
+// its workgroups start streaming at once); slot a >= 1 is the a-th active
+// routed expert.  h rows are indexed (slot * T + t), fp16, chunk-slot order.
+__global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restrict__ xh, int T,
+                                                         const float* __restrict__ logits,
+                                                         const float* __restrict__ z,
+                                                         moe_qffn routed, moe_qffn shared,
+                                                         uint16_t* __restrict__ hout) {
+    __shared__ BlockRoute R;
+    const int slot = blockIdx.x;
+    int e = 0;
+    uint32_t mask = (1u << T) - 1u;
+    if (slot > 0) {
+        block_route(logits, z, T, R);
+        if (slot - 1 >= R.nact) return;
+        e = R.active[slot - 1];
+        mask = R.tmask[slot - 1];
+    }
+    const moe_qffn q = slot == 0 ? shared : routed;
+    const int lane = threadIdx.x & 63;
+    const int n0 = blockIdx.y * 16 + (threadIdx.x >> 6) * 4;
+    uint4v wq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const size_t row = (size_t)e * I + n0 + (i & 3);
+        const uint32_t* qb = i < 4 ? q.gate_q : q.up_q;
+        wq[i] = reinterpret_cast<const uint4v*>(qb + row * (H / 8))[lane];
+    }
+    float s[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const size_t row = (size_t)e * I + n0 + (i & 3);
+        const uint16_t* sb = i < 4 ? q.gate_s : q.up_s;
+        const uint16_t* bb = i < 4 ? q.gate_b : q.up_b;
+        s[i] = fp16_to_f32(sb[row * (H / G) + (lane >> 1)]);
+        b[i] = fp16_to_f32(bb[row * (H / G) + (lane >> 1)]);
+    }
+    for (int t = 0; t < T; ++t) {
+        if (!((mask >> t) & 1u)) continue;
+        const uint4v* xr = reinterpret_cast<const uint4v*>(xh + (size_t)t * H) + lane * 4;
+        uint4v xp[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) xp[cc] = xr[cc];
+        float sx = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) sx = sum8_h(xp[cc], sx);
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float dd = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) dd = dot8_codes(wq[i][cc], xp[cc], dd);
+            acc[i] = fmaf(s[i], dd, b[i] * sx);
+        }
+        const float r = wave_sum8(acc);
+        const float u = __shfl_xor(r, 32, WAVE);
+        const int vi = (lane >> 3) & 7;
+        if (vi < 4 && (lane & 7) == 0) {
+            const float a = r / (1.f + expf(-r));
+            const float hb = bf16_to_f32(f32_to_bf16(a * u));
+            const int n = n0 + vi;
+            hout[((size_t)slot * T + t) * I + (n & ~7) + chunk_slot(n & 7)] =
+                __builtin_bit_cast(uint16_t, (_Float16)hb);
+        }
+    }
+}
+
+// grid (H/4): 4 output rows per workgroup over every active expert (wave w
+// takes slots w, w+4, ...), combine with the routing weights and the shared
+// gate, residual add.  Fixed summation order: deterministic.
+__global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restrict__ hin, int T,
+                                                       const float* __restrict__ logits,
+                                                       const float* __restrict__ z,
+                                                       moe_qffn routed, moe_qffn shared,
+                                                       uint16_t* __restrict__ y,
+                                                       const uint16_t* __restrict__ x,
+                                                       uint16_t* __restrict__ res) {
+    __shared__ BlockRoute R;
+    __shared__ float yacc[4][MOE_DECODE_T][4];
+    block_route(logits, z, T, R);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane >> 4, c = lane & 15;
+    const int m = blockIdx.x * 4 + r;
+    const int nslots = R.nact + 1;
+    float acc[MOE_DECODE_T];
+#pragma unroll
+    for (int t = 0; t < MOE_DECODE_T; ++t) acc[t] = 0.f;
+    for (int a0 = wave; a0 < nslots; a0 += 16) {
+        uint4v dw[4];
+        float ds[4], db[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int a = a0 + 4 * k < nslots ? a0 + 4 * k : a0;
+            const int e = a == 0 ? 0 : R.active[a - 1];
+            const moe_qffn& q = a == 0 ? shared : routed;
+            const size_t row = (size_t)e * H + m;
+            dw[k] = reinterpret_cast<const uint4v*>(q.down_q + row * (I / 8))[c];
+            ds[k] = fp16_to_f32(q.down_s[row * (I / G) + (c >> 1)]);
+            db[k] = fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int a = a0 + 4 * k;
+            if (a >= nslots) break;
+            const int e = a == 0 ? -1 : R.active[a - 1];
+            const uint32_t mask = a == 0 ? (1u << T) - 1u : R.tmask[a - 1];
+            for (int t = 0; t < T; ++t) {
+                if (!((mask >> t) & 1u)) continue;
+                float coef = R.sg[t];
+                if (a > 0) {
+#pragma unroll
+                    for (int j = 0; j < TOPK; ++j)
+                        if (R.ids[t][j] == e) coef = R.w[t][j];
+                }
+                const uint4v* hr =
+                    reinterpret_cast<const uint4v*>(hin + ((size_t)a * T + t) * I) + c * 4;
+                float sh_ = 0.f, dot = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const uint4v hv = hr[cc];
+                    sh_ = sum8_h(hv, sh_);
+                    dot = dot8_codes(dw[k][cc], hv, dot);
+                }
+                const float part = coef * fmaf(ds[k], dot, db[k] * sh_);
+#pragma unroll
+                for (int tt = 0; tt < MOE_DECODE_T; ++tt)
+                    if (tt == t) acc[tt] += part;
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MOE_DECODE_T; ++t) {
+        if (t < T) {
+            float v = acc[t];
+            v += __shfl_xor(v, 8, WAVE);
+            v += __shfl_xor(v, 4, WAVE);
+            v += __shfl_xor(v, 2, WAVE);
+            v += __shfl_xor(v, 1, WAVE);
+            if (c == 0) yacc[wave][t][r] = v;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < T * 4) {
+        const int t = threadIdx.x >> 2, rr = threadIdx.x & 3;
+        const float v = ((yacc[0][t][rr] + yacc[1][t][rr]) + yacc[2][t][rr]) + yacc[3][t][rr];
+        const uint32_t yb = f32_to_bf16(v);
+        const size_t o = (size_t)t * H + blockIdx.x * 4 + rr;
+        y[o] = (uint16_t)yb;
+        if (res) res[o] = (uint16_t)f32_to_bf16(bf16_to_f32(x[o]) + bf16_to_f32(yb));
+    }
+}
+
+void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
+                               float* z, uint16_t* xh, uint16_t* hbuf, uint16_t* y,
+                               uint16_t* res, hipStream_t st) {
+    hipLaunchKernelGGL(route_logits_dec, dim3(E / 4 + 1 + T), dim3(256), 0, st, x, T, L.w_router,
+                       L.router_bias, L.w_shared_gate, logits, z, xh);
+    hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T,
+                       logits, z, L.routed, L.shared, hbuf);
+    hipLaunchKernelGGL(decode_down_dec, dim3(H / 4), dim3(256), 0, st, hbuf, T, logits, z,
+                       L.routed, L.shared, y, x, res);
+}
+
 void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,
                          int32_t* ids, float* wts, float* sg, int32_t* counts, int32_t* offsets,
                          int32_t* perm, int32_t* inv, Tile* tiles, int* tile_count,

@@ -26,6 +26,9 @@ void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm
                                 const Tile* tiles, const int* tile_count, const float* wts,
                                 const float* sg, const moe_qffn& routed, const moe_qffn& shared,
                                 uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
+void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
+                               float* z, uint16_t* xh, uint16_t* hbuf, uint16_t* y,
+                               uint16_t* res, hipStream_t st);
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st);
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st);
@@ -73,7 +76,10 @@ WsLayout ws_layout(int T) {
     L.tiles = take((size_t)max_tiles(T) * sizeof(Tile));
     L.tile_count = take(4);
     L.xh = take(t * H * 2);
-    L.h = take(t * (TOPK + 1) * I * 2);
+    // h rows: 9T for the tile-based kernels; the few-token layer indexes them
+    // (slot * T + token) with up to 1 + 8T slots
+    const size_t hrows = T <= MOE_DECODE_T ? (1 + TOPK * t) * t : (TOPK + 1) * t;
+    L.h = take(hrows * I * 2);
     L.dout = take(t * (TOPK + 1) * H * 4);
     L.total = off;
     return L;
@@ -258,6 +264,13 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
     uint16_t* hbuf = at<uint16_t>(ws, L.h);
     float* dout = at<float>(ws, L.dout);
 
+    if (path == MOE_PATH_DECODE && T <= MOE_DECODE_T) {
+        // three kernels: logits (+ shared gate logit, fp16 x) | gate/up | down+combine;
+        // the routing is recomputed inside the two expert kernels
+        launch_layer_decode_small(x, T, *layer, at<float>(ws, L.logits), sg,
+                                  at<uint16_t>(ws, L.xh), hbuf, y, res, st);
+        return launch_status();
+    }
     if (path == MOE_PATH_DECODE) {
         // four kernels: logits | select (top-8, permutation, tiles) | gate/up | down+combine
         launch_route_logits(x, T, layer->w_router, layer->router_bias, at<float>(ws, L.logits),
