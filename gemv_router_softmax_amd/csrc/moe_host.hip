@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -78,7 +80,9 @@ WsLayout ws_layout(int T) {
     L.xh = take(t * H * 2);
     // h rows: 9T for the tile-based kernels; the few-token layer indexes them
     // (slot * T + token) with up to 1 + 8T slots
-    const size_t hrows = T <= MOE_DECODE_T ? (1 + TOPK * t) * t : (TOPK + 1) * t;
+    // (kept monotone in T: beyond the few-token range it never shrinks)
+    const size_t ts = t < MOE_DECODE_T ? t : MOE_DECODE_T;
+    const size_t hrows = std::max((1 + TOPK * ts) * ts, (TOPK + 1) * t);
     L.h = take(hrows * I * 2);
     L.dout = take(t * (TOPK + 1) * H * 4);
     L.total = off;
