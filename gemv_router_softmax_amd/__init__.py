@@ -33,8 +33,8 @@ MOE_PATH_DECODE = 1
 MOE_PATH_PREFILL = 2
 
 # Every symbol include/moe.h declares.
-EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_route", "moe_permute",
-           "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
+EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_status_string", "moe_route",
+           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
            "moe_probe_read", "moe_probe_copy")
 
 
@@ -74,6 +74,8 @@ def lib() -> C.CDLL:
     vp, i32, sz = C.c_void_p, C.c_int, C.c_size_t
     L.moe_workspace_bytes.argtypes = [i32]
     L.moe_workspace_bytes.restype = sz
+    L.moe_workspace_init.argtypes = [vp, sz, vp]
+    L.moe_workspace_init.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = C.c_char_p
     L.moe_route.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -86,8 +88,9 @@ def lib() -> C.CDLL:
                                        C.POINTER(moe_options)]
     L.moe_probe_read.argtypes = [vp, sz, vp, vp]
     L.moe_probe_copy.argtypes = [vp, vp, sz, vp]
-    for fn in EXPORTS[2:]:
-        getattr(L, fn).restype = i32
+    for fn in EXPORTS:
+        if fn not in ("moe_workspace_bytes", "moe_status_string"):
+            getattr(L, fn).restype = i32
     _lib = L
     return L
 
@@ -187,9 +190,17 @@ class DeviceLayer:
                 self.w_shared_gate.numel() * 2)
 
 
-def workspace(T: int, device="cuda") -> torch.Tensor:
-    """Device workspace sized by moe_workspace_bytes(T) (allocated by torch)."""
-    return torch.empty(max(moe_workspace_bytes(T), 256), dtype=torch.uint8, device=device)
+def workspace(T: int, device="cuda", stream=None) -> torch.Tensor:
+    """Device workspace sized by moe_workspace_bytes(T) (allocated by torch)
+    and prepared with moe_workspace_init."""
+    ws = torch.empty(max(moe_workspace_bytes(T), 256), dtype=torch.uint8, device=device)
+    moe_workspace_init(ws, stream)
+    return ws
+
+
+def moe_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    wsp, wsn = _ws(ws)
+    _check("moe_workspace_init", lib().moe_workspace_init(wsp, wsn, _stream(stream)))
 
 
 def _ws(ws: torch.Tensor):

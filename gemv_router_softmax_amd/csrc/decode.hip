@@ -274,39 +274,49 @@ __global__ __launch_bounds__(256) void decode_down_combine(
 }
 
 // ---------------------------------------------------------------------
-// Few-token layer (T <= MOE_DECODE_T): three kernels, no select kernel.
-// The routing (top-8 of 256 logits per token, at most 8T active experts)
-// is recomputed inside every workgroup of the two expert kernels from the
-// logits in memory -- one 1 KB read per token and ~1 us of wave work, far
-// cheaper than a kernel boundary and its dependent loads.  Every workgroup
-// runs the same deterministic code on the same logits, so all of them
-// agree on the selection.
+// Few-token layer (T <= MOE_DECODE_T): three kernels.
+//
+//   route_logits_dec   the 256 expert logits (one wave per expert row), the
+//                      shared-gate logits and the fp16 copy of x; the LAST
+//                      router workgroup to finish (a counter in the
+//                      workspace -- no workgroup ever waits) computes every
+//                      token's top-8, the weights, the shared gate and the
+//                      active-expert list once, into a small route record,
+//                      and re-arms the counter.
+//   decode_gateup_dec  slot 0 = the shared expert (needs no routing), slot
+//                      a >= 1 = the a-th active routed expert; one read of the
+//                      record tells a workgroup its expert.
+//   decode_down_dec    every active expert for 4 output rows, combine with the
+//                      routing weights and the shared gate, residual add.
+// Ids read back from the record are clamped, so a corrupted record cannot
+// send a load outside the weights.
 
-struct BlockRoute {
+struct RouteRec {
     int ids[MOE_DECODE_T][TOPK];
     float w[MOE_DECODE_T][TOPK];
     float sg[MOE_DECODE_T];
     int active[MOE_DECODE_T * TOPK];     // active experts, ascending id
     uint32_t tmask[MOE_DECODE_T * TOPK]; // tokens that selected active[a]
-    int mark[E];
-    int scr[4];
     int nact;
 };
+constexpr int REC_WORDS = (int)(sizeof(RouteRec) / 4);
+static_assert(sizeof(RouteRec) % 4 == 0, "record is copied as words");
 
-// All T tokens' top-8 (one wave per token) and the active-expert list.
+// Top-8 of every token (one wave per token) and the active-expert list, by
+// one workgroup, into R (LDS).
 __device__ void block_route(const float* __restrict__ logits, const float* __restrict__ z,
-                            int T, BlockRoute& R) {
+                            int T, RouteRec& R, int* mark, int* scr) {
     const int tid = threadIdx.x, wave = tid >> 6;
-    R.mark[tid] = 0;
+    mark[tid] = 0;
     __syncthreads();
     for (int t = wave; t < T; t += 4) wave_top8(logits + (size_t)t * E, R.ids[t], R.w[t], nullptr);
     if (tid < T) R.sg[tid] = 1.f / (1.f + expf(-z[tid]));
     __syncthreads();
-    if (tid < T * TOPK) atomicOr((unsigned*)&R.mark[R.ids[tid >> 3][tid & 7]], 1u << (tid >> 3));
+    if (tid < T * TOPK) atomicOr((unsigned*)&mark[R.ids[tid >> 3][tid & 7]], 1u << (tid >> 3));
     __syncthreads();
-    const int mk = R.mark[tid];
+    const int mk = mark[tid];
     int na;
-    const int slot = block_excl_scan256(mk ? 1 : 0, R.scr, &na);
+    const int slot = block_excl_scan256(mk ? 1 : 0, scr, &na);
     if (mk) {
         R.active[slot] = tid;
         R.tmask[slot] = (uint32_t)mk;
@@ -317,14 +327,21 @@ __device__ void block_route(const float* __restrict__ logits, const float* __res
 
 // grid (E/4 + 1 + T): blocks < E/4: logits of 4 experts each (one wave per
 // expert row); block E/4: shared-gate logits z[t] = x[t] . w_sg; the last T
-// blocks: fp16 copy of x in chunk-slot order.
+// blocks: fp16 copy of x in chunk-slot order.  counter: zero on entry, zero
+// on exit.
 __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restrict__ x, int T,
                                                         const uint16_t* __restrict__ wr,
                                                         const float* __restrict__ bias,
                                                         const uint16_t* __restrict__ wsg,
                                                         float* __restrict__ logits,
                                                         float* __restrict__ z,
-                                                        uint16_t* __restrict__ xh) {
+                                                        uint16_t* __restrict__ xh,
+                                                        unsigned* __restrict__ counter,
+                                                        RouteRec* __restrict__ rec) {
+    __shared__ RouteRec R;
+    __shared__ int mark[E];
+    __shared__ int scr[4];
+    __shared__ int last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
     if (b > E / 4) {                      // x -> fp16, token b - E/4 - 1
@@ -334,63 +351,76 @@ __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restri
             bf16x8_to_f16_slots(reinterpret_cast<const uint4v*>(x)[ci]);
         return;
     }
-    const uint16_t* row = b < E / 4 ? wr + (size_t)(b * 4 + wave) * H : wsg;
-    if (b == E / 4 && wave != 0) return;
-    const uint4v* wrow = reinterpret_cast<const uint4v*>(row) + lane * 4;
-    const uint4v w0 = wrow[0], w1 = wrow[1], w2 = wrow[2], w3 = wrow[3];
-    uint4v xv[MOE_DECODE_T][4];
+    if (b < E / 4 || wave == 0) {
+        const uint16_t* row = b < E / 4 ? wr + (size_t)(b * 4 + wave) * H : wsg;
+        const uint4v* wrow = reinterpret_cast<const uint4v*>(row) + lane * 4;
+        const uint4v w0 = wrow[0], w1 = wrow[1], w2 = wrow[2], w3 = wrow[3];
+        uint4v xv[MOE_DECODE_T][4];
 #pragma unroll
-    for (int t = 0; t < MOE_DECODE_T; ++t) {
-        if (t < T) {
-            const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
+        for (int t = 0; t < MOE_DECODE_T; ++t) {
+            if (t < T) {
+                const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) xv[t][c] = xr[c];
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < MOE_DECODE_T; ++t) {
-        if (t < T) {
-            float s = 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint4v wv = c == 0 ? w0 : (c == 1 ? w1 : (c == 2 ? w2 : w3));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t a = xv[t][c][i], bb = wv[i];
-                    s = fmaf(bf16_to_f32(a & 0xFFFFu), bf16_to_f32(bb & 0xFFFFu), s);
-                    s = fmaf(bf16_to_f32(a >> 16), bf16_to_f32(bb >> 16), s);
-                }
-            }
-            s = wave_sum(s);
-            if (lane == 0) {
-                if (b < E / 4) {
-                    const int e = b * 4 + wave;
-                    logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
-                } else {
-                    z[t] = s;
-                }
+                for (int c = 0; c < 4; ++c) xv[t][c] = xr[c];
             }
         }
+#pragma unroll
+        for (int t = 0; t < MOE_DECODE_T; ++t) {
+            if (t < T) {
+                float s = 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint4v wv = c == 0 ? w0 : (c == 1 ? w1 : (c == 2 ? w2 : w3));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t a = xv[t][c][i], bb = wv[i];
+                        s = fmaf(bf16_to_f32(a & 0xFFFFu), bf16_to_f32(bb & 0xFFFFu), s);
+                        s = fmaf(bf16_to_f32(a >> 16), bf16_to_f32(bb >> 16), s);
+                    }
+                }
+                s = wave_sum(s);
+                if (lane == 0) {
+                    if (b < E / 4) {
+                        const int e = b * 4 + wave;
+                        logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
+                    } else {
+                        z[t] = s;
+                    }
+                }
+            }
+        }
     }
+    // last of the E/4 + 1 writer workgroups does the routing
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        last = atomicAdd(counter, 1u) == (unsigned)(E / 4);
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    block_route(logits, z, T, R, mark, scr);
+    const int* src = reinterpret_cast<const int*>(&R);
+    int* dst = reinterpret_cast<int*>(rec);
+    for (int i = threadIdx.x; i < REC_WORDS; i += 256) dst[i] = src[i];
+    if (threadIdx.x == 0) atomicExch(counter, 0u);
 }
 
-// grid (1 + 8T, I/16).  Slot 0 is the shared expert (no routing needed, so
-// its workgroups start streaming at once); slot a >= 1 is the a-th active
-// routed expert.  h rows are indexed (slot * T + t), fp16, chunk-slot order.
+// grid (1 + 8T, I/16).  h rows are indexed (slot * T + t), fp16, chunk-slot
+// order.
 __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restrict__ xh, int T,
-                                                         const float* __restrict__ logits,
-                                                         const float* __restrict__ z,
+                                                         const RouteRec* __restrict__ rec,
                                                          moe_qffn routed, moe_qffn shared,
                                                          uint16_t* __restrict__ hout) {
-    __shared__ BlockRoute R;
     const int slot = blockIdx.x;
     int e = 0;
-    uint32_t mask = (1u << T) - 1u;
+    const uint32_t tall = (1u << T) - 1u;
+    uint32_t mask = tall;
     if (slot > 0) {
-        block_route(logits, z, T, R);
-        if (slot - 1 >= R.nact) return;
-        e = R.active[slot - 1];
-        mask = R.tmask[slot - 1];
+        const int nact = min(max(rec->nact, 0), TOPK * T);
+        if (slot - 1 >= nact) return;
+        e = min(max(rec->active[slot - 1], 0), E - 1);
+        mask = rec->tmask[slot - 1] & tall;
     }
     const moe_qffn q = slot == 0 ? shared : routed;
     const int lane = threadIdx.x & 63;
@@ -445,19 +475,24 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
 // takes slots w, w+4, ...), combine with the routing weights and the shared
 // gate, residual add.  Fixed summation order: deterministic.
 __global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restrict__ hin, int T,
-                                                       const float* __restrict__ logits,
-                                                       const float* __restrict__ z,
+                                                       const RouteRec* __restrict__ rec,
                                                        moe_qffn routed, moe_qffn shared,
                                                        uint16_t* __restrict__ y,
                                                        const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ res) {
-    __shared__ BlockRoute R;
+    __shared__ RouteRec R;
     __shared__ float yacc[4][MOE_DECODE_T][4];
-    block_route(logits, z, T, R);
+    {
+        const int* src = reinterpret_cast<const int*>(rec);
+        int* dst = reinterpret_cast<int*>(&R);
+        for (int i = threadIdx.x; i < REC_WORDS; i += 256) dst[i] = src[i];
+    }
+    __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane >> 4, c = lane & 15;
     const int m = blockIdx.x * 4 + r;
-    const int nslots = R.nact + 1;
+    const uint32_t tall = (1u << T) - 1u;
+    const int nslots = min(max(R.nact, 0), TOPK * T) + 1;
     float acc[MOE_DECODE_T];
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_T; ++t) acc[t] = 0.f;
@@ -467,7 +502,7 @@ __global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restric
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int a = a0 + 4 * k < nslots ? a0 + 4 * k : a0;
-            const int e = a == 0 ? 0 : R.active[a - 1];
+            const int e = a == 0 ? 0 : min(max(R.active[a - 1], 0), E - 1);
             const moe_qffn& q = a == 0 ? shared : routed;
             const size_t row = (size_t)e * H + m;
             dw[k] = reinterpret_cast<const uint4v*>(q.down_q + row * (I / 8))[c];
@@ -479,7 +514,7 @@ __global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restric
             const int a = a0 + 4 * k;
             if (a >= nslots) break;
             const int e = a == 0 ? -1 : R.active[a - 1];
-            const uint32_t mask = a == 0 ? (1u << T) - 1u : R.tmask[a - 1];
+            const uint32_t mask = (a == 0 ? tall : R.tmask[a - 1]) & tall;
             for (int t = 0; t < T; ++t) {
                 if (!((mask >> t) & 1u)) continue;
                 float coef = R.sg[t];
@@ -526,15 +561,29 @@ __global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restric
     }
 }
 
+size_t route_rec_bytes() { return sizeof(RouteRec); }
+
 void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
-                               float* z, uint16_t* xh, uint16_t* hbuf, uint16_t* y,
-                               uint16_t* res, hipStream_t st) {
+                               float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
+                               void* rec, uint16_t* y, uint16_t* res, hipStream_t st) {
+    RouteRec* R = static_cast<RouteRec*>(rec);
     hipLaunchKernelGGL(route_logits_dec, dim3(E / 4 + 1 + T), dim3(256), 0, st, x, T, L.w_router,
-                       L.router_bias, L.w_shared_gate, logits, z, xh);
-    hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T,
-                       logits, z, L.routed, L.shared, hbuf);
-    hipLaunchKernelGGL(decode_down_dec, dim3(H / 4), dim3(256), 0, st, hbuf, T, logits, z,
-                       L.routed, L.shared, y, x, res);
+                       L.router_bias, L.w_shared_gate, logits, z, xh, counter, R);
+    hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T, R,
+                       L.routed, L.shared, hbuf);
+    hipLaunchKernelGGL(decode_down_dec, dim3(H / 4), dim3(256), 0, st, hbuf, T, R, L.routed,
+                       L.shared, y, x, res);
+}
+
+// Zero the workspace's synchronisation words (a fill kernel, not a memset,
+// so the call can be captured in a graph).
+__global__ void zero_words(unsigned* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+void launch_zero_words(unsigned* p, int n, hipStream_t st) {
+    hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
 }
 
 void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,

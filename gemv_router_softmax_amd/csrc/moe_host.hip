@@ -29,8 +29,10 @@ void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm
                                 const float* sg, const moe_qffn& routed, const moe_qffn& shared,
                                 uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
-                               float* z, uint16_t* xh, uint16_t* hbuf, uint16_t* y,
-                               uint16_t* res, hipStream_t st);
+                               float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
+                               void* rec, uint16_t* y, uint16_t* res, hipStream_t st);
+size_t route_rec_bytes();
+void launch_zero_words(unsigned* p, int n, hipStream_t st);
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st);
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st);
@@ -51,9 +53,11 @@ void launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t st)
 
 namespace {
 
+constexpr int SYNC_WORDS = 64;
+
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct WsLayout {
-    size_t logits, ids, wts, sg, counts, offsets, perm, inv, chunk_counts, tiles, tile_count, xh,
+    size_t sync, rec, logits, ids, wts, sg, counts, offsets, perm, inv, chunk_counts, tiles, tile_count, xh,
         h, dout, total;
 };
 
@@ -66,6 +70,8 @@ WsLayout ws_layout(int T) {
         return o;
     };
     const size_t t = (size_t)T;
+    L.sync = take(SYNC_WORDS * 4);      // counters: zero before first use, zero after every call
+    L.rec = take(route_rec_bytes());
     L.logits = take(t * E * 4);
     L.ids = take(t * TOPK * 4);
     L.wts = take(t * TOPK * 4);
@@ -272,7 +278,8 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
         // three kernels: logits (+ shared gate logit, fp16 x) | gate/up | down+combine;
         // the routing is recomputed inside the two expert kernels
         launch_layer_decode_small(x, T, *layer, at<float>(ws, L.logits), sg,
-                                  at<uint16_t>(ws, L.xh), hbuf, y, res, st);
+                                  at<uint16_t>(ws, L.xh), hbuf, at<unsigned>(ws, L.sync),
+                                  at<char>(ws, L.rec), y, res, st);
         return launch_status();
     }
     if (path == MOE_PATH_DECODE) {
@@ -301,6 +308,14 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
 int moe_layer_forward(const uint16_t* x, int T, const moe_layer* layer, uint16_t* y, void* ws,
                       size_t ws_bytes, void* stream) {
     return moe_layer_forward_ex(x, T, layer, y, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws) return MOE_ERR_INVALID_ARG;
+    if (!a16(ws)) return MOE_ERR_ALIGN;
+    if (ws_bytes < moe_workspace_bytes(0)) return MOE_ERR_WORKSPACE;
+    launch_zero_words(at<unsigned>(ws, ws_layout(0).sync), SYNC_WORDS, (hipStream_t)stream);
+    return launch_status();
 }
 
 int moe_probe_read(const void* src, size_t bytes, float* sink, void* stream) {

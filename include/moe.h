@@ -43,9 +43,12 @@
  *   - On an error status nothing has been enqueued.  A launch failure is
  *     reported as MOE_ERR_HIP.
  *   - T == 0 is a no-op returning MOE_OK.  T may not exceed MOE_T_MAX.
- *   - Calls that share a workspace must be ordered on one stream; calls on
- *     different streams need different workspaces.  Everything is
- *     deterministic: the same inputs give bit-identical outputs.
+ *   - The workspace (moe_workspace_bytes(T) bytes, caller owned) must be
+ *     prepared once with moe_workspace_init (or be zero-filled) before its
+ *     first use; every call leaves it ready for the next one.  Calls that
+ *     share a workspace must be ordered on one stream; calls on different
+ *     streams need different workspaces.  Everything is deterministic: the
+ *     same inputs give bit-identical outputs.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -108,6 +111,12 @@ typedef struct {
 /* Workspace bytes sufficient for ANY call below with this T (monotone in T).
  * Returns 0 for T < 0 or T > MOE_T_MAX. */
 size_t moe_workspace_bytes(int T);
+
+/* Prepares a workspace for its first use (clears the library's
+ * synchronisation words at its start; the rest is scratch).  Enqueues one
+ * small fill kernel on `stream` (capturable in a graph).  ws_bytes must be
+ * at least moe_workspace_bytes(0). */
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Human-readable name of a status code. */
 const char *moe_status_string(int status);

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -139,6 +139,12 @@ def test_layer_forward_validation(L):
     lz = _layer()
     lz.w_router = None
     assert L.moe_layer_forward(A, 64, C.byref(lz), A, A, big, None) == INVALID
+
+
+def test_workspace_init_validation(L):
+    assert L.moe_workspace_init(None, 1 << 20, None) == INVALID
+    assert L.moe_workspace_init(MIS, 1 << 20, None) == ALIGN
+    assert L.moe_workspace_init(A, 8, None) == WS
 
 
 def test_probe_validation(L):

@@ -120,3 +120,19 @@ def test_graph_capture_chain(gpu):
         # unrelated eager work between replays
         moe.moe_layer_forward(xs[(s + 1) % 4], D[0], y, ws)
         torch.cuda.synchronize()
+
+
+def test_workspace_init_after_garbage(gpu):
+    """A workspace full of garbage, prepared with moe_workspace_init, gives
+    the same result as a fresh one, on every one of several calls."""
+    D = P.dev_layer(0, 0)
+    x = moe.to_device_bits(synth.make_x(4, seed=9))
+    want = torch.empty((4, 2048), dtype=torch.int16, device="cuda")
+    moe.moe_layer_forward(x, D, want, moe.workspace(4))
+    ws = torch.full((moe.moe_workspace_bytes(4),), 0xA7, dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    for _ in range(3):
+        y = torch.empty_like(want)
+        moe.moe_layer_forward(x, D, y, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, want)
