@@ -144,28 +144,32 @@ __device__ inline void wave_top8(const float* __restrict__ lg, int32_t* __restri
         sv[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vi), l));
         se[k] = 4 * l + i;
     }
-    // sort descending by value, ascending expert on ties (8 elements, uniform)
-#pragma unroll
-    for (int a = 1; a < TOPK; ++a) {
-#pragma unroll
-        for (int b = a; b > 0; --b) {
-            const bool sw = sv[b] > sv[b - 1] || (sv[b] == sv[b - 1] && se[b] < se[b - 1]);
-            if (sw) {
-                const float tv = sv[b]; sv[b] = sv[b - 1]; sv[b - 1] = tv;
-                const int te = se[b]; se[b] = se[b - 1]; se[b - 1] = te;
-            }
-        }
-    }
-    const float m0 = sv[0];
-    float ex[TOPK], s = 0.f;
-#pragma unroll
-    for (int k = 0; k < TOPK; ++k) { ex[k] = expf(sv[k] - m0); s += ex[k]; }
+    // order: rank of element k = #elements before it (larger value, or equal
+    // value and lower expert index); ranks are a permutation of 0..7
+    int rk[TOPK];
 #pragma unroll
     for (int k = 0; k < TOPK; ++k) {
-        if (lane == k) {
-            ids_out[k] = se[k];
-            w_out[k] = ex[k] / s;
-            if (ids_lds) ids_lds[k] = se[k];
+        int rnk = 0;
+#pragma unroll
+        for (int j = 0; j < TOPK; ++j)
+            rnk += (sv[j] > sv[k] || (sv[j] == sv[k] && se[j] < se[k])) ? 1 : 0;
+        rk[k] = rnk;
+    }
+    float vmax = sv[0];
+#pragma unroll
+    for (int k = 1; k < TOPK; ++k) vmax = fmaxf(vmax, sv[k]);
+    // softmax over all experts renormalised over the selected eight: the
+    // full denominator cancels, leaving exp(l - l_max) / sum_sel exp(l - l_max)
+    float ex[TOPK], s = 0.f;
+#pragma unroll
+    for (int k = 0; k < TOPK; ++k) { ex[k] = expf(sv[k] - vmax); s += ex[k]; }
+    const float inv = 1.f / s;
+#pragma unroll
+    for (int k = 0; k < TOPK; ++k) {
+        if (lane == rk[k]) {
+            ids_out[lane] = se[k];
+            w_out[lane] = ex[k] * inv;
+            if (ids_lds) ids_lds[lane] = se[k];
         }
     }
 }

@@ -325,8 +325,10 @@ __device__ void block_route(const float* __restrict__ logits, const float* __res
     __syncthreads();
 }
 
-// grid (E/4 + 1 + T): blocks < E/4: logits of 4 experts each (one wave per
-// expert row); block E/4: shared-gate logits z[t] = x[t] . w_sg; the last T
+constexpr int NRB = 16;   // router workgroups (16 experts each, 4 per wave)
+
+// grid (NRB + 1 + T): blocks < NRB: logits of 16 experts each (4 expert rows
+// per wave); block NRB: shared-gate logits z[t] = x[t] . w_sg; the last T
 // blocks: fp16 copy of x in chunk-slot order.  counter: zero on entry, zero
 // on exit.
 __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restrict__ x, int T,
@@ -344,17 +346,14 @@ __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restri
     __shared__ int last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
-    if (b > E / 4) {                      // x -> fp16, token b - E/4 - 1
-        const int t = b - E / 4 - 1;
+    if (b > NRB) {                        // x -> fp16, token b - NRB - 1
+        const int t = b - NRB - 1;
         const size_t ci = (size_t)t * (H / 8) + threadIdx.x;
         reinterpret_cast<uint4v*>(xh)[ci] =
             bf16x8_to_f16_slots(reinterpret_cast<const uint4v*>(x)[ci]);
         return;
     }
-    if (b < E / 4 || wave == 0) {
-        const uint16_t* row = b < E / 4 ? wr + (size_t)(b * 4 + wave) * H : wsg;
-        const uint4v* wrow = reinterpret_cast<const uint4v*>(row) + lane * 4;
-        const uint4v w0 = wrow[0], w1 = wrow[1], w2 = wrow[2], w3 = wrow[3];
+    if (b < NRB || wave == 0) {
         uint4v xv[MOE_DECODE_T][4];
 #pragma unroll
         for (int t = 0; t < MOE_DECODE_T; ++t) {
@@ -364,37 +363,52 @@ __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restri
                 for (int c = 0; c < 4; ++c) xv[t][c] = xr[c];
             }
         }
+        const int nrows = b < NRB ? E / NRB / 4 : 1;    // rows per wave
+        uint4v wv[E / NRB / 4][4];
 #pragma unroll
-        for (int t = 0; t < MOE_DECODE_T; ++t) {
-            if (t < T) {
-                float s = 0.f;
+        for (int k = 0; k < E / NRB / 4; ++k) {
+            if (k < nrows) {
+                const uint16_t* row =
+                    b < NRB ? wr + (size_t)(b * (E / NRB) + wave * (E / NRB / 4) + k) * H : wsg;
+                const uint4v* wrow = reinterpret_cast<const uint4v*>(row) + lane * 4;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint4v wv = c == 0 ? w0 : (c == 1 ? w1 : (c == 2 ? w2 : w3));
+                for (int c = 0; c < 4; ++c) wv[k][c] = wrow[c];
+            }
+        }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t a = xv[t][c][i], bb = wv[i];
-                        s = fmaf(bf16_to_f32(a & 0xFFFFu), bf16_to_f32(bb & 0xFFFFu), s);
-                        s = fmaf(bf16_to_f32(a >> 16), bf16_to_f32(bb >> 16), s);
+        for (int k = 0; k < E / NRB / 4; ++k) {
+            if (k >= nrows) break;
+#pragma unroll
+            for (int t = 0; t < MOE_DECODE_T; ++t) {
+                if (t < T) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t a = xv[t][c][i], bb = wv[k][c][i];
+                            s = fmaf(bf16_to_f32(a & 0xFFFFu), bf16_to_f32(bb & 0xFFFFu), s);
+                            s = fmaf(bf16_to_f32(a >> 16), bf16_to_f32(bb >> 16), s);
+                        }
                     }
-                }
-                s = wave_sum(s);
-                if (lane == 0) {
-                    if (b < E / 4) {
-                        const int e = b * 4 + wave;
-                        logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
-                    } else {
-                        z[t] = s;
+                    s = wave_sum(s);
+                    if (lane == 0) {
+                        if (b < NRB) {
+                            const int e = b * (E / NRB) + wave * (E / NRB / 4) + k;
+                            logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
+                        } else {
+                            z[t] = s;
+                        }
                     }
                 }
             }
         }
     }
-    // last of the E/4 + 1 writer workgroups does the routing
+    // last of the NRB + 1 writer workgroups does the routing
     __syncthreads();
     if (threadIdx.x == 0) {
         __threadfence();
-        last = atomicAdd(counter, 1u) == (unsigned)(E / 4);
+        last = atomicAdd(counter, 1u) == (unsigned)NRB;
     }
     __syncthreads();
     if (!last) return;
@@ -567,7 +581,7 @@ void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, flo
                                float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
                                void* rec, uint16_t* y, uint16_t* res, hipStream_t st) {
     RouteRec* R = static_cast<RouteRec*>(rec);
-    hipLaunchKernelGGL(route_logits_dec, dim3(E / 4 + 1 + T), dim3(256), 0, st, x, T, L.w_router,
+    hipLaunchKernelGGL(route_logits_dec, dim3(NRB + 1 + T), dim3(256), 0, st, x, T, L.w_router,
                        L.router_bias, L.w_shared_gate, logits, z, xh, counter, R);
     hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T, R,
                        L.routed, L.shared, hbuf);
