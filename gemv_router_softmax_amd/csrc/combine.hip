@@ -48,6 +48,57 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
 }
 
+// Prefill combine: y[t] = bf16( sum_j d16[inv[8t+j]] + d16[8T+t] ), the rows
+// already scaled by their routing weight / shared gate (fp16), summed in fp32
+// in a fixed order; optionally res = bf16(x + y).  grid (T, H/2048), one
+// thread per 8 columns.
+__global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __restrict__ d16,
+                                                          const int32_t* __restrict__ inv, int T,
+                                                          uint16_t* __restrict__ y,
+                                                          const uint16_t* __restrict__ x,
+                                                          uint16_t* __restrict__ res) {
+    const int t = blockIdx.x;
+    const int m = threadIdx.x * 8;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+    int rows[TOPK + 1];
+#pragma unroll
+    for (int jj = 0; jj < TOPK; ++jj) rows[jj] = inv[(size_t)t * TOPK + jj];
+    rows[TOPK] = TOPK * T + t;
+#pragma unroll
+    for (int jj = 0; jj <= TOPK; ++jj) {
+        const int p = rows[jj];
+        if (p < 0 || p >= (TOPK + 1) * T) continue;
+        const uint4v v = *reinterpret_cast<const uint4v*>(d16 + (size_t)p * H + m);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t w = v[k >> 1];
+            const uint16_t hb = (uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFFu));
+            acc[k] += (float)__builtin_bit_cast(_Float16, hb);
+        }
+    }
+    uint4v yo, ro;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t y0 = f32_to_bf16(acc[2 * i]), y1 = f32_to_bf16(acc[2 * i + 1]);
+        yo[i] = y0 | (y1 << 16);
+        if (res) {
+            const uint32_t xv = reinterpret_cast<const uint32_t*>(x + (size_t)t * H + m)[i];
+            const uint32_t r0 = f32_to_bf16(bf16_to_f32(xv & 0xFFFFu) + bf16_to_f32(y0));
+            const uint32_t r1 = f32_to_bf16(bf16_to_f32(xv >> 16) + bf16_to_f32(y1));
+            ro[i] = r0 | (r1 << 16);
+        }
+    }
+    *reinterpret_cast<uint4v*>(y + (size_t)t * H + m) = yo;
+    if (res) *reinterpret_cast<uint4v*>(res + (size_t)t * H + m) = ro;
+}
+
+void launch_combine_f16(const uint16_t* d16, const int32_t* inv, int T, uint16_t* y,
+                        const uint16_t* x, uint16_t* res, hipStream_t st) {
+    hipLaunchKernelGGL(combine_f16_kernel, dim3(T), dim3(256), 0, st, d16, inv, T, y, x, res);
+}
+
 void launch_combine(const float* out, const int32_t* inv, const float* wts, const float* sg, int T,
                     uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st) {
     hipLaunchKernelGGL(combine_kernel, dim3(T, H / 1024), dim3(256), 0, st, out, inv, wts, sg, T,

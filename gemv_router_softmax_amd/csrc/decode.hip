@@ -325,7 +325,7 @@ __device__ void block_route(const float* __restrict__ logits, const float* __res
     __syncthreads();
 }
 
-constexpr int NRB = 16;   // router workgroups (16 experts each, 4 per wave)
+constexpr int NRB = 64;   // router workgroups (4 experts each, one per wave)
 
 // grid (NRB + 1 + T): blocks < NRB: logits of 16 experts each (4 expert rows
 // per wave); block NRB: shared-gate logits z[t] = x[t] . w_sg; the last T

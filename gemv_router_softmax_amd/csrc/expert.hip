@@ -13,16 +13,7 @@
 //                  group scale/bias applied once per lane; writes the fp32
 //                  expert rows of the split expert-FFN call.
 //
-// Prefill (grouped GEMM on MFMA):
-//   expert_mfma<2048, true>   gate/up: tile rows x 128 columns of gate and up
-//   expert_mfma<512, false>   down:    tile rows x 256 output columns
-//   A (activations) is staged in LDS per 128-wide K chunk, already fp16 and
-//   in the chunk-slot order the dequantiser produces.  Each wave owns 64
-//   weight columns for all tile rows; its lanes load 16 B of codes per
-//   column per K chunk straight into registers, rebuild fp16 weights
-//   w = q*s + b with packed half arithmetic (one rounding), and feed
-//   v_mfma_f32_16x16x32_f16 with fp32 accumulation.  SwiGLU and the bf16
-//   rounding of h are fused into the gate/up epilogue.
+// Prefill (grouped GEMM on MFMA): expert_gemm below.
 #include "common.hpp"
 
 namespace moe {
@@ -99,19 +90,46 @@ __device__ __forceinline__ half8 dequant8(uint32_t w, half2v s2, half2v b2) {
     return r;
 }
 
-template <int KDIM, bool GATEUP>
-__global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict__ ain, int T,
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+enum GemmMode { GM_GATEUP = 0, GM_DOWN_F32 = 1, GM_DOWN_F16W = 2 };
+
+// Grouped expert GEMM on v_mfma_f32_16x16x32_f16.
+//   workgroup = one row tile (<= 128 rows of one expert) x 128 gate+128 up
+//   columns (GM_GATEUP, K = 2048) or x 256 output columns (down, K = 512);
+//   4 waves, each owning 64 weight columns for ALL rows of the tile, so every
+//   code word is dequantised once per tile.
+//   A: 128-wide K chunks of the activation rows (gathered by token for
+//   gate/up) go straight from global memory into LDS with
+//   global_load_lds_dwordx4, double buffered (2 x 32 KB); the 16 B pieces of
+//   a row are XOR-swizzled by (row & 15) so the 16 rows an MFMA operand reads
+//   hit 16 distinct LDS bank groups.
+//   B: each lane loads 16 B of codes per column per chunk (one chunk ahead)
+//   and rebuilds fp16 weights in registers (dequant8).
+//   Epilogues: GM_GATEUP -> h = bf16(silu(g) u) as fp16 in chunk-slot order;
+//   GM_DOWN_F32 -> fp32 rows (split expert-FFN call); GM_DOWN_F16W -> fp16
+//   rows pre-multiplied by the routing weight (or the shared gate) for the
+//   fused combine.
+template <int KDIM, int MODE>
+__global__ __launch_bounds__(256, 2) void expert_gemm(const uint16_t* __restrict__ ain, int T,
                                                       const int32_t* __restrict__ perm,
                                                       const Tile* __restrict__ tiles,
                                                       const int* __restrict__ tile_count,
                                                       moe_qffn routed, moe_qffn shared,
                                                       uint16_t* __restrict__ hout,
-                                                      float* __restrict__ dout) {
+                                                      float* __restrict__ dout32,
+                                                      uint16_t* __restrict__ dout16,
+                                                      const float* __restrict__ wts,
+                                                      const float* __restrict__ sg) {
+    constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NCH = KDIM / 128;              // K chunks
     constexpr int WPR = KDIM / 8;                // code words per weight row
     constexpr int SPR = KDIM / G;                // groups per weight row
     constexpr int ROWS_W = GATEUP ? I : H;       // weight rows per expert
-    __shared__ __attribute__((aligned(16))) uint16_t As[MT_ROWS * AST];
+    constexpr int CHB = 128 * 2;                 // bytes per A row per chunk
+    __shared__ __attribute__((aligned(16))) uint8_t As[2][MT_ROWS * CHB];
+    __shared__ float coef[MT_ROWS];
 
     if ((int)blockIdx.x >= *tile_count) return;
     const Tile tl = tiles[blockIdx.x];
@@ -122,7 +140,7 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
     const int r = lane & 15, j = lane >> 4;
     const int nr = tl.nrows, n_mt = (nr + 15) >> 4;
 
-    // This lane's weight row in each of the wave's four 16-column tiles.
+    // ---- B: this lane's weight row in each of the wave's four 16-column tiles
     const uint32_t* wq[4];
     const uint16_t* wsc[4];
     const uint16_t* wbi[4];
@@ -148,18 +166,31 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
         wbi[nt] = bb + row * SPR + (j >> 1);
     }
 
-    // A rows this thread stages: row (tid>>4) + 16 i, 16-byte column tid&15.
-    const uint16_t* asrc[8];
-    bool aok[8];
+    // ---- A: byte offsets of the 8 pieces this lane moves per chunk.
+    // Load instruction i of wave w fills tile rows w*32 + 4i .. +3 (1 KB);
+    // lane -> row w*32 + 4i + (lane >> 4), LDS slot (lane & 15), holding the
+    // row's piece (lane & 15) ^ (row & 15).
+    uint32_t aoff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int row = (tid >> 4) + 16 * i;
-        aok[i] = row < nr;
-        const int rr = aok[i] ? row : 0;
-        if (GATEUP)
-            asrc[i] = ain + (size_t)row_token(tl.row0 + rr, T, perm) * H + (tid & 15) * 8;
-        else
-            asrc[i] = ain + (size_t)(tl.row0 + rr) * I + (tid & 15) * 8;
+        const int row = wave * 32 + i * 4 + (lane >> 4);
+        const int rr = row < nr ? row : 0;
+        const int src = GATEUP ? row_token(tl.row0 + rr, T, perm) : tl.row0 + rr;
+        aoff[i] = (uint32_t)src * (uint32_t)(KDIM * 2) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+    }
+    const char* abase = reinterpret_cast<const char*>(ain);
+    auto issue_a = [&](int kc, int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (gbl_ptr_t)(abase + aoff[i] + kc * CHB),
+                (lds_ptr_t)(&As[buf][(wave * 32 + i * 4) * CHB]), 16, 0, 0);
+    };
+
+    if (MODE == GM_DOWN_F16W && tid < nr) {
+        const int p = tl.row0 + tid;
+        if (p < TOPK * T) coef[tid] = wts[min(max(perm[p], 0), TOPK * T - 1)];
+        else coef[tid] = sg[p - TOPK * T];
     }
 
     float4v acc[8][4];
@@ -176,6 +207,9 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
         bs[nt] = splat_h(wsc[nt][0]);
         bb[nt] = splat_h(wbi[nt][0]);
     }
+    issue_a(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
     for (int kc = 0; kc < NCH; ++kc) {
         uint4v cw[4];
@@ -183,6 +217,7 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) { cw[nt] = bw[nt]; cs[nt] = bs[nt]; cb[nt] = bb[nt]; }
         if (kc + 1 < NCH) {
+            issue_a(kc + 1, (kc + 1) & 1);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 bw[nt] = *reinterpret_cast<const uint4v*>(wq[nt] + (kc + 1) * 16);
@@ -190,14 +225,7 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
                 bb[nt] = splat_h(wbi[nt][(kc + 1) * 2]);
             }
         }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint4v v = (uint4v){0u, 0u, 0u, 0u};
-            if (aok[i]) v = *reinterpret_cast<const uint4v*>(asrc[i] + kc * 128);
-            *reinterpret_cast<uint4v*>(&As[((tid >> 4) + 16 * i) * AST + (tid & 15) * 8]) = v;
-        }
-        __syncthreads();
+        const uint8_t* Ab = As[kc & 1];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             half8 bf[4];
@@ -206,8 +234,9 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
                 if (mt < n_mt) {
-                    const half8 a =
-                        *reinterpret_cast<const half8*>(&As[(mt * 16 + r) * AST + 32 * j + 8 * s]);
+                    const int row = mt * 16 + r;
+                    const half8 a = *reinterpret_cast<const half8*>(
+                        &Ab[row * CHB + 16 * ((4 * j + s) ^ r)]);
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
                         acc[mt][nt] =
@@ -215,12 +244,15 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
                 }
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 
     if (GATEUP) {
-        // h = bf16(silu(g) * u), stored as fp16 (exact) in chunk-slot order so
-        // the down kernel can stage it without conversion.
-        __syncthreads();
+        // h = bf16(silu(g) * u) stored as fp16 (exact) in chunk-slot order,
+        // staged through LDS for 16-byte stores.
+        uint16_t* Hs = reinterpret_cast<uint16_t*>(As[0]);    // [128][136] halves
+        constexpr int HST = 136;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             if (mt < n_mt) {
@@ -231,9 +263,9 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
                         const int row = mt * 16 + 4 * j + i;
                         const int col = wave * 32 + nt * 16 + r;
                         const float g = acc[mt][nt][i], u = acc[mt][nt + 2][i];
-                        const float hv = (g / (1.f + expf(-g))) * u;
+                        const float hv = (g / (1.f + __expf(-g))) * u;
                         const _Float16 hh = (_Float16)bf16_to_f32(f32_to_bf16(hv));
-                        As[row * AST + (col & ~7) + chunk_slot(col & 7)] =
+                        Hs[row * HST + (col & ~7) + chunk_slot(col & 7)] =
                             __builtin_bit_cast(uint16_t, hh);
                     }
                 }
@@ -243,9 +275,9 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
         for (int c = tid; c < nr * 16; c += 256) {
             const int row = c >> 4, col = (c & 15) * 8;
             *reinterpret_cast<uint4v*>(hout + (size_t)(tl.row0 + row) * I + blockIdx.y * 128 + col) =
-                *reinterpret_cast<const uint4v*>(&As[row * AST + col]);
+                *reinterpret_cast<const uint4v*>(&Hs[row * HST + col]);
         }
-    } else {
+    } else if (MODE == GM_DOWN_F32) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             if (mt < n_mt) {
@@ -255,11 +287,37 @@ __global__ __launch_bounds__(256, 1) void expert_mfma(const uint16_t* __restrict
                     for (int i = 0; i < 4; ++i) {
                         const int row = mt * 16 + 4 * j + i;
                         if (row < nr)
-                            dout[(size_t)(tl.row0 + row) * H + blockIdx.y * 256 + wave * 64 +
-                                 nt * 16 + r] = acc[mt][nt][i];
+                            dout32[(size_t)(tl.row0 + row) * H + blockIdx.y * 256 + wave * 64 +
+                                   nt * 16 + r] = acc[mt][nt][i];
                     }
                 }
             }
+        }
+    } else {
+        // fp16 rows of coef * d, staged through LDS ([128][264] halves) for
+        // 16-byte stores
+        uint16_t* Ds = reinterpret_cast<uint16_t*>(As[0]);
+        constexpr int DST = 264;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            if (mt < n_mt) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = mt * 16 + 4 * j + i;
+                        const int col = wave * 64 + nt * 16 + r;
+                        const float v = row < nr ? coef[row] * acc[mt][nt][i] : 0.f;
+                        Ds[row * DST + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < nr * 32; c += 256) {
+            const int row = c >> 5, col = (c & 31) * 8;
+            *reinterpret_cast<uint4v*>(dout16 + (size_t)(tl.row0 + row) * H + blockIdx.y * 256 + col) =
+                *reinterpret_cast<const uint4v*>(&Ds[row * DST + col]);
         }
     }
 }
@@ -295,10 +353,30 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
     const size_t chunks = (size_t)T * (H / 8);
     hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
                        xh);
-    hipLaunchKernelGGL((expert_mfma<H, true>), dim3(max_tiles, I / 128), dim3(256), 0, st, xh, T,
-                       perm, tiles, tile_count, routed, shared, hbuf, (float*)nullptr);
-    hipLaunchKernelGGL((expert_mfma<I, false>), dim3(max_tiles, H / 256), dim3(256), 0, st, hbuf,
-                       T, perm, tiles, tile_count, routed, shared, (uint16_t*)nullptr, dout);
+    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(max_tiles, I / 128), dim3(256), 0, st,
+                       xh, T, perm, tiles, tile_count, routed, shared, hbuf, (float*)nullptr,
+                       (uint16_t*)nullptr, (const float*)nullptr, (const float*)nullptr);
+    hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F32>), dim3(max_tiles, H / 256), dim3(256), 0, st,
+                       hbuf, T, perm, tiles, tile_count, routed, shared, (uint16_t*)nullptr, dout,
+                       (uint16_t*)nullptr, (const float*)nullptr, (const float*)nullptr);
+}
+
+// Whole-layer prefill expert part: gate/up, then down writing fp16 rows of
+// (routing weight or shared gate) * d, summed per token by combine_f16.
+void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+                                 const int* tile_count, int max_tiles, const moe_qffn& routed,
+                                 const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf,
+                                 uint16_t* d16, const float* wts, const float* sg,
+                                 hipStream_t st) {
+    const size_t chunks = (size_t)T * (H / 8);
+    hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
+                       xh);
+    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(max_tiles, I / 128), dim3(256), 0, st,
+                       xh, T, perm, tiles, tile_count, routed, shared, hbuf, (float*)nullptr,
+                       (uint16_t*)nullptr, (const float*)nullptr, (const float*)nullptr);
+    hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F16W>), dim3(max_tiles, H / 256), dim3(256), 0, st,
+                       hbuf, T, perm, tiles, tile_count, routed, shared, (uint16_t*)nullptr,
+                       (float*)nullptr, d16, wts, sg);
 }
 
 }  // namespace moe

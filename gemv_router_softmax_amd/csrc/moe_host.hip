@@ -46,6 +46,13 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
                            const int* tile_count, int max_tiles, const moe_qffn& routed,
                            const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                            hipStream_t st);
+void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+                                 const int* tile_count, int max_tiles, const moe_qffn& routed,
+                                 const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf,
+                                 uint16_t* d16, const float* wts, const float* sg,
+                                 hipStream_t st);
+void launch_combine_f16(const uint16_t* d16, const int32_t* inv, int T, uint16_t* y,
+                        const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_combine(const float* out, const int32_t* inv, const float* wts, const float* sg, int T,
                     uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t st);
@@ -299,9 +306,11 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
                  at<float>(ws, L.logits), ids, wts, sg, st);
     launch_permute(ids, T, counts, offsets, perm, inv, at<int32_t>(ws, L.chunk_counts), st);
     launch_plan(offsets, T, tiles, tcount, st);
-    launch_expert_prefill(x, T, perm, tiles, tcount, max_tiles(T), layer->routed, layer->shared,
-                          at<uint16_t>(ws, L.xh), hbuf, dout, st);
-    launch_combine(dout, inv, wts, sg, T, y, x, res, st);
+    // fp16 rows of weight * d (half the bytes of fp32 expert outputs)
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(dout);
+    launch_expert_prefill_fused(x, T, perm, tiles, tcount, max_tiles(T), layer->routed,
+                                layer->shared, at<uint16_t>(ws, L.xh), hbuf, d16, wts, sg, st);
+    launch_combine_f16(d16, inv, T, y, x, res, st);
     return launch_status();
 }
 
