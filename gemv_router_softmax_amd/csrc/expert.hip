@@ -253,6 +253,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm(const uint16_t* __restrict
         // staged through LDS for 16-byte stores.
         uint16_t* Hs = reinterpret_cast<uint16_t*>(As[0]);    // [128][136] halves
         constexpr int HST = 136;
+        static_assert(MT_ROWS * HST * 2 <= (int)sizeof(As), "staging tile exceeds the A buffers");
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             if (mt < n_mt) {
@@ -294,10 +295,11 @@ __global__ __launch_bounds__(256, 2) void expert_gemm(const uint16_t* __restrict
             }
         }
     } else {
-        // fp16 rows of coef * d, staged through LDS ([128][264] halves) for
-        // 16-byte stores
+        // fp16 rows of coef * d, staged through LDS ([128][256] halves =
+        // exactly the 64 KB of the two A buffers) for 16-byte stores
         uint16_t* Ds = reinterpret_cast<uint16_t*>(As[0]);
-        constexpr int DST = 264;
+        constexpr int DST = 256;
+        static_assert(MT_ROWS * DST * 2 <= (int)sizeof(As), "staging tile exceeds the A buffers");
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             if (mt < n_mt) {
