@@ -91,111 +91,104 @@ __device__ __forceinline__ half8 dequant8(uint32_t w, half2v s2, half2v b2) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 enum GemmMode { GM_GATEUP = 0, GM_DOWN_F32 = 1, GM_DOWN_F16W = 2 };
 
-// Grouped expert GEMM on v_mfma_f32_16x16x32_f16.
-//   workgroup = one row tile (<= 128 rows of one expert) x 128 gate+128 up
-//   columns (GM_GATEUP, K = 2048) or x 256 output columns (down, K = 512);
-//   4 waves, each owning 64 weight columns for ALL rows of the tile, so every
+// Raw buffer resource over [p, p + bytes): loads beyond the range return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+struct GemmArgs {
+    const uint16_t* ain;
+    uint32_t ain_bytes;
+    int T;
+    const int32_t* perm;
+    uint16_t* hout;
+    float* dout32;
+    uint16_t* dout16;
+    const float* wts;
+    const float* sg;
+};
+
+// One row tile (NMT 16-row m-tiles, NMT*16 >= nrows) of the grouped GEMM.
+//   4 waves; wave w owns 64 weight columns (gate/up: 32 gate + the same 32
+//   up columns; down: 64 output columns) for ALL rows of the tile, so every
 //   code word is dequantised once per tile.
 //   A: 128-wide K chunks of the activation rows (gathered by token for
-//   gate/up) go straight from global memory into LDS with
-//   global_load_lds_dwordx4, double buffered (2 x 32 KB); the 16 B pieces of
-//   a row are XOR-swizzled by (row & 15) so the 16 rows an MFMA operand reads
-//   hit 16 distinct LDS bank groups.
-//   B: each lane loads 16 B of codes per column per chunk (one chunk ahead)
+//   gate/up) move from global memory straight into LDS (buffer loads with
+//   an LDS destination), double buffered; the 16 B pieces of a row are
+//   XOR-swizzled by (row & 15) so the 16 rows of an MFMA operand read hit 16
+//   distinct LDS bank groups.
+//   B: each lane loads 16 B of codes per column per chunk, one chunk ahead,
 //   and rebuilds fp16 weights in registers (dequant8).
-//   Epilogues: GM_GATEUP -> h = bf16(silu(g) u) as fp16 in chunk-slot order;
-//   GM_DOWN_F32 -> fp32 rows (split expert-FFN call); GM_DOWN_F16W -> fp16
-//   rows pre-multiplied by the routing weight (or the shared gate) for the
-//   fused combine.
-template <int KDIM, int MODE>
-__global__ __launch_bounds__(256, 2) void expert_gemm(const uint16_t* __restrict__ ain, int T,
-                                                      const int32_t* __restrict__ perm,
-                                                      const Tile* __restrict__ tiles,
-                                                      const int* __restrict__ tile_count,
-                                                      moe_qffn routed, moe_qffn shared,
-                                                      uint16_t* __restrict__ hout,
-                                                      float* __restrict__ dout32,
-                                                      uint16_t* __restrict__ dout16,
-                                                      const float* __restrict__ wts,
-                                                      const float* __restrict__ sg) {
+//   MFMA: v_mfma_f32_16x16x32_f16, fp32 accumulation.
+template <int KDIM, int MODE, int NMT>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, const moe_qffn& q,
+                                          int e, uint8_t* As, float* coef) {
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NCH = KDIM / 128;              // K chunks
     constexpr int WPR = KDIM / 8;                // code words per weight row
     constexpr int SPR = KDIM / G;                // groups per weight row
     constexpr int ROWS_W = GATEUP ? I : H;       // weight rows per expert
     constexpr int CHB = 128 * 2;                 // bytes per A row per chunk
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][MT_ROWS * CHB];
-    __shared__ float coef[MT_ROWS];
-
-    if ((int)blockIdx.x >= *tile_count) return;
-    const Tile tl = tiles[blockIdx.x];
-    const bool sh = tl.group >= E;
-    const int e = sh ? 0 : tl.group;
-    const moe_qffn q = sh ? shared : routed;
+    constexpr int BUFB = MT_ROWS * CHB;          // bytes per LDS buffer
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, j = lane >> 4;
-    const int nr = tl.nrows, n_mt = (nr + 15) >> 4;
+    const int nr = tl.nrows;
 
-    // ---- B: this lane's weight row in each of the wave's four 16-column tiles
-    const uint32_t* wq[4];
-    const uint16_t* wsc[4];
-    const uint16_t* wbi[4];
+    // ---- B: resources for the expert's matrices and per-lane offsets
+    const uint32_t mat_rows = (uint32_t)ROWS_W;  // rows per expert
+    const uint32_t qbytes = mat_rows * WPR * 4, sbytes = mat_rows * SPR * 2;
+    __amdgpu_buffer_rsrc_t rq[2], rs[2], rb[2];
+    if (GATEUP) {
+        rq[0] = buf_rsrc(q.gate_q + (size_t)e * ROWS_W * WPR, qbytes);
+        rq[1] = buf_rsrc(q.up_q + (size_t)e * ROWS_W * WPR, qbytes);
+        rs[0] = buf_rsrc(q.gate_s + (size_t)e * ROWS_W * SPR, sbytes);
+        rs[1] = buf_rsrc(q.up_s + (size_t)e * ROWS_W * SPR, sbytes);
+        rb[0] = buf_rsrc(q.gate_b + (size_t)e * ROWS_W * SPR, sbytes);
+        rb[1] = buf_rsrc(q.up_b + (size_t)e * ROWS_W * SPR, sbytes);
+    } else {
+        rq[0] = rq[1] = buf_rsrc(q.down_q + (size_t)e * ROWS_W * WPR, qbytes);
+        rs[0] = rs[1] = buf_rsrc(q.down_s + (size_t)e * ROWS_W * SPR, sbytes);
+        rb[0] = rb[1] = buf_rsrc(q.down_b + (size_t)e * ROWS_W * SPR, sbytes);
+    }
+    uint32_t qoff[4], soff[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-        int n;
-        const uint32_t* qb;
-        const uint16_t *sb, *bb;
-        if (GATEUP) {
-            n = blockIdx.y * 128 + wave * 32 + (nt & 1) * 16 + r;
-            qb = nt < 2 ? q.gate_q : q.up_q;
-            sb = nt < 2 ? q.gate_s : q.up_s;
-            bb = nt < 2 ? q.gate_b : q.up_b;
-        } else {
-            n = blockIdx.y * 256 + wave * 64 + nt * 16 + r;
-            qb = q.down_q;
-            sb = q.down_s;
-            bb = q.down_b;
-        }
-        const size_t row = (size_t)e * ROWS_W + n;
-        wq[nt] = qb + row * WPR + 4 * j;
-        wsc[nt] = sb + row * SPR + (j >> 1);
-        wbi[nt] = bb + row * SPR + (j >> 1);
+        const int n = GATEUP ? blockIdx.y * 128 + wave * 32 + (nt & 1) * 16 + r
+                             : blockIdx.y * 256 + wave * 64 + nt * 16 + r;
+        qoff[nt] = ((uint32_t)n * WPR + 4 * j) * 4;
+        soff[nt] = ((uint32_t)n * SPR + (j >> 1)) * 2;
     }
+    auto mat = [](int nt) { return GATEUP ? (nt >> 1) : 0; };
 
-    // ---- A: byte offsets of the 8 pieces this lane moves per chunk.
-    // Load instruction i of wave w fills tile rows w*32 + 4i .. +3 (1 KB);
+    // ---- A: per-lane source offsets of the 8 pieces moved per chunk.
+    // Load instruction i of wave w fills tile rows w*32 + 4i .. +3 (1 KB):
     // lane -> row w*32 + 4i + (lane >> 4), LDS slot (lane & 15), holding the
     // row's piece (lane & 15) ^ (row & 15).
+    const __amdgpu_buffer_rsrc_t ra = buf_rsrc(A.ain, A.ain_bytes);
     uint32_t aoff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = wave * 32 + i * 4 + (lane >> 4);
         const int rr = row < nr ? row : 0;
-        const int src = GATEUP ? row_token(tl.row0 + rr, T, perm) : tl.row0 + rr;
+        const int src = GATEUP ? row_token(tl.row0 + rr, A.T, A.perm) : tl.row0 + rr;
         aoff[i] = (uint32_t)src * (uint32_t)(KDIM * 2) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
     }
-    const char* abase = reinterpret_cast<const char*>(ain);
     auto issue_a = [&](int kc, int buf) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (gbl_ptr_t)(abase + aoff[i] + kc * CHB),
-                (lds_ptr_t)(&As[buf][(wave * 32 + i * 4) * CHB]), 16, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+            if (wave * 32 + i * 4 < NMT * 16)        // rows beyond the tile's m-tiles
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (lds_ptr_t)(As + buf * BUFB + (wave * 32 + i * 4) * CHB), 16, aoff[i],
+                    kc * CHB, 0, 0);
+        }
     };
 
-    if (MODE == GM_DOWN_F16W && tid < nr) {
-        const int p = tl.row0 + tid;
-        if (p < TOPK * T) coef[tid] = wts[min(max(perm[p], 0), TOPK * T - 1)];
-        else coef[tid] = sg[p - TOPK * T];
-    }
-
-    float4v acc[8][4];
+    float4v acc[NMT][4];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (float4v){0.f, 0.f, 0.f, 0.f};
 
@@ -203,9 +196,9 @@ __global__ __launch_bounds__(256, 2) void expert_gemm(const uint16_t* __restrict
     half2v bs[4], bb[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-        bw[nt] = *reinterpret_cast<const uint4v*>(wq[nt]);
-        bs[nt] = splat_h(wsc[nt][0]);
-        bb[nt] = splat_h(wbi[nt][0]);
+        bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rq[mat(nt)], qoff[nt], 0, 0);
+        bs[nt] = splat_h(__builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], 0, 0));
+        bb[nt] = splat_h(__builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], 0, 0));
     }
     issue_a(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -220,29 +213,30 @@ __global__ __launch_bounds__(256, 2) void expert_gemm(const uint16_t* __restrict
             issue_a(kc + 1, (kc + 1) & 1);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                bw[nt] = *reinterpret_cast<const uint4v*>(wq[nt] + (kc + 1) * 16);
-                bs[nt] = splat_h(wsc[nt][(kc + 1) * 2]);
-                bb[nt] = splat_h(wbi[nt][(kc + 1) * 2]);
+                bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rq[mat(nt)], qoff[nt], (kc + 1) * 64, 0);
+                bs[nt] = splat_h(
+                    __builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], (kc + 1) * 4, 0));
+                bb[nt] = splat_h(
+                    __builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], (kc + 1) * 4, 0));
             }
         }
-        const uint8_t* Ab = As[kc & 1];
+        const uint8_t* Ab = As + (kc & 1) * BUFB;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+            half8 a[NMT];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+                a[mt] = *reinterpret_cast<const half8*>(
+                    &Ab[(mt * 16 + r) * CHB + 16 * ((4 * j + s) ^ r)]);
             half8 bf[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) bf[nt] = dequant8(cw[nt][s], cs[nt], cb[nt]);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                if (mt < n_mt) {
-                    const int row = mt * 16 + r;
-                    const half8 a = *reinterpret_cast<const half8*>(
-                        &Ab[row * CHB + 16 * ((4 * j + s) ^ r)]);
+            for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        acc[mt][nt] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[nt], acc[mt][nt], 0, 0, 0);
-                }
-            }
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], bf[nt], acc[mt][nt], 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -251,76 +245,107 @@ __global__ __launch_bounds__(256, 2) void expert_gemm(const uint16_t* __restrict
     if (GATEUP) {
         // h = bf16(silu(g) * u) stored as fp16 (exact) in chunk-slot order,
         // staged through LDS for 16-byte stores.
-        uint16_t* Hs = reinterpret_cast<uint16_t*>(As[0]);    // [128][136] halves
+        uint16_t* Hs = reinterpret_cast<uint16_t*>(As);    // [128][136] halves
         constexpr int HST = 136;
-        static_assert(MT_ROWS * HST * 2 <= (int)sizeof(As), "staging tile exceeds the A buffers");
+        static_assert(MT_ROWS * HST * 2 <= 2 * BUFB, "staging tile exceeds the A buffers");
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            if (mt < n_mt) {
+        for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = mt * 16 + 4 * j + i;
-                        const int col = wave * 32 + nt * 16 + r;
-                        const float g = acc[mt][nt][i], u = acc[mt][nt + 2][i];
-                        const float hv = (g / (1.f + __expf(-g))) * u;
-                        const _Float16 hh = (_Float16)bf16_to_f32(f32_to_bf16(hv));
-                        Hs[row * HST + (col & ~7) + chunk_slot(col & 7)] =
-                            __builtin_bit_cast(uint16_t, hh);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int row = mt * 16 + 4 * j + i;
+                    const int col = wave * 32 + nt * 16 + r;
+                    const float g = acc[mt][nt][i], u = acc[mt][nt + 2][i];
+                    const float hv = (g / (1.f + __expf(-g))) * u;
+                    const _Float16 hh = (_Float16)bf16_to_f32(f32_to_bf16(hv));
+                    Hs[row * HST + (col & ~7) + chunk_slot(col & 7)] =
+                        __builtin_bit_cast(uint16_t, hh);
                 }
             }
         }
         __syncthreads();
         for (int c = tid; c < nr * 16; c += 256) {
             const int row = c >> 4, col = (c & 15) * 8;
-            *reinterpret_cast<uint4v*>(hout + (size_t)(tl.row0 + row) * I + blockIdx.y * 128 + col) =
-                *reinterpret_cast<const uint4v*>(&Hs[row * HST + col]);
+            *reinterpret_cast<uint4v*>(A.hout + (size_t)(tl.row0 + row) * I + blockIdx.y * 128 +
+                                       col) = *reinterpret_cast<const uint4v*>(&Hs[row * HST + col]);
         }
     } else if (MODE == GM_DOWN_F32) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            if (mt < n_mt) {
+        for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
+            for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = mt * 16 + 4 * j + i;
-                        if (row < nr)
-                            dout32[(size_t)(tl.row0 + row) * H + blockIdx.y * 256 + wave * 64 +
-                                   nt * 16 + r] = acc[mt][nt][i];
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int row = mt * 16 + 4 * j + i;
+                    if (row < nr)
+                        A.dout32[(size_t)(tl.row0 + row) * H + blockIdx.y * 256 + wave * 64 +
+                                 nt * 16 + r] = acc[mt][nt][i];
                 }
             }
         }
     } else {
         // fp16 rows of coef * d, staged through LDS ([128][256] halves =
-        // exactly the 64 KB of the two A buffers) for 16-byte stores
-        uint16_t* Ds = reinterpret_cast<uint16_t*>(As[0]);
+        // exactly the two A buffers) for 16-byte stores
+        uint16_t* Ds = reinterpret_cast<uint16_t*>(As);
         constexpr int DST = 256;
-        static_assert(MT_ROWS * DST * 2 <= (int)sizeof(As), "staging tile exceeds the A buffers");
+        static_assert(MT_ROWS * DST * 2 <= 2 * BUFB, "staging tile exceeds the A buffers");
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            if (mt < n_mt) {
+        for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
+            for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = mt * 16 + 4 * j + i;
-                        const int col = wave * 64 + nt * 16 + r;
-                        const float v = row < nr ? coef[row] * acc[mt][nt][i] : 0.f;
-                        Ds[row * DST + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int row = mt * 16 + 4 * j + i;
+                    const int col = wave * 64 + nt * 16 + r;
+                    const float v = row < nr ? coef[row] * acc[mt][nt][i] : 0.f;
+                    Ds[row * DST + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
                 }
             }
         }
         __syncthreads();
         for (int c = tid; c < nr * 32; c += 256) {
             const int row = c >> 5, col = (c & 31) * 8;
-            *reinterpret_cast<uint4v*>(dout16 + (size_t)(tl.row0 + row) * H + blockIdx.y * 256 + col) =
-                *reinterpret_cast<const uint4v*>(&Ds[row * DST + col]);
+            *reinterpret_cast<uint4v*>(A.dout16 + (size_t)(tl.row0 + row) * H + blockIdx.y * 256 +
+                                       col) = *reinterpret_cast<const uint4v*>(&Ds[row * DST + col]);
         }
+    }
+}
+
+// Grouped expert GEMM: one workgroup per (row tile, column block); the
+// tile's m-tile count selects a fully unrolled instance of gemm_tile.
+//   GM_GATEUP:   K = 2048, 128 gate + 128 up columns, h = bf16(silu(g) u)
+//                written as fp16 in chunk-slot order
+//   GM_DOWN_F32: K = 512, 256 output columns, fp32 rows (split expert-FFN)
+//   GM_DOWN_F16W: as above, fp16 rows pre-multiplied by the routing weight
+//                (or the shared gate) for the fused combine
+template <int KDIM, int MODE>
+__global__ __launch_bounds__(256, 2) void expert_gemm(GemmArgs args,
+                                                      const Tile* __restrict__ tiles,
+                                                      const int* __restrict__ tile_count,
+                                                      moe_qffn routed, moe_qffn shared) {
+    __shared__ __attribute__((aligned(16))) uint8_t As[2 * MT_ROWS * 256];
+    __shared__ float coef[MT_ROWS];
+    if ((int)blockIdx.x >= *tile_count) return;
+    const Tile tl = tiles[blockIdx.x];
+    const bool sh = tl.group >= E;
+    const int e = sh ? 0 : tl.group;
+    const moe_qffn& q = sh ? shared : routed;
+    if (MODE == GM_DOWN_F16W && (int)threadIdx.x < tl.nrows) {
+        const int p = tl.row0 + threadIdx.x;
+        const int T = args.T;
+        coef[threadIdx.x] = p < TOPK * T ? args.wts[min(max(args.perm[p], 0), TOPK * T - 1)]
+                                         : args.sg[p - TOPK * T];
+    }
+    switch ((tl.nrows + 15) >> 4) {
+        case 1: gemm_tile<KDIM, MODE, 1>(args, tl, q, e, As, coef); break;
+        case 2: gemm_tile<KDIM, MODE, 2>(args, tl, q, e, As, coef); break;
+        case 3: gemm_tile<KDIM, MODE, 3>(args, tl, q, e, As, coef); break;
+        case 4: gemm_tile<KDIM, MODE, 4>(args, tl, q, e, As, coef); break;
+        case 5: gemm_tile<KDIM, MODE, 5>(args, tl, q, e, As, coef); break;
+        case 6: gemm_tile<KDIM, MODE, 6>(args, tl, q, e, As, coef); break;
+        case 7: gemm_tile<KDIM, MODE, 7>(args, tl, q, e, As, coef); break;
+        default: gemm_tile<KDIM, MODE, 8>(args, tl, q, e, As, coef); break;
     }
 }
 
@@ -348,6 +373,20 @@ void launch_expert_decode(const uint16_t* x, int T, const int32_t* perm, const T
                        tile_count, routed, shared, dout);
 }
 
+static GemmArgs gemm_args(const uint16_t* ain, uint32_t ain_bytes, int T, const int32_t* perm) {
+    GemmArgs a;
+    a.ain = ain;
+    a.ain_bytes = ain_bytes;
+    a.T = T;
+    a.perm = perm;
+    a.hout = nullptr;
+    a.dout32 = nullptr;
+    a.dout16 = nullptr;
+    a.wts = nullptr;
+    a.sg = nullptr;
+    return a;
+}
+
 void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
                            const int* tile_count, int max_tiles, const moe_qffn& routed,
                            const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
@@ -355,12 +394,14 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
     const size_t chunks = (size_t)T * (H / 8);
     hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
                        xh);
-    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(max_tiles, I / 128), dim3(256), 0, st,
-                       xh, T, perm, tiles, tile_count, routed, shared, hbuf, (float*)nullptr,
-                       (uint16_t*)nullptr, (const float*)nullptr, (const float*)nullptr);
+    GemmArgs gu = gemm_args(xh, (uint32_t)((size_t)T * H * 2), T, perm);
+    gu.hout = hbuf;
+    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(max_tiles, I / 128), dim3(256), 0, st, gu,
+                       tiles, tile_count, routed, shared);
+    GemmArgs dn = gemm_args(hbuf, (uint32_t)((size_t)(TOPK + 1) * T * I * 2), T, perm);
+    dn.dout32 = dout;
     hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F32>), dim3(max_tiles, H / 256), dim3(256), 0, st,
-                       hbuf, T, perm, tiles, tile_count, routed, shared, (uint16_t*)nullptr, dout,
-                       (uint16_t*)nullptr, (const float*)nullptr, (const float*)nullptr);
+                       dn, tiles, tile_count, routed, shared);
 }
 
 // Whole-layer prefill expert part: gate/up, then down writing fp16 rows of
@@ -373,12 +414,16 @@ void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, 
     const size_t chunks = (size_t)T * (H / 8);
     hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
                        xh);
-    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(max_tiles, I / 128), dim3(256), 0, st,
-                       xh, T, perm, tiles, tile_count, routed, shared, hbuf, (float*)nullptr,
-                       (uint16_t*)nullptr, (const float*)nullptr, (const float*)nullptr);
+    GemmArgs gu = gemm_args(xh, (uint32_t)((size_t)T * H * 2), T, perm);
+    gu.hout = hbuf;
+    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(max_tiles, I / 128), dim3(256), 0, st, gu,
+                       tiles, tile_count, routed, shared);
+    GemmArgs dn = gemm_args(hbuf, (uint32_t)((size_t)(TOPK + 1) * T * I * 2), T, perm);
+    dn.dout16 = d16;
+    dn.wts = wts;
+    dn.sg = sg;
     hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F16W>), dim3(max_tiles, H / 256), dim3(256), 0, st,
-                       hbuf, T, perm, tiles, tile_count, routed, shared, (uint16_t*)nullptr,
-                       (float*)nullptr, d16, wts, sg);
+                       dn, tiles, tile_count, routed, shared);
 }
 
 }  // namespace moe
