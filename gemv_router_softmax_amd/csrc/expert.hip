@@ -111,13 +111,24 @@ struct GemmArgs {
     const float* sg;
 };
 
-// One row tile (NMT 16-row m-tiles, NMT*16 >= nrows) of the grouped GEMM.
-//   4 waves; wave w owns 64 weight columns (gate/up: 32 gate + the same 32
+constexpr int GW = 8;                 // waves per GEMM workgroup
+constexpr int GSTAGES = 3;            // A pipeline depth (LDS buffers)
+constexpr int CHB = 128 * 2;          // bytes per A row per 128-wide K chunk
+constexpr int BUFB = MT_ROWS * CHB;   // bytes per A buffer (32 KB)
+
+// s_waitcnt immediate: wait until at most n vector-memory operations of
+// this wave are outstanding (loads retire in issue order); expcnt and
+// lgkmcnt are left at their maximum (no wait).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// One row tile (NMT 16-row m-tiles, NMT*16 >= nrows) x one column block of
+// the grouped GEMM.
+//   8 waves; wave w owns 64 weight columns (gate/up: 32 gate + the same 32
 //   up columns; down: 64 output columns) for ALL rows of the tile, so every
-//   code word is dequantised once per tile.
+//   code word is dequantised once per tile and column block.
 //   A: 128-wide K chunks of the activation rows (gathered by token for
-//   gate/up) move from global memory straight into LDS (buffer loads with
-//   an LDS destination), double buffered; the 16 B pieces of a row are
+//   gate/up) move from global memory straight into LDS (buffer loads with an
+//   LDS destination) through a 3-stage pipeline; the 16 B pieces of a row are
 //   XOR-swizzled by (row & 15) so the 16 rows of an MFMA operand read hit 16
 //   distinct LDS bank groups.
 //   B: each lane loads 16 B of codes per column per chunk, one chunk ahead,
@@ -125,21 +136,19 @@ struct GemmArgs {
 //   MFMA: v_mfma_f32_16x16x32_f16, fp32 accumulation.
 template <int KDIM, int MODE, int NMT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, const moe_qffn& q,
-                                          int e, uint8_t* As, float* coef) {
+                                          int e, int nb, uint8_t* As, float* coef) {
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NCH = KDIM / 128;              // K chunks
     constexpr int WPR = KDIM / 8;                // code words per weight row
     constexpr int SPR = KDIM / G;                // groups per weight row
     constexpr int ROWS_W = GATEUP ? I : H;       // weight rows per expert
-    constexpr int CHB = 128 * 2;                 // bytes per A row per chunk
-    constexpr int BUFB = MT_ROWS * CHB;          // bytes per LDS buffer
+    constexpr int NBW = GATEUP ? GW * 32 : GW * 64;   // output columns per block
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, j = lane >> 4;
     const int nr = tl.nrows;
 
     // ---- B: resources for the expert's matrices and per-lane offsets
-    const uint32_t mat_rows = (uint32_t)ROWS_W;  // rows per expert
-    const uint32_t qbytes = mat_rows * WPR * 4, sbytes = mat_rows * SPR * 2;
+    const uint32_t qbytes = (uint32_t)ROWS_W * WPR * 4, sbytes = (uint32_t)ROWS_W * SPR * 2;
     __amdgpu_buffer_rsrc_t rq[2], rs[2], rb[2];
     if (GATEUP) {
         rq[0] = buf_rsrc(q.gate_q + (size_t)e * ROWS_W * WPR, qbytes);
@@ -156,34 +165,35 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
     uint32_t qoff[4], soff[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-        const int n = GATEUP ? blockIdx.y * 128 + wave * 32 + (nt & 1) * 16 + r
-                             : blockIdx.y * 256 + wave * 64 + nt * 16 + r;
+        const int n = GATEUP ? nb * NBW + wave * 32 + (nt & 1) * 16 + r
+                             : nb * NBW + wave * 64 + nt * 16 + r;
         qoff[nt] = ((uint32_t)n * WPR + 4 * j) * 4;
         soff[nt] = ((uint32_t)n * SPR + (j >> 1)) * 2;
     }
     auto mat = [](int nt) { return GATEUP ? (nt >> 1) : 0; };
 
-    // ---- A: per-lane source offsets of the 8 pieces moved per chunk.
-    // Load instruction i of wave w fills tile rows w*32 + 4i .. +3 (1 KB):
-    // lane -> row w*32 + 4i + (lane >> 4), LDS slot (lane & 15), holding the
+    // ---- A: per-lane source offsets of the 4 pieces moved per chunk.
+    // Load instruction i of wave w fills tile rows w*16 + 4i .. +3 (1 KB):
+    // lane -> row w*16 + 4i + (lane >> 4), LDS slot (lane & 15), holding the
     // row's piece (lane & 15) ^ (row & 15).
     const __amdgpu_buffer_rsrc_t ra = buf_rsrc(A.ain, A.ain_bytes);
-    uint32_t aoff[8];
+    uint32_t aoff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = wave * 32 + i * 4 + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+        const int row = wave * 16 + i * 4 + (lane >> 4);
         const int rr = row < nr ? row : 0;
         const int src = GATEUP ? row_token(tl.row0 + rr, A.T, A.perm) : tl.row0 + rr;
         aoff[i] = (uint32_t)src * (uint32_t)(KDIM * 2) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
     }
-    auto issue_a = [&](int kc, int buf) {
+    // rows this wave moves: w*16 .. w*16+15, needed only below NMT*16
+    const bool amove = wave * 16 < NMT * 16;
+    auto issue_a = [&](int kc) {
+        uint8_t* dst = As + (kc % GSTAGES) * BUFB + wave * 16 * CHB;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (wave * 32 + i * 4 < NMT * 16)        // rows beyond the tile's m-tiles
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    ra, (lds_ptr_t)(As + buf * BUFB + (wave * 32 + i * 4) * CHB), 16, aoff[i],
-                    kc * CHB, 0, 0);
-        }
+        for (int i = 0; i < 4; ++i)
+            if (amove)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + i * 4 * CHB), 16,
+                                                         aoff[i], kc * CHB, 0, 0);
     };
 
     float4v acc[NMT][4];
@@ -194,13 +204,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
 
     uint4v bw[4];
     half2v bs[4], bb[4];
+    issue_a(0);
+    if (NCH > 1) issue_a(1);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rq[mat(nt)], qoff[nt], 0, 0);
         bs[nt] = splat_h(__builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], 0, 0));
         bb[nt] = splat_h(__builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], 0, 0));
     }
-    issue_a(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -210,7 +221,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) { cw[nt] = bw[nt]; cs[nt] = bs[nt]; cb[nt] = bb[nt]; }
         if (kc + 1 < NCH) {
-            issue_a(kc + 1, (kc + 1) & 1);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rq[mat(nt)], qoff[nt], (kc + 1) * 64, 0);
@@ -220,7 +230,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
                     __builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], (kc + 1) * 4, 0));
             }
         }
-        const uint8_t* Ab = As + (kc & 1) * BUFB;
+        const bool more = kc + 2 < NCH;
+        if (more) issue_a(kc + 2);
+        const uint8_t* Ab = As + (kc % GSTAGES) * BUFB;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             half8 a[NMT];
@@ -238,16 +250,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
                     acc[mt][nt] =
                         __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], bf[nt], acc[mt][nt], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        // chunk kc+1 (A and B) must have landed; chunk kc+2's A may stay in flight
+        if (more && amove) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
     }
 
     if (GATEUP) {
         // h = bf16(silu(g) * u) stored as fp16 (exact) in chunk-slot order,
         // staged through LDS for 16-byte stores.
-        uint16_t* Hs = reinterpret_cast<uint16_t*>(As);    // [128][136] halves
-        constexpr int HST = 136;
-        static_assert(MT_ROWS * HST * 2 <= 2 * BUFB, "staging tile exceeds the A buffers");
+        uint16_t* Hs = reinterpret_cast<uint16_t*>(As);    // [128][NBW/2 + 8] halves
+        constexpr int HST = NBW / 2 + 8;
+        static_assert(MT_ROWS * HST * 2 <= GSTAGES * BUFB, "staging tile exceeds the A buffers");
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
@@ -265,9 +279,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
             }
         }
         __syncthreads();
-        for (int c = tid; c < nr * 16; c += 256) {
-            const int row = c >> 4, col = (c & 15) * 8;
-            *reinterpret_cast<uint4v*>(A.hout + (size_t)(tl.row0 + row) * I + blockIdx.y * 128 +
+        constexpr int PR = NBW / 2 / 8;      // 16-byte pieces per staged row
+        for (int c = tid; c < nr * PR; c += GW * 64) {
+            const int row = c / PR, col = (c % PR) * 8;
+            *reinterpret_cast<uint4v*>(A.hout + (size_t)(tl.row0 + row) * I + nb * (NBW / 2) +
                                        col) = *reinterpret_cast<const uint4v*>(&Hs[row * HST + col]);
         }
     } else if (MODE == GM_DOWN_F32) {
@@ -279,55 +294,74 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
                 for (int i = 0; i < 4; ++i) {
                     const int row = mt * 16 + 4 * j + i;
                     if (row < nr)
-                        A.dout32[(size_t)(tl.row0 + row) * H + blockIdx.y * 256 + wave * 64 +
-                                 nt * 16 + r] = acc[mt][nt][i];
+                        A.dout32[(size_t)(tl.row0 + row) * H + nb * NBW + wave * 64 + nt * 16 + r] =
+                            acc[mt][nt][i];
                 }
             }
         }
     } else {
-        // fp16 rows of coef * d, staged through LDS ([128][256] halves =
-        // exactly the two A buffers) for 16-byte stores
+        // fp16 rows of coef * d, staged through LDS for 16-byte stores, one
+        // half of the block's columns (four waves) at a time
         uint16_t* Ds = reinterpret_cast<uint16_t*>(As);
-        constexpr int DST = 256;
-        static_assert(MT_ROWS * DST * 2 <= 2 * BUFB, "staging tile exceeds the A buffers");
+        constexpr int HALF = NBW / 2;
+        constexpr int DST = HALF + 8;
+        static_assert(MT_ROWS * DST * 2 <= GSTAGES * BUFB, "staging tile exceeds the A buffers");
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
+        for (int hf = 0; hf < 2; ++hf) {
+            if ((wave >> 2) == hf) {
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
+                for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = mt * 16 + 4 * j + i;
-                    const int col = wave * 64 + nt * 16 + r;
-                    const float v = row < nr ? coef[row] * acc[mt][nt][i] : 0.f;
-                    Ds[row * DST + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                    for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = mt * 16 + 4 * j + i;
+                            const int col = (wave & 3) * 64 + nt * 16 + r;
+                            const float v = row < nr ? coef[row] * acc[mt][nt][i] : 0.f;
+                            Ds[row * DST + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                        }
+                    }
                 }
             }
-        }
-        __syncthreads();
-        for (int c = tid; c < nr * 32; c += 256) {
-            const int row = c >> 5, col = (c & 31) * 8;
-            *reinterpret_cast<uint4v*>(A.dout16 + (size_t)(tl.row0 + row) * H + blockIdx.y * 256 +
-                                       col) = *reinterpret_cast<const uint4v*>(&Ds[row * DST + col]);
+            __syncthreads();
+            constexpr int PR = HALF / 8;
+            for (int c = tid; c < nr * PR; c += GW * 64) {
+                const int row = c / PR, col = (c % PR) * 8;
+                *reinterpret_cast<uint4v*>(A.dout16 + (size_t)(tl.row0 + row) * H + nb * NBW +
+                                           hf * HALF + col) =
+                    *reinterpret_cast<const uint4v*>(&Ds[row * DST + col]);
+            }
+            __syncthreads();
         }
     }
 }
 
-// Grouped expert GEMM: one workgroup per (row tile, column block); the
-// tile's m-tile count selects a fully unrolled instance of gemm_tile.
-//   GM_GATEUP:   K = 2048, 128 gate + 128 up columns, h = bf16(silu(g) u)
-//                written as fp16 in chunk-slot order
-//   GM_DOWN_F32: K = 512, 256 output columns, fp32 rows (split expert-FFN)
+// Grouped expert GEMM: a 1-D grid of (row tile, column block) work items.
+// Work is split into 8 contiguous ranges, one per XCD (workgroup ids are
+// dealt to the 8 XCDs round-robin), so the column blocks of a tile run back
+// to back on the same XCD and re-read its activation rows from that XCD's
+// L2.  The tile's m-tile count selects a fully unrolled instance.
+//   GM_GATEUP:    K = 2048, 256 gate + 256 up columns per block,
+//                 h = bf16(silu(g) u) written as fp16 in chunk-slot order
+//   GM_DOWN_F32:  K = 512, 512 output columns per block, fp32 rows
 //   GM_DOWN_F16W: as above, fp16 rows pre-multiplied by the routing weight
-//                (or the shared gate) for the fused combine
+//                 (or the shared gate) for the fused combine
 template <int KDIM, int MODE>
-__global__ __launch_bounds__(256, 2) void expert_gemm(GemmArgs args,
-                                                      const Tile* __restrict__ tiles,
-                                                      const int* __restrict__ tile_count,
-                                                      moe_qffn routed, moe_qffn shared) {
-    __shared__ __attribute__((aligned(16))) uint8_t As[2 * MT_ROWS * 256];
+__global__ __launch_bounds__(GW * 64, 1) void expert_gemm(GemmArgs args,
+                                                          const Tile* __restrict__ tiles,
+                                                          const int* __restrict__ tile_count,
+                                                          moe_qffn routed, moe_qffn shared) {
+    constexpr int NB = MODE == GM_GATEUP ? I / (GW * 32) : H / (GW * 64);
+    __shared__ __attribute__((aligned(16))) uint8_t As[GSTAGES * BUFB];
     __shared__ float coef[MT_ROWS];
-    if ((int)blockIdx.x >= *tile_count) return;
-    const Tile tl = tiles[blockIdx.x];
+    const int total = *tile_count * NB;
+    const int per_xcd = (total + 7) / 8;
+    const int local = blockIdx.x / 8;
+    if (local >= per_xcd) return;
+    const int w = (blockIdx.x % 8) * per_xcd + local;
+    if (w >= total) return;
+    const Tile tl = tiles[w / NB];
+    const int nb = w % NB;
     const bool sh = tl.group >= E;
     const int e = sh ? 0 : tl.group;
     const moe_qffn& q = sh ? shared : routed;
@@ -338,15 +372,21 @@ __global__ __launch_bounds__(256, 2) void expert_gemm(GemmArgs args,
                                          : args.sg[p - TOPK * T];
     }
     switch ((tl.nrows + 15) >> 4) {
-        case 1: gemm_tile<KDIM, MODE, 1>(args, tl, q, e, As, coef); break;
-        case 2: gemm_tile<KDIM, MODE, 2>(args, tl, q, e, As, coef); break;
-        case 3: gemm_tile<KDIM, MODE, 3>(args, tl, q, e, As, coef); break;
-        case 4: gemm_tile<KDIM, MODE, 4>(args, tl, q, e, As, coef); break;
-        case 5: gemm_tile<KDIM, MODE, 5>(args, tl, q, e, As, coef); break;
-        case 6: gemm_tile<KDIM, MODE, 6>(args, tl, q, e, As, coef); break;
-        case 7: gemm_tile<KDIM, MODE, 7>(args, tl, q, e, As, coef); break;
-        default: gemm_tile<KDIM, MODE, 8>(args, tl, q, e, As, coef); break;
+        case 1: gemm_tile<KDIM, MODE, 1>(args, tl, q, e, nb, As, coef); break;
+        case 2: gemm_tile<KDIM, MODE, 2>(args, tl, q, e, nb, As, coef); break;
+        case 3: gemm_tile<KDIM, MODE, 3>(args, tl, q, e, nb, As, coef); break;
+        case 4: gemm_tile<KDIM, MODE, 4>(args, tl, q, e, nb, As, coef); break;
+        case 5: gemm_tile<KDIM, MODE, 5>(args, tl, q, e, nb, As, coef); break;
+        case 6: gemm_tile<KDIM, MODE, 6>(args, tl, q, e, nb, As, coef); break;
+        case 7: gemm_tile<KDIM, MODE, 7>(args, tl, q, e, nb, As, coef); break;
+        default: gemm_tile<KDIM, MODE, 8>(args, tl, q, e, nb, As, coef); break;
     }
+}
+
+// grid size for a GEMM over at most max_tiles tiles and nb column blocks
+static unsigned gemm_grid(int max_tiles, int nb) {
+    const int total = max_tiles * nb;
+    return (unsigned)(8 * ((total + 7) / 8));
 }
 
 // x (bf16) -> fp16 in chunk-slot order, the activation layout of the expert kernels.
@@ -396,12 +436,12 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
                        xh);
     GemmArgs gu = gemm_args(xh, (uint32_t)((size_t)T * H * 2), T, perm);
     gu.hout = hbuf;
-    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(max_tiles, I / 128), dim3(256), 0, st, gu,
-                       tiles, tile_count, routed, shared);
+    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(gemm_grid(max_tiles, I / (GW * 32))),
+                       dim3(GW * 64), 0, st, gu, tiles, tile_count, routed, shared);
     GemmArgs dn = gemm_args(hbuf, (uint32_t)((size_t)(TOPK + 1) * T * I * 2), T, perm);
     dn.dout32 = dout;
-    hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F32>), dim3(max_tiles, H / 256), dim3(256), 0, st,
-                       dn, tiles, tile_count, routed, shared);
+    hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F32>), dim3(gemm_grid(max_tiles, H / (GW * 64))),
+                       dim3(GW * 64), 0, st, dn, tiles, tile_count, routed, shared);
 }
 
 // Whole-layer prefill expert part: gate/up, then down writing fp16 rows of
@@ -416,14 +456,14 @@ void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, 
                        xh);
     GemmArgs gu = gemm_args(xh, (uint32_t)((size_t)T * H * 2), T, perm);
     gu.hout = hbuf;
-    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(max_tiles, I / 128), dim3(256), 0, st, gu,
-                       tiles, tile_count, routed, shared);
+    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(gemm_grid(max_tiles, I / (GW * 32))),
+                       dim3(GW * 64), 0, st, gu, tiles, tile_count, routed, shared);
     GemmArgs dn = gemm_args(hbuf, (uint32_t)((size_t)(TOPK + 1) * T * I * 2), T, perm);
     dn.dout16 = d16;
     dn.wts = wts;
     dn.sg = sg;
-    hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F16W>), dim3(max_tiles, H / 256), dim3(256), 0, st,
-                       dn, tiles, tile_count, routed, shared);
+    hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F16W>), dim3(gemm_grid(max_tiles, H / (GW * 64))),
+                       dim3(GW * 64), 0, st, dn, tiles, tile_count, routed, shared);
 }
 
 }  // namespace moe
