@@ -259,8 +259,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
     if (GATEUP) {
         // h = bf16(silu(g) * u) stored as fp16 (exact) in chunk-slot order,
         // staged through LDS for 16-byte stores.
-        uint16_t* Hs = reinterpret_cast<uint16_t*>(As);    // [128][NBW/2 + 8] halves
-        constexpr int HST = NBW / 2 + 8;
+        uint16_t* Hs = reinterpret_cast<uint16_t*>(As);    // [128][NBW + 8] halves
+        constexpr int HST = NBW + 8;                         // NBW h columns per block
         static_assert(MT_ROWS * HST * 2 <= GSTAGES * BUFB, "staging tile exceeds the A buffers");
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
@@ -279,11 +279,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
             }
         }
         __syncthreads();
-        constexpr int PR = NBW / 2 / 8;      // 16-byte pieces per staged row
+        constexpr int PR = NBW / 8;          // 16-byte pieces per staged row
         for (int c = tid; c < nr * PR; c += GW * 64) {
             const int row = c / PR, col = (c % PR) * 8;
-            *reinterpret_cast<uint4v*>(A.hout + (size_t)(tl.row0 + row) * I + nb * (NBW / 2) +
-                                       col) = *reinterpret_cast<const uint4v*>(&Hs[row * HST + col]);
+            *reinterpret_cast<uint4v*>(A.hout + (size_t)(tl.row0 + row) * I + nb * NBW + col) =
+                *reinterpret_cast<const uint4v*>(&Hs[row * HST + col]);
         }
     } else if (MODE == GM_DOWN_F32) {
 #pragma unroll
