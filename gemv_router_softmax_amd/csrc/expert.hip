@@ -256,7 +256,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
         __syncthreads();
     }
 
-    if (GATEUP) {
+    if constexpr (GATEUP) {
         // h = bf16(silu(g) * u) stored as fp16 (exact) in chunk-slot order,
         // staged through LDS for 16-byte stores.
         uint16_t* Hs = reinterpret_cast<uint16_t*>(As);    // [128][NBW + 8] halves
@@ -285,7 +285,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
             *reinterpret_cast<uint4v*>(A.hout + (size_t)(tl.row0 + row) * I + nb * NBW + col) =
                 *reinterpret_cast<const uint4v*>(&Hs[row * HST + col]);
         }
-    } else if (MODE == GM_DOWN_F32) {
+    } else if constexpr (MODE == GM_DOWN_F32) {
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
