@@ -8,8 +8,9 @@ layers and a fresh N(0,1) input per step): decode, T = 1.  The 40-layer
 chain is captured once in a HIP graph and replayed per step.
 
 Also measured in the same run and reported in the same JSON line:
-  - the dominant kernel of the decode step (the expert FFN launch) timed
-    with HIP events on the stream it runs on, against HBM peak;
+  - the unit the decode step repeats (one layer launch: router, top-8 and
+    both expert GEMVs with combine) timed with HIP events on the stream it
+    runs on, against HBM peak;
   - the measured sustained HBM read rate (a streaming read probe);
   - prefill, T = 4096 tokens through one layer (rotating over the 40 layers
     so the weights are not cache resident), with MFMA utilisation;
@@ -32,6 +33,9 @@ sys.path.insert(0, ROOT)
 H, I, E, TOPK = 2048, 512, 256, 8
 EXPERT_BYTES = 3 * I * H // 2 + 3 * (I * H // 64) * 2 * 2      # 1,769,472 B
 EXPERT_FLOP_PER_TOKEN = 2 * 3 * I * H                           # 6,291,456
+# algorithmic bytes of one decode layer at T = 1: 8 routed + 1 shared expert,
+# the router matrix and the shared-expert gate vector
+LAYER_DECODE_BYTES = 9 * EXPERT_BYTES + E * H * 2 + H * 2       # 16,977,920
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk/CU (fp16 = bf16 rate)
 
@@ -103,40 +107,43 @@ def decode_chain(D, args):
     return ms, xs
 
 
-def decode_kernel_timing(D, xs, reps):
-    """HIP events around the decode expert-FFN launch (plan + gate/up GEMV +
-    down GEMV) on the stream it is launched on, per layer, with the real
-    routing of the token."""
+def decode_layer_timing(D, xs, reps, batch=8):
+    """HIP events on the launch stream around each decode layer launch at
+    T = 1 -- the same call, kernels and arguments that the graph-replayed
+    chain runs (route_logits_dec, decode_gateup_dec, decode_down_dec).
+    Each batch of layer launches is queued behind a ~0.7 ms streaming read so
+    that the launches run back to back on the GPU, as they do in the graph,
+    instead of waiting for the Python host thread."""
     import torch
     import gemv_router_softmax_amd as moe
 
-    T = 1
-    ws = moe.workspace(T)
-    ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
-    w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
-    sg = torch.empty((T,), dtype=torch.float32, device="cuda")
-    counts = torch.empty(256, dtype=torch.int32, device="cuda")
-    offs = torch.empty(257, dtype=torch.int32, device="cuda")
-    perm = torch.empty(8 * T, dtype=torch.int32, device="cuda")
-    inv = torch.empty(8 * T, dtype=torch.int32, device="cuda")
-    out = torch.empty((9 * T, H), dtype=torch.float32, device="cuda")
-    pairs = event_pairs(reps * len(D))
+    ws = moe.workspace(1)
+    y = torch.empty((1, H), dtype=torch.int16, device="cuda")
+    bufs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in range(2)]
+    pad = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    pad.fill_(1)
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    n = len(D)
+    pairs = event_pairs(reps * n)
     k = 0
     for r in range(reps + 1):
-        for l, Dl in enumerate(D):
-            x = xs[(r * len(D) + l) % xs.shape[0]]
-            moe.moe_route(x, Dl.w_router, Dl.router_bias, Dl.w_shared_gate, ids, w, sg, ws)
-            moe.moe_permute(ids, counts, offs, perm, inv, ws)
-            if r == 0:      # warm-up pass
-                moe.moe_expert_ffn(x, Dl, offs, perm, out, ws, path=moe.MOE_PATH_DECODE)
-                continue
-            a, b = pairs[k]
-            a.record()
-            moe.moe_expert_ffn(x, Dl, offs, perm, out, ws, path=moe.MOE_PATH_DECODE)
-            b.record()
-            k += 1
-    torch.cuda.synchronize()
+        cur = xs[r % xs.shape[0]]
+        for l0 in range(0, n, batch):
+            moe.moe_probe_read(pad, sink)
+            for l in range(l0, min(n, l0 + batch)):
+                nxt = bufs[l % 2]
+                if r == 0:          # warm-up pass
+                    moe.moe_layer_forward_ex(cur, D[l], y, ws, residual_out=nxt)
+                else:
+                    a, b = pairs[k]
+                    a.record()
+                    moe.moe_layer_forward_ex(cur, D[l], y, ws, residual_out=nxt)
+                    b.record()
+                    k += 1
+                cur = nxt
+        torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in pairs])
+    del pad
     return float(ms.mean()), float(np.median(ms))
 
 
@@ -270,11 +277,11 @@ def main():
     tok_s = args.steps / (ms * 1e-3)
     log(f"decode chain: {ms_per_step * 1e3:.1f} us/token, {tok_s:.1f} tokens/s")
 
-    k_mean, k_med = decode_kernel_timing(D, xs, args.kernel_reps)
-    per_launch_bytes = 9 * EXPERT_BYTES
+    k_mean, k_med = decode_layer_timing(D, xs, args.kernel_reps)
+    per_launch_bytes = LAYER_DECODE_BYTES
     achieved = per_launch_bytes / (k_mean * 1e-3) / 1e9
-    log(f"decode expert FFN: {k_mean * 1e3:.2f} us/launch (median {k_med * 1e3:.2f}), "
-        f"{achieved:.0f} GB/s")
+    log(f"decode layer launch: {k_mean * 1e3:.2f} us/launch (median {k_med * 1e3:.2f}), "
+        f"{achieved:.0f} GB/s; graph chain {ms_per_step * 1e3 / args.layers:.2f} us/layer")
     ceiling = read_ceiling()
     log(f"read ceiling: {ceiling:.0f} GB/s")
 
@@ -309,8 +316,8 @@ def main():
                    "hip_graph": not args.no_graph},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode expert FFN launch (plan_tiles + decode_gateup + "
-                               "decode_down)",
+                     "kernel": "decode layer launch at T=1 (route_logits_dec + "
+                               "decode_gateup_dec + decode_down_dec)",
                      "bytes_per_launch": per_launch_bytes, "launch_us": k_mean * 1e3},
         "active_expert_bytes_per_token": chain_bytes,
         "wallclock_gbs": chain_bytes / (ms_per_step * 1e-3) / 1e9,

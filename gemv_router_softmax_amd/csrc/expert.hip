@@ -73,6 +73,14 @@ __device__ __forceinline__ half2v splat_h(uint16_t bits) {
     return (half2v){h, h};
 }
 
+// (x & m) | o in one instruction.  A VOP3 instruction on this chip may read
+// only one scalar operand, so the mask is an SGPR and o stays in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+    return r;
+}
+
 // Eight codes of one word -> fp16 weights w = q*s + b, in chunk-slot order
 // (k = 0,4,1,5,2,6,3,7).  (0x6400 | q) is the fp16 value 1024 + q, so one
 // packed subtraction recovers q exactly and one packed FMA applies the
@@ -81,7 +89,7 @@ __device__ __forceinline__ half8 dequant8(uint32_t w, half2v s2, half2v b2) {
     half8 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t p = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        const uint32_t p = and_or(w >> (4 * i), 0x000F000Fu, 0x64006400u);
         half2v h = __builtin_bit_cast(half2v, p) - (half2v){(_Float16)1024.f, (_Float16)1024.f};
         h = __builtin_elementwise_fma(h, s2, b2);
         r[2 * i] = h[0];
@@ -120,6 +128,21 @@ constexpr int BUFB = MT_ROWS * CHB;   // bytes per A buffer (32 KB)
 // this wave are outstanding (loads retire in issue order); expcnt and
 // lgkmcnt are left at their maximum (no wait).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int LGKM0_IMM = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
+
+// Workgroup barrier inside a software pipeline.  __syncthreads() also acts
+// as a memory fence, which makes every wave wait for ALL of its outstanding
+// vector-memory loads -- including the prefetches meant to stay in flight.
+// Here the caller has already waited (s_waitcnt vmcnt) for exactly the loads
+// the next stage needs; this drains only the LDS counter and synchronises
+// execution.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void pipe_barrier() {
+    __builtin_amdgcn_s_waitcnt(LGKM0_IMM);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // One row tile (NMT 16-row m-tiles, NMT*16 >= nrows) x one column block of
 // the grouped GEMM.
@@ -202,15 +225,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (float4v){0.f, 0.f, 0.f, 0.f};
 
+    // B of the next chunk is loaded into registers one chunk ahead.  Scale
+    // and bias stay raw fp16 bits until they are used, so that no arithmetic
+    // on a just-issued load forces the wave to wait for it.
     uint4v bw[4];
-    half2v bs[4], bb[4];
+    uint32_t bs[4], bb[4];
     issue_a(0);
     if (NCH > 1) issue_a(1);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rq[mat(nt)], qoff[nt], 0, 0);
-        bs[nt] = splat_h(__builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], 0, 0));
-        bb[nt] = splat_h(__builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], 0, 0));
+        bs[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], 0, 0);
+        bb[nt] = __builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -219,15 +245,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
         uint4v cw[4];
         half2v cs[4], cb[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) { cw[nt] = bw[nt]; cs[nt] = bs[nt]; cb[nt] = bb[nt]; }
+        for (int nt = 0; nt < 4; ++nt) {
+            cw[nt] = bw[nt];
+            cs[nt] = splat_h((uint16_t)bs[nt]);
+            cb[nt] = splat_h((uint16_t)bb[nt]);
+        }
         if (kc + 1 < NCH) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rq[mat(nt)], qoff[nt], (kc + 1) * 64, 0);
-                bs[nt] = splat_h(
-                    __builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], (kc + 1) * 4, 0));
-                bb[nt] = splat_h(
-                    __builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], (kc + 1) * 4, 0));
+                bs[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], (kc + 1) * 4, 0);
+                bb[nt] = __builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], (kc + 1) * 4, 0);
             }
         }
         const bool more = kc + 2 < NCH;
@@ -235,25 +263,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, con
         const uint8_t* Ab = As + (kc % GSTAGES) * BUFB;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            half8 a[NMT];
+            half8 a[NMT], bf[4];
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt)
-                a[mt] = *reinterpret_cast<const half8*>(
-                    &Ab[(mt * 16 + r) * CHB + 16 * ((4 * j + s) ^ r)]);
-            half8 bf[4];
+                a[mt] = *reinterpret_cast<const half8*>(&Ab[(mt * 16 + r) * CHB + 16 * ((4 * j + s) ^ r)]);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) bf[nt] = dequant8(cw[nt][s], cs[nt], cb[nt]);
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], bf[nt], acc[mt][nt], 0, 0, 0);
         }
         // chunk kc+1 (A and B) must have landed; chunk kc+2's A may stay in flight
         if (more && amove) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();
+        pipe_barrier();
     }
 
     if constexpr (GATEUP) {
