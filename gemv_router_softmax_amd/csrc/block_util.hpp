@@ -39,7 +39,8 @@ __device__ inline int block_excl_scan256(int v, int* lds /* >= 4 ints */, int* t
 // 4*256 ints) must be zero on entry and is zero on exit.
 __device__ inline void stable_scatter(const int32_t* __restrict__ ids, int f0, int f1, int* base,
                                int* wcnt, int32_t* __restrict__ perm,
-                               int32_t* __restrict__ inv) {
+                               int32_t* __restrict__ inv, const float* __restrict__ wsrc = nullptr,
+                               float* __restrict__ wsorted = nullptr) {
     const int tid = threadIdx.x, wave = tid >> 6;
     for (int c0 = f0; c0 < f1; c0 += 256) {
         const int f = c0 + tid;
@@ -64,6 +65,7 @@ __device__ inline void stable_scatter(const int32_t* __restrict__ ids, int f0, i
             const int pos = base[e] + pre + rank;
             perm[pos] = f;
             inv[f] = pos;
+            if (wsorted) wsorted[pos] = wsrc[f];
         }
         __syncthreads();
         int s = 0;

@@ -102,41 +102,25 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 enum GemmMode { GM_GATEUP = 0, GM_DOWN_F32 = 1, GM_DOWN_F16W = 2 };
 
-// Raw buffer resource over [p, p + bytes): loads beyond the range return 0.
+// Raw buffer resource over [p, p + bytes): loads beyond the range return 0,
+// stores beyond it write nothing.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
-struct GemmArgs {
-    const uint16_t* ain;
-    uint32_t ain_bytes;
-    int T;
-    const int32_t* perm;
-    uint16_t* hout;
-    float* dout32;
-    uint16_t* dout16;
-    const float* wts;
-    const float* sg;
-};
-
-constexpr int GW = 8;                 // waves per GEMM workgroup
-constexpr int GSTAGES = 3;            // A pipeline depth (LDS buffers)
-constexpr int CHB = 128 * 2;          // bytes per A row per 128-wide K chunk
-constexpr int BUFB = MT_ROWS * CHB;   // bytes per A buffer (32 KB)
-
 // s_waitcnt immediate: wait until at most n vector-memory operations of
-// this wave are outstanding (loads retire in issue order); expcnt and
+// this wave are outstanding (they retire in issue order); expcnt and
 // lgkmcnt are left at their maximum (no wait).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int LGKM0_IMM = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
 
 // Workgroup barrier inside a software pipeline.  __syncthreads() also acts
 // as a memory fence, which makes every wave wait for ALL of its outstanding
-// vector-memory loads -- including the prefetches meant to stay in flight.
-// Here the caller has already waited (s_waitcnt vmcnt) for exactly the loads
-// the next stage needs; this drains only the LDS counter and synchronises
-// execution.  The empty asm statements keep the compiler from moving memory
-// accesses across the barrier.
+// vector-memory operations -- including the prefetches meant to stay in
+// flight.  Here the caller has already waited (s_waitcnt vmcnt) for exactly
+// the loads the next stage needs; this drains only the LDS counter and
+// synchronises execution.  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
 __device__ __forceinline__ void pipe_barrier() {
     __builtin_amdgcn_s_waitcnt(LGKM0_IMM);
     asm volatile("" ::: "memory");
@@ -144,274 +128,617 @@ __device__ __forceinline__ void pipe_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One row tile (NMT 16-row m-tiles, NMT*16 >= nrows) x one column block of
-// the grouped GEMM.
-//   8 waves; wave w owns 64 weight columns (gate/up: 32 gate + the same 32
-//   up columns; down: 64 output columns) for ALL rows of the tile, so every
-//   code word is dequantised once per tile and column block.
-//   A: 128-wide K chunks of the activation rows (gathered by token for
-//   gate/up) move from global memory straight into LDS (buffer loads with an
-//   LDS destination) through a 3-stage pipeline; the 16 B pieces of a row are
-//   XOR-swizzled by (row & 15) so the 16 rows of an MFMA operand read hit 16
-//   distinct LDS bank groups.
-//   B: each lane loads 16 B of codes per column per chunk, one chunk ahead,
-//   and rebuilds fp16 weights in registers (dequant8).
-//   MFMA: v_mfma_f32_16x16x32_f16, fp32 accumulation.
-template <int KDIM, int MODE, int NMT>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& A, const Tile& tl, const moe_qffn& q,
-                                          int e, int nb, uint8_t* As, float* coef) {
-    constexpr bool GATEUP = MODE == GM_GATEUP;
-    constexpr int NCH = KDIM / 128;              // K chunks
-    constexpr int WPR = KDIM / 8;                // code words per weight row
-    constexpr int SPR = KDIM / G;                // groups per weight row
-    constexpr int ROWS_W = GATEUP ? I : H;       // weight rows per expert
-    constexpr int NBW = GATEUP ? GW * 32 : GW * 64;   // output columns per block
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, j = lane >> 4;
-    const int nr = tl.nrows;
+// ---------------------------------------------------------------------------
+// Persistent grouped GEMM (prefill).
+//
+// Work items are (row tile, block of 256 weight rows) pairs: gate/up has 4
+// blocks per tile (128 gate + the same 128 up rows each), down has 8.  A
+// grid of 256 workgroups -- one per compute unit, each holding the whole
+// register file (4 waves, one per SIMD, MFMA accumulators in AGPRs) and
+// ~155 KB of LDS -- walks the items with a fixed stride.  Consecutive items
+// (the blocks of one tile, which share their activation rows) are dealt to
+// workgroups of the same XCD, so the rows are fetched once into that XCD's
+// L2.
+//
+// K advances in chunks of 64 (one quantisation group).  Everything a chunk
+// needs -- the activation rows (A, fp16, gathered by token for gate/up),
+// the 4-bit codes of the 256 weight rows (B) and their scales and biases --
+// moves from global memory straight into LDS (buffer loads with an LDS
+// destination) through a 5-stage ring, 4 chunks ahead of the MFMAs.  The
+// ring runs on across item boundaries: the last 4 chunks of an item prefetch
+// the first 4 of the next, so no workgroup ever waits for a pipeline fill
+// except at its very first item.
+//
+// Every wave issues exactly LPC loads per chunk (plus one metadata load at
+// the first chunk of an item and a fixed number of stores per epilogue;
+// missing rows and items become out-of-range buffer offsets, which access no
+// memory), so the number of memory operations issued after any chunk's
+// loads is a compile-time constant and the wait for a chunk is an exact
+// s_waitcnt vmcnt.
+//
+// Wave w computes 64 weight rows (gate/up: 32 gate + the same 32 up rows;
+// down: 64 output columns) for all rows of the tile, each code word being
+// dequantised once per item (dequant8: fp16 weights in registers) and fed to
+// v_mfma_f32_32x32x16_f16 with fp32 accumulation.  SwiGLU is applied in the
+// gate/up epilogue (h = bf16(silu(g) u), stored as fp16); down writes fp32
+// rows (split interface) or fp16 rows of (routing weight or shared gate) x d.
+//
+// LDS layouts (per stage):
+//   A   [160 rows][8 pieces of 16 B]: piece p of row R sits at slot
+//       p ^ ((R >> 1) & 7), so the 16 rows of an MFMA operand read cover all
+//       64 banks.
+//   B   [256 columns][2 pieces of 16 B]: piece p of column C sits at slot
+//       p ^ ((C >> 3) & 1), so a 128-bit read by 16 lanes is conflict free.
+//   S, Bi [256 columns] dwords holding the fp16 scale (bias) of groups
+//       2*floor(kc/2) and 2*floor(kc/2)+1 (chunk kc uses half kc & 1).
+// K order inside a chunk: lane half g of MFMA step s covers k-piece 4g+s.
 
-    // ---- B: resources for the expert's matrices and per-lane offsets
-    const uint32_t qbytes = (uint32_t)ROWS_W * WPR * 4, sbytes = (uint32_t)ROWS_W * SPR * 2;
-    __amdgpu_buffer_rsrc_t rq[2], rs[2], rb[2];
-    if (GATEUP) {
-        rq[0] = buf_rsrc(q.gate_q + (size_t)e * ROWS_W * WPR, qbytes);
-        rq[1] = buf_rsrc(q.up_q + (size_t)e * ROWS_W * WPR, qbytes);
-        rs[0] = buf_rsrc(q.gate_s + (size_t)e * ROWS_W * SPR, sbytes);
-        rs[1] = buf_rsrc(q.up_s + (size_t)e * ROWS_W * SPR, sbytes);
-        rb[0] = buf_rsrc(q.gate_b + (size_t)e * ROWS_W * SPR, sbytes);
-        rb[1] = buf_rsrc(q.up_b + (size_t)e * ROWS_W * SPR, sbytes);
+struct GemmArgs {
+    const uint16_t* ain;      // A rows: x (fp16, slot order) [T][2048] or h [9T][512]
+    uint32_t ain_bytes;
+    int T;
+    const int32_t* perm;      // sorted position -> flat slot 8t+j (gate/up gathers x rows)
+    uint16_t* hout;           // gate/up: h fp16 [9T][512]
+    float* dout32;            // down, split interface: d fp32 [9T][2048]
+    uint16_t* dout16;         // down, fused layer: fp16 coef*d [9T][2048]
+    const float* wsorted;     // routing weight of each sorted position [8T]
+    const float* sg;          // shared-expert gate per token [T]
+};
+
+namespace pg {
+constexpr int WAVES = 4;
+constexpr int THREADS = WAVES * 64;
+constexpr int MT = MT_ROWS;                 // rows per tile, at most
+constexpr int NMT_MAX = MT / 32;             // 32-row m-tiles
+constexpr int KC = G;                       // K per chunk: one quantisation group
+constexpr int STAGES = 5;                   // chunk c+5 refills chunk c's stage once
+                                            // every wave is past its last read of it
+constexpr int AROW = KC * 2;                // bytes of one A row per chunk
+constexpr int A_BYTES = MT * AROW;
+constexpr int NCOL = 256;                   // weight rows per item
+constexpr int B_BYTES = NCOL * KC / 2;
+constexpr int S_BYTES = NCOL * 4;
+constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
+constexpr int META = WAVES * 256;           // per-item row metadata (tokens or weights):
+                                            // one 4-byte direct load (256 B) per wave
+constexpr int STG = 1024;                   // per-wave epilogue staging
+constexpr int LDS_BYTES = STAGES * STAGE + 2 * META + WAVES * STG;
+constexpr int A_LOADS = MT / 8 / WAVES;     // 1 KB (8 rows) per load instruction
+constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
+constexpr int LPC = A_LOADS + B_LOADS + 2;  // loads per wave per chunk
+constexpr uint32_t OOB = 0x80000000u;       // beyond every buffer: no memory access
+static_assert(MT % (8 * WAVES) == 0, "A rows must split evenly over the load instructions");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(META >= MT * 4, "row metadata must cover a tile");
+static_assert((STAGES - 2) * LPC + 1 <= 63, "vmcnt range");
+}  // namespace pg
+
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
+
+// Wave index within the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+struct GItem {
+    int valid;       // 0: past the last item (its loads are dummies)
+    int shared;      // group 256 (the shared expert)
+    int e;           // routed expert (0 for the shared one)
+    int row0, nrows, nb;
+};
+
+template <int NB>
+__device__ __forceinline__ GItem gemm_item(int it, int n_items, const Tile* __restrict__ tiles) {
+    GItem m;
+    m.valid = it < n_items;
+    const Tile tl = tiles[m.valid ? it / NB : 0];
+    m.shared = tl.group >= E;
+    m.e = (m.shared || !m.valid) ? 0 : tl.group;
+    m.row0 = tl.row0;
+    m.nrows = m.valid ? tl.nrows : 0;
+    m.nb = m.valid ? it % NB : 0;
+    return m;
+}
+
+// Where one item's chunks come from, per lane: the A rows this lane moves
+// and the code/scale words of this wave's weight rows.  Chunk kc adds a
+// wave-uniform offset (the soffset operand of the loads), so issuing a chunk
+// costs no vector arithmetic.  Rows past the tile and items past the last
+// get out-of-range offsets (the loads access no memory and fill zeros).
+struct GSrc {
+    __amdgpu_buffer_rsrc_t rq, rs, rb;   // this wave's code / scale / bias matrix
+    uint32_t a[pg::A_LOADS];             // A: instruction i -> rows (w*A_LOADS + i)*8 + lane/8
+    uint32_t b[pg::B_LOADS];             // B: instruction i -> columns (w*B_LOADS + i)*32 + lane/2
+    uint32_t s;                          // scale/bias dword of column w*64 + lane
+};
+
+// The code/scale/bias pointers of one weight matrix of one expert stack.
+struct WPtr {
+    const uint32_t* q;
+    const uint16_t* s;
+    const uint16_t* b;
+};
+
+// This wave's matrix (gate/up: waves 0-1 gate, 2-3 up; down: down) of one
+// stack, as opaque register values: a later choice between the routed and
+// the shared stack is then a select of values, never of the argument
+// structs' addresses (which would force the structs into scratch memory).
+template <int MODE>
+__device__ __forceinline__ WPtr wave_ptrs(const moe_qffn& f) {
+    WPtr w;
+    if (MODE != GM_GATEUP) {
+        w.q = f.down_q; w.s = f.down_s; w.b = f.down_b;
+    } else if (wave_id() >= 2) {
+        w.q = f.up_q; w.s = f.up_s; w.b = f.up_b;
     } else {
-        rq[0] = rq[1] = buf_rsrc(q.down_q + (size_t)e * ROWS_W * WPR, qbytes);
-        rs[0] = rs[1] = buf_rsrc(q.down_s + (size_t)e * ROWS_W * SPR, sbytes);
-        rb[0] = rb[1] = buf_rsrc(q.down_b + (size_t)e * ROWS_W * SPR, sbytes);
+        w.q = f.gate_q; w.s = f.gate_s; w.b = f.gate_b;
     }
-    uint32_t qoff[4], soff[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int n = GATEUP ? nb * NBW + wave * 32 + (nt & 1) * 16 + r
-                             : nb * NBW + wave * 64 + nt * 16 + r;
-        qoff[nt] = ((uint32_t)n * WPR + 4 * j) * 4;
-        soff[nt] = ((uint32_t)n * SPR + (j >> 1)) * 2;
-    }
-    auto mat = [](int nt) { return GATEUP ? (nt >> 1) : 0; };
+    asm volatile("" : "+s"(w.q), "+s"(w.s), "+s"(w.b));
+    return w;
+}
 
-    // ---- A: per-lane source offsets of the 4 pieces moved per chunk.
-    // Load instruction i of wave w fills tile rows w*16 + 4i .. +3 (1 KB):
-    // lane -> row w*16 + 4i + (lane >> 4), LDS slot (lane & 15), holding the
-    // row's piece (lane & 15) ^ (row & 15).
-    const __amdgpu_buffer_rsrc_t ra = buf_rsrc(A.ain, A.ain_bytes);
-    uint32_t aoff[4];
+template <int KDIM, int MODE>
+__device__ __forceinline__ GSrc gemm_src(const GItem& m, const int32_t* tok, int T,
+                                         const WPtr& pr, const WPtr& ps) {
+    constexpr bool GATEUP = MODE == GM_GATEUP;
+    constexpr int WPR = KDIM / 8, SPR = KDIM / G, ROWS_W = GATEUP ? I : H;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    GSrc g;
+    // A: LDS slot (lane & 7) of row R holds the row's piece slot ^ ((R >> 1) & 7)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = wave * 16 + i * 4 + (lane >> 4);
-        const int rr = row < nr ? row : 0;
-        const int src = GATEUP ? row_token(tl.row0 + rr, A.T, A.perm) : tl.row0 + rr;
-        aoff[i] = (uint32_t)src * (uint32_t)(KDIM * 2) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+    for (int i = 0; i < pg::A_LOADS; ++i) {
+        const int R = (wave * pg::A_LOADS + i) * 8 + (lane >> 3);
+        const int p = (lane & 7) ^ ((R >> 1) & 7);
+        int src = m.row0 + R;
+        if (GATEUP) src = m.shared ? m.row0 + R - TOPK * T : min(max(tok[R] >> 3, 0), T - 1);
+        g.a[i] = R < m.nrows ? (uint32_t)src * (uint32_t)(KDIM * 2) + 16u * (uint32_t)p : pg::OOB;
     }
-    // rows this wave moves: w*16 .. w*16+15, needed only below NMT*16
-    const bool amove = wave * 16 < NMT * 16;
-    auto issue_a = [&](int kc) {
-        uint8_t* dst = As + (kc % GSTAGES) * BUFB + wave * 16 * CHB;
+    const uint32_t* code = m.shared ? ps.q : pr.q;
+    const uint16_t* sc = m.shared ? ps.s : pr.s;
+    const uint16_t* bi = m.shared ? ps.b : pr.b;
+    const size_t eo = (size_t)m.e * ROWS_W;
+    g.rq = buf_rsrc(code + eo * WPR, ROWS_W * WPR * 4);
+    g.rs = buf_rsrc(sc + eo * SPR, ROWS_W * SPR * 2);
+    g.rb = buf_rsrc(bi + eo * SPR, ROWS_W * SPR * 2);
+    auto wrow = [&](int C) { return GATEUP ? m.nb * 128 + (C & 127) : m.nb * 256 + C; };
+    // B: LDS slot (lane & 1) of column C holds the column's piece slot ^ ((C >> 3) & 1)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (amove)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + i * 4 * CHB), 16,
-                                                         aoff[i], kc * CHB, 0, 0);
-    };
+    for (int i = 0; i < pg::B_LOADS; ++i) {
+        const int C = (wave * pg::B_LOADS + i) * 32 + (lane >> 1);
+        const int p = (lane & 1) ^ ((C >> 3) & 1);
+        g.b[i] = m.valid ? (uint32_t)(wrow(C) * WPR * 4 + 16 * p) : pg::OOB;
+    }
+    g.s = m.valid ? (uint32_t)(wrow(wave * 64 + lane) * SPR * 2) : pg::OOB;
+    return g;
+}
 
-    float4v acc[NMT][4];
+template <int SIZE>
+__device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voff,
+                                         uint32_t soff) {
+    static_assert(SIZE == 4 || SIZE == 16, "direct-to-LDS load size");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, voff, soff, 0, 0);
+}
+
+// The LPC loads of chunk kc of an item into one stage.
+__device__ __forceinline__ void issue_chunk(const GSrc& g, int kc, __amdgpu_buffer_rsrc_t ra,
+                                            uint8_t* stage) {
+    const int wave = wave_id();
+#pragma unroll
+    for (int i = 0; i < pg::A_LOADS; ++i)
+        load_lds<16>(ra, stage + (wave * pg::A_LOADS + i) * 1024, g.a[i], kc * pg::AROW);
+#pragma unroll
+    for (int i = 0; i < pg::B_LOADS; ++i)
+        load_lds<16>(g.rq, stage + pg::A_BYTES + (wave * pg::B_LOADS + i) * 1024, g.b[i], kc * 32);
+    load_lds<4>(g.rs, stage + pg::A_BYTES + pg::B_BYTES + wave * 256, g.s, (kc & ~1) * 2);
+    load_lds<4>(g.rb, stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + wave * 256, g.s, (kc & ~1) * 2);
+}
+
+// MFMA: v_mfma_f32_32x32x16_f16 (32 rows x 32 columns x 16 k).  Lane l
+// holds A row l%32 and B column l%32 for k = 8*(l/32)..+7, and accumulator
+// element i of row 8*(i/4) + 4*(l/32) + i%4, column l%32.  (The 16x16x32
+// shape issues at well under half the matrix-core rate on this chip.)
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+// LDS column (0..255 of the item) of wave w's n-tile nt, lane column l%32:
+// gate/up: n-tile 0 = gate rows w*32.., n-tile 1 = the same up rows;
+// down: 64 consecutive rows per wave.
+template <bool GATEUP>
+__device__ __forceinline__ int gemm_col(int wave, int nt, int l32) {
+    return GATEUP ? nt * 128 + wave * 32 + l32 : wave * 64 + nt * 32 + l32;
+}
+
+// K order inside a 64-wide chunk: MFMA step s (0..3), lane half g = l/32
+// covers the 8-wide k-piece 4g + s.  A lane therefore needs one contiguous
+// 16-byte half (words 4g..4g+3) of each of its columns' 32 code bytes.
+struct BFrag {
+    uint4v w[2];          // words of steps 0..3, per n-tile
+    half2v s[2], b[2];    // fp16 scale / bias, splat
+};
+
+template <bool GATEUP>
+__device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int l32 = lane & 31, g = lane >> 5;
+    BFrag B;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int C = gemm_col<GATEUP>(wave, nt, l32);
+        B.w[nt] = *reinterpret_cast<const uint4v*>(stage + pg::A_BYTES + C * 32 + 16 * (g ^ ((C >> 3) & 1)));
+        const uint32_t sd = *reinterpret_cast<const uint32_t*>(stage + pg::A_BYTES + pg::B_BYTES + C * 4);
+        const uint32_t bd =
+            *reinterpret_cast<const uint32_t*>(stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + C * 4);
+        B.s[nt] = splat_h((uint16_t)((kc & 1) ? sd >> 16 : sd));
+        B.b[nt] = splat_h((uint16_t)((kc & 1) ? bd >> 16 : bd));
+    }
+    return B;
+}
+
+// A operand of K-step s: row mt*32 + l%32, k-piece 4g + s.
+template <int NMT>
+__device__ __forceinline__ void read_a(const uint8_t* stage, int s, half8 (&a)[NMT]) {
+    const int lane = threadIdx.x & 63;
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+        const int R = mt * 32 + l32;
+        a[mt] = *reinterpret_cast<const half8*>(stage + R * pg::AROW + 16 * ((4 * g + s) ^ ((R >> 1) & 7)));
+    }
+}
+
+__device__ __forceinline__ void dequant_step(const BFrag& B, int s, half8 (&bf)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t wv = B.w[nt][s];
+        bf[nt] = dequant8(wv, B.s[nt], B.b[nt]);
+    }
+}
+
+template <int NMT>
+__device__ __forceinline__ void mfma_step(const half8 (&a)[NMT], const half8 (&bf)[2],
+                                          float16v (&acc)[NMT][2]) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (float4v){0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+}
 
-    // B of the next chunk is loaded into registers one chunk ahead.  Scale
-    // and bias stay raw fp16 bits until they are used, so that no arithmetic
-    // on a just-issued load forces the wave to wait for it.
-    uint4v bw[4];
-    uint32_t bs[4], bb[4];
-    issue_a(0);
-    if (NCH > 1) issue_a(1);
+// Scheduling hint for one MFMA step: its operand reads first, then MFMAs
+// alternating with the VALU work of the next step's dequantisation.
+template <int NMT, int DS_READS>
+__device__ __forceinline__ void sched_step() {
+    constexpr int NM = 2 * NMT;
+    constexpr int V = (32 + NM - 1) / NM;     // ~30 VALU per step's dequantisation
+    __builtin_amdgcn_sched_group_barrier(0x100, DS_READS, 0);      // DS read
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rq[mat(nt)], qoff[nt], 0, 0);
-        bs[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], 0, 0);
-        bb[nt] = __builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], 0, 0);
+    for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);          // VALU
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+}
 
-    for (int kc = 0; kc < NCH; ++kc) {
-        uint4v cw[4];
-        half2v cs[4], cb[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            cw[nt] = bw[nt];
-            cs[nt] = splat_h((uint16_t)bs[nt]);
-            cb[nt] = splat_h((uint16_t)bb[nt]);
-        }
-        if (kc + 1 < NCH) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rq[mat(nt)], qoff[nt], (kc + 1) * 64, 0);
-                bs[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs[mat(nt)], soff[nt], (kc + 1) * 4, 0);
-                bb[nt] = __builtin_amdgcn_raw_buffer_load_b16(rb[mat(nt)], soff[nt], (kc + 1) * 4, 0);
-            }
-        }
-        const bool more = kc + 2 < NCH;
-        if (more) issue_a(kc + 2);
-        const uint8_t* Ab = As + (kc % GSTAGES) * BUFB;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            half8 a[NMT], bf[4];
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-                a[mt] = *reinterpret_cast<const half8*>(&Ab[(mt * 16 + r) * CHB + 16 * ((4 * j + s) ^ r)]);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) bf[nt] = dequant8(cw[nt][s], cs[nt], cb[nt]);
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], bf[nt], acc[mt][nt], 0, 0, 0);
-        }
-        // chunk kc+1 (A and B) must have landed; chunk kc+2's A may stay in flight
-        if (more && amove) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        pipe_barrier();
-    }
+// Stores per wave per epilogue (one 16-byte store per lane per 1 KB staged).
+template <int MODE>
+constexpr int epi_stores() {
+    return MODE == GM_GATEUP ? 2 * pg::NMT_MAX : MODE == GM_DOWN_F16W ? 4 * pg::NMT_MAX : 8 * pg::NMT_MAX;
+}
 
-    if constexpr (GATEUP) {
-        // h = bf16(silu(g) * u) stored as fp16 (exact) in chunk-slot order,
-        // staged through LDS for 16-byte stores.
-        uint16_t* Hs = reinterpret_cast<uint16_t*>(As);    // [128][NBW + 8] halves
-        constexpr int HST = NBW + 8;                         // NBW h columns per block
-        static_assert(MT_ROWS * HST * 2 <= GSTAGES * BUFB, "staging tile exceeds the A buffers");
+// Staging through LDS moves values between lanes of one wave.  The wave's
+// LDS operations execute in program order, but the compiler reasons per
+// lane: a lane's read of its own 16 bytes does not alias its own writes, so
+// without this fence it could hoist the read above the other lanes' writes
+// (or the next round's writes above the read).
+__device__ __forceinline__ void lane_exchange_fence() {
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Accumulator element i of a lane lies in staged half hr = i/8 of the
+// m-tile (rows 16*hr .. 16*hr+15), at staged row 8*((i/4)&1) + 4g + i%4.
+template <int MODE, int NMT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
+                                              float16v (&acc)[NMT][2], uint8_t* stg,
+                                              const float* coef) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int l32 = lane & 31, g = lane >> 5;
+    const int T = A.T;
+    const int Rl = lane >> 2;           // staged row read back by this lane
+    if constexpr (MODE == GM_GATEUP) {
+        const __amdgpu_buffer_rsrc_t rh = buf_rsrc(A.hout, (uint32_t)((size_t)(TOPK + 1) * T * I * 2));
+        uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [16][32] fp16, slot order
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
+        for (int mt = 0; mt < pg::NMT_MAX; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int hr = 0; hr < 2; ++hr) {
+                uint4v v = (uint4v){0u, 0u, 0u, 0u};
+                uint32_t off = pg::OOB;
+                if (mt < NMT) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = mt * 16 + 4 * j + i;
-                    const int col = wave * 32 + nt * 16 + r;
-                    const float g = acc[mt][nt][i], u = acc[mt][nt + 2][i];
-                    const float hv = (g / (1.f + __expf(-g))) * u;
-                    const _Float16 hh = (_Float16)bf16_to_f32(f32_to_bf16(hv));
-                    Hs[row * HST + (col & ~7) + chunk_slot(col & 7)] =
-                        __builtin_bit_cast(uint16_t, hh);
-                }
-            }
-        }
-        __syncthreads();
-        constexpr int PR = NBW / 8;          // 16-byte pieces per staged row
-        for (int c = tid; c < nr * PR; c += GW * 64) {
-            const int row = c / PR, col = (c % PR) * 8;
-            *reinterpret_cast<uint4v*>(A.hout + (size_t)(tl.row0 + row) * I + nb * NBW + col) =
-                *reinterpret_cast<const uint4v*>(&Hs[row * HST + col]);
-        }
-    } else if constexpr (MODE == GM_DOWN_F32) {
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = mt * 16 + 4 * j + i;
-                    if (row < nr)
-                        A.dout32[(size_t)(tl.row0 + row) * H + nb * NBW + wave * 64 + nt * 16 + r] =
-                            acc[mt][nt][i];
-                }
-            }
-        }
-    } else {
-        // fp16 rows of coef * d, staged through LDS for 16-byte stores, one
-        // half of the block's columns (four waves) at a time
-        uint16_t* Ds = reinterpret_cast<uint16_t*>(As);
-        constexpr int HALF = NBW / 2;
-        constexpr int DST = HALF + 8;
-        static_assert(MT_ROWS * DST * 2 <= GSTAGES * BUFB, "staging tile exceeds the A buffers");
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            if ((wave >> 2) == hf) {
-#pragma unroll
-                for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int row = mt * 16 + 4 * j + i;
-                            const int col = (wave & 3) * 64 + nt * 16 + r;
-                            const float v = row < nr ? coef[row] * acc[mt][nt][i] : 0.f;
-                            Ds[row * DST + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
-                        }
+                    for (int q = 0; q < 8; ++q) {
+                        const int i = hr * 8 + q;
+                        const float gv = acc[mt < NMT ? mt : 0][0][i];
+                        const float uv = acc[mt < NMT ? mt : 0][1][i];
+                        const float hv = __fdividef(gv, 1.f + __expf(-gv)) * uv;
+                        const _Float16 hh = (_Float16)bf16_to_f32(f32_to_bf16(hv));
+                        const int row = 8 * (q >> 2) + 4 * g + (q & 3);
+                        st[row * 32 + (l32 & ~7) + chunk_slot(l32 & 7)] = __builtin_bit_cast(uint16_t, hh);
                     }
+                    lane_exchange_fence();
+                    v = reinterpret_cast<const uint4v*>(stg)[lane];
+                    lane_exchange_fence();
+                    const int R = mt * 32 + hr * 16 + Rl;
+                    if (R < m.nrows)
+                        off = (uint32_t)(((m.row0 + R) * I + m.nb * 128 + wave * 32 + (lane & 3) * 8) * 2);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(v, rh, off, 0, 0);
+            }
+    } else if constexpr (MODE == GM_DOWN_F16W) {
+        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(A.dout16, (uint32_t)((size_t)(TOPK + 1) * T * H * 2));
+        uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [16][32] fp16
+#pragma unroll
+        for (int mt = 0; mt < pg::NMT_MAX; ++mt)
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr) {
+                float4v cf[2] = {(float4v){0.f, 0.f, 0.f, 0.f}, (float4v){0.f, 0.f, 0.f, 0.f}};
+                if (mt < NMT) {
+                    cf[0] = *reinterpret_cast<const float4v*>(coef + mt * 32 + hr * 16 + 4 * g);
+                    cf[1] = *reinterpret_cast<const float4v*>(coef + mt * 32 + hr * 16 + 8 + 4 * g);
+                }
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    uint4v v = (uint4v){0u, 0u, 0u, 0u};
+                    uint32_t off = pg::OOB;
+                    if (mt < NMT) {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const float d = acc[mt < NMT ? mt : 0][nt][hr * 8 + q] * cf[q >> 2][q & 3];
+                            const int row = 8 * (q >> 2) + 4 * g + (q & 3);
+                            st[row * 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)d);
+                        }
+                        lane_exchange_fence();
+                    v = reinterpret_cast<const uint4v*>(stg)[lane];
+                    lane_exchange_fence();
+                        const int R = mt * 32 + hr * 16 + Rl;
+                        if (R < m.nrows)
+                            off = (uint32_t)(((size_t)(m.row0 + R) * H + m.nb * 256 + wave * 64 + nt * 32 +
+                                              (lane & 3) * 8) * 2);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
                 }
             }
-            __syncthreads();
-            constexpr int PR = HALF / 8;
-            for (int c = tid; c < nr * PR; c += GW * 64) {
-                const int row = c / PR, col = (c % PR) * 8;
-                *reinterpret_cast<uint4v*>(A.dout16 + (size_t)(tl.row0 + row) * H + nb * NBW +
-                                           hf * HALF + col) =
-                    *reinterpret_cast<const uint4v*>(&Ds[row * DST + col]);
-            }
-            __syncthreads();
+    } else {
+        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(A.dout32, (uint32_t)((size_t)(TOPK + 1) * T * H * 4));
+        float* st = reinterpret_cast<float*>(stg);          // [16][16] fp32
+#pragma unroll
+        for (int mt = 0; mt < pg::NMT_MAX; ++mt)
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int ch = 0; ch < 2; ++ch) {
+                        uint4v v = (uint4v){0u, 0u, 0u, 0u};
+                        uint32_t off = pg::OOB;
+                        if (mt < NMT) {
+                            if ((l32 >> 4) == ch) {
+#pragma unroll
+                                for (int q = 0; q < 8; ++q) {
+                                    const int row = 8 * (q >> 2) + 4 * g + (q & 3);
+                                    st[row * 16 + (l32 & 15)] = acc[mt < NMT ? mt : 0][nt][hr * 8 + q];
+                                }
+                            }
+                            lane_exchange_fence();
+                    v = reinterpret_cast<const uint4v*>(stg)[lane];
+                    lane_exchange_fence();
+                            const int R = mt * 32 + hr * 16 + Rl;
+                            if (R < m.nrows)
+                                off = (uint32_t)(((size_t)(m.row0 + R) * H + m.nb * 256 + wave * 64 + nt * 32 +
+                                                  ch * 16 + (lane & 3) * 4) * 4);
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+                    }
+    }
+}
+
+// Per-item row metadata, one load per wave at the first chunk of an item:
+// gate/up loads the NEXT item's permutation entries (token of each row),
+// down/fp16 loads the CURRENT item's row weights.  Waves 0-2 cover rows
+// 0..191; the fourth wave's load is a dummy that keeps the count uniform.
+template <int MODE>
+__device__ __forceinline__ void issue_meta(const GemmArgs& A, const GItem& m, uint8_t* meta) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int R = wave * 64 + lane;
+    const int T = A.T;
+    const bool use = m.valid && wave < 3 && R < m.nrows;
+    if constexpr (MODE == GM_GATEUP) {
+        const __amdgpu_buffer_rsrc_t rp = buf_rsrc(A.perm, (uint32_t)(TOPK * T * 4));
+        const uint32_t off = use && !m.shared ? (uint32_t)((m.row0 + R) * 4) : pg::OOB;
+        load_lds<4>(rp, meta + wave * 256, off, 0);
+    } else if constexpr (MODE == GM_DOWN_F16W) {
+        const __amdgpu_buffer_rsrc_t rw =
+            m.shared ? buf_rsrc(A.sg, (uint32_t)(T * 4)) : buf_rsrc(A.wsorted, (uint32_t)(TOPK * T * 4));
+        const int idx = m.shared ? m.row0 + R - TOPK * T : m.row0 + R;
+        const uint32_t off = use ? (uint32_t)(idx * 4) : pg::OOB;
+        load_lds<4>(rw, meta + wave * 256, off, 0);
+    } else {
+        const __amdgpu_buffer_rsrc_t rp = buf_rsrc(A.perm, 4);
+        load_lds<4>(rp, meta + wave * 256, pg::OOB, 0);
+    }
+}
+
+// One item: NCH chunks of MFMAs, then the epilogue.  Each chunk is
+// software-pipelined around the workgroup barrier: K-steps 0..2 run before
+// it (each step's MFMAs hide the next step's operand reads and
+// dequantisation); after it, while step 3's MFMAs run, this chunk's stage is
+// refilled with chunk c+5 (the ring runs on into the next item) and the next
+// chunk's operands are read and its step 0 dequantised.  Only the first
+// chunk of an item dequantises with no MFMAs to hide under.
+template <int KDIM, int MODE, int NMT>
+__device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cur, const GItem& nxt,
+                                              const GSrc& src_cur, GSrc& src_nxt, int& gc, int k,
+                                              bool first, __amdgpu_buffer_rsrc_t ra,
+                                              const WPtr& pr, const WPtr& ps, uint8_t* lds) {
+    constexpr bool GATEUP = MODE == GM_GATEUP;
+    constexpr int NCH = KDIM / pg::KC;
+    constexpr int S_EPI = epi_stores<MODE>();
+    constexpr int BASE = (pg::STAGES - 2) * pg::LPC;     // loads of the 3 chunks behind the awaited one
+    // (a count larger than the operations really issued after the awaited
+    // chunk would not wait for it; a smaller one only waits longer)
+    constexpr int W_S = BASE + S_EPI < 63 ? BASE + S_EPI : 63;
+    constexpr int W_XS = BASE + 1 + S_EPI < 63 ? BASE + 1 + S_EPI : 63;
+    uint8_t* meta = lds + pg::STAGES * pg::STAGE;
+    uint8_t* stg = meta + 2 * pg::META + wave_id() * pg::STG;
+    float16v acc[NMT][2];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (float16v)0.f;
+
+    half8 a_cur[NMT], bf_cur[2];
+    BFrag B = read_b<GATEUP>(lds + (gc % pg::STAGES) * pg::STAGE, 0);
+    read_a<NMT>(lds + (gc % pg::STAGES) * pg::STAGE, 0, a_cur);
+    dequant_step(B, 0, bf_cur);
+
+    // One chunk.  `refill(stage)` issues the loads of chunk c+5 into the
+    // stage chunk c has just released.
+    auto chunk = [&](int c, auto&& refill) {
+        const uint8_t* st = lds + (gc % pg::STAGES) * pg::STAGE;
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            half8 a_nx[NMT], bf_nx[2];
+            read_a<NMT>(st, s + 1, a_nx);
+            dequant_step(B, s + 1, bf_nx);
+            mfma_step<NMT>(a_cur, bf_cur, acc);
+            sched_step<NMT, NMT>();
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = a_nx[mt];
+            bf_cur[0] = bf_nx[0];
+            bf_cur[1] = bf_nx[1];
+        }
+
+        // chunk c+1 must have landed (issued 4 refills ago).  Issued after it
+        // and allowed to stay in flight: the loads of the next three chunks
+        // (BASE), this item's metadata load (issued after the wait of c = 0,
+        // counted for c = 1..4) and, for c <= 3, the previous item's epilogue
+        // stores.
+        if (!first && c == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(W_S));
+        else if (!first && c <= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(W_XS));
+        else if (c >= 1 && c <= 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE + 1));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE));
+        pipe_barrier();
+
+        // step 3 of this chunk under the next chunk's reads, the refill and
+        // the next chunk's first dequantisation
+        const bool more = c + 1 < NCH;
+        half8 a_nx[NMT], bf_nx[2];
+        if (more) {
+            const uint8_t* sn = lds + ((gc + 1) % pg::STAGES) * pg::STAGE;
+            B = read_b<GATEUP>(sn, c + 1);
+            read_a<NMT>(sn, 0, a_nx);
+        }
+        refill(const_cast<uint8_t*>(st));
+        if (more) dequant_step(B, 0, bf_nx);
+        mfma_step<NMT>(a_cur, bf_cur, acc);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6 + NMT, 0);       // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, pg::LPC + 1, 0);   // refill loads
+#pragma unroll
+        for (int i = 0; i < 2 * NMT - 1; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, (40 + 2 * NMT - 2) / (2 * NMT - 1), 0);
+        }
+        if (more) {
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = a_nx[mt];
+            bf_cur[0] = bf_nx[0];
+            bf_cur[1] = bf_nx[1];
+        }
+        ++gc;
+    };
+    auto own = [&](int c) { return [&, c](uint8_t* st) { issue_chunk(src_cur, c + pg::STAGES, ra, st); }; };
+    auto next = [&](int c) {
+        return [&, c](uint8_t* st) { issue_chunk(src_nxt, c + pg::STAGES - NCH, ra, st); };
+    };
+    // the next item's sources (its row tokens arrived with this item's first chunk)
+    auto make_next = [&]() {
+        src_nxt = gemm_src<KDIM, MODE>(nxt, reinterpret_cast<const int32_t*>(meta + ((k + 1) & 1) * pg::META),
+                                       A.T, pr, ps);
+    };
+
+    constexpr int MAIN = NCH - pg::STAGES;      // chunks whose refill stays in this item
+    constexpr int HEAD = 5;                     // chunks with special wait counts
+    static_assert(MAIN >= 1, "an item needs more chunks than pipeline stages");
+    // head: unrolled, so every wait count and refill target is a constant
+    chunk(0, [&](uint8_t* st) {
+        issue_chunk(src_cur, pg::STAGES, ra, st);
+        issue_meta<MODE>(A, GATEUP ? nxt : cur, meta + ((GATEUP ? k + 1 : k) & 1) * pg::META);
+    });
+#pragma unroll
+    for (int c = 1; c < HEAD; ++c) {
+        if (c < MAIN) chunk(c, own(c));
+        else {
+            if (c == MAIN) make_next();
+            chunk(c, next(c));
         }
     }
+    // main: one basic block per chunk
+    for (int c = HEAD; c < MAIN; ++c) chunk(c, own(c));
+    if (MAIN >= HEAD) make_next();
+    // tail: refills from the next item
+#pragma unroll
+    for (int c = (MAIN > HEAD ? MAIN : HEAD); c < NCH; ++c) chunk(c, next(c));
+    gemm_epilogue<MODE, NMT>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
 }
 
-// Grouped expert GEMM: a 1-D grid of (row tile, column block) work items.
-// Work is split into 8 contiguous ranges, one per XCD (workgroup ids are
-// dealt to the 8 XCDs round-robin), so the column blocks of a tile run back
-// to back on the same XCD and re-read its activation rows from that XCD's
-// L2.  The tile's m-tile count selects a fully unrolled instance.
-//   GM_GATEUP:    K = 2048, 256 gate + 256 up columns per block,
-//                 h = bf16(silu(g) u) written as fp16 in chunk-slot order
-//   GM_DOWN_F32:  K = 512, 512 output columns per block, fp32 rows
-//   GM_DOWN_F16W: as above, fp16 rows pre-multiplied by the routing weight
-//                 (or the shared gate) for the fused combine
 template <int KDIM, int MODE>
-__global__ __launch_bounds__(GW * 64, 1) void expert_gemm(GemmArgs args,
-                                                          const Tile* __restrict__ tiles,
-                                                          const int* __restrict__ tile_count,
-                                                          moe_qffn routed, moe_qffn shared) {
-    constexpr int NB = MODE == GM_GATEUP ? I / (GW * 32) : H / (GW * 64);
-    __shared__ __attribute__((aligned(16))) uint8_t As[GSTAGES * BUFB];
-    __shared__ float coef[MT_ROWS];
-    const int total = *tile_count * NB;
-    const int per_xcd = (total + 7) / 8;
-    const int local = blockIdx.x / 8;
-    if (local >= per_xcd) return;
-    const int w = (blockIdx.x % 8) * per_xcd + local;
-    if (w >= total) return;
-    const Tile tl = tiles[w / NB];
-    const int nb = w % NB;
-    const bool sh = tl.group >= E;
-    const int e = sh ? 0 : tl.group;
-    const moe_qffn& q = sh ? shared : routed;
-    if (MODE == GM_DOWN_F16W && (int)threadIdx.x < tl.nrows) {
-        const int p = tl.row0 + threadIdx.x;
-        const int T = args.T;
-        coef[threadIdx.x] = p < TOPK * T ? args.wts[min(max(args.perm[p], 0), TOPK * T - 1)]
-                                         : args.sg[p - TOPK * T];
-    }
-    switch ((tl.nrows + 15) >> 4) {
-        case 1: gemm_tile<KDIM, MODE, 1>(args, tl, q, e, nb, As, coef); break;
-        case 2: gemm_tile<KDIM, MODE, 2>(args, tl, q, e, nb, As, coef); break;
-        case 3: gemm_tile<KDIM, MODE, 3>(args, tl, q, e, nb, As, coef); break;
-        case 4: gemm_tile<KDIM, MODE, 4>(args, tl, q, e, nb, As, coef); break;
-        case 5: gemm_tile<KDIM, MODE, 5>(args, tl, q, e, nb, As, coef); break;
-        case 6: gemm_tile<KDIM, MODE, 6>(args, tl, q, e, nb, As, coef); break;
-        case 7: gemm_tile<KDIM, MODE, 7>(args, tl, q, e, nb, As, coef); break;
-        default: gemm_tile<KDIM, MODE, 8>(args, tl, q, e, nb, As, coef); break;
-    }
-}
+__global__ __launch_bounds__(pg::THREADS, 1) void grouped_gemm(GemmArgs args,
+                                                              const Tile* __restrict__ tiles,
+                                                              const int* __restrict__ tile_count,
+                                                              moe_qffn routed, moe_qffn shared) {
+    constexpr bool GATEUP = MODE == GM_GATEUP;
+    constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[pg::LDS_BYTES];
+    const int n_items = *tile_count * NB;
+    const int G8 = gridDim.x >> 3;
+    int it = (blockIdx.x & 7) * G8 + (blockIdx.x >> 3);
+    if (it >= n_items) return;
+    const int stride = gridDim.x;
+    uint8_t* meta = lds + pg::STAGES * pg::STAGE;
+    const __amdgpu_buffer_rsrc_t ra = buf_rsrc(args.ain, args.ain_bytes);
 
-// grid size for a GEMM over at most max_tiles tiles and nb column blocks
-static unsigned gemm_grid(int max_tiles, int nb) {
-    const int total = max_tiles * nb;
-    return (unsigned)(8 * ((total + 7) / 8));
+    GItem cur = gemm_item<NB>(it, n_items, tiles);
+    GItem nxt = gemm_item<NB>(it + stride, n_items, tiles);
+    if (GATEUP) {
+        // the first item's permutation entries, before any of its rows can move
+        issue_meta<MODE>(args, cur, meta);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+    }
+    const WPtr pr = wave_ptrs<MODE>(routed), ps = wave_ptrs<MODE>(shared);
+    GSrc src_cur = gemm_src<KDIM, MODE>(cur, reinterpret_cast<const int32_t*>(meta), args.T, pr, ps);
+    GSrc src_nxt = src_cur;
+    for (int c = 0; c < pg::STAGES; ++c) issue_chunk(src_cur, c, ra, lds + c * pg::STAGE);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((pg::STAGES - 1) * pg::LPC));   // chunk 0 landed
+    pipe_barrier();
+
+    int gc = 0;
+    for (int k = 0;; ++k) {
+        switch ((cur.nrows + 31) >> 5) {
+#define PG_CASE(n) \
+    case n: gemm_run_item<KDIM, MODE, n>(args, cur, nxt, src_cur, src_nxt, gc, k, k == 0, ra, pr, ps, lds); break;
+            PG_CASE(1) PG_CASE(2) PG_CASE(3) PG_CASE(4)
+            default: gemm_run_item<KDIM, MODE, pg::NMT_MAX>(args, cur, nxt, src_cur, src_nxt, gc, k,
+                                                            k == 0, ra, pr, ps, lds);
+                     break;
+#undef PG_CASE
+        }
+        it += stride;
+        if (!nxt.valid) break;
+        cur = nxt;
+        src_cur = src_nxt;
+        nxt = gemm_item<NB>(it + stride, n_items, tiles);
+    }
 }
 
 // x (bf16) -> fp16 in chunk-slot order, the activation layout of the expert kernels.
@@ -438,57 +765,59 @@ void launch_expert_decode(const uint16_t* x, int T, const int32_t* perm, const T
                        tile_count, routed, shared, dout);
 }
 
-static GemmArgs gemm_args(const uint16_t* ain, uint32_t ain_bytes, int T, const int32_t* perm) {
+static GemmArgs gemm_args(const uint16_t* ain, size_t ain_bytes, int T, const int32_t* perm) {
     GemmArgs a;
     a.ain = ain;
-    a.ain_bytes = ain_bytes;
+    a.ain_bytes = (uint32_t)ain_bytes;
     a.T = T;
     a.perm = perm;
     a.hout = nullptr;
     a.dout32 = nullptr;
     a.dout16 = nullptr;
-    a.wts = nullptr;
+    a.wsorted = nullptr;
     a.sg = nullptr;
     return a;
 }
 
-void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                           const int* tile_count, int max_tiles, const moe_qffn& routed,
-                           const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
-                           hipStream_t st) {
+constexpr unsigned GEMM_GRID = 256;   // one workgroup per compute unit (a multiple of 8 XCDs)
+
+static void launch_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+                          const int* tile_count, const moe_qffn& routed, const moe_qffn& shared,
+                          uint16_t* xh, uint16_t* hbuf, hipStream_t st) {
     const size_t chunks = (size_t)T * (H / 8);
     hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
                        xh);
-    GemmArgs gu = gemm_args(xh, (uint32_t)((size_t)T * H * 2), T, perm);
+    GemmArgs gu = gemm_args(xh, (size_t)T * H * 2, T, perm);
     gu.hout = hbuf;
-    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(gemm_grid(max_tiles, I / (GW * 32))),
-                       dim3(GW * 64), 0, st, gu, tiles, tile_count, routed, shared);
-    GemmArgs dn = gemm_args(hbuf, (uint32_t)((size_t)(TOPK + 1) * T * I * 2), T, perm);
+    hipLaunchKernelGGL((grouped_gemm<H, GM_GATEUP>), dim3(GEMM_GRID), dim3(pg::THREADS), 0, st, gu,
+                       tiles, tile_count, routed, shared);
+}
+
+void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
+                           const int* tile_count, int /*max_tiles*/, const moe_qffn& routed,
+                           const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
+                           hipStream_t st) {
+    launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, st);
+    GemmArgs dn = gemm_args(hbuf, (size_t)(TOPK + 1) * T * I * 2, T, perm);
     dn.dout32 = dout;
-    hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F32>), dim3(gemm_grid(max_tiles, H / (GW * 64))),
-                       dim3(GW * 64), 0, st, dn, tiles, tile_count, routed, shared);
+    hipLaunchKernelGGL((grouped_gemm<I, GM_DOWN_F32>), dim3(GEMM_GRID), dim3(pg::THREADS), 0, st,
+                       dn, tiles, tile_count, routed, shared);
 }
 
 // Whole-layer prefill expert part: gate/up, then down writing fp16 rows of
 // (routing weight or shared gate) * d, summed per token by combine_f16.
 void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                                 const int* tile_count, int max_tiles, const moe_qffn& routed,
+                                 const int* tile_count, int /*max_tiles*/, const moe_qffn& routed,
                                  const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf,
-                                 uint16_t* d16, const float* wts, const float* sg,
+                                 uint16_t* d16, const float* wsorted, const float* sg,
                                  hipStream_t st) {
-    const size_t chunks = (size_t)T * (H / 8);
-    hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
-                       xh);
-    GemmArgs gu = gemm_args(xh, (uint32_t)((size_t)T * H * 2), T, perm);
-    gu.hout = hbuf;
-    hipLaunchKernelGGL((expert_gemm<H, GM_GATEUP>), dim3(gemm_grid(max_tiles, I / (GW * 32))),
-                       dim3(GW * 64), 0, st, gu, tiles, tile_count, routed, shared);
-    GemmArgs dn = gemm_args(hbuf, (uint32_t)((size_t)(TOPK + 1) * T * I * 2), T, perm);
+    launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, st);
+    GemmArgs dn = gemm_args(hbuf, (size_t)(TOPK + 1) * T * I * 2, T, perm);
     dn.dout16 = d16;
-    dn.wts = wts;
+    dn.wsorted = wsorted;
     dn.sg = sg;
-    hipLaunchKernelGGL((expert_gemm<I, GM_DOWN_F16W>), dim3(gemm_grid(max_tiles, H / (GW * 64))),
-                       dim3(GW * 64), 0, st, dn, tiles, tile_count, routed, shared);
+    hipLaunchKernelGGL((grouped_gemm<I, GM_DOWN_F16W>), dim3(GEMM_GRID), dim3(pg::THREADS), 0, st,
+                       dn, tiles, tile_count, routed, shared);
 }
 
 }  // namespace moe

@@ -34,7 +34,8 @@ void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, flo
 size_t route_rec_bytes();
 void launch_zero_words(unsigned* p, int n, hipStream_t st);
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
-                    int32_t* inv, int32_t* chunk_counts, hipStream_t st);
+                    int32_t* inv, int32_t* chunk_counts, hipStream_t st,
+                    const float* wts = nullptr, float* wsorted = nullptr);
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st);
 int perm_chunks(int T);
 int max_tiles(int T);
@@ -49,7 +50,7 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
 void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
                                  const int* tile_count, int max_tiles, const moe_qffn& routed,
                                  const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf,
-                                 uint16_t* d16, const float* wts, const float* sg,
+                                 uint16_t* d16, const float* wsorted, const float* sg,
                                  hipStream_t st);
 void launch_combine_f16(const uint16_t* d16, const int32_t* inv, int T, uint16_t* y,
                         const uint16_t* x, uint16_t* res, hipStream_t st);
@@ -64,8 +65,8 @@ constexpr int SYNC_WORDS = 64;
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct WsLayout {
-    size_t sync, rec, logits, ids, wts, sg, counts, offsets, perm, inv, chunk_counts, tiles, tile_count, xh,
-        h, dout, total;
+    size_t sync, rec, logits, ids, wts, sg, counts, offsets, perm, inv, wsorted, chunk_counts, tiles,
+        tile_count, xh, h, dout, total;
 };
 
 WsLayout ws_layout(int T) {
@@ -87,6 +88,7 @@ WsLayout ws_layout(int T) {
     L.offsets = take((E + 1) * 4);
     L.perm = take(t * TOPK * 4);
     L.inv = take(t * TOPK * 4);
+    L.wsorted = take(t * TOPK * 4);
     L.chunk_counts = take((size_t)perm_chunks(T) * E * 4);
     L.tiles = take((size_t)max_tiles(T) * sizeof(Tile));
     L.tile_count = take(4);
@@ -304,12 +306,14 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
     }
     launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
                  at<float>(ws, L.logits), ids, wts, sg, st);
-    launch_permute(ids, T, counts, offsets, perm, inv, at<int32_t>(ws, L.chunk_counts), st);
+    float* wsorted = at<float>(ws, L.wsorted);
+    launch_permute(ids, T, counts, offsets, perm, inv, at<int32_t>(ws, L.chunk_counts), st, wts,
+                   wsorted);
     launch_plan(offsets, T, tiles, tcount, st);
     // fp16 rows of weight * d (half the bytes of fp32 expert outputs)
     uint16_t* d16 = reinterpret_cast<uint16_t*>(dout);
     launch_expert_prefill_fused(x, T, perm, tiles, tcount, max_tiles(T), layer->routed,
-                                layer->shared, at<uint16_t>(ws, L.xh), hbuf, d16, wts, sg, st);
+                                layer->shared, at<uint16_t>(ws, L.xh), hbuf, d16, wsorted, sg, st);
     launch_combine_f16(d16, inv, T, y, x, res, st);
     return launch_status();
 }

@@ -26,7 +26,9 @@ __global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ counts,
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ perm,
-                                                  int32_t* __restrict__ inv) {
+                                                  int32_t* __restrict__ inv,
+                                                  const float* __restrict__ wsrc,
+                                                  float* __restrict__ wsorted) {
     __shared__ int hist[256];
     __shared__ int base[256];
     __shared__ int wcnt[4 * 256];
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ id
     if (tid == 0) offsets[E] = total;
     base[tid] = off;
     __syncthreads();
-    stable_scatter(ids, 0, n, base, wcnt, perm, inv);
+    stable_scatter(ids, 0, n, base, wcnt, perm, inv, wsrc, wsorted);
 }
 
 __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int n,
@@ -91,7 +93,9 @@ __global__ __launch_bounds__(256) void perm_scan(int nchunks, int32_t* __restric
 __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ ids, int n,
                                                     const int32_t* __restrict__ chunk_base,
                                                     int32_t* __restrict__ perm,
-                                                    int32_t* __restrict__ inv) {
+                                                    int32_t* __restrict__ inv,
+                                                    const float* __restrict__ wsrc,
+                                                    float* __restrict__ wsorted) {
     __shared__ int base[256];
     __shared__ int wcnt[4 * 256];
     const int tid = threadIdx.x;
@@ -100,14 +104,25 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ 
     for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
     __syncthreads();
     const int f0 = blockIdx.x * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
-    stable_scatter(ids, f0, f1, base, wcnt, perm, inv);
+    stable_scatter(ids, f0, f1, base, wcnt, perm, inv, wsrc, wsorted);
 }
 
 // Row tiles: routed expert e owns rows offsets[e] .. offsets[e+1]-1, the
-// shared expert (group 256) owns rows 8T .. 9T-1.  Each group is cut into
-// ceil(n/MT_ROWS) tiles.  At most `cap` tiles are written (offsets from
-// moe_permute never need more than max_tiles(T); malformed caller offsets
-// cannot overrun the tile buffer).
+// shared expert (group 256) owns rows 8T .. 9T-1.  A group of n rows is cut
+// into nt = ceil(n/MT_ROWS) tiles of as equal a size as possible (the first
+// n % nt tiles get one row more), so no group leaves a small remainder tile.
+// At most `cap` tiles are written (offsets from moe_permute never need more
+// than max_tiles(T); malformed caller offsets cannot overrun the buffer).
+__device__ inline Tile balanced_tile(int group, int r0, int n, int nt, int i) {
+    const int base = n / nt, rem = n % nt;
+    Tile tl;
+    tl.group = group;
+    tl.row0 = r0 + i * base + min(i, rem);
+    tl.nrows = base + (i < rem ? 1 : 0);
+    tl.pad = 0;
+    return tl;
+}
+
 __global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ offsets, int T,
                                                   int cap, Tile* __restrict__ tiles,
                                                   int* __restrict__ tile_count) {
@@ -121,23 +136,11 @@ __global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ of
     const int nt = (n + MT_ROWS - 1) / MT_ROWS;
     int total;
     const int tb = block_excl_scan256(nt, scr, &total);
-    for (int i = 0; i < nt; ++i) {
-        Tile tl;
-        tl.group = tid;
-        tl.row0 = r0 + i * MT_ROWS;
-        tl.nrows = min(MT_ROWS, n - i * MT_ROWS);
-        tl.pad = 0;
-        if (tb + i < cap) tiles[tb + i] = tl;
-    }
+    for (int i = 0; i < nt; ++i)
+        if (tb + i < cap) tiles[tb + i] = balanced_tile(tid, r0, n, nt, i);
     const int ns = (T + MT_ROWS - 1) / MT_ROWS;
-    for (int i = tid; i < ns; i += 256) {
-        Tile tl;
-        tl.group = E;
-        tl.row0 = TOPK * T + i * MT_ROWS;
-        tl.nrows = min(MT_ROWS, T - i * MT_ROWS);
-        tl.pad = 0;
-        if (total + i < cap) tiles[total + i] = tl;
-    }
+    for (int i = tid; i < ns; i += 256)
+        if (total + i < cap) tiles[total + i] = balanced_tile(E, TOPK * T, T, ns, i);
     if (tid == 0) *tile_count = min(total + ns, cap);
 }
 
@@ -148,18 +151,22 @@ int max_tiles(int T) {
     return n / MT_ROWS + (n < E ? n : E) + (T + MT_ROWS - 1) / MT_ROWS;
 }
 
+// wts/wsorted: optional (both or neither): wsorted[p] = wts[perm[p]], the
+// routing weight of each sorted position.
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
-                    int32_t* inv, int32_t* chunk_counts, hipStream_t st) {
+                    int32_t* inv, int32_t* chunk_counts, hipStream_t st, const float* wts,
+                    float* wsorted) {
     const int n = TOPK * T;
     if (n <= SMALL_MAX) {
         hipLaunchKernelGGL(perm_small, dim3(1), dim3(256), 0, st, ids, n, counts, offsets, perm,
-                           inv);
+                           inv, wts, wsorted);
         return;
     }
     const int nb = perm_chunks(T);
     hipLaunchKernelGGL(perm_count, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts);
     hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, st, nb, chunk_counts, counts, offsets);
-    hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts, perm, inv);
+    hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts, perm, inv,
+                       wts, wsorted);
 }
 
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st) {
