@@ -206,4 +206,24 @@ __device__ __forceinline__ float wave_sum8(float v[8]) {
     return c;   // value index: 4*h32 + 2*h16 + h8
 }
 
+// s_waitcnt immediate: wait until at most n vector-memory operations of
+// this wave are outstanding (they retire in issue order); expcnt and
+// lgkmcnt are left at their maximum (no wait).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int LGKM0_IMM = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
+
+// Workgroup barrier inside a software pipeline.  __syncthreads() also acts
+// as a memory fence, which makes every wave wait for ALL of its outstanding
+// vector-memory operations -- including the prefetches meant to stay in
+// flight.  Here the caller has already waited (s_waitcnt vmcnt) for exactly
+// the loads the next stage needs; this drains only the LDS counter and
+// synchronises execution.  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void pipe_barrier() {
+    __builtin_amdgcn_s_waitcnt(LGKM0_IMM);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace moe

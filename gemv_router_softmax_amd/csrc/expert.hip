@@ -14,7 +14,7 @@
 //                  expert rows of the split expert-FFN call.
 //
 // Prefill (grouped GEMM on MFMA): expert_gemm below.
-#include "common.hpp"
+#include "block_util.hpp"
 
 namespace moe {
 
@@ -106,26 +106,6 @@ enum GemmMode { GM_GATEUP = 0, GM_DOWN_F32 = 1, GM_DOWN_F16W = 2 };
 // stores beyond it write nothing.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
-}
-
-// s_waitcnt immediate: wait until at most n vector-memory operations of
-// this wave are outstanding (they retire in issue order); expcnt and
-// lgkmcnt are left at their maximum (no wait).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int LGKM0_IMM = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
-
-// Workgroup barrier inside a software pipeline.  __syncthreads() also acts
-// as a memory fence, which makes every wave wait for ALL of its outstanding
-// vector-memory operations -- including the prefetches meant to stay in
-// flight.  Here the caller has already waited (s_waitcnt vmcnt) for exactly
-// the loads the next stage needs; this drains only the LDS counter and
-// synchronises execution.  The empty asm statements keep the compiler from
-// moving memory accesses across the barrier.
-__device__ __forceinline__ void pipe_barrier() {
-    __builtin_amdgcn_s_waitcnt(LGKM0_IMM);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -630,6 +610,9 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 
         // step 3 of this chunk under the next chunk's reads, the refill and
         // the next chunk's first dequantisation
+        // (the sched_barrier fences keep the refill loads in issue order
+        // relative to the other vector-memory operations: the wait counts
+        // above depend on that order)
         const bool more = c + 1 < NCH;
         half8 a_nx[NMT], bf_nx[2];
         if (more) {
@@ -637,16 +620,15 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
             B = read_b<GATEUP>(sn, c + 1);
             read_a<NMT>(sn, 0, a_nx);
         }
+        __builtin_amdgcn_sched_barrier(0);
         refill(const_cast<uint8_t*>(st));
+        __builtin_amdgcn_sched_barrier(0);
         if (more) dequant_step(B, 0, bf_nx);
         mfma_step<NMT>(a_cur, bf_cur, acc);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6 + NMT, 0);       // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, pg::LPC + 1, 0);   // refill loads
 #pragma unroll
-        for (int i = 0; i < 2 * NMT - 1; ++i) {
+        for (int i = 0; i < 2 * NMT; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, (40 + 2 * NMT - 2) / (2 * NMT - 1), 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (40 + 2 * NMT - 1) / (2 * NMT), 0);
         }
         if (more) {
 #pragma unroll
@@ -672,6 +654,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     // head: unrolled, so every wait count and refill target is a constant
     chunk(0, [&](uint8_t* st) {
         issue_chunk(src_cur, pg::STAGES, ra, st);
+        __builtin_amdgcn_sched_barrier(0);      // the metadata load goes after the chunk's loads
         issue_meta<MODE>(A, GATEUP ? nxt : cur, meta + ((GATEUP ? k + 1 : k) & 1) * pg::META);
     });
 #pragma unroll
@@ -688,7 +671,9 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     // tail: refills from the next item
 #pragma unroll
     for (int c = (MAIN > HEAD ? MAIN : HEAD); c < NCH; ++c) chunk(c, next(c));
+    __builtin_amdgcn_sched_barrier(0);          // epilogue stores after the last refill
     gemm_epilogue<MODE, NMT>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int KDIM, int MODE>
