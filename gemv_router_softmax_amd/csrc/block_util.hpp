@@ -87,91 +87,67 @@ __device__ __forceinline__ uint32_t fkey(float v) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+// Maximum of a per-lane key over each row of 16 lanes, left in every lane
+// of the row (DPP lane exchanges: pairs, quads, half-row mirror, row mirror).
+__device__ __forceinline__ uint32_t row16_max(uint32_t k) {
+    k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x140, 0xF, 0xF, false));  // row_mirror
+    return k;
+}
+
+__device__ __forceinline__ float fkey_inv(uint32_t k) {
+    return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Top-8 of the 256 logits of one token, computed by one wave.  Lane l holds
-// experts 4l .. 4l+3.  Writes ids / weights in descending logit order.
+// experts 4l .. 4l+3.  Eight rounds of arg-max over order-preserving integer
+// keys: the wave maximum (row maxima by DPP, then the four rows through
+// scalar registers), the lowest lane holding it and, in that lane, the
+// lowest of its four slots -- so equal logits go to the lower expert index.
+// Writes ids / weights in descending logit order; the weights are the
+// softmax over all experts renormalised over the eight, i.e.
+// exp(l - l_max) / sum_sel exp(l - l_max) (the full denominator cancels).
 __device__ inline void wave_top8(const float* __restrict__ lg, int32_t* __restrict__ ids_out,
-                          float* __restrict__ w_out, int32_t* __restrict__ ids_lds) {
+                                 float* __restrict__ w_out, int32_t* __restrict__ ids_lds) {
     const int lane = threadIdx.x & 63;
     const float4v v4 = reinterpret_cast<const float4v*>(lg)[lane];
-    const float v[4] = {v4[0], v4[1], v4[2], v4[3]};
-    uint32_t key[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = fkey(v[i]);
-    // largest K with #(key >= K) >= 8  ==  the 8th largest key
-    uint32_t prefix = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = prefix | (1u << b);
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cnt += popc64(__ballot(key[i] >= cand));
-        if (cnt >= TOPK) prefix = cand;
-    }
-    const uint32_t k8 = prefix;
-    int above = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) above += popc64(__ballot(key[i] > k8));
-    // ties at k8: the lowest expert indices fill the remaining places
-    const int need = TOPK - above;
-    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-    bool sel[4];
-    int eq_before_lane = 0;
-    uint64_t eqm[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) eqm[i] = __ballot(key[i] == k8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) eq_before_lane += popc64(eqm[i] & lt);
-    int eq_in_lane = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bool eq = key[i] == k8;
-        sel[i] = key[i] > k8 || (eq && eq_before_lane + eq_in_lane < need);
-        eq_in_lane += eq ? 1 : 0;
-    }
-    // gather the 8 selected (value, expert) pairs into uniform registers,
-    // lowest lane first within each of the four per-lane slots
-    uint64_t msk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) msk[i] = __ballot(sel[i]);
+    uint32_t key[4] = {fkey(v4[0]), fkey(v4[1]), fkey(v4[2]), fkey(v4[3])};
     float sv[TOPK];
     int se[TOPK];
 #pragma unroll
     for (int k = 0; k < TOPK; ++k) {
-        const int i = msk[0] ? 0 : (msk[1] ? 1 : (msk[2] ? 2 : 3));
-        const uint64_t mi = i == 0 ? msk[0] : (i == 1 ? msk[1] : (i == 2 ? msk[2] : msk[3]));
-        const int l = mi ? __builtin_ctzll(mi) : 0;
-        const uint64_t clr = mi & (mi - 1);
-        if (i == 0) msk[0] = clr; else if (i == 1) msk[1] = clr; else if (i == 2) msk[2] = clr;
-        else msk[3] = clr;
-        const float vi = i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
-        sv[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vi), l));
-        se[k] = 4 * l + i;
+        const uint32_t lm = max(max(key[0], key[1]), max(key[2], key[3]));
+        const uint32_t rm = row16_max(lm);
+        const uint32_t gm = max(max((uint32_t)__builtin_amdgcn_readlane((int)rm, 0),
+                                    (uint32_t)__builtin_amdgcn_readlane((int)rm, 16)),
+                                max((uint32_t)__builtin_amdgcn_readlane((int)rm, 32),
+                                    (uint32_t)__builtin_amdgcn_readlane((int)rm, 48)));
+        const uint64_t holders = __ballot(lm == gm);
+        const int wl = (int)__builtin_ctzll(holders);
+        const int slot = key[0] == gm ? 0 : (key[1] == gm ? 1 : (key[2] == gm ? 2 : 3));
+        const int ws = __builtin_amdgcn_readlane(slot, wl);
+        if (lane == wl) {
+            if (ws == 0) key[0] = 0u;
+            else if (ws == 1) key[1] = 0u;
+            else if (ws == 2) key[2] = 0u;
+            else key[3] = 0u;
+        }
+        sv[k] = fkey_inv(gm);
+        se[k] = 4 * wl + ws;
     }
-    // order: rank of element k = #elements before it (larger value, or equal
-    // value and lower expert index); ranks are a permutation of 0..7
-    int rk[TOPK];
-#pragma unroll
-    for (int k = 0; k < TOPK; ++k) {
-        int rnk = 0;
-#pragma unroll
-        for (int j = 0; j < TOPK; ++j)
-            rnk += (sv[j] > sv[k] || (sv[j] == sv[k] && se[j] < se[k])) ? 1 : 0;
-        rk[k] = rnk;
-    }
-    float vmax = sv[0];
-#pragma unroll
-    for (int k = 1; k < TOPK; ++k) vmax = fmaxf(vmax, sv[k]);
-    // softmax over all experts renormalised over the selected eight: the
-    // full denominator cancels, leaving exp(l - l_max) / sum_sel exp(l - l_max)
+    const float vmax = sv[0];
     float ex[TOPK], s = 0.f;
 #pragma unroll
     for (int k = 0; k < TOPK; ++k) { ex[k] = expf(sv[k] - vmax); s += ex[k]; }
     const float inv = 1.f / s;
 #pragma unroll
     for (int k = 0; k < TOPK; ++k) {
-        if (lane == rk[k]) {
-            ids_out[lane] = se[k];
-            w_out[lane] = ex[k] * inv;
-            if (ids_lds) ids_lds[lane] = se[k];
+        if (lane == k) {
+            ids_out[k] = se[k];
+            w_out[k] = ex[k] * inv;
+            if (ids_lds) ids_lds[k] = se[k];
         }
     }
 }

@@ -327,23 +327,18 @@ __device__ void block_route(const float* __restrict__ logits, const float* __res
 
 constexpr int NRB = 64;   // router workgroups (4 experts each, one per wave)
 
-// grid (NRB + 1 + T): blocks < NRB: logits of 16 experts each (4 expert rows
-// per wave); block NRB: shared-gate logits z[t] = x[t] . w_sg; the last T
-// blocks: fp16 copy of x in chunk-slot order.  counter: zero on entry, zero
-// on exit.
+// grid (NRB + 1 + T): blocks < NRB: logits of 4 experts each (one expert
+// row per wave); block NRB: shared-gate logits z[t] = x[t] . w_sg; the last
+// T blocks: fp16 copy of x in chunk-slot order.  The selection itself runs
+// in every routed workgroup of decode_gateup_dec (all in parallel), so this
+// kernel ends as soon as its dot products are written.
 __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restrict__ x, int T,
                                                         const uint16_t* __restrict__ wr,
                                                         const float* __restrict__ bias,
                                                         const uint16_t* __restrict__ wsg,
                                                         float* __restrict__ logits,
                                                         float* __restrict__ z,
-                                                        uint16_t* __restrict__ xh,
-                                                        unsigned* __restrict__ counter,
-                                                        RouteRec* __restrict__ rec) {
-    __shared__ RouteRec R;
-    __shared__ int mark[E];
-    __shared__ int scr[4];
-    __shared__ int last;
+                                                        uint16_t* __restrict__ xh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
     if (b > NRB) {                        // x -> fp16, token b - NRB - 1
@@ -404,37 +399,37 @@ __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restri
             }
         }
     }
-    // last of the NRB + 1 writer workgroups does the routing
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        last = atomicAdd(counter, 1u) == (unsigned)NRB;
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    block_route(logits, z, T, R, mark, scr);
-    const int* src = reinterpret_cast<const int*>(&R);
-    int* dst = reinterpret_cast<int*>(rec);
-    for (int i = threadIdx.x; i < REC_WORDS; i += 256) dst[i] = src[i];
-    if (threadIdx.x == 0) atomicExch(counter, 0u);
 }
 
-// grid (1 + 8T, I/16).  h rows are indexed (slot * T + t), fp16, chunk-slot
-// order.
+// grid (1 + 8T, I/16).  Slot 0 is the shared expert; slot s > 0 is the
+// s-th active routed expert (ascending id), which each routed workgroup
+// finds by running the selection itself on the logits (block_route); the
+// workgroup (0, 0) publishes the route record for decode_down_dec.  h rows
+// are indexed (slot * T + t), fp16, chunk-slot order.
 __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restrict__ xh, int T,
-                                                         const RouteRec* __restrict__ rec,
+                                                         const float* __restrict__ logits,
+                                                         const float* __restrict__ z,
+                                                         RouteRec* __restrict__ rec,
                                                          moe_qffn routed, moe_qffn shared,
                                                          uint16_t* __restrict__ hout) {
+    __shared__ RouteRec R;
+    __shared__ int mark[E];
+    __shared__ int scr[4];
     const int slot = blockIdx.x;
     int e = 0;
     const uint32_t tall = (1u << T) - 1u;
     uint32_t mask = tall;
+    if (slot > 0 || blockIdx.y == 0) block_route(logits, z, T, R, mark, scr);
+    if (slot == 0 && blockIdx.y == 0) {
+        const int* src = reinterpret_cast<const int*>(&R);
+        int* dst = reinterpret_cast<int*>(rec);
+        for (int i = threadIdx.x; i < REC_WORDS; i += 256) dst[i] = src[i];
+    }
     if (slot > 0) {
-        const int nact = min(max(rec->nact, 0), TOPK * T);
+        const int nact = min(max(R.nact, 0), TOPK * T);
         if (slot - 1 >= nact) return;
-        e = min(max(rec->active[slot - 1], 0), E - 1);
-        mask = rec->tmask[slot - 1] & tall;
+        e = min(max(R.active[slot - 1], 0), E - 1);
+        mask = R.tmask[slot - 1] & tall;
     }
     const moe_qffn q = slot == 0 ? shared : routed;
     const int lane = threadIdx.x & 63;
@@ -581,10 +576,11 @@ void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, flo
                                float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
                                void* rec, uint16_t* y, uint16_t* res, hipStream_t st) {
     RouteRec* R = static_cast<RouteRec*>(rec);
+    (void)counter;
     hipLaunchKernelGGL(route_logits_dec, dim3(NRB + 1 + T), dim3(256), 0, st, x, T, L.w_router,
-                       L.router_bias, L.w_shared_gate, logits, z, xh, counter, R);
-    hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T, R,
-                       L.routed, L.shared, hbuf);
+                       L.router_bias, L.w_shared_gate, logits, z, xh);
+    hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T,
+                       logits, z, R, L.routed, L.shared, hbuf);
     hipLaunchKernelGGL(decode_down_dec, dim3(H / 4), dim3(256), 0, st, hbuf, T, R, L.routed,
                        L.shared, y, x, res);
 }
