@@ -19,8 +19,10 @@ Also measured in the same run and reported in the same JSON line:
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -165,6 +167,51 @@ def read_ceiling(gib=4, reps=5):
     return buf_gbs(gib << 30, best)
 
 
+def copy_calibration(mib=256, reps=5):
+    """A plain copy of known size for scaling the HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE) of a profiled run: the counters of
+    probe_copy_kernel read against mib MiB read and mib MiB written."""
+    import torch
+    import gemv_router_softmax_amd as moe
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    for _ in range(reps):
+        moe.moe_probe_copy(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+DECODE_SOURCES = ("decode.hip", "block_util.hpp", "common.hpp", "moe_host.hip")
+
+
+def decode_source_hash():
+    """Hash of the sources of the decode layer kernels: a traffic figure
+    measured on other code is not reported."""
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "gemv_router_softmax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode layer launch from the committed rocprofv3 PMC
+    summary (JSON block in profiles/decode_layer_t1_traffic.md), or None if
+    it is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "decode_layer_t1_traffic.md")
+    try:
+        with open(path) as fh:
+            m = re.search(r"```json\n(.*?)\n```", fh.read(), re.S)
+        d = json.loads(m.group(1))
+    except (OSError, AttributeError, ValueError):
+        return None
+    if d.get("source_hash") != decode_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
 def buf_gbs(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
 
@@ -250,6 +297,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (scales profiled HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -284,6 +333,9 @@ def main():
         f"{achieved:.0f} GB/s; graph chain {ms_per_step * 1e3 / args.layers:.2f} us/layer")
     ceiling = read_ceiling()
     log(f"read ceiling: {ceiling:.0f} GB/s")
+    if args.copy_calibration:
+        copy_calibration()
+    traffic = measured_traffic()
 
     pre = None
     if not args.no_prefill:
@@ -307,15 +359,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic (seeded layers and inputs, random-init weights)",
         "config": {"workload": f"decode T=1 through a {args.layers}-layer MoE chain with "
                                "residual adds, fresh N(0,1) input per step",
                    "layers": args.layers, "T": 1, "hidden": H, "experts": E, "topk": TOPK,
                    "expert_width": I, "group": 64, "weights": "uint4 + fp16 scale/bias",
+                   "arithmetic": "fp16 (bf16 router) products, fp32 accumulation",
                    "hip_graph": not args.no_graph},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode layer launch at T=1 (route_logits_dec + "
                                "decode_gateup_dec + decode_down_dec)",
                      "bytes_per_launch": per_launch_bytes, "launch_us": k_mean * 1e3},
