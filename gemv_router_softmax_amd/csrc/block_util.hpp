@@ -6,6 +6,9 @@
 
 namespace moe {
 
+// Wave index within the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int lane = threadIdx.x & 63;
     return lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -102,54 +105,79 @@ __device__ __forceinline__ float fkey_inv(uint32_t k) {
 }
 
 // Top-8 of the 256 logits of one token, computed by one wave.  Lane l holds
-// experts 4l .. 4l+3.  Eight rounds of arg-max over order-preserving integer
-// keys: the wave maximum (row maxima by DPP, then the four rows through
-// scalar registers), the lowest lane holding it and, in that lane, the
-// lowest of its four slots -- so equal logits go to the lower expert index.
-// Writes ids / weights in descending logit order; the weights are the
-// softmax over all experts renormalised over the eight, i.e.
-// exp(l - l_max) / sum_sel exp(l - l_max) (the full denominator cancels).
-__device__ inline void wave_top8(const float* __restrict__ lg, int32_t* __restrict__ ids_out,
-                                 float* __restrict__ w_out, int32_t* __restrict__ ids_lds) {
+// experts 4l .. 4l+3 (v4).  Each lane first sorts its four candidates as
+// 64-bit values (order-preserving key of the logit, 255 - expert index), so
+// its best remaining candidate is always c[0] and equal logits are ordered
+// by the lower expert index.  Each of the eight rounds then takes the wave
+// maximum of the lanes' c[0] keys (row maxima by DPP, then the four rows
+// through scalar registers), the lowest lane holding it -- lower lanes hold
+// lower indices, so ties again go to the lower expert -- and shifts that
+// lane's list by one.  The code is branch-free: at one token this wave's
+// instruction count is the latency of the routing step.  Lane k < 8 ends
+// with the k-th selection (descending logit) and writes its id and weight;
+// the weights are the softmax over all experts renormalised over the eight,
+// i.e. exp(l - l_max) / sum_sel exp(l - l_max) (the full denominator
+// cancels).  Returns, in lane k < 8, the k-th selected expert.
+__device__ inline int wave_top8_v(float4v v4, int32_t* __restrict__ ids_out,
+                                  float* __restrict__ w_out, int32_t* __restrict__ ids_lds) {
     const int lane = threadIdx.x & 63;
-    const float4v v4 = reinterpret_cast<const float4v*>(lg)[lane];
-    uint32_t key[4] = {fkey(v4[0]), fkey(v4[1]), fkey(v4[2]), fkey(v4[3])};
-    float sv[TOPK];
-    int se[TOPK];
+    uint64_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        c[j] = ((uint64_t)fkey(v4[j]) << 32) | (uint32_t)(255 - (4 * lane + j));
+    auto ce = [](uint64_t& x, uint64_t& y) {   // x >= y afterwards
+        const bool sw = x < y;
+        const uint64_t hi = sw ? y : x, lo = sw ? x : y;
+        x = hi;
+        y = lo;
+    };
+    ce(c[0], c[1]);
+    ce(c[2], c[3]);
+    ce(c[0], c[2]);
+    ce(c[1], c[3]);
+    ce(c[1], c[2]);
+    uint32_t kmax = 0, kmine = 0;
+    int emine = 0;
 #pragma unroll
     for (int k = 0; k < TOPK; ++k) {
-        const uint32_t lm = max(max(key[0], key[1]), max(key[2], key[3]));
+        const uint32_t lm = (uint32_t)(c[0] >> 32);
         const uint32_t rm = row16_max(lm);
         const uint32_t gm = max(max((uint32_t)__builtin_amdgcn_readlane((int)rm, 0),
                                     (uint32_t)__builtin_amdgcn_readlane((int)rm, 16)),
                                 max((uint32_t)__builtin_amdgcn_readlane((int)rm, 32),
                                     (uint32_t)__builtin_amdgcn_readlane((int)rm, 48)));
-        const uint64_t holders = __ballot(lm == gm);
-        const int wl = (int)__builtin_ctzll(holders);
-        const int slot = key[0] == gm ? 0 : (key[1] == gm ? 1 : (key[2] == gm ? 2 : 3));
-        const int ws = __builtin_amdgcn_readlane(slot, wl);
-        if (lane == wl) {
-            if (ws == 0) key[0] = 0u;
-            else if (ws == 1) key[1] = 0u;
-            else if (ws == 2) key[2] = 0u;
-            else key[3] = 0u;
-        }
-        sv[k] = fkey_inv(gm);
-        se[k] = 4 * wl + ws;
+        const int wl = (int)__builtin_ctzll(__ballot(lm == gm));
+        const int e = 255 - __builtin_amdgcn_readlane((int)(uint32_t)c[0], wl);
+        const bool me = lane == wl;
+        c[0] = me ? c[1] : c[0];
+        c[1] = me ? c[2] : c[1];
+        c[2] = me ? c[3] : c[2];
+        c[3] = me ? 0ull : c[3];
+        if (k == 0) kmax = gm;
+        kmine = lane == k ? gm : kmine;
+        emine = lane == k ? e : emine;
     }
-    const float vmax = sv[0];
-    float ex[TOPK], s = 0.f;
-#pragma unroll
-    for (int k = 0; k < TOPK; ++k) { ex[k] = expf(sv[k] - vmax); s += ex[k]; }
-    const float inv = 1.f / s;
-#pragma unroll
-    for (int k = 0; k < TOPK; ++k) {
-        if (lane == k) {
-            ids_out[k] = se[k];
-            w_out[k] = ex[k] * inv;
-            if (ids_lds) ids_lds[k] = se[k];
-        }
+    const float ex = lane < TOPK ? expf(fkey_inv(kmine) - fkey_inv(kmax)) : 0.f;
+    // sum over lanes 0..7 (pairs, quads, then the half-row mirror)
+    float s = ex + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                       0, __builtin_bit_cast(int, ex), 0xB1, 0xF, 0xF, false));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x4E,
+                                                               0xF, 0xF, false));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x141,
+                                                               0xF, 0xF, false));
+    if (lane < TOPK) {
+        ids_out[lane] = emine;
+        w_out[lane] = ex * (1.f / s);
+        if (ids_lds) ids_lds[lane] = emine;
     }
+    return emine;
+}
+
+// As wave_top8_v, reading the token's 256 logits from lg.
+__device__ inline void wave_top8(const float* __restrict__ lg, int32_t* __restrict__ ids_out,
+                                 float* __restrict__ w_out, int32_t* __restrict__ ids_lds) {
+    const int lane = threadIdx.x & 63;
+    wave_top8_v(reinterpret_cast<const float4v*>(lg)[lane], ids_out, w_out, ids_lds);
 }
 
 // Sum eight per-lane values over the 64 lanes of a wave with 10 exchanges:

@@ -88,6 +88,60 @@ __device__ __forceinline__ float sum8_h(uint4v apairs, float acc) {
     return acc;
 }
 
+// The same dot product in 9 instructions per code word instead of 15, for
+// the latency-bound decode kernels.  OR-ing 0x6400 into each half of
+//   w & 0x000F000F, w & 0x00F000F0, (w >> 8) & 0x000F000F, (w >> 8) & 0x00F000F0
+// gives the exact fp16 pairs 1024 + (q0, q4), 1024 + 16 (q1, q5),
+// 1024 + (q2, q6), 1024 + 16 (q3, q7) without any shift of the odd nibbles
+// and without the subtraction.  Against activation pairs whose second and
+// fourth pair are pre-scaled by 1/16 (prescale_pairs) the dot products add
+// up to sum_k q_k x_k plus a constant part, pair_offset() of the same
+// pre-scaled pairs, which the caller subtracts once per row.
+__device__ __forceinline__ uint4v prescale_pairs(uint4v a) {
+    const half2v k = {(_Float16)0.0625f, (_Float16)0.0625f};
+    uint4v r = a;
+    const uint32_t a1 = a[1], a3 = a[3];
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a1) * k);
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a3) * k);
+    return r;
+}
+
+// 0x64006400 in a vector register the compiler cannot see through: with the
+// mask in a scalar register, each nibble pair is then one v_and_or_b32 (a
+// VOP3 instruction takes no literal operand, and two literals would split
+// it into an AND and an OR).
+__device__ __forceinline__ uint32_t fp16_1024_pair() {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(v));
+    return v;
+}
+
+// mag: fp16_1024_pair(), taken once per kernel.
+__device__ __forceinline__ float dot8_biased(uint32_t w, uint4v xs, float acc, uint32_t mag) {
+    const uint32_t w8 = w >> 8;
+    const uint32_t p[4] = {(w & 0x000F000Fu) | mag, (w & 0x00F000F0u) | mag,
+                           (w8 & 0x000F000Fu) | mag, (w8 & 0x00F000F0u) | mag};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t xi = xs[i];
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, p[i]),
+                                     __builtin_bit_cast(half2v, xi), acc, false);
+    }
+    return acc;
+}
+
+// The part of dot8_biased that does not depend on the codes: 1024 times the
+// sum of the pre-scaled pairs (exact products, fp32 accumulation).
+__device__ __forceinline__ float pair_offset(uint4v xs, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t xi = xs[i];
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, 0x64006400u),
+                                     __builtin_bit_cast(half2v, xi), acc, false);
+    }
+    return acc;
+}
+
 // Eight natural-order bf16 values -> fp16 in chunk-slot order (k = 0,4,1,5,
 // 2,6,3,7), the activation layout of every expert kernel.  bf16 -> fp16 is
 // exact for magnitudes in [2^-14, 65504]; smaller values keep fp16's

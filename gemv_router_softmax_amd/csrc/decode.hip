@@ -302,27 +302,92 @@ struct RouteRec {
 constexpr int REC_WORDS = (int)(sizeof(RouteRec) / 4);
 static_assert(sizeof(RouteRec) % 4 == 0, "record is copied as words");
 
+// Weight pointers of one expert stack as opaque scalar values, taken from
+// the kernel arguments at entry.  Choosing between the routed and the
+// shared stack by a condition on the argument structs themselves makes the
+// compiler select the structs' addresses and re-read the pointers with
+// vector-memory loads just before the weight loads -- one more memory round
+// trip on the critical path.  A choice between these values is a scalar
+// select.
+// (Global address space: behind the opaque copy the compiler could not
+// otherwise tell the pointers from generic ones and would use flat loads.)
+#define GLOBAL_AS __attribute__((address_space(1)))
+struct GUPtrs {
+    const GLOBAL_AS uint32_t *gq, *uq;
+    const GLOBAL_AS uint16_t *gs, *gb, *us, *ub;
+};
+struct DnPtrs {
+    const GLOBAL_AS uint32_t* q;
+    const GLOBAL_AS uint16_t *s, *b;
+};
+__device__ __forceinline__ GUPtrs gu_ptrs(const moe_qffn& f) {
+    GUPtrs p{(const GLOBAL_AS uint32_t*)f.gate_q, (const GLOBAL_AS uint32_t*)f.up_q,
+             (const GLOBAL_AS uint16_t*)f.gate_s, (const GLOBAL_AS uint16_t*)f.gate_b,
+             (const GLOBAL_AS uint16_t*)f.up_s,   (const GLOBAL_AS uint16_t*)f.up_b};
+    asm volatile("" : "+s"(p.gq), "+s"(p.uq), "+s"(p.gs), "+s"(p.gb), "+s"(p.us), "+s"(p.ub));
+    return p;
+}
+__device__ __forceinline__ DnPtrs dn_ptrs(const moe_qffn& f) {
+    DnPtrs p{(const GLOBAL_AS uint32_t*)f.down_q, (const GLOBAL_AS uint16_t*)f.down_s,
+             (const GLOBAL_AS uint16_t*)f.down_b};
+    asm volatile("" : "+s"(p.q), "+s"(p.s), "+s"(p.b));
+    return p;
+}
+__device__ __forceinline__ GUPtrs pick(bool c, const GUPtrs& a, const GUPtrs& b) {
+    return GUPtrs{c ? a.gq : b.gq, c ? a.uq : b.uq, c ? a.gs : b.gs,
+                  c ? a.gb : b.gb, c ? a.us : b.us, c ? a.ub : b.ub};
+}
+__device__ __forceinline__ DnPtrs pick(bool c, const DnPtrs& a, const DnPtrs& b) {
+    return DnPtrs{c ? a.q : b.q, c ? a.s : b.s, c ? a.b : b.b};
+}
+
 // Top-8 of every token (one wave per token) and the active-expert list, by
-// one workgroup, into R (LDS).
-__device__ void block_route(const float* __restrict__ logits, const float* __restrict__ z,
-                            int T, RouteRec& R, int* mark, int* scr) {
-    const int tid = threadIdx.x, wave = tid >> 6;
+// one workgroup, into R (LDS).  zv: the shared-gate logit of token tid
+// (tid < T), loaded by the caller.  The waves exchange only LDS, so the
+// barriers here leave the caller's outstanding global loads in flight.
+static_assert(MOE_DECODE_T <= 8, "block_route: at most two tokens per wave");
+__device__ void block_route(const float* __restrict__ logits, float zv, int T, RouteRec& R,
+                            int* mark) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = wave, t1 = wave + 4;
+    float4v v0 = {}, v1 = {};
+    if (t0 < T) v0 = reinterpret_cast<const float4v*>(logits + (size_t)t0 * E)[lane];
+    if (t1 < T) v1 = reinterpret_cast<const float4v*>(logits + (size_t)t1 * E)[lane];
     mark[tid] = 0;
-    __syncthreads();
-    for (int t = wave; t < T; t += 4) wave_top8(logits + (size_t)t * E, R.ids[t], R.w[t], nullptr);
-    if (tid < T) R.sg[tid] = 1.f / (1.f + expf(-z[tid]));
-    __syncthreads();
-    if (tid < T * TOPK) atomicOr((unsigned*)&mark[R.ids[tid >> 3][tid & 7]], 1u << (tid >> 3));
-    __syncthreads();
-    const int mk = mark[tid];
-    int na;
-    const int slot = block_excl_scan256(mk ? 1 : 0, scr, &na);
-    if (mk) {
-        R.active[slot] = tid;
-        R.tmask[slot] = (uint32_t)mk;
+    pipe_barrier();
+    if (t0 < T) {
+        const int e = wave_top8_v(v0, R.ids[t0], R.w[t0], nullptr);
+        if (lane < TOPK) atomicOr((unsigned*)&mark[e], 1u << t0);
     }
-    if (tid == 0) R.nact = na;
-    __syncthreads();
+    if (t1 < T) {
+        const int e = wave_top8_v(v1, R.ids[t1], R.w[t1], nullptr);
+        if (lane < TOPK) atomicOr((unsigned*)&mark[e], 1u << t1);
+    }
+    if (tid < T) R.sg[tid] = 1.f / (1.f + expf(-zv));
+    pipe_barrier();
+    if (wave == 0) {
+        // active experts in ascending id: lane l owns experts 4l .. 4l+3
+        int mk[4];
+        uint32_t nbelow = 0, nact = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mk[j] = mark[4 * lane + j];
+            const uint64_t bj = __ballot(mk[j] != 0);
+            nbelow += (uint32_t)popc64(bj & lanemask_lt());
+            nact += (uint32_t)popc64(bj);
+        }
+        int slot = (int)nbelow;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (mk[j]) {
+                R.active[slot] = 4 * lane + j;
+                R.tmask[slot] = (uint32_t)mk[j];
+                ++slot;
+            }
+        }
+        if (lane == 0) R.nact = (int)nact;
+    }
+    pipe_barrier();
 }
 
 constexpr int NRB = 64;   // router workgroups (4 experts each, one per wave)
@@ -414,12 +479,22 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
                                                          uint16_t* __restrict__ hout) {
     __shared__ RouteRec R;
     __shared__ int mark[E];
-    __shared__ int scr[4];
     const int slot = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const GUPtrs pr = gu_ptrs(routed), ps = gu_ptrs(shared);
     int e = 0;
     const uint32_t tall = (1u << T) - 1u;
     uint32_t mask = tall;
-    if (slot > 0 || blockIdx.y == 0) block_route(logits, z, T, R, mark, scr);
+    // loads that do not depend on the routing go out before it: token 0's
+    // activations and the shared-gate logits
+    uint4v x0[4];
+    {
+        const uint4v* xr = reinterpret_cast<const uint4v*>(xh) + lane * 4;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) x0[cc] = xr[cc];
+    }
+    const float zv = (int)threadIdx.x < T ? z[threadIdx.x] : 0.f;
+    if (slot > 0 || blockIdx.y == 0) block_route(logits, zv, T, R, mark);
     if (slot == 0 && blockIdx.y == 0) {
         const int* src = reinterpret_cast<const int*>(&R);
         int* dst = reinterpret_cast<int*>(rec);
@@ -431,41 +506,54 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
         e = min(max(R.active[slot - 1], 0), E - 1);
         mask = R.tmask[slot - 1] & tall;
     }
-    const moe_qffn q = slot == 0 ? shared : routed;
-    const int lane = threadIdx.x & 63;
-    const int n0 = blockIdx.y * 16 + (threadIdx.x >> 6) * 4;
+    const GUPtrs q = pick(slot == 0, ps, pr);
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int n0 = blockIdx.y * 16 + wave_id() * 4;
     uint4v wq[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const size_t row = (size_t)e * I + n0 + (i & 3);
-        const uint32_t* qb = i < 4 ? q.gate_q : q.up_q;
-        wq[i] = reinterpret_cast<const uint4v*>(qb + row * (H / 8))[lane];
+        const GLOBAL_AS uint32_t* qb = i < 4 ? q.gq : q.uq;
+        wq[i] = ((const GLOBAL_AS uint4v*)(qb + row * (H / 8)))[lane];
     }
     float s[8], b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const size_t row = (size_t)e * I + n0 + (i & 3);
-        const uint16_t* sb = i < 4 ? q.gate_s : q.up_s;
-        const uint16_t* bb = i < 4 ? q.gate_b : q.up_b;
+        const GLOBAL_AS uint16_t* sb = i < 4 ? q.gs : q.us;
+        const GLOBAL_AS uint16_t* bb = i < 4 ? q.gb : q.ub;
         s[i] = fp16_to_f32(sb[row * (H / G) + (lane >> 1)]);
         b[i] = fp16_to_f32(bb[row * (H / G) + (lane >> 1)]);
     }
+    // every weight load is in flight before the first use of one
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t mag = fp16_1024_pair();
     for (int t = 0; t < T; ++t) {
         if (!((mask >> t) & 1u)) continue;
-        const uint4v* xr = reinterpret_cast<const uint4v*>(xh + (size_t)t * H) + lane * 4;
         uint4v xp[4];
+        if (t == 0) {
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) xp[cc] = xr[cc];
-        float sx = 0.f;
+            for (int cc = 0; cc < 4; ++cc) xp[cc] = x0[cc];
+        } else {
+            const uint4v* xr = reinterpret_cast<const uint4v*>(xh + (size_t)t * H) + lane * 4;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) sx = sum8_h(xp[cc], sx);
+            for (int cc = 0; cc < 4; ++cc) xp[cc] = xr[cc];
+        }
+        float sx = 0.f, off = 0.f;
+        uint4v xs[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            sx = sum8_h(xp[cc], sx);
+            xs[cc] = prescale_pairs(xp[cc]);
+            off = pair_offset(xs[cc], off);
+        }
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float dd = 0.f;
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) dd = dot8_codes(wq[i][cc], xp[cc], dd);
-            acc[i] = fmaf(s[i], dd, b[i] * sx);
+            for (int cc = 0; cc < 4; ++cc) dd = dot8_biased(wq[i][cc], xs[cc], dd, mag);
+            acc[i] = fmaf(s[i], dd - off, b[i] * sx);
         }
         const float r = wave_sum8(acc);
         const float u = __shfl_xor(r, 32, WAVE);
@@ -483,12 +571,11 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
 // grid (H/4): 4 output rows per workgroup over every active expert (wave w
 // takes slots w, w+4, ...), combine with the routing weights and the shared
 // gate, residual add.  Fixed summation order: deterministic.
-__global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restrict__ hin, int T,
-                                                       const RouteRec* __restrict__ rec,
-                                                       moe_qffn routed, moe_qffn shared,
-                                                       uint16_t* __restrict__ y,
-                                                       const uint16_t* __restrict__ x,
-                                                       uint16_t* __restrict__ res) {
+// Two waves per SIMD keep the whole grid resident at once.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_down_dec(const uint16_t* __restrict__ hin, int T, const RouteRec* __restrict__ rec,
+                     moe_qffn routed, moe_qffn shared, uint16_t* __restrict__ y,
+                     const uint16_t* __restrict__ x, uint16_t* __restrict__ res) {
     __shared__ RouteRec R;
     __shared__ float yacc[4][MOE_DECODE_T][4];
     {
@@ -497,8 +584,10 @@ __global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restric
         for (int i = threadIdx.x; i < REC_WORDS; i += 256) dst[i] = src[i];
     }
     __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane >> 4, c = lane & 15;
+    const DnPtrs pr = dn_ptrs(routed), ps = dn_ptrs(shared);
+    const uint32_t mag = fp16_1024_pair();
     const int m = blockIdx.x * 4 + r;
     const uint32_t tall = (1u << T) - 1u;
     const int nslots = min(max(R.nact, 0), TOPK * T) + 1;
@@ -506,17 +595,29 @@ __global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restric
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_T; ++t) acc[t] = 0.f;
     for (int a0 = wave; a0 < nslots; a0 += 16) {
-        uint4v dw[4];
+        // every load of the pass goes out before any arithmetic: codes,
+        // scales and biases of up to four slots and the h row of each
+        // slot's first token
+        uint4v dw[4], h0[4][4];
         float ds[4], db[4];
+        int tf[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int a = a0 + 4 * k < nslots ? a0 + 4 * k : a0;
-            const int e = a == 0 ? 0 : min(max(R.active[a - 1], 0), E - 1);
-            const moe_qffn& q = a == 0 ? shared : routed;
+            const int e = a == 0 ? 0
+                                 : __builtin_amdgcn_readfirstlane(min(max(R.active[a - 1], 0), E - 1));
+            const uint32_t mask =
+                (a == 0 ? tall : (uint32_t)__builtin_amdgcn_readfirstlane(R.tmask[a - 1])) & tall;
+            tf[k] = mask ? __builtin_ctz(mask) : 0;
+            const DnPtrs q = pick(a == 0, ps, pr);
             const size_t row = (size_t)e * H + m;
-            dw[k] = reinterpret_cast<const uint4v*>(q.down_q + row * (I / 8))[c];
-            ds[k] = fp16_to_f32(q.down_s[row * (I / G) + (c >> 1)]);
-            db[k] = fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]);
+            dw[k] = ((const GLOBAL_AS uint4v*)(q.q + row * (I / 8)))[c];
+            ds[k] = fp16_to_f32(q.s[row * (I / G) + (c >> 1)]);
+            db[k] = fp16_to_f32(q.b[row * (I / G) + (c >> 1)]);
+            const uint4v* hr =
+                reinterpret_cast<const uint4v*>(hin + ((size_t)a * T + tf[k]) * I) + c * 4;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) h0[k][cc] = hr[cc];
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -532,16 +633,25 @@ __global__ __launch_bounds__(256) void decode_down_dec(const uint16_t* __restric
                     for (int j = 0; j < TOPK; ++j)
                         if (R.ids[t][j] == e) coef = R.w[t][j];
                 }
-                const uint4v* hr =
-                    reinterpret_cast<const uint4v*>(hin + ((size_t)a * T + t) * I) + c * 4;
-                float sh_ = 0.f, dot = 0.f;
+                uint4v hv[4];
+                if (t == tf[k]) {
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) hv[cc] = h0[k][cc];
+                } else {
+                    const uint4v* hr =
+                        reinterpret_cast<const uint4v*>(hin + ((size_t)a * T + t) * I) + c * 4;
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) hv[cc] = hr[cc];
+                }
+                float sh_ = 0.f, off = 0.f, dot = 0.f;
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
-                    const uint4v hv = hr[cc];
-                    sh_ = sum8_h(hv, sh_);
-                    dot = dot8_codes(dw[k][cc], hv, dot);
+                    sh_ = sum8_h(hv[cc], sh_);
+                    const uint4v hs = prescale_pairs(hv[cc]);
+                    off = pair_offset(hs, off);
+                    dot = dot8_biased(dw[k][cc], hs, dot, mag);
                 }
-                const float part = coef * fmaf(ds[k], dot, db[k] * sh_);
+                const float part = coef * fmaf(ds[k], dot - off, db[k] * sh_);
 #pragma unroll
                 for (int tt = 0; tt < MOE_DECODE_T; ++tt)
                     if (tt == t) acc[tt] += part;

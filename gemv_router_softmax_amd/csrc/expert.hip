@@ -195,9 +195,6 @@ static_assert((STAGES - 2) * LPC + 1 <= 63, "vmcnt range");
 
 typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
-// Wave index within the workgroup, as a wave-uniform (scalar) value.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
 struct GItem {
     int valid;       // 0: past the last item (its loads are dummies)
     int shared;      // group 256 (the shared expert)
