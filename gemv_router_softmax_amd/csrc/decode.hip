@@ -284,13 +284,16 @@ __global__ __launch_bounds__(256) void decode_down_combine(
 //                      active-expert list once, into a small route record,
 //                      and re-arms the counter.
 //   decode_gateup_dec  slot 0 = the shared expert (needs no routing), slot
-//                      a >= 1 = the a-th active routed expert; one read of the
-//                      record tells a workgroup its expert.
+//                      a >= 1 = the a-th active routed expert, which every
+//                      routed workgroup finds by running the selection on
+//                      the logits itself; workgroup (0, 0) also publishes the
+//                      down record.
 //   decode_down_dec    every active expert for 4 output rows, combine with the
 //                      routing weights and the shared gate, residual add.
 // Ids read back from the record are clamped, so a corrupted record cannot
 // send a load outside the weights.
 
+// The routing of up to MOE_DECODE_T tokens, in LDS of the gate/up kernel.
 struct RouteRec {
     int ids[MOE_DECODE_T][TOPK];
     float w[MOE_DECODE_T][TOPK];
@@ -299,8 +302,20 @@ struct RouteRec {
     uint32_t tmask[MOE_DECODE_T * TOPK]; // tokens that selected active[a]
     int nact;
 };
-constexpr int REC_WORDS = (int)(sizeof(RouteRec) / 4);
-static_assert(sizeof(RouteRec) % 4 == 0, "record is copied as words");
+
+// What the down kernel needs, in global memory: slot 0 is the shared
+// expert, slot a >= 1 the a-th active routed expert (ascending id).  Every
+// array is read with one 8-byte load per lane (lane l: slots 2l, 2l+1), all
+// issued together, and picked apart with lane reads -- one memory round
+// trip for the whole record.
+constexpr int DEC_SLOTS = 1 + MOE_DECODE_T * TOPK;
+struct DownRec {
+    int slot_e[128];                   // expert of each slot; [127]: the slot count
+    uint32_t slot_m[128];              // tokens of each slot (bit t)
+    float coef[MOE_DECODE_T][128];     // token t's weight for slot a (the shared gate for
+                                       // slot 0; 0 where the token did not pick the expert)
+};
+static_assert(DEC_SLOTS < 127, "slot count word");
 
 // Weight pointers of one expert stack as opaque scalar values, taken from
 // the kernel arguments at entry.  Choosing between the routed and the
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restri
 __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restrict__ xh, int T,
                                                          const float* __restrict__ logits,
                                                          const float* __restrict__ z,
-                                                         RouteRec* __restrict__ rec,
+                                                         DownRec* __restrict__ rec,
                                                          moe_qffn routed, moe_qffn shared,
                                                          uint16_t* __restrict__ hout) {
     __shared__ RouteRec R;
@@ -496,9 +511,23 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
     const float zv = (int)threadIdx.x < T ? z[threadIdx.x] : 0.f;
     if (slot > 0 || blockIdx.y == 0) block_route(logits, zv, T, R, mark);
     if (slot == 0 && blockIdx.y == 0) {
-        const int* src = reinterpret_cast<const int*>(&R);
-        int* dst = reinterpret_cast<int*>(rec);
-        for (int i = threadIdx.x; i < REC_WORDS; i += 256) dst[i] = src[i];
+        const int nact = min(max(R.nact, 0), TOPK * T);
+        const int a = threadIdx.x;
+        if (a <= nact) {
+            rec->slot_e[a] = a == 0 ? 0 : R.active[a - 1];
+            rec->slot_m[a] = a == 0 ? tall : R.tmask[a - 1];
+            for (int t = 0; t < T; ++t) {
+                float cf = R.sg[t];
+                if (a > 0) {
+                    cf = 0.f;
+#pragma unroll
+                    for (int j = 0; j < TOPK; ++j)
+                        if (R.ids[t][j] == R.active[a - 1]) cf = R.w[t][j];
+                }
+                rec->coef[t][a] = cf;
+            }
+        }
+        if (a == 127) rec->slot_e[127] = nact + 1;
     }
     if (slot > 0) {
         const int nact = min(max(R.nact, 0), TOPK * T);
@@ -570,45 +599,60 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
 
 // grid (H/4): 4 output rows per workgroup over every active expert (wave w
 // takes slots w, w+4, ...), combine with the routing weights and the shared
-// gate, residual add.  Fixed summation order: deterministic.
-// Two waves per SIMD keep the whole grid resident at once.
+// gate, residual add.  Fixed summation order: deterministic.  The record is
+// read with scalar loads, all issued together; every vector load of a pass
+// (codes, scales, biases and the h row of each slot's first token) goes out
+// before any arithmetic.  Two waves per SIMD keep the whole grid resident.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_down_dec(const uint16_t* __restrict__ hin, int T, const RouteRec* __restrict__ rec,
+void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __restrict__ rec,
                      moe_qffn routed, moe_qffn shared, uint16_t* __restrict__ y,
                      const uint16_t* __restrict__ x, uint16_t* __restrict__ res) {
-    __shared__ RouteRec R;
     __shared__ float yacc[4][MOE_DECODE_T][4];
-    {
-        const int* src = reinterpret_cast<const int*>(rec);
-        int* dst = reinterpret_cast<int*>(&R);
-        for (int i = threadIdx.x; i < REC_WORDS; i += 256) dst[i] = src[i];
-    }
-    __syncthreads();
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane >> 4, c = lane & 15;
+    const int m = blockIdx.x * 4 + r;
     const DnPtrs pr = dn_ptrs(routed), ps = dn_ptrs(shared);
     const uint32_t mag = fp16_1024_pair();
-    const int m = blockIdx.x * 4 + r;
     const uint32_t tall = (1u << T) - 1u;
-    const int nslots = min(max(R.nact, 0), TOPK * T) + 1;
+    // the residual input is needed only at the end: load it first
+    const int ot = threadIdx.x >> 2, orr = threadIdx.x & 3;
+    const bool writer = (int)threadIdx.x < T * 4;
+    const size_t o = (size_t)ot * H + blockIdx.x * 4 + orr;
+    const uint16_t xin = x[writer ? o : 0];
+    // the record: one load per array and lane, then lane reads
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 re = reinterpret_cast<const u32x2*>(rec->slot_e)[lane];
+    const u32x2 rm = reinterpret_cast<const u32x2*>(rec->slot_m)[lane];
+    u32x2 rc[MOE_DECODE_T];
+#pragma unroll
+    for (int t = 0; t < MOE_DECODE_T; ++t) rc[t] = reinterpret_cast<const u32x2*>(rec->coef[t])[lane];
+    // (all of it is needed next; without this the compiler sinks the later
+    // loads behind a wait for the first)
+    asm volatile("" ::"v"(re), "v"(rm), "v"(rc[0]), "v"(rc[1]), "v"(rc[2]), "v"(rc[3]), "v"(rc[4]),
+                 "v"(rc[5]), "v"(rc[6]), "v"(rc[7]));
+    auto slot_word = [](u32x2 v, int a) -> uint32_t {
+        const uint32_t lo = __builtin_amdgcn_readlane(v[0], a >> 1);
+        const uint32_t hi = __builtin_amdgcn_readlane(v[1], a >> 1);
+        return (a & 1) ? hi : lo;
+    };
+    const int nslots = min(max((int)__builtin_amdgcn_readlane(re[1], 63), 1), TOPK * T + 1);
     float acc[MOE_DECODE_T];
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_T; ++t) acc[t] = 0.f;
-    for (int a0 = wave; a0 < nslots; a0 += 16) {
-        // every load of the pass goes out before any arithmetic: codes,
-        // scales and biases of up to four slots and the h row of each
-        // slot's first token
+    // one pass: slots a0, a0+4, a0+8, a0+12 (a0 < nslots)
+    auto pass = [&](const int a0) {
+        int ak[4], tf[4];
+        uint32_t mk[4];
         uint4v dw[4], h0[4][4];
         float ds[4], db[4];
-        int tf[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int a = a0 + 4 * k < nslots ? a0 + 4 * k : a0;
-            const int e = a == 0 ? 0
-                                 : __builtin_amdgcn_readfirstlane(min(max(R.active[a - 1], 0), E - 1));
-            const uint32_t mask =
-                (a == 0 ? tall : (uint32_t)__builtin_amdgcn_readfirstlane(R.tmask[a - 1])) & tall;
-            tf[k] = mask ? __builtin_ctz(mask) : 0;
+            // slots past the last one repeat a valid slot's loads (unused)
+            const int a = min(a0 + 4 * k, nslots - 1);
+            ak[k] = a;
+            const int e = min(max((int)slot_word(re, a), 0), E - 1);
+            mk[k] = slot_word(rm, a) & tall;
+            tf[k] = mk[k] ? __builtin_ctz(mk[k]) : 0;
             const DnPtrs q = pick(a == 0, ps, pr);
             const size_t row = (size_t)e * H + m;
             dw[k] = ((const GLOBAL_AS uint4v*)(q.q + row * (I / 8)))[c];
@@ -619,20 +663,18 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const RouteRec* __
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) h0[k][cc] = hr[cc];
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int a = a0 + 4 * k;
-            if (a >= nslots) break;
-            const int e = a == 0 ? -1 : R.active[a - 1];
-            const uint32_t mask = (a == 0 ? tall : R.tmask[a - 1]) & tall;
-            for (int t = 0; t < T; ++t) {
-                if (!((mask >> t) & 1u)) continue;
-                float coef = R.sg[t];
-                if (a > 0) {
+            if (a0 + 4 * k >= nslots) break;
+            const int a = ak[k];
+            for (int t = tf[k]; t < T; ++t) {
+                if (!((mk[k] >> t) & 1u)) continue;
+                uint32_t cw = slot_word(rc[0], a);
 #pragma unroll
-                    for (int j = 0; j < TOPK; ++j)
-                        if (R.ids[t][j] == e) coef = R.w[t][j];
-                }
+                for (int tt = 1; tt < MOE_DECODE_T; ++tt)
+                    if (tt < T && t == tt) cw = slot_word(rc[tt], a);
+                const float coef = __builtin_bit_cast(float, cw);
                 uint4v hv[4];
                 if (t == tf[k]) {
 #pragma unroll
@@ -657,7 +699,12 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const RouteRec* __
                     if (tt == t) acc[tt] += part;
             }
         }
-    }
+    };
+    // the first pass is peeled, so that its loads are not held up by waits
+    // for the loop's previous iteration
+    pass(wave);
+    for (int a0 = wave + 16; a0 < nslots; a0 += 16) pass(a0);
+    // reduce the 16 lanes of each row, then the four waves in a fixed order
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_T; ++t) {
         if (t < T) {
@@ -670,22 +717,20 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const RouteRec* __
         }
     }
     __syncthreads();
-    if (threadIdx.x < T * 4) {
-        const int t = threadIdx.x >> 2, rr = threadIdx.x & 3;
-        const float v = ((yacc[0][t][rr] + yacc[1][t][rr]) + yacc[2][t][rr]) + yacc[3][t][rr];
+    if (writer) {
+        const float v = ((yacc[0][ot][orr] + yacc[1][ot][orr]) + yacc[2][ot][orr]) + yacc[3][ot][orr];
         const uint32_t yb = f32_to_bf16(v);
-        const size_t o = (size_t)t * H + blockIdx.x * 4 + rr;
         y[o] = (uint16_t)yb;
-        if (res) res[o] = (uint16_t)f32_to_bf16(bf16_to_f32(x[o]) + bf16_to_f32(yb));
+        if (res) res[o] = (uint16_t)f32_to_bf16(bf16_to_f32(xin) + bf16_to_f32(yb));
     }
 }
 
-size_t route_rec_bytes() { return sizeof(RouteRec); }
+size_t route_rec_bytes() { return sizeof(DownRec); }
 
 void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
                                float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
                                void* rec, uint16_t* y, uint16_t* res, hipStream_t st) {
-    RouteRec* R = static_cast<RouteRec*>(rec);
+    DownRec* R = static_cast<DownRec*>(rec);
     (void)counter;
     hipLaunchKernelGGL(route_logits_dec, dim3(NRB + 1 + T), dim3(256), 0, st, x, T, L.w_router,
                        L.router_bias, L.w_shared_gate, logits, z, xh);
