@@ -47,7 +47,8 @@ class MoeError(RuntimeError):
 class moe_qffn(C.Structure):
     _fields_ = [("gate_q", C.c_void_p), ("up_q", C.c_void_p), ("down_q", C.c_void_p),
                 ("gate_s", C.c_void_p), ("gate_b", C.c_void_p), ("up_s", C.c_void_p),
-                ("up_b", C.c_void_p), ("down_s", C.c_void_p), ("down_b", C.c_void_p)]
+                ("up_b", C.c_void_p), ("down_s", C.c_void_p), ("down_b", C.c_void_p),
+                ("expert_stride", C.c_int64)]
 
 
 class moe_layer(C.Structure):
@@ -136,39 +137,67 @@ _U16 = (torch.int16, torch.bfloat16, torch.float16, torch.uint16)
 _U32 = (torch.int32, torch.uint32)
 
 
+# Expert-major layout: one 2 MiB-aligned 2 MiB block per expert holding its
+# nine arrays at these byte offsets (1,769,472 bytes used).
+EXPERT_BLOCK = 2 << 20
+_BLOCK_OFFSETS = {"gate_q": 0, "up_q": 1 << 19, "down_q": 2 << 19,
+                  "gate_s": 3 << 19, "gate_b": (3 << 19) + (1 << 15), "up_s": (3 << 19) + (2 << 15),
+                  "up_b": (3 << 19) + (3 << 15), "down_s": (3 << 19) + (4 << 15),
+                  "down_b": (3 << 19) + (5 << 15)}
+
+
 class DeviceQFFN:
-    """A quantised expert stack resident in device memory."""
+    """A quantised expert stack resident in device memory.
 
-    def __init__(self, q, n: int, device="cuda"):
+    layout "dense" (default): the nine arrays each contiguous over experts
+    (moe_qffn.expert_stride = 0); "expert": every expert's codes, scales and
+    biases in one 2 MiB-aligned 2 MiB block (expert_stride = 2 MiB)."""
+
+    def __init__(self, q, n: int, device="cuda", layout: str = "dense"):
         H, I, G = MOE_HIDDEN, MOE_INTER, MOE_GROUP
-
-        def up(a, shape, dt):
-            a = np.ascontiguousarray(a)
-            assert a.shape == shape, (a.shape, shape)
-            return torch.from_numpy(a.view(dt)).to(device)
-
-        self.tensors = {
-            "gate_q": up(q.gate_q, (n, I, H // 8), np.int32),
-            "up_q": up(q.up_q, (n, I, H // 8), np.int32),
-            "down_q": up(q.down_q, (n, H, I // 8), np.int32),
-            "gate_s": up(q.gate_s, (n, I, H // G), np.int16),
-            "gate_b": up(q.gate_b, (n, I, H // G), np.int16),
-            "up_s": up(q.up_s, (n, I, H // G), np.int16),
-            "up_b": up(q.up_b, (n, I, H // G), np.int16),
-            "down_s": up(q.down_s, (n, H, I // G), np.int16),
-            "down_b": up(q.down_b, (n, H, I // G), np.int16),
-        }
-        self.c = moe_qffn(**{k: v.data_ptr() for k, v in self.tensors.items()})
+        shapes = {"gate_q": ((n, I, H // 8), np.int32), "up_q": ((n, I, H // 8), np.int32),
+                  "down_q": ((n, H, I // 8), np.int32),
+                  "gate_s": ((n, I, H // G), np.int16), "gate_b": ((n, I, H // G), np.int16),
+                  "up_s": ((n, I, H // G), np.int16), "up_b": ((n, I, H // G), np.int16),
+                  "down_s": ((n, H, I // G), np.int16), "down_b": ((n, H, I // G), np.int16)}
+        arrays = {}
+        for k, (shape, dt) in shapes.items():
+            a = np.ascontiguousarray(getattr(q, k))
+            assert a.shape == shape, (k, a.shape, shape)
+            arrays[k] = a.view(dt)
+        self.layout = layout
+        self._nbytes = sum(a.nbytes for a in arrays.values())
+        if layout == "dense":
+            self.tensors = {k: torch.from_numpy(a).to(device) for k, a in arrays.items()}
+            self.c = moe_qffn(**{k: v.data_ptr() for k, v in self.tensors.items()},
+                              expert_stride=0)
+        elif layout == "expert":
+            host = np.zeros((n, EXPERT_BLOCK), dtype=np.uint8)
+            for k, a in arrays.items():
+                per = a.reshape(n, -1).view(np.uint8)
+                o = _BLOCK_OFFSETS[k]
+                host[:, o:o + per.shape[1]] = per
+            self.buf = torch.empty(n * EXPERT_BLOCK + EXPERT_BLOCK, dtype=torch.uint8, device=device)
+            skip = (-self.buf.data_ptr()) % EXPERT_BLOCK
+            self.blocks = self.buf[skip:skip + n * EXPERT_BLOCK]
+            self.blocks.copy_(torch.from_numpy(host.reshape(-1)))
+            base = self.blocks.data_ptr()
+            self.tensors = {}
+            self.c = moe_qffn(**{k: base + o for k, o in _BLOCK_OFFSETS.items()},
+                              expert_stride=EXPERT_BLOCK)
+        else:
+            raise ValueError(f"unknown layout {layout!r}")
 
     @property
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in self.tensors.values())
+        """Bytes of weights (codes, scales, biases), without block padding."""
+        return self._nbytes
 
 
 class DeviceLayer:
     """One MoE layer resident in device memory, with its C descriptor."""
 
-    def __init__(self, layer, device="cuda"):
+    def __init__(self, layer, device="cuda", layout: str = "dense"):
         assert (layer.dims.E, layer.dims.topk, layer.dims.H, layer.dims.I, layer.dims.G) == (
             MOE_EXPERTS, MOE_TOPK, MOE_HIDDEN, MOE_INTER, MOE_GROUP), "production shape only"
         self.w_router = torch.from_numpy(np.ascontiguousarray(layer.w_router).view(np.int16)).to(device)
@@ -176,8 +205,8 @@ class DeviceLayer:
             np.ascontiguousarray(layer.w_shared_gate).view(np.int16)).to(device)
         self.router_bias = (None if layer.router_bias is None else
                             torch.from_numpy(np.ascontiguousarray(layer.router_bias, np.float32)).to(device))
-        self.routed = DeviceQFFN(layer.routed, MOE_EXPERTS, device)
-        self.shared = DeviceQFFN(layer.shared, 1, device)
+        self.routed = DeviceQFFN(layer.routed, MOE_EXPERTS, device, layout)
+        self.shared = DeviceQFFN(layer.shared, 1, device, layout)
         assert tuple(self.w_router.shape) == (MOE_EXPERTS, MOE_HIDDEN)
         assert tuple(self.w_shared_gate.shape) == (MOE_HIDDEN,)
         self.c = moe_layer(self.w_router.data_ptr(),

@@ -21,6 +21,33 @@ constexpr int WAVE = 64;
 // batch in one tile).
 constexpr int MT_ROWS = 160;
 
+// Device view of one expert stack: the nine arrays and the byte distance
+// between consecutive experts in the code arrays (sq) and in the
+// scale/bias arrays (ss) -- the dense sizes, or the caller's expert stride.
+struct QFFN {
+    const uint32_t *gate_q, *up_q, *down_q;
+    const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
+    uint32_t sq, ss;
+};
+
+constexpr uint32_t DENSE_SQ = I * H / 2;         // one expert's codes: 524288 B (any matrix)
+constexpr uint32_t DENSE_SS = I * (H / G) * 2;   // one expert's scales: 32768 B (any matrix)
+static_assert(DENSE_SQ == H * I / 2 && DENSE_SS == H * (I / G) * 2, "square per-expert blocks");
+
+inline QFFN qffn_view(const moe_qffn& q) {
+    const bool dense = q.expert_stride == 0;
+    return QFFN{q.gate_q, q.up_q, q.down_q, q.gate_s, q.gate_b, q.up_s, q.up_b, q.down_s, q.down_b,
+                dense ? DENSE_SQ : (uint32_t)q.expert_stride,
+                dense ? DENSE_SS : (uint32_t)q.expert_stride};
+}
+
+// Base of expert e's block in an array with byte stride `stride`.
+template <typename P>
+__device__ __forceinline__ P expert_at(P p, int e, uint32_t stride) {
+    typedef const char* CP;
+    return (P)((CP)p + (size_t)e * stride);
+}
+
 struct Tile {
     int group;     // 0..255 routed expert, 256 shared expert
     int row0;      // first row in the permuted row space (shared rows start at 8T)

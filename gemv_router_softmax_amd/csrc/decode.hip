@@ -124,29 +124,29 @@ __global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ perm,
                                                      const Tile* __restrict__ tiles,
                                                      const int* __restrict__ tile_count,
-                                                     moe_qffn routed, moe_qffn shared,
+                                                     QFFN routed, QFFN shared,
                                                      uint16_t* __restrict__ hout) {
     if ((int)blockIdx.x >= *tile_count) return;
     const Tile tl = tiles[blockIdx.x];
     const bool sh = tl.group >= E;
     const int e = sh ? 0 : tl.group;
-    const moe_qffn q = sh ? shared : routed;
+    const QFFN q = sh ? shared : routed;
     const int lane = threadIdx.x & 63;
     const int n0 = blockIdx.y * 16 + (threadIdx.x >> 6) * 4;
     // value index i < 4: gate row n0+i, i >= 4: up row n0+i-4
     uint4v wq[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const size_t row = (size_t)e * I + n0 + (i & 3);
-        const uint32_t* qb = i < 4 ? q.gate_q : q.up_q;
+        const size_t row = n0 + (i & 3);
+        const uint32_t* qb = expert_at(i < 4 ? q.gate_q : q.up_q, e, q.sq);
         wq[i] = reinterpret_cast<const uint4v*>(qb + row * (H / 8))[lane];
     }
     float s[8], b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const size_t row = (size_t)e * I + n0 + (i & 3);
-        const uint16_t* sb = i < 4 ? q.gate_s : q.up_s;
-        const uint16_t* bb = i < 4 ? q.gate_b : q.up_b;
+        const size_t row = n0 + (i & 3);
+        const uint16_t* sb = expert_at(i < 4 ? q.gate_s : q.up_s, e, q.ss);
+        const uint16_t* bb = expert_at(i < 4 ? q.gate_b : q.up_b, e, q.ss);
         s[i] = fp16_to_f32(sb[row * (H / G) + (lane >> 1)]);
         b[i] = fp16_to_f32(bb[row * (H / G) + (lane >> 1)]);
     }
@@ -191,8 +191,8 @@ __global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict_
 __global__ __launch_bounds__(256) void decode_down_combine(
     const uint16_t* __restrict__ hin, int T, const int32_t* __restrict__ perm,
     const Tile* __restrict__ tiles, const int* __restrict__ tile_count,
-    const float* __restrict__ wts, const float* __restrict__ sg, moe_qffn routed,
-    moe_qffn shared, uint16_t* __restrict__ y, const uint16_t* __restrict__ x,
+    const float* __restrict__ wts, const float* __restrict__ sg, QFFN routed,
+    QFFN shared, uint16_t* __restrict__ y, const uint16_t* __restrict__ x,
     uint16_t* __restrict__ res) {
     __shared__ float yacc[4][MOE_DECODE_T_MAX][4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -213,11 +213,11 @@ __global__ __launch_bounds__(256) void decode_down_combine(
             tl[k] = tiles[ti < ntiles ? ti : ti0];
             const bool sh = tl[k].group >= E;
             const int e = sh ? 0 : tl[k].group;
-            const moe_qffn& q = sh ? shared : routed;
-            const size_t row = (size_t)e * H + m;
-            dw[k] = reinterpret_cast<const uint4v*>(q.down_q + row * (I / 8))[c];
-            ds[k] = fp16_to_f32(q.down_s[row * (I / G) + (c >> 1)]);
-            db[k] = fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]);
+            const QFFN& q = sh ? shared : routed;
+            const size_t row = m;
+            dw[k] = reinterpret_cast<const uint4v*>(expert_at(q.down_q, e, q.sq) + row * (I / 8))[c];
+            ds[k] = fp16_to_f32(expert_at(q.down_s, e, q.ss)[row * (I / G) + (c >> 1)]);
+            db[k] = fp16_to_f32(expert_at(q.down_b, e, q.ss)[row * (I / G) + (c >> 1)]);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -330,30 +330,38 @@ static_assert(DEC_SLOTS < 127, "slot count word");
 struct GUPtrs {
     const GLOBAL_AS uint32_t *gq, *uq;
     const GLOBAL_AS uint16_t *gs, *gb, *us, *ub;
+    uint32_t sq, ss;
 };
 struct DnPtrs {
     const GLOBAL_AS uint32_t* q;
     const GLOBAL_AS uint16_t *s, *b;
+    uint32_t sq, ss;
 };
-__device__ __forceinline__ GUPtrs gu_ptrs(const moe_qffn& f) {
+__device__ __forceinline__ GUPtrs gu_ptrs(const QFFN& f) {
     GUPtrs p{(const GLOBAL_AS uint32_t*)f.gate_q, (const GLOBAL_AS uint32_t*)f.up_q,
              (const GLOBAL_AS uint16_t*)f.gate_s, (const GLOBAL_AS uint16_t*)f.gate_b,
-             (const GLOBAL_AS uint16_t*)f.up_s,   (const GLOBAL_AS uint16_t*)f.up_b};
+             (const GLOBAL_AS uint16_t*)f.up_s,   (const GLOBAL_AS uint16_t*)f.up_b,
+             f.sq, f.ss};
     asm volatile("" : "+s"(p.gq), "+s"(p.uq), "+s"(p.gs), "+s"(p.gb), "+s"(p.us), "+s"(p.ub));
     return p;
 }
-__device__ __forceinline__ DnPtrs dn_ptrs(const moe_qffn& f) {
+__device__ __forceinline__ DnPtrs dn_ptrs(const QFFN& f) {
     DnPtrs p{(const GLOBAL_AS uint32_t*)f.down_q, (const GLOBAL_AS uint16_t*)f.down_s,
-             (const GLOBAL_AS uint16_t*)f.down_b};
+             (const GLOBAL_AS uint16_t*)f.down_b, f.sq, f.ss};
     asm volatile("" : "+s"(p.q), "+s"(p.s), "+s"(p.b));
     return p;
 }
 __device__ __forceinline__ GUPtrs pick(bool c, const GUPtrs& a, const GUPtrs& b) {
-    return GUPtrs{c ? a.gq : b.gq, c ? a.uq : b.uq, c ? a.gs : b.gs,
-                  c ? a.gb : b.gb, c ? a.us : b.us, c ? a.ub : b.ub};
+    return GUPtrs{c ? a.gq : b.gq, c ? a.uq : b.uq, c ? a.gs : b.gs, c ? a.gb : b.gb,
+                  c ? a.us : b.us, c ? a.ub : b.ub, c ? a.sq : b.sq, c ? a.ss : b.ss};
 }
 __device__ __forceinline__ DnPtrs pick(bool c, const DnPtrs& a, const DnPtrs& b) {
-    return DnPtrs{c ? a.q : b.q, c ? a.s : b.s, c ? a.b : b.b};
+    return DnPtrs{c ? a.q : b.q, c ? a.s : b.s, c ? a.b : b.b, c ? a.sq : b.sq, c ? a.ss : b.ss};
+}
+// Expert e's block of a global-memory array with byte stride `stride`.
+template <typename T>
+__device__ __forceinline__ const GLOBAL_AS T* gexpert(const GLOBAL_AS T* p, int e, uint32_t stride) {
+    return (const GLOBAL_AS T*)((const GLOBAL_AS char*)p + (size_t)e * stride);
 }
 
 // Top-8 of every token (one wave per token) and the active-expert list, by
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
                                                          const float* __restrict__ logits,
                                                          const float* __restrict__ z,
                                                          DownRec* __restrict__ rec,
-                                                         moe_qffn routed, moe_qffn shared,
+                                                         QFFN routed, QFFN shared,
                                                          uint16_t* __restrict__ hout) {
     __shared__ RouteRec R;
     __shared__ int mark[E];
@@ -541,16 +549,16 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
     uint4v wq[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const size_t row = (size_t)e * I + n0 + (i & 3);
-        const GLOBAL_AS uint32_t* qb = i < 4 ? q.gq : q.uq;
+        const size_t row = n0 + (i & 3);
+        const GLOBAL_AS uint32_t* qb = gexpert(i < 4 ? q.gq : q.uq, e, q.sq);
         wq[i] = ((const GLOBAL_AS uint4v*)(qb + row * (H / 8)))[lane];
     }
     float s[8], b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const size_t row = (size_t)e * I + n0 + (i & 3);
-        const GLOBAL_AS uint16_t* sb = i < 4 ? q.gs : q.us;
-        const GLOBAL_AS uint16_t* bb = i < 4 ? q.gb : q.ub;
+        const size_t row = n0 + (i & 3);
+        const GLOBAL_AS uint16_t* sb = gexpert(i < 4 ? q.gs : q.us, e, q.ss);
+        const GLOBAL_AS uint16_t* bb = gexpert(i < 4 ? q.gb : q.ub, e, q.ss);
         s[i] = fp16_to_f32(sb[row * (H / G) + (lane >> 1)]);
         b[i] = fp16_to_f32(bb[row * (H / G) + (lane >> 1)]);
     }
@@ -605,7 +613,7 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
 // before any arithmetic.  Two waves per SIMD keep the whole grid resident.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __restrict__ rec,
-                     moe_qffn routed, moe_qffn shared, uint16_t* __restrict__ y,
+                     QFFN routed, QFFN shared, uint16_t* __restrict__ y,
                      const uint16_t* __restrict__ x, uint16_t* __restrict__ res) {
     __shared__ float yacc[4][MOE_DECODE_T][4];
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -654,10 +662,10 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __r
             mk[k] = slot_word(rm, a) & tall;
             tf[k] = mk[k] ? __builtin_ctz(mk[k]) : 0;
             const DnPtrs q = pick(a == 0, ps, pr);
-            const size_t row = (size_t)e * H + m;
-            dw[k] = ((const GLOBAL_AS uint4v*)(q.q + row * (I / 8)))[c];
-            ds[k] = fp16_to_f32(q.s[row * (I / G) + (c >> 1)]);
-            db[k] = fp16_to_f32(q.b[row * (I / G) + (c >> 1)]);
+            const size_t row = m;
+            dw[k] = ((const GLOBAL_AS uint4v*)(gexpert(q.q, e, q.sq) + row * (I / 8)))[c];
+            ds[k] = fp16_to_f32(gexpert(q.s, e, q.ss)[row * (I / G) + (c >> 1)]);
+            db[k] = fp16_to_f32(gexpert(q.b, e, q.ss)[row * (I / G) + (c >> 1)]);
             const uint4v* hr =
                 reinterpret_cast<const uint4v*>(hin + ((size_t)a * T + tf[k]) * I) + c * 4;
 #pragma unroll
@@ -730,14 +738,15 @@ size_t route_rec_bytes() { return sizeof(DownRec); }
 void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
                                float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
                                void* rec, uint16_t* y, uint16_t* res, hipStream_t st) {
+    const QFFN routed = qffn_view(L.routed), shared = qffn_view(L.shared);
     DownRec* R = static_cast<DownRec*>(rec);
     (void)counter;
     hipLaunchKernelGGL(route_logits_dec, dim3(NRB + 1 + T), dim3(256), 0, st, x, T, L.w_router,
                        L.router_bias, L.w_shared_gate, logits, z, xh);
     hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T,
-                       logits, z, R, L.routed, L.shared, hbuf);
-    hipLaunchKernelGGL(decode_down_dec, dim3(H / 4), dim3(256), 0, st, hbuf, T, R, L.routed,
-                       L.shared, y, x, res);
+                       logits, z, R, routed, shared, hbuf);
+    hipLaunchKernelGGL(decode_down_dec, dim3(H / 4), dim3(256), 0, st, hbuf, T, R, routed,
+                       shared, y, x, res);
 }
 
 // Zero the workspace's synchronisation words (a fill kernel, not a memset,
@@ -760,15 +769,15 @@ void launch_route_select(const float* logits, const uint16_t* x, const uint16_t*
 }
 
 void launch_decode_gateup(const uint16_t* xh, int T, const int32_t* perm, const Tile* tiles,
-                          const int* tile_count, int max_tiles, const moe_qffn& routed,
-                          const moe_qffn& shared, uint16_t* hbuf, hipStream_t st) {
+                          const int* tile_count, int max_tiles, const QFFN& routed,
+                          const QFFN& shared, uint16_t* hbuf, hipStream_t st) {
     hipLaunchKernelGGL(decode_gateup, dim3(max_tiles, I / 16), dim3(256), 0, st, xh, T, perm, tiles,
                        tile_count, routed, shared, hbuf);
 }
 
 void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm,
                                 const Tile* tiles, const int* tile_count, const float* wts,
-                                const float* sg, const moe_qffn& routed, const moe_qffn& shared,
+                                const float* sg, const QFFN& routed, const QFFN& shared,
                                 uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st) {
     hipLaunchKernelGGL(decode_down_combine, dim3(H / 4), dim3(256), 0, st, hbuf, T, perm, tiles,
                        tile_count, wts, sg, routed, shared, y, x, res);

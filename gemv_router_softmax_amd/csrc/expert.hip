@@ -33,20 +33,20 @@ __device__ __forceinline__ int row_token(int row, int T, const int32_t* __restri
 __global__ __launch_bounds__(256) void decode_down(const uint16_t* __restrict__ hin, int T,
                                                    const Tile* __restrict__ tiles,
                                                    const int* __restrict__ tile_count,
-                                                   moe_qffn routed, moe_qffn shared,
+                                                   QFFN routed, QFFN shared,
                                                    float* __restrict__ out) {
     if ((int)blockIdx.x >= *tile_count) return;
     const Tile tl = tiles[blockIdx.x];
     const bool sh = tl.group >= E;
     const int e = sh ? 0 : tl.group;
-    const moe_qffn q = sh ? shared : routed;
+    const QFFN q = sh ? shared : routed;
     const int lane = threadIdx.x & 63;
     const int c = lane & 15;
     const int m = blockIdx.y * 16 + (threadIdx.x >> 6) * 4 + (lane >> 4);
-    const size_t row = (size_t)e * H + m;
-    const uint4v dw = reinterpret_cast<const uint4v*>(q.down_q + row * (I / 8))[c];
-    const float s = fp16_to_f32(q.down_s[row * (I / G) + (c >> 1)]);
-    const float b = fp16_to_f32(q.down_b[row * (I / G) + (c >> 1)]);
+    const size_t row = m;
+    const uint4v dw = reinterpret_cast<const uint4v*>(expert_at(q.down_q, e, q.sq) + row * (I / 8))[c];
+    const float s = fp16_to_f32(expert_at(q.down_s, e, q.ss)[row * (I / G) + (c >> 1)]);
+    const float b = fp16_to_f32(expert_at(q.down_b, e, q.ss)[row * (I / G) + (c >> 1)]);
     for (int rr = 0; rr < tl.nrows; ++rr) {
         // h rows are fp16 in chunk-slot order (decode_gateup)
         const uint4v* hr = reinterpret_cast<const uint4v*>(hin + (size_t)(tl.row0 + rr) * I) + c * 4;
@@ -232,6 +232,7 @@ struct WPtr {
     const uint32_t* q;
     const uint16_t* s;
     const uint16_t* b;
+    uint32_t sq, ss;     // bytes between consecutive experts (codes, scales/biases)
 };
 
 // This wave's matrix (gate/up: waves 0-1 gate, 2-3 up; down: down) of one
@@ -239,7 +240,7 @@ struct WPtr {
 // the shared stack is then a select of values, never of the argument
 // structs' addresses (which would force the structs into scratch memory).
 template <int MODE>
-__device__ __forceinline__ WPtr wave_ptrs(const moe_qffn& f) {
+__device__ __forceinline__ WPtr wave_ptrs(const QFFN& f) {
     WPtr w;
     if (MODE != GM_GATEUP) {
         w.q = f.down_q; w.s = f.down_s; w.b = f.down_b;
@@ -249,6 +250,8 @@ __device__ __forceinline__ WPtr wave_ptrs(const moe_qffn& f) {
         w.q = f.gate_q; w.s = f.gate_s; w.b = f.gate_b;
     }
     asm volatile("" : "+s"(w.q), "+s"(w.s), "+s"(w.b));
+    w.sq = f.sq;
+    w.ss = f.ss;
     return w;
 }
 
@@ -271,10 +274,10 @@ __device__ __forceinline__ GSrc gemm_src(const GItem& m, const int32_t* tok, int
     const uint32_t* code = m.shared ? ps.q : pr.q;
     const uint16_t* sc = m.shared ? ps.s : pr.s;
     const uint16_t* bi = m.shared ? ps.b : pr.b;
-    const size_t eo = (size_t)m.e * ROWS_W;
-    g.rq = buf_rsrc(code + eo * WPR, ROWS_W * WPR * 4);
-    g.rs = buf_rsrc(sc + eo * SPR, ROWS_W * SPR * 2);
-    g.rb = buf_rsrc(bi + eo * SPR, ROWS_W * SPR * 2);
+    const uint32_t sq = m.shared ? ps.sq : pr.sq, ss = m.shared ? ps.ss : pr.ss;
+    g.rq = buf_rsrc(expert_at(code, m.e, sq), ROWS_W * WPR * 4);
+    g.rs = buf_rsrc(expert_at(sc, m.e, ss), ROWS_W * SPR * 2);
+    g.rb = buf_rsrc(expert_at(bi, m.e, ss), ROWS_W * SPR * 2);
     auto wrow = [&](int C) { return GATEUP ? m.nb * 128 + (C & 127) : m.nb * 256 + C; };
     // B: LDS slot (lane & 1) of column C holds the column's piece slot ^ ((C >> 3) & 1)
 #pragma unroll
@@ -677,7 +680,7 @@ template <int KDIM, int MODE>
 __global__ __launch_bounds__(pg::THREADS, 1) void grouped_gemm(GemmArgs args,
                                                               const Tile* __restrict__ tiles,
                                                               const int* __restrict__ tile_count,
-                                                              moe_qffn routed, moe_qffn shared) {
+                                                              QFFN routed, QFFN shared) {
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     __shared__ __attribute__((aligned(16))) uint8_t lds[pg::LDS_BYTES];
@@ -732,12 +735,12 @@ __global__ __launch_bounds__(256) void prep_x_f16(const uint16_t* __restrict__ x
 }
 
 void launch_decode_gateup(const uint16_t* xh, int T, const int32_t* perm, const Tile* tiles,
-                          const int* tile_count, int max_tiles, const moe_qffn& routed,
-                          const moe_qffn& shared, uint16_t* hbuf, hipStream_t st);
+                          const int* tile_count, int max_tiles, const QFFN& routed,
+                          const QFFN& shared, uint16_t* hbuf, hipStream_t st);
 
 void launch_expert_decode(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                          const int* tile_count, int max_tiles, const moe_qffn& routed,
-                          const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
+                          const int* tile_count, int max_tiles, const QFFN& routed,
+                          const QFFN& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                           hipStream_t st) {
     const size_t chunks = (size_t)T * (H / 8);
     hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
@@ -764,7 +767,7 @@ static GemmArgs gemm_args(const uint16_t* ain, size_t ain_bytes, int T, const in
 constexpr unsigned GEMM_GRID = 256;   // one workgroup per compute unit (a multiple of 8 XCDs)
 
 static void launch_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                          const int* tile_count, const moe_qffn& routed, const moe_qffn& shared,
+                          const int* tile_count, const QFFN& routed, const QFFN& shared,
                           uint16_t* xh, uint16_t* hbuf, hipStream_t st) {
     const size_t chunks = (size_t)T * (H / 8);
     hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
@@ -776,8 +779,8 @@ static void launch_gateup(const uint16_t* x, int T, const int32_t* perm, const T
 }
 
 void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                           const int* tile_count, int /*max_tiles*/, const moe_qffn& routed,
-                           const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
+                           const int* tile_count, int /*max_tiles*/, const QFFN& routed,
+                           const QFFN& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                            hipStream_t st) {
     launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, st);
     GemmArgs dn = gemm_args(hbuf, (size_t)(TOPK + 1) * T * I * 2, T, perm);
@@ -789,8 +792,8 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
 // Whole-layer prefill expert part: gate/up, then down writing fp16 rows of
 // (routing weight or shared gate) * d, summed per token by combine_f16.
 void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                                 const int* tile_count, int /*max_tiles*/, const moe_qffn& routed,
-                                 const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf,
+                                 const int* tile_count, int /*max_tiles*/, const QFFN& routed,
+                                 const QFFN& shared, uint16_t* xh, uint16_t* hbuf,
                                  uint16_t* d16, const float* wsorted, const float* sg,
                                  hipStream_t st) {
     launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, st);

@@ -22,11 +22,11 @@ void launch_route_select(const float* logits, const uint16_t* x, const uint16_t*
                          int32_t* perm, int32_t* inv, Tile* tiles, int* tile_count,
                          uint16_t* xh, hipStream_t st);
 void launch_decode_gateup(const uint16_t* xh, int T, const int32_t* perm, const Tile* tiles,
-                          const int* tile_count, int max_tiles, const moe_qffn& routed,
-                          const moe_qffn& shared, uint16_t* hbuf, hipStream_t st);
+                          const int* tile_count, int max_tiles, const QFFN& routed,
+                          const QFFN& shared, uint16_t* hbuf, hipStream_t st);
 void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm,
                                 const Tile* tiles, const int* tile_count, const float* wts,
-                                const float* sg, const moe_qffn& routed, const moe_qffn& shared,
+                                const float* sg, const QFFN& routed, const QFFN& shared,
                                 uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
                                float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
@@ -40,16 +40,16 @@ void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hi
 int perm_chunks(int T);
 int max_tiles(int T);
 void launch_expert_decode(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                          const int* tile_count, int max_tiles, const moe_qffn& routed,
-                          const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
+                          const int* tile_count, int max_tiles, const QFFN& routed,
+                          const QFFN& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                           hipStream_t st);
 void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                           const int* tile_count, int max_tiles, const moe_qffn& routed,
-                           const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
+                           const int* tile_count, int max_tiles, const QFFN& routed,
+                           const QFFN& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                            hipStream_t st);
 void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                                 const int* tile_count, int max_tiles, const moe_qffn& routed,
-                                 const moe_qffn& shared, uint16_t* xh, uint16_t* hbuf,
+                                 const int* tile_count, int max_tiles, const QFFN& routed,
+                                 const QFFN& shared, uint16_t* xh, uint16_t* hbuf,
                                  uint16_t* d16, const float* wsorted, const float* sg,
                                  hipStream_t st);
 void launch_combine_f16(const uint16_t* d16, const int32_t* inv, int T, uint16_t* y,
@@ -120,6 +120,11 @@ int check_qffn(const moe_qffn* q) {
         if (!p) return MOE_ERR_INVALID_ARG;
     for (const void* p : ps)
         if (!a16(p)) return MOE_ERR_ALIGN;
+    // 0 (dense) or a per-expert block of at least one code matrix, 256-byte
+    // granular, small enough for the kernels' 32-bit strides
+    const int64_t st = q->expert_stride;
+    if (st != 0 && (st < (int64_t)DENSE_SQ || st % 256 != 0 || st > (int64_t)(1u << 31)))
+        return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -233,10 +238,12 @@ int moe_expert_ffn(const uint16_t* x, int T, const moe_qffn* routed, const moe_q
     uint16_t* hbuf = at<uint16_t>(ws, L.h);
     launch_plan(expert_offsets, T, tiles, tcount, st);
     if (path == MOE_PATH_DECODE)
-        launch_expert_decode(x, T, perm, tiles, tcount, max_tiles(T), *routed, *shared,
+        launch_expert_decode(x, T, perm, tiles, tcount, max_tiles(T), qffn_view(*routed),
+                             qffn_view(*shared),
                              at<uint16_t>(ws, L.xh), hbuf, expert_out, st);
     else
-        launch_expert_prefill(x, T, perm, tiles, tcount, max_tiles(T), *routed, *shared,
+        launch_expert_prefill(x, T, perm, tiles, tcount, max_tiles(T), qffn_view(*routed),
+                              qffn_view(*shared),
                               at<uint16_t>(ws, L.xh), hbuf,
                               expert_out, st);
     return launch_status();
@@ -298,10 +305,11 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
         uint16_t* xh = at<uint16_t>(ws, L.xh);
         launch_route_select(at<float>(ws, L.logits), x, layer->w_shared_gate, T, ids, wts, sg,
                             counts, offsets, perm, inv, tiles, tcount, xh, st);
-        launch_decode_gateup(xh, T, perm, tiles, tcount, max_tiles(T), layer->routed,
-                             layer->shared, hbuf, st);
-        launch_decode_down_combine(hbuf, T, perm, tiles, tcount, wts, sg, layer->routed,
-                                   layer->shared, y, x, res, st);
+        launch_decode_gateup(xh, T, perm, tiles, tcount, max_tiles(T), qffn_view(layer->routed),
+                             qffn_view(layer->shared), hbuf, st);
+        launch_decode_down_combine(hbuf, T, perm, tiles, tcount, wts, sg,
+                                   qffn_view(layer->routed), qffn_view(layer->shared), y, x, res,
+                                   st);
         return launch_status();
     }
     launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
@@ -312,8 +320,9 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
     launch_plan(offsets, T, tiles, tcount, st);
     // fp16 rows of weight * d (half the bytes of fp32 expert outputs)
     uint16_t* d16 = reinterpret_cast<uint16_t*>(dout);
-    launch_expert_prefill_fused(x, T, perm, tiles, tcount, max_tiles(T), layer->routed,
-                                layer->shared, at<uint16_t>(ws, L.xh), hbuf, d16, wsorted, sg, st);
+    launch_expert_prefill_fused(x, T, perm, tiles, tcount, max_tiles(T), qffn_view(layer->routed),
+                                qffn_view(layer->shared), at<uint16_t>(ws, L.xh), hbuf, d16,
+                                wsorted, sg, st);
     launch_combine_f16(d16, inv, T, y, x, res, st);
     return launch_status();
 }

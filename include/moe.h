@@ -86,10 +86,20 @@ typedef enum {
     MOE_PATH_PREFILL = 2     /* grouped GEMM on fp16 MFMA */
 } moe_path;
 
-/* One quantised SwiGLU expert stack (see the format above). */
+/* One quantised SwiGLU expert stack (see the format above).
+ *
+ * expert_stride: 0 = each of the nine arrays is dense, [n][rows][cols] as
+ * above.  Otherwise it is the byte distance between expert e and expert
+ * e + 1 in EVERY one of the nine arrays (a multiple of 256, at least
+ * 524288 = one expert's code matrix), so that all of one expert's codes,
+ * scales and biases can sit together in one block of memory; within an
+ * expert each array keeps the row-major shape above (the library's
+ * binding offers 2 MiB-aligned 2 MiB blocks per expert as an option).
+ * Blocks must not overlap (not checked). */
 typedef struct {
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
+    int64_t expert_stride;
 } moe_qffn;
 
 /* One MoE layer: router, shared-expert gate, routed stack (n = 256) and

@@ -107,6 +107,11 @@ def test_expert_ffn_validation(L):
     mis.up_s = MIS
     assert f(A, 16, C.byref(q), C.byref(mis), A, A, A, A, big, None, None) == ALIGN
     assert f(A, 16, C.byref(q), C.byref(q), A, A, A, A, big - 256, None, None) == WS
+    # expert_stride: 0 (dense) or a 256-byte multiple of at least one code matrix
+    for st in (-256, 256, (1 << 19) - 256, (1 << 19) + 16, 1 << 32):
+        bs = _qffn()
+        bs.expert_stride = st
+        assert f(A, 16, C.byref(bs), C.byref(q), A, A, A, A, big, None, None) == INVALID, st
     # forcing the decode path above its limit, or an unknown path
     opt = moe.moe_options(moe.MOE_PATH_DECODE, None)
     assert f(A, moe.MOE_DECODE_T_MAX + 1, C.byref(q), C.byref(q), A, A, A, A, 1 << 40, None,

@@ -136,3 +136,20 @@ def test_workspace_init_after_garbage(gpu):
         moe.moe_layer_forward(x, D, y, ws)
         torch.cuda.synchronize()
         assert torch.equal(y, want)
+
+
+@pytest.mark.parametrize("T,path", [(1, AUTO), (8, AUTO), (20, DEC), (100, AUTO), (16, PRE)])
+def test_dense_and_expert_layouts_agree(gpu, T, path):
+    """The same weights in the dense layout (expert_stride 0) and in the
+    expert-major 2 MiB blocks give bit-identical outputs on every path."""
+    P.say(f"layouts T={T} path={path}")
+    L = P.host_layer(0, 0)
+    dense = P.dev_layer(0, 0)
+    assert dense.routed.c.expert_stride == 0
+    blocked = moe.DeviceLayer(L, layout="expert")
+    assert blocked.routed.c.expert_stride == moe.EXPERT_BLOCK
+    assert blocked.routed.c.gate_q % moe.EXPERT_BLOCK == 0
+    x = synth.make_x(T, seed=9)
+    y0, _, _ = gpu_layer(x, dense, path)
+    y1, _, _ = gpu_layer(x, blocked, path)
+    assert np.array_equal(y0, y1)
