@@ -16,6 +16,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the grouped GEMM's work claim is one lane's atomic whose result is read
+    # an item later; the atomic optimizer would broadcast it at once, which
+    # waits for every load the software pipeline keeps in flight
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -48,6 +48,11 @@ __device__ __forceinline__ P expert_at(P p, int e, uint32_t stride) {
     return (P)((CP)p + (size_t)e * stride);
 }
 
+// The tile count's workspace slot also holds the grouped GEMMs' work
+// counters, one per XCD and GEMM (gate/up: words 8..15, down: 16..23),
+// zeroed by the tile planner before each use.
+constexpr int GEMM_CTR_GATEUP = 8, GEMM_CTR_DOWN = 16, TILE_COUNT_WORDS = 24;
+
 struct Tile {
     int group;     // 0..255 routed expert, 256 shared expert
     int row0;      // first row in the permuted row space (shared rows start at 8T)

@@ -82,15 +82,21 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
 }
 
 // Eight codes of one word -> fp16 weights w = q*s + b, in chunk-slot order
-// (k = 0,4,1,5,2,6,3,7).  (0x6400 | q) is the fp16 value 1024 + q, so one
-// packed subtraction recovers q exactly and one packed FMA applies the
-// group's scale and bias with a single rounding.
+// (k = 0,4,1,5,2,6,3,7).  OR-ing an exponent into a masked pair of nibbles
+// gives exact fp16 values: nibbles at bits 0..3 of each half under 0x6400
+// are 1024 + q, nibbles at bits 4..7 under 0x5400 are 64 + q (mantissa
+// 16q, exponent 2^6), so one shift of the word by 8 serves all eight
+// codes.  One packed subtraction recovers q exactly and one packed FMA
+// applies the group's scale and bias with a single rounding.
 __device__ __forceinline__ half8 dequant8(uint32_t w, half2v s2, half2v b2) {
+    const uint32_t w8 = w >> 8;
+    const uint32_t p[4] = {and_or(w, 0x000F000Fu, 0x64006400u), and_or(w, 0x00F000F0u, 0x54005400u),
+                           and_or(w8, 0x000F000Fu, 0x64006400u), and_or(w8, 0x00F000F0u, 0x54005400u)};
     half8 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t p = and_or(w >> (4 * i), 0x000F000Fu, 0x64006400u);
-        half2v h = __builtin_bit_cast(half2v, p) - (half2v){(_Float16)1024.f, (_Float16)1024.f};
+        const _Float16 off = (i & 1) ? (_Float16)64.f : (_Float16)1024.f;
+        half2v h = __builtin_bit_cast(half2v, p[i]) - (half2v){off, off};
         h = __builtin_elementwise_fma(h, s2, b2);
         r[2 * i] = h[0];
         r[2 * i + 1] = h[1];
@@ -182,7 +188,9 @@ constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
 constexpr int META = WAVES * 256;           // per-item row metadata (tokens or weights):
                                             // one 4-byte direct load (256 B) per wave
 constexpr int STG = 1024;                   // per-wave epilogue staging
-constexpr int LDS_BYTES = STAGES * STAGE + 2 * META + WAVES * STG;
+constexpr int CLAIM = WAVES * 256 + 16;     // the claimed item index (16 B) and the
+                                            // landing area of waves 1-3's stand-in load
+constexpr int LDS_BYTES = STAGES * STAGE + 2 * META + WAVES * STG + CLAIM;
 constexpr int A_LOADS = MT / 8 / WAVES;     // 1 KB (8 rows) per load instruction
 constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
 constexpr int LPC = A_LOADS + B_LOADS + 2;  // loads per wave per chunk
@@ -190,7 +198,7 @@ constexpr uint32_t OOB = 0x80000000u;       // beyond every buffer: no memory ac
 static_assert(MT % (8 * WAVES) == 0, "A rows must split evenly over the load instructions");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(META >= MT * 4, "row metadata must cover a tile");
-static_assert((STAGES - 2) * LPC + 1 <= 63, "vmcnt range");
+static_assert((STAGES - 2) * LPC + 2 <= 63, "vmcnt range");
 }  // namespace pg
 
 typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
@@ -202,17 +210,36 @@ struct GItem {
     int row0, nrows, nb;
 };
 
+// Item j of XCD x: column block j % NB of tile x + 8 (j / NB).  nx: the
+// XCD's item count.  j is wave-uniform, so the tile is read with scalar
+// loads (which the pipeline's vector-memory wait counts do not see).
 template <int NB>
-__device__ __forceinline__ GItem gemm_item(int it, int n_items, const Tile* __restrict__ tiles) {
+__device__ __forceinline__ GItem gemm_item(int j, int nx, int xcd, const Tile* __restrict__ tiles) {
     GItem m;
-    m.valid = it < n_items;
-    const Tile tl = tiles[m.valid ? it / NB : 0];
+    m.valid = j < nx;
+    const Tile tl = tiles[m.valid ? xcd + 8 * (j / NB) : 0];
     m.shared = tl.group >= E;
     m.e = (m.shared || !m.valid) ? 0 : tl.group;
     m.row0 = tl.row0;
     m.nrows = m.valid ? tl.nrows : 0;
-    m.nb = m.valid ? it % NB : 0;
+    m.nb = m.valid ? j % NB : 0;
     return m;
+}
+
+// Claiming work: wave 0 takes the next index from the XCD's counter; the
+// other waves issue a stand-in load that touches no memory, so that every
+// wave has issued the same number of vector-memory operations.
+__device__ __forceinline__ uint32_t claim_item(int* ctr, uint8_t* claim) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    uint32_t t = 0;
+    if (wave == 0) {
+        if (lane == 0) t = (uint32_t)atomicAdd(ctr, 1);
+    } else {
+        const __amdgpu_buffer_rsrc_t r = buf_rsrc(ctr, 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(claim + 16 + wave * 256), 4,
+                                                 pg::OOB, 0, 0, 0);
+    }
+    return t;
 }
 
 // Where one item's chunks come from, per lane: the A rows this lane moves
@@ -547,6 +574,14 @@ __device__ __forceinline__ void issue_meta(const GemmArgs& A, const GItem& m, ui
     }
 }
 
+// Dynamic schedule of one workgroup: its XCD's counter and item count, the
+// first claimable index (the first two items per workgroup are static).
+struct Sched {
+    int* ctr;
+    int nx, xcd, jbase;
+    const Tile* tiles;
+};
+
 // One item: NCH chunks of MFMAs, then the epilogue.  Each chunk is
 // software-pipelined around the workgroup barrier: K-steps 0..2 run before
 // it (each step's MFMAs hide the next step's operand reads and
@@ -555,20 +590,23 @@ __device__ __forceinline__ void issue_meta(const GemmArgs& A, const GItem& m, ui
 // chunk's operands are read and its step 0 dequantised.  Only the first
 // chunk of an item dequantises with no MFMAs to hide under.
 template <int KDIM, int MODE, int NMT>
-__device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cur, const GItem& nxt,
+__device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cur, GItem& nxt,
                                               const GSrc& src_cur, GSrc& src_nxt, int& gc, int k,
                                               bool first, __amdgpu_buffer_rsrc_t ra,
-                                              const WPtr& pr, const WPtr& ps, uint8_t* lds) {
+                                              const WPtr& pr, const WPtr& ps, uint8_t* lds,
+                                              const Sched& sc, uint32_t& tick) {
     constexpr bool GATEUP = MODE == GM_GATEUP;
+    constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     constexpr int NCH = KDIM / pg::KC;
     constexpr int S_EPI = epi_stores<MODE>();
     constexpr int BASE = (pg::STAGES - 2) * pg::LPC;     // loads of the 3 chunks behind the awaited one
     // (a count larger than the operations really issued after the awaited
     // chunk would not wait for it; a smaller one only waits longer)
     constexpr int W_S = BASE + S_EPI < 63 ? BASE + S_EPI : 63;
-    constexpr int W_XS = BASE + 1 + S_EPI < 63 ? BASE + 1 + S_EPI : 63;
+    constexpr int W_XS = BASE + 2 + S_EPI < 63 ? BASE + 2 + S_EPI : 63;
     uint8_t* meta = lds + pg::STAGES * pg::STAGE;
     uint8_t* stg = meta + 2 * pg::META + wave_id() * pg::STG;
+    uint8_t* claim = meta + 2 * pg::META + pg::WAVES * pg::STG;
     float16v acc[NMT][2];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
@@ -599,12 +637,12 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 
         // chunk c+1 must have landed (issued 4 refills ago).  Issued after it
         // and allowed to stay in flight: the loads of the next three chunks
-        // (BASE), this item's metadata load (issued after the wait of c = 0,
-        // counted for c = 1..4) and, for c <= 3, the previous item's epilogue
-        // stores.
+        // (BASE), this item's metadata load and work claim (issued after the
+        // wait of c = 0, counted for c = 1..4) and, for c <= 3, the previous
+        // item's epilogue stores.
         if (!first && c == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(W_S));
         else if (!first && c <= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(W_XS));
-        else if (c >= 1 && c <= 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE + 1));
+        else if (c >= 1 && c <= 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE + 2));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE));
         pipe_barrier();
 
@@ -655,7 +693,14 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     chunk(0, [&](uint8_t* st) {
         issue_chunk(src_cur, pg::STAGES, ra, st);
         __builtin_amdgcn_sched_barrier(0);      // the metadata load goes after the chunk's loads
+        // the item after this one, claimed during the previous item (its
+        // index was written to LDS before this chunk's barrier)
+        if (!first)
+            nxt = gemm_item<NB>(sc.jbase + __builtin_amdgcn_readfirstlane(*(const int*)claim),
+                                sc.nx, sc.xcd, sc.tiles);
         issue_meta<MODE>(A, GATEUP ? nxt : cur, meta + ((GATEUP ? k + 1 : k) & 1) * pg::META);
+        tick = claim_item(sc.ctr, claim);       // the one after that
+        __builtin_amdgcn_sched_barrier(0);
     });
 #pragma unroll
     for (int c = 1; c < HEAD; ++c) {
@@ -676,24 +721,31 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Work split: workgroups are dealt to the 8 XCDs in turn, so XCD x =
+// blockIdx.x mod 8 takes tiles x, x+8, ... (the planner sorts tiles by
+// cost, so every XCD gets a similar share); a tile's column blocks then run
+// on one XCD and share its L2 for the tile's rows.  Within an XCD the first
+// two items of each workgroup are static and the rest are claimed from the
+// XCD's counter in order -- longest first.
 template <int KDIM, int MODE>
 __global__ __launch_bounds__(pg::THREADS, 1) void grouped_gemm(GemmArgs args,
                                                               const Tile* __restrict__ tiles,
-                                                              const int* __restrict__ tile_count,
+                                                              int* __restrict__ tile_count,
                                                               QFFN routed, QFFN shared) {
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     __shared__ __attribute__((aligned(16))) uint8_t lds[pg::LDS_BYTES];
-    const int n_items = *tile_count * NB;
-    const int G8 = gridDim.x >> 3;
-    int it = (blockIdx.x & 7) * G8 + (blockIdx.x >> 3);
-    if (it >= n_items) return;
-    const int stride = gridDim.x;
+    const int xcd = blockIdx.x & 7, wl = blockIdx.x >> 3, nwl = gridDim.x >> 3;
+    const int ntiles = tile_count[0];
+    const int nx = max(ntiles - xcd + 7, 0) / 8 * NB;
+    if (wl >= nx) return;
+    const Sched sc{tile_count + (GATEUP ? GEMM_CTR_GATEUP : GEMM_CTR_DOWN) + xcd, nx, xcd, 2 * nwl,
+                   tiles};
     uint8_t* meta = lds + pg::STAGES * pg::STAGE;
     const __amdgpu_buffer_rsrc_t ra = buf_rsrc(args.ain, args.ain_bytes);
 
-    GItem cur = gemm_item<NB>(it, n_items, tiles);
-    GItem nxt = gemm_item<NB>(it + stride, n_items, tiles);
+    GItem cur = gemm_item<NB>(wl, nx, xcd, tiles);
+    GItem nxt = gemm_item<NB>(wl + nwl, nx, xcd, tiles);
     if (GATEUP) {
         // the first item's permutation entries, before any of its rows can move
         issue_meta<MODE>(args, cur, meta);
@@ -708,21 +760,25 @@ __global__ __launch_bounds__(pg::THREADS, 1) void grouped_gemm(GemmArgs args,
     pipe_barrier();
 
     int gc = 0;
+    uint32_t tick = 0;
     for (int k = 0;; ++k) {
         switch ((cur.nrows + 31) >> 5) {
-#define PG_CASE(n) \
-    case n: gemm_run_item<KDIM, MODE, n>(args, cur, nxt, src_cur, src_nxt, gc, k, k == 0, ra, pr, ps, lds); break;
+#define PG_CASE(n)                                                                           \
+    case n:                                                                                  \
+        gemm_run_item<KDIM, MODE, n>(args, cur, nxt, src_cur, src_nxt, gc, k, k == 0, ra, pr, \
+                                     ps, lds, sc, tick);                                     \
+        break;
             PG_CASE(1) PG_CASE(2) PG_CASE(3) PG_CASE(4)
             default: gemm_run_item<KDIM, MODE, pg::NMT_MAX>(args, cur, nxt, src_cur, src_nxt, gc, k,
-                                                            k == 0, ra, pr, ps, lds);
+                                                            k == 0, ra, pr, ps, lds, sc, tick);
                      break;
 #undef PG_CASE
         }
-        it += stride;
         if (!nxt.valid) break;
         cur = nxt;
         src_cur = src_nxt;
-        nxt = gemm_item<NB>(it + stride, n_items, tiles);
+        // the claimed index, for the next item's first chunk (after its barrier)
+        if (threadIdx.x == 0) *reinterpret_cast<int*>(meta + 2 * pg::META + pg::WAVES * pg::STG) = (int)tick;
     }
 }
 
@@ -767,7 +823,7 @@ static GemmArgs gemm_args(const uint16_t* ain, size_t ain_bytes, int T, const in
 constexpr unsigned GEMM_GRID = 256;   // one workgroup per compute unit (a multiple of 8 XCDs)
 
 static void launch_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                          const int* tile_count, const QFFN& routed, const QFFN& shared,
+                          int* tile_count, const QFFN& routed, const QFFN& shared,
                           uint16_t* xh, uint16_t* hbuf, hipStream_t st) {
     const size_t chunks = (size_t)T * (H / 8);
     hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
@@ -779,7 +835,7 @@ static void launch_gateup(const uint16_t* x, int T, const int32_t* perm, const T
 }
 
 void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                           const int* tile_count, int /*max_tiles*/, const QFFN& routed,
+                           int* tile_count, int /*max_tiles*/, const QFFN& routed,
                            const QFFN& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                            hipStream_t st) {
     launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, st);
@@ -792,7 +848,7 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
 // Whole-layer prefill expert part: gate/up, then down writing fp16 rows of
 // (routing weight or shared gate) * d, summed per token by combine_f16.
 void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                                 const int* tile_count, int /*max_tiles*/, const QFFN& routed,
+                                 int* tile_count, int /*max_tiles*/, const QFFN& routed,
                                  const QFFN& shared, uint16_t* xh, uint16_t* hbuf,
                                  uint16_t* d16, const float* wsorted, const float* sg,
                                  hipStream_t st) {

@@ -44,11 +44,11 @@ void launch_expert_decode(const uint16_t* x, int T, const int32_t* perm, const T
                           const QFFN& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                           hipStream_t st);
 void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                           const int* tile_count, int max_tiles, const QFFN& routed,
+                           int* tile_count, int max_tiles, const QFFN& routed,
                            const QFFN& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                            hipStream_t st);
 void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
-                                 const int* tile_count, int max_tiles, const QFFN& routed,
+                                 int* tile_count, int max_tiles, const QFFN& routed,
                                  const QFFN& shared, uint16_t* xh, uint16_t* hbuf,
                                  uint16_t* d16, const float* wsorted, const float* sg,
                                  hipStream_t st);
@@ -91,7 +91,7 @@ WsLayout ws_layout(int T) {
     L.wsorted = take(t * TOPK * 4);
     L.chunk_counts = take((size_t)perm_chunks(T) * E * 4);
     L.tiles = take((size_t)max_tiles(T) * sizeof(Tile));
-    L.tile_count = take(4);
+    L.tile_count = take(TILE_COUNT_WORDS * 4);
     L.xh = take(t * H * 2);
     // h rows: 9T for the tile-based kernels; the few-token layer indexes them
     // (slot * T + token) with up to 1 + 8T slots

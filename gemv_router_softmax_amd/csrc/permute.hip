@@ -123,6 +123,10 @@ __device__ inline Tile balanced_tile(int group, int r0, int n, int nt, int i) {
     return tl;
 }
 
+// Tiles are written in descending order of their count of 32-row MFMA
+// tiles (their cost in the grouped GEMMs, whose dynamic schedule then runs
+// longest-first); within a class, routed experts in order, then the shared
+// expert.  Also zeroes the GEMMs' work counters.
 __global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ offsets, int T,
                                                   int cap, Tile* __restrict__ tiles,
                                                   int* __restrict__ tile_count) {
@@ -134,14 +138,33 @@ __global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ of
     const int r1 = min(max(offsets[tid + 1], r0), lim);
     const int n = r1 - r0;
     const int nt = (n + MT_ROWS - 1) / MT_ROWS;
-    int total;
-    const int tb = block_excl_scan256(nt, scr, &total);
-    for (int i = 0; i < nt; ++i)
-        if (tb + i < cap) tiles[tb + i] = balanced_tile(tid, r0, n, nt, i);
     const int ns = (T + MT_ROWS - 1) / MT_ROWS;
-    for (int i = tid; i < ns; i += 256)
-        if (total + i < cap) tiles[total + i] = balanced_tile(E, TOPK * T, T, ns, i);
-    if (tid == 0) *tile_count = min(total + ns, cap);
+    auto cls = [](const Tile& t) { return (t.nrows + 31) >> 5; };
+    int before = 0;
+    for (int c = MT_ROWS / 32; c >= 1; --c) {
+        int mine = 0;
+        for (int i = 0; i < nt; ++i) mine += cls(balanced_tile(tid, r0, n, nt, i)) == c;
+        for (int i = tid; i < ns; i += 256) mine += cls(balanced_tile(E, lim, T, ns, i)) == c;
+        int tot;
+        int pos = before + block_excl_scan256(mine, scr, &tot);
+        for (int i = 0; i < nt; ++i) {
+            const Tile tl = balanced_tile(tid, r0, n, nt, i);
+            if (cls(tl) == c) {
+                if (pos < cap) tiles[pos] = tl;
+                ++pos;
+            }
+        }
+        for (int i = tid; i < ns; i += 256) {
+            const Tile tl = balanced_tile(E, lim, T, ns, i);
+            if (cls(tl) == c) {
+                if (pos < cap) tiles[pos] = tl;
+                ++pos;
+            }
+        }
+        before += tot;
+    }
+    if (tid == 0) *tile_count = min(before, cap);
+    if (tid >= GEMM_CTR_GATEUP && tid < TILE_COUNT_WORDS) tile_count[tid] = 0;
 }
 
 int perm_chunks(int T) { return (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK; }
