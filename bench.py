@@ -217,6 +217,10 @@ def buf_gbs(nbytes, ms):
 
 
 def prefill(D, T, iters):
+    """One layer at T tokens, rotating over the layers so the weights are not
+    cache resident.  Each timed call is captured once in its own HIP graph
+    and replayed with HIP events around each replay, so the host's launch
+    rate never shows in the GPU time."""
     import torch
     import gemv_router_softmax_amd as moe
     from gemv_router_softmax_amd import synth
@@ -224,17 +228,6 @@ def prefill(D, T, iters):
     x = moe.to_device_bits(synth.make_x(T, seed=0))
     y = torch.empty((T, H), dtype=torch.int16, device="cuda")
     ws = moe.workspace(T)
-    for i in range(3):
-        moe.moe_layer_forward(x, D[i % len(D)], y, ws)
-    torch.cuda.synchronize()
-    pairs = event_pairs(iters)
-    for i, (a, b) in enumerate(pairs):
-        a.record()
-        moe.moe_layer_forward(x, D[(i + 3) % len(D)], y, ws)
-        b.record()
-    torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in pairs])
-    # the expert FFN (grouped GEMM) alone, on the same routing
     ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
     w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
     sg = torch.empty((T,), dtype=torch.float32, device="cuda")
@@ -243,19 +236,48 @@ def prefill(D, T, iters):
     perm = torch.empty(8 * T, dtype=torch.int32, device="cuda")
     inv = torch.empty(8 * T, dtype=torch.int32, device="cuda")
     out = torch.empty((9 * T, H), dtype=torch.float32, device="cuda")
-    fp = event_pairs(iters)
-    for i, (a, b) in enumerate(fp):
+    nl = min(iters, len(D))
+
+    def capture(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def timed(graphs):
+        for g in graphs:          # warm-up
+            g.replay()
+        torch.cuda.synchronize()
+        pairs = event_pairs(iters)
+        for i, (a, b) in enumerate(pairs):
+            a.record()
+            graphs[i % len(graphs)].replay()
+            b.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in pairs])
+
+    layer_graphs = [capture(lambda Dl=D[(i + 3) % len(D)]: moe.moe_layer_forward(x, Dl, y, ws))
+                    for i in range(nl)]
+    ms = timed(layer_graphs)
+    del layer_graphs
+    # the expert FFN (grouped GEMM) alone, on routing computed beforehand
+    ffn_graphs = []
+    for i in range(nl):
         Dl = D[(i + 7) % len(D)]
         moe.moe_route(x, Dl.w_router, Dl.router_bias, Dl.w_shared_gate, ids, w, sg, ws)
         moe.moe_permute(ids, counts, offs, perm, inv, ws)
-        a.record()
-        moe.moe_expert_ffn(x, Dl, offs, perm, out, ws, path=moe.MOE_PATH_PREFILL)
-        b.record()
-    torch.cuda.synchronize()
-    fms = np.array([a.elapsed_time(b) for a, b in fp])
+        ffn_graphs.append(capture(lambda Dl=Dl: moe.moe_expert_ffn(
+            x, Dl, offs, perm, out, ws, path=moe.MOE_PATH_PREFILL)))
+    # the routing of the last captured layer is what every FFN replay reads
+    fms = timed(ffn_graphs)
+    del ffn_graphs
     flops = EXPERT_FLOP_PER_TOKEN * 9 * T
     return {
         "T": T,
+        "timing": "HIP events around graph replays, one layer per replay",
         "layer_ms": float(ms.mean()),
         "tokens_per_s": T / (ms.mean() * 1e-3),
         "layer_mfma_util": flops / (ms.mean() * 1e-3) / (BF16_DENSE_PEAK_TFLOPS * 1e12),

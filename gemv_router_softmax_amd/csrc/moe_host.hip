@@ -35,7 +35,8 @@ size_t route_rec_bytes();
 void launch_zero_words(unsigned* p, int n, hipStream_t st);
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st,
-                    const float* wts = nullptr, float* wsorted = nullptr);
+                    const float* wts = nullptr, float* wsorted = nullptr, Tile* tiles = nullptr,
+                    int* tile_count = nullptr);
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st);
 int perm_chunks(int T);
 int max_tiles(int T);
@@ -316,8 +317,7 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
                  at<float>(ws, L.logits), ids, wts, sg, st);
     float* wsorted = at<float>(ws, L.wsorted);
     launch_permute(ids, T, counts, offsets, perm, inv, at<int32_t>(ws, L.chunk_counts), st, wts,
-                   wsorted);
-    launch_plan(offsets, T, tiles, tcount, st);
+                   wsorted, tiles, tcount);
     // fp16 rows of weight * d (half the bytes of fp32 expert outputs)
     uint16_t* d16 = reinterpret_cast<uint16_t*>(dout);
     launch_expert_prefill_fused(x, T, perm, tiles, tcount, max_tiles(T), qffn_view(layer->routed),

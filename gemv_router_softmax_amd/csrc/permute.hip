@@ -14,98 +14,16 @@
 //   plan_tiles      row tiles of <= MT_ROWS rows per expert (expert 256 is the
 //                   shared expert over all T tokens), read by the expert
 //                   kernels from device memory so the host never needs the
-//                   expert counts.
+//                   expert counts.  The layer call plans inside perm_small /
+//                   perm_scan (one launch fewer); the split interface plans
+//                   from the caller's offsets with the plan_tiles kernel.
 #include "block_util.hpp"
 
 namespace moe {
 
-constexpr int PERM_CHUNK = 4096;   // entries per chunk in the large path
-constexpr int SMALL_MAX = 4096;    // entries handled by perm_small
-
-__global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ ids, int n,
-                                                  int32_t* __restrict__ counts,
-                                                  int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ perm,
-                                                  int32_t* __restrict__ inv,
-                                                  const float* __restrict__ wsrc,
-                                                  float* __restrict__ wsorted) {
-    __shared__ int hist[256];
-    __shared__ int base[256];
-    __shared__ int wcnt[4 * 256];
-    __shared__ int scr[4];
-    const int tid = threadIdx.x;
-    hist[tid] = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
-    __syncthreads();
-    for (int f = tid; f < n; f += 256) {
-        int e = ids[f];
-        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-    }
-    __syncthreads();
-    const int c = hist[tid];
-    int total;
-    const int off = block_excl_scan256(c, scr, &total);
-    counts[tid] = c;
-    offsets[tid] = off;
-    if (tid == 0) offsets[E] = total;
-    base[tid] = off;
-    __syncthreads();
-    stable_scatter(ids, 0, n, base, wcnt, perm, inv, wsrc, wsorted);
-}
-
-__global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int n,
-                                                  int32_t* __restrict__ chunk_counts) {
-    __shared__ int hist[256];
-    const int tid = threadIdx.x;
-    hist[tid] = 0;
-    __syncthreads();
-    const int f0 = blockIdx.x * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
-    for (int f = f0 + tid; f < f1; f += 256) {
-        int e = ids[f];
-        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-    }
-    __syncthreads();
-    chunk_counts[(size_t)blockIdx.x * 256 + tid] = hist[tid];
-}
-
-// One workgroup: chunk_counts[b][e] becomes the absolute first position of
-// chunk b's entries of expert e.
-__global__ __launch_bounds__(256) void perm_scan(int nchunks, int32_t* __restrict__ chunk_counts,
-                                                 int32_t* __restrict__ counts,
-                                                 int32_t* __restrict__ offsets) {
-    __shared__ int scr[4];
-    const int tid = threadIdx.x;
-    int run = 0;
-    for (int b = 0; b < nchunks; ++b) {
-        int c = chunk_counts[(size_t)b * 256 + tid];
-        chunk_counts[(size_t)b * 256 + tid] = run;
-        run += c;
-    }
-    int total;
-    const int off = block_excl_scan256(run, scr, &total);
-    counts[tid] = run;
-    offsets[tid] = off;
-    if (tid == 0) offsets[E] = total;
-    for (int b = 0; b < nchunks; ++b) chunk_counts[(size_t)b * 256 + tid] += off;
-}
-
-__global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ ids, int n,
-                                                    const int32_t* __restrict__ chunk_base,
-                                                    int32_t* __restrict__ perm,
-                                                    int32_t* __restrict__ inv,
-                                                    const float* __restrict__ wsrc,
-                                                    float* __restrict__ wsorted) {
-    __shared__ int base[256];
-    __shared__ int wcnt[4 * 256];
-    const int tid = threadIdx.x;
-    base[tid] = chunk_base[(size_t)blockIdx.x * 256 + tid];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
-    __syncthreads();
-    const int f0 = blockIdx.x * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
-    stable_scatter(ids, f0, f1, base, wcnt, perm, inv, wsrc, wsorted);
-}
+constexpr int PERM_CHUNK = 512;    // entries per chunk in the large path (two rounds
+                                   // of the block scatter per workgroup)
+constexpr int SMALL_MAX = 1024;    // entries handled by perm_small
 
 // Row tiles: routed expert e owns rows offsets[e] .. offsets[e+1]-1, the
 // shared expert (group 256) owns rows 8T .. 9T-1.  A group of n rows is cut
@@ -126,16 +44,15 @@ __device__ inline Tile balanced_tile(int group, int r0, int n, int nt, int i) {
 // Tiles are written in descending order of their count of 32-row MFMA
 // tiles (their cost in the grouped GEMMs, whose dynamic schedule then runs
 // longest-first); within a class, routed experts in order, then the shared
-// expert.  Also zeroes the GEMMs' work counters.
-__global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ offsets, int T,
-                                                  int cap, Tile* __restrict__ tiles,
-                                                  int* __restrict__ tile_count) {
-    __shared__ int scr[4];
+// expert.  Also zeroes the GEMMs' work counters.  Thread e of the 256-thread
+// block passes expert e's rows [o0, o1) (caller-provided offsets are clamped
+// into the routed row space [0, 8T)); scr: 4 ints of LDS.
+__device__ void plan_block(int o0, int o1, int T, int cap, Tile* __restrict__ tiles,
+                           int* __restrict__ tile_count, int* scr) {
     const int tid = threadIdx.x;
-    // clamp caller-provided offsets into the routed row space [0, 8T)
     const int lim = TOPK * T;
-    const int r0 = min(max(offsets[tid], 0), lim);
-    const int r1 = min(max(offsets[tid + 1], r0), lim);
+    const int r0 = min(max(o0, 0), lim);
+    const int r1 = min(max(o1, r0), lim);
     const int n = r1 - r0;
     const int nt = (n + MT_ROWS - 1) / MT_ROWS;
     const int ns = (T + MT_ROWS - 1) / MT_ROWS;
@@ -167,29 +84,139 @@ __global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ of
     if (tid >= GEMM_CTR_GATEUP && tid < TILE_COUNT_WORDS) tile_count[tid] = 0;
 }
 
-int perm_chunks(int T) { return (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK; }
+__global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ offsets, int T,
+                                                  int cap, Tile* __restrict__ tiles,
+                                                  int* __restrict__ tile_count) {
+    __shared__ int scr[4];
+    plan_block(offsets[threadIdx.x], offsets[threadIdx.x + 1], T, cap, tiles, tile_count, scr);
+}
 
-int max_tiles(int T) {
+__host__ __device__ int max_tiles(int T) {
     const int n = TOPK * T;
     return n / MT_ROWS + (n < E ? n : E) + (T + MT_ROWS - 1) / MT_ROWS;
 }
 
+__global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ ids, int n,
+                                                  int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm,
+                                                  int32_t* __restrict__ inv,
+                                                  const float* __restrict__ wsrc,
+                                                  float* __restrict__ wsorted, int T,
+                                                  Tile* __restrict__ tiles,
+                                                  int* __restrict__ tile_count) {
+    __shared__ int hist[256];
+    __shared__ int base[256];
+    __shared__ int wcnt[4 * 256];
+    __shared__ int scr[4];
+    const int tid = threadIdx.x;
+    hist[tid] = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
+    __syncthreads();
+    for (int f = tid; f < n; f += 256) {
+        int e = ids[f];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    const int c = hist[tid];
+    int total;
+    const int off = block_excl_scan256(c, scr, &total);
+    counts[tid] = c;
+    offsets[tid] = off;
+    if (tid == 0) offsets[E] = total;
+    base[tid] = off;
+    __syncthreads();
+    stable_scatter(ids, 0, n, base, wcnt, perm, inv, wsrc, wsorted);
+    if (tiles) plan_block(off, off + c, T, max_tiles(T), tiles, tile_count, scr);
+}
+
+__global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int n,
+                                                  int32_t* __restrict__ chunk_counts) {
+    __shared__ int hist[256];
+    const int tid = threadIdx.x;
+    hist[tid] = 0;
+    __syncthreads();
+    const int f0 = blockIdx.x * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
+    for (int f = f0 + tid; f < f1; f += 256) {
+        int e = ids[f];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    chunk_counts[(size_t)blockIdx.x * 256 + tid] = hist[tid];
+}
+
+// One workgroup: chunk_counts[b][e] becomes the first position of chunk
+// b's entries of expert e relative to the expert's segment (the scatter adds
+// offsets[e]); counts and offsets are written, and the row tiles planned if
+// `tiles` is given.  Thread e reads its column 16 chunks at a time, so the
+// loads of a batch are in flight together.
+__global__ __launch_bounds__(256) void perm_scan(int nchunks, int32_t* __restrict__ chunk_counts,
+                                                 int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets, int T,
+                                                 Tile* __restrict__ tiles,
+                                                 int* __restrict__ tile_count) {
+    __shared__ int scr[4];
+    const int tid = threadIdx.x;
+    int run = 0;
+    for (int b0 = 0; b0 < nchunks; b0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            c[i] = b0 + i < nchunks ? chunk_counts[(size_t)(b0 + i) * 256 + tid] : 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (b0 + i < nchunks) chunk_counts[(size_t)(b0 + i) * 256 + tid] = run;
+            run += c[i];
+        }
+    }
+    int total;
+    const int off = block_excl_scan256(run, scr, &total);
+    counts[tid] = run;
+    offsets[tid] = off;
+    if (tid == 0) offsets[E] = total;
+    if (tiles) plan_block(off, off + run, T, max_tiles(T), tiles, tile_count, scr);
+}
+
+__global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ ids, int n,
+                                                    const int32_t* __restrict__ chunk_base,
+                                                    const int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm,
+                                                    int32_t* __restrict__ inv,
+                                                    const float* __restrict__ wsrc,
+                                                    float* __restrict__ wsorted) {
+    __shared__ int base[256];
+    __shared__ int wcnt[4 * 256];
+    const int tid = threadIdx.x;
+    base[tid] = chunk_base[(size_t)blockIdx.x * 256 + tid] + offsets[tid];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
+    __syncthreads();
+    const int f0 = blockIdx.x * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
+    stable_scatter(ids, f0, f1, base, wcnt, perm, inv, wsrc, wsorted);
+}
+
+int perm_chunks(int T) { return (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK; }
+
 // wts/wsorted: optional (both or neither): wsorted[p] = wts[perm[p]], the
 // routing weight of each sorted position.
+// tiles/tile_count: optional (both or neither): also plan the row tiles
+// (and zero the GEMMs' work counters), as launch_plan would.
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st, const float* wts,
-                    float* wsorted) {
+                    float* wsorted, Tile* tiles, int* tile_count) {
     const int n = TOPK * T;
     if (n <= SMALL_MAX) {
         hipLaunchKernelGGL(perm_small, dim3(1), dim3(256), 0, st, ids, n, counts, offsets, perm,
-                           inv, wts, wsorted);
+                           inv, wts, wsorted, T, tiles, tile_count);
         return;
     }
     const int nb = perm_chunks(T);
     hipLaunchKernelGGL(perm_count, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts);
-    hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, st, nb, chunk_counts, counts, offsets);
-    hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts, perm, inv,
-                       wts, wsorted);
+    hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, st, nb, chunk_counts, counts, offsets, T,
+                       tiles, tile_count);
+    hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts, offsets,
+                       perm, inv, wts, wsorted);
 }
 
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st) {

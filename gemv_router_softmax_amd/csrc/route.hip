@@ -8,15 +8,14 @@
 //   route_logits_gemv   T <= 32: one wave per expert row of W_r, every lane
 //                       streams 64 B of the row (coalesced 16 B loads) and
 //                       dots it with the (cached) token rows.
-//   route_fused         larger T: one workgroup per 32 tokens computes all
-//                       256 logits with bf16 MFMA 32x32x16 (fp32 accumulation
-//                       of exact bf16 products), keeps them in LDS and runs
-//                       the top-8 selection and the shared gate there.
-//   route_logits_mfma   logits only (kept for the split interface path).
-//   route_topk          one wave per token: 4 logits per lane, radix selection
-//                       of the 8th largest fp32 logit with wave ballots (ties ->
-//                       lower expert index), softmax weights renormalised over
-//                       the selected eight, and the shared-expert gate
+//   route_logits_tile   larger T: the logits as a small GEMM, one workgroup
+//                       per 32 tokens x 128 experts, bf16 MFMA 32x32x16 (fp32
+//                       accumulation of exact bf16 products) on tiles moved
+//                       into LDS by a 7-stage direct-load ring.
+//   route_topk          one wave per token: 4 logits per lane, eight arg-max
+//                       rounds over the fp32 logits (ties -> lower expert
+//                       index), softmax weights renormalised over the
+//                       selected eight, and the shared-expert gate
 //                       sigmoid(x . w_sg).
 #include "block_util.hpp"
 
@@ -53,169 +52,124 @@ __global__ __launch_bounds__(256) void route_logits_gemv(const uint16_t* __restr
     }
 }
 
-// grid: (ceil(T/64), E/64); 4 waves, wave w -> experts blockIdx.y*64 + 16w .. +16.
-__global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t* __restrict__ x, int T,
-                                                         const uint16_t* __restrict__ wr,
-                                                         const float* __restrict__ bias,
-                                                         float* __restrict__ logits) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, j = lane >> 4;
-    const int t0 = blockIdx.x * 64;
-    const int e0 = blockIdx.y * 64 + wave * 16;
-    const uint4v* wrow = reinterpret_cast<const uint4v*>(wr + (size_t)(e0 + r) * H) + j;
-    const uint4v* xrow[4];
-    bool tok_ok[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        int t = t0 + mt * 16 + r;
-        tok_ok[mt] = t < T;
-        xrow[mt] = reinterpret_cast<const uint4v*>(x + (size_t)(tok_ok[mt] ? t : 0) * H) + j;
-    }
-    float4v acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = (float4v){0.f, 0.f, 0.f, 0.f};
-    for (int step = 0; step < H / 32; ++step) {
-        uint4v b = wrow[step * 4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            uint4v a = tok_ok[mt] ? xrow[mt][step * 4] : (uint4v){0u, 0u, 0u, 0u};
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                              __builtin_bit_cast(bf16x8, b),
-                                                              acc[mt], 0, 0, 0);
-        }
-    }
-    const int e = e0 + r;
-    const float bb = bias ? bias[e] : 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int t = t0 + mt * 16 + 4 * j + i;
-            if (t < T) logits[(size_t)t * E + e] = acc[mt][i] + bb;
-        }
-    }
-}
-
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rt_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
-// Router for T > 32.  grid: ceil(T/32) workgroups of 8 waves.
-//   Logits: wave w owns experts 32w .. 32w+31 for the block's 32 tokens, a
-//   32x32 fp32 accumulator of v_mfma_f32_32x32x16_bf16 (lane l: token /
-//   expert l%32, k = 8*(l/32)..+7 of each 16-wide step).  K advances in
-//   supersteps of 64: the x tile (32 rows) and the W_r tile (256 rows) of
-//   the superstep move into LDS with coalesced direct loads (1 KB = 8 rows x
-//   128 B per instruction) through a 3-stage ring; rows are stored with
-//   their 16-byte pieces XOR-swizzled by (row >> 1) & 7 so a 16-lane operand
-//   read hits 16 distinct bank groups.  MFMA step s reads piece 4g + s
-//   (g = l/32) of both operands.  Rows past T load zeros (buffer range).
-//   Then the 32 x 256 logits (+ bias) go to LDS and each wave selects the top
-//   8 of four tokens (wave_top8) and computes their shared gate.
-constexpr int RF_TOK = 32;
-constexpr int RF_LDS_STRIDE = E + 4;               // floats per token row of logits (16 B aligned)
-constexpr int RF_STAGES = 3;
-constexpr int RF_XB = RF_TOK * 128;                // x tile bytes per superstep
-constexpr int RF_STAGE = RF_XB + E * 128;          // + W_r tile
-constexpr int RF_INSTR = RF_STAGE / 1024;          // 1 KB direct loads per superstep (36)
-static_assert(RF_STAGE % 1024 == 0, "router stage in whole load instructions");
-static_assert(RF_STAGES * RF_STAGE + RF_TOK * RF_LDS_STRIDE * 4 <= 160 * 1024, "router LDS");
+// Router logits for T > 32.  grid: (ceil(T/32), 2) workgroups of 4 waves;
+// workgroup (b, h) computes tokens 32b .. 32b+31 against experts
+// 128h .. 128h+127, wave w the 32 experts 128h + 32w .. +31, as a 32x32 fp32
+// accumulator of v_mfma_f32_32x32x16_bf16 (lane l: token / expert l%32,
+// k = 8*(l/32)..+7 of each 16-wide step).  K advances in supersteps of 64;
+// the x tile (32 rows) and the W_r tile (128 rows) of a superstep move into
+// LDS with coalesced direct loads (1 KB = 8 rows x 128 B per instruction,
+// five per wave) through a 7-stage ring, so six supersteps are in flight
+// while one is multiplied -- the kernel is bound by load latency, not by
+// the MFMAs.  Rows are stored with their 16-byte pieces XOR-swizzled by
+// (row >> 1) & 7, so a 16-lane operand read hits 16 distinct bank groups;
+// MFMA step s reads piece 4g + s (g = l/32) of both operands.  Token rows
+// past T load zeros (buffer range) and are not stored.
+constexpr int RL_TOK = 32;
+constexpr int RL_EXP = 128;
+constexpr int RL_STAGES = 7;
+constexpr int RL_STAGE = (RL_TOK + RL_EXP) * 128;     // bytes per superstep
+constexpr int RL_INSTR = RL_STAGE / 1024;             // 1 KB direct loads per superstep (20)
+constexpr int RL_PER_WAVE = RL_INSTR / 4;             // 5
+static_assert(RL_INSTR % 4 == 0, "router loads split evenly over the waves");
+static_assert(RL_STAGES * RL_STAGE <= 160 * 1024, "router LDS");
+static_assert((RL_STAGES - 2) * RL_PER_WAVE <= 63, "vmcnt range");
 
 typedef __attribute__((address_space(3))) void* rt_lds_t;
 
-// Loads of wave w: instructions j = w, w+8, ... < RF_INSTR (5 for waves 0-3,
-// 4 for waves 4-7).
-__device__ __forceinline__ int rf_loads(int wave) { return (RF_INSTR - wave + 7) / 8; }
-
-// Instruction j fills stage rows 8j .. 8j+7 (rows 0..31 are x tokens,
-// 32..287 W_r experts): lane -> row 8j + lane/8, LDS slot lane%8 holding
-// the row's piece slot ^ ((row >> 1) & 7).
-__device__ __forceinline__ void rf_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
-                                         int t0, int wave, int lane, int u, uint8_t* stage) {
+// Instruction j = wave + 4i fills stage rows 8j .. 8j+7 (rows 0..31: x
+// tokens, 32..159: W_r experts): lane -> row 8j + lane/8, LDS slot lane%8
+// holding the row's piece slot ^ ((row >> 1) & 7).
+__device__ __forceinline__ void rl_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
+                                         int t0, int e0, int wave, int lane, int u,
+                                         uint8_t* stage) {
 #pragma unroll
-    for (int i = 0; i < (RF_INSTR + 7) / 8; ++i) {
-        const int j = wave + 8 * i;
-        if (j >= RF_INSTR) break;
+    for (int i = 0; i < RL_PER_WAVE; ++i) {
+        const int j = wave + 4 * i;
         const int row = 8 * j + (lane >> 3);
         const int p = (lane & 7) ^ ((row >> 1) & 7);
         uint8_t* dst = stage + j * 1024;
-        if (j < RF_TOK / 8) {
+        if (j < RL_TOK / 8) {
             const uint32_t off = (uint32_t)(t0 + row) * (H * 2) + (uint32_t)(u * 128 + 16 * p);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (rt_lds_t)dst, 16, off, 0, 0, 0);
         } else {
-            const uint32_t off = (uint32_t)(row - RF_TOK) * (H * 2) + (uint32_t)(u * 128 + 16 * p);
+            const uint32_t off = (uint32_t)(e0 + row - RL_TOK) * (H * 2) + (uint32_t)(u * 128 + 16 * p);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (rt_lds_t)dst, 16, off, 0, 0, 0);
         }
     }
 }
 
-__global__ __launch_bounds__(512) void route_fused(const uint16_t* __restrict__ x, int T,
-                                                   const uint16_t* __restrict__ wr,
-                                                   const float* __restrict__ bias,
-                                                   const uint16_t* __restrict__ wsg,
-                                                   int32_t* __restrict__ ids,
-                                                   float* __restrict__ wts,
-                                                   float* __restrict__ sg) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[RF_STAGES * RF_STAGE + RF_TOK * RF_LDS_STRIDE * 4];
-    float* lg = reinterpret_cast<float*>(smem + RF_STAGES * RF_STAGE);
+__global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restrict__ x, int T,
+                                                         const uint16_t* __restrict__ wr,
+                                                         const float* __restrict__ bias,
+                                                         float* __restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[RL_STAGES * RL_STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
-    const int t0 = blockIdx.x * RF_TOK;
+    const int t0 = blockIdx.x * RL_TOK;
+    const int e0 = blockIdx.y * RL_EXP;
     const __amdgpu_buffer_rsrc_t rx = rt_rsrc(x, (uint32_t)((size_t)T * H * 2));
     const __amdgpu_buffer_rsrc_t rw = rt_rsrc(wr, (uint32_t)(E * H * 2));
     constexpr int NU = H / 64;    // 32 supersteps
 
-    static_assert(RF_TOK % 8 == 0, "x rows must fill whole load instructions");
-    for (int u = 0; u < RF_STAGES - 1; ++u) rf_issue(rx, rw, t0, wave, lane, u, smem + u * RF_STAGE);
+    static_assert(RL_TOK % 8 == 0, "x rows must fill whole load instructions");
+#pragma unroll
+    for (int u = 0; u < RL_STAGES - 1; ++u) rl_issue(rx, rw, t0, e0, wave, lane, u, smem + u * RL_STAGE);
 
     float16v acc = (float16v)0.f;
-    const int ra = l32, rb = RF_TOK + wave * 32 + l32;     // operand rows in the stage
+    const int ra = l32, rb = RL_TOK + wave * 32 + l32;     // operand rows in the stage
     for (int u = 0; u < NU; ++u) {
-        // superstep u landed (the next one may stay in flight), then every
-        // wave is done with the stage the refill overwrites
-        if (u + 1 < NU && rf_loads(wave) == 5) __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
-        else if (u + 1 < NU) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        // superstep u landed (the later ones may stay in flight): each wave
+        // has min(NU - 1 - u, STAGES - 2) more supersteps of loads issued
+        const int ahead = min(NU - 1 - u, RL_STAGES - 2);
+        switch (ahead) {
+            case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * RL_PER_WAVE)); break;
+            case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * RL_PER_WAVE)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * RL_PER_WAVE)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * RL_PER_WAVE)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * RL_PER_WAVE)); break;
+            default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+        }
+        // every wave's part of superstep u is in LDS, and every wave is done
+        // with the stage the refill below overwrites (superstep u - 1)
         pipe_barrier();
-        if (u + RF_STAGES - 1 < NU)
-            rf_issue(rx, rw, t0, wave, lane, u + RF_STAGES - 1, smem + ((u + RF_STAGES - 1) % RF_STAGES) * RF_STAGE);
-        const uint8_t* st = smem + (u % RF_STAGES) * RF_STAGE;
+        if (u + RL_STAGES - 1 < NU)
+            rl_issue(rx, rw, t0, e0, wave, lane, u + RL_STAGES - 1,
+                     smem + ((u + RL_STAGES - 1) % RL_STAGES) * RL_STAGE);
+        const uint8_t* st = smem + (u % RL_STAGES) * RL_STAGE;
+        // all eight operand reads first, then the four MFMAs
+        uint4v av[4], bv[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int pc = 4 * g + s;
-            const uint4v av = *reinterpret_cast<const uint4v*>(st + ra * 128 + 16 * (pc ^ ((ra >> 1) & 7)));
-            const uint4v bv = *reinterpret_cast<const uint4v*>(st + rb * 128 + 16 * (pc ^ ((rb >> 1) & 7)));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            av[s] = *reinterpret_cast<const uint4v*>(st + ra * 128 + 16 * (pc ^ ((ra >> 1) & 7)));
+            bv[s] = *reinterpret_cast<const uint4v*>(st + rb * 128 + 16 * (pc ^ ((rb >> 1) & 7)));
         }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[s]),
+                                                          __builtin_bit_cast(bf16x8, bv[s]), acc, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // MFMAs
     }
-
-    // logits (+ bias) into LDS: element i is token 8*(i/4) + 4g + i%4
-    const int e = wave * 32 + l32;
+    // element i: token 8*(i/4) + 4g + i%4, expert e0 + 32w + l32
+    const int e = e0 + wave * 32 + l32;
     const float bb = bias ? bias[e] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) lg[(8 * (i >> 2) + 4 * g + (i & 3)) * RF_LDS_STRIDE + e] = acc[i] + bb;
-    __syncthreads();
-
-    // selection and shared gate: wave w handles tokens 4w .. 4w+3
-    for (int q = 0; q < RF_TOK / 8; ++q) {
-        const int tl = wave * (RF_TOK / 8) + q;
-        const int t = t0 + tl;
-        if (t >= T) break;
-        wave_top8(lg + tl * RF_LDS_STRIDE, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
-        const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
-        const uint4v* gr = reinterpret_cast<const uint4v*>(wsg) + lane * 4;
-        float z = dot8_bf16(xr[0], gr[0]) + dot8_bf16(xr[1], gr[1]) + dot8_bf16(xr[2], gr[2]) +
-                  dot8_bf16(xr[3], gr[3]);
-        z = wave_sum(z);
-        if (lane == 0) sg[t] = 1.f / (1.f + expf(-z));
+    for (int i = 0; i < 16; ++i) {
+        const int t = t0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (t < T) logits[(size_t)t * E + e] = acc[i] + bb;
     }
 }
 
-// grid: ceil(T/4) blocks of 4 waves; wave -> token: radix-selected top-8,
+// grid: ceil(T/4) blocks of 4 waves; wave -> token: top-8 (wave_top8),
 // renormalised weights and the shared-expert gate.
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits,
                                                   const uint16_t* __restrict__ x,
@@ -241,19 +195,14 @@ void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const flo
         hipLaunchKernelGGL(route_logits_gemv, dim3(E / 4), dim3(256), 0, st, x, T, wr, bias,
                            logits);
     } else {
-        hipLaunchKernelGGL(route_logits_mfma, dim3((T + 63) / 64, E / 64), dim3(256), 0, st, x,
-                           T, wr, bias, logits);
+        hipLaunchKernelGGL(route_logits_tile, dim3((T + RL_TOK - 1) / RL_TOK, E / RL_EXP),
+                           dim3(256), 0, st, x, T, wr, bias, logits);
     }
 }
 
 void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                   const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
                   hipStream_t st) {
-    if (T > 32) {
-        hipLaunchKernelGGL(route_fused, dim3((T + RF_TOK - 1) / RF_TOK), dim3(512), 0, st, x, T, wr,
-                           bias, wsg, ids, wts, sg);
-        return;
-    }
     launch_route_logits(x, T, wr, bias, logits, st);
     hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, x, wsg, T, ids,
                        wts, sg);

@@ -36,7 +36,7 @@ def check(ids_np):
         assert np.array_equal(g, r), f"{name} differs at {np.flatnonzero(g != r)[:5]}"
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 8, 16, 31, 32, 33, 511, 512, 513, 4096, 4097, 16384, 65536])
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 16, 31, 32, 33, 127, 128, 129, 511, 512, 513, 4096, 4097, 16384, 65536])
 def test_permute_random(gpu, T):
     P.say(f"permute random T={T}")
     check(random_ids(T, T))

@@ -10,7 +10,7 @@ import parity as P
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T", [1, 8, 16, 32, 33, 100, 512, 4096])
+@pytest.mark.parametrize("T", [1, 8, 16, 32, 33, 100, 129, 512, 4096])
 def test_route_uniform(gpu, T):
     P.say(f"route T={T} seed=0 layer=0")
     L, D = P.host_layer(0, 0), P.dev_layer(0, 0)
