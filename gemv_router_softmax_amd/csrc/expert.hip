@@ -822,12 +822,14 @@ static GemmArgs gemm_args(const uint16_t* ain, size_t ain_bytes, int T, const in
 
 constexpr unsigned GEMM_GRID = 256;   // one workgroup per compute unit (a multiple of 8 XCDs)
 
+// xh_ready: the fp16 activations are already in xh (the router wrote them).
 static void launch_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
                           int* tile_count, const QFFN& routed, const QFFN& shared,
-                          uint16_t* xh, uint16_t* hbuf, hipStream_t st) {
+                          uint16_t* xh, uint16_t* hbuf, bool xh_ready, hipStream_t st) {
     const size_t chunks = (size_t)T * (H / 8);
-    hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x, T,
-                       xh);
+    if (!xh_ready)
+        hipLaunchKernelGGL(prep_x_f16, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, x,
+                           T, xh);
     GemmArgs gu = gemm_args(xh, (size_t)T * H * 2, T, perm);
     gu.hout = hbuf;
     hipLaunchKernelGGL((grouped_gemm<H, GM_GATEUP>), dim3(GEMM_GRID), dim3(pg::THREADS), 0, st, gu,
@@ -838,7 +840,7 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
                            int* tile_count, int /*max_tiles*/, const QFFN& routed,
                            const QFFN& shared, uint16_t* xh, uint16_t* hbuf, float* dout,
                            hipStream_t st) {
-    launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, st);
+    launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, false, st);
     GemmArgs dn = gemm_args(hbuf, (size_t)(TOPK + 1) * T * I * 2, T, perm);
     dn.dout32 = dout;
     hipLaunchKernelGGL((grouped_gemm<I, GM_DOWN_F32>), dim3(GEMM_GRID), dim3(pg::THREADS), 0, st,
@@ -851,8 +853,8 @@ void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, 
                                  int* tile_count, int /*max_tiles*/, const QFFN& routed,
                                  const QFFN& shared, uint16_t* xh, uint16_t* hbuf,
                                  uint16_t* d16, const float* wsorted, const float* sg,
-                                 hipStream_t st) {
-    launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, st);
+                                 bool xh_ready, hipStream_t st) {
+    launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, xh_ready, st);
     GemmArgs dn = gemm_args(hbuf, (size_t)(TOPK + 1) * T * I * 2, T, perm);
     dn.dout16 = d16;
     dn.wsorted = wsorted;

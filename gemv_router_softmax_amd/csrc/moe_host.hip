@@ -14,7 +14,7 @@
 namespace moe {
 void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                   const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
-                  hipStream_t st);
+                  hipStream_t st, uint16_t* xh = nullptr);
 void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                          float* logits, hipStream_t st);
 void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,
@@ -52,7 +52,7 @@ void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, 
                                  int* tile_count, int max_tiles, const QFFN& routed,
                                  const QFFN& shared, uint16_t* xh, uint16_t* hbuf,
                                  uint16_t* d16, const float* wsorted, const float* sg,
-                                 hipStream_t st);
+                                 bool xh_ready, hipStream_t st);
 void launch_combine_f16(const uint16_t* d16, const int32_t* inv, int T, uint16_t* y,
                         const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_combine(const float* out, const int32_t* inv, const float* wts, const float* sg, int T,
@@ -313,16 +313,18 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
                                    st);
         return launch_status();
     }
+    // the top-8 kernel also writes the fp16 activations the grouped GEMM reads
+    uint16_t* xh = at<uint16_t>(ws, L.xh);
     launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
-                 at<float>(ws, L.logits), ids, wts, sg, st);
+                 at<float>(ws, L.logits), ids, wts, sg, st, xh);
     float* wsorted = at<float>(ws, L.wsorted);
     launch_permute(ids, T, counts, offsets, perm, inv, at<int32_t>(ws, L.chunk_counts), st, wts,
                    wsorted, tiles, tcount);
     // fp16 rows of weight * d (half the bytes of fp32 expert outputs)
     uint16_t* d16 = reinterpret_cast<uint16_t*>(dout);
     launch_expert_prefill_fused(x, T, perm, tiles, tcount, max_tiles(T), qffn_view(layer->routed),
-                                qffn_view(layer->shared), at<uint16_t>(ws, L.xh), hbuf, d16,
-                                wsorted, sg, st);
+                                qffn_view(layer->shared), xh, hbuf, d16, wsorted, sg,
+                                /*xh_ready=*/true, st);
     launch_combine_f16(d16, inv, T, y, x, res, st);
     return launch_status();
 }

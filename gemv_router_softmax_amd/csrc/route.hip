@@ -170,23 +170,34 @@ __global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restr
 }
 
 // grid: ceil(T/4) blocks of 4 waves; wave -> token: top-8 (wave_top8),
-// renormalised weights and the shared-expert gate.
+// renormalised weights and the shared-expert gate; optionally (the fused
+// layer) also the fp16 copy of the token's row in chunk-slot order that the
+// grouped GEMM reads (xh), which saves the conversion kernel.
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits,
                                                   const uint16_t* __restrict__ x,
                                                   const uint16_t* __restrict__ wsg, int T,
                                                   int32_t* __restrict__ ids,
                                                   float* __restrict__ wts,
-                                                  float* __restrict__ sg) {
+                                                  float* __restrict__ sg,
+                                                  uint16_t* __restrict__ xh) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    wave_top8(logits + (size_t)t * E, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
     const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
+    const uint4v x0 = xr[0], x1 = xr[1], x2 = xr[2], x3 = xr[3];
+    wave_top8(logits + (size_t)t * E, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
     const uint4v* gr = reinterpret_cast<const uint4v*>(wsg) + lane * 4;
-    float z = dot8_bf16(xr[0], gr[0]) + dot8_bf16(xr[1], gr[1]) + dot8_bf16(xr[2], gr[2]) +
-              dot8_bf16(xr[3], gr[3]);
+    float z = dot8_bf16(x0, gr[0]) + dot8_bf16(x1, gr[1]) + dot8_bf16(x2, gr[2]) +
+              dot8_bf16(x3, gr[3]);
     z = wave_sum(z);
     if (lane == 0) sg[t] = 1.f / (1.f + expf(-z));
+    if (xh) {
+        uint4v* xo = reinterpret_cast<uint4v*>(xh + (size_t)t * H) + lane * 4;
+        xo[0] = bf16x8_to_f16_slots(x0);
+        xo[1] = bf16x8_to_f16_slots(x1);
+        xo[2] = bf16x8_to_f16_slots(x2);
+        xo[3] = bf16x8_to_f16_slots(x3);
+    }
 }
 
 void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
@@ -200,12 +211,13 @@ void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const flo
     }
 }
 
+// xh: optional fp16 activation copy.
 void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                   const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
-                  hipStream_t st) {
+                  hipStream_t st, uint16_t* xh) {
     launch_route_logits(x, T, wr, bias, logits, st);
     hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, x, wsg, T, ids,
-                       wts, sg);
+                       wts, sg, xh);
 }
 
 }  // namespace moe
