@@ -287,6 +287,104 @@ def prefill(D, T, iters):
     }
 
 
+def _graphs_timed(fns, iters):
+    """Capture each callable once in its own HIP graph, then replay them in
+    turn with HIP events around every replay; returns the per-replay ms."""
+    import torch
+    graphs = []
+    for fn in fns:
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    pairs = event_pairs(iters)
+    for i, (a, b) in enumerate(pairs):
+        a.record()
+        graphs[i % len(graphs)].replay()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in pairs])
+
+
+def prefill_sweep(D, Ts, iters):
+    """One layer at each T (rotating over the layers), graph-replayed: tokens/s,
+    MFMA utilisation of the expert flops and the algorithmic HBM rate (all 257
+    experts' weights are touched from T of a few hundred up)."""
+    import torch
+    import gemv_router_softmax_amd as moe
+    from gemv_router_softmax_amd import synth
+    out = []
+    for T in Ts:
+        x = moe.to_device_bits(synth.make_x(T, seed=0))
+        y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        ws = moe.workspace(T)
+        nl = min(iters, len(D))
+        ms = _graphs_timed([lambda Dl=D[(i + 11) % len(D)]: moe.moe_layer_forward(x, Dl, y, ws)
+                            for i in range(nl)], iters)
+        t = float(ms.mean()) * 1e-3
+        flops = EXPERT_FLOP_PER_TOKEN * 9 * T
+        wbytes = 257 * EXPERT_BYTES + E * H * 2 + H * 2 + 2 * T * H * 2
+        out.append({"T": T, "layer_ms": t * 1e3, "tokens_per_s": T / t,
+                    "mfma_util": flops / t / (BF16_DENSE_PEAK_TFLOPS * 1e12),
+                    "tflops": flops / t / 1e12, "weight_gbs": wbytes / t / 1e9,
+                    "bound": "mfma" if flops / wbytes > BF16_DENSE_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
+                             else "hbm"})
+        del x, y, ws
+    return out
+
+
+def prefill_chain(D, T, iters):
+    """T tokens through the whole layer chain with residual adds (the chain
+    captured as one HIP graph): tokens/s and per-layer time."""
+    import torch
+    import gemv_router_softmax_amd as moe
+    from gemv_router_softmax_amd import synth
+    x0 = moe.to_device_bits(synth.make_x(T, seed=0))
+    bufs = [torch.empty((T, H), dtype=torch.int16, device="cuda") for _ in range(2)]
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ws = moe.workspace(T)
+
+    def chain():
+        cur = x0
+        for l, Dl in enumerate(D):
+            nxt = bufs[l % 2]
+            moe.moe_layer_forward_ex(cur, Dl, y, ws, residual_out=nxt)
+            cur = nxt
+    ms = _graphs_timed([chain], iters)
+    t = float(ms.mean()) * 1e-3
+    return {"T": T, "layers": len(D), "chain_ms": t * 1e3, "tokens_per_s": T / t,
+            "layer_us": t / len(D) * 1e6,
+            "weight_gbs": len(D) * (257 * EXPERT_BYTES + E * H * 2) / t / 1e9}
+
+
+def skewed_chunked(T_total, chunk, iters, layers=4):
+    """The Zipf-biased router: T_total tokens in chunks of `chunk` through one
+    layer (the chunks run back to back in one HIP graph, rotating over a few
+    skewed layers): tokens/s and MFMA utilisation."""
+    import torch
+    import gemv_router_softmax_amd as moe
+    from gemv_router_softmax_amd import synth
+    Ds = [moe.DeviceLayer(L) for L in gen_layers(layers, skewed=True)]
+    x = moe.to_device_bits(synth.make_x(T_total, seed=0))
+    y = torch.empty((T_total, H), dtype=torch.int16, device="cuda")
+    ws = moe.workspace(chunk)
+
+    def run(Dl):
+        for c0 in range(0, T_total, chunk):
+            moe.moe_layer_forward(x[c0:c0 + chunk], Dl, y[c0:c0 + chunk], ws)
+    ms = _graphs_timed([lambda Dl=Dl: run(Dl) for Dl in Ds], iters)
+    t = float(ms.mean()) * 1e-3
+    flops = EXPERT_FLOP_PER_TOKEN * 9 * T_total
+    return {"T": T_total, "chunk": chunk, "ms": t * 1e3, "tokens_per_s": T_total / t,
+            "mfma_util": flops / t / (BF16_DENSE_PEAK_TFLOPS * 1e12)}
+
+
 def cpu_baseline(layers, budget_s):
     import oracle
     from gemv_router_softmax_amd import synth
@@ -316,6 +414,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the prefill T sweep, the T=512 chain and the skewed chunked run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true")
@@ -363,6 +463,14 @@ def main():
     if not args.no_prefill:
         pre = prefill(D, 4096, args.prefill_iters)
         log(f"prefill T=4096: {pre}")
+    sweep = chain512 = skewed = None
+    if not args.no_prefill and not args.no_extra:
+        sweep = prefill_sweep(D, (256, 1024, 2048, 4096), args.prefill_iters)
+        log(f"prefill sweep: {sweep}")
+        chain512 = prefill_chain(D, 512, 5)
+        log(f"prefill chain T=512: {chain512}")
+        skewed = skewed_chunked(16384, 4096, 8)
+        log(f"skewed chunked prefill: {skewed}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -398,6 +506,9 @@ def main():
         "wallclock_gbs": chain_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_read_ceiling_gbs": ceiling,
         "prefill_t4096": pre,
+        "prefill_sweep": sweep,
+        "prefill_chain_t512": chain512,
+        "prefill_skewed_t16384_chunks4096": skewed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
