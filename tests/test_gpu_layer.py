@@ -153,3 +153,56 @@ def test_dense_and_expert_layouts_agree(gpu, T, path):
     y0, _, _ = gpu_layer(x, dense, path)
     y1, _, _ = gpu_layer(x, blocked, path)
     assert np.array_equal(y0, y1)
+
+
+def test_max_t_sampled(gpu):
+    """The largest T the library accepts (MOE_T_MAX = 65536 tokens), checked
+    against the oracle on sampled tokens (routing is per token, so any subset
+    of tokens is a valid oracle input)."""
+    rng = np.random.default_rng(11)
+    T = moe.MOE_T_MAX
+    check_layer(T, AUTO, seed=12, sample=np.sort(rng.choice(T, 32, replace=False)))
+
+
+@pytest.mark.parametrize("T,nl", [(1, 3), (512, 2)])
+def test_chain_layer_by_layer(gpu, T, nl):
+    """A chain of distinct layers with residual adds (the decode and the
+    T = 512 prefill workloads): every layer's output matches the oracle run
+    on the GPU's own input to that layer, and the residual output is exactly
+    bf16(x + y)."""
+    xd = moe.to_device_bits(synth.make_x(T, seed=0, step=3))
+    for l in range(nl):
+        P.say(f"chain T={T} layer {l}")
+        L, D = P.host_layer(0, l), P.dev_layer(0, l)
+        x = moe.bits_to_numpy(xd)
+        y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+        res = torch.empty_like(y)
+        moe.moe_layer_forward_ex(xd, D, y, moe.workspace(T), residual_out=res)
+        torch.cuda.synchronize()
+        yn = moe.bits_to_numpy(y)
+        ids, _, _ = P.gpu_route(xd, D)
+        ref, _ = P.oracle_layer_substituted(L, x, ids)
+        P.assert_close(P.bf16_f64(yn), P.bf16_f64(ref.y), f"chain T={T} layer {l}")
+        want = P.orc().round_bf16(P.bf16_f64(x) + P.bf16_f64(yn))
+        assert np.array_equal(moe.bits_to_numpy(res), want)
+        xd = res
+
+
+def test_skewed_chunked_sampled(gpu):
+    """The Zipf-biased router over 16384 tokens in four 4096-token chunks
+    sharing one workspace, checked on sampled tokens of every chunk."""
+    T, C = 16384, 4096
+    L, D = P.host_layer(0, 0, True), P.dev_layer(0, 0, True)
+    x = synth.make_x(T, seed=13, layer=T)
+    xd = moe.to_device_bits(x)
+    y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    ws = moe.workspace(C)
+    for c0 in range(0, T, C):
+        moe.moe_layer_forward(xd[c0:c0 + C], D, y[c0:c0 + C], ws)
+    torch.cuda.synchronize()
+    yn = moe.bits_to_numpy(y)
+    rng = np.random.default_rng(14)
+    rows = np.sort(np.concatenate([c0 + rng.choice(C, 12, replace=False) for c0 in range(0, T, C)]))
+    ids = np.concatenate([P.gpu_route(xd[c0:c0 + C], D)[0] for c0 in range(0, T, C)])
+    ref, _ = P.oracle_layer_substituted(L, np.ascontiguousarray(x[rows]), ids[rows])
+    P.assert_close(P.bf16_f64(yn[rows]), P.bf16_f64(ref.y), "skewed chunked y")
