@@ -16,10 +16,11 @@ constexpr int G = MOE_GROUP;      // 64
 constexpr int WAVE = 64;
 
 // Row tiles of the grouped expert work: at most MT_ROWS rows of one expert
-// (group 256 = the shared expert) per tile; a group is split into equal
-// tiles (160 covers the busiest expert of a uniformly routed 4096-token
-// batch in one tile).
+// (group 256 = the shared expert) per tile at large T, MT_MIN_ROWS at small
+// T; a group is split into equal tiles (160 covers the busiest expert of a
+// uniformly routed 4096-token batch in one tile).
 constexpr int MT_ROWS = 160;
+constexpr int MT_MIN_ROWS = 32;
 
 // Device view of one expert stack: the nine arrays and the byte distance
 // between consecutive experts in the code arrays (sq) and in the
@@ -56,7 +57,7 @@ constexpr int GEMM_CTR_GATEUP = 8, GEMM_CTR_DOWN = 16, TILE_COUNT_WORDS = 24;
 struct Tile {
     int group;     // 0..255 routed expert, 256 shared expert
     int row0;      // first row in the permuted row space (shared rows start at 8T)
-    int nrows;     // 1..MT_ROWS
+    int nrows;     // 1..MT_ROWS (1..MT_MIN_ROWS for small-T plans)
     int pad;
 };
 

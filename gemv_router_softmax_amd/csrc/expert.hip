@@ -171,35 +171,43 @@ struct GemmArgs {
     const float* sg;          // shared-expert gate per token [T]
 };
 
-namespace pg {
-constexpr int WAVES = 4;
-constexpr int THREADS = WAVES * 64;
-constexpr int MT = MT_ROWS;                 // rows per tile, at most
-constexpr int NMT_MAX = MT / 32;             // 32-row m-tiles
-constexpr int KC = G;                       // K per chunk: one quantisation group
-constexpr int STAGES = 5;                   // chunk c+5 refills chunk c's stage once
-                                            // every wave is past its last read of it
-constexpr int AROW = KC * 2;                // bytes of one A row per chunk
-constexpr int A_BYTES = MT * AROW;
-constexpr int NCOL = 256;                   // weight rows per item
-constexpr int B_BYTES = NCOL * KC / 2;
-constexpr int S_BYTES = NCOL * 4;
-constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
-constexpr int META = WAVES * 256;           // per-item row metadata (tokens or weights):
-                                            // one 4-byte direct load (256 B) per wave
-constexpr int STG = 1024;                   // per-wave epilogue staging
-constexpr int CLAIM = WAVES * 256 + 16;     // the claimed item index (16 B) and the
-                                            // landing area of waves 1-3's stand-in load
-constexpr int LDS_BYTES = STAGES * STAGE + 2 * META + WAVES * STG + CLAIM;
-constexpr int A_LOADS = MT / 8 / WAVES;     // 1 KB (8 rows) per load instruction
-constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
-constexpr int LPC = A_LOADS + B_LOADS + 2;  // loads per wave per chunk
-constexpr uint32_t OOB = 0x80000000u;       // beyond every buffer: no memory access
-static_assert(MT % (8 * WAVES) == 0, "A rows must split evenly over the load instructions");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-static_assert(META >= MT * 4, "row metadata must cover a tile");
-static_assert((STAGES - 2) * LPC + 2 <= 63, "vmcnt range");
-}  // namespace pg
+constexpr uint32_t OOB_OFF = 0x80000000u;   // beyond every buffer: no memory access
+
+// Tile geometry of one instantiation: MTR = rows per row tile, at most (160
+// for large T; 32 for small T, whose LDS fits two workgroups per CU).
+template <int MTR>
+struct PG {
+    static constexpr int WAVES = 4;
+    static constexpr int THREADS = WAVES * 64;
+    static constexpr int MT = MTR;                      // rows per tile, at most
+    static constexpr int NMT_MAX = MT / 32;             // 32-row m-tiles
+    static constexpr int KC = G;                        // K per chunk: one quantisation group
+    static constexpr int STAGES = 5;                    // chunk c+5 refills chunk c's stage once
+                                                        // every wave is past its last read of it
+    static constexpr int AROW = KC * 2;                 // bytes of one A row per chunk
+    static constexpr int A_BYTES = MT * AROW;
+    static constexpr int NCOL = 256;                    // weight rows per item
+    static constexpr int B_BYTES = NCOL * KC / 2;
+    static constexpr int S_BYTES = NCOL * 4;
+    static constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
+    static constexpr int META = WAVES * 256;            // per-item row metadata (tokens or weights):
+                                                        // one 4-byte direct load (256 B) per wave
+    static constexpr int STG = 1024;                    // per-wave epilogue staging
+    static constexpr int CLAIM = WAVES * 256 + 16;      // the claimed item index (16 B) and the
+                                                        // landing area of waves 1-3's stand-in load
+    static constexpr int LDS_BYTES = STAGES * STAGE + 2 * META + WAVES * STG + CLAIM;
+    static constexpr int A_LOADS = MT / 8 / WAVES;      // 1 KB (8 rows) per load instruction
+    static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
+    static constexpr int LPC = A_LOADS + B_LOADS + 2;   // loads per wave per chunk
+    static constexpr uint32_t OOB = OOB_OFF;
+    static constexpr int WG_PER_CU = 160 * 1024 / LDS_BYTES;   // workgroups the LDS holds per CU
+    static_assert(MT % (8 * WAVES) == 0, "A rows must split evenly over the load instructions");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(META >= MT * 4, "row metadata must cover a tile");
+    static_assert((STAGES - 2) * LPC + 2 <= 63, "vmcnt range");
+};
+constexpr int MT_LARGE = MT_ROWS, MT_SMALL = 32;
+static_assert(PG<MT_SMALL>::WG_PER_CU >= 2 && PG<MT_LARGE>::WG_PER_CU == 1, "tile LDS footprints");
 
 typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
@@ -237,7 +245,7 @@ __device__ __forceinline__ uint32_t claim_item(int* ctr, uint8_t* claim) {
     } else {
         const __amdgpu_buffer_rsrc_t r = buf_rsrc(ctr, 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(claim + 16 + wave * 256), 4,
-                                                 pg::OOB, 0, 0, 0);
+                                                 OOB_OFF, 0, 0, 0);
     }
     return t;
 }
@@ -247,10 +255,11 @@ __device__ __forceinline__ uint32_t claim_item(int* ctr, uint8_t* claim) {
 // wave-uniform offset (the soffset operand of the loads), so issuing a chunk
 // costs no vector arithmetic.  Rows past the tile and items past the last
 // get out-of-range offsets (the loads access no memory and fill zeros).
+template <int MTR>
 struct GSrc {
     __amdgpu_buffer_rsrc_t rq, rs, rb;   // this wave's code / scale / bias matrix
-    uint32_t a[pg::A_LOADS];             // A: instruction i -> rows (w*A_LOADS + i)*8 + lane/8
-    uint32_t b[pg::B_LOADS];             // B: instruction i -> columns (w*B_LOADS + i)*32 + lane/2
+    uint32_t a[PG<MTR>::A_LOADS];        // A: instruction i -> rows (w*A_LOADS + i)*8 + lane/8
+    uint32_t b[PG<MTR>::B_LOADS];        // B: instruction i -> columns (w*B_LOADS + i)*32 + lane/2
     uint32_t s;                          // scale/bias dword of column w*64 + lane
 };
 
@@ -282,13 +291,14 @@ __device__ __forceinline__ WPtr wave_ptrs(const QFFN& f) {
     return w;
 }
 
-template <int KDIM, int MODE>
-__device__ __forceinline__ GSrc gemm_src(const GItem& m, const int32_t* tok, int T,
-                                         const WPtr& pr, const WPtr& ps) {
+template <int KDIM, int MODE, int MTR>
+__device__ __forceinline__ GSrc<MTR> gemm_src(const GItem& m, const int32_t* tok, int T,
+                                              const WPtr& pr, const WPtr& ps) {
+    using pg = PG<MTR>;
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int WPR = KDIM / 8, SPR = KDIM / G, ROWS_W = GATEUP ? I : H;
     const int lane = threadIdx.x & 63, wave = wave_id();
-    GSrc g;
+    GSrc<MTR> g;
     // A: LDS slot (lane & 7) of row R holds the row's piece slot ^ ((R >> 1) & 7)
 #pragma unroll
     for (int i = 0; i < pg::A_LOADS; ++i) {
@@ -328,8 +338,10 @@ __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst,
 }
 
 // The LPC loads of chunk kc of an item into one stage.
-__device__ __forceinline__ void issue_chunk(const GSrc& g, int kc, __amdgpu_buffer_rsrc_t ra,
+template <int MTR>
+__device__ __forceinline__ void issue_chunk(const GSrc<MTR>& g, int kc, __amdgpu_buffer_rsrc_t ra,
                                             uint8_t* stage) {
+    using pg = PG<MTR>;
     const int wave = wave_id();
 #pragma unroll
     for (int i = 0; i < pg::A_LOADS; ++i)
@@ -363,8 +375,9 @@ struct BFrag {
     half2v s[2], b[2];    // fp16 scale / bias, splat
 };
 
-template <bool GATEUP>
+template <bool GATEUP, int MTR>
 __device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc) {
+    using pg = PG<MTR>;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int l32 = lane & 31, g = lane >> 5;
     BFrag B;
@@ -382,8 +395,9 @@ __device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc) {
 }
 
 // A operand of K-step s: row mt*32 + l%32, k-piece 4g + s.
-template <int NMT>
+template <int NMT, int MTR>
 __device__ __forceinline__ void read_a(const uint8_t* stage, int s, half8 (&a)[NMT]) {
+    using pg = PG<MTR>;
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -426,9 +440,10 @@ __device__ __forceinline__ void sched_step() {
 }
 
 // Stores per wave per epilogue (one 16-byte store per lane per 1 KB staged).
-template <int MODE>
+template <int MODE, int MTR>
 constexpr int epi_stores() {
-    return MODE == GM_GATEUP ? 2 * pg::NMT_MAX : MODE == GM_DOWN_F16W ? 4 * pg::NMT_MAX : 8 * pg::NMT_MAX;
+    constexpr int n = PG<MTR>::NMT_MAX;
+    return MODE == GM_GATEUP ? 2 * n : MODE == GM_DOWN_F16W ? 4 * n : 8 * n;
 }
 
 // Staging through LDS moves values between lanes of one wave.  The wave's
@@ -443,10 +458,11 @@ __device__ __forceinline__ void lane_exchange_fence() {
 
 // Accumulator element i of a lane lies in staged half hr = i/8 of the
 // m-tile (rows 16*hr .. 16*hr+15), at staged row 8*((i/4)&1) + 4g + i%4.
-template <int MODE, int NMT>
+template <int MODE, int NMT, int MTR>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                                               float16v (&acc)[NMT][2], uint8_t* stg,
                                               const float* coef) {
+    using pg = PG<MTR>;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int l32 = lane & 31, g = lane >> 5;
     const int T = A.T;
@@ -560,17 +576,17 @@ __device__ __forceinline__ void issue_meta(const GemmArgs& A, const GItem& m, ui
     const bool use = m.valid && wave < 3 && R < m.nrows;
     if constexpr (MODE == GM_GATEUP) {
         const __amdgpu_buffer_rsrc_t rp = buf_rsrc(A.perm, (uint32_t)(TOPK * T * 4));
-        const uint32_t off = use && !m.shared ? (uint32_t)((m.row0 + R) * 4) : pg::OOB;
+        const uint32_t off = use && !m.shared ? (uint32_t)((m.row0 + R) * 4) : OOB_OFF;
         load_lds<4>(rp, meta + wave * 256, off, 0);
     } else if constexpr (MODE == GM_DOWN_F16W) {
         const __amdgpu_buffer_rsrc_t rw =
             m.shared ? buf_rsrc(A.sg, (uint32_t)(T * 4)) : buf_rsrc(A.wsorted, (uint32_t)(TOPK * T * 4));
         const int idx = m.shared ? m.row0 + R - TOPK * T : m.row0 + R;
-        const uint32_t off = use ? (uint32_t)(idx * 4) : pg::OOB;
+        const uint32_t off = use ? (uint32_t)(idx * 4) : OOB_OFF;
         load_lds<4>(rw, meta + wave * 256, off, 0);
     } else {
         const __amdgpu_buffer_rsrc_t rp = buf_rsrc(A.perm, 4);
-        load_lds<4>(rp, meta + wave * 256, pg::OOB, 0);
+        load_lds<4>(rp, meta + wave * 256, OOB_OFF, 0);
     }
 }
 
@@ -589,16 +605,17 @@ struct Sched {
 // refilled with chunk c+5 (the ring runs on into the next item) and the next
 // chunk's operands are read and its step 0 dequantised.  Only the first
 // chunk of an item dequantises with no MFMAs to hide under.
-template <int KDIM, int MODE, int NMT>
+template <int KDIM, int MODE, int NMT, int MTR>
 __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cur, GItem& nxt,
-                                              const GSrc& src_cur, GSrc& src_nxt, int& gc, int k,
+                                              const GSrc<MTR>& src_cur, GSrc<MTR>& src_nxt, int& gc, int k,
                                               bool first, __amdgpu_buffer_rsrc_t ra,
                                               const WPtr& pr, const WPtr& ps, uint8_t* lds,
                                               const Sched& sc, uint32_t& tick) {
+    using pg = PG<MTR>;
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     constexpr int NCH = KDIM / pg::KC;
-    constexpr int S_EPI = epi_stores<MODE>();
+    constexpr int S_EPI = epi_stores<MODE, MTR>();
     constexpr int BASE = (pg::STAGES - 2) * pg::LPC;     // loads of the 3 chunks behind the awaited one
     // (a count larger than the operations really issued after the awaited
     // chunk would not wait for it; a smaller one only waits longer)
@@ -614,8 +631,8 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (float16v)0.f;
 
     half8 a_cur[NMT], bf_cur[2];
-    BFrag B = read_b<GATEUP>(lds + (gc % pg::STAGES) * pg::STAGE, 0);
-    read_a<NMT>(lds + (gc % pg::STAGES) * pg::STAGE, 0, a_cur);
+    BFrag B = read_b<GATEUP, MTR>(lds + (gc % pg::STAGES) * pg::STAGE, 0);
+    read_a<NMT, MTR>(lds + (gc % pg::STAGES) * pg::STAGE, 0, a_cur);
     dequant_step(B, 0, bf_cur);
 
     // One chunk.  `refill(stage)` issues the loads of chunk c+5 into the
@@ -625,7 +642,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
             half8 a_nx[NMT], bf_nx[2];
-            read_a<NMT>(st, s + 1, a_nx);
+            read_a<NMT, MTR>(st, s + 1, a_nx);
             dequant_step(B, s + 1, bf_nx);
             mfma_step<NMT>(a_cur, bf_cur, acc);
             sched_step<NMT, NMT>();
@@ -655,8 +672,8 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         half8 a_nx[NMT], bf_nx[2];
         if (more) {
             const uint8_t* sn = lds + ((gc + 1) % pg::STAGES) * pg::STAGE;
-            B = read_b<GATEUP>(sn, c + 1);
-            read_a<NMT>(sn, 0, a_nx);
+            B = read_b<GATEUP, MTR>(sn, c + 1);
+            read_a<NMT, MTR>(sn, 0, a_nx);
         }
         __builtin_amdgcn_sched_barrier(0);
         refill(const_cast<uint8_t*>(st));
@@ -682,7 +699,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     };
     // the next item's sources (its row tokens arrived with this item's first chunk)
     auto make_next = [&]() {
-        src_nxt = gemm_src<KDIM, MODE>(nxt, reinterpret_cast<const int32_t*>(meta + ((k + 1) & 1) * pg::META),
+        src_nxt = gemm_src<KDIM, MODE, MTR>(nxt, reinterpret_cast<const int32_t*>(meta + ((k + 1) & 1) * pg::META),
                                        A.T, pr, ps);
     };
 
@@ -717,7 +734,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 #pragma unroll
     for (int c = (MAIN > HEAD ? MAIN : HEAD); c < NCH; ++c) chunk(c, next(c));
     __builtin_amdgcn_sched_barrier(0);          // epilogue stores after the last refill
-    gemm_epilogue<MODE, NMT>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
+    gemm_epilogue<MODE, NMT, MTR>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -727,11 +744,12 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 // on one XCD and share its L2 for the tile's rows.  Within an XCD the first
 // two items of each workgroup are static and the rest are claimed from the
 // XCD's counter in order -- longest first.
-template <int KDIM, int MODE>
-__global__ __launch_bounds__(pg::THREADS, 1) void grouped_gemm(GemmArgs args,
-                                                              const Tile* __restrict__ tiles,
-                                                              int* __restrict__ tile_count,
-                                                              QFFN routed, QFFN shared) {
+template <int KDIM, int MODE, int MTR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PG<MTR>::WG_PER_CU)))
+void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict__ tile_count,
+                  QFFN routed, QFFN shared) {
+    using pg = PG<MTR>;
+    static_assert(pg::THREADS == 256, "launch bounds");
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     __shared__ __attribute__((aligned(16))) uint8_t lds[pg::LDS_BYTES];
@@ -753,8 +771,8 @@ __global__ __launch_bounds__(pg::THREADS, 1) void grouped_gemm(GemmArgs args,
         __syncthreads();
     }
     const WPtr pr = wave_ptrs<MODE>(routed), ps = wave_ptrs<MODE>(shared);
-    GSrc src_cur = gemm_src<KDIM, MODE>(cur, reinterpret_cast<const int32_t*>(meta), args.T, pr, ps);
-    GSrc src_nxt = src_cur;
+    GSrc<MTR> src_cur = gemm_src<KDIM, MODE, MTR>(cur, reinterpret_cast<const int32_t*>(meta), args.T, pr, ps);
+    GSrc<MTR> src_nxt = src_cur;
     for (int c = 0; c < pg::STAGES; ++c) issue_chunk(src_cur, c, ra, lds + c * pg::STAGE);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((pg::STAGES - 1) * pg::LPC));   // chunk 0 landed
     pipe_barrier();
@@ -763,18 +781,22 @@ __global__ __launch_bounds__(pg::THREADS, 1) void grouped_gemm(GemmArgs args,
     uint32_t tick = 0;
     for (int k = 0;; ++k) {
         switch ((cur.nrows + 31) >> 5) {
+    // (a tile never has more than NMT_MAX m-tiles; cases from NMT_MAX up run
+    // that instance, so every case processes its item)
 #define PG_CASE(n)                                                                           \
     case n:                                                                                  \
-        gemm_run_item<KDIM, MODE, n>(args, cur, nxt, src_cur, src_nxt, gc, k, k == 0, ra, pr, \
-                                     ps, lds, sc, tick);                                     \
+        gemm_run_item<KDIM, MODE, (n < pg::NMT_MAX ? n : pg::NMT_MAX), MTR>(                 \
+            args, cur, nxt, src_cur, src_nxt, gc, k, k == 0, ra, pr, ps, lds, sc, tick);     \
         break;
             PG_CASE(1) PG_CASE(2) PG_CASE(3) PG_CASE(4)
-            default: gemm_run_item<KDIM, MODE, pg::NMT_MAX>(args, cur, nxt, src_cur, src_nxt, gc, k,
-                                                            k == 0, ra, pr, ps, lds, sc, tick);
+            default: gemm_run_item<KDIM, MODE, pg::NMT_MAX, MTR>(args, cur, nxt, src_cur, src_nxt, gc,
+                                                                 k, k == 0, ra, pr, ps, lds, sc, tick);
                      break;
 #undef PG_CASE
         }
-        if (!nxt.valid) break;
+        // no workgroup processes more items than its XCD has: the bound ends
+        // the loop even if the claimed indices were corrupted
+        if (!nxt.valid || k + 1 >= nx) break;
         cur = nxt;
         src_cur = src_nxt;
         // the claimed index, for the next item's first chunk (after its barrier)
@@ -820,7 +842,22 @@ static GemmArgs gemm_args(const uint16_t* ain, size_t ain_bytes, int T, const in
     return a;
 }
 
-constexpr unsigned GEMM_GRID = 256;   // one workgroup per compute unit (a multiple of 8 XCDs)
+// Row-tile height of the grouped GEMMs at T tokens: 32-row tiles (two
+// workgroups per CU) while the experts average at most 16 rows, 160 above.
+int gemm_tile_rows(int T) { return T <= 512 ? MT_SMALL : MT_LARGE; }
+
+// One persistent grouped GEMM: as many workgroups as the LDS lets each CU
+// hold (a multiple of the 8 XCDs).
+template <int KDIM, int MODE>
+static void launch_gemm(const GemmArgs& a, const Tile* tiles, int* tile_count, const QFFN& routed,
+                        const QFFN& shared, int mt_rows, hipStream_t st) {
+    if (mt_rows == MT_SMALL)
+        hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_SMALL>), dim3(256 * PG<MT_SMALL>::WG_PER_CU),
+                           dim3(256), 0, st, a, tiles, tile_count, routed, shared);
+    else
+        hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_LARGE>), dim3(256 * PG<MT_LARGE>::WG_PER_CU),
+                           dim3(256), 0, st, a, tiles, tile_count, routed, shared);
+}
 
 // xh_ready: the fp16 activations are already in xh (the router wrote them).
 static void launch_gateup(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
@@ -832,8 +869,7 @@ static void launch_gateup(const uint16_t* x, int T, const int32_t* perm, const T
                            T, xh);
     GemmArgs gu = gemm_args(xh, (size_t)T * H * 2, T, perm);
     gu.hout = hbuf;
-    hipLaunchKernelGGL((grouped_gemm<H, GM_GATEUP>), dim3(GEMM_GRID), dim3(pg::THREADS), 0, st, gu,
-                       tiles, tile_count, routed, shared);
+    launch_gemm<H, GM_GATEUP>(gu, tiles, tile_count, routed, shared, gemm_tile_rows(T), st);
 }
 
 void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const Tile* tiles,
@@ -843,8 +879,7 @@ void launch_expert_prefill(const uint16_t* x, int T, const int32_t* perm, const 
     launch_gateup(x, T, perm, tiles, tile_count, routed, shared, xh, hbuf, false, st);
     GemmArgs dn = gemm_args(hbuf, (size_t)(TOPK + 1) * T * I * 2, T, perm);
     dn.dout32 = dout;
-    hipLaunchKernelGGL((grouped_gemm<I, GM_DOWN_F32>), dim3(GEMM_GRID), dim3(pg::THREADS), 0, st,
-                       dn, tiles, tile_count, routed, shared);
+    launch_gemm<I, GM_DOWN_F32>(dn, tiles, tile_count, routed, shared, gemm_tile_rows(T), st);
 }
 
 // Whole-layer prefill expert part: gate/up, then down writing fp16 rows of
@@ -859,8 +894,7 @@ void launch_expert_prefill_fused(const uint16_t* x, int T, const int32_t* perm, 
     dn.dout16 = d16;
     dn.wsorted = wsorted;
     dn.sg = sg;
-    hipLaunchKernelGGL((grouped_gemm<I, GM_DOWN_F16W>), dim3(GEMM_GRID), dim3(pg::THREADS), 0, st,
-                       dn, tiles, tile_count, routed, shared);
+    launch_gemm<I, GM_DOWN_F16W>(dn, tiles, tile_count, routed, shared, gemm_tile_rows(T), st);
 }
 
 }  // namespace moe

@@ -11,7 +11,7 @@
 //   perm_count      large T: per-chunk expert histograms       (grid: chunks)
 //   perm_scan       large T: column scans -> per-chunk bases   (one workgroup)
 //   perm_scatter    large T: stable scatter of every chunk     (grid: chunks)
-//   plan_tiles      row tiles of <= MT_ROWS rows per expert (expert 256 is the
+//   plan_tiles      row tiles of <= mt_rows rows per expert (expert 256 is the
 //                   shared expert over all T tokens), read by the expert
 //                   kernels from device memory so the host never needs the
 //                   expert counts.  The layer call plans inside perm_small /
@@ -27,7 +27,7 @@ constexpr int SMALL_MAX = 1024;    // entries handled by perm_small
 
 // Row tiles: routed expert e owns rows offsets[e] .. offsets[e+1]-1, the
 // shared expert (group 256) owns rows 8T .. 9T-1.  A group of n rows is cut
-// into nt = ceil(n/MT_ROWS) tiles of as equal a size as possible (the first
+// into nt = ceil(n/mt_rows) tiles of as equal a size as possible (the first
 // n % nt tiles get one row more), so no group leaves a small remainder tile.
 // At most `cap` tiles are written (offsets from moe_permute never need more
 // than max_tiles(T); malformed caller offsets cannot overrun the buffer).
@@ -46,19 +46,20 @@ __device__ inline Tile balanced_tile(int group, int r0, int n, int nt, int i) {
 // longest-first); within a class, routed experts in order, then the shared
 // expert.  Also zeroes the GEMMs' work counters.  Thread e of the 256-thread
 // block passes expert e's rows [o0, o1) (caller-provided offsets are clamped
-// into the routed row space [0, 8T)); scr: 4 ints of LDS.
-__device__ void plan_block(int o0, int o1, int T, int cap, Tile* __restrict__ tiles,
+// into the routed row space [0, 8T)); scr: 4 ints of LDS; mt_rows: tile
+// height, a multiple of 32 in [MT_MIN_ROWS, MT_ROWS].
+__device__ void plan_block(int o0, int o1, int T, int cap, int mt_rows, Tile* __restrict__ tiles,
                            int* __restrict__ tile_count, int* scr) {
     const int tid = threadIdx.x;
     const int lim = TOPK * T;
     const int r0 = min(max(o0, 0), lim);
     const int r1 = min(max(o1, r0), lim);
     const int n = r1 - r0;
-    const int nt = (n + MT_ROWS - 1) / MT_ROWS;
-    const int ns = (T + MT_ROWS - 1) / MT_ROWS;
+    const int nt = (n + mt_rows - 1) / mt_rows;
+    const int ns = (T + mt_rows - 1) / mt_rows;
     auto cls = [](const Tile& t) { return (t.nrows + 31) >> 5; };
     int before = 0;
-    for (int c = MT_ROWS / 32; c >= 1; --c) {
+    for (int c = mt_rows / 32; c >= 1; --c) {
         int mine = 0;
         for (int i = 0; i < nt; ++i) mine += cls(balanced_tile(tid, r0, n, nt, i)) == c;
         for (int i = tid; i < ns; i += 256) mine += cls(balanced_tile(E, lim, T, ns, i)) == c;
@@ -85,15 +86,17 @@ __device__ void plan_block(int o0, int o1, int T, int cap, Tile* __restrict__ ti
 }
 
 __global__ __launch_bounds__(256) void plan_tiles(const int32_t* __restrict__ offsets, int T,
-                                                  int cap, Tile* __restrict__ tiles,
+                                                  int cap, int mt_rows, Tile* __restrict__ tiles,
                                                   int* __restrict__ tile_count) {
     __shared__ int scr[4];
-    plan_block(offsets[threadIdx.x], offsets[threadIdx.x + 1], T, cap, tiles, tile_count, scr);
+    plan_block(offsets[threadIdx.x], offsets[threadIdx.x + 1], T, cap, mt_rows, tiles, tile_count,
+               scr);
 }
 
+// Tiles any plan of T tokens can need (at the smallest tile height).
 __host__ __device__ int max_tiles(int T) {
     const int n = TOPK * T;
-    return n / MT_ROWS + (n < E ? n : E) + (T + MT_ROWS - 1) / MT_ROWS;
+    return n / MT_MIN_ROWS + (n < E ? n : E) + (T + MT_MIN_ROWS - 1) / MT_MIN_ROWS;
 }
 
 __global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ ids, int n,
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ inv,
                                                   const float* __restrict__ wsrc,
                                                   float* __restrict__ wsorted, int T,
-                                                  Tile* __restrict__ tiles,
+                                                  int mt_rows, Tile* __restrict__ tiles,
                                                   int* __restrict__ tile_count) {
     __shared__ int hist[256];
     __shared__ int base[256];
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void perm_small(const int32_t* __restrict__ id
     base[tid] = off;
     __syncthreads();
     stable_scatter(ids, 0, n, base, wcnt, perm, inv, wsrc, wsorted);
-    if (tiles) plan_block(off, off + c, T, max_tiles(T), tiles, tile_count, scr);
+    if (tiles) plan_block(off, off + c, T, max_tiles(T), mt_rows, tiles, tile_count, scr);
 }
 
 __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int n,
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ id
 __global__ __launch_bounds__(256) void perm_scan(int nchunks, int32_t* __restrict__ chunk_counts,
                                                  int32_t* __restrict__ counts,
                                                  int32_t* __restrict__ offsets, int T,
-                                                 Tile* __restrict__ tiles,
+                                                 int mt_rows, Tile* __restrict__ tiles,
                                                  int* __restrict__ tile_count) {
     __shared__ int scr[4];
     const int tid = threadIdx.x;
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256) void perm_scan(int nchunks, int32_t* __restric
     counts[tid] = run;
     offsets[tid] = off;
     if (tid == 0) offsets[E] = total;
-    if (tiles) plan_block(off, off + run, T, max_tiles(T), tiles, tile_count, scr);
+    if (tiles) plan_block(off, off + run, T, max_tiles(T), mt_rows, tiles, tile_count, scr);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ ids, int n,
@@ -200,28 +203,31 @@ int perm_chunks(int T) { return (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK; }
 
 // wts/wsorted: optional (both or neither): wsorted[p] = wts[perm[p]], the
 // routing weight of each sorted position.
+int gemm_tile_rows(int T);
+
 // tiles/tile_count: optional (both or neither): also plan the row tiles
 // (and zero the GEMMs' work counters), as launch_plan would.
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st, const float* wts,
                     float* wsorted, Tile* tiles, int* tile_count) {
+    const int mt = gemm_tile_rows(T);
     const int n = TOPK * T;
     if (n <= SMALL_MAX) {
         hipLaunchKernelGGL(perm_small, dim3(1), dim3(256), 0, st, ids, n, counts, offsets, perm,
-                           inv, wts, wsorted, T, tiles, tile_count);
+                           inv, wts, wsorted, T, mt, tiles, tile_count);
         return;
     }
     const int nb = perm_chunks(T);
     hipLaunchKernelGGL(perm_count, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts);
     hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, st, nb, chunk_counts, counts, offsets, T,
-                       tiles, tile_count);
+                       mt, tiles, tile_count);
     hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts, offsets,
                        perm, inv, wts, wsorted);
 }
 
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st) {
-    hipLaunchKernelGGL(plan_tiles, dim3(1), dim3(256), 0, st, offsets, T, max_tiles(T), tiles,
-                       tile_count);
+    hipLaunchKernelGGL(plan_tiles, dim3(1), dim3(256), 0, st, offsets, T, max_tiles(T),
+                       gemm_tile_rows(T), tiles, tile_count);
 }
 
 }  // namespace moe
