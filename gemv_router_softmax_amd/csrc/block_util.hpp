@@ -100,34 +100,34 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t k) {
     return k;
 }
 
-__device__ __forceinline__ float fkey_inv(uint32_t k) {
-    return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
 // Top-8 of the 256 logits of one token, computed by one wave.  Lane l holds
-// experts 4l .. 4l+3 (v4).  Each lane first sorts its four candidates as
-// 64-bit values (order-preserving key of the logit, 255 - expert index), so
-// its best remaining candidate is always c[0] and equal logits are ordered
-// by the lower expert index.  Each of the eight rounds then takes the wave
-// maximum of the lanes' c[0] keys (row maxima by DPP, then the four rows
-// through scalar registers), the lowest lane holding it -- lower lanes hold
-// lower indices, so ties again go to the lower expert -- and shifts that
-// lane's list by one.  The code is branch-free: at one token this wave's
-// instruction count is the latency of the routing step.  Lane k < 8 ends
-// with the k-th selection (descending logit) and writes its id and weight;
-// the weights are the softmax over all experts renormalised over the eight,
-// i.e. exp(l - l_max) / sum_sel exp(l - l_max) (the full denominator
-// cancels).  Returns, in lane k < 8, the k-th selected expert.
+// experts 4l .. 4l+3 (v4).  Each candidate becomes a 32-bit key: the
+// order-preserving key of its logit with the low 8 bits replaced by
+// 255 - expert, so all 256 keys are distinct, a larger logit gives a larger
+// key, equal logits order by the lower expert index, and logits that agree
+// in all but the last 8 of their 32 key bits (a relative difference below
+// 2^-15) are ordered by index too -- far inside the 1e-3 near-tie margin
+// within which the selection may legitimately differ.  Each lane first
+// sorts its four keys, so its best remaining candidate is always c[0].
+// Each of the eight rounds takes the wave maximum of the c[0] keys (row
+// maxima by DPP, then the four rows through scalar registers); the key
+// itself names the expert and its unique holder shifts its list by one.
+// The code is branch-free: at one token this wave's instruction count is the
+// latency of the routing step.  Lane k < 8 ends with the k-th selection and
+// writes its id and weight; the weights are computed from the exact fp32
+// logits (fetched once from their lanes at the end) as the softmax over all
+// experts renormalised over the eight, i.e. exp(l - l_0) / sum_sel
+// exp(l - l_0), with l_0 the first selection's logit (the full denominator
+// and the reference logit cancel).  Returns, in lane k < 8, the k-th
+// selected expert.
 __device__ inline int wave_top8_v(float4v v4, int32_t* __restrict__ ids_out,
                                   float* __restrict__ w_out, int32_t* __restrict__ ids_lds) {
     const int lane = threadIdx.x & 63;
-    uint64_t c[4];
+    uint32_t c[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        c[j] = ((uint64_t)fkey(v4[j]) << 32) | (uint32_t)(255 - (4 * lane + j));
-    auto ce = [](uint64_t& x, uint64_t& y) {   // x >= y afterwards
-        const bool sw = x < y;
-        const uint64_t hi = sw ? y : x, lo = sw ? x : y;
+    for (int j = 0; j < 4; ++j) c[j] = (fkey(v4[j]) & 0xFFFFFF00u) | (uint32_t)(255 - (4 * lane + j));
+    auto ce = [](uint32_t& x, uint32_t& y) {   // x >= y afterwards
+        const uint32_t hi = max(x, y), lo = min(x, y);
         x = hi;
         y = lo;
     };
@@ -136,28 +136,29 @@ __device__ inline int wave_top8_v(float4v v4, int32_t* __restrict__ ids_out,
     ce(c[0], c[2]);
     ce(c[1], c[3]);
     ce(c[1], c[2]);
-    uint32_t kmax = 0, kmine = 0;
     int emine = 0;
 #pragma unroll
     for (int k = 0; k < TOPK; ++k) {
-        const uint32_t lm = (uint32_t)(c[0] >> 32);
-        const uint32_t rm = row16_max(lm);
+        const uint32_t rm = row16_max(c[0]);
         const uint32_t gm = max(max((uint32_t)__builtin_amdgcn_readlane((int)rm, 0),
                                     (uint32_t)__builtin_amdgcn_readlane((int)rm, 16)),
                                 max((uint32_t)__builtin_amdgcn_readlane((int)rm, 32),
                                     (uint32_t)__builtin_amdgcn_readlane((int)rm, 48)));
-        const int wl = (int)__builtin_ctzll(__ballot(lm == gm));
-        const int e = 255 - __builtin_amdgcn_readlane((int)(uint32_t)c[0], wl);
-        const bool me = lane == wl;
+        const int e = 255 - (int)(gm & 0xFFu);
+        const bool me = c[0] == gm;             // the unique holder of the maximum
         c[0] = me ? c[1] : c[0];
         c[1] = me ? c[2] : c[1];
         c[2] = me ? c[3] : c[2];
-        c[3] = me ? 0ull : c[3];
-        if (k == 0) kmax = gm;
-        kmine = lane == k ? gm : kmine;
+        c[3] = me ? 0u : c[3];
         emine = lane == k ? e : emine;
     }
-    const float ex = lane < TOPK ? expf(fkey_inv(kmine) - fkey_inv(kmax)) : 0.f;
+    // exact logit of this lane's selection: slot emine & 3 of lane emine >> 2
+    const int src = emine >> 2, sl = emine & 3;
+    const float s0 = __shfl(v4[0], src, WAVE), s1 = __shfl(v4[1], src, WAVE);
+    const float s2 = __shfl(v4[2], src, WAVE), s3 = __shfl(v4[3], src, WAVE);
+    const float lv = sl == 0 ? s0 : sl == 1 ? s1 : sl == 2 ? s2 : s3;
+    const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), 0));
+    const float ex = lane < TOPK ? expf(lv - l0) : 0.f;
     // sum over lanes 0..7 (pairs, quads, then the half-row mirror)
     float s = ex + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                        0, __builtin_bit_cast(int, ex), 0xB1, 0xF, 0xF, false));

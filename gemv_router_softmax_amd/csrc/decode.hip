@@ -372,6 +372,28 @@ static_assert(MOE_DECODE_T <= 8, "block_route: at most two tokens per wave");
 __device__ void block_route(const float* __restrict__ logits, float zv, int T, RouteRec& R,
                             int* mark) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (T == 1) {
+        // one token: its 8 experts are the active list; wave 0 sorts them by
+        // id (rank = number of selected ids below its own) and writes the
+        // list directly -- no marks, one barrier
+        if (wave == 0) {
+            const float4v v = reinterpret_cast<const float4v*>(logits)[lane];
+            const int e = wave_top8_v(v, R.ids[0], R.w[0], nullptr);
+            int rank = 0;
+#pragma unroll
+            for (int j = 0; j < TOPK; ++j) rank += __builtin_amdgcn_readlane(e, j) < e ? 1 : 0;
+            if (lane < TOPK) {
+                R.active[rank] = e;
+                R.tmask[rank] = 1u;
+            }
+            if (lane == 0) {
+                R.nact = TOPK;
+                R.sg[0] = 1.f / (1.f + expf(-zv));
+            }
+        }
+        pipe_barrier();
+        return;
+    }
     const int t0 = wave, t1 = wave + 4;
     float4v v0 = {}, v1 = {};
     if (t0 < T) v0 = reinterpret_cast<const float4v*>(logits + (size_t)t0 * E)[lane];
