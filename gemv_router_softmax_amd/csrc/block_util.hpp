@@ -181,34 +181,12 @@ __device__ inline void wave_top8(const float* __restrict__ lg, int32_t* __restri
     wave_top8_v(reinterpret_cast<const float4v*>(lg)[lane], ids_out, w_out, ids_lds);
 }
 
-// Sum eight per-lane values over the 64 lanes of a wave with 10 exchanges:
-// three halving steps leave lane l holding the 8-lane partial of value
-// ((l>>5)&1)*4 + ((l>>4)&1)*2 + ((l>>3)&1), three more finish the sum.
-__device__ __forceinline__ float wave_sum8(float v[8]) {
-    const int lane = threadIdx.x & 63;
-    const bool h32 = lane & 32, h16 = lane & 16, h8 = lane & 8;
-    float a[4], b[2], c;
+// Sums of eight per-lane values over the 64 lanes of a wave, as
+// wave-uniform values (wave_sum on each; the eight DPP chains are
+// independent, so they overlap) -- no LDS traffic.
+__device__ __forceinline__ void wave_sum8(const float v[8], float out[8]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float send = h32 ? v[i] : v[i + 4];
-        const float keep = h32 ? v[i + 4] : v[i];
-        a[i] = keep + __shfl_xor(send, 32, WAVE);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float send = h16 ? a[i] : a[i + 2];
-        const float keep = h16 ? a[i + 2] : a[i];
-        b[i] = keep + __shfl_xor(send, 16, WAVE);
-    }
-    {
-        const float send = h8 ? b[0] : b[1];
-        const float keep = h8 ? b[1] : b[0];
-        c = keep + __shfl_xor(send, 8, WAVE);
-    }
-    c += __shfl_xor(c, 4, WAVE);
-    c += __shfl_xor(c, 2, WAVE);
-    c += __shfl_xor(c, 1, WAVE);
-    return c;   // value index: 4*h32 + 2*h16 + h8
+    for (int i = 0; i < 8; ++i) out[i] = wave_sum(v[i]);
 }
 
 // s_waitcnt immediate: wait until at most n vector-memory operations of

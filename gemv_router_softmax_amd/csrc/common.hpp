@@ -192,10 +192,37 @@ __device__ __forceinline__ uint4v bf16x8_to_f16_slots(uint4v v) {
     return w;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// Lane exchanges that stay in the vector ALU (no LDS round trip).
+// dpp_f<CTL>: v of another lane of the same 16-lane row -- quad_perm
+// 1,0,3,2 (lane ^ 1), quad_perm 2,3,0,1 (lane ^ 2), row_half_mirror (lane
+// i <-> 7 - i within 8), row_mirror (lane i <-> 15 - i within 16).
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+template <int CTL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTL,
+                                                                 0xF, 0xF, false));
+}
+
+// Sum of v over each 16-lane row, in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    v += dpp_f<DPP_MIRROR>(v);
     return v;
+}
+
+// Sum of v over the wave, as a wave-uniform value: row sums by DPP, then
+// row_bcast:15 adds row 0 into row 1 and row 2 into row 3 (rows 0 and 2 add
+// the 0 of their masked-off lanes), row_bcast:31 adds rows 0-1 into rows
+// 2-3, and lane 63 holds the total.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142,
+                                                               0xA, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143,
+                                                               0xC, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -170,11 +170,12 @@ __global__ __launch_bounds__(256) void decode_gateup(const uint16_t* __restrict_
             for (int cc = 0; cc < 4; ++cc) d = dot8_codes(wq[i][cc], xp[cc], d);
             acc[i] = fmaf(s[i], d, b[i] * sx);
         }
-        const float r = wave_sum8(acc);                 // lane holds value (lane>>3)&7
-        const float u = __shfl_xor(r, 32, WAVE);        // partner: up row for a gate lane
-        const int vi = (lane >> 3) & 7;
-        if (vi < 4 && (lane & 7) == 0) {
-            const float g = r;
+        float tot[8];                                   // gate rows n0.., then up rows n0..
+        wave_sum8(acc, tot);
+        if (lane < 4) {
+            const int vi = lane;
+            const float g = vi == 0 ? tot[0] : vi == 1 ? tot[1] : vi == 2 ? tot[2] : tot[3];
+            const float u = vi == 0 ? tot[4] : vi == 1 ? tot[5] : vi == 2 ? tot[6] : tot[7];
             const float a = g / (1.f + expf(-g));
             const int n = n0 + vi;
             const float hb = bf16_to_f32(f32_to_bf16(a * u));
@@ -614,11 +615,13 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
             for (int cc = 0; cc < 4; ++cc) dd = dot8_biased(wq[i][cc], xs[cc], dd, mag);
             acc[i] = fmaf(s[i], dd - off, b[i] * sx);
         }
-        const float r = wave_sum8(acc);
-        const float u = __shfl_xor(r, 32, WAVE);
-        const int vi = (lane >> 3) & 7;
-        if (vi < 4 && (lane & 7) == 0) {
-            const float a = r / (1.f + expf(-r));
+        float tot[8];                                   // value i: gate row n0+i (i < 4),
+        wave_sum8(acc, tot);                            // up row n0+i-4 (i >= 4)
+        if (lane < 4) {
+            const int vi = lane;
+            const float g = vi == 0 ? tot[0] : vi == 1 ? tot[1] : vi == 2 ? tot[2] : tot[3];
+            const float u = vi == 0 ? tot[4] : vi == 1 ? tot[5] : vi == 2 ? tot[6] : tot[7];
+            const float a = g / (1.f + expf(-g));
             const float hb = bf16_to_f32(f32_to_bf16(a * u));
             const int n = n0 + vi;
             hout[((size_t)slot * T + t) * I + (n & ~7) + chunk_slot(n & 7)] =
@@ -738,11 +741,7 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __r
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_T; ++t) {
         if (t < T) {
-            float v = acc[t];
-            v += __shfl_xor(v, 8, WAVE);
-            v += __shfl_xor(v, 4, WAVE);
-            v += __shfl_xor(v, 2, WAVE);
-            v += __shfl_xor(v, 1, WAVE);
+            const float v = row16_sum(acc[t]);
             if (c == 0) yacc[wave][t][r] = v;
         }
     }
