@@ -73,10 +73,13 @@ def decode_chain(D, args):
     ws = moe.workspace(1)
 
     def chain():
+        # each layer also pulls the next layer's router matrix toward the
+        # caches (the last one: the first layer's, for the next token)
         cur = x0
         for l, Dl in enumerate(D):
             nxt = bufs[l % 2]
-            moe.moe_layer_forward_ex(cur, Dl, y, ws, residual_out=nxt)
+            moe.moe_layer_forward_ex(cur, Dl, y, ws, residual_out=nxt,
+                                     prefetch=D[(l + 1) % len(D)].w_router)
             cur = nxt
 
     x0.copy_(xs[0])
@@ -134,12 +137,13 @@ def decode_layer_timing(D, xs, reps, batch=8):
             moe.moe_probe_read(pad, sink)
             for l in range(l0, min(n, l0 + batch)):
                 nxt = bufs[l % 2]
+                pf = D[(l + 1) % n].w_router
                 if r == 0:          # warm-up pass
-                    moe.moe_layer_forward_ex(cur, D[l], y, ws, residual_out=nxt)
+                    moe.moe_layer_forward_ex(cur, D[l], y, ws, residual_out=nxt, prefetch=pf)
                 else:
                     a, b = pairs[k]
                     a.record()
-                    moe.moe_layer_forward_ex(cur, D[l], y, ws, residual_out=nxt)
+                    moe.moe_layer_forward_ex(cur, D[l], y, ws, residual_out=nxt, prefetch=pf)
                     b.record()
                     k += 1
                 cur = nxt

@@ -27,6 +27,7 @@ MOE_GROUP = 64
 MOE_T_MAX = 65536
 MOE_DECODE_T = 8
 MOE_DECODE_T_MAX = 32
+MOE_PREFETCH_MAX = 2097152
 
 MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1
@@ -57,7 +58,8 @@ class moe_layer(C.Structure):
 
 
 class moe_options(C.Structure):
-    _fields_ = [("path", C.c_int), ("residual_out", C.c_void_p)]
+    _fields_ = [("path", C.c_int), ("residual_out", C.c_void_p), ("prefetch", C.c_void_p),
+                ("prefetch_bytes", C.c_size_t)]
 
 
 _lib = None
@@ -285,10 +287,14 @@ def moe_combine(expert_out, inv_perm, topk_w, shared_gate, y, stream=None) -> No
 
 
 def moe_layer_forward_ex(x, layer: DeviceLayer, y, ws, path: int = MOE_PATH_AUTO,
-                         residual_out=None, stream=None) -> None:
+                         residual_out=None, prefetch=None, stream=None) -> None:
+    """prefetch: optional device tensor (e.g. the next layer's w_router) that
+    the decode path reads once to pull it toward the caches."""
     T = x.shape[0]
     wsp, wsn = _ws(ws)
-    opt = moe_options(path, _ptr(residual_out, "residual_out", _U16, (T, MOE_HIDDEN)))
+    pf = _ptr(prefetch, "prefetch")
+    opt = moe_options(path, _ptr(residual_out, "residual_out", _U16, (T, MOE_HIDDEN)), pf,
+                      0 if prefetch is None else prefetch.numel() * prefetch.element_size())
     _check("moe_layer_forward_ex", lib().moe_layer_forward_ex(
         _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.c),
         _ptr(y, "y", _U16, (T, MOE_HIDDEN)), wsp, wsn, _stream(stream), C.byref(opt)))

@@ -639,7 +639,8 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __restrict__ rec,
                      QFFN routed, QFFN shared, uint16_t* __restrict__ y,
-                     const uint16_t* __restrict__ x, uint16_t* __restrict__ res) {
+                     const uint16_t* __restrict__ x, uint16_t* __restrict__ res,
+                     const uint4v* __restrict__ pf, uint32_t pf_n) {
     __shared__ float yacc[4][MOE_DECODE_T][4];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane >> 4, c = lane & 15;
@@ -672,8 +673,13 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __r
     float acc[MOE_DECODE_T];
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_T; ++t) acc[t] = 0.f;
+    // the caller's prefetch range: one 16-byte unit per thread, issued after
+    // the first pass's loads (so no wait for those loads also waits for it),
+    // read back only at the very end
+    uint4v pfv = {0u, 0u, 0u, 0u};
+    const uint32_t pfi = blockIdx.x * 256u + threadIdx.x;
     // one pass: slots a0, a0+4, a0+8, a0+12 (a0 < nslots)
-    auto pass = [&](const int a0) {
+    auto pass = [&](const int a0, const bool first) {
         int ak[4], tf[4];
         uint32_t mk[4];
         uint4v dw[4], h0[4][4];
@@ -696,6 +702,7 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __r
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) h0[k][cc] = hr[cc];
         }
+        if (first && pfi < pf_n) pfv = pf[pfi];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -735,8 +742,8 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __r
     };
     // the first pass is peeled, so that its loads are not held up by waits
     // for the loop's previous iteration
-    pass(wave);
-    for (int a0 = wave + 16; a0 < nslots; a0 += 16) pass(a0);
+    pass(wave, true);
+    for (int a0 = wave + 16; a0 < nslots; a0 += 16) pass(a0, false);
     // reduce the 16 lanes of each row, then the four waves in a fixed order
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_T; ++t) {
@@ -752,13 +759,16 @@ void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __r
         y[o] = (uint16_t)yb;
         if (res) res[o] = (uint16_t)f32_to_bf16(bf16_to_f32(xin) + bf16_to_f32(yb));
     }
+    // keeps the prefetch load (T is never negative)
+    if (T < 0 && (pfv[0] ^ pfv[1] ^ pfv[2] ^ pfv[3]) == 0x9E3779B9u) y[0] = 0;
 }
 
 size_t route_rec_bytes() { return sizeof(DownRec); }
 
 void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
                                float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
-                               void* rec, uint16_t* y, uint16_t* res, hipStream_t st) {
+                               void* rec, uint16_t* y, uint16_t* res, const void* prefetch,
+                               size_t prefetch_bytes, hipStream_t st) {
     const QFFN routed = qffn_view(L.routed), shared = qffn_view(L.shared);
     DownRec* R = static_cast<DownRec*>(rec);
     (void)counter;
@@ -766,8 +776,10 @@ void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, flo
                        L.router_bias, L.w_shared_gate, logits, z, xh);
     hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T,
                        logits, z, R, routed, shared, hbuf);
+    static_assert((H / 4) * 256 * 16 == MOE_PREFETCH_MAX, "one prefetch unit per thread");
     hipLaunchKernelGGL(decode_down_dec, dim3(H / 4), dim3(256), 0, st, hbuf, T, R, routed,
-                       shared, y, x, res);
+                       shared, y, x, res, static_cast<const uint4v*>(prefetch),
+                       (uint32_t)(prefetch ? prefetch_bytes / 16 : 0));
 }
 
 // Zero the workspace's synchronisation words (a fill kernel, not a memset,

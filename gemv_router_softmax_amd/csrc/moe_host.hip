@@ -30,7 +30,8 @@ void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm
                                 uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
                                float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
-                               void* rec, uint16_t* y, uint16_t* res, hipStream_t st);
+                               void* rec, uint16_t* y, uint16_t* res, const void* prefetch,
+                               size_t prefetch_bytes, hipStream_t st);
 size_t route_rec_bytes();
 void launch_zero_words(unsigned* p, int n, hipStream_t st);
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
@@ -273,8 +274,11 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
     if (int rc = check_qffn(&layer->routed)) return rc;
     if (int rc = check_qffn(&layer->shared)) return rc;
     uint16_t* res = opt ? opt->residual_out : nullptr;
+    const void* pf = opt ? opt->prefetch : nullptr;
+    const size_t pf_bytes = pf ? opt->prefetch_bytes : 0;
+    if (pf && (pf_bytes % 16 != 0 || pf_bytes > MOE_PREFETCH_MAX)) return MOE_ERR_INVALID_ARG;
     if (!a16(x) || !a16(y) || !a16(ws) || !a16(layer->w_router) || !a16(layer->w_shared_gate) ||
-        (layer->router_bias && !a4(layer->router_bias)) || (res && !a16(res)))
+        (layer->router_bias && !a4(layer->router_bias)) || (res && !a16(res)) || (pf && !a16(pf)))
         return MOE_ERR_ALIGN;
     const WsLayout L = ws_layout(T);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -296,7 +300,7 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
         // the routing is recomputed inside the two expert kernels
         launch_layer_decode_small(x, T, *layer, at<float>(ws, L.logits), sg,
                                   at<uint16_t>(ws, L.xh), hbuf, at<unsigned>(ws, L.sync),
-                                  at<char>(ws, L.rec), y, res, st);
+                                  at<char>(ws, L.rec), y, res, pf, pf_bytes, st);
         return launch_status();
     }
     if (path == MOE_PATH_DECODE) {

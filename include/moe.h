@@ -116,7 +116,26 @@ typedef struct {
     int path;                       /* moe_path */
     uint16_t *residual_out;         /* if non-NULL: also write bf16(x + y) here,
                                        bf16 [T][2048] (the chain's next input) */
+    const void *prefetch;           /* if non-NULL: device bytes the call reads
+                                       once and discards, to pull them toward
+                                       the caches for a later call -- e.g. the
+                                       next layer's router matrix in a decode
+                                       chain (the next layer's first kernel
+                                       then reads it from the memory-side
+                                       cache).  Never written.  16-byte aligned;
+                                       prefetch_bytes a multiple of 16, at most
+                                       MOE_PREFETCH_MAX.  Read by the few-token
+                                       (decode) layer path; other paths ignore
+                                       it.  Prefetching the next layer's
+                                       weights while this one runs is "fusing
+                                       kernel chains" in "A Rust + Metal
+                                       Inference Engine for Qwen3.6-35B-A3B on
+                                       Apple Silicon", paragraph 5. */
+    size_t prefetch_bytes;
 } moe_options;
+
+#define MOE_PREFETCH_MAX 2097152    /* bytes: one 16-byte load per thread of the
+                                       decode down kernel (512 x 256) */
 
 /* Workspace bytes sufficient for ANY call below with this T (monotone in T).
  * Returns 0 for T < 0 or T > MOE_T_MAX. */

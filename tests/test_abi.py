@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(L):
 def test_header_constants_match_binding():
     src = open(HEADER).read()
     for name in ("MOE_HIDDEN", "MOE_INTER", "MOE_EXPERTS", "MOE_TOPK", "MOE_GROUP", "MOE_T_MAX",
-                 "MOE_DECODE_T", "MOE_DECODE_T_MAX"):
+                 "MOE_DECODE_T", "MOE_DECODE_T_MAX", "MOE_PREFETCH_MAX"):
         m = re.search(rf"#define {name} (\d+)", src)
         assert int(m.group(1)) == getattr(moe, name), name
 
@@ -138,6 +138,12 @@ def test_layer_forward_validation(L):
     assert f(A, 64, C.byref(lay), MIS, A, big, None, None) == ALIGN
     opt = moe.moe_options(moe.MOE_PATH_PREFILL, MIS)
     assert f(A, 64, C.byref(lay), A, A, big, None, C.byref(opt)) == ALIGN
+    # the prefetch range: 16-byte aligned, a multiple of 16 bytes, at most
+    # MOE_PREFETCH_MAX
+    for pf, nb, want in [(MIS, 1024, ALIGN), (A, 1000, INVALID),
+                         (A, moe.MOE_PREFETCH_MAX + 16, INVALID)]:
+        opt = moe.moe_options(moe.MOE_PATH_AUTO, None, pf, nb)
+        assert f(A, 64, C.byref(lay), A, A, big, None, C.byref(opt)) == want, (pf, nb)
     lb = _layer()
     lb.router_bias = A + 2
     assert f(A, 64, C.byref(lb), A, A, big, None, None) == ALIGN

@@ -206,3 +206,22 @@ def test_skewed_chunked_sampled(gpu):
     ids = np.concatenate([P.gpu_route(xd[c0:c0 + C], D)[0] for c0 in range(0, T, C)])
     ref, _ = P.oracle_layer_substituted(L, np.ascontiguousarray(x[rows]), ids[rows])
     P.assert_close(P.bf16_f64(yn[rows]), P.bf16_f64(ref.y), "skewed chunked y")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_decode_prefetch_changes_nothing(gpu, T):
+    """A decode layer call that also prefetches another layer's router matrix
+    (and, at T = 8, the largest allowed range) writes exactly the output and
+    residual of the call without it."""
+    D, D1 = P.dev_layer(0, 0), P.dev_layer(0, 1)
+    xd = moe.to_device_bits(synth.make_x(T, seed=15))
+    outs = []
+    big = torch.zeros(moe.MOE_PREFETCH_MAX, dtype=torch.uint8, device="cuda")
+    for pf in (None, D1.w_router, big):
+        y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+        res = torch.empty_like(y)
+        moe.moe_layer_forward_ex(xd, D, y, moe.workspace(T), residual_out=res, prefetch=pf)
+        torch.cuda.synchronize()
+        outs.append((moe.bits_to_numpy(y), moe.bits_to_numpy(res)))
+    for y, r in outs[1:]:
+        assert np.array_equal(y, outs[0][0]) and np.array_equal(r, outs[0][1])
