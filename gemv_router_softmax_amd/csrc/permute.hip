@@ -152,8 +152,9 @@ __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ id
 // One workgroup: chunk_counts[b][e] becomes the first position of chunk
 // b's entries of expert e relative to the expert's segment (the scatter adds
 // offsets[e]); counts and offsets are written, and the row tiles planned if
-// `tiles` is given.  Thread e reads its column 16 chunks at a time, so the
-// loads of a batch are in flight together.
+// `tiles` is given.  Thread e reads its column 64 chunks at a time (every
+// chunk of a 4096-token call at once), so the loads of a batch are in
+// flight together.
 __global__ __launch_bounds__(256) void perm_scan(int nchunks, int32_t* __restrict__ chunk_counts,
                                                  int32_t* __restrict__ counts,
                                                  int32_t* __restrict__ offsets, int T,
@@ -162,13 +163,13 @@ __global__ __launch_bounds__(256) void perm_scan(int nchunks, int32_t* __restric
     __shared__ int scr[4];
     const int tid = threadIdx.x;
     int run = 0;
-    for (int b0 = 0; b0 < nchunks; b0 += 16) {
-        int c[16];
+    for (int b0 = 0; b0 < nchunks; b0 += 64) {
+        int c[64];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 64; ++i)
             c[i] = b0 + i < nchunks ? chunk_counts[(size_t)(b0 + i) * 256 + tid] : 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 64; ++i) {
             if (b0 + i < nchunks) chunk_counts[(size_t)(b0 + i) * 256 + tid] = run;
             run += c[i];
         }
