@@ -14,7 +14,10 @@
 namespace moe {
 void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                   const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
-                  hipStream_t st, uint16_t* xh = nullptr);
+                  hipStream_t st, uint16_t* xh = nullptr, float* part = nullptr);
+// The router's K-split partials (up to 8 slices of T x E fp32) live in the
+// h rows, which nothing reads before the gate/up GEMM rewrites them.
+static_assert((size_t)(TOPK + 1) * I * 2 >= (size_t)8 * E * 4, "router partials fit the h rows");
 void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                          float* logits, hipStream_t st);
 void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,
@@ -198,7 +201,7 @@ int moe_route(const uint16_t* x, int T, const uint16_t* w_router, const float* r
                             at<int>(ws, L.tile_count), at<uint16_t>(ws, L.xh), st);
     } else {
         launch_route(x, T, w_router, router_bias, w_shared_gate, at<float>(ws, L.logits),
-                     topk_ids, topk_w, shared_gate, st);
+                     topk_ids, topk_w, shared_gate, st, nullptr, at<float>(ws, L.h));
     }
     return launch_status();
 }
@@ -320,7 +323,7 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
     // the top-8 kernel also writes the fp16 activations the grouped GEMM reads
     uint16_t* xh = at<uint16_t>(ws, L.xh);
     launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
-                 at<float>(ws, L.logits), ids, wts, sg, st, xh);
+                 at<float>(ws, L.logits), ids, wts, sg, st, xh, at<float>(ws, L.h));
     float* wsorted = at<float>(ws, L.wsorted);
     launch_permute(ids, T, counts, offsets, perm, inv, at<int32_t>(ws, L.chunk_counts), st, wts,
                    wsorted, tiles, tcount);

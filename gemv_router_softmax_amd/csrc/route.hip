@@ -11,8 +11,11 @@
 //   route_logits_tile   larger T: the logits as a small GEMM, one workgroup
 //                       per 32 tokens x 128 experts, bf16 MFMA 32x32x16 (fp32
 //                       accumulation of exact bf16 products) on tiles moved
-//                       into LDS by a 7-stage direct-load ring.
-//   route_topk          one wave per token: 4 logits per lane, eight arg-max
+//                       into LDS by a 7-stage direct-load ring; below a
+//                       few thousand tokens K is split over up to 8
+//                       workgroup slices to fill the chip.
+//   route_topk          one wave per token (summing the K slices, if any):
+//                       4 logits per lane, eight arg-max
 //                       rounds over the fp32 logits (ties -> lower expert
 //                       index), softmax weights renormalised over the
 //                       selected eight, and the shared-expert gate
@@ -105,6 +108,12 @@ __device__ __forceinline__ void rl_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buf
     }
 }
 
+// KS > 1 splits K over blockIdx.z: slice z covers supersteps z*NU/KS ..
+// (z+1)*NU/KS - 1 and writes its unbiased partial logits to
+// logits[(z*T + t)*E + e]; route_topk sums the slices in order and adds the
+// bias.  A few hundred tokens make only T/32 x 2 workgroups, so the split is
+// what fills the chip there.
+template <int KS>
 __global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restrict__ x, int T,
                                                          const uint16_t* __restrict__ wr,
                                                          const float* __restrict__ bias,
@@ -117,11 +126,14 @@ __global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restr
     const int e0 = blockIdx.y * RL_EXP;
     const __amdgpu_buffer_rsrc_t rx = rt_rsrc(x, (uint32_t)((size_t)T * H * 2));
     const __amdgpu_buffer_rsrc_t rw = rt_rsrc(wr, (uint32_t)(E * H * 2));
-    constexpr int NU = H / 64;    // 32 supersteps
+    constexpr int NU = H / 64 / KS;   // supersteps of this K slice (32 in all)
+    static_assert((H / 64) % KS == 0, "K slices");
+    const int u0 = blockIdx.z * NU;
 
     static_assert(RL_TOK % 8 == 0, "x rows must fill whole load instructions");
 #pragma unroll
-    for (int u = 0; u < RL_STAGES - 1; ++u) rl_issue(rx, rw, t0, e0, wave, lane, u, smem + u * RL_STAGE);
+    for (int u = 0; u < RL_STAGES - 1; ++u)
+        if (u < NU) rl_issue(rx, rw, t0, e0, wave, lane, u0 + u, smem + u * RL_STAGE);
 
     float16v acc = (float16v)0.f;
     const int ra = l32, rb = RL_TOK + wave * 32 + l32;     // operand rows in the stage
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restr
         // with the stage the refill below overwrites (superstep u - 1)
         pipe_barrier();
         if (u + RL_STAGES - 1 < NU)
-            rl_issue(rx, rw, t0, e0, wave, lane, u + RL_STAGES - 1,
+            rl_issue(rx, rw, t0, e0, wave, lane, u0 + u + RL_STAGES - 1,
                      smem + ((u + RL_STAGES - 1) % RL_STAGES) * RL_STAGE);
         const uint8_t* st = smem + (u % RL_STAGES) * RL_STAGE;
         // all eight operand reads first, then the four MFMAs
@@ -161,19 +173,37 @@ __global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restr
     }
     // element i: token 8*(i/4) + 4g + i%4, expert e0 + 32w + l32
     const int e = e0 + wave * 32 + l32;
-    const float bb = bias ? bias[e] : 0.f;
+    const float bb = (KS == 1 && bias) ? bias[e] : 0.f;
+    float* out = logits + (size_t)blockIdx.z * T * E;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int t = t0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (t < T) logits[(size_t)t * E + e] = acc[i] + bb;
+        const float v = acc[i];
+        if (t < T) out[(size_t)t * E + e] = v + bb;
     }
+}
+
+// K slices of the router GEMM at T tokens: doubled while the grid stays
+// within 256 workgroups, at most RL_KS_MAX.
+constexpr int RL_KS_MAX = 8;
+static int route_ksplit(int T) {
+    const int tiles = (T + RL_TOK - 1) / RL_TOK * (E / RL_EXP);
+    int ks = 1;
+    while (ks < RL_KS_MAX && tiles * ks * 2 <= 256) ks *= 2;
+    return ks;
 }
 
 // grid: ceil(T/4) blocks of 4 waves; wave -> token: top-8 (wave_top8),
 // renormalised weights and the shared-expert gate; optionally (the fused
 // layer) also the fp16 copy of the token's row in chunk-slot order that the
 // grouped GEMM reads (xh), which saves the conversion kernel.
-__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits,
+//
+// part / nks: K-split partial logits [nks][T][E] of route_logits_tile<KS>
+// (nks > 1): summed here in slice order, plus the bias, and also stored to
+// logits.
+__global__ __launch_bounds__(256) void route_topk(float* __restrict__ logits,
+                                                  const float* __restrict__ part, int nks,
+                                                  const float* __restrict__ bias,
                                                   const uint16_t* __restrict__ x,
                                                   const uint16_t* __restrict__ wsg, int T,
                                                   int32_t* __restrict__ ids,
@@ -185,7 +215,19 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
     if (t >= T) return;
     const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
     const uint4v x0 = xr[0], x1 = xr[1], x2 = xr[2], x3 = xr[3];
-    wave_top8(logits + (size_t)t * E, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
+    if (part) {
+        float4v v = reinterpret_cast<const float4v*>(part + (size_t)t * E)[lane];
+        for (int k = 1; k < nks; ++k)
+            v += reinterpret_cast<const float4v*>(part + ((size_t)k * T + t) * E)[lane];
+        if (bias) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] += bias[lane * 4 + j];
+        }
+        reinterpret_cast<float4v*>(logits + (size_t)t * E)[lane] = v;
+        wave_top8_v(v, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
+    } else {
+        wave_top8(logits + (size_t)t * E, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
+    }
     const uint4v* gr = reinterpret_cast<const uint4v*>(wsg) + lane * 4;
     float z = dot8_bf16(x0, gr[0]) + dot8_bf16(x1, gr[1]) + dot8_bf16(x2, gr[2]) +
               dot8_bf16(x3, gr[3]);
@@ -206,18 +248,33 @@ void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const flo
         hipLaunchKernelGGL(route_logits_gemv, dim3(E / 4), dim3(256), 0, st, x, T, wr, bias,
                            logits);
     } else {
-        hipLaunchKernelGGL(route_logits_tile, dim3((T + RL_TOK - 1) / RL_TOK, E / RL_EXP),
+        hipLaunchKernelGGL(route_logits_tile<1>, dim3((T + RL_TOK - 1) / RL_TOK, E / RL_EXP),
                            dim3(256), 0, st, x, T, wr, bias, logits);
     }
 }
 
-// xh: optional fp16 activation copy.
+// xh: optional fp16 activation copy.  part: optional scratch for K-split
+// partial logits, RL_KS_MAX * T * E floats, free for the duration of the
+// call (without it the router GEMM runs unsplit).
 void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                   const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
-                  hipStream_t st, uint16_t* xh) {
-    launch_route_logits(x, T, wr, bias, logits, st);
-    hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, x, wsg, T, ids,
-                       wts, sg, xh);
+                  hipStream_t st, uint16_t* xh, float* part) {
+    const int ks = (part && T > 32) ? route_ksplit(T) : 1;
+    if (ks == 1) {
+        launch_route_logits(x, T, wr, bias, logits, st);
+        hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits,
+                           (const float*)nullptr, 0, (const float*)nullptr, x, wsg, T, ids, wts,
+                           sg, xh);
+        return;
+    }
+    const dim3 grid((T + RL_TOK - 1) / RL_TOK, E / RL_EXP, ks);
+    switch (ks) {
+        case 2: hipLaunchKernelGGL(route_logits_tile<2>, grid, dim3(256), 0, st, x, T, wr, bias, part); break;
+        case 4: hipLaunchKernelGGL(route_logits_tile<4>, grid, dim3(256), 0, st, x, T, wr, bias, part); break;
+        default: hipLaunchKernelGGL(route_logits_tile<8>, grid, dim3(256), 0, st, x, T, wr, bias, part); break;
+    }
+    hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, (const float*)part,
+                       ks, bias, x, wsg, T, ids, wts, sg, xh);
 }
 
 }  // namespace moe

@@ -10,7 +10,9 @@ import parity as P
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T", [1, 8, 16, 32, 33, 100, 129, 512, 4096])
+# (33..512 tokens run the router GEMM in 8 K slices, 1024 in 4, 2048 in 2,
+# 4096 unsplit)
+@pytest.mark.parametrize("T", [1, 8, 16, 32, 33, 100, 129, 512, 1024, 2048, 4096])
 def test_route_uniform(gpu, T):
     P.say(f"route T={T} seed=0 layer=0")
     L, D = P.host_layer(0, 0), P.dev_layer(0, 0)
@@ -30,7 +32,7 @@ def test_route_uniform(gpu, T):
         assert np.all(np.diff(ids[t])[eq] > 0), "exact ties must go to the lower index"
 
 
-@pytest.mark.parametrize("T", [7, 4096])
+@pytest.mark.parametrize("T", [7, 512, 4096])
 def test_route_skewed_bias(gpu, T):
     P.say(f"route skewed T={T}")
     L, D = P.host_layer(0, 0, True), P.dev_layer(0, 0, True)
