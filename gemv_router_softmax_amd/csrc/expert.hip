@@ -155,8 +155,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 //       64 banks.
 //   B   [256 columns][2 pieces of 16 B]: piece p of column C sits at slot
 //       p ^ ((C >> 3) & 1), so a 128-bit read by 16 lanes is conflict free.
-//   S, Bi [256 columns] dwords holding the fp16 scale (bias) of groups
-//       2*floor(kc/2) and 2*floor(kc/2)+1 (chunk kc uses half kc & 1).
+//   S, Bi [256 columns] dwords holding the fp16 scale (bias) of groups kc
+//       and kc+1, loaded by even chunks kc only: the odd chunk's loads are
+//       out-of-range stand-ins (its S and Bi are never read) and its
+//       operands use the upper halves, kept in registers by read_b.
 // K order inside a chunk: lane half g of MFMA step s covers k-piece 4g+s.
 
 struct GemmArgs {
@@ -349,8 +351,12 @@ __device__ __forceinline__ void issue_chunk(const GSrc<MTR>& g, int kc, __amdgpu
 #pragma unroll
     for (int i = 0; i < pg::B_LOADS; ++i)
         load_lds<16>(g.rq, stage + pg::A_BYTES + (wave * pg::B_LOADS + i) * 1024, g.b[i], kc * 32);
-    load_lds<4>(g.rs, stage + pg::A_BYTES + pg::B_BYTES + wave * 256, g.s, (kc & ~1) * 2);
-    load_lds<4>(g.rb, stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + wave * 256, g.s, (kc & ~1) * 2);
+    // one scale and one bias dword covers chunks kc & ~1 and kc | 1: the odd
+    // chunk's loads are out-of-range stand-ins (no memory access), and its
+    // operands reuse the even chunk's dwords (read_b)
+    const uint32_t so = (kc & 1) ? pg::OOB : g.s;
+    load_lds<4>(g.rs, stage + pg::A_BYTES + pg::B_BYTES + wave * 256, so, (kc & ~1) * 2);
+    load_lds<4>(g.rb, stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + wave * 256, so, (kc & ~1) * 2);
 }
 
 // MFMA: v_mfma_f32_32x32x16_f16 (32 rows x 32 columns x 16 k).  Lane l
@@ -375,8 +381,16 @@ struct BFrag {
     half2v s[2], b[2];    // fp16 scale / bias, splat
 };
 
+// Even chunks read the scale and bias dwords from the stage and keep their
+// upper halves (the next chunk's group) in `carry`; odd chunks, whose stage
+// holds no scales, take them from there.  Every call site's chunk parity is
+// a compile-time constant after unrolling, so the branch folds away.
+struct SCarry {
+    half2v s[2], b[2];
+};
+
 template <bool GATEUP, int MTR>
-__device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc) {
+__device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc, SCarry& carry) {
     using pg = PG<MTR>;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int l32 = lane & 31, g = lane >> 5;
@@ -385,11 +399,18 @@ __device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc) {
     for (int nt = 0; nt < 2; ++nt) {
         const int C = gemm_col<GATEUP>(wave, nt, l32);
         B.w[nt] = *reinterpret_cast<const uint4v*>(stage + pg::A_BYTES + C * 32 + 16 * (g ^ ((C >> 3) & 1)));
-        const uint32_t sd = *reinterpret_cast<const uint32_t*>(stage + pg::A_BYTES + pg::B_BYTES + C * 4);
-        const uint32_t bd =
-            *reinterpret_cast<const uint32_t*>(stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + C * 4);
-        B.s[nt] = splat_h((uint16_t)((kc & 1) ? sd >> 16 : sd));
-        B.b[nt] = splat_h((uint16_t)((kc & 1) ? bd >> 16 : bd));
+        if (kc & 1) {
+            B.s[nt] = carry.s[nt];
+            B.b[nt] = carry.b[nt];
+        } else {
+            const uint32_t sd = *reinterpret_cast<const uint32_t*>(stage + pg::A_BYTES + pg::B_BYTES + C * 4);
+            const uint32_t bd =
+                *reinterpret_cast<const uint32_t*>(stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + C * 4);
+            B.s[nt] = splat_h((uint16_t)sd);
+            B.b[nt] = splat_h((uint16_t)bd);
+            carry.s[nt] = splat_h((uint16_t)(sd >> 16));
+            carry.b[nt] = splat_h((uint16_t)(bd >> 16));
+        }
     }
     return B;
 }
@@ -631,7 +652,8 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (float16v)0.f;
 
     half8 a_cur[NMT], bf_cur[2];
-    BFrag B = read_b<GATEUP, MTR>(lds + (gc % pg::STAGES) * pg::STAGE, 0);
+    SCarry carry;
+    BFrag B = read_b<GATEUP, MTR>(lds + (gc % pg::STAGES) * pg::STAGE, 0, carry);
     read_a<NMT, MTR>(lds + (gc % pg::STAGES) * pg::STAGE, 0, a_cur);
     dequant_step(B, 0, bf_cur);
 
@@ -672,7 +694,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         half8 a_nx[NMT], bf_nx[2];
         if (more) {
             const uint8_t* sn = lds + ((gc + 1) % pg::STAGES) * pg::STAGE;
-            B = read_b<GATEUP, MTR>(sn, c + 1);
+            B = read_b<GATEUP, MTR>(sn, c + 1, carry);
             read_a<NMT, MTR>(sn, 0, a_nx);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -727,8 +749,14 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
             chunk(c, next(c));
         }
     }
-    // main: one basic block per chunk
-    for (int c = HEAD; c < MAIN; ++c) chunk(c, own(c));
+    // main: one basic block per two chunks (an even number of them, HEAD odd,
+    // so each call's chunk parity is a constant)
+    static_assert(MAIN <= HEAD || ((MAIN - HEAD) % 2 == 0 && HEAD % 2 == 1), "main chunk pairs");
+    for (int i = 0; i < (MAIN - HEAD) / 2; ++i) {
+        const int c = HEAD + 2 * i;
+        chunk(c, own(c));
+        chunk(c + 1, own(c + 1));
+    }
     if (MAIN >= HEAD) make_next();
     // tail: refills from the next item
 #pragma unroll
