@@ -4,16 +4,15 @@
 // Inference Engine for Qwen3.6-35B-A3B on Apple Silicon", paragraph 4).
 //
 // Work is described by the row-tile list built on the device (plan_tiles):
-// tile = (expert or shared group, first row, row count <= 128).
+// tile = (expert or shared group, first row, row count <= MT_ROWS).
 //
-// Decode (few tokens; the gate/up GEMV and the fused down+combine kernel
-// live in decode.hip):
-//   decode_down    16 lanes per output row (16 B of codes each), 4 rows per
-//                  wave; exact codes through v_dot2_f32_bf16 (dot8_codes),
-//                  group scale/bias applied once per lane; writes the fp32
-//                  expert rows of the split expert-FFN call.
-//
-// Prefill (grouped GEMM on MFMA): expert_gemm below.
+//   decode_down    split interface, few tokens: 16 lanes per output row
+//                  (16 B of codes each), 4 rows per wave; exact codes
+//                  through v_dot2_f32_f16 (dot8_codes), group scale/bias
+//                  applied once per lane; writes fp32 expert rows.  (The
+//                  gate/up GEMV it follows and the fused whole-layer decode
+//                  kernels live in decode.hip.)
+//   grouped_gemm   prefill: persistent grouped GEMM on fp16 MFMA (below).
 #include "block_util.hpp"
 
 namespace moe {
@@ -477,6 +476,22 @@ __device__ __forceinline__ void lane_exchange_fence() {
     asm volatile("" ::: "memory");
 }
 
+// Output buffer resources are based at the item's first row and cover only
+// its rows, so every store offset is below MT_ROWS rows whatever T is (the
+// whole fp32 output of the largest call, 9 * 65536 rows of 8 KB, is beyond
+// the 32-bit range of a buffer resource).
+static_assert((uint64_t)MT_ROWS * H * 4 < (1ull << 31), "per-item output range");
+static_assert((uint64_t)(TOPK + 1) * MOE_T_MAX * I * 2 < (1ull << 32),
+              "A rows of the down GEMM (h) are addressed with 32-bit buffer offsets");
+static_assert((uint64_t)MOE_T_MAX * H * 2 < (1ull << 32),
+              "A rows of the gate/up GEMM (x) are addressed with 32-bit buffer offsets");
+
+template <typename P>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t item_rows(P* base, const GItem& m, int row_elems) {
+    return buf_rsrc(base + (size_t)m.row0 * row_elems,
+                    (uint32_t)m.nrows * (uint32_t)row_elems * (uint32_t)sizeof(P));
+}
+
 // Accumulator element i of a lane lies in staged half hr = i/8 of the
 // m-tile (rows 16*hr .. 16*hr+15), at staged row 8*((i/4)&1) + 4g + i%4.
 template <int MODE, int NMT, int MTR>
@@ -486,10 +501,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
     using pg = PG<MTR>;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int l32 = lane & 31, g = lane >> 5;
-    const int T = A.T;
     const int Rl = lane >> 2;           // staged row read back by this lane
     if constexpr (MODE == GM_GATEUP) {
-        const __amdgpu_buffer_rsrc_t rh = buf_rsrc(A.hout, (uint32_t)((size_t)(TOPK + 1) * T * I * 2));
+        const __amdgpu_buffer_rsrc_t rh = item_rows(A.hout, m, I);
         uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [16][32] fp16, slot order
 #pragma unroll
         for (int mt = 0; mt < pg::NMT_MAX; ++mt)
@@ -513,12 +527,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                     lane_exchange_fence();
                     const int R = mt * 32 + hr * 16 + Rl;
                     if (R < m.nrows)
-                        off = (uint32_t)(((m.row0 + R) * I + m.nb * 128 + wave * 32 + (lane & 3) * 8) * 2);
+                        off = (uint32_t)((R * I + m.nb * 128 + wave * 32 + (lane & 3) * 8) * 2);
                 }
                 __builtin_amdgcn_raw_buffer_store_b128(v, rh, off, 0, 0);
             }
     } else if constexpr (MODE == GM_DOWN_F16W) {
-        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(A.dout16, (uint32_t)((size_t)(TOPK + 1) * T * H * 2));
+        const __amdgpu_buffer_rsrc_t rd = item_rows(A.dout16, m, H);
         uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [16][32] fp16
 #pragma unroll
         for (int mt = 0; mt < pg::NMT_MAX; ++mt)
@@ -545,14 +559,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                     lane_exchange_fence();
                         const int R = mt * 32 + hr * 16 + Rl;
                         if (R < m.nrows)
-                            off = (uint32_t)(((size_t)(m.row0 + R) * H + m.nb * 256 + wave * 64 + nt * 32 +
-                                              (lane & 3) * 8) * 2);
+                            off = (uint32_t)((R * H + m.nb * 256 + wave * 64 + nt * 32 + (lane & 3) * 8) * 2);
                     }
                     __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
                 }
             }
     } else {
-        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(A.dout32, (uint32_t)((size_t)(TOPK + 1) * T * H * 4));
+        const __amdgpu_buffer_rsrc_t rd = item_rows(A.dout32, m, H);
         float* st = reinterpret_cast<float*>(stg);          // [16][16] fp32
 #pragma unroll
         for (int mt = 0; mt < pg::NMT_MAX; ++mt)
@@ -577,8 +590,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                     lane_exchange_fence();
                             const int R = mt * 32 + hr * 16 + Rl;
                             if (R < m.nrows)
-                                off = (uint32_t)(((size_t)(m.row0 + R) * H + m.nb * 256 + wave * 64 + nt * 32 +
-                                                  ch * 16 + (lane & 3) * 4) * 4);
+                                off = (uint32_t)((R * H + m.nb * 256 + wave * 64 + nt * 32 + ch * 16 +
+                                                  (lane & 3) * 4) * 4);
                         }
                         __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
                     }
