@@ -39,6 +39,8 @@ MUTANTS = {
     12: "combine drops the shared expert",
     13: "bf16 rounding breaks ties away from zero",
     14: "combine reads the routed rows through a transposed slot index",
+    15: "greedy selection breaks ties toward the higher token",
+    16: "embedding lookup reads the neighbouring row",
 }
 
 
@@ -110,6 +112,13 @@ class LayerOut:
     gap: np.ndarray
 
 
+@dataclass
+class GreedyOut:
+    token: np.ndarray    # int32 [T]
+    logits: np.ndarray   # float64 [T, V] (before the fp32 rounding)
+    gap: np.ndarray      # float64 [T]: selected fp32 logit - best other fp32 logit
+
+
 class Oracle:
     def __init__(self, path: Optional[str] = None):
         self.path = path or build()
@@ -141,6 +150,10 @@ class Oracle:
         L.oracle_layer_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            vp, vp, vp, vp]
         L.oracle_layer_forward.restype = i32
+        L.oracle_lm_head_argmax.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_lm_head_argmax.restype = i32
+        L.oracle_embed.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.oracle_embed.restype = i32
         self.mutant = L.oracle_mutant()
 
     def threads(self) -> int:
@@ -252,6 +265,32 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle_layer_forward failed ({rc})")
         return LayerOut(y, y32, ids, w, sg, gap)
+
+
+    # ---- greedy decode step
+    def lm_head_argmax(self, x: np.ndarray, w_head: np.ndarray) -> GreedyOut:
+        x = np.ascontiguousarray(x, np.uint16)
+        w_head = np.ascontiguousarray(w_head, np.uint16)
+        T, H = x.shape
+        V = w_head.shape[0]
+        assert w_head.shape == (V, H)
+        token = np.empty((T,), np.int32)
+        logits = np.empty((T, V), np.float64)
+        gap = np.empty((T,), np.float64)
+        rc = self.lib.oracle_lm_head_argmax(T, H, V, _p(x), _p(w_head), _p(token), _p(logits),
+                                            _p(gap))
+        if rc:
+            raise ValueError(f"oracle_lm_head_argmax failed ({rc})")
+        return GreedyOut(token, logits, gap)
+
+    def embed(self, token: np.ndarray, emb: np.ndarray) -> np.ndarray:
+        token = np.ascontiguousarray(token, np.int32)
+        emb = np.ascontiguousarray(emb, np.uint16)
+        V, H = emb.shape
+        x = np.empty((token.shape[0], H), np.uint16)
+        if self.lib.oracle_embed(token.shape[0], H, V, _p(token), _p(emb), _p(x)):
+            raise ValueError("oracle_embed: token outside the table")
+        return x
 
 
 _DEFAULT: Optional[Oracle] = None

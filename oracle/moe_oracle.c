@@ -492,3 +492,73 @@ int oracle_layer_forward(const oracle_dims *d, int T, const uint16_t *x,
     free(ids); free(w); free(sg); free(counts); free(offsets); free(perm); free(inv); free(out);
     return rc;
 }
+
+/* ------------------------------------------------------ greedy decode step */
+
+/* Greedy next-token selection after the last layer: the token whose
+ * output-head logit is largest, kept on the GPU for the next decode step
+ * ("Perplexity Open-Sources Lily ...", section "Generation has a different
+ * bottleneck").  The pages give no output head; the reading taken: a bf16
+ * head w_head [V][H] applied to the bf16 hidden state x [T][H],
+ *   logit[t][v] = fp32( x[t] . w_head[v] )   (double accumulation, one rounding)
+ *   token[t]    = argmax_v logit[t][v], ties to the lower v.
+ * Optional outputs: logits [T][V] (double, before the fp32 rounding) and
+ * gap[t] = the selected fp32 logit minus the best other token's fp32 logit. */
+int oracle_lm_head_argmax(int T, int H, int V, const uint16_t *x, const uint16_t *w_head,
+                          int32_t *token, double *logits, double *gap)
+{
+    if (T < 0 || H <= 0 || V <= 0)
+        return 1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int t = 0; t < T; ++t) {
+        double *xv = malloc(sizeof(double) * H);
+        float *l32 = malloc(sizeof(float) * V);
+        if (!xv || !l32) { bad = 1; free(xv); free(l32); continue; }
+        for (int k = 0; k < H; ++k)
+            xv[k] = oracle_bf16_to_double(x[(int64_t)t * H + k]);
+        for (int v = 0; v < V; ++v) {
+            double acc = 0.0;
+            for (int k = 0; k < H; ++k)
+                acc += xv[k] * oracle_bf16_to_double(w_head[(int64_t)v * H + k]);
+            l32[v] = (float)acc;
+            if (logits)
+                logits[(int64_t)t * V + v] = acc;
+        }
+        int best = 0;
+        for (int v = 1; v < V; ++v) {
+#if ORACLE_MUTANT == 15
+            if (l32[v] >= l32[best])                            /* tie -> higher token */
+#else
+            if (l32[v] > l32[best])
+#endif
+                best = v;
+        }
+        token[t] = best;
+        if (gap) {
+            double other = -INFINITY;
+            for (int v = 0; v < V; ++v)
+                if (v != best && (double)l32[v] > other)
+                    other = (double)l32[v];
+            gap[t] = (double)l32[best] - other;
+        }
+        free(xv); free(l32);
+    }
+    return bad ? 2 : 0;
+}
+
+/* The next step's input rows: x[t] = emb[token[t]] (bf16 [V][H] table).
+ * Returns nonzero on a token outside 0..V-1. */
+int oracle_embed(int T, int H, int V, const int32_t *token, const uint16_t *emb, uint16_t *x)
+{
+    for (int t = 0; t < T; ++t) {
+        int v = token[t];
+        if (v < 0 || v >= V)
+            return 1;
+#if ORACLE_MUTANT == 16
+        v = (v + 1) % V;                                        /* neighbouring row */
+#endif
+        memcpy(x + (int64_t)t * H, emb + (int64_t)v * H, sizeof(uint16_t) * H);
+    }
+    return 0;
+}

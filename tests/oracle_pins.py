@@ -339,4 +339,55 @@ def pin_chunking_is_exact(o):
     assert np.array_equal(whole.y, parts)
 
 
+# --------------------------------------------------------- greedy decode step
+
+def _head(V, H, seed):
+    rng = np.random.default_rng(seed)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((3, H), dtype=np.float32))
+    w = synth.f32_to_bf16_bits(0.02 * rng.standard_normal((V, H), dtype=np.float32))
+    return x, w
+
+
+def pin_lm_head_argmax_vs_numpy(o):
+    """Logits against a float64 numpy product; the selection against
+    np.argmax over the same logits rounded to float32 (first maximum, i.e.
+    the lower token on an exact tie)."""
+    x, w = _head(1000, 128, 31)
+    r = o.lm_head_argmax(x, w)
+    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double().numpy()
+    wf = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).double().numpy()
+    ref = xf @ wf.T
+    assert np.allclose(r.logits, ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r.token, np.argmax(ref.astype(np.float32), axis=1))
+    l32 = np.sort(ref.astype(np.float32), axis=1)
+    assert np.allclose(r.gap, l32[:, -1].astype(np.float64) - l32[:, -2], rtol=0, atol=0)
+
+
+def pin_lm_head_ties_to_lower_token(o):
+    """The best row duplicated at a lower and at a higher token: the lower
+    copy wins; a one-hot input picks the row with the largest entry there."""
+    x, w = _head(300, 64, 32)
+    best = o.lm_head_argmax(x[:1], w).token[0]
+    w2 = w.copy()
+    w2[best // 2] = w[best]
+    w2[min(best + 7, 299)] = w[best]
+    assert o.lm_head_argmax(x[:1], w2).token[0] == best // 2
+    onehot = np.zeros((1, 64), np.uint16)
+    onehot[0, 9] = synth.f32_to_bf16_bits(np.float32(1.0))
+    col = torch.from_numpy(w[:, 9].copy().view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert o.lm_head_argmax(onehot, w).token[0] == int(np.argmax(col))
+
+
+def pin_embed_gather(o):
+    rng = np.random.default_rng(33)
+    emb = rng.integers(0, 1 << 16, size=(50, 24), dtype=np.uint32).astype(np.uint16)
+    tok = np.array([0, 49, 7, 7, 23], np.int32)
+    assert np.array_equal(o.embed(tok, emb), emb[tok])
+    try:
+        o.embed(np.array([50], np.int32), emb)
+        raise AssertionError("a token outside the table was accepted")
+    except ValueError:
+        pass
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
