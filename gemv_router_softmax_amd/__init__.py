@@ -27,16 +27,15 @@ MOE_GROUP = 64
 MOE_T_MAX = 65536
 MOE_DECODE_T = 8
 MOE_DECODE_T_MAX = 32
-MOE_PREFETCH_MAX = 2097152
 
 MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1
 MOE_PATH_PREFILL = 2
 
 # Every symbol include/moe.h declares.
-EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_status_string", "moe_route",
-           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
-           "moe_probe_read", "moe_probe_copy")
+EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_route", "moe_permute",
+           "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
+           "moe_chain_forward", "moe_router_transpose", "moe_probe_read", "moe_probe_copy")
 
 
 class MoeError(RuntimeError):
@@ -54,12 +53,13 @@ class moe_qffn(C.Structure):
 
 class moe_layer(C.Structure):
     _fields_ = [("w_router", C.c_void_p), ("router_bias", C.c_void_p),
-                ("w_shared_gate", C.c_void_p), ("routed", moe_qffn), ("shared", moe_qffn)]
+                ("w_shared_gate", C.c_void_p), ("routed", moe_qffn), ("shared", moe_qffn),
+                ("w_router_t", C.c_void_p)]
 
 
 class moe_options(C.Structure):
-    _fields_ = [("path", C.c_int), ("residual_out", C.c_void_p), ("prefetch", C.c_void_p),
-                ("prefetch_bytes", C.c_size_t)]
+    _fields_ = [("path", C.c_int), ("residual_out", C.c_void_p), ("route_ids", C.c_void_p),
+                ("route_w", C.c_void_p), ("route_sg", C.c_void_p)]
 
 
 _lib = None
@@ -77,8 +77,6 @@ def lib() -> C.CDLL:
     vp, i32, sz = C.c_void_p, C.c_int, C.c_size_t
     L.moe_workspace_bytes.argtypes = [i32]
     L.moe_workspace_bytes.restype = sz
-    L.moe_workspace_init.argtypes = [vp, sz, vp]
-    L.moe_workspace_init.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = C.c_char_p
     L.moe_route.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -89,6 +87,9 @@ def lib() -> C.CDLL:
     L.moe_layer_forward.argtypes = [vp, i32, C.POINTER(moe_layer), vp, vp, sz, vp]
     L.moe_layer_forward_ex.argtypes = [vp, i32, C.POINTER(moe_layer), vp, vp, sz, vp,
                                        C.POINTER(moe_options)]
+    L.moe_chain_forward.argtypes = [vp, i32, C.POINTER(moe_layer), i32, vp, vp, vp, sz, vp,
+                                    C.POINTER(moe_options)]
+    L.moe_router_transpose.argtypes = [vp, vp, vp]
     L.moe_probe_read.argtypes = [vp, sz, vp, vp]
     L.moe_probe_copy.argtypes = [vp, vp, sz, vp]
     for fn in EXPORTS:
@@ -211,9 +212,13 @@ class DeviceLayer:
         self.shared = DeviceQFFN(layer.shared, 1, device, layout)
         assert tuple(self.w_router.shape) == (MOE_EXPERTS, MOE_HIDDEN)
         assert tuple(self.w_shared_gate.shape) == (MOE_HIDDEN,)
+        # the transposed router matrix a chain's previous layer reads
+        self.w_router_t = torch.empty((MOE_HIDDEN, MOE_EXPERTS), dtype=torch.int16, device=device)
+        moe_router_transpose(self.w_router, self.w_router_t)
         self.c = moe_layer(self.w_router.data_ptr(),
                            None if self.router_bias is None else self.router_bias.data_ptr(),
-                           self.w_shared_gate.data_ptr(), self.routed.c, self.shared.c)
+                           self.w_shared_gate.data_ptr(), self.routed.c, self.shared.c,
+                           self.w_router_t.data_ptr())
 
     @property
     def nbytes(self) -> int:
@@ -221,21 +226,25 @@ class DeviceLayer:
                 self.w_shared_gate.numel() * 2)
 
 
-def workspace(T: int, device="cuda", stream=None) -> torch.Tensor:
-    """Device workspace sized by moe_workspace_bytes(T) (allocated by torch)
-    and prepared with moe_workspace_init."""
-    ws = torch.empty(max(moe_workspace_bytes(T), 256), dtype=torch.uint8, device=device)
-    moe_workspace_init(ws, stream)
-    return ws
-
-
-def moe_workspace_init(ws: torch.Tensor, stream=None) -> None:
-    wsp, wsn = _ws(ws)
-    _check("moe_workspace_init", lib().moe_workspace_init(wsp, wsn, _stream(stream)))
+def workspace(T: int, device="cuda") -> torch.Tensor:
+    """Device workspace of moe_workspace_bytes(T) bytes (allocated by torch;
+    it needs no preparation)."""
+    return torch.empty(max(moe_workspace_bytes(T), 256), dtype=torch.uint8, device=device)
 
 
 def _ws(ws: torch.Tensor):
     return _ptr(ws, "ws", torch.uint8), ws.numel()
+
+
+def _route_out(route_out, T: int, nlayers: Optional[int] = None):
+    """(ids, w, sg) device tensors -> their pointers, shapes checked."""
+    if route_out is None:
+        return None, None, None
+    ids, w, sg = route_out
+    lead = () if nlayers is None else (nlayers,)
+    return (_ptr(ids, "route ids", torch.int32, lead + (T, MOE_TOPK)),
+            _ptr(w, "route w", torch.float32, lead + (T, MOE_TOPK)),
+            _ptr(sg, "route sg", torch.float32, lead + (T,)))
 
 
 def moe_route(x, w_router, router_bias, w_shared_gate, topk_ids, topk_w, shared_gate, ws,
@@ -267,7 +276,7 @@ def moe_expert_ffn(x, layer: DeviceLayer, expert_offsets, perm, expert_out, ws,
                    path: int = MOE_PATH_AUTO, stream=None) -> None:
     T = x.shape[0]
     wsp, wsn = _ws(ws)
-    opt = moe_options(path, None)
+    opt = moe_options(path)
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.routed.c), C.byref(layer.shared.c),
         _ptr(expert_offsets, "expert_offsets", torch.int32, (MOE_EXPERTS + 1,)),
@@ -287,17 +296,44 @@ def moe_combine(expert_out, inv_perm, topk_w, shared_gate, y, stream=None) -> No
 
 
 def moe_layer_forward_ex(x, layer: DeviceLayer, y, ws, path: int = MOE_PATH_AUTO,
-                         residual_out=None, prefetch=None, stream=None) -> None:
-    """prefetch: optional device tensor (e.g. the next layer's w_router) that
-    the decode path reads once to pull it toward the caches."""
+                         residual_out=None, route_out=None, stream=None) -> None:
+    """route_out: optional (ids int32 [T,8], w fp32 [T,8], sg fp32 [T]) device
+    tensors that receive the routing the call used."""
     T = x.shape[0]
     wsp, wsn = _ws(ws)
-    pf = _ptr(prefetch, "prefetch")
-    opt = moe_options(path, _ptr(residual_out, "residual_out", _U16, (T, MOE_HIDDEN)), pf,
-                      0 if prefetch is None else prefetch.numel() * prefetch.element_size())
+    ri, rw, rs = _route_out(route_out, T)
+    opt = moe_options(path, _ptr(residual_out, "residual_out", _U16, (T, MOE_HIDDEN)), ri, rw, rs)
     _check("moe_layer_forward_ex", lib().moe_layer_forward_ex(
         _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.c),
         _ptr(y, "y", _U16, (T, MOE_HIDDEN)), wsp, wsn, _stream(stream), C.byref(opt)))
+
+
+class LayerChain:
+    """A host array of layer descriptors for moe_chain_forward (kept alive
+    with the layers it points to)."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        self.c = (moe_layer * len(self.layers))(*[L.c for L in self.layers])
+
+    def __len__(self):
+        return len(self.layers)
+
+
+def moe_chain_forward(x, chain: LayerChain, x_out, ws, y_layers=None, path: int = MOE_PATH_AUTO,
+                      route_out=None, stream=None) -> None:
+    """x_out = the residual stream after every layer of the chain;
+    y_layers: optional bf16 [nlayers, T, 2048] per-layer outputs; route_out:
+    optional (ids [nlayers,T,8], w [nlayers,T,8], sg [nlayers,T])."""
+    T, n = x.shape[0], len(chain)
+    wsp, wsn = _ws(ws)
+    ri, rw, rs = _route_out(route_out, T, n)
+    opt = moe_options(path, None, ri, rw, rs)
+    _check("moe_chain_forward", lib().moe_chain_forward(
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, chain.c, n,
+        _ptr(x_out, "x_out", _U16, (T, MOE_HIDDEN)),
+        _ptr(y_layers, "y_layers", _U16, (n, T, MOE_HIDDEN)), wsp, wsn, _stream(stream),
+        C.byref(opt)))
 
 
 def moe_layer_forward(x, layer: DeviceLayer, y, ws, stream=None) -> None:
@@ -306,6 +342,12 @@ def moe_layer_forward(x, layer: DeviceLayer, y, ws, stream=None) -> None:
     _check("moe_layer_forward", lib().moe_layer_forward(
         _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.c),
         _ptr(y, "y", _U16, (T, MOE_HIDDEN)), wsp, wsn, _stream(stream)))
+
+
+def moe_router_transpose(w_router, w_router_t, stream=None) -> None:
+    _check("moe_router_transpose", lib().moe_router_transpose(
+        _ptr(w_router, "w_router", _U16, (MOE_EXPERTS, MOE_HIDDEN)),
+        _ptr(w_router_t, "w_router_t", _U16, (MOE_HIDDEN, MOE_EXPERTS)), _stream(stream)))
 
 
 def moe_probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

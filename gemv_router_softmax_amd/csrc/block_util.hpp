@@ -101,17 +101,16 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t k) {
 }
 
 // Top-8 of the 256 logits of one token, computed by one wave.  Lane l holds
-// experts 4l .. 4l+3 (v4).  Each candidate becomes a 32-bit key: the
-// order-preserving key of its logit with the low 8 bits replaced by
-// 255 - expert, so all 256 keys are distinct, a larger logit gives a larger
-// key, equal logits order by the lower expert index, and logits that agree
-// in all but the last 8 of their 32 key bits (a relative difference below
-// 2^-15) are ordered by index too -- far inside the 1e-3 near-tie margin
-// within which the selection may legitimately differ.  Each lane first
-// sorts its four keys, so its best remaining candidate is always c[0].
-// Each of the eight rounds takes the wave maximum of the c[0] keys (row
-// maxima by DPP, then the four rows through scalar registers); the key
-// itself names the expert and its unique holder shifts its list by one.
+// experts 4l .. 4l+3 (v4).  Candidates are ordered by (logit descending,
+// expert ascending) -- exactly the selection order of the definition, for
+// every finite logit: each logit becomes its order-preserving 32-bit key
+// (distinct logits give distinct keys; -0 and +0 the same key) and equal keys
+// are ordered by expert index.  Each lane first sorts its four (key, expert)
+// pairs in that order, so its best remaining candidate is always c[0].  Each
+// of the eight rounds takes the wave maximum of the c[0] keys (row maxima by
+// DPP, then the four rows through scalar registers); the lowest lane holding
+// that key (a ballot) holds the lowest expert among equal logits, since lane
+// l's experts are all below lane l+1's, and that lane shifts its list by one.
 // The code is branch-free: at one token this wave's instruction count is the
 // latency of the routing step.  Lane k < 8 ends with the k-th selection and
 // writes its id and weight; the weights are computed from the exact fp32
@@ -124,18 +123,24 @@ __device__ inline int wave_top8_v(float4v v4, int32_t* __restrict__ ids_out,
                                   float* __restrict__ w_out, int32_t* __restrict__ ids_lds) {
     const int lane = threadIdx.x & 63;
     uint32_t c[4];
+    int id[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = (fkey(v4[j]) & 0xFFFFFF00u) | (uint32_t)(255 - (4 * lane + j));
-    auto ce = [](uint32_t& x, uint32_t& y) {   // x >= y afterwards
-        const uint32_t hi = max(x, y), lo = min(x, y);
-        x = hi;
-        y = lo;
+    for (int j = 0; j < 4; ++j) {
+        c[j] = fkey(v4[j]);
+        id[j] = 4 * lane + j;
+    }
+    // compare-exchange: (c[x], id[x]) ahead of (c[y], id[y]) afterwards
+    auto ce = [&](int x, int y) {
+        const bool sw = c[y] > c[x] || (c[y] == c[x] && id[y] < id[x]);
+        const uint32_t kx = sw ? c[y] : c[x], ky = sw ? c[x] : c[y];
+        const int ix = sw ? id[y] : id[x], iy = sw ? id[x] : id[y];
+        c[x] = kx; c[y] = ky; id[x] = ix; id[y] = iy;
     };
-    ce(c[0], c[1]);
-    ce(c[2], c[3]);
-    ce(c[0], c[2]);
-    ce(c[1], c[3]);
-    ce(c[1], c[2]);
+    ce(0, 1);
+    ce(2, 3);
+    ce(0, 2);
+    ce(1, 3);
+    ce(1, 2);
     int emine = 0;
 #pragma unroll
     for (int k = 0; k < TOPK; ++k) {
@@ -144,12 +149,17 @@ __device__ inline int wave_top8_v(float4v v4, int32_t* __restrict__ ids_out,
                                     (uint32_t)__builtin_amdgcn_readlane((int)rm, 16)),
                                 max((uint32_t)__builtin_amdgcn_readlane((int)rm, 32),
                                     (uint32_t)__builtin_amdgcn_readlane((int)rm, 48)));
-        const int e = 255 - (int)(gm & 0xFFu);
-        const bool me = c[0] == gm;             // the unique holder of the maximum
+        const uint64_t holders = __ballot(c[0] == gm);
+        const int L = (int)__builtin_ctzll(holders);     // lowest holder: the lowest expert
+        const int e = __builtin_amdgcn_readlane(id[0], L);
+        const bool me = lane == L;
         c[0] = me ? c[1] : c[0];
         c[1] = me ? c[2] : c[1];
         c[2] = me ? c[3] : c[2];
         c[3] = me ? 0u : c[3];
+        id[0] = me ? id[1] : id[0];
+        id[1] = me ? id[2] : id[1];
+        id[2] = me ? id[3] : id[2];
         emine = lane == k ? e : emine;
     }
     // exact logit of this lane's selection: slot emine & 3 of lane emine >> 2

@@ -275,24 +275,117 @@ __global__ __launch_bounds__(256) void decode_down_combine(
 }
 
 // ---------------------------------------------------------------------
-// Few-token layer (T <= MOE_DECODE_T): three kernels.
+// Few-token layer (T <= MOE_DECODE_T).
 //
-//   route_logits_dec   the 256 expert logits (one wave per expert row), the
-//                      shared-gate logits and the fp16 copy of x; the LAST
-//                      router workgroup to finish (a counter in the
-//                      workspace -- no workgroup ever waits) computes every
-//                      token's top-8, the weights, the shared gate and the
-//                      active-expert list once, into a small route record,
-//                      and re-arms the counter.
+// A layer that follows another layer of a chain is two kernels; a layer on
+// its own (or the first of a chain) adds the router kernel in front:
+//
+//   route_logits_dec   the 256 expert logits and the shared-gate logit of
+//                      each token (one wave per router row), stored as 64-bit
+//                      fixed point (below), and the fp16 copy of x in
+//                      chunk-slot order;
 //   decode_gateup_dec  slot 0 = the shared expert (needs no routing), slot
 //                      a >= 1 = the a-th active routed expert, which every
-//                      routed workgroup finds by running the selection on
-//                      the logits itself; workgroup (0, 0) also publishes the
-//                      down record.
-//   decode_down_dec    every active expert for 4 output rows, combine with the
-//                      routing weights and the shared gate, residual add.
+//                      routed workgroup finds by running the top-8 selection
+//                      itself on the logits (block_route); workgroup (0, 0)
+//                      publishes the down record.  h rows are compact: the T
+//                      shared rows, then every (expert, token) pair in
+//                      ascending expert order, 9T rows in all;
+//   decode_down_dec    32 output rows per workgroup over every slot, with
+//                      the h rows staged in LDS; combine with the routing
+//                      weights and the shared gate, residual add.  Inside a
+//                      chain it also writes the next layer's fp16
+//                      activations and adds its share of the next layer's
+//                      router logits.
+//
+// Router logits in 64-bit fixed point: a down workgroup of a chain holds 32
+// entries of the next layer's input, so it can form its partial router sums
+// for all 257 logits itself (fp32, in a fixed order) and add round(p * 2^32)
+// to the next layer's accumulators with integer atomics.  Integer addition is
+// associative, so the sum does not depend on the order in which the 64
+// workgroups' atomics land: the routing stays deterministic.  This takes the
+// router kernel and one kernel boundary off every chained layer -- the decode
+// chain fused across layers ("A Rust + Metal Inference Engine for
+// Qwen3.6-35B-A3B on Apple Silicon", paragraph 5).
+//
 // Ids read back from the record are clamped, so a corrupted record cannot
 // send a load outside the weights.
+
+// Fixed-point logit accumulators: a set is ACC_COPIES copies of [T]
+// [ACC_STRIDE] int64 words (words 0..255 of a token: the expert logits
+// without the router bias, word 256: the shared-gate logit); a logit is the
+// sum over the copies.
+//
+// The down kernel's shape (decode_down_dec): DN_RG row groups of four rows x
+// DN_SG slot groups of waves per workgroup, DN_WG workgroups.  Its
+// workgroups add their partial router sums to ACC_COPIES copies of the
+// accumulators (DN_WG / ACC_COPIES workgroups meet on one address), which
+// the gate/up kernel adds up.  Measured on the 40-layer T = 1 chain, us per
+// layer (rows per workgroup / workgroups / copies): 8 / 256 / 8: 14.75;
+// 8 / 256 / 4: 15.02; 8 / 256 / 2: 15.80; 4 / 512 / 8: 15.00; 4 / 512 / 4:
+// 15.93; 4 / 512 / 1: 23.4; 16 / 128 / 4: 16.56; 16 / 128 / 1: 17.76.  More
+// atomics on one address cost the down kernel more than reading more copies
+// costs the gate/up kernel, down to 32 workgroups per address.  (The
+// compile-time knobs exist for such sweeps.)
+#ifndef MOE_DN_RG
+#define MOE_DN_RG 2
+#endif
+#ifndef MOE_DN_SG
+#define MOE_DN_SG 4
+#endif
+#ifndef MOE_ACC_COPIES
+#define MOE_ACC_COPIES 8
+#endif
+constexpr int DN_RG = MOE_DN_RG;
+constexpr int DN_SG = MOE_DN_SG;
+constexpr int DN_WAVES = DN_RG * DN_SG;
+constexpr int DN_ROWS = 4 * DN_RG;
+constexpr int DN_WG = H / DN_ROWS;
+constexpr int DN_SPW = (1 + TOPK + DN_SG - 1) / DN_SG;   // slots per wave per pass
+constexpr int ACC_COPIES = MOE_ACC_COPIES;
+static_assert(DN_WG % ACC_COPIES == 0, "accumulator copies");
+static_assert(64 * DN_WAVES <= 1024, "workgroup size");
+
+constexpr int ACC_N = E + 1;
+typedef __attribute__((address_space(3))) void* dn_lds_t;
+constexpr int ACC_STRIDE = 264;                 // 32-byte aligned per token
+constexpr double ACC_ONE = 4294967296.0;        // 2^32
+static_assert(ACC_STRIDE >= ACC_N && ACC_STRIDE % 4 == 0, "accumulator layout");
+
+__device__ __forceinline__ long long acc_fix(float v) {
+    // |v| < 2^30 keeps 257 tokens' worth of sums far from the int64 range;
+    // larger (never finite-sensible) values are clamped
+    const double d = fmin(fmax((double)v * ACC_ONE, -0x1p62), 0x1p62);
+    return (long long)__builtin_elementwise_rint(d);
+}
+__device__ __forceinline__ float acc_val(long long q) { return (float)((double)q * (1.0 / ACC_ONE)); }
+
+// Logits of experts 4l .. 4l+3 of token t for lane l (the sum over the
+// ACC_COPIES accumulator copies of T tokens each, all loads issued
+// together), plus the router bias.
+__device__ __forceinline__ float4v load_logits4(const long long* __restrict__ acc, int T,
+                                                const float* __restrict__ bias, int t, int lane) {
+    typedef long long ll2 __attribute__((ext_vector_type(2)));
+    ll2 pa[ACC_COPIES], pb[ACC_COPIES];
+#pragma unroll
+    for (int c = 0; c < ACC_COPIES; ++c) {
+        const ll2* p = reinterpret_cast<const ll2*>(acc + ((size_t)c * T + t) * ACC_STRIDE + 4 * lane);
+        pa[c] = p[0];
+        pb[c] = p[1];
+    }
+    ll2 a = pa[0], b = pb[0];
+#pragma unroll
+    for (int c = 1; c < ACC_COPIES; ++c) {
+        a += pa[c];
+        b += pb[c];
+    }
+    float4v v = {acc_val(a[0]), acc_val(a[1]), acc_val(b[0]), acc_val(b[1])};
+    if (bias) {     // (4-byte aligned: four scalar loads)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] += bias[4 * lane + j];
+    }
+    return v;
+}
 
 // The routing of up to MOE_DECODE_T tokens, in LDS of the gate/up kernel.
 struct RouteRec {
@@ -313,6 +406,8 @@ constexpr int DEC_SLOTS = 1 + MOE_DECODE_T * TOPK;
 struct DownRec {
     int slot_e[128];                   // expert of each slot; [127]: the slot count
     uint32_t slot_m[128];              // tokens of each slot (bit t)
+    int slot_h[128];                   // first h row of each slot (its tokens' rows
+                                       // follow in ascending token order)
     float coef[MOE_DECODE_T][128];     // token t's weight for slot a (the shared gate for
                                        // slot 0; 0 where the token did not pick the expert)
 };
@@ -370,15 +465,15 @@ __device__ __forceinline__ const GLOBAL_AS T* gexpert(const GLOBAL_AS T* p, int 
 // (tid < T), loaded by the caller.  The waves exchange only LDS, so the
 // barriers here leave the caller's outstanding global loads in flight.
 static_assert(MOE_DECODE_T <= 8, "block_route: at most two tokens per wave");
-__device__ void block_route(const float* __restrict__ logits, float zv, int T, RouteRec& R,
-                            int* mark) {
+__device__ void block_route(const long long* __restrict__ acc, const float* __restrict__ bias,
+                            float zv, int T, RouteRec& R, int* mark) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (T == 1) {
         // one token: its 8 experts are the active list; wave 0 sorts them by
         // id (rank = number of selected ids below its own) and writes the
         // list directly -- no marks, one barrier
         if (wave == 0) {
-            const float4v v = reinterpret_cast<const float4v*>(logits)[lane];
+            const float4v v = load_logits4(acc, T, bias, 0, lane);
             const int e = wave_top8_v(v, R.ids[0], R.w[0], nullptr);
             int rank = 0;
 #pragma unroll
@@ -397,8 +492,8 @@ __device__ void block_route(const float* __restrict__ logits, float zv, int T, R
     }
     const int t0 = wave, t1 = wave + 4;
     float4v v0 = {}, v1 = {};
-    if (t0 < T) v0 = reinterpret_cast<const float4v*>(logits + (size_t)t0 * E)[lane];
-    if (t1 < T) v1 = reinterpret_cast<const float4v*>(logits + (size_t)t1 * E)[lane];
+    if (t0 < T) v0 = load_logits4(acc, T, bias, t0, lane);
+    if (t1 < T) v1 = load_logits4(acc, T, bias, t1, lane);
     mark[tid] = 0;
     pipe_barrier();
     if (t0 < T) {
@@ -436,6 +531,15 @@ __device__ void block_route(const float* __restrict__ logits, float zv, int T, R
     pipe_barrier();
 }
 
+// First h row of slot a >= 1 (the shared slot 0 has rows 0 .. T-1): T plus
+// the token counts of the active experts before it.  One wave, wave-uniform.
+__device__ __forceinline__ int slot_hrow(const RouteRec& R, int a, int T) {
+    if (T == 1) return a;
+    const int lane = threadIdx.x & 63;
+    const int n = lane < a - 1 ? __builtin_popcount(R.tmask[lane]) : 0;
+    return T + (int)wave_sum((float)n);      // at most 64 small integers: exact
+}
+
 constexpr int NRB = 64;   // router workgroups (4 experts each, one per wave)
 
 // grid (NRB + 1 + T): blocks < NRB: logits of 4 experts each (one expert
@@ -445,10 +549,8 @@ constexpr int NRB = 64;   // router workgroups (4 experts each, one per wave)
 // kernel ends as soon as its dot products are written.
 __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restrict__ x, int T,
                                                         const uint16_t* __restrict__ wr,
-                                                        const float* __restrict__ bias,
                                                         const uint16_t* __restrict__ wsg,
-                                                        float* __restrict__ logits,
-                                                        float* __restrict__ z,
+                                                        long long* __restrict__ acc,
                                                         uint16_t* __restrict__ xh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
@@ -498,13 +600,9 @@ __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restri
                         }
                     }
                     s = wave_sum(s);
-                    if (lane == 0) {
-                        if (b < NRB) {
-                            const int e = b * (E / NRB) + wave * (E / NRB / 4) + k;
-                            logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
-                        } else {
-                            z[t] = s;
-                        }
+                    if (lane < ACC_COPIES) {    // copy 0 holds the logit, the others zero
+                        const int e = b < NRB ? b * (E / NRB) + wave * (E / NRB / 4) + k : E;
+                        acc[((size_t)lane * T + t) * ACC_STRIDE + e] = lane == 0 ? acc_fix(s) : 0;
                     }
                 }
             }
@@ -515,14 +613,21 @@ __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restri
 // grid (1 + 8T, I/16).  Slot 0 is the shared expert; slot s > 0 is the
 // s-th active routed expert (ascending id), which each routed workgroup
 // finds by running the selection itself on the logits (block_route); the
-// workgroup (0, 0) publishes the route record for decode_down_dec.  h rows
-// are indexed (slot * T + t), fp16, chunk-slot order.
+// workgroup (0, 0) publishes the route record for decode_down_dec (and, if
+// asked, the routing itself: ids, weights and shared gates).  Workgroup
+// (0, 1) clears the next layer's logit accumulators (acc_next, if any),
+// which the down kernel then adds to.  h rows (fp16, chunk-slot order) are
+// compact, see slot_hrow.
 __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restrict__ xh, int T,
-                                                         const float* __restrict__ logits,
-                                                         const float* __restrict__ z,
+                                                         const long long* __restrict__ acc,
+                                                         const float* __restrict__ bias,
+                                                         long long* __restrict__ acc_next,
                                                          DownRec* __restrict__ rec,
                                                          QFFN routed, QFFN shared,
-                                                         uint16_t* __restrict__ hout) {
+                                                         uint16_t* __restrict__ hout,
+                                                         int32_t* __restrict__ ids_out,
+                                                         float* __restrict__ w_out,
+                                                         float* __restrict__ sg_out) {
     __shared__ RouteRec R;
     __shared__ int mark[E];
     const int slot = blockIdx.x;
@@ -539,8 +644,20 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) x0[cc] = xr[cc];
     }
-    const float zv = (int)threadIdx.x < T ? z[threadIdx.x] : 0.f;
-    if (slot > 0 || blockIdx.y == 0) block_route(logits, zv, T, R, mark);
+    float zv = 0.f;
+    {
+        const int tz = min((int)threadIdx.x, T - 1);
+        long long zq[ACC_COPIES];
+#pragma unroll
+        for (int c = 0; c < ACC_COPIES; ++c) zq[c] = acc[((size_t)c * T + tz) * ACC_STRIDE + E];
+#pragma unroll
+        for (int c = 1; c < ACC_COPIES; ++c) zq[0] += zq[c];
+        zv = acc_val(zq[0]);
+    }
+    if (acc_next && slot == 0 && blockIdx.y == 1)
+        for (int i = threadIdx.x; i < ACC_COPIES * T * ACC_STRIDE; i += 256) acc_next[i] = 0;
+    if (slot > 0 || blockIdx.y == 0) block_route(acc, bias, zv, T, R, mark);
+    int hrow = 0;
     if (slot == 0 && blockIdx.y == 0) {
         const int nact = min(max(R.nact, 0), TOPK * T);
         const int a = threadIdx.x;
@@ -558,13 +675,26 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
                 rec->coef[t][a] = cf;
             }
         }
+        // first h rows: a per-thread serial sum (one workgroup, off the
+        // other workgroups' critical path)
+        if (a <= nact) {
+            int hb = a == 0 ? 0 : T;
+            for (int s = 0; s + 1 < a; ++s) hb += __builtin_popcount(R.tmask[s]);
+            rec->slot_h[a] = hb;
+        }
         if (a == 127) rec->slot_e[127] = nact + 1;
+        if (ids_out && a < T * TOPK) {
+            ids_out[a] = R.ids[a / TOPK][a % TOPK];
+            w_out[a] = R.w[a / TOPK][a % TOPK];
+        }
+        if (sg_out && a < T) sg_out[a] = R.sg[a];
     }
     if (slot > 0) {
         const int nact = min(max(R.nact, 0), TOPK * T);
         if (slot - 1 >= nact) return;
         e = min(max(R.active[slot - 1], 0), E - 1);
         mask = R.tmask[slot - 1] & tall;
+        hrow = slot_hrow(R, slot, T);
     }
     const GUPtrs q = pick(slot == 0, ps, pr);
     e = __builtin_amdgcn_readfirstlane(e);
@@ -607,16 +737,16 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
             xs[cc] = prescale_pairs(xp[cc]);
             off = pair_offset(xs[cc], off);
         }
-        float acc[8];
+        float acc8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float dd = 0.f;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) dd = dot8_biased(wq[i][cc], xs[cc], dd, mag);
-            acc[i] = fmaf(s[i], dd - off, b[i] * sx);
+            acc8[i] = fmaf(s[i], dd - off, b[i] * sx);
         }
         float tot[8];                                   // value i: gate row n0+i (i < 4),
-        wave_sum8(acc, tot);                            // up row n0+i-4 (i >= 4)
+        wave_sum8(acc8, tot);                           // up row n0+i-4 (i >= 4)
         if (lane < 4) {
             const int vi = lane;
             const float g = vi == 0 ? tot[0] : vi == 1 ? tot[1] : vi == 2 ? tot[2] : tot[3];
@@ -624,173 +754,252 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
             const float a = g / (1.f + expf(-g));
             const float hb = bf16_to_f32(f32_to_bf16(a * u));
             const int n = n0 + vi;
-            hout[((size_t)slot * T + t) * I + (n & ~7) + chunk_slot(n & 7)] =
+            hout[(size_t)hrow * I + (n & ~7) + chunk_slot(n & 7)] =
                 __builtin_bit_cast(uint16_t, (_Float16)hb);
         }
+        ++hrow;
     }
 }
 
-// grid (H/4): 4 output rows per workgroup over every active expert (wave w
-// takes slots w, w+4, ...), combine with the routing weights and the shared
-// gate, residual add.  Fixed summation order: deterministic.  The record is
-// read with scalar loads, all issued together; every vector load of a pass
-// (codes, scales, biases and the h row of each slot's first token) goes out
-// before any arithmetic.  Two waves per SIMD keep the whole grid resident.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_down_dec(const uint16_t* __restrict__ hin, int T, const DownRec* __restrict__ rec,
-                     QFFN routed, QFFN shared, uint16_t* __restrict__ y,
-                     const uint16_t* __restrict__ x, uint16_t* __restrict__ res,
-                     const uint4v* __restrict__ pf, uint32_t pf_n) {
-    __shared__ float yacc[4][MOE_DECODE_T][4];
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int r = lane >> 4, c = lane & 15;
-    const int m = blockIdx.x * 4 + r;
+// grid (DN_WG) workgroups of DN_RG x DN_SG waves.  Wave w owns the output
+// rows m0 + 4 (w % DN_RG) .. +3 (row group) and the slots a == w / DN_RG
+// (mod DN_SG) (slot group); lane l covers the K range 8l .. 8l+7 of each of
+// its rows, so a wave reads every row as one coalesced 256-byte segment (one
+// code dword per lane) and every h row as one coalesced 1 KB piece that
+// serves all four rows.  A pass issues all loads of up to DN_SPW of its
+// slots before any arithmetic (one pass covers a token's nine slots).  Each
+// wave sums its rows over its 64 lanes; the slot groups' partial rows are
+// then added in LDS in a fixed order (deterministic).  Writes y (optional),
+// res = bf16(x + y) (optional) and, for the next layer of a chain
+// (wrt_next != NULL: its transposed router): its fp16 input in chunk-slot
+// order (xh_next) and this
+// workgroup's share of its router and shared-gate logits, added to
+// accumulator copy blockIdx.x % ACC_COPIES of acc_next.  TT: 1 when T == 1,
+// else MOE_DECODE_T (a bound on T).
+template <int TT>
+__global__ __launch_bounds__(64 * DN_WAVES) void decode_down_dec(
+    const uint16_t* __restrict__ hin, int T, const DownRec* __restrict__ rec, QFFN routed,
+    QFFN shared, uint16_t* __restrict__ y, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ res, uint16_t* __restrict__ xh_next,
+    const uint16_t* __restrict__ wrt_next, const uint16_t* __restrict__ wsg_next,
+    long long* __restrict__ acc_next) {
+    __shared__ float yp[DN_SG][MOE_DECODE_T][DN_ROWS];     // partial rows of each slot group
+    __shared__ float xs[MOE_DECODE_T][DN_ROWS];             // the next layer's input rows
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int rg = wave % DN_RG, sg = wave / DN_RG;
+    const int m0 = blockIdx.x * DN_ROWS;
+    const int mw = m0 + 4 * rg;
     const DnPtrs pr = dn_ptrs(routed), ps = dn_ptrs(shared);
     const uint32_t mag = fp16_1024_pair();
     const uint32_t tall = (1u << T) - 1u;
-    // the residual input is needed only at the end: load it first
-    const int ot = threadIdx.x >> 2, orr = threadIdx.x & 3;
-    const bool writer = (int)threadIdx.x < T * 4;
-    const size_t o = (size_t)ot * H + blockIdx.x * 4 + orr;
-    const uint16_t xin = x[writer ? o : 0];
-    // the record: one load per array and lane, then lane reads
+    const bool chained = wrt_next != nullptr;
+    // the record first: one load per array and lane, all issued together,
+    // then picked apart with lane reads
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 re = reinterpret_cast<const u32x2*>(rec->slot_e)[lane];
     const u32x2 rm = reinterpret_cast<const u32x2*>(rec->slot_m)[lane];
-    u32x2 rc[MOE_DECODE_T];
+    const u32x2 rh = reinterpret_cast<const u32x2*>(rec->slot_h)[lane];
+    u32x2 rc[TT];
 #pragma unroll
-    for (int t = 0; t < MOE_DECODE_T; ++t) rc[t] = reinterpret_cast<const u32x2*>(rec->coef[t])[lane];
-    // (all of it is needed next; without this the compiler sinks the later
-    // loads behind a wait for the first)
-    asm volatile("" ::"v"(re), "v"(rm), "v"(rc[0]), "v"(rc[1]), "v"(rc[2]), "v"(rc[3]), "v"(rc[4]),
-                 "v"(rc[5]), "v"(rc[6]), "v"(rc[7]));
+    for (int t = 0; t < TT; ++t) rc[t] = reinterpret_cast<const u32x2*>(rec->coef[t])[lane];
+    // then the loads that need no routing, needed only at the very end: the
+    // next layer's transposed router rows m0 .. m0 + DN_ROWS - 1 (thread e:
+    // entry e of each, coalesced 512-byte rows) and the same entries of its
+    // shared-gate vector (buffer loads with no branch around them: a missing
+    // next layer is an empty range, so the wait counts of the loads issued
+    // before stay exact)
+    static_assert(64 * DN_WAVES >= E, "one thread per expert for the router partials");
+    const __amdgpu_buffer_rsrc_t rwt = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(wrt_next), 0, chained ? (uint32_t)(H * E * 2) : 0u, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rwg = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(wsg_next), 0, chained ? (uint32_t)(H * 2) : 0u, 0x00020000);
+    uint16_t wt[DN_ROWS], wg[DN_ROWS];
+#pragma unroll
+    for (int k = 0; k < DN_ROWS; ++k) {
+        const uint32_t ot = tid < E ? (uint32_t)(((m0 + k) * E + tid) * 2) : 0x80000000u;
+        wt[k] = __builtin_amdgcn_raw_buffer_load_b16(rwt, ot, 0, 0);
+        wg[k] = __builtin_amdgcn_raw_buffer_load_b16(rwg, (uint32_t)((m0 + k) * 2), 0, 0);
+    }
+    // the whole record is needed next (without this the compiler issues the
+    // later record loads only after waiting for the first one)
+    asm volatile("" ::"v"(re), "v"(rm), "v"(rh));
+#pragma unroll
+    for (int t = 0; t < TT; ++t) asm volatile("" ::"v"(rc[t]));
     auto slot_word = [](u32x2 v, int a) -> uint32_t {
         const uint32_t lo = __builtin_amdgcn_readlane(v[0], a >> 1);
         const uint32_t hi = __builtin_amdgcn_readlane(v[1], a >> 1);
         return (a & 1) ? hi : lo;
     };
     const int nslots = min(max((int)__builtin_amdgcn_readlane(re[1], 63), 1), TOPK * T + 1);
-    float acc[MOE_DECODE_T];
+    const int hmax = (TOPK + 1) * T - 1;
+    float acc[4][TT];
 #pragma unroll
-    for (int t = 0; t < MOE_DECODE_T; ++t) acc[t] = 0.f;
-    // the caller's prefetch range: one 16-byte unit per thread, issued after
-    // the first pass's loads (so no wait for those loads also waits for it),
-    // read back only at the very end
-    uint4v pfv = {0u, 0u, 0u, 0u};
-    const uint32_t pfi = blockIdx.x * 256u + threadIdx.x;
-    // one pass: slots a0, a0+4, a0+8, a0+12 (a0 < nslots)
-    auto pass = [&](const int a0, const bool first) {
-        int ak[4], tf[4];
-        uint32_t mk[4];
-        uint4v dw[4], h0[4][4];
-        float ds[4], db[4];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
+    // the residual input, for the output lanes (no branch around the load)
+    const int xi = min(lane, T * 4 - 1);
+    const uint16_t xin = x[(size_t)(xi >> 2) * H + mw + (xi & 3)];
+    // one pass: this wave's slots a0 + sg + DN_SG * k, k < DN_SPW
+    auto pass = [&](const int a0) {
+        uint32_t cw[DN_SPW][4];
+        uint16_t sb[DN_SPW][8];
+        uint4v h1[DN_SPW];
+#pragma unroll
+        for (int k = 0; k < DN_SPW; ++k) {
             // slots past the last one repeat a valid slot's loads (unused)
-            const int a = min(a0 + 4 * k, nslots - 1);
-            ak[k] = a;
+            const int a = min(a0 + sg + DN_SG * k, nslots - 1);
             const int e = min(max((int)slot_word(re, a), 0), E - 1);
-            mk[k] = slot_word(rm, a) & tall;
-            tf[k] = mk[k] ? __builtin_ctz(mk[k]) : 0;
             const DnPtrs q = pick(a == 0, ps, pr);
-            const size_t row = m;
-            dw[k] = ((const GLOBAL_AS uint4v*)(gexpert(q.q, e, q.sq) + row * (I / 8)))[c];
-            ds[k] = fp16_to_f32(gexpert(q.s, e, q.ss)[row * (I / G) + (c >> 1)]);
-            db[k] = fp16_to_f32(gexpert(q.b, e, q.ss)[row * (I / G) + (c >> 1)]);
-            const uint4v* hr =
-                reinterpret_cast<const uint4v*>(hin + ((size_t)a * T + tf[k]) * I) + c * 4;
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) h0[k][cc] = hr[cc];
+            for (int r = 0; r < 4; ++r) {
+                const size_t row = mw + r;
+                cw[k][r] = (gexpert(q.q, e, q.sq) + row * (I / 8))[lane];
+                sb[k][r] = gexpert(q.s, e, q.ss)[row * (I / G) + (lane >> 3)];
+                sb[k][4 + r] = gexpert(q.b, e, q.ss)[row * (I / G) + (lane >> 3)];
+            }
+            const int hr = min(max((int)slot_word(rh, a), 0), hmax);
+            h1[k] = reinterpret_cast<const uint4v*>(hin + (size_t)hr * I)[lane];
         }
-        if (first && pfi < pf_n) pfv = pf[pfi];
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (a0 + 4 * k >= nslots) break;
-            const int a = ak[k];
-            for (int t = tf[k]; t < T; ++t) {
-                if (!((mk[k] >> t) & 1u)) continue;
-                uint32_t cw = slot_word(rc[0], a);
+        for (int k = 0; k < DN_SPW; ++k) {
+            const int a = a0 + sg + DN_SG * k;
+            if (a >= nslots) continue;     // (a guard, not a break: the loop unrolls fully)
+            const uint32_t mk = slot_word(rm, a) & tall;
+            int hrow = min(max((int)slot_word(rh, a), 0), hmax);
+            bool firsttok = true;
 #pragma unroll
-                for (int tt = 1; tt < MOE_DECODE_T; ++tt)
-                    if (tt < T && t == tt) cw = slot_word(rc[tt], a);
-                const float coef = __builtin_bit_cast(float, cw);
-                uint4v hv[4];
-                if (t == tf[k]) {
+            for (int t = 0; t < TT; ++t) {
+                if (t >= T || !((mk >> t) & 1u)) continue;
+                const float coef = __builtin_bit_cast(float, slot_word(rc[t], a));
+                uint4v hv = h1[k];
+                if (!firsttok)
+                    hv = reinterpret_cast<const uint4v*>(hin + (size_t)min(hrow, hmax) * I)[lane];
+                firsttok = false;
+                ++hrow;
+                const float sx = sum8_h(hv, 0.f);
+                const uint4v hs = prescale_pairs(hv);
+                const float off = pair_offset(hs, 0.f);
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) hv[cc] = h0[k][cc];
-                } else {
-                    const uint4v* hr =
-                        reinterpret_cast<const uint4v*>(hin + ((size_t)a * T + t) * I) + c * 4;
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) hv[cc] = hr[cc];
+                for (int r = 0; r < 4; ++r) {
+                    const float dd = dot8_biased(cw[k][r], hs, 0.f, mag);
+                    acc[r][t] += coef * fmaf(fp16_to_f32(sb[k][r]), dd - off,
+                                             fp16_to_f32(sb[k][4 + r]) * sx);
                 }
-                float sh_ = 0.f, off = 0.f, dot = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    sh_ = sum8_h(hv[cc], sh_);
-                    const uint4v hs = prescale_pairs(hv[cc]);
-                    off = pair_offset(hs, off);
-                    dot = dot8_biased(dw[k][cc], hs, dot, mag);
-                }
-                const float part = coef * fmaf(ds[k], dot - off, db[k] * sh_);
-#pragma unroll
-                for (int tt = 0; tt < MOE_DECODE_T; ++tt)
-                    if (tt == t) acc[tt] += part;
             }
         }
     };
-    // the first pass is peeled, so that its loads are not held up by waits
-    // for the loop's previous iteration
-    pass(wave, true);
-    for (int a0 = wave + 16; a0 < nslots; a0 += 16) pass(a0, false);
-    // reduce the 16 lanes of each row, then the four waves in a fixed order
+    // one token has at most 9 slots, which one pass covers: no loop whose
+    // head would make the wait counts of the loads above conservative
+    static_assert(DN_SG * DN_SPW >= 1 + TOPK, "one pass covers a token's slots");
+    if constexpr (TT == 1) {
+        pass(0);
+    } else {
+        for (int a0 = 0; a0 < nslots; a0 += DN_SG * DN_SPW) pass(a0);
+    }
+    // this wave's partial rows over its 64 lanes, then the slot groups' sums
 #pragma unroll
-    for (int t = 0; t < MOE_DECODE_T; ++t) {
-        if (t < T) {
-            const float v = row16_sum(acc[t]);
-            if (c == 0) yacc[wave][t][r] = v;
+    for (int t = 0; t < TT; ++t) {
+        if (t >= T) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = wave_sum(acc[r][t]);
+            if (lane == 0) yp[sg][t][4 * rg + r] = v;
         }
     }
     __syncthreads();
-    if (writer) {
-        const float v = ((yacc[0][ot][orr] + yacc[1][ot][orr]) + yacc[2][ot][orr]) + yacc[3][ot][orr];
+    if (sg == 0 && lane < T * 4) {
+        // lane r + 4t of each row group's first wave: row mw + r of token t
+        const int t = lane >> 2, r = lane & 3, rr = 4 * rg + r;
+        float v = yp[0][t][rr];
+#pragma unroll
+        for (int g = 1; g < DN_SG; ++g) v += yp[g][t][rr];
         const uint32_t yb = f32_to_bf16(v);
-        y[o] = (uint16_t)yb;
-        if (res) res[o] = (uint16_t)f32_to_bf16(bf16_to_f32(xin) + bf16_to_f32(yb));
+        const size_t o = (size_t)t * H + mw + r;
+        if (y) y[o] = (uint16_t)yb;
+        const uint32_t xb = f32_to_bf16(bf16_to_f32(xin) + bf16_to_f32(yb));
+        if (res) res[o] = (uint16_t)xb;
+        xs[t][rr] = bf16_to_f32(xb);
+        if (chained) {
+            const int m = mw + r;
+            xh_next[(size_t)t * H + (m & ~7) + chunk_slot(m & 7)] =
+                __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(xb));
+        }
     }
-    // keeps the prefetch load (T is never negative)
-    if (T < 0 && (pfv[0] ^ pfv[1] ^ pfv[2] ^ pfv[3]) == 0x9E3779B9u) y[0] = 0;
+    if (!chained) return;
+    __syncthreads();
+    // this workgroup's partial router and shared-gate logits of the next
+    // layer (thread e < 256: logit e, thread 256 - 256 = the shared gate is
+    // done by thread 0 as a second sum): DN_ROWS exact bf16 products summed
+    // in fp32 in order
+    long long* cp = acc_next + (size_t)(blockIdx.x % ACC_COPIES) * T * ACC_STRIDE;
+    if (tid < E) {
+        for (int t = 0; t < T; ++t) {
+            float p = 0.f, z = 0.f;
+#pragma unroll
+            for (int k = 0; k < DN_ROWS; ++k) {
+                p = fmaf(bf16_to_f32(wt[k]), xs[t][k], p);
+                z = fmaf(bf16_to_f32(wg[k]), xs[t][k], z);
+            }
+            atomicAdd(reinterpret_cast<unsigned long long*>(cp + (size_t)t * ACC_STRIDE + tid),
+                      (unsigned long long)acc_fix(p));
+            if (tid == 0)
+                atomicAdd(reinterpret_cast<unsigned long long*>(cp + (size_t)t * ACC_STRIDE + E),
+                          (unsigned long long)acc_fix(z));
+        }
+    }
+}
+
+// w_router bf16 [256][2048] -> w_router_t bf16 [2048][256], through a 64 x
+// 64 tile in LDS (grid (2048 / 64, 256 / 64), 256 threads).
+__global__ __launch_bounds__(256) void router_transpose(const uint16_t* __restrict__ wr,
+                                                        uint16_t* __restrict__ wrt) {
+    __shared__ uint16_t tile[64][66];
+    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int r = i >> 6, c = i & 63;
+        tile[r][c] = wr[(size_t)(e0 + r) * H + k0 + c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int r = i >> 6, c = i & 63;
+        wrt[(size_t)(k0 + r) * E + e0 + c] = tile[c][r];
+    }
+}
+
+void launch_router_transpose(const uint16_t* wr, uint16_t* wrt, hipStream_t st) {
+    hipLaunchKernelGGL(router_transpose, dim3(H / 64, E / 64), dim3(256), 0, st, wr, wrt);
 }
 
 size_t route_rec_bytes() { return sizeof(DownRec); }
+size_t route_acc_bytes(int T) { return (size_t)2 * ACC_COPIES * T * ACC_STRIDE * sizeof(long long); }
 
-void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
-                               float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
-                               void* rec, uint16_t* y, uint16_t* res, const void* prefetch,
-                               size_t prefetch_bytes, hipStream_t st) {
+// One few-token layer.  first: the layer computes its own router logits
+// (route_logits_dec) into acc_cur; otherwise a previous chained layer left
+// them there.  next (optional): the following layer of a chain, whose
+// router logits go to acc_next and whose fp16 input goes to xh.
+void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, bool first,
+                               long long* acc_cur, long long* acc_next, const moe_layer* next,
+                               uint16_t* xh, uint16_t* hbuf, void* rec, uint16_t* y,
+                               uint16_t* res, int32_t* ids_out, float* w_out, float* sg_out,
+                               hipStream_t st) {
     const QFFN routed = qffn_view(L.routed), shared = qffn_view(L.shared);
     DownRec* R = static_cast<DownRec*>(rec);
-    (void)counter;
-    hipLaunchKernelGGL(route_logits_dec, dim3(NRB + 1 + T), dim3(256), 0, st, x, T, L.w_router,
-                       L.router_bias, L.w_shared_gate, logits, z, xh);
+    if (first)
+        hipLaunchKernelGGL(route_logits_dec, dim3(NRB + 1 + T), dim3(256), 0, st, x, T, L.w_router,
+                           L.w_shared_gate, acc_cur, xh);
     hipLaunchKernelGGL(decode_gateup_dec, dim3(1 + TOPK * T, I / 16), dim3(256), 0, st, xh, T,
-                       logits, z, R, routed, shared, hbuf);
-    static_assert((H / 4) * 256 * 16 == MOE_PREFETCH_MAX, "one prefetch unit per thread");
-    hipLaunchKernelGGL(decode_down_dec, dim3(H / 4), dim3(256), 0, st, hbuf, T, R, routed,
-                       shared, y, x, res, static_cast<const uint4v*>(prefetch),
-                       (uint32_t)(prefetch ? prefetch_bytes / 16 : 0));
-}
-
-// Zero the workspace's synchronisation words (a fill kernel, not a memset,
-// so the call can be captured in a graph).
-__global__ void zero_words(unsigned* p, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
-
-void launch_zero_words(unsigned* p, int n, hipStream_t st) {
-    hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+                       acc_cur, L.router_bias, next ? acc_next : nullptr, R, routed, shared, hbuf,
+                       ids_out, w_out, sg_out);
+    const dim3 g(DN_WG), b(64 * DN_WAVES);
+    if (T == 1)
+        hipLaunchKernelGGL(decode_down_dec<1>, g, b, 0, st, hbuf, T, R, routed, shared, y, x, res,
+                           next ? xh : nullptr, next ? next->w_router_t : nullptr,
+                           next ? next->w_shared_gate : nullptr, next ? acc_next : nullptr);
+    else
+        hipLaunchKernelGGL(decode_down_dec<MOE_DECODE_T>, g, b, 0, st, hbuf, T, R, routed, shared, y,
+                           x, res, next ? xh : nullptr, next ? next->w_router_t : nullptr,
+                           next ? next->w_shared_gate : nullptr, next ? acc_next : nullptr);
 }
 
 void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,

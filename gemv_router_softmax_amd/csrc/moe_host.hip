@@ -31,12 +31,13 @@ void launch_decode_down_combine(const uint16_t* hbuf, int T, const int32_t* perm
                                 const Tile* tiles, const int* tile_count, const float* wts,
                                 const float* sg, const QFFN& routed, const QFFN& shared,
                                 uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
-void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, float* logits,
-                               float* z, uint16_t* xh, uint16_t* hbuf, unsigned* counter,
-                               void* rec, uint16_t* y, uint16_t* res, const void* prefetch,
-                               size_t prefetch_bytes, hipStream_t st);
+void launch_layer_decode_small(const uint16_t* x, int T, const moe_layer& L, bool first,
+                               long long* acc_cur, long long* acc_next, const moe_layer* next,
+                               uint16_t* xh, uint16_t* hbuf, void* rec, uint16_t* y,
+                               uint16_t* res, int32_t* ids_out, float* w_out, float* sg_out,
+                               hipStream_t st);
 size_t route_rec_bytes();
-void launch_zero_words(unsigned* p, int n, hipStream_t st);
+size_t route_acc_bytes(int T);
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st,
                     const float* wts = nullptr, float* wsorted = nullptr, Tile* tiles = nullptr,
@@ -61,17 +62,16 @@ void launch_combine_f16(const uint16_t* d16, const int32_t* inv, int T, uint16_t
                         const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_combine(const float* out, const int32_t* inv, const float* wts, const float* sg, int T,
                     uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
+void launch_router_transpose(const uint16_t* wr, uint16_t* wrt, hipStream_t st);
 void launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t st);
 void launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 
 namespace {
 
-constexpr int SYNC_WORDS = 64;
-
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct WsLayout {
-    size_t sync, rec, logits, ids, wts, sg, counts, offsets, perm, inv, wsorted, chunk_counts, tiles,
-        tile_count, xh, h, dout, total;
+    size_t rec, acc, logits, ids, wts, sg, counts, offsets, perm, inv, wsorted, chunk_counts, tiles,
+        tile_count, xh, h, dout, chain, total;
 };
 
 WsLayout ws_layout(int T) {
@@ -83,8 +83,10 @@ WsLayout ws_layout(int T) {
         return o;
     };
     const size_t t = (size_t)T;
-    L.sync = take(SYNC_WORDS * 4);      // counters: zero before first use, zero after every call
+    // (kept monotone in T: the few-token regions never shrink beyond that range)
+    const size_t ts = t < MOE_DECODE_T ? t : MOE_DECODE_T;
     L.rec = take(route_rec_bytes());
+    L.acc = take(route_acc_bytes((int)ts));     // two sets of fixed-point logits
     L.logits = take(t * E * 4);
     L.ids = take(t * TOPK * 4);
     L.wts = take(t * TOPK * 4);
@@ -98,13 +100,9 @@ WsLayout ws_layout(int T) {
     L.tiles = take((size_t)max_tiles(T) * sizeof(Tile));
     L.tile_count = take(TILE_COUNT_WORDS * 4);
     L.xh = take(t * H * 2);
-    // h rows: 9T for the tile-based kernels; the few-token layer indexes them
-    // (slot * T + token) with up to 1 + 8T slots
-    // (kept monotone in T: beyond the few-token range it never shrinks)
-    const size_t ts = t < MOE_DECODE_T ? t : MOE_DECODE_T;
-    const size_t hrows = std::max((1 + TOPK * ts) * ts, (TOPK + 1) * t);
-    L.h = take(hrows * I * 2);
+    L.h = take((TOPK + 1) * t * I * 2);
     L.dout = take(t * (TOPK + 1) * H * 4);
+    L.chain = take(3 * t * H * 2);              // chains: two residual buffers and a y buffer
     L.total = off;
     return L;
 }
@@ -266,29 +264,40 @@ int moe_combine(const float* expert_out, const int32_t* inv_perm, const float* t
     return launch_status();
 }
 
-int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint16_t* y, void* ws,
-                         size_t ws_bytes, void* stream, const moe_options* opt) {
-    if (check_T(T)) return MOE_ERR_INVALID_ARG;
-    int path;
-    if (pick_path(T, opt, &path)) return MOE_ERR_INVALID_ARG;
-    if (T == 0) return MOE_OK;
-    if (!x || !layer || !y || !ws || !layer->w_router || !layer->w_shared_gate)
-        return MOE_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+// Validation shared by the layer and chain calls (one layer descriptor).
+int check_layer(const moe_layer* layer) {
+    if (!layer || !layer->w_router || !layer->w_shared_gate) return MOE_ERR_INVALID_ARG;
     if (int rc = check_qffn(&layer->routed)) return rc;
     if (int rc = check_qffn(&layer->shared)) return rc;
-    uint16_t* res = opt ? opt->residual_out : nullptr;
-    const void* pf = opt ? opt->prefetch : nullptr;
-    const size_t pf_bytes = pf ? opt->prefetch_bytes : 0;
-    if (pf && (pf_bytes % 16 != 0 || pf_bytes > MOE_PREFETCH_MAX)) return MOE_ERR_INVALID_ARG;
-    if (!a16(x) || !a16(y) || !a16(ws) || !a16(layer->w_router) || !a16(layer->w_shared_gate) ||
-        (layer->router_bias && !a4(layer->router_bias)) || (res && !a16(res)) || (pf && !a16(pf)))
+    if (!a16(layer->w_router) || !a16(layer->w_shared_gate) ||
+        (layer->router_bias && !a4(layer->router_bias)) ||
+        (layer->w_router_t && !a16(layer->w_router_t)))
         return MOE_ERR_ALIGN;
-    const WsLayout L = ws_layout(T);
-    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
-    int32_t* ids = at<int32_t>(ws, L.ids);
-    float* wts = at<float>(ws, L.wts);
-    float* sg = at<float>(ws, L.sg);
+    return MOE_OK;
+}
+
+// Route outputs requested through moe_options: all three or none.
+int check_route_out(const moe_options* opt) {
+    if (!opt) return MOE_OK;
+    const int n = (opt->route_ids != nullptr) + (opt->route_w != nullptr) + (opt->route_sg != nullptr);
+    if (n != 0 && n != 3) return MOE_ERR_INVALID_ARG;
+    if (n == 3 && (!a4(opt->route_ids) || !a4(opt->route_w) || !a4(opt->route_sg))) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+// One layer, arguments already validated.  ids_out/w_out/sg_out: the
+// caller's route outputs, or NULL (the routing then stays in the workspace).
+void layer_forward(const uint16_t* x, int T, int path, const moe_layer* layer, uint16_t* y,
+                   uint16_t* res, void* ws, const WsLayout& L, int32_t* ids_out, float* w_out,
+                   float* sg_out, hipStream_t st) {
+    int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
+    float* wts = ids_out ? w_out : at<float>(ws, L.wts);
+    float* sg = ids_out ? sg_out : at<float>(ws, L.sg);
     int32_t* counts = at<int32_t>(ws, L.counts);
     int32_t* offsets = at<int32_t>(ws, L.offsets);
     int32_t* perm = at<int32_t>(ws, L.perm);
@@ -297,31 +306,27 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
     int* tcount = at<int>(ws, L.tile_count);
     uint16_t* hbuf = at<uint16_t>(ws, L.h);
     float* dout = at<float>(ws, L.dout);
+    uint16_t* xh = at<uint16_t>(ws, L.xh);
 
     if (path == MOE_PATH_DECODE && T <= MOE_DECODE_T) {
-        // three kernels: logits (+ shared gate logit, fp16 x) | gate/up | down+combine;
-        // the routing is recomputed inside the two expert kernels
-        launch_layer_decode_small(x, T, *layer, at<float>(ws, L.logits), sg,
-                                  at<uint16_t>(ws, L.xh), hbuf, at<unsigned>(ws, L.sync),
-                                  at<char>(ws, L.rec), y, res, pf, pf_bytes, st);
-        return launch_status();
+        // router logits, gate/up (routing inside), down + combine
+        launch_layer_decode_small(x, T, *layer, /*first=*/true, at<long long>(ws, L.acc), nullptr,
+                                  nullptr, xh, hbuf, at<char>(ws, L.rec), y, res, ids_out, w_out,
+                                  sg_out, st);
+        return;
     }
     if (path == MOE_PATH_DECODE) {
         // four kernels: logits | select (top-8, permutation, tiles) | gate/up | down+combine
-        launch_route_logits(x, T, layer->w_router, layer->router_bias, at<float>(ws, L.logits),
-                            st);
-        uint16_t* xh = at<uint16_t>(ws, L.xh);
+        launch_route_logits(x, T, layer->w_router, layer->router_bias, at<float>(ws, L.logits), st);
         launch_route_select(at<float>(ws, L.logits), x, layer->w_shared_gate, T, ids, wts, sg,
                             counts, offsets, perm, inv, tiles, tcount, xh, st);
         launch_decode_gateup(xh, T, perm, tiles, tcount, max_tiles(T), qffn_view(layer->routed),
                              qffn_view(layer->shared), hbuf, st);
-        launch_decode_down_combine(hbuf, T, perm, tiles, tcount, wts, sg,
-                                   qffn_view(layer->routed), qffn_view(layer->shared), y, x, res,
-                                   st);
-        return launch_status();
+        launch_decode_down_combine(hbuf, T, perm, tiles, tcount, wts, sg, qffn_view(layer->routed),
+                                   qffn_view(layer->shared), y, x, res, st);
+        return;
     }
     // the top-8 kernel also writes the fp16 activations the grouped GEMM reads
-    uint16_t* xh = at<uint16_t>(ws, L.xh);
     launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
                  at<float>(ws, L.logits), ids, wts, sg, st, xh, at<float>(ws, L.h));
     float* wsorted = at<float>(ws, L.wsorted);
@@ -333,6 +338,29 @@ int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint1
                                 qffn_view(layer->shared), xh, hbuf, d16, wsorted, sg,
                                 /*xh_ready=*/true, st);
     launch_combine_f16(d16, inv, T, y, x, res, st);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_layer_forward_ex(const uint16_t* x, int T, const moe_layer* layer, uint16_t* y, void* ws,
+                         size_t ws_bytes, void* stream, const moe_options* opt) {
+    if (check_T(T)) return MOE_ERR_INVALID_ARG;
+    int path;
+    if (pick_path(T, opt, &path)) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
+    if (int rc = check_layer(layer)) return rc;
+    if (int rc = check_route_out(opt)) return rc;
+    uint16_t* res = opt ? opt->residual_out : nullptr;
+    if (!a16(x) || !a16(y) || !a16(ws) || (res && !a16(res))) return MOE_ERR_ALIGN;
+    const WsLayout L = ws_layout(T);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    const bool ro = opt && opt->route_ids;
+    layer_forward(x, T, path, layer, y, res, ws, L, ro ? opt->route_ids : nullptr,
+                  ro ? opt->route_w : nullptr, ro ? opt->route_sg : nullptr, (hipStream_t)stream);
     return launch_status();
 }
 
@@ -341,11 +369,58 @@ int moe_layer_forward(const uint16_t* x, int T, const moe_layer* layer, uint16_t
     return moe_layer_forward_ex(x, T, layer, y, ws, ws_bytes, stream, nullptr);
 }
 
-int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
-    if (!ws) return MOE_ERR_INVALID_ARG;
-    if (!a16(ws)) return MOE_ERR_ALIGN;
-    if (ws_bytes < moe_workspace_bytes(0)) return MOE_ERR_WORKSPACE;
-    launch_zero_words(at<unsigned>(ws, ws_layout(0).sync), SYNC_WORDS, (hipStream_t)stream);
+int moe_chain_forward(const uint16_t* x, int T, const moe_layer* layers, int nlayers,
+                      uint16_t* x_out, uint16_t* y_layers, void* ws, size_t ws_bytes, void* stream,
+                      const moe_options* opt) {
+    if (check_T(T) || nlayers < 0) return MOE_ERR_INVALID_ARG;
+    int path;
+    if (pick_path(T, opt, &path)) return MOE_ERR_INVALID_ARG;
+    if (opt && opt->residual_out) return MOE_ERR_INVALID_ARG;     // the chain's output is x_out
+    if (T == 0 || nlayers == 0) return MOE_OK;
+    if (!x || !layers || !x_out || !ws) return MOE_ERR_INVALID_ARG;
+    for (int l = 0; l < nlayers; ++l)
+        if (int rc = check_layer(&layers[l])) return rc;
+    if (int rc = check_route_out(opt)) return rc;
+    if (!a16(x) || !a16(x_out) || !a16(ws) || (y_layers && !a16(y_layers))) return MOE_ERR_ALIGN;
+    const WsLayout L = ws_layout(T);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t tH = (size_t)T * H;
+    uint16_t* xb[2] = {at<uint16_t>(ws, L.chain), at<uint16_t>(ws, L.chain) + tH};
+    uint16_t* yscratch = at<uint16_t>(ws, L.chain) + 2 * tH;
+    const bool ro = opt && opt->route_ids;
+    const bool few = path == MOE_PATH_DECODE && T <= MOE_DECODE_T;
+    long long* acc[2] = {at<long long>(ws, L.acc),
+                         at<long long>(ws, L.acc) + route_acc_bytes(T) / 2 / sizeof(long long)};
+    for (int l = 0; l < nlayers; ++l) {
+        const uint16_t* xl = l == 0 ? x : xb[(l - 1) & 1];
+        uint16_t* res = l == nlayers - 1 ? x_out : xb[l & 1];
+        uint16_t* yl = y_layers ? y_layers + (size_t)l * tH : yscratch;
+        int32_t* ids = ro ? opt->route_ids + (size_t)l * T * TOPK : nullptr;
+        float* w = ro ? opt->route_w + (size_t)l * T * TOPK : nullptr;
+        float* sg = ro ? opt->route_sg + (size_t)l * T : nullptr;
+        if (few) {
+            // two kernels per layer after the first: each down kernel also
+            // forms the next layer's router logits and fp16 input (when the
+            // next layer carries its transposed router matrix)
+            const bool fused_in = l > 0 && layers[l].w_router_t != nullptr;
+            const moe_layer* next =
+                l + 1 < nlayers && layers[l + 1].w_router_t ? &layers[l + 1] : nullptr;
+            launch_layer_decode_small(xl, T, layers[l], !fused_in, acc[l & 1], acc[(l + 1) & 1], next,
+                                      at<uint16_t>(ws, L.xh), at<uint16_t>(ws, L.h),
+                                      at<char>(ws, L.rec), y_layers ? yl : nullptr, res, ids, w, sg,
+                                      st);
+        } else {
+            layer_forward(xl, T, path, &layers[l], yl, res, ws, L, ids, w, sg, st);
+        }
+    }
+    return launch_status();
+}
+
+int moe_router_transpose(const uint16_t* w_router, uint16_t* w_router_t, void* stream) {
+    if (!w_router || !w_router_t) return MOE_ERR_INVALID_ARG;
+    if (!a16(w_router) || !a16(w_router_t)) return MOE_ERR_ALIGN;
+    launch_router_transpose(w_router, w_router_t, (hipStream_t)stream);
     return launch_status();
 }
 

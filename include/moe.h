@@ -43,12 +43,19 @@
  *   - On an error status nothing has been enqueued.  A launch failure is
  *     reported as MOE_ERR_HIP.
  *   - T == 0 is a no-op returning MOE_OK.  T may not exceed MOE_T_MAX.
- *   - The workspace (moe_workspace_bytes(T) bytes, caller owned) must be
- *     prepared once with moe_workspace_init (or be zero-filled) before its
- *     first use; every call leaves it ready for the next one.  Calls that
- *     share a workspace must be ordered on one stream; calls on different
- *     streams need different workspaces.  Everything is deterministic: the
- *     same inputs give bit-identical outputs.
+ *   - The workspace (moe_workspace_bytes(T) bytes, caller owned) is
+ *     scratch: no call reads anything a previous call left in it, so it
+ *     needs no preparation.  Calls that share a workspace must be ordered on
+ *     one stream; calls on different streams need different workspaces.
+ *   - Everything is deterministic: the same inputs give bit-identical
+ *     outputs.
+ *   - Activations and the SwiGLU intermediate h are carried as fp16 inside
+ *     the expert kernels (bf16 -> fp16 is exact for magnitudes in
+ *     [2^-14, 65504]; smaller ones keep fp16's subnormal spacing 2^-24).
+ *     Inputs are expected to keep |x| and |h| below 65504; a token whose x
+ *     or h leaves that range gets a non-finite output row (other tokens are
+ *     unaffected).  Routing is computed from the bf16 x in fp32 and is not
+ *     affected.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -91,11 +98,12 @@ typedef enum {
  * expert_stride: 0 = each of the nine arrays is dense, [n][rows][cols] as
  * above.  Otherwise it is the byte distance between expert e and expert
  * e + 1 in EVERY one of the nine arrays (a multiple of 256, at least
- * 524288 = one expert's code matrix), so that all of one expert's codes,
- * scales and biases can sit together in one block of memory; within an
- * expert each array keeps the row-major shape above (the library's
- * binding offers 2 MiB-aligned 2 MiB blocks per expert as an option).
- * Blocks must not overlap (not checked). */
+ * 524288 = one expert's code matrix, at most 2^31), so that all of one
+ * expert's codes, scales and biases can sit together in one block of memory
+ * (fewer distinct pages touched per active expert; the library's binding
+ * offers 2 MiB-aligned 2 MiB blocks per expert as an option); within an
+ * expert each array keeps the row-major shape above.  Blocks must not
+ * overlap (not checked); anything else returns MOE_ERR_INVALID_ARG. */
 typedef struct {
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
@@ -103,101 +111,148 @@ typedef struct {
 } moe_qffn;
 
 /* One MoE layer: router, shared-expert gate, routed stack (n = 256) and
- * shared expert (n = 1). */
+ * shared expert (n = 1).  w_router_t (optional, may be NULL): the same
+ * router matrix transposed, bf16 [2048][256] (see moe_router_transpose);
+ * a chain's few-token path fuses a layer into the one before it only when
+ * the layer has it (otherwise that layer runs its own router kernel). */
 typedef struct {
     const uint16_t *w_router;
     const float *router_bias;       /* may be NULL */
     const uint16_t *w_shared_gate;
     moe_qffn routed;
     moe_qffn shared;
+    const uint16_t *w_router_t;     /* may be NULL */
 } moe_layer;
 
 typedef struct {
     int path;                       /* moe_path */
     uint16_t *residual_out;         /* if non-NULL: also write bf16(x + y) here,
-                                       bf16 [T][2048] (the chain's next input) */
-    const void *prefetch;           /* if non-NULL: device bytes the call reads
-                                       once and discards, to pull them toward
-                                       the caches for a later call -- e.g. the
-                                       next layer's router matrix in a decode
-                                       chain (the next layer's first kernel
-                                       then reads it from the memory-side
-                                       cache).  Never written.  16-byte aligned;
-                                       prefetch_bytes a multiple of 16, at most
-                                       MOE_PREFETCH_MAX.  Read by the few-token
-                                       (decode) layer path; other paths ignore
-                                       it.  Prefetching the next layer's
-                                       weights while this one runs is "fusing
-                                       kernel chains" in "A Rust + Metal
-                                       Inference Engine for Qwen3.6-35B-A3B on
-                                       Apple Silicon", paragraph 5. */
-    size_t prefetch_bytes;
+                                       bf16 [T][2048] (layer calls only; a
+                                       chain call rejects it) */
+    int32_t *route_ids;             /* route outputs, all three or none: the
+                                       routing the call used -- ids int32
+                                       [T][8] in selection order, weights fp32
+                                       [T][8], shared gate fp32 [T] (chain
+                                       calls: [nlayers][...], layer by layer);
+                                       4-byte aligned device memory */
+    float *route_w;
+    float *route_sg;
 } moe_options;
-
-#define MOE_PREFETCH_MAX 2097152    /* bytes: one 16-byte load per thread of the
-                                       decode down kernel (512 x 256) */
 
 /* Workspace bytes sufficient for ANY call below with this T (monotone in T).
  * Returns 0 for T < 0 or T > MOE_T_MAX. */
 size_t moe_workspace_bytes(int T);
 
-/* Prepares a workspace for its first use (clears the library's
- * synchronisation words at its start; the rest is scratch).  Enqueues one
- * small fill kernel on `stream` (capturable in a graph).  ws_bytes must be
- * at least moe_workspace_bytes(0). */
-int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
-
 /* Human-readable name of a status code. */
 const char *moe_status_string(int status);
 
-/* Router (routing kept on the GPU: "Perplexity Open-Sources Lily ...",
- * section "The optimizations follow the workload").  For each token t:
- * logits l = x[t] W_r^T (+ router_bias), fp32 accumulation of exact bf16
- * products; topk_ids[t][0..7] = the 8 largest logits in descending order,
- * ties to the lower expert index; topk_w[t][j] = softmax(l)[id_j]
- * renormalised over the 8; shared_gate[t] = sigmoid(x[t] . w_shared_gate).
- * Outputs: topk_ids int32 [T][8], topk_w fp32 [T][8], shared_gate fp32 [T].
- * ws: workspace of moe_workspace_bytes(T) bytes. */
+/* Router.  Every token goes to 8 of the 256 experts plus the shared expert
+ * ("Perplexity Open-Sources Lily ...", section "A runtime shaped around one
+ * model"), and the routing stays on the GPU with no host synchronisation
+ * (same page, section "The optimizations follow the workload").  For each
+ * token t: logits l = x[t] W_r^T (+ router_bias), fp32 accumulation of
+ * exact bf16 products; topk_ids[t][0..7] = the 8 largest logits in
+ * descending order, ties to the lower expert index; topk_w[t][j] =
+ * softmax(l)[id_j] renormalised over the 8; shared_gate[t] =
+ * sigmoid(x[t] . w_shared_gate).
+ * In: x bf16 [T][2048], w_router bf16 [256][2048], router_bias fp32 [256] or
+ * NULL, w_shared_gate bf16 [2048] (16-byte aligned except router_bias: 4).
+ * Out: topk_ids int32 [T][8], topk_w fp32 [T][8], shared_gate fp32 [T].
+ * ws: workspace of moe_workspace_bytes(T) bytes.
+ * Errors: NULL pointer or T out of range -> MOE_ERR_INVALID_ARG; alignment
+ * -> MOE_ERR_ALIGN; ws_bytes too small -> MOE_ERR_WORKSPACE. */
 int moe_route(const uint16_t *x, int T, const uint16_t *w_router,
               const float *router_bias, const uint16_t *w_shared_gate,
               int32_t *topk_ids, float *topk_w, float *shared_gate,
               void *ws, size_t ws_bytes, void *stream);
 
-/* Token -> expert permutation: a stable counting sort of the flat slots
- * f = 8t + j by expert id (histogram, exclusive scan, scatter; bit-exact).
- * expert_counts int32 [256]; expert_offsets int32 [257] (offsets[256] = 8T);
- * perm int32 [8T]: sorted position -> slot f (each expert's segment is in
- * ascending f); inv_perm int32 [8T]: slot f -> sorted position.  Ids outside
- * 0..255 are not counted or placed (their inv_perm entry is -1 and the
- * offsets then end below 8T). */
+/* Token -> expert permutation, the step that turns the routing into the
+ * per-expert row groups of the grouped matrix products ("Perplexity
+ * Open-Sources Lily ...", section "The optimizations follow the workload":
+ * routing and the grouped products stay on the GPU).  A stable counting
+ * sort of the flat slots f = 8t + j by expert id (histogram, exclusive scan,
+ * scatter; bit-exact).
+ * In: topk_ids int32 [T][8].  Out: expert_counts int32 [256];
+ * expert_offsets int32 [257] (offsets[256] = 8T); perm int32 [8T]: sorted
+ * position -> slot f (each expert's segment is in ascending f); inv_perm
+ * int32 [8T]: slot f -> sorted position.  Ids outside 0..255 are not counted
+ * or placed (their inv_perm entry is -1 and the offsets then end below 8T).
+ * All arrays 4-byte aligned; ws as for moe_route.  Errors as for moe_route. */
 int moe_permute(const int32_t *topk_ids, int T, int32_t *expert_counts,
                 int32_t *expert_offsets, int32_t *perm, int32_t *inv_perm,
                 void *ws, size_t ws_bytes, void *stream);
 
-/* Expert FFNs with the 4-bit weights dequantised inside the kernels.
- * expert_out fp32 [8T + T][2048]: row p < 8T is sorted position p (token
- * perm[p] / 8 through the expert whose offsets segment contains p), row
- * 8T + t is the shared expert on token t.  `opt` may be NULL. */
+/* Expert FFNs with the 4-bit weights rebuilt inside the kernels rather than
+ * expanded in memory ("Perplexity Open-Sources Lily ...", section "The
+ * optimizations follow the workload"; "A Rust + Metal Inference Engine for
+ * Qwen3.6-35B-A3B on Apple Silicon", paragraph 4).  For routed row p < 8T
+ * (sorted position p: token perm[p] / 8 through the expert whose
+ * expert_offsets segment contains p) and shared row 8T + t (the shared
+ * expert on token t): expert_out[row] = Wd (bf16(silu(Wg x) * (Wu x))).
+ * In: x bf16 [T][2048]; routed (n = 256) and shared (n = 1) stacks;
+ * expert_offsets int32 [257] and perm int32 [8T] as from moe_permute.
+ * Out: expert_out fp32 [9T][2048] (16-byte aligned).  opt may be NULL (only
+ * opt->path is read: decode GEMVs up to MOE_DECODE_T_MAX tokens, else the
+ * grouped MFMA GEMM).  Errors as for moe_route, plus MOE_ERR_INVALID_ARG for
+ * a bad expert_stride or path. */
 int moe_expert_ffn(const uint16_t *x, int T, const moe_qffn *routed,
                    const moe_qffn *shared, const int32_t *expert_offsets,
                    const int32_t *perm, float *expert_out, void *ws, size_t ws_bytes,
                    void *stream, const moe_options *opt);
 
-/* Weighted un-permute plus the shared expert:
+/* Weighted un-permute plus the sigmoid-gated shared expert (the layer's
+ * output: the 8 routed experts plus the shared expert, "Perplexity
+ * Open-Sources Lily ...", section "A runtime shaped around one model"):
  * y[t] = bf16( sum_j topk_w[t][j] expert_out[inv_perm[8t+j]]
- *              + shared_gate[t] expert_out[8T+t] ),  fp32 accumulation. */
+ *              + shared_gate[t] expert_out[8T+t] ),  fp32 accumulation in
+ * that order.  In: expert_out fp32 [9T][2048] (16-byte aligned), inv_perm
+ * int32 [8T] (entries outside 0..8T-1 are skipped), topk_w fp32 [T][8],
+ * shared_gate fp32 [T].  Out: y bf16 [T][2048] (16-byte aligned).  Needs no
+ * workspace.  Errors: NULL / T -> MOE_ERR_INVALID_ARG, alignment ->
+ * MOE_ERR_ALIGN. */
 int moe_combine(const float *expert_out, const int32_t *inv_perm, const float *topk_w,
                 const float *shared_gate, int T, uint16_t *y, void *stream);
 
-/* The whole layer, route -> permute -> expert FFN -> combine, enqueued on
- * one stream with no host synchronisation.  y bf16 [T][2048]. */
+/* The whole layer -- route, permute, expert FFN, combine -- enqueued on one
+ * stream with no host synchronisation (routing kept on the GPU:
+ * "Perplexity Open-Sources Lily ...", section "The optimizations follow the
+ * workload"; kernel chains fused: "A Rust + Metal Inference Engine for
+ * Qwen3.6-35B-A3B on Apple Silicon", paragraph 5).  In: x bf16 [T][2048].
+ * Out: y bf16 [T][2048].  Up to MOE_DECODE_T tokens run the few-token path
+ * (three kernels), more the grouped-GEMM path.  Errors as for moe_route. */
 int moe_layer_forward(const uint16_t *x, int T, const moe_layer *layer, uint16_t *y,
                       void *ws, size_t ws_bytes, void *stream);
 
-/* As moe_layer_forward, with options (path override, residual output).
- * `opt` may be NULL. */
+/* As moe_layer_forward, with options: path override, residual output
+ * (bf16(x + y)), route outputs.  opt may be NULL. */
 int moe_layer_forward_ex(const uint16_t *x, int T, const moe_layer *layer, uint16_t *y,
                          void *ws, size_t ws_bytes, void *stream, const moe_options *opt);
+
+/* A chain of layers with residual adds: x_0 = x, y_l = layer_l(x_l),
+ * x_{l+1} = bf16(x_l + y_l); x_out = x_nlayers.  The fused kernel chain of
+ * decode ("A Rust + Metal Inference Engine for Qwen3.6-35B-A3B on Apple
+ * Silicon", paragraph 5): on the few-token path every layer after the first
+ * is two kernels, because each layer's down kernel also forms the next
+ * layer's router logits and fp16 input (deterministically: fixed-point
+ * integer sums).  More tokens run one grouped-GEMM layer after another.
+ * In: x bf16 [T][2048]; layers[nlayers] (host array of descriptors, read
+ * during the call).  Out: x_out bf16 [T][2048]; y_layers: optional bf16
+ * [nlayers][T][2048], each layer's y.  opt: path override and route outputs
+ * (per layer); residual_out must be NULL.  All buffers 16-byte aligned;
+ * ws: moe_workspace_bytes(T) bytes (it also holds the intermediate x_l).
+ * Errors as for moe_layer_forward_ex; nlayers == 0 or T == 0 is a no-op. */
+int moe_chain_forward(const uint16_t *x, int T, const moe_layer *layers, int nlayers,
+                      uint16_t *x_out, uint16_t *y_layers, void *ws, size_t ws_bytes,
+                      void *stream, const moe_options *opt);
+
+/* w_router_t[k][e] = w_router[e][k]: the transposed router matrix a
+ * chained layer's predecessor reads (rows k of it are the router entries
+ * for hidden unit k, so a down kernel holding hidden units m0..m0+3 of the
+ * layer's input reads four contiguous 512-byte rows).  In: w_router bf16
+ * [256][2048]; out: w_router_t bf16 [2048][256]; both 16-byte aligned device
+ * memory, not overlapping.  Enqueues one kernel on stream.  Errors: NULL ->
+ * MOE_ERR_INVALID_ARG, alignment -> MOE_ERR_ALIGN. */
+int moe_router_transpose(const uint16_t *w_router, uint16_t *w_router_t, void *stream);
 
 /* Measurement probes (the pages' method of quoting kernels against the
  * fastest sustained weight-read rate: leslieli.dev note on the Lily engine,

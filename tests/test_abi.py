@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(L):
 def test_header_constants_match_binding():
     src = open(HEADER).read()
     for name in ("MOE_HIDDEN", "MOE_INTER", "MOE_EXPERTS", "MOE_TOPK", "MOE_GROUP", "MOE_T_MAX",
-                 "MOE_DECODE_T", "MOE_DECODE_T_MAX", "MOE_PREFETCH_MAX"):
+                 "MOE_DECODE_T", "MOE_DECODE_T_MAX"):
         m = re.search(rf"#define {name} (\d+)", src)
         assert int(m.group(1)) == getattr(moe, name), name
 
@@ -70,7 +70,7 @@ def _qffn(p=A):
 
 
 def _layer(p=A):
-    return moe.moe_layer(p, None, p, _qffn(p), _qffn(p))
+    return moe.moe_layer(p, None, p, _qffn(p), _qffn(p), None)
 
 
 def test_route_validation(L):
@@ -138,24 +138,68 @@ def test_layer_forward_validation(L):
     assert f(A, 64, C.byref(lay), MIS, A, big, None, None) == ALIGN
     opt = moe.moe_options(moe.MOE_PATH_PREFILL, MIS)
     assert f(A, 64, C.byref(lay), A, A, big, None, C.byref(opt)) == ALIGN
-    # the prefetch range: 16-byte aligned, a multiple of 16 bytes, at most
-    # MOE_PREFETCH_MAX
-    for pf, nb, want in [(MIS, 1024, ALIGN), (A, 1000, INVALID),
-                         (A, moe.MOE_PREFETCH_MAX + 16, INVALID)]:
-        opt = moe.moe_options(moe.MOE_PATH_AUTO, None, pf, nb)
-        assert f(A, 64, C.byref(lay), A, A, big, None, C.byref(opt)) == want, (pf, nb)
+    # route outputs: all three or none, 4-byte aligned
+    for ids, w, sg, want in [(A, None, None, INVALID), (A, A, None, INVALID),
+                             (A, A, A + 2, ALIGN)]:
+        opt = moe.moe_options(moe.MOE_PATH_AUTO, None, ids, w, sg)
+        assert f(A, 64, C.byref(lay), A, A, big, None, C.byref(opt)) == want, (ids, w, sg)
     lb = _layer()
     lb.router_bias = A + 2
     assert f(A, 64, C.byref(lb), A, A, big, None, None) == ALIGN
     lz = _layer()
     lz.w_router = None
     assert L.moe_layer_forward(A, 64, C.byref(lz), A, A, big, None) == INVALID
+    lt = _layer()
+    lt.w_router_t = MIS
+    assert f(A, 64, C.byref(lt), A, A, big, None, None) == ALIGN
 
 
-def test_workspace_init_validation(L):
-    assert L.moe_workspace_init(None, 1 << 20, None) == INVALID
-    assert L.moe_workspace_init(MIS, 1 << 20, None) == ALIGN
-    assert L.moe_workspace_init(A, 8, None) == WS
+def test_chain_forward_validation(L):
+    big = moe.moe_workspace_bytes(4)
+    f = L.moe_chain_forward
+    arr = (moe.moe_layer * 3)(_layer(), _layer(), _layer())
+    assert f(A, 0, arr, 3, A, None, A, big, None, None) == OK           # T = 0: no-op
+    assert f(A, 4, arr, 0, A, None, A, big, None, None) == OK           # no layers: no-op
+    assert f(A, 4, arr, -1, A, None, A, big, None, None) == INVALID
+    assert f(A, 4, None, 3, A, None, A, big, None, None) == INVALID
+    assert f(A, 4, arr, 3, None, None, A, big, None, None) == INVALID
+    assert f(A, 4, arr, 3, A, MIS, A, big, None, None) == ALIGN
+    assert f(A, 4, arr, 3, A, None, A, big - 1, None, None) == WS
+    bad = (moe.moe_layer * 3)(_layer(), _layer(), _layer())
+    bad[2].shared.down_s = MIS                                            # checked in every layer
+    assert f(A, 4, bad, 3, A, None, A, big, None, None) == ALIGN
+    opt = moe.moe_options(moe.MOE_PATH_AUTO, A)                           # residual_out: not for chains
+    assert f(A, 4, arr, 3, A, None, A, big, None, C.byref(opt)) == INVALID
+    opt = moe.moe_options(moe.MOE_PATH_DECODE, None)
+    assert f(A, moe.MOE_DECODE_T_MAX + 1, arr, 3, A, None, A, 1 << 40, None, C.byref(opt)) == INVALID
+
+
+def test_buffer_ranges_fit_32bit_offsets():
+    """The kernels address their buffers with 32-bit buffer-resource ranges
+    and offsets.  At the largest T every whole-buffer range they use must stay
+    below 2^32; the fp32 expert output of the split call does not (9 * 65536
+    rows of 8 KB = 4.83e9 B), which is why the grouped GEMM bases each item's
+    output range at the item's first row (at most 160 rows)."""
+    T, H, I = moe.MOE_T_MAX, moe.MOE_HIDDEN, moe.MOE_INTER
+    whole = {
+        "x rows of the gate/up GEMM (fp16)": T * H * 2,
+        "h rows of the down GEMM (fp16)": 9 * T * I * 2,
+        "router input x (bf16)": T * H * 2,
+        "permutation entries": 8 * T * 4,
+        "fp16 weighted down rows of the fused layer": 9 * T * H * 2,
+    }
+    for what, n in whole.items():
+        assert n < 2 ** 32, what
+    assert 9 * T * H * 4 >= 2 ** 32          # the split call's output: per-item ranges needed
+    assert 160 * H * 4 < 2 ** 31             # one item's rows: far inside the range
+    # the largest row offset inside any whole-buffer range, as the kernels form it
+    assert (9 * T - 1) * I * 2 + (I * 2 - 16) < 2 ** 32
+
+
+def test_router_transpose_validation(L):
+    assert L.moe_router_transpose(None, A, None) == INVALID
+    assert L.moe_router_transpose(A, None, None) == INVALID
+    assert L.moe_router_transpose(A, MIS, None) == ALIGN
 
 
 def test_probe_validation(L):

@@ -92,3 +92,32 @@ def test_combine_within_rounding(gpu, T):
     same = np.mean(got == ref)
     P.say(f"  combine T={T}: identical to the oracle's bf16 on {same:.5f} of outputs")
     assert same > 0.999
+
+
+def test_expert_ffn_max_t_split(gpu):
+    """The split FFN at the largest T (65536 tokens, the grouped-GEMM path):
+    its fp32 output is 4.83e9 bytes, beyond a 32-bit range, so rows past 2^32
+    bytes -- the shared-expert rows 8T .. 9T-1 among them -- must land where
+    they belong.  Seeded random routing (any routing is a valid input here);
+    sampled rows against the oracle, including the first and last routed and
+    shared rows."""
+    T = moe.MOE_T_MAX
+    P.say(f"expert_ffn split T={T}")
+    L = P.host_layer(0, 0)
+    rng = np.random.default_rng(65536)
+    ids = np.argsort(rng.random((T, 256), dtype=np.float32), axis=1)[:, :8].astype(np.int32)
+    pm = P.orc().permute(synth.PROD, ids)
+    x = synth.make_x(T, seed=17, layer=5)
+    D = P.dev_layer(0, 0)
+    out = torch.empty(((8 + 1) * T, 2048), dtype=torch.float32, device="cuda")
+    out.fill_(float("nan"))
+    moe.moe_expert_ffn(moe.to_device_bits(x), D, torch.from_numpy(pm.offsets).cuda(),
+                       torch.from_numpy(pm.perm).cuda(), out, moe.workspace(T), path=PRE)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([rng.choice(9 * T, 60, replace=False),
+                                     [0, 1, 8 * T - 1, 8 * T, 8 * T + 1, 9 * T - 1]])).astype(np.int32)
+    got = out[torch.from_numpy(rows.astype(np.int64)).cuda()].cpu().numpy().astype(np.float64)
+    del out
+    assert np.all(np.isfinite(got)), "a sampled row was never written"
+    ref = P.orc().expert_ffn(L, x, pm.offsets, pm.perm, rows=rows)
+    P.assert_close(got, ref, f"expert_out sampled T={T}")
