@@ -27,6 +27,8 @@ MOE_GROUP = 64
 MOE_T_MAX = 65536
 MOE_DECODE_T = 8
 MOE_DECODE_T_MAX = 32
+MOE_NOALLOC_T_MAX = 64
+MOE_NOALLOC_WS_BYTES = 8388608
 
 MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1
@@ -35,7 +37,8 @@ MOE_PATH_PREFILL = 2
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
-           "moe_chain_forward", "moe_router_transpose", "moe_probe_read", "moe_probe_copy")
+           "moe_chain_forward", "moe_chain_forward_noalloc", "moe_router_transpose",
+           "moe_probe_read", "moe_probe_copy")
 
 
 class MoeError(RuntimeError):
@@ -89,6 +92,8 @@ def lib() -> C.CDLL:
                                        C.POINTER(moe_options)]
     L.moe_chain_forward.argtypes = [vp, i32, C.POINTER(moe_layer), i32, vp, vp, vp, sz, vp,
                                     C.POINTER(moe_options)]
+    L.moe_chain_forward_noalloc.argtypes = [vp, i32, C.POINTER(moe_layer), i32, vp, vp, vp,
+                                            C.POINTER(moe_options)]
     L.moe_router_transpose.argtypes = [vp, vp, vp]
     L.moe_probe_read.argtypes = [vp, sz, vp, vp]
     L.moe_probe_copy.argtypes = [vp, vp, sz, vp]
@@ -342,6 +347,19 @@ def moe_layer_forward(x, layer: DeviceLayer, y, ws, stream=None) -> None:
     _check("moe_layer_forward", lib().moe_layer_forward(
         _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.c),
         _ptr(y, "y", _U16, (T, MOE_HIDDEN)), wsp, wsn, _stream(stream)))
+
+
+def moe_chain_forward_noalloc(x, chain: LayerChain, x_out, y_layers=None,
+                              path: int = MOE_PATH_AUTO, route_out=None, stream=None) -> None:
+    """moe_chain_forward with the library's own fixed device workspace (no
+    allocation in the call; T <= MOE_NOALLOC_T_MAX)."""
+    T, n = x.shape[0], len(chain)
+    ri, rw, rs = _route_out(route_out, T, n)
+    opt = moe_options(path, None, ri, rw, rs)
+    _check("moe_chain_forward_noalloc", lib().moe_chain_forward_noalloc(
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, chain.c, n,
+        _ptr(x_out, "x_out", _U16, (T, MOE_HIDDEN)),
+        _ptr(y_layers, "y_layers", _U16, (n, T, MOE_HIDDEN)), _stream(stream), C.byref(opt)))
 
 
 def moe_router_transpose(w_router, w_router_t, stream=None) -> None:

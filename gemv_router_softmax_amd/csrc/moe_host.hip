@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -415,6 +416,52 @@ int moe_chain_forward(const uint16_t* x, int T, const moe_layer* layers, int nla
         }
     }
     return launch_status();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The workspace of moe_chain_forward_noalloc: a fixed device array that the
+// library owns (each GPU the library runs on holds its own copy until the
+// process ends), for callers that cannot allocate.  In host code the array's
+// name is only a stand-in for its device address; the address each device
+// actually uses is taken once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_WS_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's scratch address (NULL on a HIP error).
+void* scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int moe_chain_forward_noalloc(const uint16_t* x, int T, const moe_layer* layers, int nlayers,
+                              uint16_t* x_out, uint16_t* y_layers, void* stream,
+                              const moe_options* opt) {
+    if (T < 0 || T > MOE_NOALLOC_T_MAX) return MOE_ERR_INVALID_ARG;
+    static_assert(MOE_NOALLOC_WS_BYTES % 256 == 0, "scratch size");
+    const size_t need = moe_workspace_bytes(T);
+    if (need > MOE_NOALLOC_WS_BYTES) return MOE_ERR_WORKSPACE;   // (never, for T in range)
+    if (T == 0 || nlayers == 0) return moe_chain_forward(x, T, layers, nlayers, x_out, y_layers,
+                                                         nullptr, 0, stream, opt);
+    void* ws = scratch_ptr();
+    if (!ws) return MOE_ERR_HIP;
+    return moe_chain_forward(x, T, layers, nlayers, x_out, y_layers, ws, MOE_NOALLOC_WS_BYTES,
+                             stream, opt);
 }
 
 int moe_router_transpose(const uint16_t* w_router, uint16_t* w_router_t, void* stream) {

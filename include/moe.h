@@ -245,6 +245,24 @@ int moe_chain_forward(const uint16_t *x, int T, const moe_layer *layers, int nla
                       uint16_t *x_out, uint16_t *y_layers, void *ws, size_t ws_bytes,
                       void *stream, const moe_options *opt);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as moe_chain_forward with the workspace taken from a fixed device
+ * array the library owns (MOE_NOALLOC_WS_BYTES per GPU, held until the
+ * process ends), for up to MOE_NOALLOC_T_MAX tokens; larger T returns
+ * MOE_ERR_INVALID_ARG.  No allocation or free happens in the call.  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or different host threads without ordering)
+ * race and must not be made; calls ordered on one stream are fine.  Nothing
+ * in the array needs clearing between calls.  Other arguments, outputs and
+ * errors as for moe_chain_forward; a HIP error while locating the array
+ * returns MOE_ERR_HIP. */
+#define MOE_NOALLOC_T_MAX 64
+#define MOE_NOALLOC_WS_BYTES 8388608
+int moe_chain_forward_noalloc(const uint16_t *x, int T, const moe_layer *layers, int nlayers,
+                              uint16_t *x_out, uint16_t *y_layers, void *stream,
+                              const moe_options *opt);
+
 /* w_router_t[k][e] = w_router[e][k]: the transposed router matrix a
  * chained layer's predecessor reads (rows k of it are the router entries
  * for hidden unit k, so a down kernel holding hidden units m0..m0+3 of the

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(L):
 def test_header_constants_match_binding():
     src = open(HEADER).read()
     for name in ("MOE_HIDDEN", "MOE_INTER", "MOE_EXPERTS", "MOE_TOPK", "MOE_GROUP", "MOE_T_MAX",
-                 "MOE_DECODE_T", "MOE_DECODE_T_MAX"):
+                 "MOE_DECODE_T", "MOE_DECODE_T_MAX", "MOE_NOALLOC_T_MAX", "MOE_NOALLOC_WS_BYTES"):
         m = re.search(rf"#define {name} (\d+)", src)
         assert int(m.group(1)) == getattr(moe, name), name
 
@@ -194,6 +194,15 @@ def test_buffer_ranges_fit_32bit_offsets():
     assert 160 * H * 4 < 2 ** 31             # one item's rows: far inside the range
     # the largest row offset inside any whole-buffer range, as the kernels form it
     assert (9 * T - 1) * I * 2 + (I * 2 - 16) < 2 ** 32
+
+
+def test_chain_noalloc_validation(L):
+    f = L.moe_chain_forward_noalloc
+    arr = (moe.moe_layer * 2)(_layer(), _layer())
+    assert f(A, 0, arr, 2, A, None, None, None) == OK                      # T = 0: no-op
+    assert f(A, moe.MOE_NOALLOC_T_MAX + 1, arr, 2, A, None, None, None) == INVALID
+    assert f(A, -1, arr, 2, A, None, None, None) == INVALID
+    assert moe.moe_workspace_bytes(moe.MOE_NOALLOC_T_MAX) <= moe.MOE_NOALLOC_WS_BYTES
 
 
 def test_router_transpose_validation(L):
