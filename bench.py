@@ -371,6 +371,47 @@ def skewed_chunked(T_total, chunk, iters, layers=4):
             "mfma_util": flops / t / (BF16_DENSE_PEAK_TFLOPS * 1e12)}
 
 
+GREEDY_V = 151936     # synthetic vocabulary (the pages give none): a Qwen-family size
+
+
+def greedy_decode(D, steps, V=GREEDY_V, reps=10):
+    """The greedy decode step kept on the GPU: embedding lookup of the
+    previous token -> the whole layer chain -> output-head GEMV + argmax ->
+    the next token, in device memory for the next step; one HIP graph per
+    step.  Also the head kernel alone (HIP events around eager calls):
+    V x 4 KB of bf16 head per call."""
+    import torch
+    import gemv_router_softmax_amd as moe
+    from gemv_router_softmax_amd import synth
+    head, emb = synth.make_head(V, seed=0)
+    hd, ed = moe.to_device_bits(head), moe.to_device_bits(emb)
+    del head, emb
+    chain = moe.LayerChain(D)
+    tok = torch.tensor([1], dtype=torch.int32, device="cuda")
+    x = torch.empty((1, H), dtype=torch.int16, device="cuda")
+    xo = torch.empty_like(x)
+    ws = moe.workspace(1)
+
+    def step():
+        moe.moe_embed(tok, ed, x)
+        moe.moe_chain_forward(x, chain, xo, ws)
+        moe.moe_lm_head_argmax(xo, hd, tok, ws)
+    ms = _graphs_timed([step], steps)
+    pairs = event_pairs(reps)
+    for a, b in pairs:
+        a.record()
+        moe.moe_lm_head_argmax(xo, hd, tok, ws)
+        b.record()
+    torch.cuda.synchronize()
+    hms = np.array([a.elapsed_time(b) for a, b in pairs])
+    hbytes = V * H * 2 + H * 2
+    t = float(ms.mean()) * 1e-3
+    return {"vocab": V, "layers": len(D), "step_ms": t * 1e3, "tokens_per_s": 1.0 / t,
+            "head_ms": float(hms.mean()), "head_gbs": hbytes / (hms.mean() * 1e-3) / 1e9,
+            "head_frac_of_hbm_peak": hbytes / (hms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "timing": "graph replays of the whole step; head: HIP events around eager calls"}
+
+
 def cpu_baseline(layers, budget_s):
     import oracle
     from gemv_router_softmax_amd import synth
@@ -458,6 +499,11 @@ def main():
         skewed = skewed_chunked(16384, 4096, 8)
         log(f"skewed chunked prefill: {skewed}")
 
+    greedy = None
+    if not args.no_extra:
+        greedy = greedy_decode(D, 200)
+        log(f"greedy decode step: {greedy}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host, args.cpu_seconds)
@@ -495,6 +541,7 @@ def main():
         "prefill_sweep": sweep,
         "prefill_chain_t512": chain512,
         "prefill_skewed_t16384_chunks4096": skewed,
+        "greedy_decode_step": greedy,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -37,8 +37,8 @@ MOE_PATH_PREFILL = 2
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
-           "moe_chain_forward", "moe_chain_forward_noalloc", "moe_router_transpose",
-           "moe_probe_read", "moe_probe_copy")
+           "moe_chain_forward", "moe_chain_forward_noalloc", "moe_lm_head_argmax", "moe_embed",
+           "moe_router_transpose", "moe_probe_read", "moe_probe_copy")
 
 
 class MoeError(RuntimeError):
@@ -95,6 +95,8 @@ def lib() -> C.CDLL:
     L.moe_chain_forward_noalloc.argtypes = [vp, i32, C.POINTER(moe_layer), i32, vp, vp, vp,
                                             C.POINTER(moe_options)]
     L.moe_router_transpose.argtypes = [vp, vp, vp]
+    L.moe_lm_head_argmax.argtypes = [vp, i32, vp, i32, vp, vp, sz, vp]
+    L.moe_embed.argtypes = [vp, i32, vp, i32, vp, vp]
     L.moe_probe_read.argtypes = [vp, sz, vp, vp]
     L.moe_probe_copy.argtypes = [vp, vp, sz, vp]
     for fn in EXPORTS:
@@ -360,6 +362,23 @@ def moe_chain_forward_noalloc(x, chain: LayerChain, x_out, y_layers=None,
         _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, chain.c, n,
         _ptr(x_out, "x_out", _U16, (T, MOE_HIDDEN)),
         _ptr(y_layers, "y_layers", _U16, (n, T, MOE_HIDDEN)), _stream(stream), C.byref(opt)))
+
+
+def moe_lm_head_argmax(x, w_head, token, ws, stream=None) -> None:
+    """token[t] = argmax_v x[t] . w_head[v] (ties to the lower v), on the device."""
+    T, V = x.shape[0], w_head.shape[0]
+    wsp, wsn = _ws(ws)
+    _check("moe_lm_head_argmax", lib().moe_lm_head_argmax(
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, _ptr(w_head, "w_head", _U16, (V, MOE_HIDDEN)), V,
+        _ptr(token, "token", torch.int32, (T,)), wsp, wsn, _stream(stream)))
+
+
+def moe_embed(token, emb, x, stream=None) -> None:
+    """x[t] = emb[token[t]] (zeros for a token outside the table), on the device."""
+    T, V = token.shape[0], emb.shape[0]
+    _check("moe_embed", lib().moe_embed(
+        _ptr(token, "token", torch.int32, (T,)), T, _ptr(emb, "emb", _U16, (V, MOE_HIDDEN)), V,
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), _stream(stream)))
 
 
 def moe_router_transpose(w_router, w_router_t, stream=None) -> None:

@@ -64,6 +64,11 @@ void launch_combine_f16(const uint16_t* d16, const int32_t* inv, int T, uint16_t
 void launch_combine(const float* out, const int32_t* inv, const float* wts, const float* sg, int T,
                     uint16_t* y, const uint16_t* x, uint16_t* res, hipStream_t st);
 void launch_router_transpose(const uint16_t* wr, uint16_t* wrt, hipStream_t st);
+size_t head_part_bytes();
+void launch_head_argmax(const uint16_t* x, int T, const uint16_t* w, int V, int32_t* token,
+                        unsigned long long* part, hipStream_t st);
+void launch_embed(const int32_t* token, int T, const uint16_t* emb, int V, uint16_t* x,
+                  hipStream_t st);
 void launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t st);
 void launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 
@@ -71,8 +76,8 @@ namespace {
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct WsLayout {
-    size_t rec, acc, logits, ids, wts, sg, counts, offsets, perm, inv, wsorted, chunk_counts, tiles,
-        tile_count, xh, h, dout, chain, total;
+    size_t rec, acc, head, logits, ids, wts, sg, counts, offsets, perm, inv, wsorted, chunk_counts,
+        tiles, tile_count, xh, h, dout, chain, total;
 };
 
 WsLayout ws_layout(int T) {
@@ -88,6 +93,7 @@ WsLayout ws_layout(int T) {
     const size_t ts = t < MOE_DECODE_T ? t : MOE_DECODE_T;
     L.rec = take(route_rec_bytes());
     L.acc = take(route_acc_bytes((int)ts));     // two sets of fixed-point logits
+    L.head = take(head_part_bytes());           // greedy selection: per-workgroup keys
     L.logits = take(t * E * 4);
     L.ids = take(t * TOPK * 4);
     L.wts = take(t * TOPK * 4);
@@ -462,6 +468,27 @@ int moe_chain_forward_noalloc(const uint16_t* x, int T, const moe_layer* layers,
     if (!ws) return MOE_ERR_HIP;
     return moe_chain_forward(x, T, layers, nlayers, x_out, y_layers, ws, MOE_NOALLOC_WS_BYTES,
                              stream, opt);
+}
+
+int moe_lm_head_argmax(const uint16_t* x, int T, const uint16_t* w_head, int V, int32_t* token,
+                       void* ws, size_t ws_bytes, void* stream) {
+    if (T < 1 || T > MOE_DECODE_T || V < 1) return MOE_ERR_INVALID_ARG;
+    if (!x || !w_head || !token || !ws) return MOE_ERR_INVALID_ARG;
+    if (!a16(x) || !a16(w_head) || !a4(token) || !a16(ws)) return MOE_ERR_ALIGN;
+    const WsLayout L = ws_layout(T);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    launch_head_argmax(x, T, w_head, V, token, at<unsigned long long>(ws, L.head),
+                       (hipStream_t)stream);
+    return launch_status();
+}
+
+int moe_embed(const int32_t* token, int T, const uint16_t* emb, int V, uint16_t* x, void* stream) {
+    if (check_T(T) || V < 1) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!token || !emb || !x) return MOE_ERR_INVALID_ARG;
+    if (!a4(token) || !a16(emb) || !a16(x)) return MOE_ERR_ALIGN;
+    launch_embed(token, T, emb, V, x, (hipStream_t)stream);
+    return launch_status();
 }
 
 int moe_router_transpose(const uint16_t* w_router, uint16_t* w_router_t, void* stream) {

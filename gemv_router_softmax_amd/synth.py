@@ -47,6 +47,8 @@ _TID_WSG = 2
 _TID_ROUTED = 3      # 3..8: gate_q, gate_s, up_q, up_s, down_q, down_s
 _TID_SHARED = 9      # 9..14: same for the shared expert
 _TID_RANKS = 15
+_TID_HEAD = 16       # greedy step: output head [V, H]
+_TID_EMB = 17        # greedy step: embedding table [V, H]
 _STEP_BASE = 100000  # chain-step inputs use layer key STEP_BASE + step
 
 
@@ -169,6 +171,14 @@ def make_x(T: int, dims: Dims = PROD, seed: int = 0, layer: int = 0,
     key = layer if step is None else _STEP_BASE + step
     a = _rng(seed, key, _TID_X).standard_normal((T, dims.H), dtype=np.float32)
     return f32_to_bf16_bits(a)
+
+
+def make_head(V: int, dims: Dims = PROD, seed: int = 0) -> tuple:
+    """The greedy decode step's synthetic tables (the pages give none): an
+    output head and an embedding table, bf16 bits [V, H], ~N(0, 0.02^2)."""
+    head = 0.02 * _rng(seed, 0, _TID_HEAD).standard_normal((V, dims.H), dtype=np.float32)
+    emb = 0.02 * _rng(seed, 0, _TID_EMB).standard_normal((V, dims.H), dtype=np.float32)
+    return f32_to_bf16_bits(head), f32_to_bf16_bits(emb)
 
 
 # ---- hand-built layers for closed-form pins -------------------------------

@@ -245,6 +245,27 @@ int moe_chain_forward(const uint16_t *x, int T, const moe_layer *layers, int nla
                       uint16_t *x_out, uint16_t *y_layers, void *ws, size_t ws_bytes,
                       void *stream, const moe_options *opt);
 
+/* Greedy next-token selection after the last layer, kept on the GPU for
+ * the next decode step ("Perplexity Open-Sources Lily ...", section
+ * "Generation has a different bottleneck").  The pages give no output head;
+ * the library's: a bf16 head w_head [V][2048] applied to the bf16 hidden
+ * state, logit[t][v] = x[t] . w_head[v] with fp32 accumulation of exact
+ * bf16 products, token[t] = argmax_v logit[t][v], ties to the lower v.
+ * In: x bf16 [T][2048], 1 <= T <= MOE_DECODE_T; w_head bf16 [V][2048],
+ * 1 <= V < 2^31 (16-byte aligned).  Out: token int32 [T] (device memory, 4-byte
+ * aligned).  ws: moe_workspace_bytes(T) bytes.  Errors: NULL, T or V out of
+ * range -> MOE_ERR_INVALID_ARG; alignment -> MOE_ERR_ALIGN; ws too small ->
+ * MOE_ERR_WORKSPACE. */
+int moe_lm_head_argmax(const uint16_t *x, int T, const uint16_t *w_head, int V, int32_t *token,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* The next decode step's input rows from the selected tokens, read on the
+ * device: x[t] = emb[token[t]] (a row of zeros for a token outside 0..V-1).
+ * In: token int32 [T] (device), emb bf16 [V][2048] (16-byte aligned).  Out:
+ * x bf16 [T][2048].  T in 0..MOE_T_MAX (0: no-op).  Errors: NULL or a size
+ * out of range -> MOE_ERR_INVALID_ARG; alignment -> MOE_ERR_ALIGN. */
+int moe_embed(const int32_t *token, int T, const uint16_t *emb, int V, uint16_t *x, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * call as moe_chain_forward with the workspace taken from a fixed device

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -203,6 +203,22 @@ def test_chain_noalloc_validation(L):
     assert f(A, moe.MOE_NOALLOC_T_MAX + 1, arr, 2, A, None, None, None) == INVALID
     assert f(A, -1, arr, 2, A, None, None, None) == INVALID
     assert moe.moe_workspace_bytes(moe.MOE_NOALLOC_T_MAX) <= moe.MOE_NOALLOC_WS_BYTES
+
+
+def test_greedy_validation(L):
+    big = moe.moe_workspace_bytes(8)
+    f = L.moe_lm_head_argmax
+    assert f(A, 0, A, 100, A, A, big, None) == INVALID
+    assert f(A, moe.MOE_DECODE_T + 1, A, 100, A, A, 1 << 40, None) == INVALID
+    assert f(A, 1, A, 0, A, A, big, None) == INVALID
+    assert f(A, 1, None, 100, A, A, big, None) == INVALID
+    assert f(MIS, 1, A, 100, A, A, big, None) == ALIGN
+    assert f(A, 1, A, 100, A, A, 16, None) == WS
+    g = L.moe_embed
+    assert g(A, 0, A, 100, A, None) == OK
+    assert g(A, 3, A, 0, A, None) == INVALID
+    assert g(A, 3, None, 100, A, None) == INVALID
+    assert g(A, 3, A, 100, MIS, None) == ALIGN
 
 
 def test_router_transpose_validation(L):
