@@ -188,20 +188,59 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode layer launch from the committed rocprofv3 PMC
-    summary (JSON block in profiles/decode_layer_t1_traffic.md), or None if
-    it is missing or was taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "decode_layer_t1_traffic.md")
+EXPERT_SOURCES = ("expert.hip", "block_util.hpp", "common.hpp", "moe_host.hip")
+
+
+def expert_source_hash():
+    """Hash of the sources of the prefill grouped GEMM."""
+    h = hashlib.sha256()
+    for f in EXPERT_SOURCES:
+        with open(os.path.join(ROOT, "gemv_router_softmax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profile_json(name, source_hash):
+    """The JSON block of a committed rocprofv3 summary under profiles/, or
+    None if it is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as fh:
             m = re.search(r"```json\n(.*?)\n```", fh.read(), re.S)
         d = json.loads(m.group(1))
     except (OSError, AttributeError, ValueError):
         return None
-    if d.get("source_hash") != decode_source_hash():
+    if d.get("source_hash") != source_hash:
         return None
-    return d.get("bytes_per_launch")
+    return d
+
+
+def measured_traffic():
+    """HBM bytes per chained decode layer (decode_gateup_dec +
+    decode_down_dec) from the rocprofv3 PMC summary."""
+    d = profile_json("decode_layer_t1_traffic.md", decode_source_hash())
+    return None if d is None else d.get("bytes_per_launch")
+
+
+def kernel_level_decode():
+    """SURVEY's kernel-level decode figure: the active-expert bytes of a
+    layer (9 x 1,769,472 B) over the summed average rocprofv3 durations of
+    the two expert kernels of a chained layer, from the kernel-trace
+    summary of the 40-layer chain."""
+    d = profile_json("decode_t1_chain40_kernel_stats.md", decode_source_hash())
+    if d is None:
+        return None
+    us = d["decode_gateup_dec_avg_us"] + d["decode_down_dec_avg_us"]
+    gbs = 9 * EXPERT_BYTES / (us * 1e-6) / 1e9
+    return {"expert_bytes": 9 * EXPERT_BYTES, "kernels_us": us, "gbs": gbs,
+            "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "source": "profiles/decode_t1_chain40_kernel_stats.md"}
+
+
+def gemm_clock():
+    """Shader clock inside the prefill GEMM kernels (GRBM_GUI_ACTIVE cycles
+    over the dispatch duration, from the rocprofv3 counter summary)."""
+    d = profile_json("prefill_t4096_gemm_clock.md", expert_source_hash())
+    return None if d is None else {"per_kernel_ghz": d["ghz"], "time_weighted_ghz": d["ghz_weighted"]}
 
 
 def buf_gbs(nbytes, ms):
@@ -267,9 +306,14 @@ def prefill(D, T, iters):
     fms = timed(ffn_graphs)
     del ffn_graphs
     flops = EXPERT_FLOP_PER_TOKEN * 9 * T
+    clk = gemm_clock()
     return {
         "T": T,
         "timing": "HIP events around graph replays, one layer per replay",
+        "gemm_clock_ghz": clk,
+        "expert_ffn_mfma_util_at_measured_clock": (
+            None if clk is None else flops / (fms.mean() * 1e-3)
+            / (BF16_DENSE_PEAK_TFLOPS * 1e12 * clk["time_weighted_ghz"] / 2.4)),
         "layer_ms": float(ms.mean()),
         "tokens_per_s": T / (ms.mean() * 1e-3),
         "layer_mfma_util": flops / (ms.mean() * 1e-3) / (BF16_DENSE_PEAK_TFLOPS * 1e12),
@@ -412,24 +456,64 @@ def greedy_decode(D, steps, V=GREEDY_V, reps=10):
             "timing": "graph replays of the whole step; head: HIP events around eager calls"}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(layers, budget_s):
+    """The oracle (plain fp64 C, OpenMP) timed on this host on bounded
+    samples: decode T = 1 through the whole chain on all threads (the line's
+    value) and on one thread, and the first 512 tokens of the T = 4096
+    prefill input through one layer."""
     import oracle
     from gemv_router_softmax_amd import synth
     o = oracle.load()
+    nthreads = o.threads()
+
+    def decode(budget, max_steps):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            x = synth.make_x(1, seed=0, step=n)
+            for L in layers:
+                y = o.layer_forward(L, x).y
+                x = o.round_bf16(o.bf16_decode(x) + o.bf16_decode(y))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget or n >= max_steps:
+                return n, el
+
+    n, el = decode(budget_s * 0.6, 64)
+    o.set_threads(1)
+    n1, el1 = decode(budget_s * 0.25, 64)
+    o.set_threads(nthreads)
+    xp = synth.make_x(4096, seed=0)[:512]
     t0 = time.perf_counter()
-    n = 0
-    while True:
-        x = synth.make_x(1, seed=0, step=n)
-        for L in layers:
-            y = o.layer_forward(L, x).y
-            x = o.round_bf16(o.bf16_decode(x) + o.bf16_decode(y))
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 64:
-            break
-    return {"value": n / el, "unit": "tokens/s", "cores": o.threads(), "kind": "oracle",
+    o.layer_forward(layers[3 % len(layers)], xp)
+    elp = time.perf_counter() - t0
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except OSError:
+        affinity = None
+    return {"value": n / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{n} decode steps (T=1) through the same {len(layers)}-layer chain, "
-                      f"{el:.1f} s of CPU work"}
+                      f"{el:.1f} s of CPU work on {nthreads} threads",
+            "single_thread": {"value": n1 / el1, "unit": "tokens/s",
+                              "sample": f"{n1} decode steps through the {len(layers)}-layer "
+                                        f"chain, {el1:.1f} s"},
+            "prefill_t4096_sample": {"value": 512 / elp, "unit": "tokens/s",
+                                     "sample": f"the first 512 of the 4096 prefill tokens "
+                                               f"through one layer, {elp:.1f} s on {nthreads} "
+                                               f"threads"},
+            "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+            "affinity_cpus": affinity}
 
 
 def main():
@@ -533,7 +617,9 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode layer at T=1 inside the chain (decode_gateup_dec + "
                                "decode_down_dec), eager chain behind a long read",
-                     "bytes_per_launch": per_launch_bytes, "launch_us": k_mean * 1e3},
+                     "bytes_per_launch": per_launch_bytes, "launch_us": k_mean * 1e3,
+                     "frac_of_read_ceiling": achieved / ceiling,
+                     "kernel_level": kernel_level_decode()},
         "active_expert_bytes_per_token": chain_bytes,
         "wallclock_gbs": chain_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_read_ceiling_gbs": ceiling,

@@ -1,16 +1,24 @@
-// decode.hip -- the few-token (decode) path of the MoE layer.
+// decode.hip -- the decode (dequantising GEMV) paths of the MoE layer.
 //
 // Decode is memory bound (leslieli.dev note on the Lily engine, paragraph 5:
-// the sparse GEMV barely changes when its arithmetic is removed) and, at one
-// token, dominated by latency, so the layer runs as four kernels with no
-// host involvement:
+// the sparse GEMV barely changes when its arithmetic is removed) and, at a
+// few tokens, dominated by latency.  Two paths, neither with host
+// involvement:
+//
+// Few tokens (T <= MOE_DECODE_T, the default there), further below: a layer
+// on its own is three kernels (router logits | gate/up with the top-8 inside
+// | down with the combine and the residual add); inside a chain every layer
+// after the first is two, because the down kernel also forms the next
+// layer's router logits.
+//
+// Up to MOE_DECODE_T_MAX tokens when the decode path is forced, four
+// kernels:
 //
 //   route_logits_gemv   (route.hip) logits of the 256 experts
-//   route_select        ONE workgroup: top-8 per token by radix selection on
-//                       the fp32 logits (ties to the lower expert index),
-//                       renormalised softmax weights, the shared-expert gate,
-//                       the stable permutation, the row-tile list and the fp16
-//                       copy of x the GEMV reads
+//   route_select        ONE workgroup: top-8 per token (ties to the lower
+//                       expert index), renormalised softmax weights, the
+//                       shared-expert gate, the stable permutation, the
+//                       row-tile list and the fp16 copy of x the GEMV reads
 //   decode_gateup       16 gate rows + 16 up rows of one active expert per
 //                       workgroup; every lane streams 16 B of each row
 //                       (coalesced 128-bit loads, all issued up front) and
@@ -291,22 +299,23 @@ __global__ __launch_bounds__(256) void decode_down_combine(
 //                      publishes the down record.  h rows are compact: the T
 //                      shared rows, then every (expert, token) pair in
 //                      ascending expert order, 9T rows in all;
-//   decode_down_dec    32 output rows per workgroup over every slot, with
-//                      the h rows staged in LDS; combine with the routing
+//   decode_down_dec    DN_ROWS output rows per workgroup over every slot
+//                      (each wave a row group x a slot group), h rows read
+//                      straight from global memory; combine with the routing
 //                      weights and the shared gate, residual add.  Inside a
 //                      chain it also writes the next layer's fp16
 //                      activations and adds its share of the next layer's
 //                      router logits.
 //
-// Router logits in 64-bit fixed point: a down workgroup of a chain holds 32
-// entries of the next layer's input, so it can form its partial router sums
-// for all 257 logits itself (fp32, in a fixed order) and add round(p * 2^32)
-// to the next layer's accumulators with integer atomics.  Integer addition is
-// associative, so the sum does not depend on the order in which the 64
-// workgroups' atomics land: the routing stays deterministic.  This takes the
-// router kernel and one kernel boundary off every chained layer -- the decode
-// chain fused across layers ("A Rust + Metal Inference Engine for
-// Qwen3.6-35B-A3B on Apple Silicon", paragraph 5).
+// Router logits in 64-bit fixed point: a down workgroup of a chain holds
+// DN_ROWS entries of the next layer's input, so it can form its partial
+// router sums for all 257 logits itself (fp32, in a fixed order) and add
+// round(p * 2^32) to the next layer's accumulators with integer atomics.
+// Integer addition is associative, so the sum does not depend on the order
+// in which the DN_WG workgroups' atomics land: the routing stays
+// deterministic.  This takes the router kernel and one kernel boundary off
+// every chained layer -- the decode chain fused across layers ("A Rust +
+// Metal Inference Engine for Qwen3.6-35B-A3B on Apple Silicon", paragraph 5).
 //
 // Ids read back from the record are clamped, so a corrupted record cannot
 // send a load outside the weights.
@@ -347,7 +356,6 @@ static_assert(DN_WG % ACC_COPIES == 0, "accumulator copies");
 static_assert(64 * DN_WAVES <= 1024, "workgroup size");
 
 constexpr int ACC_N = E + 1;
-typedef __attribute__((address_space(3))) void* dn_lds_t;
 constexpr int ACC_STRIDE = 264;                 // 32-byte aligned per token
 constexpr double ACC_ONE = 4294967296.0;        // 2^32
 static_assert(ACC_STRIDE >= ACC_N && ACC_STRIDE % 4 == 0, "accumulator layout");

@@ -127,6 +127,8 @@ class Oracle:
         vp, i32, i64 = C.c_void_p, C.c_int, C.c_int64
         L.oracle_mutant.restype = i32
         L.oracle_threads.restype = i32
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_set_threads.restype = None
         L.oracle_bf16_to_double.argtypes = [C.c_uint16]
         L.oracle_bf16_to_double.restype = C.c_double
         L.oracle_fp16_to_double.argtypes = [C.c_uint16]
@@ -158,6 +160,10 @@ class Oracle:
 
     def threads(self) -> int:
         return int(self.lib.oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Thread count of the OpenMP loops from here on (timing only)."""
+        self.lib.oracle_set_threads(int(n))
 
     # ---- formats
     def round_bf16(self, a) -> np.ndarray:

@@ -65,6 +65,11 @@ int oracle_mutant(void) { return ORACLE_MUTANT; }
 /* Threads the OpenMP loops use (reported with the CPU baseline). */
 int oracle_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the thread count of the OpenMP loops that follow (n >= 1); for timing
+ * the same code on one core and on all of them.  No effect on the results:
+ * every loop writes disjoint outputs. */
+void oracle_set_threads(int n) { omp_set_num_threads(n < 1 ? 1 : n); }
+
 /* ---------------------------------------------------------------- formats */
 
 /* bf16 is the upper half of an IEEE binary32 word. */
