@@ -374,6 +374,13 @@ __device__ __forceinline__ float acc_val(long long q) { return (float)((double)q
 __device__ __forceinline__ float4v load_logits4(const long long* __restrict__ acc, int T,
                                                 const float* __restrict__ bias, int t, int lane) {
     typedef long long ll2 __attribute__((ext_vector_type(2)));
+    // the bias first, with no branch around the load (a missing bias is an
+    // empty buffer range, which reads as zeros): behind a branch the load
+    // would go out only after the logits had arrived
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(bias), 0, bias ? (uint32_t)(E * sizeof(float)) : 0u, 0x00020000);
+    const float4v bv = __builtin_bit_cast(
+        float4v, __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(16 * lane), 0, 0));
     ll2 pa[ACC_COPIES], pb[ACC_COPIES];
 #pragma unroll
     for (int c = 0; c < ACC_COPIES; ++c) {
@@ -388,11 +395,7 @@ __device__ __forceinline__ float4v load_logits4(const long long* __restrict__ ac
         b += pb[c];
     }
     float4v v = {acc_val(a[0]), acc_val(a[1]), acc_val(b[0]), acc_val(b[1])};
-    if (bias) {     // (4-byte aligned: four scalar loads)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] += bias[4 * lane + j];
-    }
-    return v;
+    return v + bv;
 }
 
 // The routing of up to MOE_DECODE_T tokens, in LDS of the gate/up kernel.
@@ -468,19 +471,39 @@ __device__ __forceinline__ const GLOBAL_AS T* gexpert(const GLOBAL_AS T* p, int 
     return (const GLOBAL_AS T*)((const GLOBAL_AS char*)p + (size_t)e * stride);
 }
 
+// The shared-gate logit of token t: the ACC_COPIES accumulator words, loads
+// issued here and summed by acc_zsum where the logit is needed, so that the
+// loads travel with the router logits' loads instead of before them.
+struct ZLoads {
+    long long q[ACC_COPIES];
+};
+__device__ __forceinline__ ZLoads acc_zload(const long long* __restrict__ acc, int T, int t) {
+    ZLoads z;
+#pragma unroll
+    for (int c = 0; c < ACC_COPIES; ++c) z.q[c] = acc[((size_t)c * T + t) * ACC_STRIDE + E];
+    return z;
+}
+__device__ __forceinline__ float acc_zsum(const ZLoads& z) {
+    long long s = z.q[0];
+#pragma unroll
+    for (int c = 1; c < ACC_COPIES; ++c) s += z.q[c];
+    return acc_val(s);
+}
+
 // Top-8 of every token (one wave per token) and the active-expert list, by
-// one workgroup, into R (LDS).  zv: the shared-gate logit of token tid
-// (tid < T), loaded by the caller.  The waves exchange only LDS, so the
-// barriers here leave the caller's outstanding global loads in flight.
+// one workgroup, into R (LDS), with the shared gate of every token.  The
+// waves exchange only LDS, so the barriers here leave the caller's
+// outstanding global loads in flight.
 static_assert(MOE_DECODE_T <= 8, "block_route: at most two tokens per wave");
 __device__ void block_route(const long long* __restrict__ acc, const float* __restrict__ bias,
-                            float zv, int T, RouteRec& R, int* mark) {
+                            int T, RouteRec& R, int* mark) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (T == 1) {
         // one token: its 8 experts are the active list; wave 0 sorts them by
         // id (rank = number of selected ids below its own) and writes the
         // list directly -- no marks, one barrier
         if (wave == 0) {
+            const ZLoads z = acc_zload(acc, T, 0);
             const float4v v = load_logits4(acc, T, bias, 0, lane);
             const int e = wave_top8_v(v, R.ids[0], R.w[0], nullptr);
             int rank = 0;
@@ -492,13 +515,14 @@ __device__ void block_route(const long long* __restrict__ acc, const float* __re
             }
             if (lane == 0) {
                 R.nact = TOPK;
-                R.sg[0] = 1.f / (1.f + expf(-zv));
+                R.sg[0] = 1.f / (1.f + expf(-acc_zsum(z)));
             }
         }
         pipe_barrier();
         return;
     }
     const int t0 = wave, t1 = wave + 4;
+    const ZLoads z = acc_zload(acc, T, min(tid, T - 1));
     float4v v0 = {}, v1 = {};
     if (t0 < T) v0 = load_logits4(acc, T, bias, t0, lane);
     if (t1 < T) v1 = load_logits4(acc, T, bias, t1, lane);
@@ -512,7 +536,7 @@ __device__ void block_route(const long long* __restrict__ acc, const float* __re
         const int e = wave_top8_v(v1, R.ids[t1], R.w[t1], nullptr);
         if (lane < TOPK) atomicOr((unsigned*)&mark[e], 1u << t1);
     }
-    if (tid < T) R.sg[tid] = 1.f / (1.f + expf(-zv));
+    if (tid < T) R.sg[tid] = 1.f / (1.f + expf(-acc_zsum(z)));
     pipe_barrier();
     if (wave == 0) {
         // active experts in ascending id: lane l owns experts 4l .. 4l+3
@@ -645,26 +669,16 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
     const uint32_t tall = (1u << T) - 1u;
     uint32_t mask = tall;
     // loads that do not depend on the routing go out before it: token 0's
-    // activations and the shared-gate logits
+    // activations
     uint4v x0[4];
     {
         const uint4v* xr = reinterpret_cast<const uint4v*>(xh) + lane * 4;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) x0[cc] = xr[cc];
     }
-    float zv = 0.f;
-    {
-        const int tz = min((int)threadIdx.x, T - 1);
-        long long zq[ACC_COPIES];
-#pragma unroll
-        for (int c = 0; c < ACC_COPIES; ++c) zq[c] = acc[((size_t)c * T + tz) * ACC_STRIDE + E];
-#pragma unroll
-        for (int c = 1; c < ACC_COPIES; ++c) zq[0] += zq[c];
-        zv = acc_val(zq[0]);
-    }
     if (acc_next && slot == 0 && blockIdx.y == 1)
         for (int i = threadIdx.x; i < ACC_COPIES * T * ACC_STRIDE; i += 256) acc_next[i] = 0;
-    if (slot > 0 || blockIdx.y == 0) block_route(acc, bias, zv, T, R, mark);
+    if (slot > 0 || blockIdx.y == 0) block_route(acc, bias, T, R, mark);
     int hrow = 0;
     if (slot == 0 && blockIdx.y == 0) {
         const int nact = min(max(R.nact, 0), TOPK * T);
