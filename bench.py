@@ -395,8 +395,10 @@ def prefill_chain(D, T, iters):
 
 def skewed_chunked(T_total, chunk, iters, layers=4):
     """The Zipf-biased router: T_total tokens in chunks of `chunk` through one
-    layer (the chunks run back to back in one HIP graph, rotating over a few
-    skewed layers): tokens/s and MFMA utilisation."""
+    layer, rotating over a few skewed layers, each call one HIP graph:
+    pipelined (moe_layer_forward_chunked: the next chunk's routing and
+    permutation on a second stream under the current chunk's GEMMs) and, for
+    comparison, the chunks back to back on one stream."""
     import torch
     import gemv_router_softmax_amd as moe
     from gemv_router_softmax_amd import synth
@@ -404,15 +406,22 @@ def skewed_chunked(T_total, chunk, iters, layers=4):
     x = moe.to_device_bits(synth.make_x(T_total, seed=0))
     y = torch.empty((T_total, H), dtype=torch.int16, device="cuda")
     ws = moe.workspace(chunk)
+    ws1 = moe.workspace(chunk)
 
-    def run(Dl):
+    def run_seq(Dl):
         for c0 in range(0, T_total, chunk):
             moe.moe_layer_forward(x[c0:c0 + chunk], Dl, y[c0:c0 + chunk], ws)
-    ms = _graphs_timed([lambda Dl=Dl: run(Dl) for Dl in Ds], iters)
-    t = float(ms.mean()) * 1e-3
+
+    def run_pipe(Dl):
+        moe.moe_layer_forward_chunked(x, Dl, y, chunk, ws, ws1)
+    seq = float(_graphs_timed([lambda Dl=Dl: run_seq(Dl) for Dl in Ds], iters).mean()) * 1e-3
+    t = float(_graphs_timed([lambda Dl=Dl: run_pipe(Dl) for Dl in Ds], iters).mean()) * 1e-3
     flops = EXPERT_FLOP_PER_TOKEN * 9 * T_total
+    nch = (T_total + chunk - 1) // chunk
     return {"T": T_total, "chunk": chunk, "ms": t * 1e3, "tokens_per_s": T_total / t,
-            "mfma_util": flops / t / (BF16_DENSE_PEAK_TFLOPS * 1e12)}
+            "mfma_util": flops / t / (BF16_DENSE_PEAK_TFLOPS * 1e12),
+            "ms_back_to_back": seq * 1e3, "us_per_chunk": t / nch * 1e6,
+            "us_per_chunk_back_to_back": seq / nch * 1e6}
 
 
 GREEDY_V = 151936     # synthetic vocabulary (the pages give none): a Qwen-family size

@@ -37,8 +37,9 @@ MOE_PATH_PREFILL = 2
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
-           "moe_chain_forward", "moe_chain_forward_noalloc", "moe_lm_head_argmax", "moe_embed",
-           "moe_router_transpose", "moe_probe_read", "moe_probe_copy")
+           "moe_layer_forward_chunked", "moe_chain_forward", "moe_chain_forward_noalloc",
+           "moe_lm_head_argmax", "moe_embed", "moe_router_transpose", "moe_probe_read",
+           "moe_probe_copy")
 
 
 class MoeError(RuntimeError):
@@ -90,6 +91,8 @@ def lib() -> C.CDLL:
     L.moe_layer_forward.argtypes = [vp, i32, C.POINTER(moe_layer), vp, vp, sz, vp]
     L.moe_layer_forward_ex.argtypes = [vp, i32, C.POINTER(moe_layer), vp, vp, sz, vp,
                                        C.POINTER(moe_options)]
+    L.moe_layer_forward_chunked.argtypes = [vp, i32, C.POINTER(moe_layer), vp, i32, vp, vp, sz,
+                                            vp]
     L.moe_chain_forward.argtypes = [vp, i32, C.POINTER(moe_layer), i32, vp, vp, vp, sz, vp,
                                     C.POINTER(moe_options)]
     L.moe_chain_forward_noalloc.argtypes = [vp, i32, C.POINTER(moe_layer), i32, vp, vp, vp,
@@ -313,6 +316,19 @@ def moe_layer_forward_ex(x, layer: DeviceLayer, y, ws, path: int = MOE_PATH_AUTO
     _check("moe_layer_forward_ex", lib().moe_layer_forward_ex(
         _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.c),
         _ptr(y, "y", _U16, (T, MOE_HIDDEN)), wsp, wsn, _stream(stream), C.byref(opt)))
+
+
+def moe_layer_forward_chunked(x, layer: DeviceLayer, y, chunk: int, ws0, ws1,
+                              stream=None) -> None:
+    """One layer over T tokens in chunks of `chunk`, the next chunk's routing
+    overlapping the current chunk's expert GEMMs; ws0 / ws1: two workspaces
+    of at least moe_workspace_bytes(chunk) bytes each."""
+    T = x.shape[0]
+    w0, n0 = _ws(ws0)
+    w1, n1 = _ws(ws1)
+    _check("moe_layer_forward_chunked", lib().moe_layer_forward_chunked(
+        _ptr(x, "x", _U16, (T, MOE_HIDDEN)), T, C.byref(layer.c),
+        _ptr(y, "y", _U16, (T, MOE_HIDDEN)), int(chunk), w0, w1, min(n0, n1), _stream(stream)))
 
 
 class LayerChain:

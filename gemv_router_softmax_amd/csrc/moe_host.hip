@@ -297,6 +297,35 @@ int check_route_out(const moe_options* opt) {
     return MOE_OK;
 }
 
+// The prefill path of one layer in two halves: the front (router GEMM,
+// top-8, permutation and tile plan) writes only the workspace; the back
+// (grouped GEMMs, combine) reads the workspace and writes y (and res).
+// ids/wts/sg: where the front puts the routing (the caller's route outputs
+// or the workspace's); the back reads sg from the same place.
+void prefill_front(const uint16_t* x, int T, const moe_layer* layer, void* ws, const WsLayout& L,
+                   int32_t* ids, float* wts, float* sg, hipStream_t st) {
+    // the top-8 kernel also writes the fp16 activations the grouped GEMM reads
+    launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
+                 at<float>(ws, L.logits), ids, wts, sg, st, at<uint16_t>(ws, L.xh),
+                 at<float>(ws, L.h));
+    launch_permute(ids, T, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                   at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
+                   at<int32_t>(ws, L.chunk_counts), st, wts, at<float>(ws, L.wsorted),
+                   at<Tile>(ws, L.tiles), at<int>(ws, L.tile_count));
+}
+
+void prefill_back(const uint16_t* x, int T, const moe_layer* layer, uint16_t* y, uint16_t* res,
+                  void* ws, const WsLayout& L, const float* sg, hipStream_t st) {
+    // fp16 rows of weight * d (half the bytes of fp32 expert outputs)
+    uint16_t* d16 = at<uint16_t>(ws, L.dout);
+    launch_expert_prefill_fused(x, T, at<int32_t>(ws, L.perm), at<Tile>(ws, L.tiles),
+                                at<int>(ws, L.tile_count), max_tiles(T), qffn_view(layer->routed),
+                                qffn_view(layer->shared), at<uint16_t>(ws, L.xh),
+                                at<uint16_t>(ws, L.h), d16, at<float>(ws, L.wsorted), sg,
+                                /*xh_ready=*/true, st);
+    launch_combine_f16(d16, at<int32_t>(ws, L.inv), T, y, x, res, st);
+}
+
 // One layer, arguments already validated.  ids_out/w_out/sg_out: the
 // caller's route outputs, or NULL (the routing then stays in the workspace).
 void layer_forward(const uint16_t* x, int T, int path, const moe_layer* layer, uint16_t* y,
@@ -333,18 +362,8 @@ void layer_forward(const uint16_t* x, int T, int path, const moe_layer* layer, u
                                    qffn_view(layer->shared), y, x, res, st);
         return;
     }
-    // the top-8 kernel also writes the fp16 activations the grouped GEMM reads
-    launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
-                 at<float>(ws, L.logits), ids, wts, sg, st, xh, at<float>(ws, L.h));
-    float* wsorted = at<float>(ws, L.wsorted);
-    launch_permute(ids, T, counts, offsets, perm, inv, at<int32_t>(ws, L.chunk_counts), st, wts,
-                   wsorted, tiles, tcount);
-    // fp16 rows of weight * d (half the bytes of fp32 expert outputs)
-    uint16_t* d16 = reinterpret_cast<uint16_t*>(dout);
-    launch_expert_prefill_fused(x, T, perm, tiles, tcount, max_tiles(T), qffn_view(layer->routed),
-                                qffn_view(layer->shared), xh, hbuf, d16, wsorted, sg,
-                                /*xh_ready=*/true, st);
-    launch_combine_f16(d16, inv, T, y, x, res, st);
+    prefill_front(x, T, layer, ws, L, ids, wts, sg, st);
+    prefill_back(x, T, layer, y, res, ws, L, sg, st);
 }
 
 }  // namespace
@@ -420,6 +439,105 @@ int moe_chain_forward(const uint16_t* x, int T, const moe_layer* layers, int nla
         } else {
             layer_forward(xl, T, path, &layers[l], yl, res, ws, L, ids, w, sg, st);
         }
+    }
+    return launch_status();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Chunked prefill: a second stream per device (default priority), created on
+// the first chunked call on that device, and the events that order it
+// against the caller's stream.
+namespace {
+struct ChunkStreams {
+    hipStream_t aux = nullptr;
+    hipEvent_t fork = nullptr, routed[2] = {}, done[2] = {};
+};
+std::mutex g_chunk_mutex;
+ChunkStreams g_chunk[64];
+
+// The current device's stream and events (NULL on a HIP error).
+ChunkStreams* chunk_streams() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_chunk_mutex);
+    ChunkStreams& c = g_chunk[dev];
+    if (!c.aux) {
+        ChunkStreams n;
+        bool ok = hipStreamCreateWithFlags(&n.aux, hipStreamNonBlocking) == hipSuccess;
+        hipEvent_t* evs[5] = {&n.fork, &n.routed[0], &n.routed[1], &n.done[0], &n.done[1]};
+        for (hipEvent_t* e : evs)
+            ok = ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+        if (!ok) return nullptr;      // (a partial set is not kept; the call reports the error)
+        c = n;
+    }
+    return &c;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_chunked(const uint16_t* x, int T, const moe_layer* layer, uint16_t* y,
+                              int chunk, void* ws0, void* ws1, size_t ws_bytes, void* stream) {
+    if (check_T(T) || chunk < 1 || chunk > MOE_T_MAX) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !y || !ws0 || !ws1) return MOE_ERR_INVALID_ARG;
+    if (int rc = check_layer(layer)) return rc;
+    if (!a16(x) || !a16(y) || !a16(ws0) || !a16(ws1)) return MOE_ERR_ALIGN;
+    const size_t need = ws_layout(chunk).total;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    {   // the two workspaces must not overlap
+        const char *a = static_cast<const char*>(ws0), *b = static_cast<const char*>(ws1);
+        if (a < b + need && b < a + need) return MOE_ERR_INVALID_ARG;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const int nch = (T + chunk - 1) / chunk;
+    void* ws[2] = {ws0, ws1};
+    auto part = [&](int c, const uint16_t*& xc, uint16_t*& yc, int& tc) {
+        xc = x + (size_t)c * chunk * H;
+        yc = y + (size_t)c * chunk * H;
+        tc = std::min(chunk, T - c * chunk);
+    };
+    if (nch == 1) {
+        const WsLayout L = ws_layout(T);
+        prefill_front(x, T, layer, ws0, L, at<int32_t>(ws0, L.ids), at<float>(ws0, L.wts),
+                      at<float>(ws0, L.sg), st);
+        prefill_back(x, T, layer, y, nullptr, ws0, L, at<float>(ws0, L.sg), st);
+        return launch_status();
+    }
+    ChunkStreams* cs = chunk_streams();
+    if (!cs) return MOE_ERR_HIP;
+    // fork: the second stream starts after the caller's earlier work
+    if (hipEventRecord(cs->fork, st) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamWaitEvent(cs->aux, cs->fork, 0) != hipSuccess) return MOE_ERR_HIP;
+    auto front = [&](int c) -> bool {
+        const uint16_t* xc; uint16_t* yc; int tc;
+        part(c, xc, yc, tc);
+        const int p = c & 1;
+        // chunk c - 2's back half is done with this workspace
+        if (c >= 2 && hipStreamWaitEvent(cs->aux, cs->done[p], 0) != hipSuccess) return false;
+        const WsLayout L = ws_layout(tc);
+        prefill_front(xc, tc, layer, ws[p], L, at<int32_t>(ws[p], L.ids), at<float>(ws[p], L.wts),
+                      at<float>(ws[p], L.sg), cs->aux);
+        return hipEventRecord(cs->routed[p], cs->aux) == hipSuccess;
+    };
+    auto back = [&](int c) -> bool {
+        const uint16_t* xc; uint16_t* yc; int tc;
+        part(c, xc, yc, tc);
+        const int p = c & 1;
+        if (hipStreamWaitEvent(st, cs->routed[p], 0) != hipSuccess) return false;
+        const WsLayout L = ws_layout(tc);
+        prefill_back(xc, tc, layer, yc, nullptr, ws[p], L, at<float>(ws[p], L.sg), st);
+        return hipEventRecord(cs->done[p], st) == hipSuccess;
+    };
+    // the front of chunk c + 1 is queued before the back of chunk c, so the
+    // second stream runs one chunk ahead; the last back half waits for the
+    // last front half, which joins the second stream's work into the caller's
+    if (!front(0)) return MOE_ERR_HIP;
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch && !front(c + 1)) return MOE_ERR_HIP;
+        if (!back(c)) return MOE_ERR_HIP;
     }
     return launch_status();
 }

@@ -228,6 +228,34 @@ int moe_layer_forward(const uint16_t *x, int T, const moe_layer *layer, uint16_t
 int moe_layer_forward_ex(const uint16_t *x, int T, const moe_layer *layer, uint16_t *y,
                          void *ws, size_t ws_bytes, void *stream, const moe_options *opt);
 
+/* A long prompt through one layer in chunks of `chunk` tokens, pipelined:
+ * the routing and permutation of chunk c+1 run while the expert GEMMs and
+ * the combine of chunk c run.  Long prompts are processed in chunks
+ * (leslieli.dev note on the Lily engine, paragraph 3), and the runtime
+ * keeps uneven expert workloads moving ("Perplexity Open-Sources Lily ...",
+ * section "A runtime shaped around one model").
+ * In: x bf16 [T][2048], 1 <= T <= MOE_T_MAX; 1 <= chunk <= MOE_T_MAX.
+ * Out: y bf16 [T][2048].  ws0, ws1: two non-overlapping workspaces of
+ * ws_bytes >= moe_workspace_bytes(chunk) bytes each; x, y, ws0, ws1 16-byte
+ * aligned.  Every chunk takes the grouped-GEMM path whatever its size, and
+ * y equals, bit for bit, moe_layer_forward_ex on each chunk in turn with
+ * path MOE_PATH_PREFILL.
+ * Streams: the front half of each chunk (router GEMM, top-8, permutation)
+ * runs on a second stream the library owns (one per device, default
+ * priority, created with its events on the first chunked call on that
+ * device -- that first call must not be made under stream capture), the
+ * back half (grouped GEMMs, combine) on `stream`; events order the two, the
+ * second stream's work starts after `stream`'s earlier work and ends before
+ * the call's last work on `stream`, so the call can be captured into a HIP
+ * graph on `stream` like any other.  Two calls on one device must not
+ * overlap (they share the second stream's events).  A single chunk
+ * (T <= chunk) runs on `stream` alone.
+ * Errors: NULL / T / chunk / overlapping workspaces -> MOE_ERR_INVALID_ARG;
+ * alignment -> MOE_ERR_ALIGN; small workspaces -> MOE_ERR_WORKSPACE;
+ * stream or event creation -> MOE_ERR_HIP. */
+int moe_layer_forward_chunked(const uint16_t *x, int T, const moe_layer *layer, uint16_t *y,
+                              int chunk, void *ws0, void *ws1, size_t ws_bytes, void *stream);
+
 /* A chain of layers with residual adds: x_0 = x, y_l = layer_l(x_l),
  * x_{l+1} = bf16(x_l + y_l); x_out = x_nlayers.  The fused kernel chain of
  * decode ("A Rust + Metal Inference Engine for Qwen3.6-35B-A3B on Apple

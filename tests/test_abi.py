@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -152,6 +152,23 @@ def test_layer_forward_validation(L):
     lt = _layer()
     lt.w_router_t = MIS
     assert f(A, 64, C.byref(lt), A, A, big, None, None) == ALIGN
+
+
+def test_chunked_validation(L):
+    big = moe.moe_workspace_bytes(256)
+    f = L.moe_layer_forward_chunked
+    lay = _layer()
+    B = A + (1 << 30)             # a second fake workspace far from the first
+    assert f(A, 0, C.byref(lay), A, 256, A, B, big, None) == OK          # T = 0: no-op
+    assert f(A, 1000, C.byref(lay), A, 0, A, B, big, None) == INVALID    # chunk < 1
+    assert f(A, 1000, C.byref(lay), A, moe.MOE_T_MAX + 1, A, B, big, None) == INVALID
+    assert f(A, moe.MOE_T_MAX + 1, C.byref(lay), A, 256, A, B, big, None) == INVALID
+    assert f(A, 1000, None, A, 256, A, B, big, None) == INVALID
+    assert f(A, 1000, C.byref(lay), A, 256, A, None, big, None) == INVALID
+    assert f(A, 1000, C.byref(lay), A, 256, A, B, big - 1, None) == WS   # sized by the chunk
+    assert f(A, 1000, C.byref(lay), A, 256, A, A + big - 256, big, None) == INVALID   # overlap
+    assert f(A, 1000, C.byref(lay), A, 256, A, B + 4, big, None) == ALIGN
+    assert f(MIS, 1000, C.byref(lay), A, 256, A, B, big, None) == ALIGN
 
 
 def test_chain_forward_validation(L):
