@@ -118,21 +118,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 //
 // Work items are (row tile, block of 256 weight rows) pairs: gate/up has 4
 // blocks per tile (128 gate + the same 128 up rows each), down has 8.  A
-// grid of 256 workgroups -- one per compute unit, each holding the whole
-// register file (4 waves, one per SIMD, MFMA accumulators in AGPRs) and
-// ~155 KB of LDS -- walks the items with a fixed stride.  Consecutive items
-// (the blocks of one tile, which share their activation rows) are dealt to
+// grid of one workgroup per compute unit (two for the small-tile down GEMM,
+// whose LDS fits twice) -- 4 waves, one per SIMD, MFMA accumulators in
+// AGPRs -- walks the items with a fixed stride.  Consecutive items (the
+// blocks of one tile, which share their activation rows) are dealt to
 // workgroups of the same XCD, so the rows are fetched once into that XCD's
-// L2.
+// L2.  Row tiles hold up to 160 rows, or 32 rows up to a few hundred tokens
+// (experts then have a few dozen rows at most).
 //
-// K advances in chunks of 64 (one quantisation group).  Everything a chunk
-// needs -- the activation rows (A, fp16, gathered by token for gate/up),
-// the 4-bit codes of the 256 weight rows (B) and their scales and biases --
-// moves from global memory straight into LDS (buffer loads with an LDS
-// destination) through a 5-stage ring, 4 chunks ahead of the MFMAs.  The
-// ring runs on across item boundaries: the last 4 chunks of an item prefetch
-// the first 4 of the next, so no workgroup ever waits for a pipeline fill
-// except at its very first item.
+// K advances in chunks of one quantisation group (64), or two (128) in the
+// small-tile gate/up GEMM.  Everything a chunk needs -- the activation rows
+// (A, fp16, gathered by token for gate/up), the 4-bit codes of the 256
+// weight rows (B) and their scales and biases -- moves from global memory
+// straight into LDS (buffer loads with an LDS destination) through a
+// 5-stage ring, 4 chunks ahead of the MFMAs.  The ring runs on across item
+// boundaries: the last 4 chunks of an item prefetch the first 4 of the
+// next, so no workgroup ever waits for a pipeline fill except at its very
+// first item.
 //
 // Every wave issues exactly LPC loads per chunk (plus one metadata load at
 // the first chunk of an item and a fixed number of stores per epilogue;
@@ -148,17 +150,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 // gate/up epilogue (h = bf16(silu(g) u), stored as fp16); down writes fp32
 // rows (split interface) or fp16 rows of (routing weight or shared gate) x d.
 //
-// LDS layouts (per stage):
-//   A   [160 rows][8 pieces of 16 B]: piece p of row R sits at slot
-//       p ^ ((R >> 1) & 7), so the 16 rows of an MFMA operand read cover all
-//       64 banks.
-//   B   [256 columns][2 pieces of 16 B]: piece p of column C sits at slot
-//       p ^ ((C >> 3) & 1), so a 128-bit read by 16 lanes is conflict free.
-//   S, Bi [256 columns] dwords holding the fp16 scale (bias) of groups kc
-//       and kc+1, loaded by even chunks kc only: the odd chunk's loads are
-//       out-of-range stand-ins (its S and Bi are never read) and its
-//       operands use the upper halves, kept in registers by read_b.
-// K order inside a chunk: lane half g of MFMA step s covers k-piece 4g+s.
+// LDS layouts (per stage; a_swz and b_swz below):
+//   A   [rows][8 or 16 pieces of 16 B], piece p of row R at slot
+//       p ^ a_swz(R): the 16 rows of an MFMA operand read cover all 64 banks.
+//   B   [256 columns][2 or 4 pieces of 16 B], piece p of column C at slot
+//       p ^ b_swz(C): a 128-bit read by 16 lanes is conflict free.
+//   S, Bi [256 columns] dwords holding the fp16 scale (bias) of two
+//       consecutive groups.  With one group per chunk they are loaded by the
+//       even chunks only: the odd chunk's loads are out-of-range stand-ins
+//       (its S and Bi are never read) and its operands use the upper halves,
+//       kept in registers by read_b.  With two groups per chunk, each chunk
+//       loads its own and lane half g uses half g.
+// K order inside a chunk: lane half g of MFMA step s covers k-piece
+// STEPS g + s.
 
 struct GemmArgs {
     const uint16_t* ain;      // A rows: x (fp16, slot order) [T][2048] or h [9T][512]
@@ -175,20 +179,28 @@ struct GemmArgs {
 constexpr uint32_t OOB_OFF = 0x80000000u;   // beyond every buffer: no memory access
 
 // Tile geometry of one instantiation: MTR = rows per row tile, at most (160
-// for large T; 32 for small T, whose LDS fits two workgroups per CU).
-template <int MTR>
+// for large T; 32 for small T); KCH = K per pipeline chunk, one quantisation
+// group (64) or two (128: each weight row's code request then fetches 64
+// bytes instead of 32, half the L1 line requests of the code stream, which
+// bound the small-tile gate/up GEMM).
+template <int MTR, int KCH>
 struct PG {
     static constexpr int WAVES = 4;
     static constexpr int THREADS = WAVES * 64;
     static constexpr int MT = MTR;                      // rows per tile, at most
     static constexpr int NMT_MAX = MT / 32;             // 32-row m-tiles
-    static constexpr int KC = G;                        // K per chunk: one quantisation group
+    static constexpr int KC = KCH;                      // K per chunk
+    static_assert(KC == G || KC == 2 * G, "one or two quantisation groups per chunk");
+    static constexpr int STEPS = KC / 16;               // MFMA k-steps per chunk
     static constexpr int STAGES = 5;                    // chunk c+5 refills chunk c's stage once
                                                         // every wave is past its last read of it
     static constexpr int AROW = KC * 2;                 // bytes of one A row per chunk
+    static constexpr int A_PIECES = AROW / 16;          // 16-byte pieces of an A row (8 or 16)
     static constexpr int A_BYTES = MT * AROW;
     static constexpr int NCOL = 256;                    // weight rows per item
-    static constexpr int B_BYTES = NCOL * KC / 2;
+    static constexpr int BCOL = KC / 2;                 // code bytes of one weight row per chunk
+    static constexpr int B_PIECES = BCOL / 16;          // (2 or 4)
+    static constexpr int B_BYTES = NCOL * BCOL;
     static constexpr int S_BYTES = NCOL * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
     static constexpr int META = WAVES * 256;            // per-item row metadata (tokens or weights):
@@ -197,18 +209,27 @@ struct PG {
     static constexpr int CLAIM = WAVES * 256 + 16;      // the claimed item index (16 B) and the
                                                         // landing area of waves 1-3's stand-in load
     static constexpr int LDS_BYTES = STAGES * STAGE + 2 * META + WAVES * STG + CLAIM;
-    static constexpr int A_LOADS = MT / 8 / WAVES;      // 1 KB (8 rows) per load instruction
+    static constexpr int A_RPL = 1024 / AROW;           // A rows per 1 KB load instruction
+    static constexpr int A_LOADS = MT / A_RPL / WAVES;
+    static constexpr int B_CPL = 1024 / BCOL;           // weight rows per 1 KB load instruction
     static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
     static constexpr int LPC = A_LOADS + B_LOADS + 2;   // loads per wave per chunk
     static constexpr uint32_t OOB = OOB_OFF;
     static constexpr int WG_PER_CU = 160 * 1024 / LDS_BYTES;   // workgroups the LDS holds per CU
-    static_assert(MT % (8 * WAVES) == 0, "A rows must split evenly over the load instructions");
+    static_assert(MT % (A_RPL * WAVES) == 0, "A rows must split evenly over the load instructions");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(META >= MT * 4, "row metadata must cover a tile");
     static_assert((STAGES - 2) * LPC + 2 <= 63, "vmcnt range");
 };
 constexpr int MT_LARGE = MT_ROWS, MT_SMALL = 32;
-static_assert(PG<MT_SMALL>::WG_PER_CU >= 2 && PG<MT_LARGE>::WG_PER_CU == 1, "tile LDS footprints");
+// The chunk width of an instantiation: two groups for the small-tile gate/up
+// GEMM (K = 2048); one elsewhere (the down GEMM's K = 512 has too few
+// 128-wide chunks for the ring, and the large tiles are bound by the MFMA
+// issue, not by line requests).
+template <int KDIM, int MTR>
+constexpr int gemm_kc() { return (MTR == MT_SMALL && KDIM == H) ? 2 * G : G; }
+static_assert(PG<MT_SMALL, G>::WG_PER_CU >= 2 && PG<MT_LARGE, G>::WG_PER_CU == 1 &&
+              PG<MT_SMALL, 2 * G>::WG_PER_CU == 1, "tile LDS footprints");
 
 typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
@@ -251,16 +272,28 @@ __device__ __forceinline__ uint32_t claim_item(int* ctr, uint8_t* claim) {
     return t;
 }
 
+// LDS swizzles.  A rows are 128 B (one group per chunk) or 256 B (two): the
+// 16 rows of one MFMA operand read (16 lanes x 16 B) must cover all 64
+// banks.  At 128 B two consecutive rows fill the 64 banks, so the piece is
+// XORed with (R >> 1) & 7; at 256 B every row spans them, so with R & 15.
+// B columns are 32 B (two pieces: XOR with (C >> 3) & 1, so 16 lanes reading
+// one piece of 16 consecutive columns hit distinct banks) or 64 B (four
+// pieces: XOR with (C >> 2) & 3).
+template <int KCH>
+__device__ __forceinline__ int a_swz(int R) { return KCH == G ? ((R >> 1) & 7) : (R & 15); }
+template <int KCH>
+__device__ __forceinline__ int b_swz(int C) { return KCH == G ? ((C >> 3) & 1) : ((C >> 2) & 3); }
+
 // Where one item's chunks come from, per lane: the A rows this lane moves
 // and the code/scale words of this wave's weight rows.  Chunk kc adds a
 // wave-uniform offset (the soffset operand of the loads), so issuing a chunk
 // costs no vector arithmetic.  Rows past the tile and items past the last
 // get out-of-range offsets (the loads access no memory and fill zeros).
-template <int MTR>
+template <int MTR, int KCH>
 struct GSrc {
     __amdgpu_buffer_rsrc_t rq, rs, rb;   // this wave's code / scale / bias matrix
-    uint32_t a[PG<MTR>::A_LOADS];        // A: instruction i -> rows (w*A_LOADS + i)*8 + lane/8
-    uint32_t b[PG<MTR>::B_LOADS];        // B: instruction i -> columns (w*B_LOADS + i)*32 + lane/2
+    uint32_t a[PG<MTR, KCH>::A_LOADS];   // A: instruction i -> rows (w*A_LOADS + i)*A_RPL + ..
+    uint32_t b[PG<MTR, KCH>::B_LOADS];   // B: instruction i -> columns (w*B_LOADS + i)*B_CPL + ..
     uint32_t s;                          // scale/bias dword of column w*64 + lane
 };
 
@@ -292,19 +325,20 @@ __device__ __forceinline__ WPtr wave_ptrs(const QFFN& f) {
     return w;
 }
 
-template <int KDIM, int MODE, int MTR>
-__device__ __forceinline__ GSrc<MTR> gemm_src(const GItem& m, const int32_t* tok, int T,
-                                              const WPtr& pr, const WPtr& ps) {
-    using pg = PG<MTR>;
+template <int KDIM, int MODE, int MTR, int KCH>
+__device__ __forceinline__ GSrc<MTR, KCH> gemm_src(const GItem& m, const int32_t* tok, int T,
+                                                   const WPtr& pr, const WPtr& ps) {
+    using pg = PG<MTR, KCH>;
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int WPR = KDIM / 8, SPR = KDIM / G, ROWS_W = GATEUP ? I : H;
     const int lane = threadIdx.x & 63, wave = wave_id();
-    GSrc<MTR> g;
-    // A: LDS slot (lane & 7) of row R holds the row's piece slot ^ ((R >> 1) & 7)
+    GSrc<MTR, KCH> g;
+    // A: LDS slot (lane % A_PIECES) of row R holds the row's piece
+    // slot ^ a_swz(R)
 #pragma unroll
     for (int i = 0; i < pg::A_LOADS; ++i) {
-        const int R = (wave * pg::A_LOADS + i) * 8 + (lane >> 3);
-        const int p = (lane & 7) ^ ((R >> 1) & 7);
+        const int R = (wave * pg::A_LOADS + i) * pg::A_RPL + lane / pg::A_PIECES;
+        const int p = (lane % pg::A_PIECES) ^ a_swz<KCH>(R);
         int src = m.row0 + R;
         if (GATEUP) src = m.shared ? m.row0 + R - TOPK * T : min(max(tok[R] >> 3, 0), T - 1);
         g.a[i] = R < m.nrows ? (uint32_t)src * (uint32_t)(KDIM * 2) + 16u * (uint32_t)p : pg::OOB;
@@ -317,11 +351,12 @@ __device__ __forceinline__ GSrc<MTR> gemm_src(const GItem& m, const int32_t* tok
     g.rs = buf_rsrc(expert_at(sc, m.e, ss), ROWS_W * SPR * 2);
     g.rb = buf_rsrc(expert_at(bi, m.e, ss), ROWS_W * SPR * 2);
     auto wrow = [&](int C) { return GATEUP ? m.nb * 128 + (C & 127) : m.nb * 256 + C; };
-    // B: LDS slot (lane & 1) of column C holds the column's piece slot ^ ((C >> 3) & 1)
+    // B: LDS slot (lane % B_PIECES) of column C holds the column's piece
+    // slot ^ b_swz(C)
 #pragma unroll
     for (int i = 0; i < pg::B_LOADS; ++i) {
-        const int C = (wave * pg::B_LOADS + i) * 32 + (lane >> 1);
-        const int p = (lane & 1) ^ ((C >> 3) & 1);
+        const int C = (wave * pg::B_LOADS + i) * pg::B_CPL + lane / pg::B_PIECES;
+        const int p = (lane % pg::B_PIECES) ^ b_swz<KCH>(C);
         g.b[i] = m.valid ? (uint32_t)(wrow(C) * WPR * 4 + 16 * p) : pg::OOB;
     }
     g.s = m.valid ? (uint32_t)(wrow(wave * 64 + lane) * SPR * 2) : pg::OOB;
@@ -339,23 +374,27 @@ __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst,
 }
 
 // The LPC loads of chunk kc of an item into one stage.
-template <int MTR>
-__device__ __forceinline__ void issue_chunk(const GSrc<MTR>& g, int kc, __amdgpu_buffer_rsrc_t ra,
-                                            uint8_t* stage) {
-    using pg = PG<MTR>;
+template <int MTR, int KCH>
+__device__ __forceinline__ void issue_chunk(const GSrc<MTR, KCH>& g, int kc,
+                                            __amdgpu_buffer_rsrc_t ra, uint8_t* stage) {
+    using pg = PG<MTR, KCH>;
     const int wave = wave_id();
 #pragma unroll
     for (int i = 0; i < pg::A_LOADS; ++i)
         load_lds<16>(ra, stage + (wave * pg::A_LOADS + i) * 1024, g.a[i], kc * pg::AROW);
 #pragma unroll
     for (int i = 0; i < pg::B_LOADS; ++i)
-        load_lds<16>(g.rq, stage + pg::A_BYTES + (wave * pg::B_LOADS + i) * 1024, g.b[i], kc * 32);
-    // one scale and one bias dword covers chunks kc & ~1 and kc | 1: the odd
-    // chunk's loads are out-of-range stand-ins (no memory access), and its
-    // operands reuse the even chunk's dwords (read_b)
-    const uint32_t so = (kc & 1) ? pg::OOB : g.s;
-    load_lds<4>(g.rs, stage + pg::A_BYTES + pg::B_BYTES + wave * 256, so, (kc & ~1) * 2);
-    load_lds<4>(g.rb, stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + wave * 256, so, (kc & ~1) * 2);
+        load_lds<16>(g.rq, stage + pg::A_BYTES + (wave * pg::B_LOADS + i) * 1024, g.b[i],
+                     kc * pg::BCOL);
+    // one scale and one bias dword covers two groups.  One group per chunk:
+    // the dword of chunks kc & ~1 and kc | 1, loaded by the even chunk; the
+    // odd chunk's loads are out-of-range stand-ins (no memory access), and
+    // its operands reuse the even chunk's dwords (read_b).  Two groups per
+    // chunk: every chunk loads its own dword.
+    const uint32_t so = (KCH == G && (kc & 1)) ? pg::OOB : g.s;
+    const uint32_t sb = KCH == G ? (uint32_t)((kc & ~1) * 2) : (uint32_t)(kc * 4);
+    load_lds<4>(g.rs, stage + pg::A_BYTES + pg::B_BYTES + wave * 256, so, sb);
+    load_lds<4>(g.rb, stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + wave * 256, so, sb);
 }
 
 // MFMA: v_mfma_f32_32x32x16_f16 (32 rows x 32 columns x 16 k).  Lane l
@@ -372,11 +411,13 @@ __device__ __forceinline__ int gemm_col(int wave, int nt, int l32) {
     return GATEUP ? nt * 128 + wave * 32 + l32 : wave * 64 + nt * 32 + l32;
 }
 
-// K order inside a 64-wide chunk: MFMA step s (0..3), lane half g = l/32
-// covers the 8-wide k-piece 4g + s.  A lane therefore needs one contiguous
-// 16-byte half (words 4g..4g+3) of each of its columns' 32 code bytes.
+// K order inside a chunk of STEPS k-steps: MFMA step s, lane half g = l/32
+// covers the 8-wide k-piece STEPS g + s.  A lane therefore needs one
+// contiguous run of STEPS code words (the half g of each of its columns'
+// code bytes of the chunk), and with two groups per chunk lane half g works
+// in group 2 kc + g throughout.
 struct BFrag {
-    uint4v w[2];          // words of steps 0..3, per n-tile
+    uint4v w[2][2];       // per n-tile: words of steps 0..3 (and 4..7)
     half2v s[2], b[2];    // fp16 scale / bias, splat
 };
 
@@ -388,16 +429,28 @@ struct SCarry {
     half2v s[2], b[2];
 };
 
-template <bool GATEUP, int MTR>
+template <bool GATEUP, int MTR, int KCH>
 __device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc, SCarry& carry) {
-    using pg = PG<MTR>;
+    using pg = PG<MTR, KCH>;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int l32 = lane & 31, g = lane >> 5;
     BFrag B;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         const int C = gemm_col<GATEUP>(wave, nt, l32);
-        B.w[nt] = *reinterpret_cast<const uint4v*>(stage + pg::A_BYTES + C * 32 + 16 * (g ^ ((C >> 3) & 1)));
+        const uint8_t* col = stage + pg::A_BYTES + C * pg::BCOL;
+        if constexpr (KCH != G) {
+            // two groups: pieces 2g and 2g+1, and half g of the stage's dwords
+            B.w[nt][0] = *reinterpret_cast<const uint4v*>(col + 16 * ((2 * g) ^ b_swz<KCH>(C)));
+            B.w[nt][1] = *reinterpret_cast<const uint4v*>(col + 16 * ((2 * g + 1) ^ b_swz<KCH>(C)));
+            const uint32_t sd = *reinterpret_cast<const uint32_t*>(stage + pg::A_BYTES + pg::B_BYTES + C * 4);
+            const uint32_t bd =
+                *reinterpret_cast<const uint32_t*>(stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + C * 4);
+            B.s[nt] = splat_h((uint16_t)(g ? sd >> 16 : sd));
+            B.b[nt] = splat_h((uint16_t)(g ? bd >> 16 : bd));
+            continue;
+        }
+        B.w[nt][0] = *reinterpret_cast<const uint4v*>(col + 16 * (g ^ b_swz<KCH>(C)));
         if (kc & 1) {
             B.s[nt] = carry.s[nt];
             B.b[nt] = carry.b[nt];
@@ -414,23 +467,24 @@ __device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc, SCarry& ca
     return B;
 }
 
-// A operand of K-step s: row mt*32 + l%32, k-piece 4g + s.
-template <int NMT, int MTR>
+// A operand of K-step s: row mt*32 + l%32, k-piece STEPS g + s.
+template <int NMT, int MTR, int KCH>
 __device__ __forceinline__ void read_a(const uint8_t* stage, int s, half8 (&a)[NMT]) {
-    using pg = PG<MTR>;
+    using pg = PG<MTR, KCH>;
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
         const int R = mt * 32 + l32;
-        a[mt] = *reinterpret_cast<const half8*>(stage + R * pg::AROW + 16 * ((4 * g + s) ^ ((R >> 1) & 7)));
+        a[mt] = *reinterpret_cast<const half8*>(stage + R * pg::AROW +
+                                                16 * ((pg::STEPS * g + s) ^ a_swz<KCH>(R)));
     }
 }
 
 __device__ __forceinline__ void dequant_step(const BFrag& B, int s, half8 (&bf)[2]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const uint32_t wv = B.w[nt][s];
+        const uint32_t wv = B.w[nt][s >> 2][s & 3];
         bf[nt] = dequant8(wv, B.s[nt], B.b[nt]);
     }
 }
@@ -462,7 +516,7 @@ __device__ __forceinline__ void sched_step() {
 // Stores per wave per epilogue (one 16-byte store per lane per 1 KB staged).
 template <int MODE, int MTR>
 constexpr int epi_stores() {
-    constexpr int n = PG<MTR>::NMT_MAX;
+    constexpr int n = PG<MTR, G>::NMT_MAX;
     return MODE == GM_GATEUP ? 2 * n : MODE == GM_DOWN_F16W ? 4 * n : 8 * n;
 }
 
@@ -498,7 +552,7 @@ template <int MODE, int NMT, int MTR>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                                               float16v (&acc)[NMT][2], uint8_t* stg,
                                               const float* coef) {
-    using pg = PG<MTR>;
+    using pg = PG<MTR, G>;              // (the fields used here do not depend on the chunk)
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int l32 = lane & 31, g = lane >> 5;
     const int Rl = lane >> 2;           // staged row read back by this lane
@@ -639,13 +693,13 @@ struct Sched {
 // refilled with chunk c+5 (the ring runs on into the next item) and the next
 // chunk's operands are read and its step 0 dequantised.  Only the first
 // chunk of an item dequantises with no MFMAs to hide under.
-template <int KDIM, int MODE, int NMT, int MTR>
+template <int KDIM, int MODE, int NMT, int MTR, int KCH>
 __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cur, GItem& nxt,
-                                              const GSrc<MTR>& src_cur, GSrc<MTR>& src_nxt, int& gc, int k,
+                                              const GSrc<MTR, KCH>& src_cur, GSrc<MTR, KCH>& src_nxt, int& gc, int k,
                                               bool first, __amdgpu_buffer_rsrc_t ra,
                                               const WPtr& pr, const WPtr& ps, uint8_t* lds,
                                               const Sched& sc, uint32_t& tick) {
-    using pg = PG<MTR>;
+    using pg = PG<MTR, KCH>;
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     constexpr int NCH = KDIM / pg::KC;
@@ -666,8 +720,8 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 
     half8 a_cur[NMT], bf_cur[2];
     SCarry carry;
-    BFrag B = read_b<GATEUP, MTR>(lds + (gc % pg::STAGES) * pg::STAGE, 0, carry);
-    read_a<NMT, MTR>(lds + (gc % pg::STAGES) * pg::STAGE, 0, a_cur);
+    BFrag B = read_b<GATEUP, MTR, KCH>(lds + (gc % pg::STAGES) * pg::STAGE, 0, carry);
+    read_a<NMT, MTR, KCH>(lds + (gc % pg::STAGES) * pg::STAGE, 0, a_cur);
     dequant_step(B, 0, bf_cur);
 
     // One chunk.  `refill(stage)` issues the loads of chunk c+5 into the
@@ -675,9 +729,9 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     auto chunk = [&](int c, auto&& refill) {
         const uint8_t* st = lds + (gc % pg::STAGES) * pg::STAGE;
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
+        for (int s = 0; s < pg::STEPS - 1; ++s) {
             half8 a_nx[NMT], bf_nx[2];
-            read_a<NMT, MTR>(st, s + 1, a_nx);
+            read_a<NMT, MTR, KCH>(st, s + 1, a_nx);
             dequant_step(B, s + 1, bf_nx);
             mfma_step<NMT>(a_cur, bf_cur, acc);
             sched_step<NMT, NMT>();
@@ -698,8 +752,8 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE));
         pipe_barrier();
 
-        // step 3 of this chunk under the next chunk's reads, the refill and
-        // the next chunk's first dequantisation
+        // the last step of this chunk under the next chunk's reads, the
+        // refill and the next chunk's first dequantisation
         // (the sched_barrier fences keep the refill loads in issue order
         // relative to the other vector-memory operations: the wait counts
         // above depend on that order)
@@ -707,8 +761,8 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         half8 a_nx[NMT], bf_nx[2];
         if (more) {
             const uint8_t* sn = lds + ((gc + 1) % pg::STAGES) * pg::STAGE;
-            B = read_b<GATEUP, MTR>(sn, c + 1, carry);
-            read_a<NMT, MTR>(sn, 0, a_nx);
+            B = read_b<GATEUP, MTR, KCH>(sn, c + 1, carry);
+            read_a<NMT, MTR, KCH>(sn, 0, a_nx);
         }
         __builtin_amdgcn_sched_barrier(0);
         refill(const_cast<uint8_t*>(st));
@@ -734,7 +788,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     };
     // the next item's sources (its row tokens arrived with this item's first chunk)
     auto make_next = [&]() {
-        src_nxt = gemm_src<KDIM, MODE, MTR>(nxt, reinterpret_cast<const int32_t*>(meta + ((k + 1) & 1) * pg::META),
+        src_nxt = gemm_src<KDIM, MODE, MTR, KCH>(nxt, reinterpret_cast<const int32_t*>(meta + ((k + 1) & 1) * pg::META),
                                        A.T, pr, ps);
     };
 
@@ -786,10 +840,12 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 // two items of each workgroup are static and the rest are claimed from the
 // XCD's counter in order -- longest first.
 template <int KDIM, int MODE, int MTR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PG<MTR>::WG_PER_CU)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(PG<MTR, gemm_kc<KDIM, MTR>()>::WG_PER_CU)))
 void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict__ tile_count,
                   QFFN routed, QFFN shared) {
-    using pg = PG<MTR>;
+    constexpr int KCH = gemm_kc<KDIM, MTR>();
+    using pg = PG<MTR, KCH>;
     static_assert(pg::THREADS == 256, "launch bounds");
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
@@ -812,8 +868,9 @@ void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict
         __syncthreads();
     }
     const WPtr pr = wave_ptrs<MODE>(routed), ps = wave_ptrs<MODE>(shared);
-    GSrc<MTR> src_cur = gemm_src<KDIM, MODE, MTR>(cur, reinterpret_cast<const int32_t*>(meta), args.T, pr, ps);
-    GSrc<MTR> src_nxt = src_cur;
+    GSrc<MTR, KCH> src_cur =
+        gemm_src<KDIM, MODE, MTR, KCH>(cur, reinterpret_cast<const int32_t*>(meta), args.T, pr, ps);
+    GSrc<MTR, KCH> src_nxt = src_cur;
     for (int c = 0; c < pg::STAGES; ++c) issue_chunk(src_cur, c, ra, lds + c * pg::STAGE);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((pg::STAGES - 1) * pg::LPC));   // chunk 0 landed
     pipe_barrier();
@@ -826,12 +883,13 @@ void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict
     // that instance, so every case processes its item)
 #define PG_CASE(n)                                                                           \
     case n:                                                                                  \
-        gemm_run_item<KDIM, MODE, (n < pg::NMT_MAX ? n : pg::NMT_MAX), MTR>(                 \
+        gemm_run_item<KDIM, MODE, (n < pg::NMT_MAX ? n : pg::NMT_MAX), MTR, KCH>(            \
             args, cur, nxt, src_cur, src_nxt, gc, k, k == 0, ra, pr, ps, lds, sc, tick);     \
         break;
             PG_CASE(1) PG_CASE(2) PG_CASE(3) PG_CASE(4)
-            default: gemm_run_item<KDIM, MODE, pg::NMT_MAX, MTR>(args, cur, nxt, src_cur, src_nxt, gc,
-                                                                 k, k == 0, ra, pr, ps, lds, sc, tick);
+            default: gemm_run_item<KDIM, MODE, pg::NMT_MAX, MTR, KCH>(args, cur, nxt, src_cur, src_nxt,
+                                                                      gc, k, k == 0, ra, pr, ps, lds,
+                                                                      sc, tick);
                      break;
 #undef PG_CASE
         }
@@ -885,7 +943,13 @@ static GemmArgs gemm_args(const uint16_t* ain, size_t ain_bytes, int T, const in
 
 // Row-tile height of the grouped GEMMs at T tokens: 32-row tiles (two
 // workgroups per CU) while the experts average at most 16 rows, 160 above.
-int gemm_tile_rows(int T) { return T <= 512 ? MT_SMALL : MT_LARGE; }
+// The small tiles stream the weights better up to several hundred tokens
+// (T = 768: 209-217 against 247 us per layer on 160-row tiles; T = 1024:
+// 274-279 against 263-265), so the switch sits in between.
+#ifndef MOE_SMALL_TILE_T
+#define MOE_SMALL_TILE_T 896
+#endif
+int gemm_tile_rows(int T) { return T <= MOE_SMALL_TILE_T ? MT_SMALL : MT_LARGE; }
 
 // One persistent grouped GEMM: as many workgroups as the LDS lets each CU
 // hold (a multiple of the 8 XCDs).
@@ -893,10 +957,12 @@ template <int KDIM, int MODE>
 static void launch_gemm(const GemmArgs& a, const Tile* tiles, int* tile_count, const QFFN& routed,
                         const QFFN& shared, int mt_rows, hipStream_t st) {
     if (mt_rows == MT_SMALL)
-        hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_SMALL>), dim3(256 * PG<MT_SMALL>::WG_PER_CU),
+        hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_SMALL>),
+                           dim3(256 * PG<MT_SMALL, gemm_kc<KDIM, MT_SMALL>()>::WG_PER_CU),
                            dim3(256), 0, st, a, tiles, tile_count, routed, shared);
     else
-        hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_LARGE>), dim3(256 * PG<MT_LARGE>::WG_PER_CU),
+        hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_LARGE>),
+                           dim3(256 * PG<MT_LARGE, gemm_kc<KDIM, MT_LARGE>()>::WG_PER_CU),
                            dim3(256), 0, st, a, tiles, tile_count, routed, shared);
 }
 

@@ -30,7 +30,8 @@ def gpu_ffn(x, D, pm, T, path):
 
 
 @pytest.mark.parametrize("T,path", [(1, DEC), (8, DEC), (16, DEC), (16, PRE), (32, DEC),
-                                    (1, PRE), (64, PRE), (200, PRE), (512, PRE), (513, PRE)])
+                                    (1, PRE), (64, PRE), (200, PRE), (512, PRE), (513, PRE),
+                                    (896, PRE), (897, PRE)])
 def test_expert_ffn(gpu, T, path):
     P.say(f"expert_ffn T={T} path={path}")
     L, x, r, pm = routed_inputs(T, seed=T)

@@ -57,7 +57,7 @@ def test_decode_auto(gpu, T):
     check_layer(T, AUTO, seed=3)
 
 
-@pytest.mark.parametrize("T", [9, 64, 100, 129, 512, 513])
+@pytest.mark.parametrize("T", [9, 64, 100, 129, 512, 513, 896, 897])
 def test_prefill_auto(gpu, T):
     check_layer(T, AUTO, seed=4)
 
