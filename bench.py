@@ -537,7 +537,11 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the prefill T sweep, the T=512 chain and the skewed chunked run")
+                    help="skip the prefill T sweep, the T=512 chain, the skewed chunked run and "
+                         "the greedy step")
+    ap.add_argument("--legs", default="t4096,sweep,chain512,skewed,greedy",
+                    help="which of the extra measurements to run (comma list; for profiling "
+                         "one of them alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true")
@@ -581,21 +585,24 @@ def main():
         copy_calibration()
     traffic = measured_traffic()
 
+    legs = set(args.legs.split(",")) if not args.no_extra else {"t4096"}
     pre = None
-    if not args.no_prefill:
+    if not args.no_prefill and "t4096" in legs:
         pre = prefill(D, 4096, args.prefill_iters)
         log(f"prefill T=4096: {pre}")
     sweep = chain512 = skewed = None
-    if not args.no_prefill and not args.no_extra:
+    if not args.no_prefill and "sweep" in legs:
         sweep = prefill_sweep(D, (256, 1024, 2048, 4096), args.prefill_iters)
         log(f"prefill sweep: {sweep}")
+    if not args.no_prefill and "chain512" in legs:
         chain512 = prefill_chain(D, 512, 5)
         log(f"prefill chain T=512: {chain512}")
+    if not args.no_prefill and "skewed" in legs:
         skewed = skewed_chunked(16384, 4096, 8)
         log(f"skewed chunked prefill: {skewed}")
 
     greedy = None
-    if not args.no_extra:
+    if "greedy" in legs:
         greedy = greedy_decode(D, 200)
         log(f"greedy decode step: {greedy}")
 
