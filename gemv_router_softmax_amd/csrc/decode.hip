@@ -292,13 +292,15 @@ __global__ __launch_bounds__(256) void decode_down_combine(
 //                      each token (one wave per router row), stored as 64-bit
 //                      fixed point (below), and the fp16 copy of x in
 //                      chunk-slot order;
-//   decode_gateup_dec  slot 0 = the shared expert (needs no routing), slot
-//                      a >= 1 = the a-th active routed expert, which every
-//                      routed workgroup finds by running the top-8 selection
-//                      itself on the logits (block_route); workgroup (0, 0)
-//                      publishes the down record.  h rows are compact: the T
-//                      shared rows, then every (expert, token) pair in
-//                      ascending expert order, 9T rows in all;
+//   decode_gateup_dec  slot 0 = the shared expert (needs no routing); one
+//                      token: slot a >= 1 = the a-th active routed expert,
+//                      which every routed workgroup finds by running the
+//                      top-8 selection itself on the logits (block_route),
+//                      and workgroup (0, 0) publishes the down record; more
+//                      tokens: slot 1 + 8t + j = token t's j-th expert, from
+//                      token t's logits alone.  h rows are compact: the T
+//                      shared rows, then one row per routed (slot, token),
+//                      9T rows in all;
 //   decode_down_dec    DN_ROWS output rows per workgroup over every slot
 //                      (each wave a row group x a slot group), h rows read
 //                      straight from global memory; combine with the routing
@@ -642,14 +644,18 @@ __global__ __launch_bounds__(256) void route_logits_dec(const uint16_t* __restri
     }
 }
 
-// grid (1 + 8T, I/16).  Slot 0 is the shared expert; slot s > 0 is the
-// s-th active routed expert (ascending id), which each routed workgroup
-// finds by running the selection itself on the logits (block_route); the
-// workgroup (0, 0) publishes the route record for decode_down_dec (and, if
-// asked, the routing itself: ids, weights and shared gates).  Workgroup
-// (0, 1) clears the next layer's logit accumulators (acc_next, if any),
-// which the down kernel then adds to.  h rows (fp16, chunk-slot order) are
-// compact, see slot_hrow.
+// grid (1 + 8T, I/16).  Slot 0 is the shared expert.  One token: slot s > 0
+// is the s-th active routed expert (ascending id), which each routed
+// workgroup finds by running the selection itself on the logits
+// (block_route); the workgroup (0, 0) publishes the route record for
+// decode_down_dec (and, if asked, the routing itself: ids, weights and
+// shared gates).  Two or more tokens: slot 1 + 8t + j is the j-th expert of
+// token t alone, found from token t's logits only; each routed workgroup of
+// row chunk 0 publishes its slot's record entry (and token t's routing),
+// workgroup (0, 0) the shared slot's.  Workgroup (0, 1) clears the next
+// layer's logit accumulators (acc_next, if any), which the down kernel then
+// adds to.  h rows (fp16, chunk-slot order) are compact: the T shared rows,
+// then one row per (slot, token) -- see slot_hrow for one token.
 __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restrict__ xh, int T,
                                                          const long long* __restrict__ acc,
                                                          const float* __restrict__ bias,
@@ -668,19 +674,71 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
     int e = 0;
     const uint32_t tall = (1u << T) - 1u;
     uint32_t mask = tall;
-    // loads that do not depend on the routing go out before it: token 0's
-    // activations
+    // two or more tokens: one slot per (token, rank) pair (slot 1 + 8t + j:
+    // the j-th expert of token t, for token t alone), so a workgroup needs
+    // only its own token's logits and top-8 -- not every token's, which the
+    // active-expert list of the single-token path would need in every
+    // workgroup.  Two tokens sharing an expert then read its weights twice.
+    const bool pairs = T >= 2;
+    const int town = pairs && slot > 0 ? (slot - 1) >> 3 : 0;     // this slot's token
+    // loads that do not depend on the routing go out before it: the
+    // activations of this slot's (first) token
     uint4v x0[4];
     {
-        const uint4v* xr = reinterpret_cast<const uint4v*>(xh) + lane * 4;
+        const uint4v* xr = reinterpret_cast<const uint4v*>(xh + (size_t)town * H) + lane * 4;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) x0[cc] = xr[cc];
     }
     if (acc_next && slot == 0 && blockIdx.y == 1)
         for (int i = threadIdx.x; i < ACC_COPIES * T * ACC_STRIDE; i += 256) acc_next[i] = 0;
-    if (slot > 0 || blockIdx.y == 0) block_route(acc, bias, T, R, mark);
     int hrow = 0;
-    if (slot == 0 && blockIdx.y == 0) {
+    if (pairs) {
+        const int tid = threadIdx.x;
+        if (slot > 0) {
+            const int j = (slot - 1) & 7;
+            if (wave_id() == 0) {
+                const ZLoads z = acc_zload(acc, T, town);
+                const float4v v = load_logits4(acc, T, bias, town, lane);
+                wave_top8_v(v, R.ids[town], R.w[town], nullptr);
+                if (lane == 0) R.sg[town] = 1.f / (1.f + expf(-acc_zsum(z)));
+            }
+            pipe_barrier();
+            e = min(max(R.ids[town][j], 0), E - 1);
+            mask = 1u << town;
+            hrow = T + slot - 1;
+            if (blockIdx.y == 0) {
+                if (tid == 0) {
+                    rec->slot_e[slot] = e;
+                    rec->slot_m[slot] = mask;
+                    rec->slot_h[slot] = hrow;
+                    rec->coef[town][slot] = R.w[town][j];
+                }
+                if (j == 0 && tid < TOPK) {        // the routing of token `town`
+                    if (ids_out) {
+                        ids_out[town * TOPK + tid] = R.ids[town][tid];
+                        w_out[town * TOPK + tid] = R.w[town][tid];
+                    }
+                    if (sg_out && tid == 0) sg_out[town] = R.sg[town];
+                }
+            }
+        } else if (blockIdx.y == 0) {
+            // the shared slot: every token, weighted by its gate; and the
+            // slot count
+            if (tid < T) {
+                const ZLoads z = acc_zload(acc, T, tid);
+                rec->coef[tid][0] = 1.f / (1.f + expf(-acc_zsum(z)));
+            }
+            if (tid == 0) {
+                rec->slot_e[0] = 0;
+                rec->slot_m[0] = tall;
+                rec->slot_h[0] = 0;
+                rec->slot_e[127] = 1 + TOPK * T;
+            }
+        }
+    } else if (slot > 0 || blockIdx.y == 0) {
+        block_route(acc, bias, T, R, mark);
+    }
+    if (!pairs && slot == 0 && blockIdx.y == 0) {
         const int nact = min(max(R.nact, 0), TOPK * T);
         const int a = threadIdx.x;
         if (a <= nact) {
@@ -711,7 +769,7 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
         }
         if (sg_out && a < T) sg_out[a] = R.sg[a];
     }
-    if (slot > 0) {
+    if (!pairs && slot > 0) {
         const int nact = min(max(R.nact, 0), TOPK * T);
         if (slot - 1 >= nact) return;
         e = min(max(R.active[slot - 1], 0), E - 1);
@@ -743,7 +801,7 @@ __global__ __launch_bounds__(256) void decode_gateup_dec(const uint16_t* __restr
     for (int t = 0; t < T; ++t) {
         if (!((mask >> t) & 1u)) continue;
         uint4v xp[4];
-        if (t == 0) {
+        if (t == town) {
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) xp[cc] = x0[cc];
         } else {
