@@ -118,23 +118,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 //
 // Work items are (row tile, block of 256 weight rows) pairs: gate/up has 4
 // blocks per tile (128 gate + the same 128 up rows each), down has 8.  A
-// grid of one workgroup per compute unit (two for the small-tile down GEMM,
-// whose LDS fits twice) -- 4 waves, one per SIMD, MFMA accumulators in
-// AGPRs -- walks the items with a fixed stride.  Consecutive items (the
-// blocks of one tile, which share their activation rows) are dealt to
-// workgroups of the same XCD, so the rows are fetched once into that XCD's
-// L2.  Row tiles hold up to 160 rows, or 32 rows up to a few hundred tokens
-// (experts then have a few dozen rows at most).
+// grid of one workgroup per compute unit -- 8 waves, two per SIMD -- or, for
+// the small-tile down GEMM, two workgroups of 4 waves per compute unit,
+// walks the items with a fixed stride.  Consecutive items (the blocks of
+// one tile, which share their activation rows) are dealt to workgroups of
+// the same XCD, so the rows are fetched once into that XCD's L2.  Row tiles
+// hold up to 160 rows, or 32 rows up to a few hundred tokens (experts then
+// have a few dozen rows at most).
 //
-// K advances in chunks of one quantisation group (64), or two (128) in the
-// small-tile gate/up GEMM.  Everything a chunk needs -- the activation rows
-// (A, fp16, gathered by token for gate/up), the 4-bit codes of the 256
-// weight rows (B) and their scales and biases -- moves from global memory
-// straight into LDS (buffer loads with an LDS destination) through a
-// 5-stage ring, 4 chunks ahead of the MFMAs.  The ring runs on across item
-// boundaries: the last 4 chunks of an item prefetch the first 4 of the
-// next, so no workgroup ever waits for a pipeline fill except at its very
-// first item.
+// K advances in chunks of one quantisation group (64; down) or two (128;
+// gate/up).  Everything a chunk needs -- the activation rows (A, fp16,
+// gathered by token for gate/up), the 4-bit codes of the 256 weight rows
+// (B) and their scales and biases -- moves from global memory straight into
+// LDS (buffer loads with an LDS destination) through a ring of STAGES
+// stages, STAGES-1 chunks ahead of the MFMAs (5 stages; 2 for the 160-row
+// gate/up tiles, whose 128-k stages take 58 KB).  The ring runs on across
+// item boundaries: the last chunks of an item prefetch the first ones of
+// the next, so no workgroup ever waits for a pipeline fill except at its
+// very first item.
 //
 // Every wave issues exactly LPC loads per chunk (plus one metadata load at
 // the first chunk of an item and a fixed number of stores per epilogue;
@@ -143,12 +144,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 // loads is a compile-time constant and the wait for a chunk is an exact
 // s_waitcnt vmcnt.
 //
-// Wave w computes 64 weight rows (gate/up: 32 gate + the same 32 up rows;
-// down: 64 output columns) for all rows of the tile, each code word being
-// dequantised once per item (dequant8: fp16 weights in registers) and fed to
-// v_mfma_f32_32x32x16_f16 with fp32 accumulation.  SwiGLU is applied in the
-// gate/up epilogue (h = bf16(silu(g) u), stored as fp16); down writes fp32
-// rows (split interface) or fp16 rows of (routing weight or shared gate) x d.
+// Wave w computes 32 weight rows with 8 waves (gate/up: 16 gate + the same
+// 16 up rows; down: 32 output columns) or 64 with 4 waves, for all rows of
+// the tile, each code word being dequantised once per item (dequant8: fp16
+// weights in registers) and fed to v_mfma_f32_32x32x16_f16 with fp32
+// accumulation.  SwiGLU is applied in the gate/up epilogue (h =
+// bf16(silu(g) u), stored as fp16); down writes fp32 rows (split interface)
+// or fp16 rows of (routing weight or shared gate) x d.
+//
+// Measured limits (4096 tokens, 160-row gate/up): removing the
+// dequantisation saves 7-10% of the kernel, removing the activation reads
+// from LDS 14%, removing every global load 21-24%, and all three together
+// leave 54% -- the MFMAs, barriers, epilogues and the last items' tail.  A
+// second wave per SIMD changes none of these shares: VALU work overlaps the
+// MFMAs of its own wave, but a VALU wave and an MFMA wave on one SIMD slow
+// each other down.
 //
 // LDS layouts (per stage; a_swz and b_swz below):
 //   A   [rows][8 or 16 pieces of 16 B], piece p of row R at slot
@@ -185,15 +195,22 @@ constexpr uint32_t OOB_OFF = 0x80000000u;   // beyond every buffer: no memory ac
 // bound the small-tile gate/up GEMM).
 template <int MTR, int KCH>
 struct PG {
-    static constexpr int WAVES = 4;
+    // 8 waves, two per SIMD, each owning one 32-column n-tile (gate/up: 16
+    // gate and the same 16 up rows) for the 160-row tiles and the 128-k
+    // gate/up instances (one workgroup per CU); 4 waves of two n-tiles each
+    // (64 columns) for the 32-row down GEMM, two workgroups per CU.
+    static constexpr int WAVES = (MTR > 32 || KCH == 2 * G) ? 8 : 4;
     static constexpr int THREADS = WAVES * 64;
+    static constexpr int NT = 8 / WAVES;                // 32-column n-tiles per wave
     static constexpr int MT = MTR;                      // rows per tile, at most
     static constexpr int NMT_MAX = MT / 32;             // 32-row m-tiles
     static constexpr int KC = KCH;                      // K per chunk
     static_assert(KC == G || KC == 2 * G, "one or two quantisation groups per chunk");
     static constexpr int STEPS = KC / 16;               // MFMA k-steps per chunk
-    static constexpr int STAGES = 5;                    // chunk c+5 refills chunk c's stage once
-                                                        // every wave is past its last read of it
+    // ring depth: chunk c+STAGES refills chunk c's stage once every wave is
+    // past its last read of it (5 stages; 2 for 160-row tiles of 128 k,
+    // 58 KB each)
+    static constexpr int STAGES = (MTR > 32 && KCH == 2 * G) ? 2 : 5;
     static constexpr int AROW = KC * 2;                 // bytes of one A row per chunk
     static constexpr int A_PIECES = AROW / 16;          // 16-byte pieces of an A row (8 or 16)
     static constexpr int A_BYTES = MT * AROW;
@@ -203,31 +220,48 @@ struct PG {
     static constexpr int B_BYTES = NCOL * BCOL;
     static constexpr int S_BYTES = NCOL * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
-    static constexpr int META = WAVES * 256;            // per-item row metadata (tokens or weights):
-                                                        // one 4-byte direct load (256 B) per wave
-    static constexpr int STG = 1024;                    // per-wave epilogue staging
-    static constexpr int CLAIM = WAVES * 256 + 16;      // the claimed item index (16 B) and the
-                                                        // landing area of waves 1-3's stand-in load
-    static constexpr int LDS_BYTES = STAGES * STAGE + 2 * META + WAVES * STG + CLAIM;
     static constexpr int A_RPL = 1024 / AROW;           // A rows per 1 KB load instruction
-    static constexpr int A_LOADS = MT / A_RPL / WAVES;
+    static constexpr int A_REAL = MT / A_RPL;           // 1 KB A loads per chunk
+    static constexpr int A_LOADS = (A_REAL + WAVES - 1) / WAVES;   // per wave; the excess are
+                                                        // stand-ins landing in DUMMY
     static constexpr int B_CPL = 1024 / BCOL;           // weight rows per 1 KB load instruction
     static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
-    static constexpr int LPC = A_LOADS + B_LOADS + 2;   // loads per wave per chunk
+    static constexpr int SB_LOADS = 8 / WAVES;          // scale/bias dword loads per wave per chunk
+                                                        // (4 waves: both; 8: waves 0-3 scales,
+                                                        // 4-7 biases)
+    static constexpr int LPC = A_LOADS + B_LOADS + SB_LOADS;   // loads per wave per chunk
+    static constexpr int DUMMY = A_LOADS * WAVES > A_REAL ? 1024 : 0;   // stand-in A landing area
+    static constexpr int META = 4 * 256;                // per-item row metadata (tokens or weights):
+                                                        // waves 0-2 load rows 0..191, one 4-byte
+                                                        // direct load each; the other waves' loads
+                                                        // land in the fourth 256 B
+    static constexpr int STG = WAVES == 8 ? 512 : 1024; // per-wave epilogue staging
+    static constexpr int CLAIM = 16 + 256;              // the claimed item index (16 B) and the
+                                                        // landing area of the other waves'
+                                                        // stand-in loads
+    static constexpr int RING = STAGES * STAGE;
+    static constexpr int META_OFF = RING + DUMMY;       // [2][META], then [WAVES][STG], then CLAIM
+    static constexpr int LDS_BYTES = META_OFF + 2 * META + WAVES * STG + CLAIM;
     static constexpr uint32_t OOB = OOB_OFF;
     static constexpr int WG_PER_CU = 160 * 1024 / LDS_BYTES;   // workgroups the LDS holds per CU
-    static_assert(MT % (A_RPL * WAVES) == 0, "A rows must split evenly over the load instructions");
+    static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES / 4;
+    static_assert(B_BYTES % (1024 * WAVES) == 0, "code loads must split evenly over the waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(META >= MT * 4, "row metadata must cover a tile");
+    static_assert(META >= MT * 4 && MT <= 192, "row metadata must cover a tile");
     static_assert((STAGES - 2) * LPC + 2 <= 63, "vmcnt range");
 };
 constexpr int MT_LARGE = MT_ROWS, MT_SMALL = 32;
-// The chunk width of an instantiation: two groups for the small-tile gate/up
-// GEMM (K = 2048); one elsewhere (the down GEMM's K = 512 has too few
-// 128-wide chunks for the ring, and the large tiles are bound by the MFMA
-// issue, not by line requests).
+// The chunk width of an instantiation: two groups for the gate/up GEMMs
+// (K = 2048; the 160-row tiles then fit a 2-stage ring only, yet measured
+// 212.5 against 227.1 us at 4096 tokens with one group and 5 stages: half
+// the barriers and half the code line requests); one for the down GEMMs
+// (K = 512 has too few 128-wide chunks, and its 8-wave instances would
+// spill).
+#ifndef MOE_LARGE_KC
+#define MOE_LARGE_KC 128
+#endif
 template <int KDIM, int MTR>
-constexpr int gemm_kc() { return (MTR == MT_SMALL && KDIM == H) ? 2 * G : G; }
+constexpr int gemm_kc() { return KDIM != H ? G : MTR == MT_SMALL ? 2 * G : MOE_LARGE_KC; }
 static_assert(PG<MT_SMALL, G>::WG_PER_CU >= 2 && PG<MT_LARGE, G>::WG_PER_CU == 1 &&
               PG<MT_SMALL, 2 * G>::WG_PER_CU == 1, "tile LDS footprints");
 
@@ -265,9 +299,9 @@ __device__ __forceinline__ uint32_t claim_item(int* ctr, uint8_t* claim) {
     if (wave == 0) {
         if (lane == 0) t = (uint32_t)atomicAdd(ctr, 1);
     } else {
+        // (every such load writes zeros to the same 256 B, which nothing reads)
         const __amdgpu_buffer_rsrc_t r = buf_rsrc(ctr, 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(claim + 16 + wave * 256), 4,
-                                                 OOB_OFF, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(claim + 16), 4, OOB_OFF, 0, 0, 0);
     }
     return t;
 }
@@ -284,6 +318,18 @@ __device__ __forceinline__ int a_swz(int R) { return KCH == G ? ((R >> 1) & 7) :
 template <int KCH>
 __device__ __forceinline__ int b_swz(int C) { return KCH == G ? ((C >> 3) & 1) : ((C >> 2) & 3); }
 
+// A wave-uniform pointer as a scalar value.  The compiler cannot always
+// prove an item's matrix pointers uniform (they flow through the item loop's
+// merges), and a buffer resource it holds in vector registers costs a
+// waterfall loop around every load that uses it.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
 // Where one item's chunks come from, per lane: the A rows this lane moves
 // and the code/scale words of this wave's weight rows.  Chunk kc adds a
 // wave-uniform offset (the soffset operand of the loads), so issuing a chunk
@@ -294,7 +340,7 @@ struct GSrc {
     __amdgpu_buffer_rsrc_t rq, rs, rb;   // this wave's code / scale / bias matrix
     uint32_t a[PG<MTR, KCH>::A_LOADS];   // A: instruction i -> rows (w*A_LOADS + i)*A_RPL + ..
     uint32_t b[PG<MTR, KCH>::B_LOADS];   // B: instruction i -> columns (w*B_LOADS + i)*B_CPL + ..
-    uint32_t s;                          // scale/bias dword of column w*64 + lane
+    uint32_t s;                          // scale/bias dword of column (w % 4)*64 + lane
 };
 
 // The code/scale/bias pointers of one weight matrix of one expert stack.
@@ -305,19 +351,26 @@ struct WPtr {
     uint32_t sq, ss;     // bytes between consecutive experts (codes, scales/biases)
 };
 
-// This wave's matrix (gate/up: waves 0-1 gate, 2-3 up; down: down) of one
+// The matrices this wave loads from (down: down; gate/up: the codes of item
+// columns 0-127 are gate rows and 128-255 the same up rows -- with 4 waves
+// waves 0-1 load gate codes and 2-3 up codes, with 8 waves waves 0-3 gate
+// and 4-7 up; the scale/bias dwords of 64 columns per wave (4 waves) or
+// per wave pair w, w+4 (8 waves) come from gate for the first 128) of one
 // stack, as opaque register values: a later choice between the routed and
 // the shared stack is then a select of values, never of the argument
 // structs' addresses (which would force the structs into scratch memory).
-template <int MODE>
+template <int MODE, int NW>
 __device__ __forceinline__ WPtr wave_ptrs(const QFFN& f) {
     WPtr w;
+    const int wave = wave_id();
     if (MODE != GM_GATEUP) {
         w.q = f.down_q; w.s = f.down_s; w.b = f.down_b;
-    } else if (wave_id() >= 2) {
-        w.q = f.up_q; w.s = f.up_s; w.b = f.up_b;
     } else {
-        w.q = f.gate_q; w.s = f.gate_s; w.b = f.gate_b;
+        const bool up_codes = wave >= NW / 2;
+        const bool up_scales = (wave & 3) >= 2;
+        w.q = up_codes ? f.up_q : f.gate_q;
+        w.s = up_scales ? f.up_s : f.gate_s;
+        w.b = up_scales ? f.up_b : f.gate_b;
     }
     asm volatile("" : "+s"(w.q), "+s"(w.s), "+s"(w.b));
     w.sq = f.sq;
@@ -347,9 +400,9 @@ __device__ __forceinline__ GSrc<MTR, KCH> gemm_src(const GItem& m, const int32_t
     const uint16_t* sc = m.shared ? ps.s : pr.s;
     const uint16_t* bi = m.shared ? ps.b : pr.b;
     const uint32_t sq = m.shared ? ps.sq : pr.sq, ss = m.shared ? ps.ss : pr.ss;
-    g.rq = buf_rsrc(expert_at(code, m.e, sq), ROWS_W * WPR * 4);
-    g.rs = buf_rsrc(expert_at(sc, m.e, ss), ROWS_W * SPR * 2);
-    g.rb = buf_rsrc(expert_at(bi, m.e, ss), ROWS_W * SPR * 2);
+    g.rq = buf_rsrc(uniform_ptr(expert_at(code, m.e, sq)), ROWS_W * WPR * 4);
+    g.rs = buf_rsrc(uniform_ptr(expert_at(sc, m.e, ss)), ROWS_W * SPR * 2);
+    g.rb = buf_rsrc(uniform_ptr(expert_at(bi, m.e, ss)), ROWS_W * SPR * 2);
     auto wrow = [&](int C) { return GATEUP ? m.nb * 128 + (C & 127) : m.nb * 256 + C; };
     // B: LDS slot (lane % B_PIECES) of column C holds the column's piece
     // slot ^ b_swz(C)
@@ -359,7 +412,7 @@ __device__ __forceinline__ GSrc<MTR, KCH> gemm_src(const GItem& m, const int32_t
         const int p = (lane % pg::B_PIECES) ^ b_swz<KCH>(C);
         g.b[i] = m.valid ? (uint32_t)(wrow(C) * WPR * 4 + 16 * p) : pg::OOB;
     }
-    g.s = m.valid ? (uint32_t)(wrow(wave * 64 + lane) * SPR * 2) : pg::OOB;
+    g.s = m.valid ? (uint32_t)(wrow((wave & 3) * 64 + lane) * SPR * 2) : pg::OOB;
     return g;
 }
 
@@ -376,12 +429,18 @@ __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst,
 // The LPC loads of chunk kc of an item into one stage.
 template <int MTR, int KCH>
 __device__ __forceinline__ void issue_chunk(const GSrc<MTR, KCH>& g, int kc,
-                                            __amdgpu_buffer_rsrc_t ra, uint8_t* stage) {
+                                            __amdgpu_buffer_rsrc_t ra, uint8_t* stage,
+                                            uint8_t* lds) {
     using pg = PG<MTR, KCH>;
     const int wave = wave_id();
 #pragma unroll
-    for (int i = 0; i < pg::A_LOADS; ++i)
-        load_lds<16>(ra, stage + (wave * pg::A_LOADS + i) * 1024, g.a[i], kc * pg::AROW);
+    for (int i = 0; i < pg::A_LOADS; ++i) {
+        // (stand-ins past the tile's last 1 KB land in the dummy area after the ring)
+        const int idx = wave * pg::A_LOADS + i;
+        uint8_t* dst = stage + idx * 1024;
+        if (pg::DUMMY && idx >= pg::A_REAL) dst = lds + pg::RING;
+        load_lds<16>(ra, dst, g.a[i], kc * pg::AROW);
+    }
 #pragma unroll
     for (int i = 0; i < pg::B_LOADS; ++i)
         load_lds<16>(g.rq, stage + pg::A_BYTES + (wave * pg::B_LOADS + i) * 1024, g.b[i],
@@ -393,8 +452,15 @@ __device__ __forceinline__ void issue_chunk(const GSrc<MTR, KCH>& g, int kc,
     // chunk: every chunk loads its own dword.
     const uint32_t so = (KCH == G && (kc & 1)) ? pg::OOB : g.s;
     const uint32_t sb = KCH == G ? (uint32_t)((kc & ~1) * 2) : (uint32_t)(kc * 4);
-    load_lds<4>(g.rs, stage + pg::A_BYTES + pg::B_BYTES + wave * 256, so, sb);
-    load_lds<4>(g.rb, stage + pg::A_BYTES + pg::B_BYTES + pg::S_BYTES + wave * 256, so, sb);
+    uint8_t* sbase = stage + pg::A_BYTES + pg::B_BYTES;
+    if constexpr (pg::WAVES == 4) {
+        load_lds<4>(g.rs, sbase + wave * 256, so, sb);
+        load_lds<4>(g.rb, sbase + pg::S_BYTES + wave * 256, so, sb);
+    } else {
+        // waves 0-3 the scales, 4-7 the biases of columns (w % 4)*64 ..
+        const bool bias = wave >= 4;
+        load_lds<4>(bias ? g.rb : g.rs, sbase + (bias ? pg::S_BYTES : 0) + (wave & 3) * 256, so, sb);
+    }
 }
 
 // MFMA: v_mfma_f32_32x32x16_f16 (32 rows x 32 columns x 16 k).  Lane l
@@ -403,11 +469,16 @@ __device__ __forceinline__ void issue_chunk(const GSrc<MTR, KCH>& g, int kc,
 // shape issues at well under half the matrix-core rate on this chip.)
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-// LDS column (0..255 of the item) of wave w's n-tile nt, lane column l%32:
-// gate/up: n-tile 0 = gate rows w*32.., n-tile 1 = the same up rows;
-// down: 64 consecutive rows per wave.
-template <bool GATEUP>
+// LDS column (0..255 of the item) of wave w's n-tile nt, lane column l%32.
+// Two n-tiles per wave (4 waves): gate/up n-tile 0 = gate rows w*32..,
+// n-tile 1 = the same up rows; down: 64 consecutive rows per wave.  One
+// n-tile per wave (8 waves): gate/up lanes l%32 < 16 take gate rows
+// w*16 + l%32, lanes l%32 >= 16 the same up rows (so each gate value and
+// its up value sit in lanes l and l ^ 16 of one wave); down: 32 rows.
+template <bool GATEUP, int NT>
 __device__ __forceinline__ int gemm_col(int wave, int nt, int l32) {
+    if constexpr (NT == 1)
+        return GATEUP ? (l32 >> 4) * 128 + wave * 16 + (l32 & 15) : wave * 32 + l32;
     return GATEUP ? nt * 128 + wave * 32 + l32 : wave * 64 + nt * 32 + l32;
 }
 
@@ -416,28 +487,31 @@ __device__ __forceinline__ int gemm_col(int wave, int nt, int l32) {
 // contiguous run of STEPS code words (the half g of each of its columns'
 // code bytes of the chunk), and with two groups per chunk lane half g works
 // in group 2 kc + g throughout.
+template <int NT>
 struct BFrag {
-    uint4v w[2][2];       // per n-tile: words of steps 0..3 (and 4..7)
-    half2v s[2], b[2];    // fp16 scale / bias, splat
+    uint4v w[NT][2];      // per n-tile: words of steps 0..3 (and 4..7)
+    half2v s[NT], b[NT];  // fp16 scale / bias, splat
 };
 
 // Even chunks read the scale and bias dwords from the stage and keep their
 // upper halves (the next chunk's group) in `carry`; odd chunks, whose stage
 // holds no scales, take them from there.  Every call site's chunk parity is
 // a compile-time constant after unrolling, so the branch folds away.
+template <int NT>
 struct SCarry {
-    half2v s[2], b[2];
+    half2v s[NT], b[NT];
 };
 
 template <bool GATEUP, int MTR, int KCH>
-__device__ __forceinline__ BFrag read_b(const uint8_t* stage, int kc, SCarry& carry) {
+__device__ __forceinline__ BFrag<PG<MTR, KCH>::NT> read_b(const uint8_t* stage, int kc,
+                                                          SCarry<PG<MTR, KCH>::NT>& carry) {
     using pg = PG<MTR, KCH>;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int l32 = lane & 31, g = lane >> 5;
-    BFrag B;
+    BFrag<pg::NT> B;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int C = gemm_col<GATEUP>(wave, nt, l32);
+    for (int nt = 0; nt < pg::NT; ++nt) {
+        const int C = gemm_col<GATEUP, pg::NT>(wave, nt, l32);
         const uint8_t* col = stage + pg::A_BYTES + C * pg::BCOL;
         if constexpr (KCH != G) {
             // two groups: pieces 2g and 2g+1, and half g of the stage's dwords
@@ -481,30 +555,31 @@ __device__ __forceinline__ void read_a(const uint8_t* stage, int s, half8 (&a)[N
     }
 }
 
-__device__ __forceinline__ void dequant_step(const BFrag& B, int s, half8 (&bf)[2]) {
+template <int NT>
+__device__ __forceinline__ void dequant_step(const BFrag<NT>& B, int s, half8 (&bf)[NT]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         const uint32_t wv = B.w[nt][s >> 2][s & 3];
         bf[nt] = dequant8(wv, B.s[nt], B.b[nt]);
     }
 }
 
-template <int NMT>
-__device__ __forceinline__ void mfma_step(const half8 (&a)[NMT], const half8 (&bf)[2],
-                                          float16v (&acc)[NMT][2]) {
+template <int NMT, int NT>
+__device__ __forceinline__ void mfma_step(const half8 (&a)[NMT], const half8 (&bf)[NT],
+                                          float16v (&acc)[NMT][NT]) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt], bf[nt], acc[mt][nt], 0, 0, 0);
 }
 
 // Scheduling hint for one MFMA step: its operand reads first, then MFMAs
 // alternating with the VALU work of the next step's dequantisation.
-template <int NMT, int DS_READS>
+template <int NMT, int NT, int DS_READS>
 __device__ __forceinline__ void sched_step() {
-    constexpr int NM = 2 * NMT;
-    constexpr int V = (32 + NM - 1) / NM;     // ~30 VALU per step's dequantisation
+    constexpr int NM = NT * NMT;
+    constexpr int V = (16 * NT + NM - 1) / NM;    // ~15 VALU per n-tile's dequantisation
     __builtin_amdgcn_sched_group_barrier(0x100, DS_READS, 0);      // DS read
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -546,8 +621,120 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t item_rows(P* base, const GItem
                     (uint32_t)m.nrows * (uint32_t)row_elems * (uint32_t)sizeof(P));
 }
 
-// Accumulator element i of a lane lies in staged half hr = i/8 of the
-// m-tile (rows 16*hr .. 16*hr+15), at staged row 8*((i/4)&1) + 4g + i%4.
+// One n-tile per wave (8 waves, 512 B of staging each).  Accumulator
+// element i of lane l holds row 8*(i/4) + 4*(l/32) + i%4 of the m-tile.
+//   gate/up: lanes l%32 < 16 (gate) and l ^ 16 (up) exchange half of their
+//     elements, so that the first lane forms h for elements 0..7 (rows
+//     0..15) and the second for elements 8..15 (rows 16..31); each half is
+//     staged as [16 rows][16 columns] and stored 8 bytes per lane.
+//   down: elements 4b..4b+3 (rows 8b..8b+7) are staged per b, as
+//     [8][32] fp16 (times the row's weight), or [8][16] fp32 per half of
+//     the columns.
+template <int MODE, int NMT, int MTR>
+__device__ __forceinline__ void gemm_epilogue_w8(const GemmArgs& A, const GItem& m,
+                                                 float16v (&acc)[NMT][1], uint8_t* stg,
+                                                 const float* coef) {
+    using pg = PG<MTR, G>;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int l32 = lane & 31, g = lane >> 5;
+    if constexpr (MODE == GM_GATEUP) {
+        const __amdgpu_buffer_rsrc_t rh = item_rows(A.hout, m, I);
+        uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [16][16] fp16, slot order
+        const bool lo = l32 < 16;
+        const int j = l32 & 15;                              // h column of the wave's 16
+#pragma unroll
+        for (int mt = 0; mt < pg::NMT_MAX; ++mt) {
+            uint16_t hv[8];
+            if (mt < NMT) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float a0 = acc[mt < NMT ? mt : 0][0][q], a1 = acc[mt < NMT ? mt : 0][0][8 + q];
+                    const float mine = lo ? a0 : a1;            // gate (elem q) / up (elem 8+q)
+                    const float other = __shfl_xor(lo ? a1 : a0, 16);
+                    const float gv = lo ? mine : other, uv = lo ? other : mine;
+                    const float h = __fdividef(gv, 1.f + __expf(-gv)) * uv;
+                    hv[q] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(f32_to_bf16(h)));
+                }
+            }
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr) {
+                uint2v v = (uint2v){0u, 0u};
+                uint32_t off = pg::OOB;
+                if (mt < NMT) {
+                    if ((lo ? 0 : 1) == hr) {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int row = 8 * (q >> 2) + 4 * g + (q & 3);
+                            st[row * 16 + (j & ~7) + chunk_slot(j & 7)] = hv[q];
+                        }
+                    }
+                    lane_exchange_fence();
+                    v = reinterpret_cast<const uint2v*>(stg)[lane];
+                    lane_exchange_fence();
+                    const int R = mt * 32 + hr * 16 + (lane >> 2);
+                    if (R < m.nrows)
+                        off = (uint32_t)((R * I + m.nb * 128 + wave * 16 + (lane & 3) * 4) * 2);
+                }
+                __builtin_amdgcn_raw_buffer_store_b64(v, rh, off, 0, 0);
+            }
+        }
+    } else if constexpr (MODE == GM_DOWN_F16W) {
+        const __amdgpu_buffer_rsrc_t rd = item_rows(A.dout16, m, H);
+        uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [8][32] fp16
+#pragma unroll
+        for (int mt = 0; mt < pg::NMT_MAX; ++mt)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                uint2v v = (uint2v){0u, 0u};
+                uint32_t off = pg::OOB;
+                if (mt < NMT) {
+                    const float4v cf = *reinterpret_cast<const float4v*>(coef + mt * 32 + 8 * b + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float d = acc[mt < NMT ? mt : 0][0][4 * b + r] * cf[r];
+                        st[(4 * g + r) * 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)d);
+                    }
+                    lane_exchange_fence();
+                    v = reinterpret_cast<const uint2v*>(stg)[lane];
+                    lane_exchange_fence();
+                    const int R = mt * 32 + 8 * b + (lane >> 3);
+                    if (R < m.nrows)
+                        off = (uint32_t)((R * H + m.nb * 256 + wave * 32 + (lane & 7) * 4) * 2);
+                }
+                __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, 0);
+            }
+    } else {
+        const __amdgpu_buffer_rsrc_t rd = item_rows(A.dout32, m, H);
+        float* st = reinterpret_cast<float*>(stg);          // [8][16] fp32
+#pragma unroll
+        for (int mt = 0; mt < pg::NMT_MAX; ++mt)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int ch = 0; ch < 2; ++ch) {
+                    uint2v v = (uint2v){0u, 0u};
+                    uint32_t off = pg::OOB;
+                    if (mt < NMT) {
+                        if ((l32 >> 4) == ch) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                st[(4 * g + r) * 16 + (l32 & 15)] = acc[mt < NMT ? mt : 0][0][4 * b + r];
+                        }
+                        lane_exchange_fence();
+                        v = reinterpret_cast<const uint2v*>(stg)[lane];
+                        lane_exchange_fence();
+                        const int R = mt * 32 + 8 * b + (lane >> 3);
+                        if (R < m.nrows)
+                            off = (uint32_t)((R * H + m.nb * 256 + wave * 32 + ch * 16 + (lane & 7) * 2) * 4);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, 0);
+                }
+    }
+}
+
+// Two n-tiles per wave (4 waves, 1 KB of staging each).  Accumulator
+// element i of a lane lies in staged half hr = i/8 of the m-tile (rows
+// 16*hr .. 16*hr+15), at staged row 8*((i/4)&1) + 4g + i%4.
 template <int MODE, int NMT, int MTR>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                                               float16v (&acc)[NMT][2], uint8_t* stg,
@@ -655,7 +842,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
 // Per-item row metadata, one load per wave at the first chunk of an item:
 // gate/up loads the NEXT item's permutation entries (token of each row),
 // down/fp16 loads the CURRENT item's row weights.  Waves 0-2 cover rows
-// 0..191; the fourth wave's load is a dummy that keeps the count uniform.
+// 0..191; the other waves' loads are dummies that keep the count uniform
+// (they all land in the fourth 256 B).
 template <int MODE>
 __device__ __forceinline__ void issue_meta(const GemmArgs& A, const GItem& m, uint8_t* meta) {
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -665,16 +853,16 @@ __device__ __forceinline__ void issue_meta(const GemmArgs& A, const GItem& m, ui
     if constexpr (MODE == GM_GATEUP) {
         const __amdgpu_buffer_rsrc_t rp = buf_rsrc(A.perm, (uint32_t)(TOPK * T * 4));
         const uint32_t off = use && !m.shared ? (uint32_t)((m.row0 + R) * 4) : OOB_OFF;
-        load_lds<4>(rp, meta + wave * 256, off, 0);
+        load_lds<4>(rp, meta + min(wave, 3) * 256, off, 0);
     } else if constexpr (MODE == GM_DOWN_F16W) {
         const __amdgpu_buffer_rsrc_t rw =
             m.shared ? buf_rsrc(A.sg, (uint32_t)(T * 4)) : buf_rsrc(A.wsorted, (uint32_t)(TOPK * T * 4));
         const int idx = m.shared ? m.row0 + R - TOPK * T : m.row0 + R;
         const uint32_t off = use ? (uint32_t)(idx * 4) : OOB_OFF;
-        load_lds<4>(rw, meta + wave * 256, off, 0);
+        load_lds<4>(rw, meta + min(wave, 3) * 256, off, 0);
     } else {
         const __amdgpu_buffer_rsrc_t rp = buf_rsrc(A.perm, 4);
-        load_lds<4>(rp, meta + wave * 256, OOB_OFF, 0);
+        load_lds<4>(rp, meta + min(wave, 3) * 256, OOB_OFF, 0);
     }
 }
 
@@ -704,51 +892,53 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     constexpr int NCH = KDIM / pg::KC;
     constexpr int S_EPI = epi_stores<MODE, MTR>();
-    constexpr int BASE = (pg::STAGES - 2) * pg::LPC;     // loads of the 3 chunks behind the awaited one
+    constexpr int S = pg::STAGES;
+    constexpr int BASE = (S - 2) * pg::LPC;     // loads of the chunks behind the awaited one
     // (a count larger than the operations really issued after the awaited
     // chunk would not wait for it; a smaller one only waits longer)
     constexpr int W_S = BASE + S_EPI < 63 ? BASE + S_EPI : 63;
     constexpr int W_XS = BASE + 2 + S_EPI < 63 ? BASE + 2 + S_EPI : 63;
-    uint8_t* meta = lds + pg::STAGES * pg::STAGE;
+    uint8_t* meta = lds + pg::META_OFF;
     uint8_t* stg = meta + 2 * pg::META + wave_id() * pg::STG;
     uint8_t* claim = meta + 2 * pg::META + pg::WAVES * pg::STG;
-    float16v acc[NMT][2];
+    constexpr int NT = pg::NT;
+    float16v acc[NMT][NT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = (float16v)0.f;
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (float16v)0.f;
 
-    half8 a_cur[NMT], bf_cur[2];
-    SCarry carry;
-    BFrag B = read_b<GATEUP, MTR, KCH>(lds + (gc % pg::STAGES) * pg::STAGE, 0, carry);
+    half8 a_cur[NMT], bf_cur[NT];
+    SCarry<NT> carry;
+    BFrag<NT> B = read_b<GATEUP, MTR, KCH>(lds + (gc % pg::STAGES) * pg::STAGE, 0, carry);
     read_a<NMT, MTR, KCH>(lds + (gc % pg::STAGES) * pg::STAGE, 0, a_cur);
     dequant_step(B, 0, bf_cur);
 
-    // One chunk.  `refill(stage)` issues the loads of chunk c+5 into the
+    // One chunk.  `refill(stage)` issues the loads of chunk c+S into the
     // stage chunk c has just released.
     auto chunk = [&](int c, auto&& refill) {
         const uint8_t* st = lds + (gc % pg::STAGES) * pg::STAGE;
 #pragma unroll
         for (int s = 0; s < pg::STEPS - 1; ++s) {
-            half8 a_nx[NMT], bf_nx[2];
+            half8 a_nx[NMT], bf_nx[NT];
             read_a<NMT, MTR, KCH>(st, s + 1, a_nx);
             dequant_step(B, s + 1, bf_nx);
-            mfma_step<NMT>(a_cur, bf_cur, acc);
-            sched_step<NMT, NMT>();
+            mfma_step<NMT, NT>(a_cur, bf_cur, acc);
+            sched_step<NMT, NT, NMT>();
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = a_nx[mt];
-            bf_cur[0] = bf_nx[0];
-            bf_cur[1] = bf_nx[1];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bf_cur[nt] = bf_nx[nt];
         }
 
-        // chunk c+1 must have landed (issued 4 refills ago).  Issued after it
-        // and allowed to stay in flight: the loads of the next three chunks
+        // chunk c+1 must have landed (issued S-1 refills ago).  Issued after
+        // it and allowed to stay in flight: the loads of the next S-2 chunks
         // (BASE), this item's metadata load and work claim (issued after the
-        // wait of c = 0, counted for c = 1..4) and, for c <= 3, the previous
-        // item's epilogue stores.
+        // wait of c = 0, counted for c = 1..S-1) and, for c <= S-2, the
+        // previous item's epilogue stores.
         if (!first && c == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(W_S));
-        else if (!first && c <= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(W_XS));
-        else if (c >= 1 && c <= 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE + 2));
+        else if (!first && c <= S - 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(W_XS));
+        else if (c >= 1 && c <= S - 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE + 2));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(BASE));
         pipe_barrier();
 
@@ -758,7 +948,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         // relative to the other vector-memory operations: the wait counts
         // above depend on that order)
         const bool more = c + 1 < NCH;
-        half8 a_nx[NMT], bf_nx[2];
+        half8 a_nx[NMT], bf_nx[NT];
         if (more) {
             const uint8_t* sn = lds + ((gc + 1) % pg::STAGES) * pg::STAGE;
             B = read_b<GATEUP, MTR, KCH>(sn, c + 1, carry);
@@ -768,23 +958,23 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         refill(const_cast<uint8_t*>(st));
         __builtin_amdgcn_sched_barrier(0);
         if (more) dequant_step(B, 0, bf_nx);
-        mfma_step<NMT>(a_cur, bf_cur, acc);
+        mfma_step<NMT, NT>(a_cur, bf_cur, acc);
 #pragma unroll
-        for (int i = 0; i < 2 * NMT; ++i) {
+        for (int i = 0; i < NT * NMT; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, (40 + 2 * NMT - 1) / (2 * NMT), 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (20 * NT + NT * NMT - 1) / (NT * NMT), 0);
         }
         if (more) {
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = a_nx[mt];
-            bf_cur[0] = bf_nx[0];
-            bf_cur[1] = bf_nx[1];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bf_cur[nt] = bf_nx[nt];
         }
         ++gc;
     };
-    auto own = [&](int c) { return [&, c](uint8_t* st) { issue_chunk(src_cur, c + pg::STAGES, ra, st); }; };
+    auto own = [&](int c) { return [&, c](uint8_t* st) { issue_chunk(src_cur, c + pg::STAGES, ra, st, lds); }; };
     auto next = [&](int c) {
-        return [&, c](uint8_t* st) { issue_chunk(src_nxt, c + pg::STAGES - NCH, ra, st); };
+        return [&, c](uint8_t* st) { issue_chunk(src_nxt, c + pg::STAGES - NCH, ra, st, lds); };
     };
     // the next item's sources (its row tokens arrived with this item's first chunk)
     auto make_next = [&]() {
@@ -792,12 +982,12 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
                                        A.T, pr, ps);
     };
 
-    constexpr int MAIN = NCH - pg::STAGES;      // chunks whose refill stays in this item
-    constexpr int HEAD = 5;                     // chunks with special wait counts
+    constexpr int MAIN = NCH - S;               // chunks whose refill stays in this item
+    constexpr int HEAD = S;                     // chunks with special wait counts
     static_assert(MAIN >= 1, "an item needs more chunks than pipeline stages");
     // head: unrolled, so every wait count and refill target is a constant
     chunk(0, [&](uint8_t* st) {
-        issue_chunk(src_cur, pg::STAGES, ra, st);
+        issue_chunk(src_cur, pg::STAGES, ra, st, lds);
         __builtin_amdgcn_sched_barrier(0);      // the metadata load goes after the chunk's loads
         // the item after this one, claimed during the previous item (its
         // index was written to LDS before this chunk's barrier)
@@ -816,9 +1006,9 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
             chunk(c, next(c));
         }
     }
-    // main: one basic block per two chunks (an even number of them, HEAD odd,
-    // so each call's chunk parity is a constant)
-    static_assert(MAIN <= HEAD || ((MAIN - HEAD) % 2 == 0 && HEAD % 2 == 1), "main chunk pairs");
+    // main: one basic block per two chunks (an even number of them, so each
+    // call's chunk parity is a constant)
+    static_assert(MAIN <= HEAD || (MAIN - HEAD) % 2 == 0, "main chunk pairs");
     for (int i = 0; i < (MAIN - HEAD) / 2; ++i) {
         const int c = HEAD + 2 * i;
         chunk(c, own(c));
@@ -829,7 +1019,10 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 #pragma unroll
     for (int c = (MAIN > HEAD ? MAIN : HEAD); c < NCH; ++c) chunk(c, next(c));
     __builtin_amdgcn_sched_barrier(0);          // epilogue stores after the last refill
-    gemm_epilogue<MODE, NMT, MTR>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
+    if constexpr (NT == 1)
+        gemm_epilogue_w8<MODE, NMT, MTR>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
+    else
+        gemm_epilogue<MODE, NMT, MTR>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -840,13 +1033,12 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 // two items of each workgroup are static and the rest are claimed from the
 // XCD's counter in order -- longest first.
 template <int KDIM, int MODE, int MTR>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(PG<MTR, gemm_kc<KDIM, MTR>()>::WG_PER_CU)))
+__global__ __launch_bounds__((PG<MTR, gemm_kc<KDIM, MTR>()>::THREADS))
+__attribute__((amdgpu_waves_per_eu(PG<MTR, gemm_kc<KDIM, MTR>()>::WAVES_PER_SIMD)))
 void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict__ tile_count,
                   QFFN routed, QFFN shared) {
     constexpr int KCH = gemm_kc<KDIM, MTR>();
     using pg = PG<MTR, KCH>;
-    static_assert(pg::THREADS == 256, "launch bounds");
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     __shared__ __attribute__((aligned(16))) uint8_t lds[pg::LDS_BYTES];
@@ -856,7 +1048,7 @@ void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict
     if (wl >= nx) return;
     const Sched sc{tile_count + (GATEUP ? GEMM_CTR_GATEUP : GEMM_CTR_DOWN) + xcd, nx, xcd, 2 * nwl,
                    tiles};
-    uint8_t* meta = lds + pg::STAGES * pg::STAGE;
+    uint8_t* meta = lds + pg::META_OFF;
     const __amdgpu_buffer_rsrc_t ra = buf_rsrc(args.ain, args.ain_bytes);
 
     GItem cur = gemm_item<NB>(wl, nx, xcd, tiles);
@@ -867,11 +1059,11 @@ void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
     }
-    const WPtr pr = wave_ptrs<MODE>(routed), ps = wave_ptrs<MODE>(shared);
+    const WPtr pr = wave_ptrs<MODE, pg::WAVES>(routed), ps = wave_ptrs<MODE, pg::WAVES>(shared);
     GSrc<MTR, KCH> src_cur =
         gemm_src<KDIM, MODE, MTR, KCH>(cur, reinterpret_cast<const int32_t*>(meta), args.T, pr, ps);
     GSrc<MTR, KCH> src_nxt = src_cur;
-    for (int c = 0; c < pg::STAGES; ++c) issue_chunk(src_cur, c, ra, lds + c * pg::STAGE);
+    for (int c = 0; c < pg::STAGES; ++c) issue_chunk(src_cur, c, ra, lds + c * pg::STAGE, lds);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((pg::STAGES - 1) * pg::LPC));   // chunk 0 landed
     pipe_barrier();
 
@@ -959,11 +1151,13 @@ static void launch_gemm(const GemmArgs& a, const Tile* tiles, int* tile_count, c
     if (mt_rows == MT_SMALL)
         hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_SMALL>),
                            dim3(256 * PG<MT_SMALL, gemm_kc<KDIM, MT_SMALL>()>::WG_PER_CU),
-                           dim3(256), 0, st, a, tiles, tile_count, routed, shared);
+                           dim3(PG<MT_SMALL, gemm_kc<KDIM, MT_SMALL>()>::THREADS), 0, st, a, tiles,
+                           tile_count, routed, shared);
     else
         hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_LARGE>),
                            dim3(256 * PG<MT_LARGE, gemm_kc<KDIM, MT_LARGE>()>::WG_PER_CU),
-                           dim3(256), 0, st, a, tiles, tile_count, routed, shared);
+                           dim3(PG<MT_LARGE, gemm_kc<KDIM, MT_LARGE>()>::THREADS), 0, st, a, tiles,
+                           tile_count, routed, shared);
 }
 
 // xh_ready: the fp16 activations are already in xh (the router wrote them).
