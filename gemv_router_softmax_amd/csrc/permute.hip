@@ -8,9 +8,13 @@
 // ascending order.
 //
 //   perm_small      one workgroup does everything (8T <= SMALL_MAX entries)
-//   perm_count      large T: per-chunk expert histograms       (grid: chunks)
-//   perm_scan       large T: column scans -> per-chunk bases   (one workgroup)
-//   perm_scatter    large T: stable scatter of every chunk     (grid: chunks)
+//   perm_count      larger T: per-chunk expert histograms      (grid: chunks)
+//   perm_scan_scatter  up to SCAN_CHUNKS chunks: every workgroup derives its
+//                   chunk's bases from all the histograms, then scatters it;
+//                   workgroup 0 also writes the counts and offsets and plans
+//                   the row tiles                              (grid: chunks)
+//   perm_scan       more chunks: column scans -> per-chunk bases (one workgroup)
+//   perm_scatter    more chunks: stable scatter of every chunk   (grid: chunks)
 //   plan_tiles      row tiles of <= mt_rows rows per expert (expert 256 is the
 //                   shared expert over all T tokens), read by the expert
 //                   kernels from device memory so the host never needs the
@@ -24,6 +28,8 @@ namespace moe {
 constexpr int PERM_CHUNK = 512;    // entries per chunk in the large path (two rounds
                                    // of the block scatter per workgroup)
 constexpr int SMALL_MAX = 1024;    // entries handled by perm_small
+constexpr int SCAN_CHUNKS = 64;    // chunks handled by perm_scan_scatter (T <= 4096); each of
+                                   // its workgroups reads every chunk's histogram
 
 // Row tiles: routed expert e owns rows offsets[e] .. offsets[e+1]-1, the
 // shared expert (group 256) owns rows 8T .. 9T-1.  A group of n rows is cut
@@ -200,6 +206,51 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ 
     stable_scatter(ids, f0, f1, base, wcnt, perm, inv, wsrc, wsorted);
 }
 
+// Up to SCAN_CHUNKS chunks.  Thread e reads expert e's count in every chunk
+// (all loads in flight together): its entries in chunks before this one
+// give the chunk's base inside the expert's segment, the total its segment
+// length; a block scan of the totals gives the segment starts.  The scan
+// is repeated by every workgroup instead of run once between two launches.
+__global__ __launch_bounds__(256) void perm_scan_scatter(const int32_t* __restrict__ ids, int n,
+                                                         int nchunks,
+                                                         const int32_t* __restrict__ chunk_counts,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ perm,
+                                                         int32_t* __restrict__ inv,
+                                                         const float* __restrict__ wsrc,
+                                                         float* __restrict__ wsorted, int T,
+                                                         int mt_rows, Tile* __restrict__ tiles,
+                                                         int* __restrict__ tile_count) {
+    __shared__ int base[256];
+    __shared__ int wcnt[4 * 256];
+    __shared__ int scr[4];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    int c[SCAN_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < SCAN_CHUNKS; ++i) c[i] = i < nchunks ? chunk_counts[(size_t)i * 256 + tid] : 0;
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < SCAN_CHUNKS; ++i) {
+        pre += i < b ? c[i] : 0;
+        tot += c[i];
+    }
+    int total;
+    const int off = block_excl_scan256(tot, scr, &total);
+    base[tid] = off + pre;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
+    __syncthreads();
+    const int f0 = b * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
+    stable_scatter(ids, f0, f1, base, wcnt, perm, inv, wsrc, wsorted);
+    if (b == 0) {
+        counts[tid] = tot;
+        offsets[tid] = off;
+        if (tid == 0) offsets[E] = total;
+        if (tiles) plan_block(off, off + tot, T, max_tiles(T), mt_rows, tiles, tile_count, scr);
+    }
+}
+
 int perm_chunks(int T) { return (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK; }
 
 // wts/wsorted: optional (both or neither): wsorted[p] = wts[perm[p]], the
@@ -220,6 +271,11 @@ void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets
     }
     const int nb = perm_chunks(T);
     hipLaunchKernelGGL(perm_count, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts);
+    if (nb <= SCAN_CHUNKS) {
+        hipLaunchKernelGGL(perm_scan_scatter, dim3(nb), dim3(256), 0, st, ids, n, nb, chunk_counts,
+                           counts, offsets, perm, inv, wts, wsorted, T, mt, tiles, tile_count);
+        return;
+    }
     hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, st, nb, chunk_counts, counts, offsets, T,
                        mt, tiles, tile_count);
     hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts, offsets,
