@@ -22,6 +22,13 @@ constexpr int WAVE = 64;
 constexpr int MT_ROWS = 160;
 constexpr int MT_MIN_ROWS = 32;
 
+// Permutation of 8T (token, rank) entries: one workgroup sorts up to
+// PERM_SMALL_MAX entries alone; above that the entries are histogrammed,
+// scanned and scattered in chunks of PERM_CHUNK (the layer call's top-8
+// kernel adds each token's eight picks to its chunk's histogram).
+constexpr int PERM_CHUNK = 512;
+constexpr int PERM_SMALL_MAX = 1024;
+
 // Device view of one expert stack: the nine arrays and the byte distance
 // between consecutive experts in the code arrays (sq) and in the
 // scale/bias arrays (ss) -- the dense sizes, or the caller's expert stride.

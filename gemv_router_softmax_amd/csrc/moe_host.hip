@@ -15,12 +15,14 @@
 namespace moe {
 void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                   const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
-                  hipStream_t st, uint16_t* xh = nullptr, float* part = nullptr);
+                  hipStream_t st, uint16_t* xh = nullptr, float* part = nullptr,
+                  int32_t* chunk_counts = nullptr);
+bool route_counts_chunks(int T);
 // The router's K-split partials (up to 8 slices of T x E fp32) live in the
 // h rows, which nothing reads before the gate/up GEMM rewrites them.
 static_assert((size_t)(TOPK + 1) * I * 2 >= (size_t)8 * E * 4, "router partials fit the h rows");
 void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
-                         float* logits, hipStream_t st);
+                         float* logits, hipStream_t st, int32_t* zero = nullptr, int nzero = 0);
 void launch_route_select(const float* logits, const uint16_t* x, const uint16_t* wsg, int T,
                          int32_t* ids, float* wts, float* sg, int32_t* counts, int32_t* offsets,
                          int32_t* perm, int32_t* inv, Tile* tiles, int* tile_count,
@@ -42,7 +44,7 @@ size_t route_acc_bytes(int T);
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st,
                     const float* wts = nullptr, float* wsorted = nullptr, Tile* tiles = nullptr,
-                    int* tile_count = nullptr);
+                    int* tile_count = nullptr, bool counted = false);
 void launch_plan(const int32_t* offsets, int T, Tile* tiles, int* tile_count, hipStream_t st);
 int perm_chunks(int T);
 int max_tiles(int T);
@@ -305,13 +307,14 @@ int check_route_out(const moe_options* opt) {
 void prefill_front(const uint16_t* x, int T, const moe_layer* layer, void* ws, const WsLayout& L,
                    int32_t* ids, float* wts, float* sg, hipStream_t st) {
     // the top-8 kernel also writes the fp16 activations the grouped GEMM reads
+    // and, for chunked permutations, the chunk histograms
     launch_route(x, T, layer->w_router, layer->router_bias, layer->w_shared_gate,
                  at<float>(ws, L.logits), ids, wts, sg, st, at<uint16_t>(ws, L.xh),
-                 at<float>(ws, L.h));
+                 at<float>(ws, L.h), at<int32_t>(ws, L.chunk_counts));
     launch_permute(ids, T, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
                    at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
                    at<int32_t>(ws, L.chunk_counts), st, wts, at<float>(ws, L.wsorted),
-                   at<Tile>(ws, L.tiles), at<int>(ws, L.tile_count));
+                   at<Tile>(ws, L.tiles), at<int>(ws, L.tile_count), route_counts_chunks(T));
 }
 
 void prefill_back(const uint16_t* x, int T, const moe_layer* layer, uint16_t* y, uint16_t* res,

@@ -7,7 +7,7 @@
 // decide a position).  Each expert's segment lists its slots f = 8t + j in
 // ascending order.
 //
-//   perm_small      one workgroup does everything (8T <= SMALL_MAX entries)
+//   perm_small      one workgroup does everything (8T <= PERM_SMALL_MAX entries)
 //   perm_count      larger T: per-chunk expert histograms      (grid: chunks)
 //   perm_scan_scatter  up to SCAN_CHUNKS chunks: every workgroup derives its
 //                   chunk's bases from all the histograms, then scatters it;
@@ -25,9 +25,8 @@
 
 namespace moe {
 
-constexpr int PERM_CHUNK = 512;    // entries per chunk in the large path (two rounds
-                                   // of the block scatter per workgroup)
-constexpr int SMALL_MAX = 1024;    // entries handled by perm_small
+// (PERM_CHUNK entries per chunk in the large path: two rounds of the block
+// scatter per workgroup; PERM_SMALL_MAX entries handled by perm_small)
 constexpr int SCAN_CHUNKS = 64;    // chunks handled by perm_scan_scatter (T <= 4096); each of
                                    // its workgroups reads every chunk's histogram
 
@@ -259,18 +258,20 @@ int gemm_tile_rows(int T);
 
 // tiles/tile_count: optional (both or neither): also plan the row tiles
 // (and zero the GEMMs' work counters), as launch_plan would.
+// counted: chunk_counts already holds the chunk histograms (the layer
+// call's top-8 kernel accumulates them).
 void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets, int32_t* perm,
                     int32_t* inv, int32_t* chunk_counts, hipStream_t st, const float* wts,
-                    float* wsorted, Tile* tiles, int* tile_count) {
+                    float* wsorted, Tile* tiles, int* tile_count, bool counted) {
     const int mt = gemm_tile_rows(T);
     const int n = TOPK * T;
-    if (n <= SMALL_MAX) {
+    if (n <= PERM_SMALL_MAX) {
         hipLaunchKernelGGL(perm_small, dim3(1), dim3(256), 0, st, ids, n, counts, offsets, perm,
                            inv, wts, wsorted, T, mt, tiles, tile_count);
         return;
     }
     const int nb = perm_chunks(T);
-    hipLaunchKernelGGL(perm_count, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts);
+    if (!counted) hipLaunchKernelGGL(perm_count, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts);
     if (nb <= SCAN_CHUNKS) {
         hipLaunchKernelGGL(perm_scan_scatter, dim3(nb), dim3(256), 0, st, ids, n, nb, chunk_counts,
                            counts, offsets, perm, inv, wts, wsorted, T, mt, tiles, tile_count);

@@ -113,12 +113,22 @@ __device__ __forceinline__ void rl_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buf
 // logits[(z*T + t)*E + e]; route_topk sums the slices in order and adds the
 // bias.  A few hundred tokens make only T/32 x 2 workgroups, so the split is
 // what fills the chip there.
+//
+// zero / nzero: optional int array the workgroups clear on the way (the
+// permutation's chunk histograms, which the top-8 kernel after this one
+// accumulates).
 template <int KS>
 __global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restrict__ x, int T,
                                                          const uint16_t* __restrict__ wr,
                                                          const float* __restrict__ bias,
-                                                         float* __restrict__ logits) {
+                                                         float* __restrict__ logits,
+                                                         int32_t* __restrict__ zero, int nzero) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[RL_STAGES * RL_STAGE];
+    if (zero) {
+        const int nwg = gridDim.x * gridDim.y * gridDim.z;
+        const int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+        for (int i = wg * 256 + (int)threadIdx.x; i < nzero; i += nwg * 256) zero[i] = 0;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
@@ -201,6 +211,10 @@ static int route_ksplit(int T) {
 // part / nks: K-split partial logits [nks][T][E] of route_logits_tile<KS>
 // (nks > 1): summed here in slice order, plus the bias, and also stored to
 // logits.
+//
+// chunk_counts: optional; each token's eight experts are added to the
+// histogram of its permutation chunk, chunk_counts[8t / PERM_CHUNK][e]
+// (integer atomics: the counts do not depend on their order).
 __global__ __launch_bounds__(256) void route_topk(float* __restrict__ logits,
                                                   const float* __restrict__ part, int nks,
                                                   const float* __restrict__ bias,
@@ -209,10 +223,12 @@ __global__ __launch_bounds__(256) void route_topk(float* __restrict__ logits,
                                                   int32_t* __restrict__ ids,
                                                   float* __restrict__ wts,
                                                   float* __restrict__ sg,
-                                                  uint16_t* __restrict__ xh) {
+                                                  uint16_t* __restrict__ xh,
+                                                  int32_t* __restrict__ chunk_counts) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
+    int e;
     const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
     const uint4v x0 = xr[0], x1 = xr[1], x2 = xr[2], x3 = xr[3];
     if (part) {
@@ -224,10 +240,13 @@ __global__ __launch_bounds__(256) void route_topk(float* __restrict__ logits,
             for (int j = 0; j < 4; ++j) v[j] += bias[lane * 4 + j];
         }
         reinterpret_cast<float4v*>(logits + (size_t)t * E)[lane] = v;
-        wave_top8_v(v, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
+        e = wave_top8_v(v, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
     } else {
-        wave_top8(logits + (size_t)t * E, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
+        e = wave_top8_v(reinterpret_cast<const float4v*>(logits + (size_t)t * E)[lane],
+                        ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
     }
+    if (chunk_counts && lane < TOPK)
+        atomicAdd(&chunk_counts[(size_t)(t * TOPK / PERM_CHUNK) * E + e], 1);
     const uint4v* gr = reinterpret_cast<const uint4v*>(wsg) + lane * 4;
     float z = dot8_bf16(x0, gr[0]) + dot8_bf16(x1, gr[1]) + dot8_bf16(x2, gr[2]) +
               dot8_bf16(x3, gr[3]);
@@ -243,38 +262,47 @@ __global__ __launch_bounds__(256) void route_topk(float* __restrict__ logits,
 }
 
 void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
-                         float* logits, hipStream_t st) {
+                         float* logits, hipStream_t st, int32_t* zero, int nzero) {
     if (T <= 32) {
         hipLaunchKernelGGL(route_logits_gemv, dim3(E / 4), dim3(256), 0, st, x, T, wr, bias,
                            logits);
     } else {
         hipLaunchKernelGGL(route_logits_tile<1>, dim3((T + RL_TOK - 1) / RL_TOK, E / RL_EXP),
-                           dim3(256), 0, st, x, T, wr, bias, logits);
+                           dim3(256), 0, st, x, T, wr, bias, logits, zero, nzero);
     }
 }
 
+// Whether launch_route accumulates the permutation's chunk histograms (when
+// given them): every T whose permutation runs in chunks.
+bool route_counts_chunks(int T) { return TOPK * T > PERM_SMALL_MAX; }
+
 // xh: optional fp16 activation copy.  part: optional scratch for K-split
 // partial logits, RL_KS_MAX * T * E floats, free for the duration of the
-// call (without it the router GEMM runs unsplit).
+// call (without it the router GEMM runs unsplit).  chunk_counts: optional
+// permutation chunk histograms (perm_chunks(T) x E ints), cleared by the
+// router GEMM and accumulated by the top-8 kernel when
+// route_counts_chunks(T).
 void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
                   const uint16_t* wsg, float* logits, int32_t* ids, float* wts, float* sg,
-                  hipStream_t st, uint16_t* xh, float* part) {
+                  hipStream_t st, uint16_t* xh, float* part, int32_t* chunk_counts) {
+    if (!route_counts_chunks(T)) chunk_counts = nullptr;
+    const int nzero = chunk_counts ? (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK * E : 0;
     const int ks = (part && T > 32) ? route_ksplit(T) : 1;
     if (ks == 1) {
-        launch_route_logits(x, T, wr, bias, logits, st);
+        launch_route_logits(x, T, wr, bias, logits, st, chunk_counts, nzero);
         hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits,
                            (const float*)nullptr, 0, (const float*)nullptr, x, wsg, T, ids, wts,
-                           sg, xh);
+                           sg, xh, chunk_counts);
         return;
     }
     const dim3 grid((T + RL_TOK - 1) / RL_TOK, E / RL_EXP, ks);
     switch (ks) {
-        case 2: hipLaunchKernelGGL(route_logits_tile<2>, grid, dim3(256), 0, st, x, T, wr, bias, part); break;
-        case 4: hipLaunchKernelGGL(route_logits_tile<4>, grid, dim3(256), 0, st, x, T, wr, bias, part); break;
-        default: hipLaunchKernelGGL(route_logits_tile<8>, grid, dim3(256), 0, st, x, T, wr, bias, part); break;
+        case 2: hipLaunchKernelGGL(route_logits_tile<2>, grid, dim3(256), 0, st, x, T, wr, bias, part, chunk_counts, nzero); break;
+        case 4: hipLaunchKernelGGL(route_logits_tile<4>, grid, dim3(256), 0, st, x, T, wr, bias, part, chunk_counts, nzero); break;
+        default: hipLaunchKernelGGL(route_logits_tile<8>, grid, dim3(256), 0, st, x, T, wr, bias, part, chunk_counts, nzero); break;
     }
     hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, (const float*)part,
-                       ks, bias, x, wsg, T, ids, wts, sg, xh);
+                       ks, bias, x, wsg, T, ids, wts, sg, xh, chunk_counts);
 }
 
 }  // namespace moe
