@@ -118,21 +118,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 //
 // Work items are (row tile, block of 256 weight rows) pairs: gate/up has 4
 // blocks per tile (128 gate + the same 128 up rows each), down has 8.  A
-// grid of one workgroup per compute unit -- 8 waves, two per SIMD -- or, for
-// the small-tile down GEMM, two workgroups of 4 waves per compute unit,
+// grid of 8-wave workgroups, one per compute unit (two for 32-row tiles),
 // walks the items with a fixed stride.  Consecutive items (the blocks of
 // one tile, which share their activation rows) are dealt to workgroups of
 // the same XCD, so the rows are fetched once into that XCD's L2.  Row tiles
 // hold up to 160 rows, or 32 rows up to a few hundred tokens (experts then
 // have a few dozen rows at most).
 //
-// K advances in chunks of one quantisation group (64; down) or two (128;
-// gate/up).  Everything a chunk needs -- the activation rows (A, fp16,
-// gathered by token for gate/up), the 4-bit codes of the 256 weight rows
-// (B) and their scales and biases -- moves from global memory straight into
-// LDS (buffer loads with an LDS destination) through a ring of STAGES
-// stages, STAGES-1 chunks ahead of the MFMAs (5 stages; 2 for the 160-row
-// gate/up tiles, whose 128-k stages take 58 KB).  The ring runs on across
+// K advances in chunks of two quantisation groups (128), or one (64) in the
+// 160-row down GEMM.  Everything a chunk needs -- the activation rows (A,
+// fp16, gathered by token for gate/up), the 4-bit codes of the 256 weight
+// rows (B) and their scales and biases -- moves from global memory straight
+// into LDS (buffer loads with an LDS destination) through a ring of STAGES
+// stages, STAGES-1 chunks ahead of the MFMAs (2 stages of 128 k; 5 of
+// 64 k).  The ring runs on across
 // item boundaries: the last chunks of an item prefetch the first ones of
 // the next, so no workgroup ever waits for a pipeline fill except at its
 // very first item.
@@ -144,10 +143,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 // loads is a compile-time constant and the wait for a chunk is an exact
 // s_waitcnt vmcnt.
 //
-// Wave w computes 32 weight rows with 8 waves (gate/up: 16 gate + the same
-// 16 up rows; down: 32 output columns) or 64 with 4 waves, for all rows of
-// the tile, each code word being dequantised once per item (dequant8: fp16
-// weights in registers) and fed to v_mfma_f32_32x32x16_f16 with fp32
+// Wave w computes 32 weight rows (gate/up: 16 gate + the same 16 up rows;
+// down: 32 output columns) for all rows of the tile, each code word being
+// dequantised once per item (dequant8: fp16 weights in registers) and fed to v_mfma_f32_32x32x16_f16 with fp32
 // accumulation.  SwiGLU is applied in the gate/up epilogue (h =
 // bf16(silu(g) u), stored as fp16); down writes fp32 rows (split interface)
 // or fp16 rows of (routing weight or shared gate) x d.
@@ -195,22 +193,22 @@ constexpr uint32_t OOB_OFF = 0x80000000u;   // beyond every buffer: no memory ac
 // bound the small-tile gate/up GEMM).
 template <int MTR, int KCH>
 struct PG {
-    // 8 waves, two per SIMD, each owning one 32-column n-tile (gate/up: 16
-    // gate and the same 16 up rows) for the 160-row tiles and the 128-k
-    // gate/up instances (one workgroup per CU); 4 waves of two n-tiles each
-    // (64 columns) for the 32-row down GEMM, two workgroups per CU.
-    static constexpr int WAVES = (MTR > 32 || KCH == 2 * G) ? 8 : 4;
+    // 8 waves, each owning one 32-column n-tile of the item's 256 weight
+    // rows (gate/up: 16 gate and the same 16 up rows); two waves per SIMD
+    // (one workgroup per CU, or two 8-wave workgroups for 32-row tiles).
+    static constexpr int WAVES = 8;
     static constexpr int THREADS = WAVES * 64;
-    static constexpr int NT = 8 / WAVES;                // 32-column n-tiles per wave
+    static constexpr int NT = 1;                        // 32-column n-tiles per wave
     static constexpr int MT = MTR;                      // rows per tile, at most
     static constexpr int NMT_MAX = MT / 32;             // 32-row m-tiles
     static constexpr int KC = KCH;                      // K per chunk
     static_assert(KC == G || KC == 2 * G, "one or two quantisation groups per chunk");
     static constexpr int STEPS = KC / 16;               // MFMA k-steps per chunk
     // ring depth: chunk c+STAGES refills chunk c's stage once every wave is
-    // past its last read of it (5 stages; 2 for 160-row tiles of 128 k,
-    // 58 KB each)
-    static constexpr int STAGES = (MTR > 32 && KCH == 2 * G) ? 2 : 5;
+    // past its last read of it (5 stages with 64 k per chunk; 2 with 128 k,
+    // whose 160-row stages take 58 KB and whose 32-row stages then fit two
+    // workgroups per CU)
+    static constexpr int STAGES = KCH == 2 * G ? 2 : 5;
     static constexpr int AROW = KC * 2;                 // bytes of one A row per chunk
     static constexpr int A_PIECES = AROW / 16;          // 16-byte pieces of an A row (8 or 16)
     static constexpr int A_BYTES = MT * AROW;
@@ -226,16 +224,15 @@ struct PG {
                                                         // stand-ins landing in DUMMY
     static constexpr int B_CPL = 1024 / BCOL;           // weight rows per 1 KB load instruction
     static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
-    static constexpr int SB_LOADS = 8 / WAVES;          // scale/bias dword loads per wave per chunk
-                                                        // (4 waves: both; 8: waves 0-3 scales,
-                                                        // 4-7 biases)
+    static constexpr int SB_LOADS = 1;                  // scale/bias dword loads per wave per chunk
+                                                        // (waves 0-3 scales, 4-7 biases)
     static constexpr int LPC = A_LOADS + B_LOADS + SB_LOADS;   // loads per wave per chunk
     static constexpr int DUMMY = A_LOADS * WAVES > A_REAL ? 1024 : 0;   // stand-in A landing area
     static constexpr int META = 4 * 256;                // per-item row metadata (tokens or weights):
                                                         // waves 0-2 load rows 0..191, one 4-byte
                                                         // direct load each; the other waves' loads
                                                         // land in the fourth 256 B
-    static constexpr int STG = WAVES == 8 ? 512 : 1024; // per-wave epilogue staging
+    static constexpr int STG = 512;                     // per-wave epilogue staging
     static constexpr int CLAIM = 16 + 256;              // the claimed item index (16 B) and the
                                                         // landing area of the other waves'
                                                         // stand-in loads
@@ -251,19 +248,18 @@ struct PG {
     static_assert((STAGES - 2) * LPC + 2 <= 63, "vmcnt range");
 };
 constexpr int MT_LARGE = MT_ROWS, MT_SMALL = 32;
-// The chunk width of an instantiation: two groups for the gate/up GEMMs
-// (K = 2048; the 160-row tiles then fit a 2-stage ring only, yet measured
-// 212.5 against 227.1 us at 4096 tokens with one group and 5 stages: half
-// the barriers and half the code line requests); one for the down GEMMs
-// (K = 512 has too few 128-wide chunks, and its 8-wave instances would
-// spill).
+// The chunk width of an instantiation: two groups (128 k, 2-stage ring)
+// everywhere except the 160-row down GEMM, whose 128-k instances would
+// spill.  Same-run timings: 160-row gate/up 212.5 against 227.1 us at 4096
+// tokens with one group and 5 stages (half the barriers and half the code
+// line requests); 32-row down 45.3 against 52.6 us in the 512-token chain.
 #ifndef MOE_LARGE_KC
 #define MOE_LARGE_KC 128
 #endif
 template <int KDIM, int MTR>
-constexpr int gemm_kc() { return KDIM != H ? G : MTR == MT_SMALL ? 2 * G : MOE_LARGE_KC; }
-static_assert(PG<MT_SMALL, G>::WG_PER_CU >= 2 && PG<MT_LARGE, G>::WG_PER_CU == 1 &&
-              PG<MT_SMALL, 2 * G>::WG_PER_CU == 1, "tile LDS footprints");
+constexpr int gemm_kc() { return MTR == MT_SMALL ? 2 * G : KDIM == H ? MOE_LARGE_KC : G; }
+static_assert(PG<MT_SMALL, 2 * G>::WG_PER_CU == 2 && PG<MT_LARGE, G>::WG_PER_CU == 1 &&
+              PG<MT_LARGE, 2 * G>::WG_PER_CU == 1, "tile LDS footprints");
 
 typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
@@ -352,21 +348,20 @@ struct WPtr {
 };
 
 // The matrices this wave loads from (down: down; gate/up: the codes of item
-// columns 0-127 are gate rows and 128-255 the same up rows -- with 4 waves
-// waves 0-1 load gate codes and 2-3 up codes, with 8 waves waves 0-3 gate
-// and 4-7 up; the scale/bias dwords of 64 columns per wave (4 waves) or
-// per wave pair w, w+4 (8 waves) come from gate for the first 128) of one
-// stack, as opaque register values: a later choice between the routed and
-// the shared stack is then a select of values, never of the argument
-// structs' addresses (which would force the structs into scratch memory).
-template <int MODE, int NW>
+// columns 0-127 are gate rows and 128-255 the same up rows, loaded by waves
+// 0-3 and 4-7; the scale/bias dwords of the 64 columns of wave pair w,
+// w+4 come from gate for the first 128) of one stack, as opaque register
+// values: a later choice between the routed and the shared stack is then a
+// select of values, never of the argument structs' addresses (which would
+// force the structs into scratch memory).
+template <int MODE>
 __device__ __forceinline__ WPtr wave_ptrs(const QFFN& f) {
     WPtr w;
     const int wave = wave_id();
     if (MODE != GM_GATEUP) {
         w.q = f.down_q; w.s = f.down_s; w.b = f.down_b;
     } else {
-        const bool up_codes = wave >= NW / 2;
+        const bool up_codes = wave >= 4;
         const bool up_scales = (wave & 3) >= 2;
         w.q = up_codes ? f.up_q : f.gate_q;
         w.s = up_scales ? f.up_s : f.gate_s;
@@ -452,15 +447,10 @@ __device__ __forceinline__ void issue_chunk(const GSrc<MTR, KCH>& g, int kc,
     // chunk: every chunk loads its own dword.
     const uint32_t so = (KCH == G && (kc & 1)) ? pg::OOB : g.s;
     const uint32_t sb = KCH == G ? (uint32_t)((kc & ~1) * 2) : (uint32_t)(kc * 4);
+    // waves 0-3 the scales, 4-7 the biases of columns (w % 4)*64 ..
     uint8_t* sbase = stage + pg::A_BYTES + pg::B_BYTES;
-    if constexpr (pg::WAVES == 4) {
-        load_lds<4>(g.rs, sbase + wave * 256, so, sb);
-        load_lds<4>(g.rb, sbase + pg::S_BYTES + wave * 256, so, sb);
-    } else {
-        // waves 0-3 the scales, 4-7 the biases of columns (w % 4)*64 ..
-        const bool bias = wave >= 4;
-        load_lds<4>(bias ? g.rb : g.rs, sbase + (bias ? pg::S_BYTES : 0) + (wave & 3) * 256, so, sb);
-    }
+    const bool bias = wave >= 4;
+    load_lds<4>(bias ? g.rb : g.rs, sbase + (bias ? pg::S_BYTES : 0) + (wave & 3) * 256, so, sb);
 }
 
 // MFMA: v_mfma_f32_32x32x16_f16 (32 rows x 32 columns x 16 k).  Lane l
@@ -469,17 +459,13 @@ __device__ __forceinline__ void issue_chunk(const GSrc<MTR, KCH>& g, int kc,
 // shape issues at well under half the matrix-core rate on this chip.)
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-// LDS column (0..255 of the item) of wave w's n-tile nt, lane column l%32.
-// Two n-tiles per wave (4 waves): gate/up n-tile 0 = gate rows w*32..,
-// n-tile 1 = the same up rows; down: 64 consecutive rows per wave.  One
-// n-tile per wave (8 waves): gate/up lanes l%32 < 16 take gate rows
-// w*16 + l%32, lanes l%32 >= 16 the same up rows (so each gate value and
-// its up value sit in lanes l and l ^ 16 of one wave); down: 32 rows.
-template <bool GATEUP, int NT>
-__device__ __forceinline__ int gemm_col(int wave, int nt, int l32) {
-    if constexpr (NT == 1)
-        return GATEUP ? (l32 >> 4) * 128 + wave * 16 + (l32 & 15) : wave * 32 + l32;
-    return GATEUP ? nt * 128 + wave * 32 + l32 : wave * 64 + nt * 32 + l32;
+// LDS column (0..255 of the item) of wave w's n-tile, lane column l%32:
+// gate/up lanes l%32 < 16 take gate rows w*16 + l%32, lanes l%32 >= 16 the
+// same up rows (so each gate value and its up value sit in lanes l and
+// l ^ 16 of one wave); down: 32 consecutive rows per wave.
+template <bool GATEUP>
+__device__ __forceinline__ int gemm_col(int wave, int l32) {
+    return GATEUP ? (l32 >> 4) * 128 + wave * 16 + (l32 & 15) : wave * 32 + l32;
 }
 
 // K order inside a chunk of STEPS k-steps: MFMA step s, lane half g = l/32
@@ -511,7 +497,7 @@ __device__ __forceinline__ BFrag<PG<MTR, KCH>::NT> read_b(const uint8_t* stage, 
     BFrag<pg::NT> B;
 #pragma unroll
     for (int nt = 0; nt < pg::NT; ++nt) {
-        const int C = gemm_col<GATEUP, pg::NT>(wave, nt, l32);
+        const int C = gemm_col<GATEUP>(wave, l32);
         const uint8_t* col = stage + pg::A_BYTES + C * pg::BCOL;
         if constexpr (KCH != G) {
             // two groups: pieces 2g and 2g+1, and half g of the stage's dwords
@@ -621,7 +607,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t item_rows(P* base, const GItem
                     (uint32_t)m.nrows * (uint32_t)row_elems * (uint32_t)sizeof(P));
 }
 
-// One n-tile per wave (8 waves, 512 B of staging each).  Accumulator
+// One n-tile per wave (512 B of staging each).  Accumulator
 // element i of lane l holds row 8*(i/4) + 4*(l/32) + i%4 of the m-tile.
 //   gate/up: lanes l%32 < 16 (gate) and l ^ 16 (up) exchange half of their
 //     elements, so that the first lane forms h for elements 0..7 (rows
@@ -631,7 +617,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t item_rows(P* base, const GItem
 //     [8][32] fp16 (times the row's weight), or [8][16] fp32 per half of
 //     the columns.
 template <int MODE, int NMT, int MTR>
-__device__ __forceinline__ void gemm_epilogue_w8(const GemmArgs& A, const GItem& m,
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                                                  float16v (&acc)[NMT][1], uint8_t* stg,
                                                  const float* coef) {
     using pg = PG<MTR, G>;
@@ -729,113 +715,6 @@ __device__ __forceinline__ void gemm_epilogue_w8(const GemmArgs& A, const GItem&
                     }
                     __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, 0);
                 }
-    }
-}
-
-// Two n-tiles per wave (4 waves, 1 KB of staging each).  Accumulator
-// element i of a lane lies in staged half hr = i/8 of the m-tile (rows
-// 16*hr .. 16*hr+15), at staged row 8*((i/4)&1) + 4g + i%4.
-template <int MODE, int NMT, int MTR>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
-                                              float16v (&acc)[NMT][2], uint8_t* stg,
-                                              const float* coef) {
-    using pg = PG<MTR, G>;              // (the fields used here do not depend on the chunk)
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int l32 = lane & 31, g = lane >> 5;
-    const int Rl = lane >> 2;           // staged row read back by this lane
-    if constexpr (MODE == GM_GATEUP) {
-        const __amdgpu_buffer_rsrc_t rh = item_rows(A.hout, m, I);
-        uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [16][32] fp16, slot order
-#pragma unroll
-        for (int mt = 0; mt < pg::NMT_MAX; ++mt)
-#pragma unroll
-            for (int hr = 0; hr < 2; ++hr) {
-                uint4v v = (uint4v){0u, 0u, 0u, 0u};
-                uint32_t off = pg::OOB;
-                if (mt < NMT) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const int i = hr * 8 + q;
-                        const float gv = acc[mt < NMT ? mt : 0][0][i];
-                        const float uv = acc[mt < NMT ? mt : 0][1][i];
-                        const float hv = __fdividef(gv, 1.f + __expf(-gv)) * uv;
-                        const _Float16 hh = (_Float16)bf16_to_f32(f32_to_bf16(hv));
-                        const int row = 8 * (q >> 2) + 4 * g + (q & 3);
-                        st[row * 32 + (l32 & ~7) + chunk_slot(l32 & 7)] = __builtin_bit_cast(uint16_t, hh);
-                    }
-                    lane_exchange_fence();
-                    v = reinterpret_cast<const uint4v*>(stg)[lane];
-                    lane_exchange_fence();
-                    const int R = mt * 32 + hr * 16 + Rl;
-                    if (R < m.nrows)
-                        off = (uint32_t)((R * I + m.nb * 128 + wave * 32 + (lane & 3) * 8) * 2);
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(v, rh, off, 0, 0);
-            }
-    } else if constexpr (MODE == GM_DOWN_F16W) {
-        const __amdgpu_buffer_rsrc_t rd = item_rows(A.dout16, m, H);
-        uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [16][32] fp16
-#pragma unroll
-        for (int mt = 0; mt < pg::NMT_MAX; ++mt)
-#pragma unroll
-            for (int hr = 0; hr < 2; ++hr) {
-                float4v cf[2] = {(float4v){0.f, 0.f, 0.f, 0.f}, (float4v){0.f, 0.f, 0.f, 0.f}};
-                if (mt < NMT) {
-                    cf[0] = *reinterpret_cast<const float4v*>(coef + mt * 32 + hr * 16 + 4 * g);
-                    cf[1] = *reinterpret_cast<const float4v*>(coef + mt * 32 + hr * 16 + 8 + 4 * g);
-                }
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    uint4v v = (uint4v){0u, 0u, 0u, 0u};
-                    uint32_t off = pg::OOB;
-                    if (mt < NMT) {
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const float d = acc[mt < NMT ? mt : 0][nt][hr * 8 + q] * cf[q >> 2][q & 3];
-                            const int row = 8 * (q >> 2) + 4 * g + (q & 3);
-                            st[row * 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)d);
-                        }
-                        lane_exchange_fence();
-                    v = reinterpret_cast<const uint4v*>(stg)[lane];
-                    lane_exchange_fence();
-                        const int R = mt * 32 + hr * 16 + Rl;
-                        if (R < m.nrows)
-                            off = (uint32_t)((R * H + m.nb * 256 + wave * 64 + nt * 32 + (lane & 3) * 8) * 2);
-                    }
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
-                }
-            }
-    } else {
-        const __amdgpu_buffer_rsrc_t rd = item_rows(A.dout32, m, H);
-        float* st = reinterpret_cast<float*>(stg);          // [16][16] fp32
-#pragma unroll
-        for (int mt = 0; mt < pg::NMT_MAX; ++mt)
-#pragma unroll
-            for (int hr = 0; hr < 2; ++hr)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int ch = 0; ch < 2; ++ch) {
-                        uint4v v = (uint4v){0u, 0u, 0u, 0u};
-                        uint32_t off = pg::OOB;
-                        if (mt < NMT) {
-                            if ((l32 >> 4) == ch) {
-#pragma unroll
-                                for (int q = 0; q < 8; ++q) {
-                                    const int row = 8 * (q >> 2) + 4 * g + (q & 3);
-                                    st[row * 16 + (l32 & 15)] = acc[mt < NMT ? mt : 0][nt][hr * 8 + q];
-                                }
-                            }
-                            lane_exchange_fence();
-                    v = reinterpret_cast<const uint4v*>(stg)[lane];
-                    lane_exchange_fence();
-                            const int R = mt * 32 + hr * 16 + Rl;
-                            if (R < m.nrows)
-                                off = (uint32_t)((R * H + m.nb * 256 + wave * 64 + nt * 32 + ch * 16 +
-                                                  (lane & 3) * 4) * 4);
-                        }
-                        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
-                    }
     }
 }
 
@@ -1019,10 +898,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 #pragma unroll
     for (int c = (MAIN > HEAD ? MAIN : HEAD); c < NCH; ++c) chunk(c, next(c));
     __builtin_amdgcn_sched_barrier(0);          // epilogue stores after the last refill
-    if constexpr (NT == 1)
-        gemm_epilogue_w8<MODE, NMT, MTR>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
-    else
-        gemm_epilogue<MODE, NMT, MTR>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
+    gemm_epilogue<MODE, NMT, MTR>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -1059,7 +935,7 @@ void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
     }
-    const WPtr pr = wave_ptrs<MODE, pg::WAVES>(routed), ps = wave_ptrs<MODE, pg::WAVES>(shared);
+    const WPtr pr = wave_ptrs<MODE>(routed), ps = wave_ptrs<MODE>(shared);
     GSrc<MTR, KCH> src_cur =
         gemm_src<KDIM, MODE, MTR, KCH>(cur, reinterpret_cast<const int32_t*>(meta), args.T, pr, ps);
     GSrc<MTR, KCH> src_nxt = src_cur;
