@@ -249,15 +249,13 @@ struct PG {
 };
 constexpr int MT_LARGE = MT_ROWS, MT_SMALL = 32;
 // The chunk width of an instantiation: two groups (128 k, 2-stage ring)
-// everywhere except the 160-row down GEMM, whose 128-k instances would
-// spill.  Same-run timings: 160-row gate/up 212.5 against 227.1 us at 4096
-// tokens with one group and 5 stages (half the barriers and half the code
-// line requests); 32-row down 45.3 against 52.6 us in the 512-token chain.
-#ifndef MOE_LARGE_KC
-#define MOE_LARGE_KC 128
-#endif
-template <int KDIM, int MTR>
-constexpr int gemm_kc() { return MTR == MT_SMALL ? 2 * G : KDIM == H ? MOE_LARGE_KC : G; }
+// everywhere except the split interface's 160-row down GEMM (fp32 rows),
+// whose 128-k instance would spill.  Same-run timings: 160-row gate/up
+// 212.5 against 227.1 us at 4096 tokens with one group and 5 stages (half
+// the barriers and half the code line requests); 32-row down 45.3 against
+// 52.6 us in the 512-token chain.
+template <int KDIM, int MODE, int MTR>
+constexpr int gemm_kc() { return (MTR == MT_LARGE && MODE == GM_DOWN_F32) ? G : 2 * G; }
 static_assert(PG<MT_SMALL, 2 * G>::WG_PER_CU == 2 && PG<MT_LARGE, G>::WG_PER_CU == 1 &&
               PG<MT_LARGE, 2 * G>::WG_PER_CU == 1, "tile LDS footprints");
 
@@ -331,11 +329,19 @@ __device__ __forceinline__ P* uniform_ptr(P* p) {
 // wave-uniform offset (the soffset operand of the loads), so issuing a chunk
 // costs no vector arithmetic.  Rows past the tile and items past the last
 // get out-of-range offsets (the loads access no memory and fill zeros).
+//
+// Instruction i of wave w moves A rows (8i + w)*A_RPL + .. (consecutive
+// instructions of a wave are 8*A_RPL rows apart, a multiple of the swizzle
+// period, so a lane reads the same piece of each row) and B columns
+// (w*B_LOADS + i)*B_CPL + .. .  Where the rows are contiguous (down: h
+// rows; B: weight rows) only instruction 0's offset is kept per lane and the
+// others add a wave-uniform step in the scalar offset: fewer registers.
+// Gate/up gathers its A rows by token, so each instruction has its own.
 template <int MTR, int KCH>
 struct GSrc {
     __amdgpu_buffer_rsrc_t rq, rs, rb;   // this wave's code / scale / bias matrix
-    uint32_t a[PG<MTR, KCH>::A_LOADS];   // A: instruction i -> rows (w*A_LOADS + i)*A_RPL + ..
-    uint32_t b[PG<MTR, KCH>::B_LOADS];   // B: instruction i -> columns (w*B_LOADS + i)*B_CPL + ..
+    uint32_t a[PG<MTR, KCH>::A_LOADS];   // A offsets (only a[0] without the gather)
+    uint32_t b;                          // B offset of instruction 0
     uint32_t s;                          // scale/bias dword of column (w % 4)*64 + lane
 };
 
@@ -384,11 +390,13 @@ __device__ __forceinline__ GSrc<MTR, KCH> gemm_src(const GItem& m, const int32_t
     // A: LDS slot (lane % A_PIECES) of row R holds the row's piece
     // slot ^ a_swz(R)
 #pragma unroll
-    for (int i = 0; i < pg::A_LOADS; ++i) {
-        const int R = (wave * pg::A_LOADS + i) * pg::A_RPL + lane / pg::A_PIECES;
+    for (int i = 0; i < (GATEUP ? pg::A_LOADS : 1); ++i) {
+        const int R = (i * pg::WAVES + wave) * pg::A_RPL + lane / pg::A_PIECES;
         const int p = (lane % pg::A_PIECES) ^ a_swz<KCH>(R);
         int src = m.row0 + R;
         if (GATEUP) src = m.shared ? m.row0 + R - TOPK * T : min(max(tok[R] >> 3, 0), T - 1);
+        // (without the gather the later instructions' rows past the tile read
+        // other rows or, past the buffer, zeros: never stored)
         g.a[i] = R < m.nrows ? (uint32_t)src * (uint32_t)(KDIM * 2) + 16u * (uint32_t)p : pg::OOB;
     }
     const uint32_t* code = m.shared ? ps.q : pr.q;
@@ -401,11 +409,12 @@ __device__ __forceinline__ GSrc<MTR, KCH> gemm_src(const GItem& m, const int32_t
     auto wrow = [&](int C) { return GATEUP ? m.nb * 128 + (C & 127) : m.nb * 256 + C; };
     // B: LDS slot (lane % B_PIECES) of column C holds the column's piece
     // slot ^ b_swz(C)
-#pragma unroll
-    for (int i = 0; i < pg::B_LOADS; ++i) {
-        const int C = (wave * pg::B_LOADS + i) * pg::B_CPL + lane / pg::B_PIECES;
+    {
+        // (a wave's B_LOADS * B_CPL columns stay inside one half, gate or up,
+        // and B_CPL is a multiple of the swizzle period)
+        const int C = wave * pg::B_LOADS * pg::B_CPL + lane / pg::B_PIECES;
         const int p = (lane % pg::B_PIECES) ^ b_swz<KCH>(C);
-        g.b[i] = m.valid ? (uint32_t)(wrow(C) * WPR * 4 + 16 * p) : pg::OOB;
+        g.b = m.valid ? (uint32_t)(wrow(C) * WPR * 4 + 16 * p) : pg::OOB;
     }
     g.s = m.valid ? (uint32_t)(wrow((wave & 3) * 64 + lane) * SPR * 2) : pg::OOB;
     return g;
@@ -421,25 +430,28 @@ __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst,
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, voff, soff, 0, 0);
 }
 
-// The LPC loads of chunk kc of an item into one stage.
-template <int MTR, int KCH>
+// The LPC loads of chunk kc of an item into one stage (KDIM: the row
+// length of the A and code matrices; GATHER: per-instruction A offsets).
+template <int KDIM, bool GATHER, int MTR, int KCH>
 __device__ __forceinline__ void issue_chunk(const GSrc<MTR, KCH>& g, int kc,
                                             __amdgpu_buffer_rsrc_t ra, uint8_t* stage,
                                             uint8_t* lds) {
     using pg = PG<MTR, KCH>;
+    constexpr uint32_t A_STEP = GATHER ? 0 : pg::WAVES * pg::A_RPL * KDIM * 2;
+    constexpr uint32_t B_STEP = pg::B_CPL * (KDIM / 2);
     const int wave = wave_id();
 #pragma unroll
     for (int i = 0; i < pg::A_LOADS; ++i) {
         // (stand-ins past the tile's last 1 KB land in the dummy area after the ring)
-        const int idx = wave * pg::A_LOADS + i;
+        const int idx = i * pg::WAVES + wave;
         uint8_t* dst = stage + idx * 1024;
         if (pg::DUMMY && idx >= pg::A_REAL) dst = lds + pg::RING;
-        load_lds<16>(ra, dst, g.a[i], kc * pg::AROW);
+        load_lds<16>(ra, dst, GATHER ? g.a[i] : g.a[0], kc * pg::AROW + i * A_STEP);
     }
 #pragma unroll
     for (int i = 0; i < pg::B_LOADS; ++i)
-        load_lds<16>(g.rq, stage + pg::A_BYTES + (wave * pg::B_LOADS + i) * 1024, g.b[i],
-                     kc * pg::BCOL);
+        load_lds<16>(g.rq, stage + pg::A_BYTES + (wave * pg::B_LOADS + i) * 1024, g.b,
+                     kc * pg::BCOL + i * B_STEP);
     // one scale and one bias dword covers two groups.  One group per chunk:
     // the dword of chunks kc & ~1 and kc | 1, loaded by the even chunk; the
     // odd chunk's loads are out-of-range stand-ins (no memory access), and
@@ -851,9 +863,11 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
         }
         ++gc;
     };
-    auto own = [&](int c) { return [&, c](uint8_t* st) { issue_chunk(src_cur, c + pg::STAGES, ra, st, lds); }; };
+    auto own = [&](int c) {
+        return [&, c](uint8_t* st) { issue_chunk<KDIM, GATEUP>(src_cur, c + pg::STAGES, ra, st, lds); };
+    };
     auto next = [&](int c) {
-        return [&, c](uint8_t* st) { issue_chunk(src_nxt, c + pg::STAGES - NCH, ra, st, lds); };
+        return [&, c](uint8_t* st) { issue_chunk<KDIM, GATEUP>(src_nxt, c + pg::STAGES - NCH, ra, st, lds); };
     };
     // the next item's sources (its row tokens arrived with this item's first chunk)
     auto make_next = [&]() {
@@ -866,7 +880,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     static_assert(MAIN >= 1, "an item needs more chunks than pipeline stages");
     // head: unrolled, so every wait count and refill target is a constant
     chunk(0, [&](uint8_t* st) {
-        issue_chunk(src_cur, pg::STAGES, ra, st, lds);
+        issue_chunk<KDIM, GATEUP>(src_cur, pg::STAGES, ra, st, lds);
         __builtin_amdgcn_sched_barrier(0);      // the metadata load goes after the chunk's loads
         // the item after this one, claimed during the previous item (its
         // index was written to LDS before this chunk's barrier)
@@ -909,11 +923,11 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 // two items of each workgroup are static and the rest are claimed from the
 // XCD's counter in order -- longest first.
 template <int KDIM, int MODE, int MTR>
-__global__ __launch_bounds__((PG<MTR, gemm_kc<KDIM, MTR>()>::THREADS))
-__attribute__((amdgpu_waves_per_eu(PG<MTR, gemm_kc<KDIM, MTR>()>::WAVES_PER_SIMD)))
+__global__ __launch_bounds__((PG<MTR, gemm_kc<KDIM, MODE, MTR>()>::THREADS))
+__attribute__((amdgpu_waves_per_eu(PG<MTR, gemm_kc<KDIM, MODE, MTR>()>::WAVES_PER_SIMD)))
 void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict__ tile_count,
                   QFFN routed, QFFN shared) {
-    constexpr int KCH = gemm_kc<KDIM, MTR>();
+    constexpr int KCH = gemm_kc<KDIM, MODE, MTR>();
     using pg = PG<MTR, KCH>;
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
@@ -939,7 +953,7 @@ void grouped_gemm(GemmArgs args, const Tile* __restrict__ tiles, int* __restrict
     GSrc<MTR, KCH> src_cur =
         gemm_src<KDIM, MODE, MTR, KCH>(cur, reinterpret_cast<const int32_t*>(meta), args.T, pr, ps);
     GSrc<MTR, KCH> src_nxt = src_cur;
-    for (int c = 0; c < pg::STAGES; ++c) issue_chunk(src_cur, c, ra, lds + c * pg::STAGE, lds);
+    for (int c = 0; c < pg::STAGES; ++c) issue_chunk<KDIM, GATEUP>(src_cur, c, ra, lds + c * pg::STAGE, lds);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((pg::STAGES - 1) * pg::LPC));   // chunk 0 landed
     pipe_barrier();
 
@@ -1026,13 +1040,13 @@ static void launch_gemm(const GemmArgs& a, const Tile* tiles, int* tile_count, c
                         const QFFN& shared, int mt_rows, hipStream_t st) {
     if (mt_rows == MT_SMALL)
         hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_SMALL>),
-                           dim3(256 * PG<MT_SMALL, gemm_kc<KDIM, MT_SMALL>()>::WG_PER_CU),
-                           dim3(PG<MT_SMALL, gemm_kc<KDIM, MT_SMALL>()>::THREADS), 0, st, a, tiles,
+                           dim3(256 * PG<MT_SMALL, gemm_kc<KDIM, MODE, MT_SMALL>()>::WG_PER_CU),
+                           dim3(PG<MT_SMALL, gemm_kc<KDIM, MODE, MT_SMALL>()>::THREADS), 0, st, a, tiles,
                            tile_count, routed, shared);
     else
         hipLaunchKernelGGL((grouped_gemm<KDIM, MODE, MT_LARGE>),
-                           dim3(256 * PG<MT_LARGE, gemm_kc<KDIM, MT_LARGE>()>::WG_PER_CU),
-                           dim3(PG<MT_LARGE, gemm_kc<KDIM, MT_LARGE>()>::THREADS), 0, st, a, tiles,
+                           dim3(256 * PG<MT_LARGE, gemm_kc<KDIM, MODE, MT_LARGE>()>::WG_PER_CU),
+                           dim3(PG<MT_LARGE, gemm_kc<KDIM, MODE, MT_LARGE>()>::THREADS), 0, st, a, tiles,
                            tile_count, routed, shared);
 }
 
