@@ -11,8 +11,8 @@
 //   perm_count      larger T: per-chunk expert histograms      (grid: chunks)
 //   perm_scan_scatter  up to SCAN_CHUNKS chunks: every workgroup derives its
 //                   chunk's bases from all the histograms, then scatters it;
-//                   workgroup 0 also writes the counts and offsets and plans
-//                   the row tiles                              (grid: chunks)
+//                   one more workgroup writes the counts and offsets and
+//                   plans the row tiles meanwhile            (grid: chunks + 1)
 //   perm_scan       more chunks: column scans -> per-chunk bases (one workgroup)
 //   perm_scatter    more chunks: stable scatter of every chunk   (grid: chunks)
 //   plan_tiles      row tiles of <= mt_rows rows per expert (expert 256 is the
@@ -210,6 +210,8 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ 
 // give the chunk's base inside the expert's segment, the total its segment
 // length; a block scan of the totals gives the segment starts.  The scan
 // is repeated by every workgroup instead of run once between two launches.
+// Workgroup `nchunks` (the last) scatters nothing: it writes counts and
+// offsets and plans the row tiles while the others scatter.
 __global__ __launch_bounds__(256) void perm_scan_scatter(const int32_t* __restrict__ ids, int n,
                                                          int nchunks,
                                                          const int32_t* __restrict__ chunk_counts,
@@ -240,14 +242,15 @@ __global__ __launch_bounds__(256) void perm_scan_scatter(const int32_t* __restri
 #pragma unroll
     for (int w = 0; w < 4; ++w) wcnt[w * 256 + tid] = 0;
     __syncthreads();
-    const int f0 = b * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
-    stable_scatter(ids, f0, f1, base, wcnt, perm, inv, wsrc, wsorted);
-    if (b == 0) {
+    if (b == nchunks) {
         counts[tid] = tot;
         offsets[tid] = off;
         if (tid == 0) offsets[E] = total;
         if (tiles) plan_block(off, off + tot, T, max_tiles(T), mt_rows, tiles, tile_count, scr);
+        return;
     }
+    const int f0 = b * PERM_CHUNK, f1 = min(n, f0 + PERM_CHUNK);
+    stable_scatter(ids, f0, f1, base, wcnt, perm, inv, wsrc, wsorted);
 }
 
 int perm_chunks(int T) { return (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK; }
@@ -273,7 +276,7 @@ void launch_permute(const int32_t* ids, int T, int32_t* counts, int32_t* offsets
     const int nb = perm_chunks(T);
     if (!counted) hipLaunchKernelGGL(perm_count, dim3(nb), dim3(256), 0, st, ids, n, chunk_counts);
     if (nb <= SCAN_CHUNKS) {
-        hipLaunchKernelGGL(perm_scan_scatter, dim3(nb), dim3(256), 0, st, ids, n, nb, chunk_counts,
+        hipLaunchKernelGGL(perm_scan_scatter, dim3(nb + 1), dim3(256), 0, st, ids, n, nb, chunk_counts,
                            counts, offsets, perm, inv, wts, wsorted, T, mt, tiles, tile_count);
         return;
     }
