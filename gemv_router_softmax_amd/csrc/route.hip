@@ -61,48 +61,62 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rt_rsrc(const void* p, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
-// Router logits for T > 32.  grid: (ceil(T/32), 2) workgroups of 4 waves;
-// workgroup (b, h) computes tokens 32b .. 32b+31 against experts
-// 128h .. 128h+127, wave w the 32 experts 128h + 32w .. +31, as a 32x32 fp32
-// accumulator of v_mfma_f32_32x32x16_bf16 (lane l: token / expert l%32,
-// k = 8*(l/32)..+7 of each 16-wide step).  K advances in supersteps of 64;
-// the x tile (32 rows) and the W_r tile (128 rows) of a superstep move into
-// LDS with coalesced direct loads (1 KB = 8 rows x 128 B per instruction,
-// five per wave) through a 7-stage ring, so six supersteps are in flight
-// while one is multiplied -- the kernel is bound by load latency, not by
-// the MFMAs.  Rows are stored with their 16-byte pieces XOR-swizzled by
-// (row >> 1) & 7, so a 16-lane operand read hits 16 distinct bank groups;
-// MFMA step s reads piece 4g + s (g = l/32) of both operands.  Token rows
-// past T load zeros (buffer range) and are not stored.
-constexpr int RL_TOK = 32;
+// Router logits for T > 32.  grid: (ceil(T/TOK), 2) workgroups of 4 waves;
+// workgroup (b, h) computes tokens TOK b .. TOK b + TOK-1 against experts
+// 128h .. 128h+127, wave w the 32 experts 128h + 32w .. +31, as TOK/32
+// 32x32 fp32 accumulators of v_mfma_f32_32x32x16_bf16 (lane l: token /
+// expert l%32, k = 8*(l/32)..+7 of each 16-wide step).  K advances in
+// supersteps of 64; the x tile (TOK rows) and the W_r tile (128 rows) of a
+// superstep move into LDS with coalesced direct loads (1 KB = 8 rows x
+// 128 B per instruction) through a ring of 7 stages (6 for 64-token
+// tiles), so that many supersteps are in flight while one is multiplied.
+// The kernel is bound by that load ring, not by the MFMAs; 64-token tiles
+// read the router matrix once per 64 tokens instead of per 32.  Rows are
+// stored with their 16-byte pieces XOR-swizzled by (row >> 1) & 7, so a
+// 16-lane operand read hits 16 distinct bank groups; MFMA step s reads
+// piece 4g + s (g = l/32) of both operands.  Token rows past T load zeros
+// (buffer range) and are not stored.
 constexpr int RL_EXP = 128;
-constexpr int RL_STAGES = 7;
-constexpr int RL_STAGE = (RL_TOK + RL_EXP) * 128;     // bytes per superstep
-constexpr int RL_INSTR = RL_STAGE / 1024;             // 1 KB direct loads per superstep (20)
-constexpr int RL_PER_WAVE = RL_INSTR / 4;             // 5
-static_assert(RL_INSTR % 4 == 0, "router loads split evenly over the waves");
-static_assert(RL_STAGES * RL_STAGE <= 160 * 1024, "router LDS");
-static_assert((RL_STAGES - 2) * RL_PER_WAVE <= 63, "vmcnt range");
+template <int TOK>
+struct RLG {
+    static constexpr int STAGES = TOK == 64 ? 6 : 7;
+    static constexpr int STAGE = (TOK + RL_EXP) * 128;   // bytes per superstep
+    static constexpr int INSTR = STAGE / 1024;           // 1 KB direct loads per superstep
+    static constexpr int PER_WAVE = INSTR / 4;
+    static constexpr int MT = TOK / 32;                  // 32-token MFMA tiles
+    static_assert(TOK == 32 || TOK == 64, "token tile");
+    static_assert(INSTR % 4 == 0, "router loads split evenly over the waves");
+    static_assert(STAGES * STAGE <= 160 * 1024, "router LDS");
+    static_assert((STAGES - 2) * PER_WAVE <= 63, "vmcnt range");
+};
+// Token tile of the router GEMM at T tokens (the 64-token tile halves the
+// router-matrix traffic; below a few thousand tokens the 32-token tile
+// keeps twice the workgroups).
+#ifndef RL_TOK64_MIN_T
+#define RL_TOK64_MIN_T 2048
+#endif
+static int route_tok(int T) { return T >= RL_TOK64_MIN_T ? 64 : 32; }
 
 typedef __attribute__((address_space(3))) void* rt_lds_t;
 
-// Instruction j = wave + 4i fills stage rows 8j .. 8j+7 (rows 0..31: x
-// tokens, 32..159: W_r experts): lane -> row 8j + lane/8, LDS slot lane%8
+// Instruction j = wave + 4i fills stage rows 8j .. 8j+7 (rows 0..TOK-1: x
+// tokens, then 128 W_r experts): lane -> row 8j + lane/8, LDS slot lane%8
 // holding the row's piece slot ^ ((row >> 1) & 7).
+template <int TOK>
 __device__ __forceinline__ void rl_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
                                          int t0, int e0, int wave, int lane, int u,
                                          uint8_t* stage) {
 #pragma unroll
-    for (int i = 0; i < RL_PER_WAVE; ++i) {
+    for (int i = 0; i < RLG<TOK>::PER_WAVE; ++i) {
         const int j = wave + 4 * i;
         const int row = 8 * j + (lane >> 3);
         const int p = (lane & 7) ^ ((row >> 1) & 7);
         uint8_t* dst = stage + j * 1024;
-        if (j < RL_TOK / 8) {
+        if (j < TOK / 8) {
             const uint32_t off = (uint32_t)(t0 + row) * (H * 2) + (uint32_t)(u * 128 + 16 * p);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (rt_lds_t)dst, 16, off, 0, 0, 0);
         } else {
-            const uint32_t off = (uint32_t)(e0 + row - RL_TOK) * (H * 2) + (uint32_t)(u * 128 + 16 * p);
+            const uint32_t off = (uint32_t)(e0 + row - TOK) * (H * 2) + (uint32_t)(u * 128 + 16 * p);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (rt_lds_t)dst, 16, off, 0, 0, 0);
         }
     }
@@ -111,19 +125,20 @@ __device__ __forceinline__ void rl_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buf
 // KS > 1 splits K over blockIdx.z: slice z covers supersteps z*NU/KS ..
 // (z+1)*NU/KS - 1 and writes its unbiased partial logits to
 // logits[(z*T + t)*E + e]; route_topk sums the slices in order and adds the
-// bias.  A few hundred tokens make only T/32 x 2 workgroups, so the split is
-// what fills the chip there.
+// bias.  A few hundred tokens make only T/TOK x 2 workgroups, so the split
+// is what fills the chip there.
 //
 // zero / nzero: optional int array the workgroups clear on the way (the
 // permutation's chunk histograms, which the top-8 kernel after this one
 // accumulates).
-template <int KS>
+template <int KS, int TOK>
 __global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restrict__ x, int T,
                                                          const uint16_t* __restrict__ wr,
                                                          const float* __restrict__ bias,
                                                          float* __restrict__ logits,
                                                          int32_t* __restrict__ zero, int nzero) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[RL_STAGES * RL_STAGE];
+    using rg = RLG<TOK>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[rg::STAGES * rg::STAGE];
     if (zero) {
         const int nwg = gridDim.x * gridDim.y * gridDim.z;
         const int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
@@ -132,72 +147,86 @@ __global__ __launch_bounds__(256) void route_logits_tile(const uint16_t* __restr
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
-    const int t0 = blockIdx.x * RL_TOK;
+    const int t0 = blockIdx.x * TOK;
     const int e0 = blockIdx.y * RL_EXP;
     const __amdgpu_buffer_rsrc_t rx = rt_rsrc(x, (uint32_t)((size_t)T * H * 2));
     const __amdgpu_buffer_rsrc_t rw = rt_rsrc(wr, (uint32_t)(E * H * 2));
     constexpr int NU = H / 64 / KS;   // supersteps of this K slice (32 in all)
     static_assert((H / 64) % KS == 0, "K slices");
+    constexpr int S = rg::STAGES, PW = rg::PER_WAVE;
     const int u0 = blockIdx.z * NU;
 
-    static_assert(RL_TOK % 8 == 0, "x rows must fill whole load instructions");
+    static_assert(TOK % 8 == 0, "x rows must fill whole load instructions");
 #pragma unroll
-    for (int u = 0; u < RL_STAGES - 1; ++u)
-        if (u < NU) rl_issue(rx, rw, t0, e0, wave, lane, u0 + u, smem + u * RL_STAGE);
+    for (int u = 0; u < S - 1; ++u)
+        if (u < NU) rl_issue<TOK>(rx, rw, t0, e0, wave, lane, u0 + u, smem + u * rg::STAGE);
 
-    float16v acc = (float16v)0.f;
-    const int ra = l32, rb = RL_TOK + wave * 32 + l32;     // operand rows in the stage
+    float16v acc[rg::MT];
+#pragma unroll
+    for (int m = 0; m < rg::MT; ++m) acc[m] = (float16v)0.f;
+    const int rb = TOK + wave * 32 + l32;     // expert operand row in the stage
     for (int u = 0; u < NU; ++u) {
         // superstep u landed (the later ones may stay in flight): each wave
-        // has min(NU - 1 - u, STAGES - 2) more supersteps of loads issued
-        const int ahead = min(NU - 1 - u, RL_STAGES - 2);
+        // has min(NU - 1 - u, S - 2) more supersteps of loads issued
+        const int ahead = min(NU - 1 - u, S - 2);
         switch (ahead) {
-            case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * RL_PER_WAVE)); break;
-            case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * RL_PER_WAVE)); break;
-            case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * RL_PER_WAVE)); break;
-            case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * RL_PER_WAVE)); break;
-            case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * RL_PER_WAVE)); break;
+            case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * PW)); break;
+            case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PW)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PW)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PW)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * PW)); break;
             default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
         }
+        static_assert(S - 2 <= 5, "wait cases");
         // every wave's part of superstep u is in LDS, and every wave is done
         // with the stage the refill below overwrites (superstep u - 1)
         pipe_barrier();
-        if (u + RL_STAGES - 1 < NU)
-            rl_issue(rx, rw, t0, e0, wave, lane, u0 + u + RL_STAGES - 1,
-                     smem + ((u + RL_STAGES - 1) % RL_STAGES) * RL_STAGE);
-        const uint8_t* st = smem + (u % RL_STAGES) * RL_STAGE;
-        // all eight operand reads first, then the four MFMAs
-        uint4v av[4], bv[4];
+        if (u + S - 1 < NU)
+            rl_issue<TOK>(rx, rw, t0, e0, wave, lane, u0 + u + S - 1,
+                          smem + ((u + S - 1) % S) * rg::STAGE);
+        const uint8_t* st = smem + (u % S) * rg::STAGE;
+        // all operand reads first, then the MFMAs
+        uint4v av[rg::MT][4], bv[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int pc = 4 * g + s;
-            av[s] = *reinterpret_cast<const uint4v*>(st + ra * 128 + 16 * (pc ^ ((ra >> 1) & 7)));
+#pragma unroll
+            for (int m = 0; m < rg::MT; ++m) {
+                const int ra = m * 32 + l32;
+                av[m][s] = *reinterpret_cast<const uint4v*>(st + ra * 128 + 16 * (pc ^ ((ra >> 1) & 7)));
+            }
             bv[s] = *reinterpret_cast<const uint4v*>(st + rb * 128 + 16 * (pc ^ ((rb >> 1) & 7)));
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[s]),
-                                                          __builtin_bit_cast(bf16x8, bv[s]), acc, 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // MFMAs
+#pragma unroll
+            for (int m = 0; m < rg::MT; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[m][s]),
+                                                                 __builtin_bit_cast(bf16x8, bv[s]), acc[m],
+                                                                 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (rg::MT + 1), 0);    // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * rg::MT, 0);          // MFMAs
     }
-    // element i: token 8*(i/4) + 4g + i%4, expert e0 + 32w + l32
+    // element i of tile m: token 32m + 8*(i/4) + 4g + i%4, expert e0 + 32w + l32
     const int e = e0 + wave * 32 + l32;
     const float bb = (KS == 1 && bias) ? bias[e] : 0.f;
     float* out = logits + (size_t)blockIdx.z * T * E;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = t0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        const float v = acc[i];
-        if (t < T) out[(size_t)t * E + e] = v + bb;
-    }
+    for (int m = 0; m < rg::MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = t0 + 32 * m + 8 * (i >> 2) + 4 * g + (i & 3);
+            const float v = acc[m][i];
+            if (t < T) out[(size_t)t * E + e] = v + bb;
+        }
 }
 
 // K slices of the router GEMM at T tokens: doubled while the grid stays
 // within 256 workgroups, at most RL_KS_MAX.
 constexpr int RL_KS_MAX = 8;
 static int route_ksplit(int T) {
-    const int tiles = (T + RL_TOK - 1) / RL_TOK * (E / RL_EXP);
+    const int tok = route_tok(T);
+    const int tiles = (T + tok - 1) / tok * (E / RL_EXP);
     int ks = 1;
     while (ks < RL_KS_MAX && tiles * ks * 2 <= 256) ks *= 2;
     return ks;
@@ -267,7 +296,8 @@ void launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const flo
         hipLaunchKernelGGL(route_logits_gemv, dim3(E / 4), dim3(256), 0, st, x, T, wr, bias,
                            logits);
     } else {
-        hipLaunchKernelGGL(route_logits_tile<1>, dim3((T + RL_TOK - 1) / RL_TOK, E / RL_EXP),
+        // (unsplit: the 32-token tile keeps more workgroups)
+        hipLaunchKernelGGL((route_logits_tile<1, 32>), dim3((T + 31) / 32, E / RL_EXP),
                            dim3(256), 0, st, x, T, wr, bias, logits, zero, nzero);
     }
 }
@@ -288,19 +318,35 @@ void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bia
     if (!route_counts_chunks(T)) chunk_counts = nullptr;
     const int nzero = chunk_counts ? (TOPK * T + PERM_CHUNK - 1) / PERM_CHUNK * E : 0;
     const int ks = (part && T > 32) ? route_ksplit(T) : 1;
+    const int tok = route_tok(T);
     if (ks == 1) {
-        launch_route_logits(x, T, wr, bias, logits, st, chunk_counts, nzero);
+        if (T > 32 && tok == 64)
+            hipLaunchKernelGGL((route_logits_tile<1, 64>), dim3((T + 63) / 64, E / RL_EXP), dim3(256), 0,
+                               st, x, T, wr, bias, logits, chunk_counts, nzero);
+        else
+            launch_route_logits(x, T, wr, bias, logits, st, chunk_counts, nzero);
         hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits,
                            (const float*)nullptr, 0, (const float*)nullptr, x, wsg, T, ids, wts,
                            sg, xh, chunk_counts);
         return;
     }
-    const dim3 grid((T + RL_TOK - 1) / RL_TOK, E / RL_EXP, ks);
-    switch (ks) {
-        case 2: hipLaunchKernelGGL(route_logits_tile<2>, grid, dim3(256), 0, st, x, T, wr, bias, part, chunk_counts, nzero); break;
-        case 4: hipLaunchKernelGGL(route_logits_tile<4>, grid, dim3(256), 0, st, x, T, wr, bias, part, chunk_counts, nzero); break;
-        default: hipLaunchKernelGGL(route_logits_tile<8>, grid, dim3(256), 0, st, x, T, wr, bias, part, chunk_counts, nzero); break;
+    const dim3 grid((T + tok - 1) / tok, E / RL_EXP, ks);
+#define RL_LAUNCH(K, TK) \
+    hipLaunchKernelGGL((route_logits_tile<K, TK>), grid, dim3(256), 0, st, x, T, wr, bias, part, chunk_counts, nzero)
+    if (tok == 64) {
+        switch (ks) {
+            case 2: RL_LAUNCH(2, 64); break;
+            case 4: RL_LAUNCH(4, 64); break;
+            default: RL_LAUNCH(8, 64); break;
+        }
+    } else {
+        switch (ks) {
+            case 2: RL_LAUNCH(2, 32); break;
+            case 4: RL_LAUNCH(4, 32); break;
+            default: RL_LAUNCH(8, 32); break;
+        }
     }
+#undef RL_LAUNCH
     hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, (const float*)part,
                        ks, bias, x, wsg, T, ids, wts, sg, xh, chunk_counts);
 }
