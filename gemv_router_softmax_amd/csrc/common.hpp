@@ -84,12 +84,11 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __builtin_bit_cast(float, bits16 << 16);
 }
 
-// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+// float -> bf16 bits, round to nearest even (one v_cvt_pk_bf16_f32 on this
+// chip; it agrees bit for bit with the integer rounding sequence on ties,
+// subnormals and large values); NaN stays NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float fp16_to_f32(uint16_t bits) {

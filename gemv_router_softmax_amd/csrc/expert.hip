@@ -648,7 +648,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                 for (int q = 0; q < 8; ++q) {
                     const float a0 = acc[mt < NMT ? mt : 0][0][q], a1 = acc[mt < NMT ? mt : 0][0][8 + q];
                     const float mine = lo ? a0 : a1;            // gate (elem q) / up (elem 8+q)
-                    const float other = __shfl_xor(lo ? a1 : a0, 16);
+                    // lane l ^ 16's value: v_permlane16_swap exchanges the
+                    // odd 16-lane rows of its first operand with the even
+                    // rows of its second, so each half takes its partner's
+                    // value from one of the two results
+                    const uint32_t snd = __builtin_bit_cast(uint32_t, lo ? a1 : a0);
+                    const auto sw = __builtin_amdgcn_permlane16_swap(snd, snd, false, false);
+                    const float other = __builtin_bit_cast(float, lo ? sw[1] : sw[0]);
                     const float gv = lo ? mine : other, uv = lo ? other : mine;
                     const float h = __fdividef(gv, 1.f + __expf(-gv)) * uv;
                     hv[q] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(f32_to_bf16(h)));
