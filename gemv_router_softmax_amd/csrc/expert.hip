@@ -232,7 +232,9 @@ struct PG {
                                                         // waves 0-2 load rows 0..191, one 4-byte
                                                         // direct load each; the other waves' loads
                                                         // land in the fourth 256 B
-    static constexpr int STG = 512;                     // per-wave epilogue staging
+    static constexpr int STG = KCH == 2 * G ? 2048 : 512;   // per-wave epilogue staging: a whole
+                                                        // m-tile of h or coef*d rows at once,
+                                                        // or 512 B rounds where the LDS is full
     static constexpr int CLAIM = 16 + 256;              // the claimed item index (16 B) and the
                                                         // landing area of the other waves'
                                                         // stand-in loads
@@ -586,11 +588,13 @@ __device__ __forceinline__ void sched_step() {
     }
 }
 
-// Stores per wave per epilogue (one 16-byte store per lane per 1 KB staged).
-template <int MODE, int MTR>
+// Stores per wave per epilogue: per 32-row m-tile, gate/up one (2 KB
+// staging) or two, fp16 down two or four, fp32 down eight.
+template <int MODE, int MTR, int KCH>
 constexpr int epi_stores() {
     constexpr int n = PG<MTR, G>::NMT_MAX;
-    return MODE == GM_GATEUP ? 2 * n : MODE == GM_DOWN_F16W ? 4 * n : 8 * n;
+    constexpr bool wide = PG<MTR, KCH>::STG >= 2048;
+    return MODE == GM_GATEUP ? (wide ? 1 : 2) * n : MODE == GM_DOWN_F16W ? (wide ? 2 : 4) * n : 8 * n;
 }
 
 // Staging through LDS moves values between lanes of one wave.  The wave's
@@ -619,20 +623,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t item_rows(P* base, const GItem
                     (uint32_t)m.nrows * (uint32_t)row_elems * (uint32_t)sizeof(P));
 }
 
-// One n-tile per wave (512 B of staging each).  Accumulator
-// element i of lane l holds row 8*(i/4) + 4*(l/32) + i%4 of the m-tile.
+// One n-tile per wave.  Accumulator element i of lane l holds row
+// 8*(i/4) + 4*(l/32) + i%4 of the m-tile.
 //   gate/up: lanes l%32 < 16 (gate) and l ^ 16 (up) exchange half of their
 //     elements, so that the first lane forms h for elements 0..7 (rows
-//     0..15) and the second for elements 8..15 (rows 16..31); each half is
-//     staged as [16 rows][16 columns] and stored 8 bytes per lane.
-//   down: elements 4b..4b+3 (rows 8b..8b+7) are staged per b, as
-//     [8][32] fp16 (times the row's weight), or [8][16] fp32 per half of
-//     the columns.
-template <int MODE, int NMT, int MTR>
+//     0..15) and the second for elements 8..15 (rows 16..31).  With 2 KB of
+//     staging the m-tile is staged at once as [32 rows][16 columns] and
+//     stored 16 bytes per lane; with 512 B, one half at a time, 8 bytes.
+//   down, fp16 rows of coef x d: with 2 KB the m-tile at once as [32][32],
+//     two 16-byte stores per lane; with 512 B elements 4b..4b+3 (rows
+//     8b..8b+7) per b as [8][32].  fp32 rows: [8][16] per b and half of the
+//     columns.
+template <int MODE, int NMT, int MTR, int KCH>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                                                  float16v (&acc)[NMT][1], uint8_t* stg,
                                                  const float* coef) {
     using pg = PG<MTR, G>;
+    constexpr bool WIDE = PG<MTR, KCH>::STG >= 2048;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int l32 = lane & 31, g = lane >> 5;
     if constexpr (MODE == GM_GATEUP) {
@@ -660,6 +667,25 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
                     hv[q] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(f32_to_bf16(h)));
                 }
             }
+            if constexpr (WIDE) {
+                uint4v v = (uint4v){0u, 0u, 0u, 0u};
+                uint32_t off = pg::OOB;
+                if (mt < NMT) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int row = (lo ? 0 : 16) + 8 * (q >> 2) + 4 * g + (q & 3);
+                        st[row * 16 + (j & ~7) + chunk_slot(j & 7)] = hv[q];
+                    }
+                    lane_exchange_fence();
+                    v = reinterpret_cast<const uint4v*>(stg)[lane];
+                    lane_exchange_fence();
+                    const int R = mt * 32 + (lane >> 1);
+                    if (R < m.nrows)
+                        off = (uint32_t)((R * I + m.nb * 128 + wave * 16 + (lane & 1) * 8) * 2);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(v, rh, off, 0, 0);
+                continue;
+            }
 #pragma unroll
             for (int hr = 0; hr < 2; ++hr) {
                 uint2v v = (uint2v){0u, 0u};
@@ -684,7 +710,38 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& A, const GItem& m,
         }
     } else if constexpr (MODE == GM_DOWN_F16W) {
         const __amdgpu_buffer_rsrc_t rd = item_rows(A.dout16, m, H);
-        uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [8][32] fp16
+        uint16_t* st = reinterpret_cast<uint16_t*>(stg);    // [32][32] or [8][32] fp16
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int mt = 0; mt < pg::NMT_MAX; ++mt) {
+                uint4v v[2] = {(uint4v){0u, 0u, 0u, 0u}, (uint4v){0u, 0u, 0u, 0u}};
+                uint32_t off[2] = {pg::OOB, pg::OOB};
+                if (mt < NMT) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const float4v cf = *reinterpret_cast<const float4v*>(coef + mt * 32 + 8 * b + 4 * g);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float d = acc[mt < NMT ? mt : 0][0][4 * b + r] * cf[r];
+                            st[(8 * b + 4 * g + r) * 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)d);
+                        }
+                    }
+                    lane_exchange_fence();
+                    v[0] = reinterpret_cast<const uint4v*>(stg)[lane];
+                    v[1] = reinterpret_cast<const uint4v*>(stg)[lane + 64];
+                    lane_exchange_fence();
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int R = mt * 32 + 16 * h + (lane >> 2);
+                        if (R < m.nrows)
+                            off[h] = (uint32_t)((R * H + m.nb * 256 + wave * 32 + (lane & 3) * 8) * 2);
+                    }
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(v[0], rd, off[0], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v[1], rd, off[1], 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int mt = 0; mt < pg::NMT_MAX; ++mt)
 #pragma unroll
@@ -788,7 +845,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
     constexpr bool GATEUP = MODE == GM_GATEUP;
     constexpr int NB = GATEUP ? 2 * I / pg::NCOL : H / pg::NCOL;
     constexpr int NCH = KDIM / pg::KC;
-    constexpr int S_EPI = epi_stores<MODE, MTR>();
+    constexpr int S_EPI = epi_stores<MODE, MTR, KCH>();
     constexpr int S = pg::STAGES;
     constexpr int BASE = (S - 2) * pg::LPC;     // loads of the chunks behind the awaited one
     // (a count larger than the operations really issued after the awaited
@@ -918,7 +975,7 @@ __device__ __forceinline__ void gemm_run_item(const GemmArgs& A, const GItem& cu
 #pragma unroll
     for (int c = (MAIN > HEAD ? MAIN : HEAD); c < NCH; ++c) chunk(c, next(c));
     __builtin_amdgcn_sched_barrier(0);          // epilogue stores after the last refill
-    gemm_epilogue<MODE, NMT, MTR>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
+    gemm_epilogue<MODE, NMT, MTR, KCH>(A, cur, acc, stg, reinterpret_cast<const float*>(meta + (k & 1) * pg::META));
     __builtin_amdgcn_sched_barrier(0);
 }
 
