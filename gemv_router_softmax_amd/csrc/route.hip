@@ -238,8 +238,8 @@ static int route_ksplit(int T) {
 // grouped GEMM reads (xh), which saves the conversion kernel.
 //
 // part / nks: K-split partial logits [nks][T][E] of route_logits_tile<KS>
-// (nks > 1): summed here in slice order, plus the bias, and also stored to
-// logits.
+// (nks > 1): summed here in slice order, plus the bias (and stored to
+// logits if it is given).
 //
 // chunk_counts: optional; each token's eight experts are added to the
 // histogram of its permutation chunk, chunk_counts[8t / PERM_CHUNK][e]
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void route_topk(float* __restrict__ logits,
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] += bias[lane * 4 + j];
         }
-        reinterpret_cast<float4v*>(logits + (size_t)t * E)[lane] = v;
+        if (logits) reinterpret_cast<float4v*>(logits + (size_t)t * E)[lane] = v;
         e = wave_top8_v(v, ids + (size_t)t * TOPK, wts + (size_t)t * TOPK, nullptr);
     } else {
         e = wave_top8_v(reinterpret_cast<const float4v*>(logits + (size_t)t * E)[lane],
@@ -347,8 +347,9 @@ void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bia
         }
     }
 #undef RL_LAUNCH
-    hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, (const float*)part,
-                       ks, bias, x, wsg, T, ids, wts, sg, xh, chunk_counts);
+    // (nothing reads the summed logits after the top-8: not stored)
+    hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, (float*)nullptr,
+                       (const float*)part, ks, bias, x, wsg, T, ids, wts, sg, xh, chunk_counts);
 }
 
 }  // namespace moe
