@@ -204,3 +204,52 @@ def constant_layer(dims: Dims, code: int, scale_bits: int, bias_bits: int,
     wr = w_router if w_router is not None else np.zeros((E, H), np.uint16)
     wsg = w_shared_gate if w_shared_gate is not None else np.zeros((H,), np.uint16)
     return Layer(dims, wr, wsg, q(E), q(1), None, {"constant": code})
+
+
+# ------------------------------------------------- gated delta rule inputs
+#
+# One recurrent (Gated DeltaNet) layer's scan inputs, shapes of the
+# published layer form this library takes (the pages give none): hk key
+# heads and hv value heads of dimension 128 (hv a multiple of hk), for T
+# tokens of one sequence.
+#   k      bf16 [T, hk, d]   unit-length random directions
+#   q      bf16 [T, hk, d]   unit-length random directions / sqrt(d)
+#   v      bf16 [T, hv, d]   ~ N(0, 1)
+#   beta   fp32 [T, hv]      1 / (1 + exp(-z)), z ~ N(0, 1)
+#   g      fp32 [T, hv]      -log(1 + exp(z)), z ~ N(-4.5, 1) (decay e^g
+#                            around 0.99 per token, about 0.5 per 64 tokens)
+#   s0     fp32 [hv, d, d]   ~ N(0, 0.05^2) (a state carried in), optional
+GDN_DIM = 128
+GDN_HK = 16
+GDN_HV = 32
+_TID_GDN = 20        # 20..25: q, k, v, beta, g, s0
+
+
+@dataclass
+class GdnInputs:
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    s0: Optional[np.ndarray]
+
+
+def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    a = rng.standard_normal(shape, dtype=np.float32)
+    return a / np.linalg.norm(a, axis=-1, keepdims=True)
+
+
+def make_gdn(T: int, hk: int = GDN_HK, hv: int = GDN_HV, d: int = GDN_DIM, seed: int = 0,
+             with_state: bool = True) -> GdnInputs:
+    q = f32_to_bf16_bits(_unit_rows(_rng(seed, 0, _TID_GDN), (T, hk, d)) / np.float32(np.sqrt(d)))
+    k = f32_to_bf16_bits(_unit_rows(_rng(seed, 0, _TID_GDN + 1), (T, hk, d)))
+    v = f32_to_bf16_bits(_rng(seed, 0, _TID_GDN + 2).standard_normal((T, hv, d), dtype=np.float32))
+    zb = _rng(seed, 0, _TID_GDN + 3).standard_normal((T, hv))
+    beta = (1.0 / (1.0 + np.exp(-zb))).astype(np.float32)
+    zg = _rng(seed, 0, _TID_GDN + 4).normal(-4.5, 1.0, (T, hv))
+    g = (-np.log1p(np.exp(zg))).astype(np.float32)
+    s0 = None
+    if with_state:
+        s0 = (0.05 * _rng(seed, 0, _TID_GDN + 5).standard_normal((hv, d, d))).astype(np.float32)
+    return GdnInputs(q, k, v, g, beta, s0)

@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
 benchmark's CPU-baseline leg are the only users.  The HIP library never
 imports, links or calls anything in this package.
 
-``load()`` compiles ``moe_oracle.c`` with gcc (OpenMP, -O2, no fast-math)
+``load()`` compiles ``moe_oracle.c`` and ``gdn_oracle.c`` with gcc (OpenMP, -O2, no fast-math)
 when the shared object is missing or older than the source, then wraps it.
 ``build(mutant=n)`` produces a build with planted mistake ``n`` for the
 mutation tests.
@@ -21,6 +21,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "moe_oracle.c")
+SRCS = [SRC, os.path.join(HERE, "gdn_oracle.c")]
 LIB = os.path.join(HERE, "libmoe_oracle.so")
 
 # Planted mistakes available through ORACLE_MUTANT (see moe_oracle.c).
@@ -41,16 +42,20 @@ MUTANTS = {
     14: "combine reads the routed rows through a transposed slot index",
     15: "greedy selection breaks ties toward the higher token",
     16: "embedding lookup reads the neighbouring row",
+    17: "gated delta rule decays the new write as well",
+    18: "gated delta rule erases with beta = 1",
+    19: "gated delta rule maps value head h to key head h % hk",
+    20: "gated delta rule output read before the token's update",
 }
 
 
 def build(out: Optional[str] = None, mutant: int = 0, force: bool = False) -> str:
     out = out or LIB
     if (not force and mutant == 0 and os.path.exists(out)
-            and os.path.getmtime(out) >= os.path.getmtime(SRC)):
+            and all(os.path.getmtime(out) >= os.path.getmtime(f) for f in SRCS)):
         return out
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
-           "-fno-fast-math", "-ffp-contract=off", SRC, "-o", out + ".tmp", "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", *SRCS, "-o", out + ".tmp", "-lm"]
     if mutant:
         cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
     subprocess.run(cmd, check=True)
@@ -113,6 +118,13 @@ class LayerOut:
 
 
 @dataclass
+class GdnOut:
+    o: np.ndarray        # float64 [T, hv, dv]
+    o_bf16: np.ndarray   # uint16 bf16 bits [T, hv, dv]
+    state: np.ndarray    # float64 [hv, dv, dk]: the state after the last token
+
+
+@dataclass
 class GreedyOut:
     token: np.ndarray    # int32 [T]
     logits: np.ndarray   # float64 [T, V] (before the fp32 rounding)
@@ -155,6 +167,8 @@ class Oracle:
         L.oracle_lm_head_argmax.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_lm_head_argmax.restype = i32
         L.oracle_embed.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.oracle_gdn_scan.argtypes = [i32] * 5 + [vp] * 9
+        L.oracle_gdn_scan.restype = i32
         L.oracle_embed.restype = i32
         self.mutant = L.oracle_mutant()
 
@@ -297,6 +311,31 @@ class Oracle:
         if self.lib.oracle_embed(token.shape[0], H, V, _p(token), _p(emb), _p(x)):
             raise ValueError("oracle_embed: token outside the table")
         return x
+
+
+    # ---- gated delta rule scan
+    def gdn_scan(self, q, k, v, g, beta, s0=None) -> GdnOut:
+        """q, k: bf16 bits [T, hk, dk]; v: bf16 bits [T, hv, dv]; g, beta:
+        float32 [T, hv]; s0: float32 [hv, dv, dk] or None (zero state)."""
+        q = np.ascontiguousarray(q, np.uint16)
+        k = np.ascontiguousarray(k, np.uint16)
+        v = np.ascontiguousarray(v, np.uint16)
+        g = np.ascontiguousarray(g, np.float32)
+        beta = np.ascontiguousarray(beta, np.float32)
+        T, hk, dk = k.shape
+        hv, dv = v.shape[1], v.shape[2]
+        assert q.shape == k.shape and v.shape[0] == T and g.shape == (T, hv) == beta.shape
+        if s0 is not None:
+            s0 = np.ascontiguousarray(s0, np.float32)
+            assert s0.shape == (hv, dv, dk)
+        o = np.empty((T, hv, dv), np.float64)
+        ob = np.empty((T, hv, dv), np.uint16)
+        st = np.empty((hv, dv, dk), np.float64)
+        rc = self.lib.oracle_gdn_scan(T, hk, hv, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                      _p(s0), _p(o), _p(ob), _p(st))
+        if rc:
+            raise ValueError(f"oracle_gdn_scan failed ({rc})")
+        return GdnOut(o, ob, st)
 
 
 _DEFAULT: Optional[Oracle] = None

@@ -390,4 +390,136 @@ def pin_embed_gather(o):
         pass
 
 
+# ------------------------------------------------------ gated delta rule scan
+#
+# The recurrence (published gated delta rule; the pages name the scan but do
+# not define it): S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+# a_t = exp(g_t), o_t = S_t q_t.
+
+def _bf(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def pin_gdn_beta_zero_is_pure_decay(o):
+    """beta = 0: nothing is written or erased, so S_t = exp(g_1 + .. + g_t)
+    S_0 and o_t = S_t q_t."""
+    x = synth.make_gdn(20, 1, 2, 16, seed=40)
+    r = o.gdn_scan(x.q, x.k, x.v, x.g, np.zeros_like(x.beta), x.s0)
+    gam = np.cumsum(x.g.astype(np.float64), axis=0)
+    S0 = x.s0.astype(np.float64)
+    q = _bf(x.q)
+    for h in range(2):
+        for t in range(20):
+            assert np.allclose(r.o[t, h], np.exp(gam[t, h]) * (S0[h] @ q[t, 0]), rtol=1e-12, atol=1e-15)
+        assert np.allclose(r.state[h], np.exp(gam[-1, h]) * S0[h], rtol=1e-12, atol=1e-15)
+
+
+def pin_gdn_single_token(o):
+    """One token from the zero state: S_1 = beta v k^T and o_1 = beta (k.q) v,
+    whatever the decay."""
+    x = synth.make_gdn(1, 1, 3, 16, seed=41, with_state=False)
+    r = o.gdn_scan(x.q, x.k, x.v, x.g, x.beta)
+    q, k, v = _bf(x.q)[0, 0], _bf(x.k)[0, 0], _bf(x.v)[0]
+    for h in range(3):
+        b = float(x.beta[0, h])
+        assert np.allclose(r.o[0, h], b * (k @ q) * v[h], rtol=1e-12, atol=1e-15)
+        assert np.allclose(r.state[h], b * np.outer(v[h], k), rtol=1e-12, atol=1e-15)
+
+
+def pin_gdn_orthonormal_keys_exact_retrieval(o):
+    """beta = 1 with one-hot keys: a write stores its value exactly under its
+    key (replacing what was there), keys do not disturb one another, and a
+    query of a key returns its last value times the decay since."""
+    d, T = 16, 10
+    keys = [3, 7, 0, 12, 5, 3, 9, 7, 1, 15]      # keys 3 and 7 written twice
+    qsel = [3, 7, 3, 0, 12, 3, 5, 7, 9, 1]       # a key written at or before t
+    k = np.zeros((T, 1, d), np.float32)
+    q = np.zeros((T, 1, d), np.float32)
+    for t in range(T):
+        k[t, 0, keys[t]] = 1.0
+        q[t, 0, qsel[t]] = 1.0
+    rng = np.random.default_rng(42)
+    v = synth.f32_to_bf16_bits(rng.standard_normal((T, 1, d), dtype=np.float32))
+    g = np.full((T, 1), np.log(0.5), np.float32)
+    a = np.exp(np.float64(g[0, 0]))
+    r = o.gdn_scan(synth.f32_to_bf16_bits(q), synth.f32_to_bf16_bits(k), v, g,
+                   np.ones((T, 1), np.float32))
+    vf = _bf(v)[:, 0]
+    for t in range(T):
+        last = max(j for j in range(t + 1) if keys[j] == qsel[t])
+        assert np.allclose(r.o[t, 0], a ** (t - last) * vf[last], rtol=1e-13, atol=0)
+
+
+def _gdn_chunked(q, k, v, g, beta, s0, C):
+    """The scan over chunks of C tokens, derived independently from the
+    recurrence: unrolled over a chunk with cumulative log decay gam and
+    b = exp(gam), the chunk's corrected values U solve
+      (I + L) U = diag(beta) (V - diag(b) K S0^T),
+      L_ij = beta_i exp(gam_i - gam_j) k_i . k_j  (j < i),
+    then O = diag(b) Q S0^T + (exp(gam_i - gam_j) q_i . k_j, j <= i) U and
+    S = b_n S0 + U^T diag(exp(gam_n - gam)) K."""
+    T, hk, d = k.shape
+    hv, dv = v.shape[1], v.shape[2]
+    O = np.zeros((T, hv, dv))
+    states = []
+    for h in range(hv):
+        kh = h // (hv // hk)
+        S = s0[h].astype(np.float64).copy() if s0 is not None else np.zeros((dv, d))
+        for c0 in range(0, T, C):
+            Kc, Qc, Vc = k[c0:c0 + C, kh], q[c0:c0 + C, kh], v[c0:c0 + C, h]
+            gam = np.cumsum(g[c0:c0 + C, h].astype(np.float64))
+            b = np.exp(gam)
+            be = beta[c0:c0 + C, h].astype(np.float64)
+            D = np.exp(gam[:, None] - gam[None, :])
+            L = np.tril(be[:, None] * D * (Kc @ Kc.T), -1)
+            U = np.linalg.solve(np.eye(len(gam)) + L, be[:, None] * (Vc - b[:, None] * (Kc @ S.T)))
+            O[c0:c0 + C, h] = b[:, None] * (Qc @ S.T) + (np.tril(D) * (Qc @ Kc.T)) @ U
+            S = b[-1] * S + U.T @ (np.exp(gam[-1] - gam)[:, None] * Kc)
+        states.append(S)
+    return O, np.array(states)
+
+
+def pin_gdn_chunked_derivation(o):
+    x = synth.make_gdn(150, 2, 4, 32, seed=43)
+    r = o.gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.s0)
+    O, S = _gdn_chunked(_bf(x.q), _bf(x.k), _bf(x.v), x.g, x.beta, x.s0, 64)
+    assert np.allclose(r.o, O, rtol=1e-9, atol=1e-12)
+    assert np.allclose(r.state, S, rtol=1e-9, atol=1e-12)
+
+
+def pin_gdn_split_carries_state(o):
+    """Scanning 90 tokens equals scanning 37 and then the other 53 from the
+    state the first scan returned (passed on as fp32)."""
+    x = synth.make_gdn(90, 1, 2, 16, seed=44)
+    full = o.gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.s0)
+    a = o.gdn_scan(x.q[:37], x.k[:37], x.v[:37], x.g[:37], x.beta[:37], x.s0)
+    b = o.gdn_scan(x.q[37:], x.k[37:], x.v[37:], x.g[37:], x.beta[37:], a.state.astype(np.float32))
+    assert np.allclose(full.o[:37], a.o, rtol=0, atol=0)
+    assert np.allclose(full.o[37:], b.o, rtol=1e-5, atol=1e-8)
+    assert np.allclose(full.state, b.state, rtol=1e-5, atol=1e-8)
+
+
+def pin_gdn_value_heads_share_key_heads(o):
+    """hv = 4 value heads over hk = 2 key heads: value head h reads key head
+    h // 2, i.e. equals a scan of that key head and that value head alone."""
+    x = synth.make_gdn(30, 2, 4, 16, seed=45)
+    r = o.gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.s0)
+    for h in range(4):
+        kh = h // 2
+        s = o.gdn_scan(x.q[:, kh:kh + 1], x.k[:, kh:kh + 1], x.v[:, h:h + 1], x.g[:, h:h + 1],
+                       x.beta[:, h:h + 1], x.s0[h:h + 1])
+        assert np.array_equal(r.o[:, h], s.o[:, 0])
+        assert np.array_equal(r.state[h], s.state[0])
+
+
+def pin_gdn_linear_in_values_and_state(o):
+    """Doubling v and S_0 doubles every output and the final state exactly."""
+    x = synth.make_gdn(40, 1, 2, 16, seed=46)
+    r1 = o.gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.s0)
+    v2 = synth.f32_to_bf16_bits(2.0 * _bf(x.v).astype(np.float32))
+    r2 = o.gdn_scan(x.q, x.k, v2, x.g, x.beta, 2.0 * x.s0)
+    assert np.array_equal(r2.o, 2.0 * r1.o)
+    assert np.array_equal(r2.state, 2.0 * r1.state)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
