@@ -467,6 +467,37 @@ def greedy_decode(D, steps, V=GREEDY_V, reps=10):
             "timing": "graph replays of the whole step; head: HIP events around eager calls"}
 
 
+def gdn_scan_leg(T=2048, hk=None, hv=None, iters=50):
+    """The gated delta rule scan of one recurrent layer over T tokens
+    (moe_gdn_scan: gdn_prep + gdn_scan), HIP events around graph replays of
+    the call.  Algorithmic work: the chunked form's matrix products as the
+    kernels issue them (fp16 MFMA), per 64-token chunk and value head
+    11.5 MFLOP; bytes: q, k, v, g, beta in, o out, the state in and out."""
+    import torch
+    import gemv_router_softmax_amd as moe
+    from gemv_router_softmax_amd import synth
+    hk = hk or synth.GDN_HK
+    hv = hv or synth.GDN_HV
+    x = synth.make_gdn(T, hk, hv, seed=0)
+    q, k, v = (moe.to_device_bits(a) for a in (x.q, x.k, x.v))
+    g, beta, s0 = (torch.from_numpy(a).cuda() for a in (x.g, x.beta, x.s0))
+    o = torch.empty((T, hv, 128), dtype=torch.int16, device="cuda")
+    s_out = torch.empty((hv, 128, 128), dtype=torch.float32, device="cuda")
+    ws = moe.gdn_workspace(T, hv)
+    ms = _graphs_timed([lambda: moe.moe_gdn_scan(q, k, v, g, beta, o, ws, s0=s0, s_out=s_out)],
+                       iters)
+    t = float(ms.mean()) * 1e-3
+    nch = (T + 63) // 64
+    flops = nch * hv * 11534336
+    nbytes = T * hk * 128 * 2 * 2 + T * hv * 128 * 2 * 2 + T * hv * 4 * 2 + hv * 128 * 128 * 4 * 2
+    return {"T": T, "key_heads": hk, "value_heads": hv, "dim": 128, "chunk": 64,
+            "us": t * 1e6, "tokens_per_s": T / t, "mfma_gflop": flops / 1e9,
+            "tflops": flops / t / 1e12, "mfma_util": flops / t / (BF16_DENSE_PEAK_TFLOPS * 1e12),
+            "io_bytes": nbytes, "io_gbs": nbytes / t / 1e9,
+            "workspace_bytes": moe.moe_gdn_workspace_bytes(T, hv),
+            "timing": "HIP events around graph replays of one moe_gdn_scan call"}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -539,7 +570,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the prefill T sweep, the T=512 chain, the skewed chunked run and "
                          "the greedy step")
-    ap.add_argument("--legs", default="t4096,sweep,chain512,skewed,greedy",
+    ap.add_argument("--legs", default="t4096,sweep,chain512,skewed,greedy,gdn",
                     help="which of the extra measurements to run (comma list; for profiling "
                          "one of them alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -605,6 +636,10 @@ def main():
     if "greedy" in legs:
         greedy = greedy_decode(D, 200)
         log(f"greedy decode step: {greedy}")
+    gdn = None
+    if "gdn" in legs:
+        gdn = gdn_scan_leg()
+        log(f"gated delta rule scan: {gdn}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -646,6 +681,7 @@ def main():
         "prefill_chain_t512": chain512,
         "prefill_skewed_t16384_chunks4096": skewed,
         "greedy_decode_step": greedy,
+        "gdn_scan_t2048": gdn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

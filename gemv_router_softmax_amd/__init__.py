@@ -30,6 +30,9 @@ MOE_DECODE_T_MAX = 32
 MOE_NOALLOC_T_MAX = 64
 MOE_NOALLOC_WS_BYTES = 8388608
 
+MOE_GDN_DIM = 128
+MOE_GDN_CHUNK = 64
+MOE_GDN_HEADS_MAX = 64
 MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1
 MOE_PATH_PREFILL = 2
@@ -39,7 +42,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_route", "moe_permute
            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_ex",
            "moe_layer_forward_chunked", "moe_chain_forward", "moe_chain_forward_noalloc",
            "moe_lm_head_argmax", "moe_embed", "moe_router_transpose", "moe_probe_read",
-           "moe_probe_copy")
+           "moe_probe_copy", "moe_gdn_workspace_bytes", "moe_gdn_scan")
 
 
 class MoeError(RuntimeError):
@@ -102,8 +105,11 @@ def lib() -> C.CDLL:
     L.moe_embed.argtypes = [vp, i32, vp, i32, vp, vp]
     L.moe_probe_read.argtypes = [vp, sz, vp, vp]
     L.moe_probe_copy.argtypes = [vp, vp, sz, vp]
+    L.moe_gdn_workspace_bytes.argtypes = [i32, i32]
+    L.moe_gdn_workspace_bytes.restype = sz
+    L.moe_gdn_scan.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     for fn in EXPORTS:
-        if fn not in ("moe_workspace_bytes", "moe_status_string"):
+        if fn not in ("moe_workspace_bytes", "moe_status_string", "moe_gdn_workspace_bytes"):
             getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -414,6 +420,30 @@ def moe_probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     assert dst.numel() * dst.element_size() >= n
     _check("moe_probe_copy", lib().moe_probe_copy(
         _ptr(dst, "dst"), _ptr(src, "src"), n, _stream(stream)))
+
+
+def moe_gdn_workspace_bytes(T: int, hv: int) -> int:
+    return int(lib().moe_gdn_workspace_bytes(T, hv))
+
+
+def gdn_workspace(T: int, hv: int, device="cuda") -> torch.Tensor:
+    """Device scratch of moe_gdn_workspace_bytes(T, hv) bytes for moe_gdn_scan."""
+    return torch.empty(max(moe_gdn_workspace_bytes(T, hv), 256), dtype=torch.uint8, device=device)
+
+
+def moe_gdn_scan(q, k, v, g, beta, o, ws, s0=None, s_out=None, stream=None) -> None:
+    """Gated delta rule scan of one sequence: q, k bf16 [T, hk, 128], v bf16
+    [T, hv, 128], g and beta fp32 [T, hv], s0 / s_out fp32 [hv, 128, 128]
+    (optional), o bf16 [T, hv, 128]."""
+    T, hk = k.shape[0], k.shape[1]
+    hv = v.shape[1]
+    D = MOE_GDN_DIM
+    _check("moe_gdn_scan", lib().moe_gdn_scan(
+        _ptr(q, "q", _U16, (T, hk, D)), _ptr(k, "k", _U16, (T, hk, D)),
+        _ptr(v, "v", _U16, (T, hv, D)), _ptr(g, "g", torch.float32, (T, hv)),
+        _ptr(beta, "beta", torch.float32, (T, hv)), T, hk, hv,
+        _ptr(s0, "s0", torch.float32, (hv, D, D)), _ptr(o, "o", _U16, (T, hv, D)),
+        _ptr(s_out, "s_out", torch.float32, (hv, D, D)), *_ws(ws), _stream(stream)))
 
 
 def to_device_bits(a: np.ndarray, device="cuda") -> torch.Tensor:

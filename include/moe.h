@@ -294,6 +294,38 @@ int moe_lm_head_argmax(const uint16_t *x, int T, const uint16_t *w_head, int V, 
  * out of range -> MOE_ERR_INVALID_ARG; alignment -> MOE_ERR_ALIGN. */
 int moe_embed(const int32_t *token, int T, const uint16_t *emb, int V, uint16_t *x, void *stream);
 
+/* Gated delta rule scan: the recurrent (Gated DeltaNet) layers of the
+ * model, whose scan the engine keeps in registers ("leslieli.dev note on
+ * the Perplexity Lily engine", paragraph 3; "Perplexity Open-Sources Lily
+ * ...", section "A runtime shaped around one model").  The pages do not
+ * define the recurrence; this is the published gated delta rule (Yang,
+ * Kautz, Hatamizadeh, "Gated Delta Networks: Improving Mamba2 with Delta
+ * Rule").  Per value head h (key head h / (hv / hk)) with state S (128 x
+ * 128, rows = value channels, columns = key channels):
+ *   S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *   o_t = S_t q_t.
+ * q and k are used as given (any normalisation or scaling of them is the
+ * caller's).  Computed in chunks of MOE_GDN_CHUNK tokens on fp16 MFMA with
+ * fp32 accumulation and an fp32 state (fp16 operands: see the library's
+ * documentation for the error this gives).
+ * In: q, k bf16 [T][hk][128]; v bf16 [T][hv][128] (16-byte aligned);
+ * g (log decay) and beta fp32 [T][hv]; s0 fp32 [hv][128][128], the state
+ * entering token 0, or NULL for zero.  Out: o bf16 [T][hv][128] (rounded
+ * to nearest even); s_out fp32 [hv][128][128], the state after token T-1,
+ * or NULL.  ws: moe_gdn_workspace_bytes(T, hv) bytes of device scratch,
+ * 256-byte aligned, not read before it is written.  1 <= hk, hv <=
+ * MOE_GDN_HEADS_MAX, hv a multiple of hk, 0 <= T <= MOE_T_MAX (T == 0:
+ * s_out, if given, receives s0 or zeros).  Errors: NULL or a size out of
+ * range -> MOE_ERR_INVALID_ARG; alignment -> MOE_ERR_ALIGN; ws too small
+ * -> MOE_ERR_WORKSPACE.  Deterministic. */
+#define MOE_GDN_DIM 128
+#define MOE_GDN_CHUNK 64
+#define MOE_GDN_HEADS_MAX 64
+size_t moe_gdn_workspace_bytes(int T, int hv);   /* 0 for arguments out of range */
+int moe_gdn_scan(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                 const float *beta, int T, int hk, int hv, const float *s0, uint16_t *o,
+                 float *s_out, void *ws, size_t ws_bytes, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * call as moe_chain_forward with the workspace taken from a fixed device

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -42,7 +42,8 @@ def test_exports_every_declared_symbol(L):
 def test_header_constants_match_binding():
     src = open(HEADER).read()
     for name in ("MOE_HIDDEN", "MOE_INTER", "MOE_EXPERTS", "MOE_TOPK", "MOE_GROUP", "MOE_T_MAX",
-                 "MOE_DECODE_T", "MOE_DECODE_T_MAX", "MOE_NOALLOC_T_MAX", "MOE_NOALLOC_WS_BYTES"):
+                 "MOE_DECODE_T", "MOE_DECODE_T_MAX", "MOE_NOALLOC_T_MAX", "MOE_NOALLOC_WS_BYTES",
+                 "MOE_GDN_DIM", "MOE_GDN_CHUNK", "MOE_GDN_HEADS_MAX"):
         m = re.search(rf"#define {name} (\d+)", src)
         assert int(m.group(1)) == getattr(moe, name), name
 
@@ -258,3 +259,42 @@ def test_product_path_never_touches_the_oracle():
                 src = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), fn
                 assert "moe_oracle" not in src and "libmoe_oracle" not in src, fn
+
+
+def test_gdn_workspace_bytes(L):
+    assert moe.moe_gdn_workspace_bytes(-1, 4) == 0
+    assert moe.moe_gdn_workspace_bytes(10, 0) == 0
+    assert moe.moe_gdn_workspace_bytes(10, moe.MOE_GDN_HEADS_MAX + 1) == 0
+    assert moe.moe_gdn_workspace_bytes(moe.MOE_T_MAX + 1, 4) == 0
+    assert moe.moe_gdn_workspace_bytes(0, 4) == 0
+    prev = 0
+    for T in [1, 63, 64, 65, 2048, 65536]:
+        b = moe.moe_gdn_workspace_bytes(T, 32)
+        assert b >= prev and b % 256 == 0
+        assert b == moe.moe_gdn_workspace_bytes(1, 32) * ((T + 63) // 64)
+        prev = b
+
+
+def test_gdn_rejects_bad_arguments(L):
+    """moe_gdn_scan(q, k, v, g, beta, T, hk, hv, s0, o, s_out, ws, ws_bytes, stream)."""
+    f = L.moe_gdn_scan
+    big = 1 << 40
+    ok = dict(q=A, k=A, v=A, g=A, beta=A, T=100, hk=2, hv=4, s0=None, o=A, s_out=None, ws=A,
+              ws_bytes=big)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["T"], a["hk"], a["hv"], a["s0"],
+                 a["o"], a["s_out"], a["ws"], a["ws_bytes"], None)
+    assert call(hv=3) == INVALID                       # hv not a multiple of hk
+    assert call(hk=0) == INVALID
+    assert call(hv=moe.MOE_GDN_HEADS_MAX + 2, hk=2) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(T=moe.MOE_T_MAX + 1) == INVALID
+    assert call(q=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(k=MIS) == ALIGN
+    assert call(ws=A + 16) == ALIGN                    # workspace must be 256-byte aligned
+    assert call(s_out=A + 2) == ALIGN
+    assert call(ws_bytes=moe.moe_gdn_workspace_bytes(100, 4) - 1) == WS
+    assert call(T=0, s_out=None) == OK                 # nothing to do

@@ -1,0 +1,109 @@
+"""Gated delta rule scan (moe_gdn_scan) against the fp64 oracle.
+
+The kernel computes in chunks of 64 tokens on fp16 MFMA with fp32
+accumulation and an fp32 state; the oracle runs the recurrence token by
+token in double.  Tolerances (relative L2 over all outputs / over the final
+state, and the largest error against the output scale) follow from fp16
+operand rounding (relative 2^-11 per operand, a few chained products per
+chunk, errors in the state damped by the decay), see the library's
+documentation."""
+import numpy as np
+import pytest
+import torch
+
+import gemv_router_softmax_amd as moe
+from gemv_router_softmax_amd import synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+O_REL, S_REL, O_MAX = 5e-3, 5e-3, 2e-2
+
+
+def _bf(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _run(x, s0=True, ws=None):
+    T, hk = x.k.shape[0], x.k.shape[1]
+    hv = x.v.shape[1]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, k, v = (moe.to_device_bits(a) for a in (x.q, x.k, x.v))
+    g, beta = dev(x.g), dev(x.beta)
+    s0d = dev(x.s0) if (s0 and x.s0 is not None) else None
+    o = torch.empty((T, hv, 128), dtype=torch.int16, device="cuda")
+    s_out = torch.empty((hv, 128, 128), dtype=torch.float32, device="cuda")
+    ws = moe.gdn_workspace(T, hv) if ws is None else ws
+    moe.moe_gdn_scan(q, k, v, g, beta, o, ws, s0=s0d, s_out=s_out)
+    torch.cuda.synchronize()
+    return moe.bits_to_numpy(o), s_out.cpu().numpy().astype(np.float64)
+
+
+def _check(x, s0=True):
+    o_bits, st = _run(x, s0)
+    ref = oracle.load().gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.s0 if s0 else None)
+    got, want = _bf(o_bits), _bf(ref.o_bf16)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    mab = np.abs(got - want).max() / np.abs(want).max()
+    srel = np.linalg.norm(st - ref.state) / np.linalg.norm(ref.state)
+    print(f"T={x.k.shape[0]} hk={x.k.shape[1]} hv={x.v.shape[1]} o relL2={rel:.2e} "
+          f"max/scale={mab:.2e} state relL2={srel:.2e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert rel <= O_REL and mab <= O_MAX and srel <= S_REL
+    return rel, srel
+
+
+@pytest.mark.parametrize("T,hk,hv,s0", [(1, 1, 1, True), (1, 1, 2, False), (63, 1, 2, True),
+                                        (64, 2, 2, False), (65, 1, 1, True), (130, 2, 4, True),
+                                        (300, 4, 8, False), (517, 2, 4, True)])
+def test_gdn_small(T, hk, hv, s0):
+    _check(synth.make_gdn(T, hk, hv, seed=T + 7 * hv), s0)
+
+
+def test_gdn_full_size_t2048():
+    """The workload of the scan's benchmark: 2048 tokens, 16 key heads, 32
+    value heads, a carried-in state; every output and the final state."""
+    _check(synth.make_gdn(2048, synth.GDN_HK, synth.GDN_HV, seed=1))
+
+
+def test_gdn_t0_passes_state():
+    x = synth.make_gdn(1, 1, 2, seed=3)
+    s0 = torch.from_numpy(x.s0).cuda()
+    s_out = torch.full((2, 128, 128), 7.0, dtype=torch.float32, device="cuda")
+    z = torch.empty((0, 1, 128), dtype=torch.int16, device="cuda")
+    zv = torch.empty((0, 2, 128), dtype=torch.int16, device="cuda")
+    zg = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    ws = moe.gdn_workspace(0, 2)
+    moe.moe_gdn_scan(z, z, zv, zg, zg, zv, ws, s0=s0, s_out=s_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_out.cpu().numpy(), x.s0)
+    moe.moe_gdn_scan(z, z, zv, zg, zg, zv, ws, s0=None, s_out=s_out)
+    torch.cuda.synchronize()
+    assert not s_out.cpu().numpy().any()
+
+
+def test_gdn_deterministic_and_workspace_garbage():
+    x = synth.make_gdn(200, 2, 4, seed=5)
+    ws = moe.gdn_workspace(200, 4)
+    ws.fill_(0xA5)
+    a = _run(x, ws=ws)
+    ws.fill_(0x3C)
+    b = _run(x, ws=ws)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_gdn_split_matches_oracle():
+    """Two calls with the state carried between them (the split falls inside
+    a chunk) agree with the oracle's single scan."""
+    x = synth.make_gdn(300, 2, 4, seed=9)
+    T1 = 137
+    first = synth.GdnInputs(x.q[:T1], x.k[:T1], x.v[:T1], x.g[:T1], x.beta[:T1], x.s0)
+    o1, st1 = _run(first)
+    second = synth.GdnInputs(x.q[T1:], x.k[T1:], x.v[T1:], x.g[T1:], x.beta[T1:],
+                             st1.astype(np.float32))
+    o2, st2 = _run(second)
+    ref = oracle.load().gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.s0)
+    got = _bf(np.concatenate([o1, o2]))
+    want = _bf(ref.o_bf16)
+    assert np.linalg.norm(got - want) / np.linalg.norm(want) <= O_REL
+    assert np.linalg.norm(st2 - ref.state) / np.linalg.norm(ref.state) <= S_REL
