@@ -28,10 +28,12 @@
 //             (fp32), W and A (fp16) and gam to the workspace.
 //   gdn_scan  grid (hv, 4): one workgroup per head and 32-row slice of the
 //             state (rows are value channels, independent of one another).
-//             The slice (32 x 128 fp32) stays in the four waves' MFMA
+//             The slice (32 x 128 fp32) stays in four compute waves' MFMA
 //             accumulators for the whole sequence; per chunk it is staged
-//             once to LDS as fp16 for the products S0^T, the chunk's inputs
-//             having been fetched into registers during the previous chunk.
+//             once to LDS as fp16 for the products S0^T.  gdn_prep leaves
+//             each chunk's operands in the workspace as an LDS image, which
+//             three more waves move in with direct-to-LDS loads (a two-stage
+//             ring) while the previous chunk is computed.
 //
 // Precision: products on v_mfma_f32_32x32x16_f16 (fp32 accumulation);
 // q, k, v are bf16 inputs converted to fp16 (exact within fp16's range);
@@ -45,11 +47,23 @@ constexpr int GD = MOE_GDN_DIM;       // 128: key and value head dimension
 constexpr int GC = MOE_GDN_CHUNK;     // 64 tokens per chunk
 constexpr int LD_D = GD + 8;          // LDS row stride (halves) of 128-wide fp16 rows
 constexpr int LD_C = GC + 8;          // LDS row stride (halves) of 64-wide fp16 rows
-// workspace block of one (chunk, head): Ut fp32 [64][128], W fp16 [64][128],
-// A fp16 [64][64], gam fp32 [64]
-constexpr size_t GW_UT = 0, GW_W = GW_UT + GC * GD * 4, GW_A = GW_W + GC * GD * 2,
-                 GW_GAM = GW_A + GC * GC * 2, GW_BLK = GW_GAM + GC * 4;
+// Workspace block of one (chunk, head): the chunk's operands exactly as
+// gdn_scan holds them in LDS (padded rows included), so that the scan
+// moves them with direct-to-LDS loads -- a part common to the head's four
+// state slices, then the four slices' columns of Ut.
+constexpr int IMG_Q = 0;                          // fp16 Q [64][136]
+constexpr int IMG_W = IMG_Q + GC * LD_D * 2;      // fp16 W [64][136]
+constexpr int IMG_KD = IMG_W + GC * LD_D * 2;     // fp16 (e^{gam_n - gam_j} k_j)^T [128][72]
+constexpr int IMG_A = IMG_KD + GD * LD_C * 2;     // fp16 A [64][72]
+constexpr int IMG_GAM = IMG_A + GC * LD_C * 2;    // fp32 gam [64] (in a 1 KB slot)
+constexpr int IMG_COMMON = IMG_GAM + 1024;        // 62 KB
+constexpr int UT_SLICE = GC * 32 * 4;             // fp32 Ut[:, 32 z .. 32 z + 31] as [64][32]
+constexpr int GW_BLK = IMG_COMMON + 4 * UT_SLICE;
+constexpr int STAGE_IMG = IMG_COMMON + UT_SLICE;  // 70 KB moved per chunk and slice
+constexpr int STAGE = STAGE_IMG + 2048;           // one image and two stand-in slots
+static_assert(IMG_COMMON % 1024 == 0 && STAGE_IMG % 1024 == 0 && STAGE >= STAGE_IMG, "1 KB slots");
 static_assert(GW_BLK % 256 == 0, "workspace blocks stay 256-byte aligned");
+constexpr uint32_t GDN_OOB = 0x80000000u;         // beyond every buffer range
 
 typedef float float16v __attribute__((ext_vector_type(16)));
 
@@ -97,7 +111,8 @@ struct GdnArgs {
 
 __global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
     __shared__ __attribute__((aligned(16))) _Float16 Ks[GC * LD_D], Qs[GC * LD_D];
-    __shared__ __attribute__((aligned(16))) _Float16 VbT[GD * LD_C], KbT[GD * LD_C], Ts[GC * LD_C];
+    __shared__ __attribute__((aligned(16))) _Float16 VbT[GD * LD_C], KbT[GD * LD_C], KdT[GD * LD_C];
+    __shared__ __attribute__((aligned(16))) _Float16 Ts[GC * LD_C];
     __shared__ __attribute__((aligned(16))) float Lp[GC * GC];   // row i: L[i][4q+s] at s*16+q
     __shared__ float gam[GC], bet[GC];
     const int c = blockIdx.x, h = blockIdx.y;
@@ -116,53 +131,73 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
         }
         gam[l] = x;
         bet[l] = l < n ? p.beta[(size_t)(t0 + l) * p.hv + h] : 0.f;
-        reinterpret_cast<float*>(blk + GW_GAM)[l] = x;
+        reinterpret_cast<float*>(blk + IMG_GAM)[l] = x;
     }
     __syncthreads();
-    // K, Q rows as fp16; beta v and beta b k transposed ([channel][token])
+    // K, Q rows as fp16; beta v, beta b k and e^{gam_n - gam} k transposed
+    // ([channel][token]); rows past the chunk's last token are zero.  Thread:
+    // token i = tid % 64, channels 32 (tid / 64) .. +31, so that the
+    // transposed writes of a wave cover 64 consecutive tokens of a channel.
+    const float gn = gam[GC - 1];     // = gam[n - 1]: g is zero past n
+    {
+        const int i = tid & 63, cg = tid >> 6;
+        uint4v kw[4], qw[4], vw[4];
 #pragma unroll
-    for (int pi = 0; pi < 4; ++pi) {
-        const int idx = pi * 256 + tid, i = idx >> 4, c8 = (idx & 15) * 8;
-        uint4v kw = {0, 0, 0, 0}, qw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
+        for (int u = 0; u < 4; ++u) kw[u] = qw[u] = vw[u] = (uint4v){0, 0, 0, 0};
         if (i < n) {
-            kw = *reinterpret_cast<const uint4v*>(p.k + ((size_t)(t0 + i) * p.hk + kh) * GD + c8);
-            qw = *reinterpret_cast<const uint4v*>(p.q + ((size_t)(t0 + i) * p.hk + kh) * GD + c8);
-            vw = *reinterpret_cast<const uint4v*>(p.v + ((size_t)(t0 + i) * p.hv + h) * GD + c8);
-        }
-        const half8 kv = bf16x8_to_h8(kw);
-        *reinterpret_cast<half8*>(Ks + i * LD_D + c8) = kv;
-        *reinterpret_cast<half8*>(Qs + i * LD_D + c8) = bf16x8_to_h8(qw);
-        const float bv = bet[i], bk = bet[i] * __expf(gam[i]);
+            const uint4v* kr = reinterpret_cast<const uint4v*>(p.k + ((size_t)(t0 + i) * p.hk + kh) * GD + 32 * cg);
+            const uint4v* qr = reinterpret_cast<const uint4v*>(p.q + ((size_t)(t0 + i) * p.hk + kh) * GD + 32 * cg);
+            const uint4v* vr = reinterpret_cast<const uint4v*>(p.v + ((size_t)(t0 + i) * p.hv + h) * GD + 32 * cg);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            VbT[(c8 + 2 * x) * LD_C + i] = (_Float16)(bv * bf16_to_f32(vw[x] & 0xFFFFu));
-            VbT[(c8 + 2 * x + 1) * LD_C + i] = (_Float16)(bv * bf16_to_f32(vw[x] >> 16));
-            KbT[(c8 + 2 * x) * LD_C + i] = (_Float16)(bk * bf16_to_f32(kw[x] & 0xFFFFu));
-            KbT[(c8 + 2 * x + 1) * LD_C + i] = (_Float16)(bk * bf16_to_f32(kw[x] >> 16));
+            for (int u = 0; u < 4; ++u) {
+                kw[u] = kr[u];
+                qw[u] = qr[u];
+                vw[u] = vr[u];
+            }
+        }
+        const float bv = bet[i], bk = bet[i] * __expf(gam[i]), dk = __expf(gn - gam[i]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c8 = 32 * cg + 8 * u;
+            *reinterpret_cast<half8*>(Ks + i * LD_D + c8) = bf16x8_to_h8(kw[u]);
+            *reinterpret_cast<half8*>(Qs + i * LD_D + c8) = bf16x8_to_h8(qw[u]);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const float kf = bf16_to_f32(x & 1 ? kw[u][x >> 1] >> 16 : kw[u][x >> 1] & 0xFFFFu);
+                const float vf = bf16_to_f32(x & 1 ? vw[u][x >> 1] >> 16 : vw[u][x >> 1] & 0xFFFFu);
+                VbT[(c8 + x) * LD_C + i] = (_Float16)(bv * vf);
+                KbT[(c8 + x) * LD_C + i] = (_Float16)(bk * kf);
+                KdT[(c8 + x) * LD_C + i] = (_Float16)(dk * kf);
+            }
         }
     }
     __syncthreads();
+    // the Q and decayed-K images as they are
+    for (int idx = tid; idx < GC * LD_D / 8; idx += 256)
+        reinterpret_cast<uint4v*>(blk + IMG_Q)[idx] = reinterpret_cast<const uint4v*>(Qs)[idx];
+    for (int idx = tid; idx < GD * LD_C / 8; idx += 256)
+        reinterpret_cast<uint4v*>(blk + IMG_KD)[idx] = reinterpret_cast<const uint4v*>(KdT)[idx];
     // K K^T and Q K^T: wave w owns the 32 x 32 tile (w/2, w%2)
     {
         const int ti = w >> 1, tj = w & 1;
         float16v aG = (float16v)0.f, aQ = (float16v)0.f;
         mma_rows<GD>(Ks + 32 * ti * LD_D, LD_D, Ks + 32 * tj * LD_D, LD_D, aG);
         mma_rows<GD>(Qs + 32 * ti * LD_D, LD_D, Ks + 32 * tj * LD_D, LD_D, aQ);
-        _Float16* Aw = reinterpret_cast<_Float16*>(blk + GW_A);
+        _Float16* Aw = reinterpret_cast<_Float16*>(blk + IMG_A);
         const int j = 32 * tj + (l & 31);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int i = 32 * ti + acc_row(e, l);
             const float d = j <= i ? __expf(gam[i] - gam[j]) : 0.f;
             Lp[i * GC + (j & 3) * 16 + (j >> 2)] = j < i ? bet[i] * d * aG[e] : 0.f;
-            Aw[i * GC + j] = (_Float16)(d * aQ[e]);
+            Aw[i * LD_C + j] = (_Float16)(d * aQ[e]);
         }
     }
     __syncthreads();
     // T = (I + L)^{-1}, L strictly lower: column m by the quad of lanes
     // 4m .. 4m+3, lane s holding rows 4q + s (q = 0..15) in registers;
     // row i: T[i][m] = [i == m] - sum_{j<i} L[i][j] T[j][m] (the rows j >= i
-    // are still zero, as are L's entries there)
+    // are still zero, as are L's entries there); four partial sums per lane
     {
         const int m = tid >> 2, s = tid & 3;
         float tq[16];
@@ -171,16 +206,18 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
 #pragma unroll
         for (int i = 0; i < GC; ++i) {
             const float4v* lr = reinterpret_cast<const float4v*>(Lp + i * GC + s * 16);
-            float part = 0.f;
+            float part[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const float4v lv = lr[b];
+                part[b] = lv[0] * tq[4 * b];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) part = fmaf(lv[x], tq[4 * b + x], part);
+                for (int x = 1; x < 4; ++x) part[b] = fmaf(lv[x], tq[4 * b + x], part[b]);
             }
-            part += dpp_f<DPP_XOR1>(part);
-            part += dpp_f<DPP_XOR2>(part);
-            const float tim = (i == m ? 1.f : 0.f) - part;
+            float sum = (part[0] + part[1]) + (part[2] + part[3]);
+            sum += dpp_f<DPP_XOR1>(sum);
+            sum += dpp_f<DPP_XOR2>(sum);
+            const float tim = (i == m ? 1.f : 0.f) - sum;
             if (s == (i & 3)) tq[i >> 2] = tim;
         }
 #pragma unroll
@@ -188,23 +225,22 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
     }
     __syncthreads();
     // Ut = T (beta V) and W = T (beta b K): wave w owns row tile w/2 and
-    // column tiles 2 (w%2), 2 (w%2) + 1 of both
+    // column tiles 2 (w%2), 2 (w%2) + 1 of both (column tile = state slice)
     {
         const int ti = w >> 1;
-        float* Ut = reinterpret_cast<float*>(blk + GW_UT);
-        _Float16* Ww = reinterpret_cast<_Float16*>(blk + GW_W);
+        _Float16* Ww = reinterpret_cast<_Float16*>(blk + IMG_W);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tc = 2 * (w & 1) + u;
             float16v aU = (float16v)0.f, aW = (float16v)0.f;
             mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, VbT + 32 * tc * LD_C, LD_C, aU);
             mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, KbT + 32 * tc * LD_C, LD_C, aW);
-            const int col = 32 * tc + (l & 31);
+            float* Ut = reinterpret_cast<float*>(blk + IMG_COMMON + tc * UT_SLICE);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int i = 32 * ti + acc_row(e, l);
-                Ut[i * GD + col] = aU[e];
-                Ww[i * GD + col] = (_Float16)aW[e];
+                Ut[i * 32 + (l & 31)] = aU[e];
+                Ww[i * LD_D + 32 * tc + (l & 31)] = (_Float16)aW[e];
             }
         }
     }
@@ -212,117 +248,159 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
 
 // ------------------------------------------------------------------ scan
 
-// One chunk's inputs for one workgroup, in registers while the previous
-// chunk is computed: W rows (fp16), Q and K rows (bf16), A (fp16), this
-// slice's 32 columns of Ut (fp32) and gam.
-struct ChunkRegs {
-    uint4v w[4], q[4], k[4], a[2], u[2];
-    float gam;
-};
+typedef __attribute__((address_space(3))) void* gdn_lds_t;
 
-__device__ __forceinline__ void fetch_chunk(const GdnArgs& p, int c, int h, int kh, int r0,
-                                            ChunkRegs& R) {
-    const int tid = threadIdx.x, t0 = c * GC, n = min(GC, p.T - t0);
-    const uint8_t* blk = p.ws + ((size_t)c * p.hv + h) * GW_BLK;
-#pragma unroll
-    for (int pi = 0; pi < 4; ++pi) {
-        const int idx = pi * 256 + tid, i = idx >> 4, c8 = (idx & 15) * 8;
-        R.w[pi] = *reinterpret_cast<const uint4v*>(blk + GW_W + (size_t)(i * GD + c8) * 2);
-        R.q[pi] = R.k[pi] = (uint4v){0, 0, 0, 0};
-        if (i < n) {
-            R.q[pi] = *reinterpret_cast<const uint4v*>(p.q + ((size_t)(t0 + i) * p.hk + kh) * GD + c8);
-            R.k[pi] = *reinterpret_cast<const uint4v*>(p.k + ((size_t)(t0 + i) * p.hk + kh) * GD + c8);
-        }
-    }
-#pragma unroll
-    for (int pi = 0; pi < 2; ++pi) {
-        const int idx = pi * 256 + tid;
-        R.a[pi] = *reinterpret_cast<const uint4v*>(blk + GW_A + (size_t)idx * 16);
-        const int i = idx >> 3, c4 = (idx & 7) * 4;
-        R.u[pi] = *reinterpret_cast<const uint4v*>(blk + GW_UT + (size_t)(i * GD + r0 + c4) * 4);
-    }
-    R.gam = tid < GC ? reinterpret_cast<const float*>(blk + GW_GAM)[tid] : 0.f;
+// A wave-uniform 64-bit pointer as scalar values (for buffer resources).
+template <typename P>
+__device__ __forceinline__ P* gdn_uniform(P* q) {
+    const uint64_t v = reinterpret_cast<uint64_t>(q);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
 }
 
-__global__ __launch_bounds__(256) void gdn_scan(GdnArgs p) {
-    __shared__ __attribute__((aligned(16))) _Float16 S16[32 * LD_D], Ws[GC * LD_D], Qs[GC * LD_D];
-    __shared__ __attribute__((aligned(16))) _Float16 As[GC * LD_C], KT[GD * LD_C];
-    __shared__ __attribute__((aligned(16))) _Float16 UT[32 * LD_C], UdT[32 * LD_C];
-    __shared__ __attribute__((aligned(16))) float Us[GC * 32];
-    __shared__ float gam[GC];
-    const int h = blockIdx.x, r0 = blockIdx.y * 32;
-    const int kh = h / (p.hv / p.hk);
-    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gdn_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Mover m's share of chunk c's image for state slice z into one LDS stage:
+// slots 24 m .. 24 m + 23, where 1 KB slot j comes from byte j K of the
+// block's common part (j < 62) or of the slice's Ut columns (j = 62 .. 69);
+// slots 70 and 71 are stand-ins (an out-of-range offset: no memory access)
+// that land in the stage's spare 2 KB.
+constexpr int MV_SLOTS = 24;
+__device__ __forceinline__ void gdn_issue(const GdnArgs& p, int c, int h, int z, int m,
+                                          uint8_t* __restrict__ stage) {
+    const uint8_t* blk = gdn_uniform(p.ws + ((size_t)c * p.hv + h) * GW_BLK);
+    const __amdgpu_buffer_rsrc_t r = gdn_rsrc(blk, GW_BLK);
+    const uint32_t lane16 = (threadIdx.x & 63) * 16;
+#pragma unroll
+    for (int i = 0; i < MV_SLOTS; ++i) {
+        const int j = m * MV_SLOTS + i;
+        const uint32_t src = j < IMG_COMMON / 1024 ? (uint32_t)j * 1024
+                             : j < STAGE_IMG / 1024
+                                 ? (uint32_t)(IMG_COMMON + z * UT_SLICE + (j - IMG_COMMON / 1024) * 1024)
+                                 : GDN_OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (gdn_lds_t)(stage + j * 1024), 16, lane16, src, 0, 0);
+    }
+}
+
+__device__ __forceinline__ constexpr int gdn_vmcnt(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);   // vmcnt(n), other counters free
+}
+
+// A workgroup barrier without a memory fence: this wave's LDS operations
+// are complete before it (lgkmcnt(0)), so LDS written before it is visible
+// after it, while global memory operations in flight -- the image loads --
+// stay in flight (__syncthreads would wait for them).  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void gdn_barrier() {
+    __builtin_amdgcn_s_waitcnt((3 << 14) | (7 << 4) | 15);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The image movers (waves 4, 5, 6): chunk c + 1 into nxt while the compute
+// waves work on chunk c.  They read no LDS and the compute waves issue no
+// image loads, so no wait for the loads ever lands in the compute waves'
+// code.  The 70 loads of an image are split so that no mover holds up a
+// barrier: mover 0 issues slots 0..23 after barrier (1) (the compute waves
+// then multiply for a while), movers 1 and 2 slots 24..47 and 48..71 after
+// barrier (2).  Three barriers per chunk, matched one for one by gdn_chunk.
+__device__ __forceinline__ void gdn_mover_chunk(const GdnArgs& p, int c, int nch, int h, int z,
+                                                int m, uint8_t* __restrict__ nxt) {
+    __builtin_amdgcn_s_waitcnt(gdn_vmcnt(0));       // this mover's part of chunk c landed
+    gdn_barrier();                                // (1) chunk c ready, S16 staged
+    // (nxt was last read before barrier (3) of chunk c - 1)
+    if (m == 0 && c + 1 < nch) gdn_issue(p, c + 1, h, z, m, nxt);
+    gdn_barrier();                                // (2)
+    if (m != 0 && c + 1 < nch) gdn_issue(p, c + 1, h, z, m, nxt);
+    gdn_barrier();                                // (3)
+}
+
+// One chunk of the scan for the state slice held in S (compute waves 0-3).
+// cur holds chunk c's image.
+__device__ __forceinline__ void gdn_chunk(const GdnArgs& p, int c, int h, int z, int w,
+                                          const uint8_t* __restrict__ cur,
+                                          _Float16* __restrict__ S16, _Float16* __restrict__ UT,
+                                          __amdgpu_buffer_rsrc_t ro, float16v& S) {
+    const int l = threadIdx.x & 63, r0 = z * 32;
+    const int t0 = c * GC, n = min(GC, p.T - t0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) S16[acc_row(e, l) * LD_D + 32 * w + (l & 31)] = (_Float16)S[e];
+    gdn_barrier();                                // (1)
+    const _Float16* Qs = reinterpret_cast<const _Float16*>(cur + IMG_Q);
+    const _Float16* Ws = reinterpret_cast<const _Float16*>(cur + IMG_W);
+    const _Float16* KdT = reinterpret_cast<const _Float16*>(cur + IMG_KD);
+    const _Float16* As = reinterpret_cast<const _Float16*>(cur + IMG_A);
+    const float* gam = reinterpret_cast<const float*>(cur + IMG_GAM);
+    const float* Us = reinterpret_cast<const float*>(cur + IMG_COMMON);
+
+    // waves 0, 1: X = W S0^T (rows 32 w ..); waves 2, 3: Y = Q S0^T (rows 32 (w - 2) ..)
+    const int ti = w & 1;
+    float16v XY = (float16v)0.f;
+    mma_rows<GD>((w < 2 ? Ws : Qs) + 32 * ti * LD_D, LD_D, S16, LD_D, XY);
+    if (w < 2) {
+        // U = Ut - W S0^T, as U^T (rows past the chunk's tokens are zero in
+        // both terms)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int i = 32 * ti + acc_row(e, l), r = l & 31;
+            UT[r * LD_C + i] = (_Float16)(Us[i * 32 + r] - XY[e]);
+        }
+    }
+    gdn_barrier();                                // (2)
+    if (w >= 2) {
+        // O = diag(b) Q S0^T + A U for rows 32 (w - 2) ..
+        float16v Zo = (float16v)0.f;
+        mma_rows<GC>(As + 32 * ti * LD_C, LD_C, UT, LD_C, Zo);
+        const uint32_t ob = (uint32_t)(((size_t)t0 * p.hv + h) * GD + r0 + (l & 31)) * 2;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int i = 32 * ti + acc_row(e, l);
+            const float ov = __expf(gam[i]) * XY[e] + Zo[e];
+            const uint32_t off = i < n ? ob + (uint32_t)(i * p.hv * GD * 2) : GDN_OOB;
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16(ov), ro, off, 0, 0);
+        }
+    }
+    // S1 = b_n S0 + U^T (e^{gam_n - gam} K), tile w
+    const float bn = __expf(gam[n - 1]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) S[e] *= bn;
+    mma_rows<GC>(UT, LD_C, KdT + 32 * w * LD_C, LD_C, S);
+    gdn_barrier();                                // (3)
+}
+
+// grid (hv, 4) workgroups of 7 waves: waves 0-3 compute (wave w holds the
+// state tile of key channels 32 w ..), waves 4-6 move the chunk images.
+__global__ __launch_bounds__(448) void gdn_scan(GdnArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage0[STAGE], stage1[STAGE];
+    __shared__ __attribute__((aligned(16))) _Float16 S16[32 * LD_D], UT[32 * LD_C];
+    const int h = blockIdx.x, z = blockIdx.y, r0 = z * 32;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nch = (p.T + GC - 1) / GC;
 
+    if (w >= 4) {
+        const int m = w - 4;
+        if (nch > 0) gdn_issue(p, 0, h, z, m, stage0);
+        for (int c = 0; c < nch; c += 2) {
+            gdn_mover_chunk(p, c, nch, h, z, m, stage1);
+            if (c + 1 < nch) gdn_mover_chunk(p, c + 1, nch, h, z, m, stage0);
+        }
+        return;
+    }
+    // output rows through a buffer range: rows past T are not written
+    const __amdgpu_buffer_rsrc_t ro = gdn_rsrc(p.o, (uint32_t)((size_t)p.T * p.hv * GD * 2));
     // the state slice: wave w holds S[r0 + row][32 w + l % 32] (accumulator layout)
     float16v S;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
         S[e] = p.s0 ? p.s0[((size_t)h * GD + r0 + acc_row(e, l)) * GD + 32 * w + (l & 31)] : 0.f;
-
-    ChunkRegs R;
-    if (nch > 0) fetch_chunk(p, 0, h, kh, r0, R);
-    for (int c = 0; c < nch; ++c) {
-        const int t0 = c * GC, n = min(GC, p.T - t0);
-        // chunk c's inputs and the state (fp16) into LDS
-#pragma unroll
-        for (int pi = 0; pi < 4; ++pi) {
-            const int idx = pi * 256 + tid, i = idx >> 4, c8 = (idx & 15) * 8;
-            *reinterpret_cast<uint4v*>(Ws + i * LD_D + c8) = R.w[pi];
-            *reinterpret_cast<half8*>(Qs + i * LD_D + c8) = bf16x8_to_h8(R.q[pi]);
-            const half8 kv = bf16x8_to_h8(R.k[pi]);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) KT[(c8 + x) * LD_C + i] = kv[x];
-        }
-#pragma unroll
-        for (int pi = 0; pi < 2; ++pi) {
-            const int idx = pi * 256 + tid;
-            *reinterpret_cast<uint4v*>(As + (idx >> 3) * LD_C + (idx & 7) * 8) = R.a[pi];
-            *reinterpret_cast<uint4v*>(Us + idx * 4) = R.u[pi];
-        }
-        if (tid < GC) gam[tid] = R.gam;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) S16[acc_row(e, l) * LD_D + 32 * w + (l & 31)] = (_Float16)S[e];
-        __syncthreads();
-        // the next chunk's inputs travel while this one is computed
-        if (c + 1 < nch) fetch_chunk(p, c + 1, h, kh, r0, R);
-
-        // waves 0, 1: X = W S0^T (rows 32 w ..); waves 2, 3: Y = Q S0^T (rows 32 (w - 2) ..)
-        const int ti = w & 1;
-        float16v XY = (float16v)0.f;
-        mma_rows<GD>((w < 2 ? Ws : Qs) + 32 * ti * LD_D, LD_D, S16, LD_D, XY);
-        const float bn = __expf(gam[n - 1]);
-        if (w < 2) {
-            // U = Ut - W S0^T (zero past the chunk's last token), as U^T and
-            // as U^T scaled by e^{gam_n - gam_j} for the state update
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int i = 32 * ti + acc_row(e, l), r = l & 31;
-                const float u = i < n ? Us[i * 32 + r] - XY[e] : 0.f;
-                UT[r * LD_C + i] = (_Float16)u;
-                UdT[r * LD_C + i] = (_Float16)(u * __expf(gam[n - 1] - gam[i]));
-            }
-        }
-        __syncthreads();
-        if (w >= 2) {
-            // O = diag(b) Q S0^T + A U for rows 32 (w - 2) ..
-            float16v Z = (float16v)0.f;
-            mma_rows<GC>(As + 32 * ti * LD_C, LD_C, UT, LD_C, Z);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int i = 32 * ti + acc_row(e, l), r = l & 31;
-                if (i < n) {
-                    const float ov = __expf(gam[i]) * XY[e] + Z[e];
-                    p.o[((size_t)(t0 + i) * p.hv + h) * GD + r0 + r] = (uint16_t)f32_to_bf16(ov);
-                }
-            }
-        }
-        // S1 = b_n S0 + U^T diag(e^{gam_n - gam}) K, tile w
-#pragma unroll
-        for (int e = 0; e < 16; ++e) S[e] *= bn;
-        mma_rows<GC>(UdT, LD_C, KT + 32 * w * LD_C, LD_C, S);
-        __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+        gdn_chunk(p, c, h, z, w, stage0, S16, UT, ro, S);
+        if (c + 1 < nch) gdn_chunk(p, c + 1, h, z, w, stage1, S16, UT, ro, S);
     }
     if (p.s_out) {
 #pragma unroll
@@ -356,6 +434,6 @@ extern "C" int moe_gdn_scan(const uint16_t* q, const uint16_t* k, const uint16_t
     const int nch = (T + moe::GC - 1) / moe::GC;
     if (nch > 0) hipLaunchKernelGGL(moe::gdn_prep, dim3(nch, hv), dim3(256), 0, st, p);
     // (with no tokens the scan kernel only passes the state through)
-    hipLaunchKernelGGL(moe::gdn_scan, dim3(hv, moe::GD / 32), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(moe::gdn_scan, dim3(hv, moe::GD / 32), dim3(448), 0, st, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
