@@ -109,18 +109,53 @@ struct GdnArgs {
 
 // ------------------------------------------------------------------ prep
 
-__global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
-    __shared__ __attribute__((aligned(16))) _Float16 Ks[GC * LD_D], Qs[GC * LD_D];
-    __shared__ __attribute__((aligned(16))) _Float16 VbT[GD * LD_C], KbT[GD * LD_C], KdT[GD * LD_C];
-    __shared__ __attribute__((aligned(16))) _Float16 Ts[GC * LD_C];
-    __shared__ __attribute__((aligned(16))) float Lp[GC * GC];   // row i: L[i][4q+s] at s*16+q
+// LDS of gdn_prep, one region reused across the phases (byte offsets):
+//   load / K K^T, Q K^T   Ks [0, 17408)   Qs [17408, 34816)   KdT [34816, 53248)
+//   triangular solve      Lp [34816, 51200)   (KdT copied out first)
+//   (A staged)            [17408, 26624)      (Qs read before)
+//   Ut, W                 Ts [0, 9216)  VbT [9216, 27648)  KbT [27648, 46080)
+//   (Ut, W staged)        [0, 32768) and [32768, 50176)
+// so that three workgroups fit on a compute unit.
+constexpr int PR_QS = GC * LD_D * 2, PR_KD = 2 * GC * LD_D * 2, PR_LP = PR_KD;
+constexpr int PR_VB = GC * LD_C * 2, PR_KB = PR_VB + GD * LD_C * 2;
+constexpr int PR_BYTES = PR_KD + GD * LD_C * 2;
+static_assert(PR_LP + GC * GC * 4 <= PR_BYTES && PR_KB + GD * LD_C * 2 <= PR_BYTES &&
+              4 * UT_SLICE + GC * LD_D * 2 <= PR_BYTES && PR_QS + GC * LD_C * 2 <= PR_LP, "prep LDS");
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void gdn_prep(GdnArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[PR_BYTES];
     __shared__ float gam[GC], bet[GC];
+    _Float16* Ks = reinterpret_cast<_Float16*>(lds);
+    _Float16* Qs = reinterpret_cast<_Float16*>(lds + PR_QS);
+    _Float16* KdT = reinterpret_cast<_Float16*>(lds + PR_KD);
+    float* Lp = reinterpret_cast<float*>(lds + PR_LP);          // row i: L[i][4q+s] at s*16+q
+    _Float16* Ts = reinterpret_cast<_Float16*>(lds);
+    _Float16* VbT = reinterpret_cast<_Float16*>(lds + PR_VB);
+    _Float16* KbT = reinterpret_cast<_Float16*>(lds + PR_KB);
     const int c = blockIdx.x, h = blockIdx.y;
     const int kh = h / (p.hv / p.hk);
     const int t0 = c * GC, n = min(GC, p.T - t0);
     const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
     uint8_t* blk = p.ws + ((size_t)c * p.hv + h) * GW_BLK;
 
+    // this thread's rows: token i = tid % 64, channels 32 (tid / 64) .. +31
+    // (so that a wave's transposed writes cover 64 consecutive tokens of a
+    // channel); loaded first, while the decays are summed
+    const int ti_ = tid & 63, cg = tid >> 6;
+    uint4v kw[4], qw[4], vw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kw[u] = qw[u] = vw[u] = (uint4v){0, 0, 0, 0};
+    if (ti_ < n) {
+        const uint4v* kr = reinterpret_cast<const uint4v*>(p.k + ((size_t)(t0 + ti_) * p.hk + kh) * GD + 32 * cg);
+        const uint4v* qr = reinterpret_cast<const uint4v*>(p.q + ((size_t)(t0 + ti_) * p.hk + kh) * GD + 32 * cg);
+        const uint4v* vr = reinterpret_cast<const uint4v*>(p.v + ((size_t)(t0 + ti_) * p.hv + h) * GD + 32 * cg);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            kw[u] = kr[u];
+            qw[u] = qr[u];
+            vw[u] = vr[u];
+        }
+    }
     // cumulative log decay over the chunk (tokens past n: g = 0, beta = 0)
     if (w == 0) {
         float x = l < n ? p.g[(size_t)(t0 + l) * p.hv + h] : 0.f;
@@ -134,41 +169,19 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
         reinterpret_cast<float*>(blk + IMG_GAM)[l] = x;
     }
     __syncthreads();
-    // K, Q rows as fp16; beta v, beta b k and e^{gam_n - gam} k transposed
-    // ([channel][token]); rows past the chunk's last token are zero.  Thread:
-    // token i = tid % 64, channels 32 (tid / 64) .. +31, so that the
-    // transposed writes of a wave cover 64 consecutive tokens of a channel.
     const float gn = gam[GC - 1];     // = gam[n - 1]: g is zero past n
+    // K, Q rows as fp16; e^{gam_n - gam} k transposed ([channel][token])
     {
-        const int i = tid & 63, cg = tid >> 6;
-        uint4v kw[4], qw[4], vw[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) kw[u] = qw[u] = vw[u] = (uint4v){0, 0, 0, 0};
-        if (i < n) {
-            const uint4v* kr = reinterpret_cast<const uint4v*>(p.k + ((size_t)(t0 + i) * p.hk + kh) * GD + 32 * cg);
-            const uint4v* qr = reinterpret_cast<const uint4v*>(p.q + ((size_t)(t0 + i) * p.hk + kh) * GD + 32 * cg);
-            const uint4v* vr = reinterpret_cast<const uint4v*>(p.v + ((size_t)(t0 + i) * p.hv + h) * GD + 32 * cg);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                kw[u] = kr[u];
-                qw[u] = qr[u];
-                vw[u] = vr[u];
-            }
-        }
-        const float bv = bet[i], bk = bet[i] * __expf(gam[i]), dk = __expf(gn - gam[i]);
+        const float dk = __expf(gn - gam[ti_]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c8 = 32 * cg + 8 * u;
-            *reinterpret_cast<half8*>(Ks + i * LD_D + c8) = bf16x8_to_h8(kw[u]);
-            *reinterpret_cast<half8*>(Qs + i * LD_D + c8) = bf16x8_to_h8(qw[u]);
+            *reinterpret_cast<half8*>(Ks + ti_ * LD_D + c8) = bf16x8_to_h8(kw[u]);
+            *reinterpret_cast<half8*>(Qs + ti_ * LD_D + c8) = bf16x8_to_h8(qw[u]);
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const float kf = bf16_to_f32(x & 1 ? kw[u][x >> 1] >> 16 : kw[u][x >> 1] & 0xFFFFu);
-                const float vf = bf16_to_f32(x & 1 ? vw[u][x >> 1] >> 16 : vw[u][x >> 1] & 0xFFFFu);
-                VbT[(c8 + x) * LD_C + i] = (_Float16)(bv * vf);
-                KbT[(c8 + x) * LD_C + i] = (_Float16)(bk * kf);
-                KdT[(c8 + x) * LD_C + i] = (_Float16)(dk * kf);
-            }
+            for (int x = 0; x < 8; ++x)
+                KdT[(c8 + x) * LD_C + ti_] =
+                    (_Float16)(dk * bf16_to_f32(x & 1 ? kw[u][x >> 1] >> 16 : kw[u][x >> 1] & 0xFFFFu));
         }
     }
     __syncthreads();
@@ -178,22 +191,26 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
     for (int idx = tid; idx < GD * LD_C / 8; idx += 256)
         reinterpret_cast<uint4v*>(blk + IMG_KD)[idx] = reinterpret_cast<const uint4v*>(KdT)[idx];
     // K K^T and Q K^T: wave w owns the 32 x 32 tile (w/2, w%2)
+    const int ti = w >> 1, tj = w & 1;
+    float16v aG = (float16v)0.f, aQ = (float16v)0.f;
+    mma_rows<GD>(Ks + 32 * ti * LD_D, LD_D, Ks + 32 * tj * LD_D, LD_D, aG);
+    mma_rows<GD>(Qs + 32 * ti * LD_D, LD_D, Ks + 32 * tj * LD_D, LD_D, aQ);
+    __syncthreads();                  // KdT copied, Ks and Qs read: Lp may overwrite KdT
     {
-        const int ti = w >> 1, tj = w & 1;
-        float16v aG = (float16v)0.f, aQ = (float16v)0.f;
-        mma_rows<GD>(Ks + 32 * ti * LD_D, LD_D, Ks + 32 * tj * LD_D, LD_D, aG);
-        mma_rows<GD>(Qs + 32 * ti * LD_D, LD_D, Ks + 32 * tj * LD_D, LD_D, aQ);
-        _Float16* Aw = reinterpret_cast<_Float16*>(blk + IMG_A);
+        // A is staged in the Qs region in its image layout, then stored
+        _Float16* As = reinterpret_cast<_Float16*>(lds + PR_QS);
         const int j = 32 * tj + (l & 31);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int i = 32 * ti + acc_row(e, l);
             const float d = j <= i ? __expf(gam[i] - gam[j]) : 0.f;
             Lp[i * GC + (j & 3) * 16 + (j >> 2)] = j < i ? bet[i] * d * aG[e] : 0.f;
-            Aw[i * LD_C + j] = (_Float16)(d * aQ[e]);
+            As[i * LD_C + j] = (_Float16)(d * aQ[e]);
         }
     }
     __syncthreads();
+    for (int idx = tid; idx < GC * LD_C / 8; idx += 256)
+        reinterpret_cast<uint4v*>(blk + IMG_A)[idx] = reinterpret_cast<const uint4v*>(lds + PR_QS)[idx];
     // T = (I + L)^{-1}, L strictly lower: column m by the quad of lanes
     // 4m .. 4m+3, lane s holding rows 4q + s (q = 0..15) in registers;
     // row i: T[i][m] = [i == m] - sum_{j<i} L[i][j] T[j][m] (the rows j >= i
@@ -223,27 +240,56 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs p) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) Ts[(4 * q + s) * LD_C + m] = (_Float16)tq[q];
     }
-    __syncthreads();
-    // Ut = T (beta V) and W = T (beta b K): wave w owns row tile w/2 and
-    // column tiles 2 (w%2), 2 (w%2) + 1 of both (column tile = state slice)
+    __syncthreads();                  // Lp read: VbT and KbT may overwrite it
+    // beta v and beta b k transposed ([channel][token])
     {
-        const int ti = w >> 1;
-        _Float16* Ww = reinterpret_cast<_Float16*>(blk + IMG_W);
+        const float bv = bet[ti_], bk = bet[ti_] * __expf(gam[ti_]);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tc = 2 * (w & 1) + u;
-            float16v aU = (float16v)0.f, aW = (float16v)0.f;
-            mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, VbT + 32 * tc * LD_C, LD_C, aU);
-            mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, KbT + 32 * tc * LD_C, LD_C, aW);
-            float* Ut = reinterpret_cast<float*>(blk + IMG_COMMON + tc * UT_SLICE);
+        for (int u = 0; u < 4; ++u) {
+            const int c8 = 32 * cg + 8 * u;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int i = 32 * ti + acc_row(e, l);
-                Ut[i * 32 + (l & 31)] = aU[e];
-                Ww[i * LD_D + 32 * tc + (l & 31)] = (_Float16)aW[e];
+            for (int x = 0; x < 8; ++x) {
+                const float kf = bf16_to_f32(x & 1 ? kw[u][x >> 1] >> 16 : kw[u][x >> 1] & 0xFFFFu);
+                const float vf = bf16_to_f32(x & 1 ? vw[u][x >> 1] >> 16 : vw[u][x >> 1] & 0xFFFFu);
+                VbT[(c8 + x) * LD_C + ti_] = (_Float16)(bv * vf);
+                KbT[(c8 + x) * LD_C + ti_] = (_Float16)(bk * kf);
             }
         }
     }
+    __syncthreads();
+    // Ut = T (beta V) and W = T (beta b K): wave w owns row tile w/2 and
+    // column tiles 2 (w%2), 2 (w%2) + 1 of both (column tile = state slice)
+    float16v aU[2], aW[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tc = 2 * (w & 1) + u;
+        aU[u] = aW[u] = (float16v)0.f;
+        mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, VbT + 32 * tc * LD_C, LD_C, aU[u]);
+        mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, KbT + 32 * tc * LD_C, LD_C, aW[u]);
+    }
+    __syncthreads();                  // Ts, VbT, KbT read: the region stages the outputs
+    // staged in their image layouts (Ut: 4 slices of [64][32] fp32, then W
+    // [64][136] fp16), then stored with 16-byte writes
+    {
+        float* Us = reinterpret_cast<float*>(lds);
+        _Float16* Wst = reinterpret_cast<_Float16*>(lds + 4 * UT_SLICE);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tc = 2 * (w & 1) + u;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int i = 32 * ti + acc_row(e, l);
+                Us[tc * (UT_SLICE / 4) + i * 32 + (l & 31)] = aU[u][e];
+                Wst[i * LD_D + 32 * tc + (l & 31)] = (_Float16)aW[u][e];
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 4 * UT_SLICE / 16; idx += 256)
+        reinterpret_cast<uint4v*>(blk + IMG_COMMON)[idx] = reinterpret_cast<const uint4v*>(lds)[idx];
+    for (int idx = tid; idx < GC * LD_D / 8; idx += 256)
+        reinterpret_cast<uint4v*>(blk + IMG_W)[idx] =
+            reinterpret_cast<const uint4v*>(lds + 4 * UT_SLICE)[idx];
 }
 
 // ------------------------------------------------------------------ scan
