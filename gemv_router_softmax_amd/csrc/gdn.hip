@@ -57,10 +57,10 @@ constexpr int IMG_KD = IMG_W + GC * LD_D * 2;     // fp16 (e^{gam_n - gam_j} k_j
 constexpr int IMG_A = IMG_KD + GD * LD_C * 2;     // fp16 A [64][72]
 constexpr int IMG_GAM = IMG_A + GC * LD_C * 2;    // fp32 gam [64] (in a 1 KB slot)
 constexpr int IMG_COMMON = IMG_GAM + 1024;        // 62 KB
-constexpr int UT_SLICE = GC * 32 * 4;             // fp32 Ut[:, 32 z .. 32 z + 31] as [64][32]
+constexpr int UT_SLICE = GC * 32 * 2;             // fp16 Ut[:, 32 z .. 32 z + 31] as [64][32]
 constexpr int GW_BLK = IMG_COMMON + 4 * UT_SLICE;
-constexpr int STAGE_IMG = IMG_COMMON + UT_SLICE;  // 70 KB moved per chunk and slice
-constexpr int STAGE = STAGE_IMG + 2048;           // one image and two stand-in slots
+constexpr int STAGE_IMG = IMG_COMMON + UT_SLICE;  // 66 KB moved per chunk and slice
+constexpr int STAGE = STAGE_IMG;                  // one LDS stage holds one image
 static_assert(IMG_COMMON % 1024 == 0 && STAGE_IMG % 1024 == 0 && STAGE >= STAGE_IMG, "1 KB slots");
 static_assert(GW_BLK % 256 == 0, "workspace blocks stay 256-byte aligned");
 constexpr uint32_t GDN_OOB = 0x80000000u;         // beyond every buffer range
@@ -220,13 +220,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         float tq[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) tq[q] = 0.f;
+        // row i + 1 of L is read while row i is reduced
+        float4v lcur[4], lnxt[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) lcur[b] = reinterpret_cast<const float4v*>(Lp + s * 16)[b];
 #pragma unroll
         for (int i = 0; i < GC; ++i) {
-            const float4v* lr = reinterpret_cast<const float4v*>(Lp + i * GC + s * 16);
+            if (i + 1 < GC) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    lnxt[b] = reinterpret_cast<const float4v*>(Lp + (i + 1) * GC + s * 16)[b];
+            }
             float part[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const float4v lv = lr[b];
+                const float4v lv = lcur[b];
                 part[b] = lv[0] * tq[4 * b];
 #pragma unroll
                 for (int x = 1; x < 4; ++x) part[b] = fmaf(lv[x], tq[4 * b + x], part[b]);
@@ -236,6 +244,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             sum += dpp_f<DPP_XOR2>(sum);
             const float tim = (i == m ? 1.f : 0.f) - sum;
             if (s == (i & 3)) tq[i >> 2] = tim;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) lcur[b] = lnxt[b];
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q) Ts[(4 * q + s) * LD_C + m] = (_Float16)tq[q];
@@ -268,10 +278,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, KbT + 32 * tc * LD_C, LD_C, aW[u]);
     }
     __syncthreads();                  // Ts, VbT, KbT read: the region stages the outputs
-    // staged in their image layouts (Ut: 4 slices of [64][32] fp32, then W
+    // staged in their image layouts (Ut: 4 slices of [64][32] fp16, then W
     // [64][136] fp16), then stored with 16-byte writes
     {
-        float* Us = reinterpret_cast<float*>(lds);
+        _Float16* Us = reinterpret_cast<_Float16*>(lds);
         _Float16* Wst = reinterpret_cast<_Float16*>(lds + 4 * UT_SLICE);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int i = 32 * ti + acc_row(e, l);
-                Us[tc * (UT_SLICE / 4) + i * 32 + (l & 31)] = aU[u][e];
+                Us[tc * (UT_SLICE / 2) + i * 32 + (l & 31)] = (_Float16)aU[u][e];
                 Wst[i * LD_D + 32 * tc + (l & 31)] = (_Float16)aW[u][e];
             }
         }
@@ -310,11 +320,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gdn_rsrc(const void* base, uin
 }
 
 // Mover m's share of chunk c's image for state slice z into one LDS stage:
-// slots 24 m .. 24 m + 23, where 1 KB slot j comes from byte j K of the
-// block's common part (j < 62) or of the slice's Ut columns (j = 62 .. 69);
-// slots 70 and 71 are stand-ins (an out-of-range offset: no memory access)
-// that land in the stage's spare 2 KB.
-constexpr int MV_SLOTS = 24;
+// slots 22 m .. 22 m + 21, where 1 KB slot j comes from byte j K of the
+// block's common part (j < 62) or of the slice's Ut columns (j = 62 .. 65).
+constexpr int MV_SLOTS = 22;
+static_assert(3 * MV_SLOTS * 1024 == STAGE_IMG, "three movers cover an image");
 __device__ __forceinline__ void gdn_issue(const GdnArgs& p, int c, int h, int z, int m,
                                           uint8_t* __restrict__ stage) {
     const uint8_t* blk = gdn_uniform(p.ws + ((size_t)c * p.hv + h) * GW_BLK);
@@ -323,10 +332,9 @@ __device__ __forceinline__ void gdn_issue(const GdnArgs& p, int c, int h, int z,
 #pragma unroll
     for (int i = 0; i < MV_SLOTS; ++i) {
         const int j = m * MV_SLOTS + i;
-        const uint32_t src = j < IMG_COMMON / 1024 ? (uint32_t)j * 1024
-                             : j < STAGE_IMG / 1024
-                                 ? (uint32_t)(IMG_COMMON + z * UT_SLICE + (j - IMG_COMMON / 1024) * 1024)
-                                 : GDN_OOB;
+        const uint32_t src = j < IMG_COMMON / 1024
+                                 ? (uint32_t)j * 1024
+                                 : (uint32_t)(IMG_COMMON + z * UT_SLICE + (j - IMG_COMMON / 1024) * 1024);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (gdn_lds_t)(stage + j * 1024), 16, lane16, src, 0, 0);
     }
 }
@@ -350,9 +358,9 @@ __device__ __forceinline__ void gdn_barrier() {
 // The image movers (waves 4, 5, 6): chunk c + 1 into nxt while the compute
 // waves work on chunk c.  They read no LDS and the compute waves issue no
 // image loads, so no wait for the loads ever lands in the compute waves'
-// code.  The 70 loads of an image are split so that no mover holds up a
-// barrier: mover 0 issues slots 0..23 after barrier (1) (the compute waves
-// then multiply for a while), movers 1 and 2 slots 24..47 and 48..71 after
+// code.  The 66 loads of an image are split so that no mover holds up a
+// barrier: mover 0 issues slots 0..21 after barrier (1) (the compute waves
+// then multiply for a while), movers 1 and 2 slots 22..43 and 44..65 after
 // barrier (2).  Three barriers per chunk, matched one for one by gdn_chunk.
 __device__ __forceinline__ void gdn_mover_chunk(const GdnArgs& p, int c, int nch, int h, int z,
                                                 int m, uint8_t* __restrict__ nxt) {
@@ -381,7 +389,7 @@ __device__ __forceinline__ void gdn_chunk(const GdnArgs& p, int c, int h, int z,
     const _Float16* KdT = reinterpret_cast<const _Float16*>(cur + IMG_KD);
     const _Float16* As = reinterpret_cast<const _Float16*>(cur + IMG_A);
     const float* gam = reinterpret_cast<const float*>(cur + IMG_GAM);
-    const float* Us = reinterpret_cast<const float*>(cur + IMG_COMMON);
+    const _Float16* Us = reinterpret_cast<const _Float16*>(cur + IMG_COMMON);
 
     // waves 0, 1: X = W S0^T (rows 32 w ..); waves 2, 3: Y = Q S0^T (rows 32 (w - 2) ..)
     const int ti = w & 1;
@@ -393,7 +401,7 @@ __device__ __forceinline__ void gdn_chunk(const GdnArgs& p, int c, int h, int z,
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int i = 32 * ti + acc_row(e, l), r = l & 31;
-            UT[r * LD_C + i] = (_Float16)(Us[i * 32 + r] - XY[e]);
+            UT[r * LD_C + i] = (_Float16)((float)Us[i * 32 + r] - XY[e]);
         }
     }
     gdn_barrier();                                // (2)
