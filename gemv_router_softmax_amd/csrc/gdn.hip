@@ -55,7 +55,7 @@ constexpr int IMG_Q = 0;                          // fp16 Q [64][136]
 constexpr int IMG_W = IMG_Q + GC * LD_D * 2;      // fp16 W [64][136]
 constexpr int IMG_KD = IMG_W + GC * LD_D * 2;     // fp16 (e^{gam_n - gam_j} k_j)^T [128][72]
 constexpr int IMG_A = IMG_KD + GD * LD_C * 2;     // fp16 A [64][72]
-constexpr int IMG_GAM = IMG_A + GC * LD_C * 2;    // fp32 gam [64] (in a 1 KB slot)
+constexpr int IMG_GAM = IMG_A + GC * LD_C * 2;    // fp32 gam [64], then e^{gam} [64] (a 1 KB slot)
 constexpr int IMG_COMMON = IMG_GAM + 1024;        // 62 KB
 constexpr int UT_SLICE = GC * 32 * 2;             // fp16 Ut[:, 32 z .. 32 z + 31] as [64][32]
 constexpr int GW_BLK = IMG_COMMON + 4 * UT_SLICE;
@@ -167,6 +167,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         gam[l] = x;
         bet[l] = l < n ? p.beta[(size_t)(t0 + l) * p.hv + h] : 0.f;
         reinterpret_cast<float*>(blk + IMG_GAM)[l] = x;
+        reinterpret_cast<float*>(blk + IMG_GAM)[GC + l] = __expf(x);
     }
     __syncthreads();
     const float gn = gam[GC - 1];     // = gam[n - 1]: g is zero past n
@@ -388,7 +389,7 @@ __device__ __forceinline__ void gdn_chunk(const GdnArgs& p, int c, int h, int z,
     const _Float16* Ws = reinterpret_cast<const _Float16*>(cur + IMG_W);
     const _Float16* KdT = reinterpret_cast<const _Float16*>(cur + IMG_KD);
     const _Float16* As = reinterpret_cast<const _Float16*>(cur + IMG_A);
-    const float* gam = reinterpret_cast<const float*>(cur + IMG_GAM);
+    const float* bexp = reinterpret_cast<const float*>(cur + IMG_GAM) + GC;   // e^{gam}
     const _Float16* Us = reinterpret_cast<const _Float16*>(cur + IMG_COMMON);
 
     // waves 0, 1: X = W S0^T (rows 32 w ..); waves 2, 3: Y = Q S0^T (rows 32 (w - 2) ..)
@@ -413,13 +414,13 @@ __device__ __forceinline__ void gdn_chunk(const GdnArgs& p, int c, int h, int z,
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int i = 32 * ti + acc_row(e, l);
-            const float ov = __expf(gam[i]) * XY[e] + Zo[e];
+            const float ov = bexp[i] * XY[e] + Zo[e];
             const uint32_t off = i < n ? ob + (uint32_t)(i * p.hv * GD * 2) : GDN_OOB;
             __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16(ov), ro, off, 0, 0);
         }
     }
     // S1 = b_n S0 + U^T (e^{gam_n - gam} K), tile w
-    const float bn = __expf(gam[n - 1]);
+    const float bn = bexp[n - 1];
 #pragma unroll
     for (int e = 0; e < 16; ++e) S[e] *= bn;
     mma_rows<GC>(UT, LD_C, KdT + 32 * w * LD_C, LD_C, S);

@@ -66,6 +66,17 @@ def test_gdn_full_size_t2048():
     _check(synth.make_gdn(2048, synth.GDN_HK, synth.GDN_HV, seed=1))
 
 
+def test_gdn_longest_sequence():
+    """MOE_T_MAX tokens (1024 chunk steps) with two value heads over one key
+    head: every output and the final state."""
+    _check(synth.make_gdn(65536, 1, 2, seed=11))
+
+
+def test_gdn_most_heads():
+    """MOE_GDN_HEADS_MAX value heads over 8 key heads."""
+    _check(synth.make_gdn(100, 8, 64, seed=13))
+
+
 def test_gdn_t0_passes_state():
     x = synth.make_gdn(1, 1, 2, seed=3)
     s0 = torch.from_numpy(x.s0).cuda()
