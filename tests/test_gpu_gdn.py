@@ -77,6 +77,21 @@ def test_gdn_most_heads():
     _check(synth.make_gdn(100, 8, 64, seed=13))
 
 
+@pytest.mark.parametrize("regime", ["strong_decay", "no_decay"])
+def test_gdn_decay_extremes(regime):
+    """Strong decay (about e^-1 per token: within a chunk the old state and
+    early tokens fall below fp16's range in the scaled operands) and none at
+    all (g = 0: nothing is forgotten, the state only changes by the delta
+    writes)."""
+    x = synth.make_gdn(300, 2, 4, seed=17)
+    rng = np.random.default_rng(17)
+    if regime == "strong_decay":
+        g = (-rng.uniform(0.5, 1.5, x.g.shape)).astype(np.float32)
+    else:
+        g = np.zeros_like(x.g)
+    _check(synth.GdnInputs(x.q, x.k, x.v, g, x.beta, x.s0))
+
+
 def test_gdn_t0_passes_state():
     x = synth.make_gdn(1, 1, 2, seed=3)
     s0 = torch.from_numpy(x.s0).cuda()
