@@ -24,8 +24,8 @@
 //
 //   gdn_prep  grid (chunks, hv): per chunk and head, K K^T and Q K^T on
 //             MFMA, the masks and decays, T by forward substitution (fp32,
-//             one quad of lanes per column), Ut and W on MFMA; writes Ut
-//             (fp32), W and A (fp16) and gam to the workspace.
+//             one quad of lanes per column), Ut and W on MFMA; writes Q, W,
+//             A, Ut (fp16), the decayed K^T (fp16) and gam to the workspace.
 //   gdn_scan  grid (hv, 4): one workgroup per head and 32-row slice of the
 //             state (rows are value channels, independent of one another).
 //             The slice (32 x 128 fp32) stays in four compute waves' MFMA
