@@ -63,7 +63,6 @@ constexpr int STAGE_IMG = IMG_COMMON + UT_SLICE;  // 66 KB moved per chunk and s
 constexpr int STAGE = STAGE_IMG;                  // one LDS stage holds one image
 static_assert(IMG_COMMON % 1024 == 0 && STAGE_IMG % 1024 == 0 && STAGE >= STAGE_IMG, "1 KB slots");
 static_assert(GW_BLK % 256 == 0, "workspace blocks stay 256-byte aligned");
-constexpr uint32_t GDN_OOB = 0x80000000u;         // beyond every buffer range
 
 typedef float float16v __attribute__((ext_vector_type(16)));
 
@@ -374,12 +373,34 @@ __device__ __forceinline__ void gdn_mover_chunk(const GdnArgs& p, int c, int nch
     gdn_barrier();                                // (3)
 }
 
+// Output rows of one chunk (waves 2, 3: rows 32 (w - 2) .. of the chunk
+// starting at token t0), packed as bf16 pairs in accumulator order.  The
+// per-lane offset is computed once; each element adds a wave-uniform step
+// (the scalar offset operand).  Rows past T lie past the buffer's range,
+// so their stores write nothing; every offset stays below 2^32 (at most
+// 65599 token rows of at most 64 heads x 256 bytes).
+__device__ __forceinline__ void gdn_store_out(const GdnArgs& p, int t0, int h, int r0, int ti,
+                                              const uint32_t (&pk)[8], __amdgpu_buffer_rsrc_t ro) {
+    const int l = threadIdx.x & 63;
+    const uint32_t rs = (uint32_t)p.hv * GD * 2;      // bytes per token of o
+    const uint32_t voff = (uint32_t)(((size_t)t0 * p.hv + h) * GD + r0 + (l & 31)) * 2 + 4u * (l >> 5) * rs;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t soff = (uint32_t)(32 * ti + 8 * (e >> 2) + (e & 3)) * rs;
+        const uint32_t v = (e & 1) ? pk[e >> 1] >> 16 : pk[e >> 1];
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, ro, voff, soff, 0);
+    }
+}
+
 // One chunk of the scan for the state slice held in S (compute waves 0-3).
-// cur holds chunk c's image.
+// cur holds chunk c's image.  Waves 2, 3 form this chunk's outputs but
+// store them during the next chunk's U phase (pend, from token pend_t0;
+// -1: none), where they would otherwise wait for waves 0, 1.
 __device__ __forceinline__ void gdn_chunk(const GdnArgs& p, int c, int h, int z, int w,
                                           const uint8_t* __restrict__ cur,
                                           _Float16* __restrict__ S16, _Float16* __restrict__ UT,
-                                          __amdgpu_buffer_rsrc_t ro, float16v& S) {
+                                          __amdgpu_buffer_rsrc_t ro, float16v& S, uint32_t (&pend)[8],
+                                          int& pend_t0) {
     const int l = threadIdx.x & 63, r0 = z * 32;
     const int t0 = c * GC, n = min(GC, p.T - t0);
 #pragma unroll
@@ -404,26 +425,31 @@ __device__ __forceinline__ void gdn_chunk(const GdnArgs& p, int c, int h, int z,
             const int i = 32 * ti + acc_row(e, l), r = l & 31;
             UT[r * LD_C + i] = (_Float16)((float)Us[i * 32 + r] - XY[e]);
         }
+    } else if (pend_t0 >= 0) {
+        gdn_store_out(p, pend_t0, h, r0, ti, pend, ro);
     }
     gdn_barrier();                                // (2)
-    if (w >= 2) {
-        // O = diag(b) Q S0^T + A U for rows 32 (w - 2) ..
-        float16v Zo = (float16v)0.f;
-        mma_rows<GC>(As + 32 * ti * LD_C, LD_C, UT, LD_C, Zo);
-        const uint32_t ob = (uint32_t)(((size_t)t0 * p.hv + h) * GD + r0 + (l & 31)) * 2;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = 32 * ti + acc_row(e, l);
-            const float ov = bexp[i] * XY[e] + Zo[e];
-            const uint32_t off = i < n ? ob + (uint32_t)(i * p.hv * GD * 2) : GDN_OOB;
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16(ov), ro, off, 0, 0);
-        }
-    }
-    // S1 = b_n S0 + U^T (e^{gam_n - gam} K), tile w
+    // S1 = b_n S0 + U^T (e^{gam_n - gam} K), tile w; waves 2, 3 also
+    // O = diag(b) Q S0^T + A U for rows 32 (w - 2) .. (two independent MFMA
+    // chains in one block)
     const float bn = bexp[n - 1];
 #pragma unroll
     for (int e = 0; e < 16; ++e) S[e] *= bn;
-    mma_rows<GC>(UT, LD_C, KdT + 32 * w * LD_C, LD_C, S);
+    if (w >= 2) {
+        float16v Zo = (float16v)0.f;
+        mma_rows<GC>(As + 32 * ti * LD_C, LD_C, UT, LD_C, Zo);
+        mma_rows<GC>(UT, LD_C, KdT + 32 * w * LD_C, LD_C, S);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i0 = 32 * ti + acc_row(2 * j, l), i1 = 32 * ti + acc_row(2 * j + 1, l);
+            const float o0 = bexp[i0] * XY[2 * j] + Zo[2 * j];
+            const float o1 = bexp[i1] * XY[2 * j + 1] + Zo[2 * j + 1];
+            pend[j] = f32_to_bf16(o0) | (f32_to_bf16(o1) << 16);
+        }
+        pend_t0 = t0;
+    } else {
+        mma_rows<GC>(UT, LD_C, KdT + 32 * w * LD_C, LD_C, S);
+    }
     gdn_barrier();                                // (3)
 }
 
@@ -453,10 +479,13 @@ __global__ __launch_bounds__(448) void gdn_scan(GdnArgs p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e)
         S[e] = p.s0 ? p.s0[((size_t)h * GD + r0 + acc_row(e, l)) * GD + 32 * w + (l & 31)] : 0.f;
+    uint32_t pend[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int pend_t0 = -1;
     for (int c = 0; c < nch; c += 2) {
-        gdn_chunk(p, c, h, z, w, stage0, S16, UT, ro, S);
-        if (c + 1 < nch) gdn_chunk(p, c + 1, h, z, w, stage1, S16, UT, ro, S);
+        gdn_chunk(p, c, h, z, w, stage0, S16, UT, ro, S, pend, pend_t0);
+        if (c + 1 < nch) gdn_chunk(p, c + 1, h, z, w, stage1, S16, UT, ro, S, pend, pend_t0);
     }
+    if (w >= 2 && pend_t0 >= 0) gdn_store_out(p, pend_t0, h, r0, w & 1, pend, ro);
     if (p.s_out) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
