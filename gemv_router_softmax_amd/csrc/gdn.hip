@@ -109,28 +109,29 @@ struct GdnArgs {
 // ------------------------------------------------------------------ prep
 
 // LDS of gdn_prep, one region reused across the phases (byte offsets):
-//   load / K K^T, Q K^T   Ks [0, 17408)   Qs [17408, 34816)   KdT [34816, 53248)
-//   triangular solve      Lp [34816, 51200)   (KdT copied out first)
-//   (A staged)            [17408, 26624)      (Qs read before)
-//   Ut, W                 Ts [0, 9216)  VbT [9216, 27648)  KbT [27648, 46080)
-//   (Ut, W staged)        [0, 32768) and [32768, 50176)
-// so that three workgroups fit on a compute unit.
-constexpr int PR_QS = GC * LD_D * 2, PR_KD = 2 * GC * LD_D * 2, PR_LP = PR_KD;
-constexpr int PR_VB = GC * LD_C * 2, PR_KB = PR_VB + GD * LD_C * 2;
-constexpr int PR_BYTES = PR_KD + GD * LD_C * 2;
-static_assert(PR_LP + GC * GC * 4 <= PR_BYTES && PR_KB + GD * LD_C * 2 <= PR_BYTES &&
-              4 * UT_SLICE + GC * LD_D * 2 <= PR_BYTES && PR_QS + GC * LD_C * 2 <= PR_LP, "prep LDS");
+//   K K^T, Q K^T          Ks [0, 17408)       Qs [17408, 34816)
+//   masks, decays         Lp [0, 16384)       A staged [17408, 26624) (Qs read before)
+//   triangular solve      Lp read, T written to Ts [26624, 35840)
+//   Ut, then W            beta V, then beta b K (transposed) [0, 18432); Ts
+//   (Ut, W staged)        [0, 16384) and [16384, 33792)
+// 35 KB, so that four workgroups fit on a compute unit: 1024 of them (the
+// 32 chunks x 32 heads of 2048 tokens) run in one round.  The Q and
+// decayed-K images go from registers straight to the workspace.
+constexpr int PR_QS = GC * LD_D * 2, PR_A = PR_QS, PR_LP = 0, PR_TS = PR_QS + GC * LD_C * 2;
+constexpr int PR_BT = 0;                          // beta V / beta b K, transposed
+constexpr int PR_BYTES = PR_TS + GC * LD_C * 2;
+static_assert(PR_LP + GC * GC * 4 <= PR_QS && PR_BT + GD * LD_C * 2 <= PR_TS &&
+              4 * UT_SLICE + GC * LD_D * 2 <= PR_BYTES && 2 * PR_QS <= PR_BYTES &&
+              4 * (PR_BYTES + 512) <= 160 * 1024, "prep LDS");
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void gdn_prep(GdnArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_prep(GdnArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[PR_BYTES];
     __shared__ float gam[GC], bet[GC];
     _Float16* Ks = reinterpret_cast<_Float16*>(lds);
     _Float16* Qs = reinterpret_cast<_Float16*>(lds + PR_QS);
-    _Float16* KdT = reinterpret_cast<_Float16*>(lds + PR_KD);
     float* Lp = reinterpret_cast<float*>(lds + PR_LP);          // row i: L[i][4q+s] at s*16+q
-    _Float16* Ts = reinterpret_cast<_Float16*>(lds);
-    _Float16* VbT = reinterpret_cast<_Float16*>(lds + PR_VB);
-    _Float16* KbT = reinterpret_cast<_Float16*>(lds + PR_KB);
+    _Float16* Ts = reinterpret_cast<_Float16*>(lds + PR_TS);
+    _Float16* BT = reinterpret_cast<_Float16*>(lds + PR_BT);
     const int c = blockIdx.x, h = blockIdx.y;
     const int kh = h / (p.hv / p.hk);
     const int t0 = c * GC, n = min(GC, p.T - t0);
@@ -170,35 +171,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
     __syncthreads();
     const float gn = gam[GC - 1];     // = gam[n - 1]: g is zero past n
-    // K, Q rows as fp16; e^{gam_n - gam} k transposed ([channel][token])
+    // K, Q rows as fp16 to LDS; Q also to its image; e^{gam_n - gam} k
+    // transposed ([channel][token]) to its image, a wave's 64 tokens of a
+    // channel in one 128-byte store
     {
         const float dk = __expf(gn - gam[ti_]);
+        _Float16* kd_img = reinterpret_cast<_Float16*>(blk + IMG_KD);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c8 = 32 * cg + 8 * u;
+            const half8 qh = bf16x8_to_h8(qw[u]);
             *reinterpret_cast<half8*>(Ks + ti_ * LD_D + c8) = bf16x8_to_h8(kw[u]);
-            *reinterpret_cast<half8*>(Qs + ti_ * LD_D + c8) = bf16x8_to_h8(qw[u]);
+            *reinterpret_cast<half8*>(Qs + ti_ * LD_D + c8) = qh;
+            *reinterpret_cast<half8*>(blk + IMG_Q + (ti_ * LD_D + c8) * 2) = qh;
 #pragma unroll
             for (int x = 0; x < 8; ++x)
-                KdT[(c8 + x) * LD_C + ti_] =
+                kd_img[(c8 + x) * LD_C + ti_] =
                     (_Float16)(dk * bf16_to_f32(x & 1 ? kw[u][x >> 1] >> 16 : kw[u][x >> 1] & 0xFFFFu));
         }
     }
     __syncthreads();
-    // the Q and decayed-K images as they are
-    for (int idx = tid; idx < GC * LD_D / 8; idx += 256)
-        reinterpret_cast<uint4v*>(blk + IMG_Q)[idx] = reinterpret_cast<const uint4v*>(Qs)[idx];
-    for (int idx = tid; idx < GD * LD_C / 8; idx += 256)
-        reinterpret_cast<uint4v*>(blk + IMG_KD)[idx] = reinterpret_cast<const uint4v*>(KdT)[idx];
     // K K^T and Q K^T: wave w owns the 32 x 32 tile (w/2, w%2)
     const int ti = w >> 1, tj = w & 1;
     float16v aG = (float16v)0.f, aQ = (float16v)0.f;
     mma_rows<GD>(Ks + 32 * ti * LD_D, LD_D, Ks + 32 * tj * LD_D, LD_D, aG);
     mma_rows<GD>(Qs + 32 * ti * LD_D, LD_D, Ks + 32 * tj * LD_D, LD_D, aQ);
-    __syncthreads();                  // KdT copied, Ks and Qs read: Lp may overwrite KdT
+    __syncthreads();                  // Ks and Qs read: Lp and A may overwrite them
     {
-        // A is staged in the Qs region in its image layout, then stored
-        _Float16* As = reinterpret_cast<_Float16*>(lds + PR_QS);
+        // A is staged in its image layout, then stored
+        _Float16* As = reinterpret_cast<_Float16*>(lds + PR_A);
         const int j = 32 * tj + (l & 31);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
     __syncthreads();
     for (int idx = tid; idx < GC * LD_C / 8; idx += 256)
-        reinterpret_cast<uint4v*>(blk + IMG_A)[idx] = reinterpret_cast<const uint4v*>(lds + PR_QS)[idx];
+        reinterpret_cast<uint4v*>(blk + IMG_A)[idx] = reinterpret_cast<const uint4v*>(lds + PR_A)[idx];
     // T = (I + L)^{-1}, L strictly lower: column m by the quad of lanes
     // 4m .. 4m+3, lane s holding rows 4q + s (q = 0..15) in registers;
     // row i: T[i][m] = [i == m] - sum_{j<i} L[i][j] T[j][m] (the rows j >= i
@@ -247,37 +248,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
             for (int b = 0; b < 4; ++b) lcur[b] = lnxt[b];
         }
+        // (Ts lies past Lp and the A staging, which other threads may still read)
 #pragma unroll
         for (int q = 0; q < 16; ++q) Ts[(4 * q + s) * LD_C + m] = (_Float16)tq[q];
     }
-    __syncthreads();                  // Lp read: VbT and KbT may overwrite it
-    // beta v and beta b k transposed ([channel][token])
-    {
-        const float bv = bet[ti_], bk = bet[ti_] * __expf(gam[ti_]);
+    __syncthreads();                  // Lp read: beta V may overwrite it
+    // Ut = T (beta V), then W = T (beta b K), through one transposed
+    // ([channel][token]) region: wave w owns row tile w/2 and column tiles
+    // 2 (w%2), 2 (w%2) + 1 of both (column tile = state slice)
+    float16v aU[2], aW[2];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const float sc = pass == 0 ? bet[ti_] : bet[ti_] * __expf(gam[ti_]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c8 = 32 * cg + 8 * u;
+            const uint4v src = pass == 0 ? vw[u] : kw[u];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const float kf = bf16_to_f32(x & 1 ? kw[u][x >> 1] >> 16 : kw[u][x >> 1] & 0xFFFFu);
-                const float vf = bf16_to_f32(x & 1 ? vw[u][x >> 1] >> 16 : vw[u][x >> 1] & 0xFFFFu);
-                VbT[(c8 + x) * LD_C + ti_] = (_Float16)(bv * vf);
-                KbT[(c8 + x) * LD_C + ti_] = (_Float16)(bk * kf);
-            }
+            for (int x = 0; x < 8; ++x)
+                BT[(c8 + x) * LD_C + ti_] =
+                    (_Float16)(sc * bf16_to_f32(x & 1 ? src[x >> 1] >> 16 : src[x >> 1] & 0xFFFFu));
         }
-    }
-    __syncthreads();
-    // Ut = T (beta V) and W = T (beta b K): wave w owns row tile w/2 and
-    // column tiles 2 (w%2), 2 (w%2) + 1 of both (column tile = state slice)
-    float16v aU[2], aW[2];
+        __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int tc = 2 * (w & 1) + u;
-        aU[u] = aW[u] = (float16v)0.f;
-        mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, VbT + 32 * tc * LD_C, LD_C, aU[u]);
-        mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, KbT + 32 * tc * LD_C, LD_C, aW[u]);
+        for (int u = 0; u < 2; ++u) {
+            const int tc = 2 * (w & 1) + u;
+            float16v a = (float16v)0.f;
+            mma_rows<GC>(Ts + 32 * ti * LD_C, LD_C, BT + 32 * tc * LD_C, LD_C, a);
+            if (pass == 0) aU[u] = a;
+            else aW[u] = a;
+        }
+        __syncthreads();              // BT (and after the second pass Ts) read
     }
-    __syncthreads();                  // Ts, VbT, KbT read: the region stages the outputs
     // staged in their image layouts (Ut: 4 slices of [64][32] fp16, then W
     // [64][136] fp16), then stored with 16-byte writes
     {
