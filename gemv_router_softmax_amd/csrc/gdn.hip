@@ -221,24 +221,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         float tq[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) tq[q] = 0.f;
-        // row i + 1 of L is read while row i is reduced
+        // row i + 1 of L is read while row i is reduced.  Only rows j < i
+        // contribute (the rest of T's column is still zero), i.e. q <
+        // ceil(i / 4): with i a constant after unrolling, the other terms
+        // and their reads are left out (up to the sign of a zero, the sums
+        // are the same)
         float4v lcur[4], lnxt[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) lcur[b] = reinterpret_cast<const float4v*>(Lp + s * 16)[b];
+        for (int b = 0; b < 4; ++b) lcur[b] = lnxt[b] = (float4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < GC; ++i) {
+            const int nq = (i + 3) / 4, nqn = (i + 4) / 4;   // active q of rows i and i + 1
             if (i + 1 < GC) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    lnxt[b] = reinterpret_cast<const float4v*>(Lp + (i + 1) * GC + s * 16)[b];
+                    if (4 * b < nqn) lnxt[b] = reinterpret_cast<const float4v*>(Lp + (i + 1) * GC + s * 16)[b];
             }
-            float part[4];
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
+                if (4 * b >= nq) continue;
                 const float4v lv = lcur[b];
                 part[b] = lv[0] * tq[4 * b];
 #pragma unroll
-                for (int x = 1; x < 4; ++x) part[b] = fmaf(lv[x], tq[4 * b + x], part[b]);
+                for (int x = 1; x < 4; ++x)
+                    if (4 * b + x < nq) part[b] = fmaf(lv[x], tq[4 * b + x], part[b]);
             }
             float sum = (part[0] + part[1]) + (part[2] + part[3]);
             sum += dpp_f<DPP_XOR1>(sum);
