@@ -218,9 +218,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     // are still zero, as are L's entries there); four partial sums per lane
     {
         const int m = tid >> 2, s = tid & 3;
+        // the column starts as the identity's: row m's 1 is final (the sum
+        // of row m is over rows j < m, where the column is zero), and rows
+        // not yet solved are multiplied only by L's zeros on and above the
+        // diagonal, so step i just subtracts its sum from the row's entry
         float tq[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) tq[q] = 0.f;
+        for (int q = 0; q < 16; ++q) tq[q] = 4 * q + s == m ? 1.f : 0.f;
+        bool mine[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) mine[x] = s == x;
         // row i + 1 of L is read while row i is reduced.  Only rows j < i
         // contribute (the rest of T's column is still zero), i.e. q <
         // ceil(i / 4): with i a constant after unrolling, the other terms
@@ -250,8 +257,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             float sum = (part[0] + part[1]) + (part[2] + part[3]);
             sum += dpp_f<DPP_XOR1>(sum);
             sum += dpp_f<DPP_XOR2>(sum);
-            const float tim = (i == m ? 1.f : 0.f) - sum;
-            if (s == (i & 3)) tq[i >> 2] = tim;
+            const float tim = tq[i >> 2] - sum;
+            tq[i >> 2] = mine[i & 3] ? tim : tq[i >> 2];
 #pragma unroll
             for (int b = 0; b < 4; ++b) lcur[b] = lnxt[b];
         }
