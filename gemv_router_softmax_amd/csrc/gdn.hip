@@ -24,8 +24,9 @@
 //
 //   gdn_prep  grid (chunks, hv): per chunk and head, K K^T and Q K^T on
 //             MFMA, the masks and decays, T by forward substitution (fp32,
-//             one quad of lanes per column), Ut and W on MFMA; writes Q, W,
-//             A, Ut (fp16), the decayed K^T (fp16) and gam to the workspace.
+//             one quad of lanes per column), Ut and W on MFMA; writes W, A,
+//             Ut, the decayed K^T (fp16), gam and -- once per key head -- Q
+//             (fp16) to the workspace.
 //   gdn_scan  grid (hv, 4): one workgroup per head and 32-row slice of the
 //             state (rows are value channels, independent of one another).
 //             The slice (32 x 128 fp32) stays in four compute waves' MFMA
@@ -61,7 +62,8 @@ constexpr int UT_SLICE = GC * 32 * 2;             // fp16 Ut[:, 32 z .. 32 z + 3
 constexpr int GW_BLK = IMG_COMMON + 4 * UT_SLICE;
 constexpr int STAGE_IMG = IMG_COMMON + UT_SLICE;  // 66 KB moved per chunk and slice
 constexpr int STAGE = STAGE_IMG;                  // one LDS stage holds one image
-static_assert(IMG_COMMON % 1024 == 0 && STAGE_IMG % 1024 == 0 && STAGE >= STAGE_IMG, "1 KB slots");
+static_assert(IMG_COMMON % 1024 == 0 && IMG_W % 1024 == 0 && STAGE_IMG % 1024 == 0 && STAGE >= STAGE_IMG,
+              "1 KB slots");
 static_assert(GW_BLK % 256 == 0, "workspace blocks stay 256-byte aligned");
 
 typedef float float16v __attribute__((ext_vector_type(16)));
@@ -183,7 +185,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             const half8 qh = bf16x8_to_h8(qw[u]);
             *reinterpret_cast<half8*>(Ks + ti_ * LD_D + c8) = bf16x8_to_h8(kw[u]);
             *reinterpret_cast<half8*>(Qs + ti_ * LD_D + c8) = qh;
-            *reinterpret_cast<half8*>(blk + IMG_Q + (ti_ * LD_D + c8) * 2) = qh;
+            if (h % (p.hv / p.hk) == 0)   // (one copy per key head)
+                *reinterpret_cast<half8*>(blk + IMG_Q + (ti_ * LD_D + c8) * 2) = qh;
 #pragma unroll
             for (int x = 0; x < 8; ++x)
                 kd_img[(c8 + x) * LD_C + ti_] =
@@ -340,17 +343,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gdn_rsrc(const void* base, uin
 // block's common part (j < 62) or of the slice's Ut columns (j = 62 .. 65).
 constexpr int MV_SLOTS = 22;
 static_assert(3 * MV_SLOTS * 1024 == STAGE_IMG, "three movers cover an image");
+// The Q image depends only on the key head: the first value head of each
+// key head's group holds it for the group, so the range starts at that
+// head's block.
 __device__ __forceinline__ void gdn_issue(const GdnArgs& p, int c, int h, int z, int m,
                                           uint8_t* __restrict__ stage) {
-    const uint8_t* blk = gdn_uniform(p.ws + ((size_t)c * p.hv + h) * GW_BLK);
-    const __amdgpu_buffer_rsrc_t r = gdn_rsrc(blk, GW_BLK);
+    const int grp = p.hv / p.hk, hq = h - h % grp;
+    const uint8_t* blk = gdn_uniform(p.ws + ((size_t)c * p.hv + hq) * GW_BLK);
+    const __amdgpu_buffer_rsrc_t r = gdn_rsrc(blk, (uint32_t)grp * GW_BLK);
+    const uint32_t own = (uint32_t)(h - hq) * GW_BLK;
     const uint32_t lane16 = (threadIdx.x & 63) * 16;
 #pragma unroll
     for (int i = 0; i < MV_SLOTS; ++i) {
         const int j = m * MV_SLOTS + i;
-        const uint32_t src = j < IMG_COMMON / 1024
-                                 ? (uint32_t)j * 1024
-                                 : (uint32_t)(IMG_COMMON + z * UT_SLICE + (j - IMG_COMMON / 1024) * 1024);
+        const uint32_t src = j < IMG_W / 1024 ? (uint32_t)j * 1024
+                             : j < IMG_COMMON / 1024
+                                 ? own + (uint32_t)j * 1024
+                                 : own + (uint32_t)(IMG_COMMON + z * UT_SLICE + (j - IMG_COMMON / 1024) * 1024);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (gdn_lds_t)(stage + j * 1024), 16, lane16, src, 0, 0);
     }
 }
