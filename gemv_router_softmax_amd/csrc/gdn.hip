@@ -386,16 +386,16 @@ __device__ __forceinline__ void gdn_barrier() {
 // code.  The 66 loads of an image are split so that no mover holds up a
 // barrier: mover 0 issues slots 0..21 after barrier (1) (the compute waves
 // then multiply for a while), movers 1 and 2 slots 22..43 and 44..65 after
-// barrier (2).  Three barriers per chunk, matched one for one by gdn_chunk.
+// barrier (2).  Two barriers per chunk, matched one for one by gdn_chunk.
 __device__ __forceinline__ void gdn_mover_chunk(const GdnArgs& p, int c, int nch, int h, int z,
                                                 int m, uint8_t* __restrict__ nxt) {
     __builtin_amdgcn_s_waitcnt(gdn_vmcnt(0));       // this mover's part of chunk c landed
     gdn_barrier();                                // (1) chunk c ready, S16 staged
-    // (nxt was last read before barrier (3) of chunk c - 1)
+    // (every compute wave read nxt, chunk c - 1's image, before it staged
+    // S16 for chunk c and reached barrier (1))
     if (m == 0 && c + 1 < nch) gdn_issue(p, c + 1, h, z, m, nxt);
     gdn_barrier();                                // (2)
     if (m != 0 && c + 1 < nch) gdn_issue(p, c + 1, h, z, m, nxt);
-    gdn_barrier();                                // (3)
 }
 
 // Output rows of one chunk (waves 2, 3: rows 32 (w - 2) .. of the chunk
@@ -475,7 +475,10 @@ __device__ __forceinline__ void gdn_chunk(const GdnArgs& p, int c, int h, int z,
     } else {
         mma_rows<GC>(UT, LD_C, KdT + 32 * w * LD_C, LD_C, S);
     }
-    gdn_barrier();                                // (3)
+    // No barrier here: the next chunk's S16 writes follow this chunk's S16
+    // reads across barrier (2), its U^T writes follow every wave's U^T reads
+    // across its barrier (1), and the movers refill this chunk's image only
+    // after that barrier too.
 }
 
 // grid (hv, 4) workgroups of 7 waves: waves 0-3 compute (wave w holds the
