@@ -498,6 +498,36 @@ def gdn_scan_leg(T=2048, hk=None, hv=None, iters=50):
             "timing": "HIP events around graph replays of one moe_gdn_scan call"}
 
 
+def gdn_step_leg(layers=40, hk=None, hv=None, iters=50, T=1):
+    """One decode token (or T tokens) through `layers` recurrent layers
+    (moe_gdn_scan; T = 1 takes the token-by-token kernel), each layer with
+    its own state updated in place, captured as one HIP graph; per-layer
+    time from HIP events.  Bytes per layer: the state read and written
+    (fp32 [hv][128][128] each way) plus q, k, v, g, beta and o."""
+    import torch
+    import gemv_router_softmax_amd as moe
+    from gemv_router_softmax_amd import synth
+    hk = hk or synth.GDN_HK
+    hv = hv or synth.GDN_HV
+    xs = [synth.make_gdn(T, hk, hv, seed=100 + i) for i in range(layers)]
+    dev = [tuple(moe.to_device_bits(a) for a in (x.q, x.k, x.v)) +
+           tuple(torch.from_numpy(a).cuda() for a in (x.g, x.beta, x.s0)) for x in xs]
+    o = torch.empty((T, hv, 128), dtype=torch.int16, device="cuda")
+    ws = moe.gdn_workspace(T, hv)
+
+    def step():
+        for q, k, v, g, beta, st in dev:
+            moe.moe_gdn_scan(q, k, v, g, beta, o, ws, s0=st, s_out=st)
+
+    ms = _graphs_timed([step], iters)
+    t = float(ms.mean()) * 1e-3 / layers
+    nbytes = hv * 128 * 128 * 4 * 2 + T * (hk * 128 * 2 * 2 + hv * 128 * 2 * 2 + hv * 4 * 2)
+    return {"T": T, "layers": layers, "key_heads": hk, "value_heads": hv, "dim": 128,
+            "us_per_layer": t * 1e6, "bytes_per_layer": nbytes, "gbs": nbytes / t / 1e9,
+            "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
+            "timing": "HIP events around graph replays of the layers' calls, one after another"}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -637,9 +667,12 @@ def main():
         greedy = greedy_decode(D, 200)
         log(f"greedy decode step: {greedy}")
     gdn = None
+    gdn_step = None
     if "gdn" in legs:
         gdn = gdn_scan_leg()
         log(f"gated delta rule scan: {gdn}")
+        gdn_step = gdn_step_leg()
+        log(f"gated delta rule decode step: {gdn_step}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -682,6 +715,7 @@ def main():
         "prefill_skewed_t16384_chunks4096": skewed,
         "greedy_decode_step": greedy,
         "gdn_scan_t2048": gdn,
+        "gdn_step_t1": gdn_step,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -32,6 +32,7 @@ MOE_NOALLOC_WS_BYTES = 8388608
 
 MOE_GDN_DIM = 128
 MOE_GDN_CHUNK = 64
+MOE_GDN_STEP_T_MAX = 48
 MOE_GDN_HEADS_MAX = 64
 MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1

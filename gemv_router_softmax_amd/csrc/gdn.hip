@@ -521,6 +521,83 @@ __global__ __launch_bounds__(448) void gdn_scan(GdnArgs p) {
     }
 }
 
+// ------------------------------------------------------------------ step
+
+// Token by token, for short calls (decode: a few tokens per call), where
+// the chunked form's two kernels and per-chunk preparation cost more than
+// the state's own traffic.  grid (hv, 8) workgroups of 256 threads, each
+// holding 16 value rows of one head's state in registers, in fp32: thread
+// tid has row 16 blockIdx.y + tid / 16 and key channels 8 (tid % 16) .. +7,
+// so a row's 16 threads are one 16-lane DPP row.  Per token, with a = e^g:
+//   Sk_r = sum_c S[r][c] k[c]                      (row all-reduce)
+//   S[r][c] = a S[r][c] + beta (v_r - a Sk_r) k[c]  (= a S (I - beta k k^T) + beta v k^T)
+//   o_r = sum_c S[r][c] q[c]
+// The operands of the next four tokens are in flight while one is processed.
+constexpr int GS_ROWS = 16, GS_PF = 4;
+
+__device__ __forceinline__ void bf16x8_to_f32(uint4v w, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+}
+
+__global__ __launch_bounds__(256) void gdn_step(GdnArgs p) {
+    const int h = blockIdx.x, r = blockIdx.y * GS_ROWS + (threadIdx.x >> 4), cg = threadIdx.x & 15;
+    const int kh = h / (p.hv / p.hk);
+    // (the state arrays are only 4-byte aligned)
+    const size_t so = ((size_t)h * GD + r) * GD + 8 * cg;
+    float S[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S[i] = p.s0 ? p.s0[so + i] : 0.f;
+    // operands of tokens t .. t + GS_PF - 1 in flight (slot t % GS_PF; the
+    // loop is unrolled by GS_PF so that the slots are registers)
+    uint4v kn[GS_PF], qn[GS_PF];
+    uint32_t vn[GS_PF];
+    float gn[GS_PF], bn[GS_PF];
+    auto fetch = [&](int t, int u) {
+        if (t < p.T) {
+            kn[u] = *reinterpret_cast<const uint4v*>(p.k + ((size_t)t * p.hk + kh) * GD + 8 * cg);
+            qn[u] = *reinterpret_cast<const uint4v*>(p.q + ((size_t)t * p.hk + kh) * GD + 8 * cg);
+            vn[u] = p.v[((size_t)t * p.hv + h) * GD + r];
+            gn[u] = p.g[(size_t)t * p.hv + h];
+            bn[u] = p.beta[(size_t)t * p.hv + h];
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < GS_PF; ++u) fetch(u, u);
+    for (int t0 = 0; t0 < p.T; t0 += GS_PF) {
+#pragma unroll
+        for (int u = 0; u < GS_PF; ++u) {
+            const int t = t0 + u;
+            if (t >= p.T) break;
+            float kk[8], qq[8];
+            bf16x8_to_f32(kn[u], kk);
+            bf16x8_to_f32(qn[u], qq);
+            const float vr = bf16_to_f32(vn[u]), a = __expf(gn[u]), bt = bn[u];
+            fetch(t + GS_PF, u);
+            float sk = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sk = fmaf(S[c], kk[c], sk);
+            sk = row16_sum(sk);
+            const float coef = bt * (vr - a * sk);
+            float so = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                S[c] = fmaf(coef, kk[c], a * S[c]);
+                so = fmaf(S[c], qq[c], so);
+            }
+            so = row16_sum(so);
+            if (cg == 0) p.o[((size_t)t * p.hv + h) * GD + r] = (uint16_t)f32_to_bf16(so);
+        }
+    }
+    if (p.s_out) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p.s_out[so + i] = S[i];
+    }
+}
+
 }  // namespace moe
 
 extern "C" size_t moe_gdn_workspace_bytes(int T, int hv) {
@@ -543,9 +620,13 @@ extern "C" int moe_gdn_scan(const uint16_t* q, const uint16_t* k, const uint16_t
     if (T > 0 && ws_bytes < moe_gdn_workspace_bytes(T, hv)) return MOE_ERR_WORKSPACE;
     moe::GdnArgs p{q, k, v, g, beta, s0, o, s_out, (uint8_t*)ws, T, hk, hv};
     const hipStream_t st = (hipStream_t)stream;
-    const int nch = (T + moe::GC - 1) / moe::GC;
-    if (nch > 0) hipLaunchKernelGGL(moe::gdn_prep, dim3(nch, hv), dim3(256), 0, st, p);
-    // (with no tokens the scan kernel only passes the state through)
-    hipLaunchKernelGGL(moe::gdn_scan, dim3(hv, moe::GD / 32), dim3(448), 0, st, p);
+    if (T <= MOE_GDN_STEP_T_MAX) {
+        // (with no tokens the state only passes through)
+        hipLaunchKernelGGL(moe::gdn_step, dim3(hv, moe::GD / moe::GS_ROWS), dim3(256), 0, st, p);
+    } else {
+        const int nch = (T + moe::GC - 1) / moe::GC;
+        hipLaunchKernelGGL(moe::gdn_prep, dim3(nch, hv), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(moe::gdn_scan, dim3(hv, moe::GD / 32), dim3(448), 0, st, p);
+    }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

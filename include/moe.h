@@ -305,14 +305,18 @@ int moe_embed(const int32_t *token, int T, const uint16_t *emb, int V, uint16_t 
  *   S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
  *   o_t = S_t q_t.
  * q and k are used as given (any normalisation or scaling of them is the
- * caller's).  Computed in chunks of MOE_GDN_CHUNK tokens on fp16 MFMA with
- * fp32 accumulation and an fp32 state (fp16 operands: see the library's
- * documentation for the error this gives).
+ * caller's).  Calls of up to MOE_GDN_STEP_T_MAX tokens (decode) run the
+ * recurrence token by token in fp32 with the state in registers (the
+ * workspace is then not used); longer ones are computed in chunks of
+ * MOE_GDN_CHUNK tokens on fp16 MFMA with fp32 accumulation and an fp32
+ * state (fp16 operands: see the library's documentation for the error this
+ * gives).
  * In: q, k bf16 [T][hk][128]; v bf16 [T][hv][128] (16-byte aligned);
  * g (log decay) and beta fp32 [T][hv]; s0 fp32 [hv][128][128], the state
  * entering token 0, or NULL for zero.  Out: o bf16 [T][hv][128] (rounded
  * to nearest even); s_out fp32 [hv][128][128], the state after token T-1,
- * or NULL.  ws: moe_gdn_workspace_bytes(T, hv) bytes of device scratch,
+ * or NULL; it may be s0 itself (the state updated in place, as a decode
+ * loop does).  ws: moe_gdn_workspace_bytes(T, hv) bytes of device scratch,
  * 256-byte aligned, not read before it is written.  1 <= hk, hv <=
  * MOE_GDN_HEADS_MAX, hv a multiple of hk, 0 <= T <= MOE_T_MAX (T == 0:
  * s_out, if given, receives s0 or zeros).  Errors: NULL or a size out of
@@ -320,6 +324,7 @@ int moe_embed(const int32_t *token, int T, const uint16_t *emb, int V, uint16_t 
  * -> MOE_ERR_WORKSPACE.  Deterministic. */
 #define MOE_GDN_DIM 128
 #define MOE_GDN_CHUNK 64
+#define MOE_GDN_STEP_T_MAX 48
 #define MOE_GDN_HEADS_MAX 64
 size_t moe_gdn_workspace_bytes(int T, int hv);   /* 0 for arguments out of range */
 int moe_gdn_scan(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,

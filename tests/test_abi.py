@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
     src = open(HEADER).read()
     for name in ("MOE_HIDDEN", "MOE_INTER", "MOE_EXPERTS", "MOE_TOPK", "MOE_GROUP", "MOE_T_MAX",
                  "MOE_DECODE_T", "MOE_DECODE_T_MAX", "MOE_NOALLOC_T_MAX", "MOE_NOALLOC_WS_BYTES",
-                 "MOE_GDN_DIM", "MOE_GDN_CHUNK", "MOE_GDN_HEADS_MAX"):
+                 "MOE_GDN_DIM", "MOE_GDN_CHUNK", "MOE_GDN_STEP_T_MAX", "MOE_GDN_HEADS_MAX"):
         m = re.search(rf"#define {name} (\d+)", src)
         assert int(m.group(1)) == getattr(moe, name), name
 
