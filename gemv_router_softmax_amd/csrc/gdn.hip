@@ -546,11 +546,22 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4v w, float (&f)[8]) {
 __global__ __launch_bounds__(256) void gdn_step(GdnArgs p) {
     const int h = blockIdx.x, r = blockIdx.y * GS_ROWS + (threadIdx.x >> 4), cg = threadIdx.x & 15;
     const int kh = h / (p.hv / p.hk);
-    // (the state arrays are only 4-byte aligned)
+    // (16-byte accesses where the state arrays allow them; they need only
+    // be 4-byte aligned)
     const size_t so = ((size_t)h * GD + r) * GD + 8 * cg;
     float S[8];
+    if (p.s0 && ((uintptr_t)p.s0 & 15) == 0) {
+        const float4v* sp = reinterpret_cast<const float4v*>(p.s0 + so);
+        const float4v s0 = sp[0], s1 = sp[1];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S[i] = p.s0 ? p.s0[so + i] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            S[i] = s0[i];
+            S[4 + i] = s1[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S[i] = p.s0 ? p.s0[so + i] : 0.f;
+    }
     // operands of tokens t .. t + GS_PF - 1 in flight (slot t % GS_PF; the
     // loop is unrolled by GS_PF so that the slots are registers)
     uint4v kn[GS_PF], qn[GS_PF];
@@ -592,7 +603,11 @@ __global__ __launch_bounds__(256) void gdn_step(GdnArgs p) {
             if (cg == 0) p.o[((size_t)t * p.hv + h) * GD + r] = (uint16_t)f32_to_bf16(so);
         }
     }
-    if (p.s_out) {
+    if (p.s_out && ((uintptr_t)p.s_out & 15) == 0) {
+        float4v* sp = reinterpret_cast<float4v*>(p.s_out + so);
+        sp[0] = (float4v){S[0], S[1], S[2], S[3]};
+        sp[1] = (float4v){S[4], S[5], S[6], S[7]};
+    } else if (p.s_out) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) p.s_out[so + i] = S[i];
     }
