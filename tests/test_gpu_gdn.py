@@ -191,3 +191,30 @@ def test_gdn_split_across_paths_in_place():
     srel = np.linalg.norm(st.cpu().numpy() - ref.state) / np.linalg.norm(ref.state)
     print(f"split across paths: o relL2={rel:.2e} state relL2={srel:.2e}", flush=True)
     assert rel <= O_REL and srel <= S_REL
+
+
+def test_gdn_step_state_4_byte_aligned():
+    """The state arrays need only be 4-byte aligned: a state one float off a
+    16-byte boundary (the token-by-token kernel's per-element path) gives
+    exactly what the 16-byte-aligned state gives."""
+    x = synth.make_gdn(3, 1, 2, seed=31)
+    n = x.s0.size
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, k, v = (moe.to_device_bits(a) for a in (x.q, x.k, x.v))
+    g, beta = dev(x.g), dev(x.beta)
+    ws = moe.gdn_workspace(3, 2)
+    outs = []
+    for off in (0, 1):
+        buf = torch.zeros(2 * n + 8, dtype=torch.float32, device="cuda")
+        s0 = buf[off:off + n].view(x.s0.shape)
+        s0.copy_(dev(x.s0))
+        s_out = buf[n + 4 + off:n + 4 + off + n].view(x.s0.shape)
+        assert (s0.data_ptr() % 16 == 0) == (off == 0)
+        o = torch.empty((3, 2, 128), dtype=torch.int16, device="cuda")
+        moe.moe_gdn_scan(q, k, v, g, beta, o, ws, s0=s0, s_out=s_out)
+        torch.cuda.synchronize()
+        outs.append((moe.bits_to_numpy(o), s_out.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    ref = oracle.load().gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.s0)
+    srel = np.linalg.norm(outs[1][1] - ref.state) / np.linalg.norm(ref.state)
+    assert srel <= STEP_S_REL
