@@ -237,15 +237,18 @@ static int route_ksplit(int T) {
 // layer) also the fp16 copy of the token's row in chunk-slot order that the
 // grouped GEMM reads (xh), which saves the conversion kernel.
 //
-// part / nks: K-split partial logits [nks][T][E] of route_logits_tile<KS>
-// (nks > 1): summed here in slice order, plus the bias (and stored to
-// logits if it is given).
+// part / NKS: K-split partial logits [NKS][T][E] of route_logits_tile<KS>
+// (NKS > 1; 0: none, the logits are read): summed here in slice order, plus
+// the bias (and stored to logits if it is given).  NKS is a template
+// argument so that every slice's load is in flight before the sum (a loop
+// bounded at run time waited for each load before issuing the next).
 //
 // chunk_counts: optional; each token's eight experts are added to the
 // histogram of its permutation chunk, chunk_counts[8t / PERM_CHUNK][e]
 // (integer atomics: the counts do not depend on their order).
+template <int NKS>
 __global__ __launch_bounds__(256) void route_topk(float* __restrict__ logits,
-                                                  const float* __restrict__ part, int nks,
+                                                  const float* __restrict__ part,
                                                   const float* __restrict__ bias,
                                                   const uint16_t* __restrict__ x,
                                                   const uint16_t* __restrict__ wsg, int T,
@@ -260,10 +263,14 @@ __global__ __launch_bounds__(256) void route_topk(float* __restrict__ logits,
     int e;
     const uint4v* xr = reinterpret_cast<const uint4v*>(x + (size_t)t * H) + lane * 4;
     const uint4v x0 = xr[0], x1 = xr[1], x2 = xr[2], x3 = xr[3];
-    if (part) {
-        float4v v = reinterpret_cast<const float4v*>(part + (size_t)t * E)[lane];
-        for (int k = 1; k < nks; ++k)
-            v += reinterpret_cast<const float4v*>(part + ((size_t)k * T + t) * E)[lane];
+    if constexpr (NKS > 0) {
+        float4v pv[NKS];
+#pragma unroll
+        for (int k = 0; k < NKS; ++k)
+            pv[k] = reinterpret_cast<const float4v*>(part + ((size_t)k * T + t) * E)[lane];
+        float4v v = pv[0];
+#pragma unroll
+        for (int k = 1; k < NKS; ++k) v += pv[k];
         if (bias) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] += bias[lane * 4 + j];
@@ -325,8 +332,8 @@ void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bia
                                st, x, T, wr, bias, logits, chunk_counts, nzero);
         else
             launch_route_logits(x, T, wr, bias, logits, st, chunk_counts, nzero);
-        hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits,
-                           (const float*)nullptr, 0, (const float*)nullptr, x, wsg, T, ids, wts,
+        hipLaunchKernelGGL(route_topk<0>, dim3((T + 3) / 4), dim3(256), 0, st, logits,
+                           (const float*)nullptr, (const float*)nullptr, x, wsg, T, ids, wts,
                            sg, xh, chunk_counts);
         return;
     }
@@ -348,8 +355,15 @@ void launch_route(const uint16_t* x, int T, const uint16_t* wr, const float* bia
     }
 #undef RL_LAUNCH
     // (nothing reads the summed logits after the top-8: not stored)
-    hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, st, (float*)nullptr,
-                       (const float*)part, ks, bias, x, wsg, T, ids, wts, sg, xh, chunk_counts);
+#define RT_LAUNCH(K)                                                                        \
+    hipLaunchKernelGGL(route_topk<K>, dim3((T + 3) / 4), dim3(256), 0, st, (float*)nullptr,       \
+                       (const float*)part, bias, x, wsg, T, ids, wts, sg, xh, chunk_counts)
+    switch (ks) {
+        case 2: RT_LAUNCH(2); break;
+        case 4: RT_LAUNCH(4); break;
+        default: RT_LAUNCH(8); break;
+    }
+#undef RT_LAUNCH
 }
 
 }  // namespace moe
