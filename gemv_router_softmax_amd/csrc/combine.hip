@@ -16,14 +16,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int t = blockIdx.x;
     const int m = (blockIdx.y * 256 + threadIdx.x) * 4;
     float4v acc = (float4v){0.f, 0.f, 0.f, 0.f};
+    // (every row's load in flight at once; an entry out of range reads row
+    // 0 and adds nothing)
+    float4v dv[TOPK];
+    float wv[TOPK];
+    bool ok[TOPK];
 #pragma unroll
     for (int j = 0; j < TOPK; ++j) {
         const int p = inv[(size_t)t * TOPK + j];
-        if (p < 0 || p >= TOPK * T) continue;
-        const float w = wts[(size_t)t * TOPK + j];
-        const float4v d = *reinterpret_cast<const float4v*>(out + (size_t)p * H + m);
-        acc += w * d;
+        ok[j] = p >= 0 && p < TOPK * T;
+        wv[j] = wts[(size_t)t * TOPK + j];
+        dv[j] = *reinterpret_cast<const float4v*>(out + (size_t)(ok[j] ? p : 0) * H + m);
     }
+#pragma unroll
+    for (int j = 0; j < TOPK; ++j)
+        if (ok[j]) acc += wv[j] * dv[j];
     {
         const float4v d = *reinterpret_cast<const float4v*>(out + ((size_t)TOPK * T + t) * H + m);
         acc += sg[t] * d;
@@ -66,16 +73,23 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __rest
 #pragma unroll
     for (int jj = 0; jj < TOPK; ++jj) rows[jj] = inv[(size_t)t * TOPK + jj];
     rows[TOPK] = TOPK * T + t;
+    // all nine rows in flight at once (a load under a condition was waited
+    // for before the next was issued); an entry out of range reads row 0
+    // and adds nothing
+    uint4v rv[TOPK + 1];
+    bool ok[TOPK + 1];
 #pragma unroll
     for (int jj = 0; jj <= TOPK; ++jj) {
-        const int p = rows[jj];
-        if (p < 0 || p >= (TOPK + 1) * T) continue;
-        const uint4v v = *reinterpret_cast<const uint4v*>(d16 + (size_t)p * H + m);
+        ok[jj] = rows[jj] >= 0 && rows[jj] < (TOPK + 1) * T;
+        rv[jj] = *reinterpret_cast<const uint4v*>(d16 + (size_t)(ok[jj] ? rows[jj] : 0) * H + m);
+    }
+#pragma unroll
+    for (int jj = 0; jj <= TOPK; ++jj) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const uint32_t w = v[k >> 1];
+            const uint32_t w = rv[jj][k >> 1];
             const uint16_t hb = (uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFFu));
-            acc[k] += (float)__builtin_bit_cast(_Float16, hb);
+            if (ok[jj]) acc[k] += (float)__builtin_bit_cast(_Float16, hb);
         }
     }
     uint4v yo, ro;
