@@ -548,10 +548,10 @@ __global__ __launch_bounds__(256) void gdn_step(GdnArgs p) {
     const int kh = h / (p.hv / p.hk);
     // (16-byte accesses where the state arrays allow them; they need only
     // be 4-byte aligned)
-    const size_t so = ((size_t)h * GD + r) * GD + 8 * cg;
+    const size_t soff = ((size_t)h * GD + r) * GD + 8 * cg;
     float S[8];
     if (p.s0 && ((uintptr_t)p.s0 & 15) == 0) {
-        const float4v* sp = reinterpret_cast<const float4v*>(p.s0 + so);
+        const float4v* sp = reinterpret_cast<const float4v*>(p.s0 + soff);
         const float4v s0 = sp[0], s1 = sp[1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256) void gdn_step(GdnArgs p) {
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) S[i] = p.s0 ? p.s0[so + i] : 0.f;
+        for (int i = 0; i < 8; ++i) S[i] = p.s0 ? p.s0[soff + i] : 0.f;
     }
     // operands of tokens t .. t + GS_PF - 1 in flight (slot t % GS_PF; the
     // loop is unrolled by GS_PF so that the slots are registers)
@@ -593,23 +593,23 @@ __global__ __launch_bounds__(256) void gdn_step(GdnArgs p) {
             for (int c = 0; c < 8; ++c) sk = fmaf(S[c], kk[c], sk);
             sk = row16_sum(sk);
             const float coef = bt * (vr - a * sk);
-            float so = 0.f;
+            float ov = 0.f;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 S[c] = fmaf(coef, kk[c], a * S[c]);
-                so = fmaf(S[c], qq[c], so);
+                ov = fmaf(S[c], qq[c], ov);
             }
-            so = row16_sum(so);
-            if (cg == 0) p.o[((size_t)t * p.hv + h) * GD + r] = (uint16_t)f32_to_bf16(so);
+            ov = row16_sum(ov);
+            if (cg == 0) p.o[((size_t)t * p.hv + h) * GD + r] = (uint16_t)f32_to_bf16(ov);
         }
     }
     if (p.s_out && ((uintptr_t)p.s_out & 15) == 0) {
-        float4v* sp = reinterpret_cast<float4v*>(p.s_out + so);
+        float4v* sp = reinterpret_cast<float4v*>(p.s_out + soff);
         sp[0] = (float4v){S[0], S[1], S[2], S[3]};
         sp[1] = (float4v){S[4], S[5], S[6], S[7]};
     } else if (p.s_out) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p.s_out[so + i] = S[i];
+        for (int i = 0; i < 8; ++i) p.s_out[soff + i] = S[i];
     }
 }
 
