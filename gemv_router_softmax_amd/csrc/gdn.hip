@@ -40,6 +40,11 @@
 // q, k, v are bf16 inputs converted to fp16 (exact within fp16's range);
 // beta v, beta b k, T, W, A, U and the staged state are rounded to fp16 as
 // MFMA operands; the state, Ut and every accumulation stay fp32.
+//
+// Calls of up to MOE_GDN_STEP_T_MAX tokens (decode) skip all of this:
+//   gdn_step  grid (hv, 8): the recurrence itself, token by token, in fp32,
+//             each workgroup holding 16 rows of a head's state in registers
+//             (see the kernel).
 #include "common.hpp"
 
 namespace moe {
